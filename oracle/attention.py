@@ -1,0 +1,277 @@
+"""Exact attention over a paged KV cache, in float64, written from definitions.
+
+TEST INFRASTRUCTURE: see the package docstring for who may import this.
+
+What is computed (Ye et al. record, *boundary*: the engine's result is plain
+exact attention; backend-selection note, *Arithmetic intensity*: the paged
+layout changes where K/V are read from, not the FLOPs):
+
+    for query row q (one query token, one q head h, kv head g = h // (Hq/Hkv)):
+        s_t  = sm_scale * <q, K[t]>              over the visible keys t
+        lse  = ln sum_t exp(s_t)                 (natural log)
+        o    = sum_t exp(s_t - lse) * V[t]
+    no visible key:  o = 0, lse = -inf
+
+Readings where the pages are silent (each also listed in the design notes):
+* q head h reads kv head h // (Hq/Hkv) (contiguous groups);
+* token t of a sequence is in page ``indices[start + t // ps]``, slot ``t % ps``;
+* append: the i-th of qo new queries sits at absolute position L - qo + i and
+  sees keys 0..L-qo+i (bottom-right causal alignment);
+* the LSE is reported in natural log;
+* merging states (o_j, lse_j) is the log-sum-exp identity, folded left in
+  index order; merging with (x, -inf) is the identity.
+
+Inputs are NumPy arrays; pools may be float32 (bf16 values are exact in fp32)
+and every gathered row is upcast to float64 before any arithmetic.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _heads_of(kv_head: int, group: int) -> slice:
+    return slice(kv_head * group, (kv_head + 1) * group)
+
+
+def gather_tokens(pool, indices, start: int, length: int, page_size: int,
+                  kv_head: int) -> np.ndarray:
+    """Tokens 0..length-1 of one sequence for one kv head, in token order.
+
+    Block-table gather (backend-selection note, *Arithmetic intensity*; Ye et
+    al. record, *summary*: block-sparse KV storage). ``pool`` is
+    ``[num_pages, Hkv, page_size, D]``. Pinned by: brute force against a dense
+    cache scattered into random pages, pool-permutation and page-size
+    invariance, needle keys placed across page boundaries.
+    """
+    d = pool.shape[-1]
+    if length <= 0:
+        return np.zeros((0, d), dtype=np.float64)
+    n_pages = (length + page_size - 1) // page_size
+    pages = np.asarray(indices[start:start + n_pages], dtype=np.int64)
+    assert pages.size == n_pages, "block table shorter than the sequence"
+    tiles = np.asarray(pool[pages, kv_head], dtype=np.float64)   # [n, ps, D]
+    return tiles.reshape(n_pages * page_size, d)[:length]
+
+
+def attend(q, k, v, sm_scale: float, visible=None):
+    """Exact softmax attention of query rows ``q [n, D]`` over ``k, v [L, D]``.
+
+    Returns ``(o [n, D], lse [n])``. ``visible`` is an optional ``[n, L]``
+    boolean mask. Rows that see no key get ``o = 0, lse = -inf``. Pinned by:
+    torch's scaled_dot_product_attention in float64 (o), closed forms for L=1,
+    equal logits, two tokens and a needle (o and lse), constant V.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n, d = q.shape[0], v.shape[1] if v.ndim == 2 else q.shape[1]
+    o = np.zeros((n, d), dtype=np.float64)
+    lse = np.full(n, NEG_INF, dtype=np.float64)
+    if k.shape[0] == 0 or n == 0:
+        return o, lse
+    s = float(sm_scale) * (q @ k.T)
+    if visible is not None:
+        s = np.where(visible, s, NEG_INF)
+    m = s.max(axis=1)
+    live = m > NEG_INF
+    if not live.any():
+        return o, lse
+    w = np.exp(s[live] - m[live, None])
+    z = w.sum(axis=1)
+    lse[live] = m[live] + np.log(z)
+    o[live] = (w @ v) / z[:, None]
+    return o, lse
+
+
+def _req_list(batch, requests):
+    return range(batch) if requests is None else [int(r) for r in requests]
+
+
+def paged_decode(q, k_pool, v_pool, kv_indptr, kv_indices, kv_len, page_size: int,
+                 sm_scale: float, requests=None):
+    """Decode attention: one query token per request over its paged KV.
+
+    ``q [B, Hq, D]``; returns ``o [B, Hq, D]``, ``lse [B, Hq]`` (rows of
+    requests not in ``requests`` are NaN). Pinned by: dense brute force via
+    torch SDPA, invariants (pool permutation, page size, split + merge),
+    needle and poison tests.
+    """
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    o = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for r in _req_list(B, requests):
+        a, L = int(kv_indptr[r]), int(kv_len[r])
+        for g in range(Hkv):
+            K = gather_tokens(k_pool, kv_indices, a, L, page_size, g)
+            V = gather_tokens(v_pool, kv_indices, a, L, page_size, g)
+            hs = _heads_of(g, G)
+            o[r, hs], lse[r, hs] = attend(q[r, hs], K, V, sm_scale)
+    return o, lse
+
+
+def paged_append(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
+                 page_size: int, sm_scale: float, causal: bool = True, requests=None):
+    """Attention for ``qo`` new query tokens per request over ``kv_len`` keys
+    (which already include the new tokens). Causal: query i (0-based among the
+    request's qo queries) sees keys ``t <= kv_len - qo + i``.
+
+    ``q [T, Hq, D]`` with request r's queries at rows ``qo_indptr[r]..``.
+    Returns ``o [T, Hq, D]``, ``lse [T, Hq]``. Pinned by: torch SDPA with an
+    explicit bottom-right mask, append with qo=1 == decode, a needle key
+    placed just past a query's horizon.
+    """
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    o = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    for r in _req_list(len(kv_len), requests):
+        q0, q1 = int(qo_indptr[r]), int(qo_indptr[r + 1])
+        nq, L, a = q1 - q0, int(kv_len[r]), int(kv_indptr[r])
+        if nq == 0:
+            continue
+        for g in range(Hkv):
+            K = gather_tokens(k_pool, kv_indices, a, L, page_size, g)
+            V = gather_tokens(v_pool, kv_indices, a, L, page_size, g)
+            hs = _heads_of(g, G)
+            rows = np.asarray(q[q0:q1, hs], dtype=np.float64).reshape(nq * G, D)
+            vis = None
+            if causal:
+                qpos = (L - nq) + np.repeat(np.arange(nq), G)        # row -> position
+                vis = np.arange(L)[None, :] <= qpos[:, None]
+            ob, lb = attend(rows, K, V, sm_scale, vis)
+            o[q0:q1, hs] = ob.reshape(nq, G, D)
+            lse[q0:q1, hs] = lb.reshape(nq, G)
+    return o, lse
+
+
+def scatter_new_kv(k_pool, v_pool, k_new, v_new, qo_indptr, kv_indptr, kv_indices,
+                   kv_len, page_size: int):
+    """Copies of the pools with the new tokens' K/V written into their slots.
+
+    New token i of request r (of qo) is sequence position ``kv_len - qo + i``.
+    Every other pool element is unchanged. Pinned by: direct element checks in
+    the tests (written slots equal the inputs, all other bytes untouched).
+    """
+    k_out, v_out = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    for r in range(len(kv_len)):
+        q0, q1 = int(qo_indptr[r]), int(qo_indptr[r + 1])
+        L, a = int(kv_len[r]), int(kv_indptr[r])
+        for i in range(q1 - q0):
+            pos = L - (q1 - q0) + i
+            page = int(kv_indices[a + pos // page_size])
+            k_out[page, :, pos % page_size, :] = k_new[q0 + i]
+            v_out[page, :, pos % page_size, :] = v_new[q0 + i]
+    return k_out, v_out
+
+
+def merge_two(o1, l1, o2, l2):
+    """Combine two attention states over disjoint key sets.
+
+    With M = max(l1, l2):  lse = M + ln(e^(l1-M) + e^(l2-M)),
+    o = (e^(l1-M) o1 + e^(l2-M) o2) / (e^(l1-M) + e^(l2-M)).  Two empty states
+    give (0, -inf). Works elementwise over leading dims (``o`` has a trailing D).
+    Pinned by: split-and-merge equals attention over the union (any partition),
+    commutativity, associativity, identity element.
+    """
+    o1 = np.asarray(o1, dtype=np.float64)
+    o2 = np.asarray(o2, dtype=np.float64)
+    l1 = np.asarray(l1, dtype=np.float64)
+    l2 = np.asarray(l2, dtype=np.float64)
+    M = np.maximum(l1, l2)
+    empty = M == NEG_INF
+    Ms = np.where(empty, 0.0, M)
+    w1 = np.where(l1 == NEG_INF, 0.0, np.exp(l1 - Ms))
+    w2 = np.where(l2 == NEG_INF, 0.0, np.exp(l2 - Ms))
+    z = w1 + w2
+    zs = np.where(empty, 1.0, z)
+    lse = np.where(empty, NEG_INF, Ms + np.log(zs))
+    o = (w1[..., None] * o1 + w2[..., None] * o2) / zs[..., None]
+    o = np.where(empty[..., None], 0.0, o)
+    return o, lse
+
+
+def merge_states(v, s):
+    """Fixed-order fold of ``S`` states per row: ``v [N, S, H, D]``,
+    ``s [N, S, H]`` -> ``([N, H, D], [N, H])``, combining index 0 first
+    (PR #4038, *What it does*: fp32 partials reduced in a fixed order).
+    """
+    v = np.asarray(v, dtype=np.float64)
+    s = np.asarray(s, dtype=np.float64)
+    N, S, H, D = v.shape
+    if S == 0:
+        return np.zeros((N, H, D)), np.full((N, H), NEG_INF)
+    o, l = v[:, 0], s[:, 0]
+    for j in range(1, S):
+        o, l = merge_two(o, l, v[:, j], s[:, j])
+    return o, l
+
+
+def _cascade_kv(k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len, req_group,
+                kv_indptr, kv_indices, kv_len, page_size, r, g):
+    grp = int(req_group[r])
+    parts_k, parts_v = [], []
+    if grp >= 0:
+        a, L = int(prefix_indptr[grp]), int(prefix_len[grp])
+        parts_k.append(gather_tokens(k_pool, prefix_indices, a, L, page_size, g))
+        parts_v.append(gather_tokens(v_pool, prefix_indices, a, L, page_size, g))
+    a, L = int(kv_indptr[r]), int(kv_len[r])
+    suf_k = gather_tokens(k_pool, kv_indices, a, L, page_size, g)
+    suf_v = gather_tokens(v_pool, kv_indices, a, L, page_size, g)
+    return parts_k, parts_v, suf_k, suf_v
+
+
+def cascade_flat(q, k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len, req_group,
+                 kv_indptr, kv_indices, kv_len, page_size: int, sm_scale: float,
+                 requests=None):
+    """The definition of the cascade result: decode attention of each request
+    over the concatenation (its group's shared prefix) || (its own suffix)
+    (backend-selection note, *Arithmetic intensity*: the prefix is read once and
+    reused across requests; the result is the same attention). Pinned by:
+    equality with the two-level form, and with plain decode over a flat table.
+    """
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    o = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for r in _req_list(B, requests):
+        for g in range(Hkv):
+            pk, pv, sk, sv = _cascade_kv(k_pool, v_pool, prefix_indptr, prefix_indices,
+                                         prefix_len, req_group, kv_indptr, kv_indices,
+                                         kv_len, page_size, r, g)
+            K = np.concatenate(pk + [sk]) if pk else sk
+            V = np.concatenate(pv + [sv]) if pv else sv
+            hs = _heads_of(g, G)
+            o[r, hs], lse[r, hs] = attend(q[r, hs], K, V, sm_scale)
+    return o, lse
+
+
+def cascade_two_level(q, k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len,
+                      req_group, kv_indptr, kv_indices, kv_len, page_size: int,
+                      sm_scale: float, requests=None):
+    """Two-level form: (attention over the prefix) merged with (attention over
+    the suffix), prefix first. Must equal ``cascade_flat``."""
+    B, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    o = np.full((B, Hq, D), np.nan)
+    lse = np.full((B, Hq), np.nan)
+    for r in _req_list(B, requests):
+        for g in range(Hkv):
+            pk, pv, sk, sv = _cascade_kv(k_pool, v_pool, prefix_indptr, prefix_indices,
+                                         prefix_len, req_group, kv_indptr, kv_indices,
+                                         kv_len, page_size, r, g)
+            hs = _heads_of(g, G)
+            if pk:
+                op, lp = attend(q[r, hs], pk[0], pv[0], sm_scale)
+            else:
+                op, lp = np.zeros((G, D)), np.full(G, NEG_INF)
+            os_, ls = attend(q[r, hs], sk, sv, sm_scale)
+            o[r, hs], lse[r, hs] = merge_two(op, lp, os_, ls)
+    return o, lse

@@ -1,0 +1,203 @@
+"""Reference statement of the work plan (load-balanced split of KV ranges).
+
+TEST INFRASTRUCTURE: see the package docstring for who may import this.
+
+The pages say the engine splits long KV ranges into load-balanced chunks with a
+schedule that stays valid under static graph capture (Ye et al. record,
+*summary*), and that split partials are kept in fp32 and reduced in a fixed
+order (PR #4038, *What it does*). They give no algorithm, so the rule below is
+a reading, restated here in plain Python so that the library's C++ planner can
+be compared with it element for element:
+
+1. Work units. Each request's query rows (query token i, head h of kv head g:
+   row = i*G + h) are cut into blocks of ``rows_per_block`` rows. A unit is
+   (request, block, kv head), enumerated in that nesting order. For the
+   cascade prefix level a unit is (group, block, kv head) over the rows of the
+   group's member requests (ascending request index).
+2. Key range. A unit sees tokens [0, t_lim): t_lim = kv_len, or under the
+   causal mask min(kv_len, kv_len - qo + i_last + 1) with i_last the last
+   query token in the block. It spans n = ceil(t_lim / ps) pages.
+3. Chunk size. Deterministic mode: c = det_chunk_pages, a constant, so chunk
+   boundaries depend on the request alone. Balanced mode: c = max(1,
+   min_chunk_pages, ceil(W / S)) with W the level's total unit pages and S the
+   number of persistent workers.
+4. Chunks. k = ceil(n / c) chunks; chunk j covers pages
+   [floor(j*n/k), floor((j+1)*n/k)).
+5. Outputs. A unit with k == 1 writes its final rows directly; k > 1 writes
+   fp32 partial rows (allocated in enumeration order) that a merge folds in
+   chunk order. Cascade writes partials for everything and merges the prefix
+   chunk(s) first, then the suffix chunks.
+6. Placement. Longest-processing-time-first (Graham): items sorted by
+   (cost descending, enumeration index), cost = pages + 1, each given to the
+   worker with the smallest load, ties to the lowest worker index. A worker
+   runs its items in the order they were given to it.
+"""
+
+from __future__ import annotations
+
+import heapq
+
+FLAG_LIST_Q = 1     # query rows come from the member list (cascade prefix)
+FLAG_PARTIAL = 2    # write fp32 partial rows instead of final rows
+FLAG_CAUSAL = 4     # bottom-right causal mask
+FLAG_PREFIX = 8     # page list is the shared-prefix table
+
+ITEM_FIELDS = ("q_base", "row0", "n_rows", "kv_head", "page_off", "flags",
+               "t_begin", "t_end", "q_pos0", "dst", "unit", "chunk")
+
+
+def _ceil_div(a, b):
+    return -(-a // b)
+
+
+def _chunk_size(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages):
+    if deterministic:
+        return max(1, int(det_chunk_pages))
+    W = sum(u["n_pages"] for u in units)
+    return max(1, int(min_chunk_pages), _ceil_div(W, num_workers))
+
+
+def _lpt(items, num_workers):
+    order = sorted(range(len(items)),
+                   key=lambda i: (-(items[i]["t_pages"] + 1), i))
+    heap = [(0, w) for w in range(num_workers)]
+    per_worker = [[] for _ in range(num_workers)]
+    for i in order:
+        load, w = heapq.heappop(heap)
+        per_worker[w].append(i)
+        heapq.heappush(heap, (load + items[i]["t_pages"] + 1, w))
+    flat, indptr = [], [0]
+    for w in range(num_workers):
+        flat.extend(per_worker[w])
+        indptr.append(len(flat))
+    return flat, indptr
+
+
+def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
+             num_workers, rows_per_block, deterministic=False, det_chunk_pages=64,
+             min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
+             prefix_len=None, req_group=None):
+    """Return the plan as plain lists.
+
+    ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
+    with one entry per level (cascade: [prefix, suffix]; otherwise one).
+    Result: ``{"levels": [{"items": [...12-tuples...], "worker_indptr": [...]}],
+    "merges": [(q_tok, head0, n_heads, parts_off, n_parts)], "parts": [...],
+    "qlist": [...], "n_part_rows": int}``.
+    """
+    B = len(kv_len)
+    G = num_qo_heads // num_kv_heads
+    ps = page_size
+    kv_len = [int(x) for x in kv_len]
+    kv_indptr = [int(x) for x in kv_indptr]
+
+    def request_units(rpb, qo_of, qtok_of, is_causal):
+        units = []
+        for r in range(B):
+            nq, L = qo_of(r), kv_len[r]
+            rows = nq * G
+            for b in range(_ceil_div(rows, rpb)):
+                r0, r1 = b * rpb, min(rows, (b + 1) * rpb)
+                i_last = (r1 - 1) // G
+                t_lim = min(L, L - nq + i_last + 1) if is_causal else L
+                for g in range(num_kv_heads):
+                    units.append(dict(unit=r, q_base=qtok_of(r), row0=r0, n_rows=r1 - r0,
+                                      g=g, page_off=kv_indptr[r], t_lim=t_lim,
+                                      n_pages=_ceil_div(t_lim, ps),
+                                      q_pos0=(L - nq) if is_causal else 0,
+                                      flags=FLAG_CAUSAL if is_causal else 0, nq=nq))
+        return units
+
+    qlist = []
+    levels_units = []
+    if kind == "cascade":
+        NG = len(prefix_len)
+        pu = []
+        rpb = rows_per_block[0]
+        for grp in range(NG):
+            members = [r for r in range(B) if int(req_group[r]) == grp]
+            PL = int(prefix_len[grp])
+            if not members or PL == 0:
+                continue
+            off = len(qlist)
+            qlist.extend(members)
+            rows = len(members) * G
+            for b in range(_ceil_div(rows, rpb)):
+                r0, r1 = b * rpb, min(rows, (b + 1) * rpb)
+                for g in range(num_kv_heads):
+                    pu.append(dict(unit=grp, q_base=off, row0=r0, n_rows=r1 - r0, g=g,
+                                   page_off=int(prefix_indptr[grp]), t_lim=PL,
+                                   n_pages=_ceil_div(PL, ps), q_pos0=0,
+                                   flags=FLAG_LIST_Q | FLAG_PREFIX, nq=None))
+        levels_units.append(pu)
+        levels_units.append(request_units(rows_per_block[1], lambda r: 1, lambda r: r, False))
+    elif kind == "append":
+        qo = [int(qo_indptr[r + 1]) - int(qo_indptr[r]) for r in range(B)]
+        levels_units.append(request_units(rows_per_block[0], lambda r: qo[r],
+                                          lambda r: int(qo_indptr[r]), bool(causal)))
+    else:
+        levels_units.append(request_units(rows_per_block[0], lambda r: 1, lambda r: r, False))
+
+    all_partial = kind == "cascade"
+    next_row = 0
+    levels = []
+    unit_chunks = []    # per level: per unit list of (dst_row) for partial chunks, or "final"
+    for units in levels_units:
+        c = _chunk_size(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages)
+        items = []
+        chunks_of = []
+        for u in units:
+            n = u["n_pages"]
+            k = _ceil_div(n, c) if n > 0 else 0
+            partial = all_partial or k > 1
+            dsts = []
+            for j in range(k):
+                p0, p1 = (j * n) // k, ((j + 1) * n) // k
+                dst = -1
+                if partial:
+                    dst = next_row
+                    next_row += u["n_rows"]
+                    dsts.append(dst)
+                items.append(dict(
+                    q_base=u["q_base"], row0=u["row0"], n_rows=u["n_rows"], kv_head=u["g"],
+                    page_off=u["page_off"], flags=u["flags"] | (FLAG_PARTIAL if partial else 0),
+                    t_begin=p0 * ps, t_end=min(p1 * ps, u["t_lim"]), q_pos0=u["q_pos0"],
+                    dst=dst, unit=u["unit"], chunk=j, t_pages=p1 - p0))
+            chunks_of.append((k, dsts))
+        order, indptr = _lpt(items, num_workers)
+        levels.append(dict(items=[tuple(items[i][f] for f in ITEM_FIELDS) for i in order],
+                           worker_indptr=indptr))
+        unit_chunks.append(chunks_of)
+
+    merges, parts = [], []
+    if kind == "cascade":
+        pu, su = levels_units
+        pchunks, schunks = unit_chunks
+        # prefix partial row of (request r, kv head g): find r's unit and local row
+        pref = {}
+        for ui, u in enumerate(pu):
+            k, dsts = pchunks[ui]
+            members = qlist[u["q_base"]:]
+            for local in range(0, u["n_rows"], G):
+                r = members[(u["row0"] + local) // G]
+                pref[(r, u["g"])] = [d + local for d in dsts]
+        for ui, u in enumerate(su):
+            r, g = u["unit"], u["g"]
+            k, dsts = schunks[ui]
+            plist = pref.get((r, g), []) + list(dsts)
+            merges.append((r, g * G, G, len(parts), len(plist)))
+            parts.extend(plist)
+    else:
+        units, (chunks_of) = levels_units[0], unit_chunks[0]
+        for ui, u in enumerate(units):
+            k, dsts = chunks_of[ui]
+            if k == 1:
+                continue
+            r0, r1 = u["row0"], u["row0"] + u["n_rows"]
+            for i in range(r0 // G, (r1 - 1) // G + 1):
+                a, b = max(r0, i * G), min(r1, (i + 1) * G)
+                plist = [d + (a - r0) for d in dsts]
+                merges.append((u["q_base"] + i, u["g"] * G + (a - i * G), b - a,
+                               len(parts), len(plist)))
+                parts.extend(plist)
+    return dict(levels=levels, merges=merges, parts=parts, qlist=qlist, n_part_rows=next_row)

@@ -1,0 +1,457 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself.
+
+* torch's scaled_dot_product_attention (float64, CPU) on dense K/V that the
+  test itself scatters into a randomly permuted page pool (pins the gather,
+  the head grouping, the scale, the softmax and the causal alignment);
+* closed forms (one key, equal logits, two keys, constant V, needle);
+* invariants (pool permutation, page size, split + merge, cascade == flat,
+  append with one query == decode);
+* mutation checks: mistakes planted in the oracle (on the CPU) must fail at
+  least one pin.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import attention as A
+
+RNG = np.random.default_rng(20241203)
+
+
+# ---------------------------------------------------------------------------
+# helpers that build paged inputs from dense ones (independent of the oracle)
+
+
+def paginate(dense_list, page_size, rng, slack_pages=3, fill=np.nan):
+    """dense_list[r] is [Hkv, L_r, D]; returns (pool, indptr, indices, lens)
+    with pages placed at random pool slots and unused slots set to ``fill``."""
+    Hkv, D = dense_list[0].shape[0], dense_list[0].shape[2]
+    counts = [-(-d.shape[1] // page_size) for d in dense_list]
+    total = sum(counts)
+    P = total + slack_pages
+    perm = rng.permutation(P)
+    pool = np.full((P, Hkv, page_size, D), fill)
+    indptr = np.zeros(len(dense_list) + 1, dtype=np.int64)
+    indices = np.zeros(total, dtype=np.int64)
+    pos = 0
+    for r, d in enumerate(dense_list):
+        L = d.shape[1]
+        for p in range(counts[r]):
+            page = perm[pos]
+            indices[pos] = page
+            for s in range(page_size):
+                t = p * page_size + s
+                if t < L:
+                    pool[page, :, s, :] = d[:, t, :]
+            pos += 1
+        indptr[r + 1] = pos
+    return pool, indptr, indices, np.array([d.shape[1] for d in dense_list])
+
+
+def sdpa(q, k, v, scale, mask=None):
+    """torch SDPA on float64 CPU tensors: q [n, D], k/v [L, D]."""
+    qt = torch.from_numpy(np.ascontiguousarray(q))[None, None]
+    kt = torch.from_numpy(np.ascontiguousarray(k))[None, None]
+    vt = torch.from_numpy(np.ascontiguousarray(v))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    return out[0, 0].numpy()
+
+
+def decode_case(B, Hq, Hkv, D, ps, lens, rng):
+    dense_k = [rng.standard_normal((Hkv, L, D)) for L in lens]
+    dense_v = [rng.standard_normal((Hkv, L, D)) for L in lens]
+    kp, indptr, indices, L = paginate(dense_k, ps, rng)
+    vp = np.full_like(kp, np.nan)
+    # same page placement for V: copy through the same table
+    for r, dv in enumerate(dense_v):
+        for t in range(dv.shape[1]):
+            vp[indices[indptr[r] + t // ps], :, t % ps, :] = dv[:, t, :]
+    q = rng.standard_normal((B, Hq, D))
+    return q, dense_k, dense_v, kp, vp, indptr, indices, L
+
+
+# ---------------------------------------------------------------------------
+# pins against torch SDPA
+
+
+def check_decode_vs_sdpa(ps, D, Hq=8, Hkv=2, lens=(1, 7, 33, 40), seed=1):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    q, dk, dv, kp, vp, indptr, indices, L = decode_case(B, Hq, Hkv, D, ps, lens, rng)
+    scale = 1.0 / math.sqrt(D)
+    o, lse = A.paged_decode(q, kp, vp, indptr, indices, L, ps, scale)
+    G = Hq // Hkv
+    for r in range(B):
+        for h in range(Hq):
+            ref = sdpa(q[r, h][None], dk[r][h // G], dv[r][h // G], scale)[0]
+            np.testing.assert_allclose(o[r, h], ref, rtol=0, atol=1e-12)
+            # lse: log of the SDPA normaliser, via scipy's logsumexp on the dense logits
+            from scipy.special import logsumexp
+            s = scale * dk[r][h // G] @ q[r, h]
+            assert abs(lse[r, h] - logsumexp(s)) <= 1e-12 * max(1.0, abs(lse[r, h]))
+
+
+@pytest.mark.parametrize("ps", [1, 16, 64])
+@pytest.mark.parametrize("D", [4, 64])
+def test_decode_matches_sdpa(ps, D):
+    check_decode_vs_sdpa(ps, D)
+
+
+def check_append_vs_sdpa(ps=16, D=8, Hq=4, Hkv=2, prefixes=(5, 30), qos=(3, 17), seed=2):
+    rng = np.random.default_rng(seed)
+    G = Hq // Hkv
+    lens = [p + n for p, n in zip(prefixes, qos)]
+    _, dk, dv, kp, vp, indptr, indices, L = decode_case(len(lens), Hq, Hkv, D, ps, lens, rng)
+    qo_indptr = np.concatenate([[0], np.cumsum(qos)])
+    q = rng.standard_normal((int(qo_indptr[-1]), Hq, D))
+    scale = 0.3
+    o, lse = A.paged_append(q, qo_indptr, kp, vp, indptr, indices, L, ps, scale, causal=True)
+    for r, (P, n) in enumerate(zip(prefixes, qos)):
+        Lr = P + n
+        mask = np.arange(Lr)[None, :] <= (P + np.arange(n))[:, None]   # bottom-right
+        for h in range(Hq):
+            ref = sdpa(q[qo_indptr[r]:qo_indptr[r + 1], h], dk[r][h // G], dv[r][h // G],
+                       scale, mask)
+            np.testing.assert_allclose(o[qo_indptr[r]:qo_indptr[r + 1], h], ref,
+                                       rtol=0, atol=1e-12)
+
+
+def test_append_matches_sdpa_bottom_right_causal():
+    check_append_vs_sdpa()
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+
+
+def test_single_key():
+    q = RNG.standard_normal((3, 16))
+    k = RNG.standard_normal((1, 16))
+    v = RNG.standard_normal((1, 16))
+    o, lse = A.attend(q, k, v, 0.25)
+    np.testing.assert_array_equal(o, np.repeat(v, 3, axis=0))
+    np.testing.assert_allclose(lse, 0.25 * (q @ k[0]), rtol=0, atol=1e-15)
+
+
+def test_equal_logits_mean_and_log_count():
+    L = 37
+    k = np.tile(RNG.standard_normal((1, 8)), (L, 1))
+    v = RNG.standard_normal((L, 8))
+    q = RNG.standard_normal((2, 8))
+    o, lse = A.attend(q, k, v, 0.5)
+    np.testing.assert_allclose(o, np.repeat(v.mean(0, keepdims=True), 2, 0), atol=1e-14)
+    np.testing.assert_allclose(lse, 0.5 * (q @ k[0]) + math.log(L), atol=1e-13)
+    o0, lse0 = A.attend(np.zeros((1, 8)), RNG.standard_normal((L, 8)), v, 1.0)
+    np.testing.assert_allclose(lse0, [math.log(L)], atol=1e-14)
+
+
+def test_constant_values():
+    v = np.full((50, 4), 2.5)
+    o, _ = A.attend(RNG.standard_normal((3, 4)), RNG.standard_normal((50, 4)), v, 1.0)
+    np.testing.assert_allclose(o, 2.5, atol=1e-14)
+
+
+def test_two_keys_closed_form():
+    q = np.array([[1.0, -2.0]])
+    k = np.array([[0.5, 1.0], [2.0, 0.25]])
+    v = np.array([[1.0, 3.0], [-4.0, 0.5]])
+    sc = 0.7
+    s0 = sc * (1.0 * 0.5 + -2.0 * 1.0)
+    s1 = sc * (1.0 * 2.0 + -2.0 * 0.25)
+    lse = math.log(math.exp(s0) + math.exp(s1))
+    a = 1.0 / (1.0 + math.exp(s1 - s0))   # sigma(s0 - s1)
+    o_ref = [a * 1.0 + (1 - a) * -4.0, a * 3.0 + (1 - a) * 0.5]
+    o, l = A.attend(q, k, v, sc)
+    assert abs(l[0] - lse) < 1e-15
+    np.testing.assert_allclose(o[0], o_ref, atol=1e-15)
+
+
+@pytest.mark.parametrize("t_star", [0, 15, 16, 17, 63, 64, 99])
+def test_needle_across_page_boundaries(t_star):
+    """One key with a logit 60+ above all others: o is that key's value row."""
+    ps, D, L = 16, 32, 100
+    rng = np.random.default_rng(t_star)
+    k = rng.standard_normal((1, L, D)) * 0.01
+    q = np.zeros((1, 1, D))
+    q[0, 0, 0] = 1.0
+    k[0, t_star, 0] = 100.0
+    v = rng.standard_normal((1, L, D))
+    kp, indptr, indices, Ls = paginate([k], ps, np.random.default_rng(t_star + 1))
+    vp, _, _, _ = paginate([v], ps, np.random.default_rng(t_star + 1))  # same seed -> same perm
+    assert np.array_equal(np.isnan(kp), np.isnan(vp))
+    o, lse = A.paged_decode(q, kp, vp, indptr, indices, Ls, ps, 1.0)
+    np.testing.assert_allclose(o[0, 0], v[0, t_star], rtol=1e-20, atol=1e-20)
+    assert abs(lse[0, 0] - 100.0) < 1e-20 + 1e-15 * 100
+
+
+def test_empty_sequence_is_zero_and_neg_inf():
+    o, lse = A.attend(np.ones((2, 4)), np.zeros((0, 4)), np.zeros((0, 4)), 1.0)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+    vis = np.zeros((2, 3), dtype=bool)
+    o, lse = A.attend(np.ones((2, 4)), np.ones((3, 4)), np.ones((3, 4)), 1.0, vis)
+    assert np.all(o == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+
+
+def test_pool_permutation_is_bit_identical():
+    rng = np.random.default_rng(5)
+    q, dk, dv, kp, vp, indptr, indices, L = decode_case(3, 4, 2, 16, 8, [9, 40, 23], rng)
+    o1, l1 = A.paged_decode(q, kp, vp, indptr, indices, L, 8, 0.25)
+    P = kp.shape[0]
+    perm = rng.permutation(P)            # page p moves to slot perm[p]
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    o2, l2 = A.paged_decode(q, kp2, vp2, indptr, perm[indices], L, 8, 0.25)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_page_size_is_bit_identical():
+    rng = np.random.default_rng(6)
+    lens = [1, 16, 65, 200]
+    dk = [rng.standard_normal((2, L, 16)) for L in lens]
+    dv = [rng.standard_normal((2, L, 16)) for L in lens]
+    q = rng.standard_normal((4, 8, 16))
+    outs = []
+    for ps in (1, 16, 64):
+        kp, ip, ix, L = paginate(dk, ps, np.random.default_rng(ps))
+        vp, _, _, _ = paginate(dv, ps, np.random.default_rng(ps))
+        outs.append(A.paged_decode(q, kp, vp, ip, ix, L, ps, 0.25))
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
+
+
+@pytest.mark.parametrize("cuts", [[5], [1, 2, 3], [10, 11, 50, 90], [0, 0, 40]])
+def test_split_and_merge_equals_whole(cuts):
+    rng = np.random.default_rng(len(cuts))
+    L = 100
+    q = rng.standard_normal((4, 32))
+    k = rng.standard_normal((L, 32))
+    v = rng.standard_normal((L, 32))
+    o_full, l_full = A.attend(q, k, v, 0.2)
+    bounds = [0] + sorted(cuts) + [L]
+    states = [A.attend(q, k[a:b], v[a:b], 0.2) for a, b in zip(bounds[:-1], bounds[1:])]
+    vs = np.stack([s[0] for s in states], axis=1)[:, :, None, :]     # [N=4, S, H=1, D]
+    ss = np.stack([s[1] for s in states], axis=1)[:, :, None]
+    o, l = A.merge_states(vs, ss)
+    np.testing.assert_allclose(o[:, 0], o_full, atol=1e-12)
+    np.testing.assert_allclose(l[:, 0], l_full, atol=1e-12)
+
+
+def test_merge_algebra():
+    rng = np.random.default_rng(7)
+    o = rng.standard_normal((3, 5, 8))
+    lse = rng.standard_normal((3, 5)) * 3
+    a, b, c = [(o[i], lse[i]) for i in range(3)]
+    ab = A.merge_two(*a, *b)
+    ba = A.merge_two(*b, *a)
+    np.testing.assert_allclose(ab[0], ba[0], atol=1e-14)
+    np.testing.assert_allclose(ab[1], ba[1], atol=1e-14)
+    l_ = A.merge_two(*A.merge_two(*a, *b), *c)
+    r_ = A.merge_two(*a, *A.merge_two(*b, *c))
+    np.testing.assert_allclose(l_[0], r_[0], atol=1e-13)
+    np.testing.assert_allclose(l_[1], r_[1], atol=1e-13)
+    empty = (np.zeros_like(o[0]), np.full(5, -np.inf))
+    ident = A.merge_two(*a, *empty)
+    np.testing.assert_array_equal(ident[1], a[1])
+    np.testing.assert_allclose(ident[0], a[0], atol=1e-15)
+    both = A.merge_two(*empty, *empty)
+    assert np.all(both[0] == 0) and np.all(both[1] == -np.inf)
+
+
+def test_cascade_flat_equals_two_level_and_flat_decode():
+    rng = np.random.default_rng(8)
+    ps, Hq, Hkv, D = 8, 4, 2, 16
+    pref_lens = [32, 24]
+    suf_lens = [5, 0, 17, 9, 30]
+    groups = [0, 0, 1, -1, 0]
+    dense_pref_k = [rng.standard_normal((Hkv, L, D)) for L in pref_lens]
+    dense_pref_v = [rng.standard_normal((Hkv, L, D)) for L in pref_lens]
+    dense_suf_k = [rng.standard_normal((Hkv, L, D)) for L in suf_lens]
+    dense_suf_v = [rng.standard_normal((Hkv, L, D)) for L in suf_lens]
+    allk = dense_pref_k + dense_suf_k
+    allv = dense_pref_v + dense_suf_v
+    kp, ip, ix, _ = paginate(allk, ps, np.random.default_rng(1))
+    vp, _, _, _ = paginate(allv, ps, np.random.default_rng(1))
+    npf = len(pref_lens)
+    prefix_indptr = ip[:npf + 1]
+    prefix_indices = ix
+    kv_indptr = ip[npf:] - 0
+    q = rng.standard_normal((len(suf_lens), Hq, D))
+    args = (q, kp, vp, prefix_indptr, prefix_indices, np.array(pref_lens), np.array(groups),
+            kv_indptr, ix, np.array(suf_lens), ps, 0.25)
+    of, lf = A.cascade_flat(*args)
+    o2, l2 = A.cascade_two_level(*args)
+    np.testing.assert_allclose(of, o2, atol=1e-12)
+    np.testing.assert_allclose(lf, l2, atol=1e-12)
+    # flat page tables (prefixes are page aligned) through plain decode
+    fl_indptr, fl_idx, fl_len = [0], [], []
+    for r, g in enumerate(groups):
+        pages = []
+        L = suf_lens[r]
+        if g >= 0:
+            pages += list(ix[prefix_indptr[g]:prefix_indptr[g + 1]])
+            L += pref_lens[g]
+        pages += list(ix[kv_indptr[r]:kv_indptr[r + 1]])
+        fl_idx += pages
+        fl_indptr.append(len(fl_idx))
+        fl_len.append(L)
+    od, ld = A.paged_decode(q, kp, vp, np.array(fl_indptr), np.array(fl_idx), np.array(fl_len),
+                            ps, 0.25)
+    assert np.array_equal(od, of) and np.array_equal(ld, lf)
+
+
+def test_append_single_query_equals_decode():
+    rng = np.random.default_rng(9)
+    q, dk, dv, kp, vp, indptr, indices, L = decode_case(3, 8, 2, 16, 16, [3, 40, 77], rng)
+    od, ld = A.paged_decode(q, kp, vp, indptr, indices, L, 16, 0.25)
+    oa, la = A.paged_append(q, np.arange(4), kp, vp, indptr, indices, L, 16, 0.25, causal=True)
+    np.testing.assert_allclose(oa, od, atol=1e-15)
+    np.testing.assert_allclose(la, ld, atol=1e-15)
+
+
+def test_causal_horizon_needle():
+    """A dominant key at position p is seen by exactly the queries whose
+    position is >= p (bottom-right alignment)."""
+    ps, D = 4, 8
+    P, n = 10, 6
+    L = P + n
+    rng = np.random.default_rng(10)
+    for p_needle in (P - 1, P, P + 2, L - 1):
+        k = rng.standard_normal((1, L, D)) * 0.01
+        k[0, p_needle, 0] = 80.0
+        v = rng.standard_normal((1, L, D))
+        kp, ip, ix, Ls = paginate([k], ps, np.random.default_rng(3))
+        vp, _, _, _ = paginate([v], ps, np.random.default_rng(3))
+        q = np.zeros((n, 1, D))
+        q[:, 0, 0] = 1.0
+        o, _ = A.paged_append(q, np.array([0, n]), kp, vp, ip, ix, Ls, ps, 1.0, causal=True)
+        for i in range(n):
+            sees = P + i >= p_needle
+            hit = np.allclose(o[i, 0], v[0, p_needle], atol=1e-20)
+            assert hit == sees, (p_needle, i)
+
+
+def test_scatter_writes_only_new_slots():
+    rng = np.random.default_rng(11)
+    ps, Hkv, D = 4, 2, 8
+    lens = np.array([7, 12])
+    qo = np.array([3, 5])
+    indptr = np.array([0, 2, 5])
+    indices = np.array([4, 0, 2, 6, 1])
+    pool = rng.standard_normal((8, Hkv, ps, D))
+    pool_v = rng.standard_normal((8, Hkv, ps, D))
+    qo_indptr = np.array([0, 3, 8])
+    k_new = rng.standard_normal((8, Hkv, D))
+    v_new = rng.standard_normal((8, Hkv, D))
+    k2, v2 = A.scatter_new_kv(pool, pool_v, k_new, v_new, qo_indptr, indptr, indices, lens, ps)
+    touched = np.zeros((8, ps), dtype=bool)
+    # request 0: positions 4,5,6 -> page indices[0 + 1] = 0, slots 0,1,2
+    for pos, tok in zip([4, 5, 6], [0, 1, 2]):
+        pg = indices[0 + pos // ps]
+        np.testing.assert_array_equal(k2[pg, :, pos % ps], k_new[tok])
+        np.testing.assert_array_equal(v2[pg, :, pos % ps], v_new[tok])
+        touched[pg, pos % ps] = True
+    # request 1: positions 7..11 -> pages indices[2 + pos//4]
+    for pos, tok in zip(range(7, 12), range(3, 8)):
+        pg = indices[2 + pos // ps]
+        np.testing.assert_array_equal(k2[pg, :, pos % ps], k_new[tok])
+        touched[pg, pos % ps] = True
+    keep = ~touched
+    np.testing.assert_array_equal(k2.transpose(0, 2, 1, 3)[keep], pool.transpose(0, 2, 1, 3)[keep])
+    np.testing.assert_array_equal(v2.transpose(0, 2, 1, 3)[keep], pool_v.transpose(0, 2, 1, 3)[keep])
+
+
+# ---------------------------------------------------------------------------
+# mutation checks: plausible mistakes planted in the oracle must fail a pin
+
+
+def _mut_gather_reverse_pages(pool, indices, start, length, page_size, kv_head):
+    d = pool.shape[-1]
+    if length <= 0:
+        return np.zeros((0, d))
+    n = -(-length // page_size)
+    pages = np.asarray(indices[start:start + n])[::-1]
+    return np.asarray(pool[pages, kv_head], np.float64).reshape(-1, d)[:length]
+
+
+def _mut_gather_wrong_head(pool, indices, start, length, page_size, kv_head):
+    return _ORIG["gather_tokens"](pool, indices, start, length, page_size,
+                                  (kv_head + 1) % pool.shape[1])
+
+
+def _mut_attend_no_scale(q, k, v, sm_scale, visible=None):
+    return _ORIG["attend"](q, k, v, 1.0, visible)
+
+
+def _mut_attend_log2(q, k, v, sm_scale, visible=None):
+    o, l = _ORIG["attend"](q, k, v, sm_scale, visible)
+    return o, l / math.log(2.0)
+
+
+def _mut_attend_transposed_v(q, k, v, sm_scale, visible=None):
+    o, l = _ORIG["attend"](q, k, v[::-1], sm_scale, visible)
+    return o, l
+
+
+def _mut_merge_sign(o1, l1, o2, l2):
+    o, l = _ORIG["merge_two"](o1, l1, o2, -np.asarray(l2))
+    return o, l
+
+
+_ORIG = {n: getattr(A, n) for n in ("gather_tokens", "attend", "merge_two", "paged_append")}
+
+
+def _mut_append_top_left(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
+                         page_size, sm_scale, causal=True, requests=None):
+    # top-left alignment: query i sees keys 0..i (a classic mistake)
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    o = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    for r in range(len(kv_len)):
+        q0, q1 = int(qo_indptr[r]), int(qo_indptr[r + 1])
+        for g in range(Hkv):
+            K = A.gather_tokens(k_pool, kv_indices, int(kv_indptr[r]), int(kv_len[r]), page_size, g)
+            V = A.gather_tokens(v_pool, kv_indices, int(kv_indptr[r]), int(kv_len[r]), page_size, g)
+            for i in range(q1 - q0):
+                hs = slice(g * G, (g + 1) * G)
+                o[q0 + i, hs], lse[q0 + i, hs] = A.attend(q[q0 + i, hs], K[:i + 1], V[:i + 1],
+                                                          sm_scale)
+    return o, lse
+
+
+MUTATIONS = {
+    "gather_reverse_pages": ("gather_tokens", _mut_gather_reverse_pages,
+                             lambda: check_decode_vs_sdpa(16, 4)),
+    "gather_wrong_head": ("gather_tokens", _mut_gather_wrong_head,
+                          lambda: check_decode_vs_sdpa(16, 4)),
+    "attend_no_scale": ("attend", _mut_attend_no_scale, lambda: check_decode_vs_sdpa(16, 4)),
+    "attend_lse_log2": ("attend", _mut_attend_log2, test_two_keys_closed_form),
+    "attend_transposed_v": ("attend", _mut_attend_transposed_v, test_two_keys_closed_form),
+    "merge_sign": ("merge_two", _mut_merge_sign, lambda: test_split_and_merge_equals_whole([5])),
+    "append_top_left": ("paged_append", _mut_append_top_left, check_append_vs_sdpa),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name, monkeypatch):
+    attr, fn, pin = MUTATIONS[name]
+    pin()                                   # passes on the real oracle
+    monkeypatch.setattr(A, attr, fn)
+    with pytest.raises(AssertionError):
+        pin()
+
+
+def test_oracle_exports():
+    for n in ("attend", "paged_decode", "paged_append", "merge_states", "cascade_flat",
+              "plan_ref"):
+        assert hasattr(oracle, n)

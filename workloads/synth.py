@@ -1,0 +1,321 @@
+"""Seeded synthetic paged-KV workloads.
+
+Every tensor is drawn from a CPU ``torch.Generator`` so that the same seed gives
+the same bits on any machine. Draw order is fixed: lengths, forced positions,
+page permutation, q, K pool, V pool, k_new, v_new.
+
+Layouts (the ones the library's C ABI takes):
+
+* ``q``            bf16 ``[T, Hq, D]``   (decode and cascade: T = batch)
+* ``k_cache``      bf16 ``[P, Hkv, ps, D]`` ("HND": one (page, kv head) tile is
+  contiguous); ``v_cache`` the same
+* ``kv_indptr``    int32 ``[B+1]``  page offsets into ``kv_indices``
+* ``kv_indices``   int32 ``[nnz]``  page ids into the pool
+* ``kv_len``       int32 ``[B]``    tokens per request
+* ``qo_indptr``    int32 ``[B+1]``  (append) query-token offsets into ``q``
+* ``k_new/v_new``  bf16 ``[sum(qo), Hkv, D]`` (append) keys/values of the new tokens
+* cascade: ``prefix_indptr [G+1]``, ``prefix_indices``, ``prefix_len [G]``,
+  ``req_prefix_group [B]`` (-1 = no shared prefix); ``kv_*`` then describe the
+  per-request suffixes.
+
+Token ``t`` of a sequence sits in page ``indices[indptr[r] + t // ps]`` at slot
+``t % ps``. With ``poison=True`` the pages no request uses are NaN, the slots
+past a request's length in its last page hold 1e4, and (append) the slots the
+new tokens will occupy hold NaN until the kernel scatters them: a kernel that
+reads a byte it should not shows up in the output.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, fields
+from typing import Optional, Sequence
+
+import torch
+
+BASE_SEED = 1234
+POOL_SLACK = 0.125        # pool holds 12.5% more pages than the batch uses
+TAIL_POISON = 1.0e4       # finite poison for slots past a sequence's end
+_GEN_CHUNK_PAGES = 2048   # pool pages drawn per randn call (bounds host memory)
+
+CONFIG_NAMES = (
+    "tiny_decode",            # B=4, 8/2 heads, D=64, ps=16, L~U[37,300]
+    "llama3_8b_decode",       # B=64, 32/8 heads, D=128, ps=16, L~U[512,4096]
+    "skewed_decode",          # B=128, lognormal(median 1024, sigma 1) + 4 x 32768
+    "cascade_shared_prefix",  # 64 x (8192 shared + U[256,1024] own)
+    "mixed_append",           # 16 x (U[1024,8192] prefix + U[1,128] new, causal)
+)
+
+
+def fp32_scale(head_dim: int) -> float:
+    """1/sqrt(head_dim) rounded to fp32, returned as the exact Python float."""
+    return float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32).item())
+
+
+@dataclass
+class Workload:
+    name: str
+    kind: str                      # "decode" | "append" | "cascade"
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    sm_scale: float
+    seed: int
+    kv_len: torch.Tensor
+    kv_indptr: torch.Tensor
+    kv_indices: torch.Tensor
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    causal: bool = False
+    qo_indptr: Optional[torch.Tensor] = None
+    k_new: Optional[torch.Tensor] = None
+    v_new: Optional[torch.Tensor] = None
+    prefix_indptr: Optional[torch.Tensor] = None
+    prefix_indices: Optional[torch.Tensor] = None
+    prefix_len: Optional[torch.Tensor] = None
+    req_prefix_group: Optional[torch.Tensor] = None
+
+    @property
+    def batch(self) -> int:
+        return int(self.kv_len.numel())
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    def to(self, device) -> "Workload":
+        """Copy with every tensor moved to ``device``."""
+        kw = {}
+        for f in fields(self):
+            v = getattr(self, f.name)
+            if isinstance(v, torch.Tensor):
+                v = v.to(device)
+            kw[f.name] = v
+        return Workload(**kw)
+
+    def kv_bytes(self) -> int:
+        """Algorithmic K+V bytes one pass reads: exactly kv_len tokens per
+        request per kv head (a shared prefix counted once)."""
+        per_tok = self.num_kv_heads * self.head_dim * 2 * 2
+        toks = int(self.kv_len.sum())
+        if self.prefix_len is not None:
+            toks += int(self.prefix_len.sum())
+        return toks * per_tok
+
+
+# --------------------------------------------------------------------------
+# building blocks
+
+
+def _pages_for(lengths: torch.Tensor, ps: int) -> torch.Tensor:
+    return (lengths + ps - 1) // ps
+
+
+def _indptr(counts: torch.Tensor) -> torch.Tensor:
+    out = torch.zeros(counts.numel() + 1, dtype=torch.int64)
+    out[1:] = torch.cumsum(counts.to(torch.int64), 0)
+    return out.to(torch.int32)
+
+
+def _randn_bf16(gen: torch.Generator, shape) -> torch.Tensor:
+    return torch.randn(shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+
+
+def _randn_pool(gen, n_pages, hkv, ps, d) -> torch.Tensor:
+    out = torch.empty((n_pages, hkv, ps, d), dtype=torch.bfloat16)
+    for p0 in range(0, n_pages, _GEN_CHUNK_PAGES):
+        p1 = min(n_pages, p0 + _GEN_CHUNK_PAGES)
+        out[p0:p1] = _randn_bf16(gen, (p1 - p0, hkv, ps, d))
+    return out
+
+
+def _pool_size(used_pages: int) -> int:
+    return max(1, int(math.ceil(used_pages * (1.0 + POOL_SLACK))))
+
+
+def _poison_pool(pool: torch.Tensor, used: torch.Tensor, tables) -> None:
+    """NaN in unused pages; TAIL_POISON in slots past each sequence's end.
+    ``tables`` is a list of (indices, start, length) for every sequence."""
+    ps = pool.shape[2]
+    mask = torch.ones(pool.shape[0], dtype=torch.bool)
+    mask[used.to(torch.int64)] = False
+    pool[mask] = float("nan")
+    for indices, start, length in tables:
+        if length % ps:
+            last = int(indices[start + (length - 1) // ps])
+            pool[last, :, length % ps:, :] = TAIL_POISON
+
+
+def _lengths_uniform(gen, n, lo, hi) -> torch.Tensor:
+    return torch.randint(lo, hi + 1, (n,), generator=gen, dtype=torch.int64)
+
+
+# --------------------------------------------------------------------------
+# public constructors
+
+
+def make_decode(lengths: Sequence[int], num_qo_heads: int, num_kv_heads: int,
+                head_dim: int, page_size: int, seed: int, poison: bool = True,
+                name: str = "decode", _gen: Optional[torch.Generator] = None) -> Workload:
+    """One query token per request, attending to ``lengths[r]`` cached tokens."""
+    gen = _gen if _gen is not None else torch.Generator().manual_seed(seed)
+    L = torch.as_tensor(list(lengths) if not isinstance(lengths, torch.Tensor) else lengths,
+                        dtype=torch.int64)
+    n = _pages_for(L, page_size)
+    total = int(n.sum())
+    pool = _pool_size(total)
+    perm = torch.randperm(pool, generator=gen).to(torch.int32)
+    indptr = _indptr(n)
+    indices = perm[:total].clone()
+    B = L.numel()
+    q = _randn_bf16(gen, (B, num_qo_heads, head_dim))
+    k = _randn_pool(gen, pool, num_kv_heads, page_size, head_dim)
+    v = _randn_pool(gen, pool, num_kv_heads, page_size, head_dim)
+    if poison:
+        tabs = [(indices, int(indptr[r]), int(L[r])) for r in range(B)]
+        _poison_pool(k, indices, tabs)
+        _poison_pool(v, indices, tabs)
+    return Workload(name=name, kind="decode", num_qo_heads=num_qo_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
+                    sm_scale=fp32_scale(head_dim), seed=seed,
+                    kv_len=L.to(torch.int32), kv_indptr=indptr, kv_indices=indices,
+                    q=q, k_cache=k, v_cache=v)
+
+
+def make_append(prefix_lens: Sequence[int], qo_lens: Sequence[int], num_qo_heads: int,
+                num_kv_heads: int, head_dim: int, page_size: int, seed: int,
+                poison: bool = True, causal: bool = True, with_new_kv: bool = True,
+                name: str = "append", _gen: Optional[torch.Generator] = None) -> Workload:
+    """``qo_lens[r]`` new query tokens per request appended after ``prefix_lens[r]``
+    cached tokens; kv_len = prefix + qo. With ``with_new_kv`` the new tokens' K/V
+    come in ``k_new``/``v_new`` (their pool slots start as NaN under poison);
+    otherwise they are already in the pool."""
+    gen = _gen if _gen is not None else torch.Generator().manual_seed(seed)
+    P = torch.as_tensor(list(prefix_lens), dtype=torch.int64)
+    Qn = torch.as_tensor(list(qo_lens), dtype=torch.int64)
+    L = P + Qn
+    n = _pages_for(L, page_size)
+    total = int(n.sum())
+    pool = _pool_size(total)
+    perm = torch.randperm(pool, generator=gen).to(torch.int32)
+    indptr = _indptr(n)
+    indices = perm[:total].clone()
+    qo_indptr = _indptr(Qn)
+    T = int(Qn.sum())
+    B = L.numel()
+    q = _randn_bf16(gen, (T, num_qo_heads, head_dim))
+    k = _randn_pool(gen, pool, num_kv_heads, page_size, head_dim)
+    v = _randn_pool(gen, pool, num_kv_heads, page_size, head_dim)
+    k_new = v_new = None
+    if with_new_kv:
+        k_new = _randn_bf16(gen, (T, num_kv_heads, head_dim))
+        v_new = _randn_bf16(gen, (T, num_kv_heads, head_dim))
+    if poison:
+        tabs = [(indices, int(indptr[r]), int(L[r])) for r in range(B)]
+        _poison_pool(k, indices, tabs)
+        _poison_pool(v, indices, tabs)
+        if with_new_kv:
+            for r in range(B):
+                for t in range(int(P[r]), int(L[r])):
+                    pg = int(indices[int(indptr[r]) + t // page_size])
+                    k[pg, :, t % page_size, :] = float("nan")
+                    v[pg, :, t % page_size, :] = float("nan")
+    return Workload(name=name, kind="append", num_qo_heads=num_qo_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
+                    sm_scale=fp32_scale(head_dim), seed=seed,
+                    kv_len=L.to(torch.int32), kv_indptr=indptr, kv_indices=indices,
+                    q=q, k_cache=k, v_cache=v, causal=causal,
+                    qo_indptr=qo_indptr, k_new=k_new, v_new=v_new)
+
+
+def make_cascade(prefix_lens: Sequence[int], req_group: Sequence[int],
+                 suffix_lens: Sequence[int], num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int, page_size: int, seed: int, poison: bool = True,
+                 name: str = "cascade", _gen: Optional[torch.Generator] = None) -> Workload:
+    """Decode queries over (shared prefix of group ``req_group[r]``) || (own suffix).
+    Each prefix is stored once in the pool; ``req_group[r] = -1`` means no prefix."""
+    gen = _gen if _gen is not None else torch.Generator().manual_seed(seed)
+    PL = torch.as_tensor(list(prefix_lens), dtype=torch.int64)
+    S = torch.as_tensor(list(suffix_lens), dtype=torch.int64)
+    grp = torch.as_tensor(list(req_group), dtype=torch.int64)
+    npf = _pages_for(PL, page_size)
+    ns = _pages_for(S, page_size)
+    tot_pf, tot_s = int(npf.sum()), int(ns.sum())
+    pool = _pool_size(tot_pf + tot_s)
+    perm = torch.randperm(pool, generator=gen).to(torch.int32)
+    prefix_indptr = _indptr(npf)
+    prefix_indices = perm[:tot_pf].clone()
+    indptr = _indptr(ns)
+    indices = perm[tot_pf:tot_pf + tot_s].clone()
+    B = S.numel()
+    q = _randn_bf16(gen, (B, num_qo_heads, head_dim))
+    k = _randn_pool(gen, pool, num_kv_heads, page_size, head_dim)
+    v = _randn_pool(gen, pool, num_kv_heads, page_size, head_dim)
+    if poison:
+        used = perm[:tot_pf + tot_s]
+        tabs = [(prefix_indices, int(prefix_indptr[g]), int(PL[g])) for g in range(PL.numel())]
+        tabs += [(indices, int(indptr[r]), int(S[r])) for r in range(B)]
+        _poison_pool(k, used, tabs)
+        _poison_pool(v, used, tabs)
+    return Workload(name=name, kind="cascade", num_qo_heads=num_qo_heads,
+                    num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
+                    sm_scale=fp32_scale(head_dim), seed=seed,
+                    kv_len=S.to(torch.int32), kv_indptr=indptr, kv_indices=indices,
+                    q=q, k_cache=k, v_cache=v,
+                    prefix_indptr=prefix_indptr, prefix_indices=prefix_indices,
+                    prefix_len=PL.to(torch.int32), req_prefix_group=grp.to(torch.int32))
+
+
+def cascade_flat_tables(w: Workload):
+    """(kv_indptr, kv_indices, kv_len) of the flat table prefix || suffix per
+    request. Only defined when every prefix length is a multiple of the page
+    size, so the flat page list is the plain concatenation of the two lists."""
+    assert w.kind == "cascade"
+    ps = w.page_size
+    assert all(int(x) % ps == 0 for x in w.prefix_len), "prefix not page aligned"
+    idx, counts, lens = [], [], []
+    for r in range(w.batch):
+        g = int(w.req_prefix_group[r])
+        a, b = int(w.kv_indptr[r]), int(w.kv_indptr[r + 1])
+        pages = []
+        L = int(w.kv_len[r])
+        if g >= 0:
+            pa, pb = int(w.prefix_indptr[g]), int(w.prefix_indptr[g + 1])
+            pages.append(w.prefix_indices[pa:pb])
+            L += int(w.prefix_len[g])
+        pages.append(w.kv_indices[a:b])
+        cat = torch.cat(pages)
+        idx.append(cat)
+        counts.append(cat.numel())
+        lens.append(L)
+    return (_indptr(torch.tensor(counts)), torch.cat(idx).to(torch.int32),
+            torch.tensor(lens, dtype=torch.int32))
+
+
+def make_config(k: int, poison: bool = False, seed: Optional[int] = None) -> Workload:
+    """The five benchmark configurations, by 0-based index (see CONFIG_NAMES)."""
+    seed = BASE_SEED + k if seed is None else seed
+    gen = torch.Generator().manual_seed(seed)
+    name = CONFIG_NAMES[k]
+    if k == 0:
+        L = _lengths_uniform(gen, 4, 37, 300)
+        return make_decode(L, 8, 2, 64, 16, seed, poison, name, _gen=gen)
+    if k == 1:
+        L = _lengths_uniform(gen, 64, 512, 4096)
+        return make_decode(L, 32, 8, 128, 16, seed, poison, name, _gen=gen)
+    if k == 2:
+        z = torch.randn(128, generator=gen, dtype=torch.float64)
+        L = torch.round(torch.exp(math.log(1024.0) + 1.0 * z)).clamp(1, 32768).to(torch.int64)
+        forced = torch.randperm(128, generator=gen)[:4]
+        L[forced] = 32768
+        return make_decode(L, 32, 8, 128, 16, seed, poison, name, _gen=gen)
+    if k == 3:
+        S = _lengths_uniform(gen, 64, 256, 1024)
+        return make_cascade([8192], [0] * 64, S, 32, 8, 128, 16, seed, poison, name, _gen=gen)
+    if k == 4:
+        P = _lengths_uniform(gen, 16, 1024, 8192)
+        Qn = _lengths_uniform(gen, 16, 1, 128)
+        return make_append(P, Qn, 32, 8, 128, 16, seed, poison, True, True, name, _gen=gen)
+    raise ValueError(f"no config {k}")
