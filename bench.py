@@ -1,0 +1,206 @@
+"""Paged decode benchmark on one MI355X.
+
+A step is one fi_paged_decode call (block-table gather, q.K, online softmax,
+P.V, fp32 partials and the fixed-order merge) over the whole Llama-3-8B-like
+decode batch: 64 requests, 32 q / 8 kv heads, head_dim 128, page size 16,
+kv_len ~ U[512, 4096], bf16 N(0,1) K/V in a randomly permuted page pool. The
+plan (host) is built once per batch, as a serving step reuses it for every
+layer; its host time is reported separately.
+
+Prints one JSON line. ``value`` is the achieved KV throughput (algorithmic
+K+V bytes over the measured time per call, inputs resident in HBM).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention µs/call and achieved KV HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+CONFIG_INDEX = 1               # the Llama-3-8B-like decode batch
+KERNEL_SOURCES = ("paged_kv_attention_amd/csrc/fi_attention.hip",)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_decode.json")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(w) -> dict:
+    """Bytes a perfect kernel must move for one call: K and V of exactly
+    kv_len tokens per request and kv head, q, o, lse and the page ids."""
+    kv = w.kv_bytes()
+    q = w.q.numel() * 2
+    o = q
+    lse = w.batch * w.num_qo_heads * 4
+    idx = int(w.kv_indptr[-1]) * 4
+    return dict(kv=kv, total=kv + q + o + lse + idx)
+
+
+def measured_traffic(launches_bytes: float):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle on the host cores over the same batch, repeated until
+    about ``budget_s`` seconds of work are done."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    kp, vp = w.k_cache.float().numpy(), w.v_cache.float().numpy()
+    q = w.q.double().numpy()
+    args = (w.kv_indptr.numpy(), w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size, w.sm_scale)
+    # size the sample: time one request, then take enough requests for the budget
+    t0 = time.perf_counter()
+    oracle.paged_decode(q, kp, vp, *args, requests=[0])
+    per_req = max(1e-3, time.perf_counter() - t0)
+    n_req = max(1, min(w.batch, int(budget_s / per_req)))
+    reps = max(1, int(budget_s / (per_req * n_req)))
+    reqs = list(range(n_req))
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        oracle.paged_decode(q, kp, vp, *args, requests=reqs)
+    dt = time.perf_counter() - t0
+    per_tok = w.num_kv_heads * w.head_dim * 2 * 2
+    kv = int(w.kv_len[:n_req].sum()) * per_tok * reps
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": kv / dt / 1e9, "unit": "GB/s", "cores": int(min(cores, blas_threads)),
+            "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, first {n_req} of {w.batch} requests x {reps} repeat(s), "
+                      f"{dt:.1f} s wall, KV bytes of the sample / wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--mode", choices=("balanced", "deterministic"), default="balanced")
+    ap.add_argument("--workers-per-cu", type=int, default=0)
+    ap.add_argument("--min-chunk-pages", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for cpu_baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build measures one GPU only; --gpus must be 1 "
+              "(the path's multi-GPU sharding is a design note, not a run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import paged_kv_attention_amd as fi
+    from workloads import CONFIG_NAMES, make_config
+
+    dev = torch.device("cuda:0")
+    fi.load()
+    print(f"bench: generating {CONFIG_NAMES[CONFIG_INDEX]}", file=sys.stderr, flush=True)
+    w = make_config(CONFIG_INDEX, poison=False)
+    g = w.to(dev)
+    nbytes = algorithmic_bytes(w)
+
+    plan_kw = dict(deterministic=args.mode == "deterministic",
+                   workers_per_cu=args.workers_per_cu, min_chunk_pages=args.min_chunk_pages)
+    t0 = time.perf_counter()
+    plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                   w.page_size, device=dev, **plan_kw)
+    torch.cuda.synchronize()
+    plan_ms_first = (time.perf_counter() - t0) * 1e3
+    # steady-state host plan time (re-plan into the same workspace)
+    reps = 20
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
+                       w.head_dim, w.page_size, device=dev, workspace=plan.workspace, **plan_kw)
+    torch.cuda.synchronize()
+    plan_us = (time.perf_counter() - t0) / reps * 1e6
+
+    out = torch.empty_like(g.q)
+    lse = torch.empty(w.batch, w.num_qo_heads, dtype=torch.float32, device=dev)
+
+    def step():
+        fi.paged_decode(plan, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale, out=out,
+                        lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"bench: warmup done ({args.warmup} calls), timing {args.steps}", file=sys.stderr,
+          flush=True)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with fi.KernelTimer(args.steps) as kt:
+        ev0.record()
+        for _ in range(args.steps):
+            step()
+        ev1.record()
+        torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    kern_ms = kt.total_ms / max(1, kt.calls)
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    gbs = nbytes["kv"] / (ms_per_step * 1e-3) / 1e9
+    achieved = nbytes["total"] / (kern_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(nbytes["total"]),
+            "kernel": "attention_kernel<128,1>", "algorithmic_bytes_per_launch": nbytes["total"],
+            "avg_launch_us": round(kern_ms * 1e3, 2)}
+    res = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": CONFIG_NAMES[CONFIG_INDEX], "batch": w.batch,
+                   "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
+                   "head_dim": w.head_dim, "page_size": w.page_size,
+                   "kv_len": "uniform [512, 4096]", "seed": w.seed, "mode": args.mode,
+                   "kv_tokens": int(w.kv_len.sum())},
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "plan_host_us": round(plan_us, 1), "plan_first_ms": round(plan_ms_first, 2),
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

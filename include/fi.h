@@ -1,0 +1,212 @@
+/*
+ * fi.h -- C ABI of the MI355X (gfx950) paged-KV attention library (libfi.so).
+ *
+ * What the library computes: exact softmax attention of query rows over K/V
+ * gathered through a per-request block table (a block-sparse row format over a
+ * pool of fixed-size pages), with grouped-query heads, the KV range of each
+ * request split into load-balanced chunks by a host-side plan, and the chunks'
+ * fp32 partial states (o, lse) merged in a fixed order. Sources:
+ *   - Ye et al. catalogue record of the FlashInfer paper, fields "summary"
+ *     (block-sparse KV representations; load-balanced scheduling that stays
+ *     valid under static graph capture) and "boundary" (exact attention and
+ *     paged KV storage are inherited, not changed);
+ *   - research note "flashinfer-backend-selection", section "Arithmetic
+ *     intensity" (decode reads K/V through a gathered block table; cascade
+ *     reads a shared prefix once for all requests that share it);
+ *   - FlashInfer PR #4038, section "What it does" (split partials kept in fp32
+ *     and reduced in a fixed order, so results repeat bit for bit).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Layouts (row-major, element types as named):
+ *   q        bf16 [T][Hq][D]      T = batch for decode/cascade, sum(qo) for append
+ *   o        bf16 [T][Hq][D]      lse  fp32 [T][Hq] (natural log; may be NULL)
+ *   k_cache, v_cache  bf16 [num_pages][Hkv][page_size][D]
+ *   kv_indices int32 page ids; request r's pages are
+ *            kv_indices[kv_indptr[r] .. kv_indptr[r+1]), token t of the request
+ *            in page kv_indices[kv_indptr[r] + t / page_size], slot t % page_size.
+ *   q head h reads kv head h / (Hq / Hkv).
+ * Ownership: every pointer passed to a run call is caller-owned device memory
+ *   and must stay valid until the stream work finishes. The library allocates
+ *   no device memory: the plan lives in a caller-owned device workspace and a
+ *   caller-owned pinned host staging buffer (sizes from fi_workspace_size).
+ *   The fi_plan_t handle itself is library-owned host memory.
+ * Streams: `stream` is a hipStream_t (NULL = default stream). Run calls only
+ *   enqueue work and return; device faults surface at the caller's next
+ *   synchronisation. Run calls neither allocate nor synchronise, so they may be
+ *   captured in a HIP graph; a later fi_plan on the same workspace (same
+ *   capacity) updates what a captured graph reads.
+ * Errors: every call returns FI_OK (0) or an error code and launches nothing
+ *   on error; fi_last_error() gives a thread-local message. Device-side arrays
+ *   (kv_indices) are trusted to agree with the host arrays given to fi_plan.
+ * Threads: distinct plans are independent; one plan must not be used on two
+ *   streams at once, and a re-plan of a workspace must not overlap its use.
+ */
+#ifndef FI_H
+#define FI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fi_status {
+  FI_OK = 0,
+  FI_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent host arrays */
+  FI_ERR_UNSUPPORTED = 2,   /* head_dim not 64/128, page size, head grouping    */
+  FI_ERR_WORKSPACE = 3,     /* a workspace is smaller than the plan needs       */
+  FI_ERR_PLAN_MISMATCH = 4, /* plan of another kind used, or no plan            */
+  FI_ERR_HIP = 5            /* HIP runtime error (message has its text)         */
+} fi_status;
+
+typedef enum fi_kind {
+  FI_KIND_DECODE = 0,   /* one query token per request                      */
+  FI_KIND_APPEND = 1,   /* qo_r query tokens per request, optional causal   */
+  FI_KIND_CASCADE = 2   /* decode over (shared prefix) || (own suffix)      */
+} fi_kind;
+
+typedef enum fi_dtype { FI_DTYPE_BF16 = 0, FI_DTYPE_F32 = 1 } fi_dtype;
+
+/* Plan description. Zero in an optional field selects its default. */
+typedef struct fi_plan_desc {
+  int32_t kind;              /* fi_kind                                        */
+  int32_t batch;             /* number of requests B (>= 0)                    */
+  int32_t num_qo_heads;      /* Hq                                             */
+  int32_t num_kv_heads;      /* Hkv, divides Hq                                */
+  int32_t head_dim;          /* D: 64 or 128                                   */
+  int32_t page_size;         /* tokens per page: power of two in [8, 256]      */
+  int32_t causal;            /* append: 1 = bottom-right causal mask           */
+  int32_t deterministic;     /* 1 = chunk boundaries depend on the request only */
+  int32_t det_chunk_pages;   /* deterministic chunk size in pages (default 64) */
+  int32_t min_chunk_pages;   /* balanced mode lower bound on chunk pages (default 8) */
+  int32_t num_cus;           /* compute units to plan for (0 = current device) */
+  int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 8) */
+  int32_t num_prefix_groups; /* cascade: number of shared prefixes             */
+} fi_plan_desc;
+
+typedef struct fi_plan fi_plan_t;
+
+/* Introspection of a plan's host-side arrays (for tests and tools). The
+ * pointers stay valid until fi_plan_destroy. Item and merge records are
+ * FI_ITEM_INTS / FI_MERGE_INTS int32 each, field order as in fi_internal.h. */
+#define FI_ITEM_INTS 12
+#define FI_MERGE_INTS 5
+typedef struct fi_plan_info {
+  int32_t kind;
+  int32_t num_levels;            /* 2 for cascade (prefix, suffix), else 1 */
+  int32_t num_workers;
+  int32_t rows_per_block[2];
+  int32_t chunk_pages[2];
+  int32_t num_items[2];
+  const int32_t* items[2];       /* grouped by worker                      */
+  const int32_t* worker_indptr[2];
+  int32_t num_merges;
+  const int32_t* merges;
+  int32_t num_parts;
+  const int32_t* parts;
+  int32_t num_qlist;
+  const int32_t* qlist;
+  int32_t num_part_rows;
+  int32_t num_scatter;
+  size_t dev_bytes_used;
+  size_t host_bytes_used;
+} fi_plan_info;
+
+/* Upper bound on the device and pinned-host workspace bytes of any plan with
+ * this description and at most the given totals (all requests' KV pages, all
+ * query tokens, all prefix pages). Allocate once at these sizes to keep
+ * addresses fixed across plans (graph capture). Pure host computation.
+ * Errors: FI_ERR_INVALID_ARG (null/negative), FI_ERR_UNSUPPORTED (shape). */
+fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_pages,
+                            int64_t max_qo_tokens, int64_t max_prefix_pages,
+                            size_t* dev_bytes, size_t* host_bytes);
+
+/* Build the work plan (Ye et al. record, "summary": load-balanced scheduling
+ * compatible with static graphs). Host arrays (all int32, host memory):
+ *   kv_indptr_h [B+1] page offsets (kv_indptr_h[0] == 0, non-decreasing),
+ *   kv_len_h [B] tokens, with kv_indptr_h[r+1]-kv_indptr_h[r] ==
+ *     ceil(kv_len_h[r] / page_size) (cascade: the per-request suffixes);
+ *   qo_indptr_h [B+1] (append only, else NULL): query-token offsets,
+ *     qo_r <= kv_len_h[r]; kv_len counts the new tokens;
+ *   prefix_indptr_h [NG+1], prefix_len_h [NG], req_prefix_group_h [B]
+ *     (cascade only, else NULL): each group's prefix pages and tokens, and the
+ *     group of each request (-1 = none).
+ * The plan splits each request's KV range into chunks (deterministic mode:
+ * det_chunk_pages each; balanced: about equal total work per worker), places
+ * chunks on num_cus*workers_per_cu persistent workers (longest first), and
+ * uploads the result into ws_dev with one hipMemcpyAsync on `stream` from the
+ * pinned ws_host. ws_dev == NULL builds the plan on the host only (no HIP
+ * call; run calls then refuse it) -- used for CPU tests with num_cus > 0.
+ * Before overwriting ws_host the call waits for this workspace's previous
+ * upload. On success *out receives a new handle (free with fi_plan_destroy).
+ * Errors: FI_ERR_INVALID_ARG, FI_ERR_UNSUPPORTED, FI_ERR_WORKSPACE, FI_ERR_HIP. */
+fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_h,
+                  const int32_t* kv_len_h, const int32_t* qo_indptr_h,
+                  const int32_t* prefix_indptr_h, const int32_t* prefix_len_h,
+                  const int32_t* req_prefix_group_h, void* ws_dev,
+                  size_t ws_dev_bytes, void* ws_host, size_t ws_host_bytes,
+                  void* stream, fi_plan_t** out);
+
+void fi_plan_destroy(fi_plan_t* plan);
+
+fi_status fi_plan_get_info(const fi_plan_t* plan, fi_plan_info* info);
+
+/* Decode attention over the paged cache (research note "flashinfer-backend-
+ * selection", "Arithmetic intensity": decode through a gathered block table).
+ * Plan kind FI_KIND_DECODE. q [B][Hq][D] bf16 -> o [B][Hq][D] bf16 and lse
+ * [B][Hq] fp32 (NULL to skip). Split requests are merged in chunk order.
+ * A request with kv_len 0 gets o = 0, lse = -inf. */
+fi_status fi_paged_decode(const fi_plan_t* plan, const void* q, const void* k_cache,
+                          const void* v_cache, const int32_t* kv_indices,
+                          float sm_scale, void* o, float* lse, void* stream);
+
+/* Append / prefill attention for a mixed batch (research note, "Arithmetic
+ * intensity": prefill and decode rows of one batch). Plan kind
+ * FI_KIND_APPEND. If k_new and v_new ([sum qo][Hkv][D] bf16) are non-NULL,
+ * first writes them into the cache slots of the new tokens (positions
+ * kv_len-qo .. kv_len-1 of each request); then query i of request r (global
+ * row qo_indptr[r]+i) attends to keys 0..kv_len-qo+i (causal plan) or to all
+ * kv_len keys. Both or neither of k_new/v_new. */
+fi_status fi_paged_append(const fi_plan_t* plan, const void* q, const void* k_new,
+                          const void* v_new, void* k_cache, void* v_cache,
+                          const int32_t* kv_indices, float sm_scale, void* o,
+                          float* lse, void* stream);
+
+/* Cascade decode (research note, "Arithmetic intensity": a shared prefix's KV
+ * is read once and reused by every request that shares it). Plan kind
+ * FI_KIND_CASCADE. Level 0 attends all member queries of a group to the
+ * group's prefix pages (prefix_indices), level 1 each request to its own
+ * suffix (kv_indices); the two states are merged prefix first. The result is
+ * attention over prefix || suffix. */
+fi_status fi_cascade(const fi_plan_t* plan, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* prefix_indices,
+                     const int32_t* kv_indices, float sm_scale, void* o, float* lse,
+                     void* stream);
+
+/* Merge S attention states per row in fixed order, index 0 first (PR #4038,
+ * "What it does": fp32 partials reduced in a fixed order). v [N][S][H][D] of
+ * v_dtype, s [N][S][H] fp32 natural-log LSE -> v_out [N][H][D] of out_dtype,
+ * s_out [N][H] (NULL to skip). States with s = -inf contribute nothing; if all
+ * are -inf the row is 0 with s_out -inf. D in [1, 1024], a multiple of 4. */
+fi_status fi_merge_states(const void* v, int32_t v_dtype, const float* s, int32_t N,
+                          int32_t S, int32_t H, int32_t D, void* v_out,
+                          int32_t out_dtype, float* s_out, void* stream);
+
+/* Thread-local text of the last error returned on this thread ("" if none). */
+const char* fi_last_error(void);
+
+/* Kernel timer for measurement: while enabled, every run call records a HIP
+ * event pair on its stream around its attention kernel(s) (not the merge or
+ * scatter). fi_timer_begin(capacity) starts a fresh window of up to capacity
+ * calls; fi_timer_end synchronises on the recorded events and returns the
+ * summed milliseconds and the number of calls recorded, then disables it. */
+fi_status fi_timer_begin(int32_t capacity);
+fi_status fi_timer_end(double* total_ms, int32_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FI_H */

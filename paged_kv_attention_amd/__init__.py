@@ -1,0 +1,17 @@
+"""MI355X-native paged-KV attention: plan, paged decode, append, cascade and
+state merge, backed by hand-written HIP kernels for gfx950 in libfi.so.
+
+The shared library is required: importing works without it, but every call
+raises until it is built (``python -m paged_kv_attention_amd.build``).
+"""
+
+from ._lib import FIError, LIB_PATH, SIGNATURES, load  # noqa: F401
+from .api import (  # noqa: F401
+    KernelTimer,
+    Plan,
+    Workspace,
+    cascade,
+    merge_states,
+    paged_append,
+    paged_decode,
+)

@@ -1,0 +1,286 @@
+"""Python binding over the C ABI: argument marshalling only.
+
+Every step of the computation runs in libfi.so's HIP kernels; this module
+checks tensor shapes/dtypes, passes raw pointers and the current torch stream,
+and turns error codes into exceptions. PyTorch supplies device memory and
+streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_KINDS = {"decode": L.FI_KIND_DECODE, "append": L.FI_KIND_APPEND, "cascade": L.FI_KIND_CASCADE}
+
+
+def _host_i32(x) -> Optional[np.ndarray]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(L.I32P)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class Workspace:
+    """Caller-owned plan storage: a device buffer and a pinned host staging
+    buffer. Reusing one workspace across plans keeps device addresses fixed."""
+
+    def __init__(self, dev_bytes: int, host_bytes: int, device="cuda"):
+        self.dev = torch.empty(max(int(dev_bytes), 256), dtype=torch.uint8, device=device)
+        self.host = torch.empty(max(int(host_bytes), 256), dtype=torch.uint8, pin_memory=True)
+
+    @staticmethod
+    def bound(desc: L.PlanDesc, max_kv_pages: int, max_qo_tokens: int = 0,
+              max_prefix_pages: int = 0):
+        dev, host = ctypes.c_size_t(), ctypes.c_size_t()
+        L.check(L.load().fi_workspace_size(ctypes.byref(desc), int(max_kv_pages),
+                                           int(max_qo_tokens), int(max_prefix_pages),
+                                           ctypes.byref(dev), ctypes.byref(host)),
+                "fi_workspace_size")
+        return dev.value, host.value
+
+
+class Plan:
+    """A work plan for one batch (fi_plan). ``device=None`` builds it on the
+    host only (needs ``num_cus``), which the run calls refuse."""
+
+    def __init__(self, kind: str, kv_indptr, kv_len, num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int, page_size: int, *, qo_indptr=None, causal: bool = False,
+                 prefix_indptr=None, prefix_len=None, req_prefix_group=None,
+                 deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
+                 num_cus: int = 0, workers_per_cu: int = 0, device="cuda",
+                 workspace: Optional[Workspace] = None):
+        lib = L.load()
+        self.kind = kind
+        self._ha = dict(kv_indptr=_host_i32(kv_indptr), kv_len=_host_i32(kv_len),
+                        qo_indptr=_host_i32(qo_indptr), prefix_indptr=_host_i32(prefix_indptr),
+                        prefix_len=_host_i32(prefix_len),
+                        req_prefix_group=_host_i32(req_prefix_group))
+        B = int(self._ha["kv_len"].size)
+        ng = 0 if prefix_len is None else int(self._ha["prefix_len"].size)
+        self.desc = L.PlanDesc(kind=_KINDS[kind], batch=B, num_qo_heads=num_qo_heads,
+                               num_kv_heads=num_kv_heads, head_dim=head_dim,
+                               page_size=page_size, causal=int(causal),
+                               deterministic=int(deterministic),
+                               det_chunk_pages=det_chunk_pages, min_chunk_pages=min_chunk_pages,
+                               num_cus=num_cus, workers_per_cu=workers_per_cu,
+                               num_prefix_groups=ng)
+        self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
+        self.head_dim, self.page_size, self.batch = head_dim, page_size, B
+        self.device = None if device is None else torch.device(device)
+        self.workspace = workspace
+        ws_dev = ws_host = None
+        dev_b = host_b = 0
+        if self.device is not None:
+            if self.workspace is None:
+                n_q = 0 if qo_indptr is None else int(self._ha["qo_indptr"][-1])
+                n_p = 0 if prefix_indptr is None else int(self._ha["prefix_indptr"][-1])
+                n_kv = int(self._ha["kv_indptr"][-1]) if B else 0
+                db, hb = Workspace.bound(self.desc, n_kv, n_q, n_p)
+                self.workspace = Workspace(db, hb, self.device)
+            ws_dev, ws_host = _ptr(self.workspace.dev), _ptr(self.workspace.host)
+            dev_b, host_b = self.workspace.dev.numel(), self.workspace.host.numel()
+            stream = _stream(self.device)
+        else:
+            stream = None
+        h = ctypes.c_void_p()
+        a = self._ha
+        L.check(lib.fi_plan(ctypes.byref(self.desc), _p(a["kv_indptr"]), _p(a["kv_len"]),
+                            _p(a["qo_indptr"]), _p(a["prefix_indptr"]), _p(a["prefix_len"]),
+                            _p(a["req_prefix_group"]), ws_dev, dev_b, ws_host, host_b, stream,
+                            ctypes.byref(h)), "fi_plan")
+        self._h = h
+        self.num_q_tokens = B if qo_indptr is None else int(self._ha["qo_indptr"][-1])
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            try:
+                L.load().fi_plan_destroy(h)
+            except Exception:
+                pass
+            self._h = None
+
+    def info(self) -> dict:
+        """Copies of the plan's host arrays (items, worker lists, merges...)."""
+        inf = L.PlanInfo()
+        L.check(L.load().fi_plan_get_info(self._h, ctypes.byref(inf)), "fi_plan_get_info")
+
+        def arr(ptr, n):
+            if n == 0:
+                return np.zeros(0, dtype=np.int32)
+            return np.ctypeslib.as_array(ptr, shape=(n,)).copy()
+
+        levels = []
+        for l in range(inf.num_levels):
+            levels.append(dict(
+                rows_per_block=inf.rows_per_block[l], chunk_pages=inf.chunk_pages[l],
+                items=arr(inf.items[l], inf.num_items[l] * L.FI_ITEM_INTS).reshape(-1, L.FI_ITEM_INTS),
+                worker_indptr=arr(inf.worker_indptr[l], inf.num_workers + 1)))
+        return dict(kind=inf.kind, num_workers=inf.num_workers, levels=levels,
+                    merges=arr(inf.merges, inf.num_merges * L.FI_MERGE_INTS).reshape(-1, L.FI_MERGE_INTS),
+                    parts=arr(inf.parts, inf.num_parts), qlist=arr(inf.qlist, inf.num_qlist),
+                    num_part_rows=inf.num_part_rows, num_scatter=inf.num_scatter,
+                    dev_bytes_used=inf.dev_bytes_used, host_bytes_used=inf.host_bytes_used)
+
+
+def _check_tensor(t, name, dtype, device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_cache(plan: Plan, k_cache, v_cache):
+    dev = plan.device
+    _check_tensor(k_cache, "k_cache", torch.bfloat16, dev)
+    _check_tensor(v_cache, "v_cache", torch.bfloat16, dev, k_cache.shape)
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (plan.num_kv_heads, plan.page_size,
+                                                          plan.head_dim):
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match the plan "
+                         f"[P, {plan.num_kv_heads}, {plan.page_size}, {plan.head_dim}]")
+
+
+def _outputs(plan: Plan, q, out, lse):
+    T = plan.num_q_tokens
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor(out, "out", torch.bfloat16, plan.device, (T, plan.num_qo_heads, plan.head_dim))
+    if lse is not None:
+        _check_tensor(lse, "lse", torch.float32, plan.device, (T, plan.num_qo_heads))
+    return out, lse
+
+
+def _check_run(plan: Plan, kind: str):
+    if plan.kind != kind:
+        raise ValueError(f"plan kind is {plan.kind}, not {kind}")
+    if plan.device is None:
+        raise ValueError("host-only plan: build it with a device to run it")
+
+
+def paged_decode(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, out=None,
+                 lse=None, return_lse: bool = True):
+    """fi_paged_decode: q [B, Hq, D] bf16 -> (out [B, Hq, D] bf16, lse [B, Hq] fp32)."""
+    _check_run(plan, "decode")
+    _check_tensor(q, "q", torch.bfloat16, plan.device,
+                  (plan.batch, plan.num_qo_heads, plan.head_dim))
+    _check_cache(plan, k_cache, v_cache)
+    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    if lse is None and return_lse:
+        lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
+    out, lse = _outputs(plan, q, out, lse)
+    L.check(L.load().fi_paged_decode(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                     _ptr(kv_indices), float(sm_scale), _ptr(out), _ptr(lse),
+                                     _stream(plan.device)), "fi_paged_decode")
+    return out, lse
+
+
+def paged_append(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, k_new=None,
+                 v_new=None, out=None, lse=None, return_lse: bool = True):
+    """fi_paged_append: q [sum qo, Hq, D]; optional k_new/v_new [sum qo, Hkv, D]
+    are scattered into the cache first."""
+    _check_run(plan, "append")
+    T = plan.num_q_tokens
+    _check_tensor(q, "q", torch.bfloat16, plan.device, (T, plan.num_qo_heads, plan.head_dim))
+    _check_cache(plan, k_cache, v_cache)
+    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        shp = (T, plan.num_kv_heads, plan.head_dim)
+        _check_tensor(k_new, "k_new", torch.bfloat16, plan.device, shp)
+        _check_tensor(v_new, "v_new", torch.bfloat16, plan.device, shp)
+    if lse is None and return_lse:
+        lse = torch.empty(T, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
+    out, lse = _outputs(plan, q, out, lse)
+    L.check(L.load().fi_paged_append(plan.handle, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(k_cache), _ptr(v_cache), _ptr(kv_indices),
+                                     float(sm_scale), _ptr(out), _ptr(lse),
+                                     _stream(plan.device)), "fi_paged_append")
+    return out, lse
+
+
+def cascade(plan: Plan, q, k_cache, v_cache, prefix_indices, kv_indices, sm_scale: float,
+            out=None, lse=None, return_lse: bool = True):
+    """fi_cascade: decode over (group prefix) || (own suffix), prefix read once."""
+    _check_run(plan, "cascade")
+    _check_tensor(q, "q", torch.bfloat16, plan.device,
+                  (plan.batch, plan.num_qo_heads, plan.head_dim))
+    _check_cache(plan, k_cache, v_cache)
+    _check_tensor(prefix_indices, "prefix_indices", torch.int32, plan.device)
+    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    if lse is None and return_lse:
+        lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
+    out, lse = _outputs(plan, q, out, lse)
+    L.check(L.load().fi_cascade(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                _ptr(prefix_indices), _ptr(kv_indices), float(sm_scale),
+                                _ptr(out), _ptr(lse), _stream(plan.device)), "fi_cascade")
+    return out, lse
+
+
+def merge_states(v, s, out_dtype=None, return_lse: bool = True):
+    """fi_merge_states: v [N, S, H, D] (bf16 or fp32), s [N, S, H] fp32 ->
+    (v_out [N, H, D], s_out [N, H]), folding index 0 first."""
+    if v.dim() != 4 or s.dim() != 3 or tuple(s.shape) != tuple(v.shape[:3]):
+        raise ValueError("expected v [N, S, H, D] and s [N, S, H]")
+    if v.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("v must be bf16 or fp32")
+    _check_tensor(v, "v", v.dtype, v.device)
+    _check_tensor(s, "s", torch.float32, v.device)
+    out_dtype = v.dtype if out_dtype is None else out_dtype
+    N, S, H, D = v.shape
+    v_out = torch.empty(N, H, D, dtype=out_dtype, device=v.device)
+    s_out = torch.empty(N, H, dtype=torch.float32, device=v.device) if return_lse else None
+    dt = lambda t: L.FI_DTYPE_F32 if t == torch.float32 else L.FI_DTYPE_BF16  # noqa: E731
+    L.check(L.load().fi_merge_states(_ptr(v), dt(v.dtype), _ptr(s), N, S, H, D, _ptr(v_out),
+                                     dt(out_dtype), _ptr(s_out), _stream(v.device)),
+            "fi_merge_states")
+    return v_out, s_out
+
+
+class KernelTimer:
+    """Context manager over fi_timer_begin/fi_timer_end: HIP events recorded on
+    the launch stream around each run call's attention kernel(s)."""
+
+    def __init__(self, capacity: int):
+        self.capacity = capacity
+        self.total_ms = None
+        self.calls = None
+
+    def __enter__(self):
+        L.check(L.load().fi_timer_begin(self.capacity), "fi_timer_begin")
+        return self
+
+    def __exit__(self, *exc):
+        ms, n = ctypes.c_double(), ctypes.c_int32()
+        L.check(L.load().fi_timer_end(ctypes.byref(ms), ctypes.byref(n)), "fi_timer_end")
+        self.total_ms, self.calls = ms.value, n.value
+        return False

@@ -1,0 +1,251 @@
+// fi_api.cpp -- run entry points of the C ABI: argument checks, carving the
+// plan's arrays out of the caller's workspace, kernel launches, and the
+// optional kernel timer used by measurement tools.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include <mutex>
+#include <utility>
+#include <vector>
+
+#include "fi_host.h"
+
+using namespace fi;
+
+namespace {
+
+// ---------------------------------------------------------------- timer
+
+std::mutex g_timer_mu;
+bool g_timer_on = false;
+int32_t g_timer_used = 0;
+std::vector<std::pair<hipEvent_t, hipEvent_t>> g_timer_events;
+
+struct TimerScope {
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  explicit TimerScope(hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_timer_mu);
+    if (g_timer_on && g_timer_used < (int32_t)g_timer_events.size()) {
+      auto& pr = g_timer_events[g_timer_used++];
+      if (hipEventRecord(pr.first, s) == hipSuccess) stop = pr.second;
+    }
+  }
+  void done() {
+    if (stop) (void)hipEventRecord(stop, s);
+    stop = nullptr;
+  }
+};
+
+template <typename T>
+T* at(const fi_plan_t* p, size_t off) {
+  return (T*)(p->dev_base + off);
+}
+
+fi_status check_plan(const fi_plan_t* p, int32_t kind, const char* who) {
+  if (!p) return set_error(FI_ERR_PLAN_MISMATCH, "%s: plan is NULL", who);
+  if (p->hp.desc.kind != kind)
+    return set_error(FI_ERR_PLAN_MISMATCH, "%s: plan was built for kind %d", who, p->hp.desc.kind);
+  if (!p->on_device)
+    return set_error(FI_ERR_PLAN_MISMATCH, "%s: host-only plan (built without a device workspace)",
+                     who);
+  return FI_OK;
+}
+
+fi_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return FI_OK;
+  return set_error(FI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, const void* v,
+                   const int32_t* kv_indices, const int32_t* prefix_indices, float sm_scale,
+                   void* o, float* lse) {
+  const fi_plan_desc& d = p->hp.desc;
+  AttnArgs a;
+  a.items = at<int32_t>(p, p->lay.items[level]);
+  a.worker_indptr = at<int32_t>(p, p->lay.windptr[level]);
+  a.num_workers = p->hp.level[level].num_items() > 0 ? p->hp.num_workers : 0;
+  a.qlist = at<int32_t>(p, p->lay.qlist);
+  a.q = (const uint16_t*)q;
+  a.k_cache = (const uint16_t*)k;
+  a.v_cache = (const uint16_t*)v;
+  a.kv_indices = kv_indices;
+  a.prefix_indices = prefix_indices;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.part_o = at<float>(p, p->lay.part_o);
+  a.part_lse = at<float>(p, p->lay.part_lse);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.num_qo_heads = d.num_qo_heads;
+  a.num_kv_heads = d.num_kv_heads;
+  a.group = d.num_qo_heads / d.num_kv_heads;
+  a.page_size = d.page_size;
+  a.page_shift = __builtin_ctz((unsigned)d.page_size);
+  return a;
+}
+
+fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
+  MergeArgs m;
+  m.merges = at<int32_t>(p, p->lay.merges);
+  m.num_merges = (int32_t)(p->hp.merges.size() / MERGE_INTS);
+  m.parts = at<int32_t>(p, p->lay.parts);
+  m.part_o = at<float>(p, p->lay.part_o);
+  m.part_lse = at<float>(p, p->lay.part_lse);
+  m.o = (uint16_t*)o;
+  m.lse = lse;
+  m.num_qo_heads = p->hp.desc.num_qo_heads;
+  m.head_dim = p->hp.desc.head_dim;
+  return hip_status(launch_merge(m, s), "merge launch");
+}
+
+}  // namespace
+
+extern "C" fi_status fi_paged_decode(const fi_plan_t* p, const void* q, const void* k_cache,
+                                     const void* v_cache, const int32_t* kv_indices,
+                                     float sm_scale, void* o, float* lse, void* stream) {
+  clear_error();
+  fi_status st = check_plan(p, FI_KIND_DECODE, "fi_paged_decode");
+  if (st != FI_OK) return st;
+  if (!isfinite(sm_scale)) return set_error(FI_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (p->hp.desc.batch > 0 && (!q || !k_cache || !v_cache || !kv_indices || !o))
+    return set_error(FI_ERR_INVALID_ARG, "fi_paged_decode: NULL tensor pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const AttnArgs a =
+      attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
+  TimerScope t(s);
+  st = hip_status(launch_attention(a, p->hp.desc.head_dim, p->hp.level[0].rows_per_block, s),
+                  "attention launch");
+  t.done();
+  if (st != FI_OK) return st;
+  return run_merge(p, o, lse, s);
+}
+
+extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const void* k_new,
+                                     const void* v_new, void* k_cache, void* v_cache,
+                                     const int32_t* kv_indices, float sm_scale, void* o,
+                                     float* lse, void* stream) {
+  clear_error();
+  fi_status st = check_plan(p, FI_KIND_APPEND, "fi_paged_append");
+  if (st != FI_OK) return st;
+  if (!isfinite(sm_scale)) return set_error(FI_ERR_INVALID_ARG, "sm_scale is not finite");
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return set_error(FI_ERR_INVALID_ARG, "fi_paged_append: give both k_new and v_new or neither");
+  if (p->hp.desc.batch > 0 && (!q || !k_cache || !v_cache || !kv_indices || !o))
+    return set_error(FI_ERR_INVALID_ARG, "fi_paged_append: NULL tensor pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const fi_plan_desc& d = p->hp.desc;
+  if (k_new) {
+    ScatterArgs sa;
+    sa.scatter = at<int32_t>(p, p->lay.scatter);
+    sa.num_tokens = (int32_t)(p->hp.scatter.size() / 2);
+    sa.kv_indices = kv_indices;
+    sa.k_new = (const uint16_t*)k_new;
+    sa.v_new = (const uint16_t*)v_new;
+    sa.k_cache = (uint16_t*)k_cache;
+    sa.v_cache = (uint16_t*)v_cache;
+    sa.num_kv_heads = d.num_kv_heads;
+    sa.page_size = d.page_size;
+    sa.head_dim = d.head_dim;
+    st = hip_status(launch_scatter(sa, s), "scatter launch");
+    if (st != FI_OK) return st;
+  }
+  const AttnArgs a =
+      attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
+  TimerScope t(s);
+  st = hip_status(launch_attention(a, d.head_dim, p->hp.level[0].rows_per_block, s),
+                  "attention launch");
+  t.done();
+  if (st != FI_OK) return st;
+  return run_merge(p, o, lse, s);
+}
+
+extern "C" fi_status fi_cascade(const fi_plan_t* p, const void* q, const void* k_cache,
+                                const void* v_cache, const int32_t* prefix_indices,
+                                const int32_t* kv_indices, float sm_scale, void* o, float* lse,
+                                void* stream) {
+  clear_error();
+  fi_status st = check_plan(p, FI_KIND_CASCADE, "fi_cascade");
+  if (st != FI_OK) return st;
+  if (!isfinite(sm_scale)) return set_error(FI_ERR_INVALID_ARG, "sm_scale is not finite");
+  if (p->hp.desc.batch > 0 && (!q || !k_cache || !v_cache || !kv_indices || !o))
+    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: NULL tensor pointer");
+  if (p->hp.level[0].num_items() > 0 && !prefix_indices)
+    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: NULL prefix_indices");
+  hipStream_t s = (hipStream_t)stream;
+  const int D = p->hp.desc.head_dim;
+  TimerScope t(s);
+  for (int l = 0; l < 2; ++l) {
+    const AttnArgs a =
+        attn_args(p, l, q, k_cache, v_cache, kv_indices, prefix_indices, sm_scale, o, lse);
+    st = hip_status(launch_attention(a, D, p->hp.level[l].rows_per_block, s), "attention launch");
+    if (st != FI_OK) return st;
+  }
+  t.done();
+  return run_merge(p, o, lse, s);
+}
+
+extern "C" fi_status fi_merge_states(const void* v, int32_t v_dtype, const float* s, int32_t N,
+                                     int32_t S, int32_t H, int32_t D, void* v_out,
+                                     int32_t out_dtype, float* s_out, void* stream) {
+  clear_error();
+  if (N < 0 || S < 0 || H < 0) return set_error(FI_ERR_INVALID_ARG, "negative size");
+  if (D < 4 || D > 1024 || D % 4)
+    return set_error(FI_ERR_UNSUPPORTED, "D = %d (need a multiple of 4 in [4, 1024])", D);
+  if ((v_dtype != FI_DTYPE_BF16 && v_dtype != FI_DTYPE_F32) ||
+      (out_dtype != FI_DTYPE_BF16 && out_dtype != FI_DTYPE_F32))
+    return set_error(FI_ERR_INVALID_ARG, "unknown dtype");
+  if ((int64_t)N * H == 0) return FI_OK;
+  if (!v_out || (S > 0 && (!v || !s)))
+    return set_error(FI_ERR_INVALID_ARG, "fi_merge_states: NULL tensor pointer");
+  MergeStatesArgs a;
+  a.v = v;
+  a.v_f32 = v_dtype == FI_DTYPE_F32;
+  a.s = s;
+  a.N = N;
+  a.S = S;
+  a.H = H;
+  a.D = D;
+  a.v_out = v_out;
+  a.out_f32 = out_dtype == FI_DTYPE_F32;
+  a.s_out = s_out;
+  return hip_status(launch_merge_states(a, (hipStream_t)stream), "merge_states launch");
+}
+
+extern "C" fi_status fi_timer_begin(int32_t capacity) {
+  clear_error();
+  if (capacity < 1) return set_error(FI_ERR_INVALID_ARG, "capacity %d < 1", capacity);
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  while ((int32_t)g_timer_events.size() < capacity) {
+    hipEvent_t a = nullptr, b = nullptr;
+    hipError_t e = hipEventCreate(&a);
+    if (e == hipSuccess) e = hipEventCreate(&b);
+    if (e != hipSuccess) return hip_status(e, "event create");
+    g_timer_events.emplace_back(a, b);
+  }
+  g_timer_used = 0;
+  g_timer_on = true;
+  return FI_OK;
+}
+
+extern "C" fi_status fi_timer_end(double* total_ms, int32_t* calls) {
+  clear_error();
+  if (!total_ms || !calls) return set_error(FI_ERR_INVALID_ARG, "NULL output");
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  double sum = 0.0;
+  for (int32_t i = 0; i < g_timer_used; ++i) {
+    hipError_t e = hipEventSynchronize(g_timer_events[i].second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timer_events[i].first, g_timer_events[i].second);
+    if (e != hipSuccess) {
+      g_timer_on = false;
+      return hip_status(e, "event timing");
+    }
+    sum += ms;
+  }
+  *total_ms = sum;
+  *calls = g_timer_used;
+  g_timer_on = false;
+  g_timer_used = 0;
+  return FI_OK;
+}

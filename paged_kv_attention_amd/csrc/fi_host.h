@@ -1,0 +1,59 @@
+// fi_host.h -- host-side plan state and error reporting shared by the C ABI
+// translation units.
+#pragma once
+
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "fi.h"
+#include "fi_internal.h"
+
+namespace fi {
+
+fi_status set_error(fi_status st, const char* fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+struct Level {
+  int32_t rows_per_block = 0;
+  int32_t chunk_pages = 0;
+  std::vector<int32_t> items;          // ITEM_INTS per item, grouped by worker
+  std::vector<int32_t> worker_indptr;  // num_workers + 1
+  int32_t num_items() const { return (int32_t)(items.size() / ITEM_INTS); }
+};
+
+struct HostPlan {
+  fi_plan_desc desc{};     // defaults filled in
+  int32_t num_workers = 0;
+  int32_t num_levels = 0;
+  Level level[2];
+  std::vector<int32_t> merges;   // MERGE_INTS per entry
+  std::vector<int32_t> parts;
+  std::vector<int32_t> qlist;
+  std::vector<int32_t> scatter;  // 2 per new token (append)
+  int32_t num_part_rows = 0;
+};
+
+// Byte offsets of each section inside the workspace blob.
+struct Layout {
+  size_t items[2] = {0, 0}, windptr[2] = {0, 0};
+  size_t merges = 0, parts = 0, qlist = 0, scatter = 0;
+  size_t blob_bytes = 0;     // int32 sections (host staging size)
+  size_t part_o = 0, part_lse = 0;
+  size_t dev_bytes = 0;      // blob + fp32 partial states
+};
+
+Layout layout_for(int32_t num_workers, const size_t n_items[2], size_t n_merges,
+                  size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
+                  int32_t head_dim);
+
+}  // namespace fi
+
+struct fi_plan {
+  fi::HostPlan hp;
+  fi::Layout lay;
+  bool on_device = false;
+  char* dev_base = nullptr;   // caller's device workspace
+};

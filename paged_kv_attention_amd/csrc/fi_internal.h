@@ -1,0 +1,105 @@
+// fi_internal.h -- shared definitions of the plan records and kernel launchers.
+//
+// Work item record (FI_ITEM_INTS = 12 int32), one per (unit, chunk):
+//   0 q_base   first query token of the request (contiguous rows), or offset in
+//              the member list of the item's group (FLAG_LIST_Q)
+//   1 row0     first query row of the item within its unit's rows;
+//              row rho -> query (rho / G), head kv_head*G + rho % G
+//   2 n_rows   rows in the item (<= rows per block of its level)
+//   3 kv_head
+//   4 page_off start of the sequence's page list in its index array
+//   5 flags    FLAG_* below
+//   6 t_begin  first token (page aligned)
+//   7 t_end    one past the last token
+//   8 q_pos0   causal: sequence position of query 0 (kv_len - qo)
+//   9 dst      first fp32 partial row (FLAG_PARTIAL), else -1
+//  10 unit     request (or prefix group) id, informational
+//  11 chunk    chunk index within the unit, informational
+// Merge record (FI_MERGE_INTS = 5): q_tok, head0, n_heads, parts_off, n_parts;
+// head head0+k of token q_tok folds partial rows parts[parts_off+j]+k, j in
+// order. Scatter record (2 int32 per new token): index into kv_indices of the
+// token's page, slot within the page.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fi {
+
+enum ItemField {
+  F_Q_BASE = 0, F_ROW0, F_NROWS, F_KVHEAD, F_PAGEOFF, F_FLAGS,
+  F_TBEGIN, F_TEND, F_QPOS0, F_DST, F_UNIT, F_CHUNK, ITEM_INTS
+};
+enum MergeField { M_QTOK = 0, M_HEAD0, M_NHEADS, M_OFF, M_N, MERGE_INTS };
+enum ItemFlag { FLAG_LIST_Q = 1, FLAG_PARTIAL = 2, FLAG_CAUSAL = 4, FLAG_PREFIX = 8 };
+
+// Query rows one wavefront carries through the MFMA tiles: 16 per row block.
+constexpr int ROWS_DECODE = 16;   // decode and cascade suffix: 1 block
+constexpr int ROWS_APPEND = 32;   // append: 2 blocks
+constexpr int ROWS_PREFIX = 64;   // cascade prefix: 4 blocks
+constexpr int WAVES_PER_BLOCK = 4;
+
+struct AttnArgs {
+  const int32_t* items;
+  const int32_t* worker_indptr;
+  int32_t num_workers;
+  const int32_t* qlist;
+  const uint16_t* q;
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* kv_indices;
+  const int32_t* prefix_indices;
+  uint16_t* o;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  float scale_log2;        // sm_scale * log2(e): logits are kept in base 2
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t group;           // Hq / Hkv
+  int32_t page_size;
+  int32_t page_shift;      // log2(page_size)
+};
+
+struct MergeArgs {
+  const int32_t* merges;
+  int32_t num_merges;
+  const int32_t* parts;
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* o;
+  float* lse;
+  int32_t num_qo_heads;
+  int32_t head_dim;
+};
+
+struct ScatterArgs {
+  const int32_t* scatter;   // 2 int32 per new token
+  int32_t num_tokens;
+  const int32_t* kv_indices;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t head_dim;
+};
+
+struct MergeStatesArgs {
+  const void* v;
+  int32_t v_f32;
+  const float* s;
+  int32_t N, S, H, D;
+  void* v_out;
+  int32_t out_f32;
+  float* s_out;
+};
+
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int rows_per_block,
+                            hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
+hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream);
+
+}  // namespace fi

@@ -1,0 +1,584 @@
+// fi_plan.cpp -- the host-side work plan: validation, load-balanced chunking,
+// longest-first placement on persistent workers, merge lists, and the upload
+// of the plan into the caller's device workspace.
+//
+// The pages state the goal (Ye et al. record, "summary": KV ranges split into
+// load-balanced chunks, scheduled so that a statically captured graph stays
+// valid; PR #4038, "What it does": fp32 partials reduced in a fixed order) but
+// give no algorithm. The rule implemented here:
+//   units   : (request, row block, kv head); cascade prefix: (group, row block,
+//             kv head) over the member requests' rows
+//   key range of a unit: [0, t_lim), t_lim = kv_len, or min(kv_len,
+//             kv_len - qo + i_last + 1) under the bottom-right causal mask
+//   chunk c : deterministic -> det_chunk_pages; balanced -> max(1,
+//             min_chunk_pages, ceil(W / S)), W = level's total unit pages,
+//             S = num_cus * workers_per_cu
+//   chunks  : k = ceil(n / c), chunk j = pages [floor(jn/k), floor((j+1)n/k))
+//   outputs : k == 1 final rows, else fp32 partial rows + merge (cascade: all
+//             partial, merged prefix first)
+//   placing : Graham's longest-processing-time rule, cost = pages + 1, ties to
+//             the lower enumeration index and to the lower worker index.
+// The grid is always S workers, whatever the batch, so a captured graph is
+// re-pointed at a new batch by re-planning into the same workspace.
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <functional>
+#include <map>
+#include <mutex>
+#include <numeric>
+#include <queue>
+#include <utility>
+
+#include "fi_host.h"
+
+namespace fi {
+
+// ---------------------------------------------------------------- errors
+
+static thread_local std::string g_last_error;
+
+fi_status set_error(fi_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+// ---------------------------------------------------------------- layout
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+Layout layout_for(int32_t num_workers, const size_t n_items[2], size_t n_merges,
+                  size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
+                  int32_t head_dim) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t n_int32) {
+    size_t at = off;
+    off = align_up(off + n_int32 * 4, 256);
+    return at;
+  };
+  for (int l = 0; l < 2; ++l) {
+    L.items[l] = take(n_items[l] * ITEM_INTS);
+    L.windptr[l] = take((size_t)num_workers + 1);
+  }
+  L.merges = take(n_merges * MERGE_INTS);
+  L.parts = take(n_parts);
+  L.qlist = take(n_qlist);
+  L.scatter = take(n_scatter * 2);
+  L.blob_bytes = off;
+  L.part_o = off;
+  off = align_up(off + n_part_rows * (size_t)head_dim * 4, 256);
+  L.part_lse = off;
+  off = align_up(off + n_part_rows * 4, 256);
+  L.dev_bytes = off;
+  return L;
+}
+
+// ---------------------------------------------------------------- planning
+
+namespace {
+
+struct Unit {
+  int32_t unit, q_base, row0, n_rows, g, page_off, t_lim, n_pages, q_pos0, flags;
+};
+
+struct ItemRec {
+  int32_t f[ITEM_INTS];
+  int32_t pages;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Units of a level whose rows are request query tokens (decode, append,
+// cascade suffix). Enumeration order: request, row block, kv head.
+void request_units(std::vector<Unit>& out, int32_t B, int32_t G, int32_t Hkv, int32_t ps,
+                   int32_t rpb, const int32_t* kv_indptr, const int32_t* kv_len,
+                   const int32_t* qo_indptr, bool causal) {
+  for (int32_t r = 0; r < B; ++r) {
+    const int32_t nq = qo_indptr ? qo_indptr[r + 1] - qo_indptr[r] : 1;
+    const int32_t qtok = qo_indptr ? qo_indptr[r] : r;
+    const int32_t L = kv_len[r];
+    const int64_t rows = (int64_t)nq * G;
+    const int64_t nblk = ceil_div(rows, rpb);
+    for (int64_t b = 0; b < nblk; ++b) {
+      const int32_t r0 = (int32_t)(b * rpb);
+      const int32_t r1 = (int32_t)std::min<int64_t>(rows, (b + 1) * rpb);
+      const int32_t i_last = (r1 - 1) / G;
+      const int32_t t_lim = causal ? std::min(L, L - nq + i_last + 1) : L;
+      for (int32_t g = 0; g < Hkv; ++g) {
+        Unit u;
+        u.unit = r;
+        u.q_base = qtok;
+        u.row0 = r0;
+        u.n_rows = r1 - r0;
+        u.g = g;
+        u.page_off = kv_indptr[r];
+        u.t_lim = t_lim;
+        u.n_pages = (int32_t)ceil_div(t_lim, ps);
+        u.q_pos0 = causal ? L - nq : 0;
+        u.flags = causal ? FLAG_CAUSAL : 0;
+        out.push_back(u);
+      }
+    }
+  }
+}
+
+struct LevelBuild {
+  std::vector<ItemRec> items;                // enumeration order
+  std::vector<std::pair<int32_t, std::vector<int32_t>>> chunks;  // per unit: k, partial dsts
+};
+
+void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, int32_t S,
+                 bool all_partial, int32_t& next_row, LevelBuild& lb, Level& lv) {
+  int64_t c;
+  if (d.deterministic) {
+    c = std::max(1, d.det_chunk_pages);
+  } else {
+    int64_t W = 0;
+    for (const Unit& u : units) W += u.n_pages;
+    c = std::max<int64_t>({1, d.min_chunk_pages, ceil_div(W, S)});
+  }
+  lv.chunk_pages = (int32_t)c;
+  const int32_t ps = d.page_size;
+  lb.items.clear();
+  lb.chunks.clear();
+  for (const Unit& u : units) {
+    const int64_t n = u.n_pages;
+    const int64_t k = n > 0 ? ceil_div(n, c) : 0;
+    const bool partial = all_partial || k > 1;
+    std::vector<int32_t> dsts;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t p0 = (j * n) / k, p1 = ((j + 1) * n) / k;
+      int32_t dst = -1;
+      if (partial) {
+        dst = next_row;
+        next_row += u.n_rows;
+        dsts.push_back(dst);
+      }
+      ItemRec it;
+      it.f[F_Q_BASE] = u.q_base;
+      it.f[F_ROW0] = u.row0;
+      it.f[F_NROWS] = u.n_rows;
+      it.f[F_KVHEAD] = u.g;
+      it.f[F_PAGEOFF] = u.page_off;
+      it.f[F_FLAGS] = u.flags | (partial ? FLAG_PARTIAL : 0);
+      it.f[F_TBEGIN] = (int32_t)(p0 * ps);
+      it.f[F_TEND] = (int32_t)std::min<int64_t>(p1 * ps, u.t_lim);
+      it.f[F_QPOS0] = u.q_pos0;
+      it.f[F_DST] = dst;
+      it.f[F_UNIT] = u.unit;
+      it.f[F_CHUNK] = (int32_t)j;
+      it.pages = (int32_t)(p1 - p0);
+      lb.items.push_back(it);
+    }
+    lb.chunks.emplace_back((int32_t)k, std::move(dsts));
+  }
+  // Longest processing time first: stable sort keeps enumeration order on ties.
+  const size_t n = lb.items.size();
+  std::vector<int32_t> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+    return lb.items[a].pages > lb.items[b].pages;
+  });
+  typedef std::pair<int64_t, int32_t> LoadW;
+  std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> heap;
+  for (int32_t w = 0; w < S; ++w) heap.push(LoadW(0, w));
+  std::vector<std::vector<int32_t>> per(S);
+  for (int32_t i : order) {
+    LoadW top = heap.top();
+    heap.pop();
+    per[top.second].push_back(i);
+    heap.push(LoadW(top.first + lb.items[i].pages + 1, top.second));
+  }
+  lv.items.clear();
+  lv.items.reserve(n * ITEM_INTS);
+  lv.worker_indptr.assign(1, 0);
+  for (int32_t w = 0; w < S; ++w) {
+    for (int32_t i : per[w])
+      lv.items.insert(lv.items.end(), lb.items[i].f, lb.items[i].f + ITEM_INTS);
+    lv.worker_indptr.push_back((int32_t)(lv.items.size() / ITEM_INTS));
+  }
+}
+
+}  // namespace
+
+static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
+  if (!din) return set_error(FI_ERR_INVALID_ARG, "desc is NULL");
+  d = *din;
+  if (d.kind < FI_KIND_DECODE || d.kind > FI_KIND_CASCADE)
+    return set_error(FI_ERR_INVALID_ARG, "unknown plan kind %d", d.kind);
+  if (d.batch < 0) return set_error(FI_ERR_INVALID_ARG, "batch %d < 0", d.batch);
+  if (d.num_qo_heads < 1 || d.num_kv_heads < 1)
+    return set_error(FI_ERR_INVALID_ARG, "head counts must be >= 1");
+  if (d.num_qo_heads % d.num_kv_heads)
+    return set_error(FI_ERR_INVALID_ARG, "num_qo_heads %d not a multiple of num_kv_heads %d",
+                     d.num_qo_heads, d.num_kv_heads);
+  if (d.head_dim != 64 && d.head_dim != 128)
+    return set_error(FI_ERR_UNSUPPORTED, "head_dim %d (supported: 64, 128)", d.head_dim);
+  if (d.page_size < 8 || d.page_size > 256 || (d.page_size & (d.page_size - 1)))
+    return set_error(FI_ERR_UNSUPPORTED, "page_size %d (supported: powers of two 8..256)",
+                     d.page_size);
+  const int32_t G = d.num_qo_heads / d.num_kv_heads;
+  if (d.kind == FI_KIND_CASCADE && (G > ROWS_DECODE || ROWS_PREFIX % G))
+    return set_error(FI_ERR_UNSUPPORTED, "cascade needs a head group size dividing 16, got %d",
+                     G);
+  if (d.det_chunk_pages < 0 || d.min_chunk_pages < 0 || d.workers_per_cu < 0 ||
+      d.num_cus < 0 || d.num_prefix_groups < 0)
+    return set_error(FI_ERR_INVALID_ARG, "negative tuning field in desc");
+  if (d.det_chunk_pages == 0) d.det_chunk_pages = 64;
+  if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
+  if (d.workers_per_cu == 0) d.workers_per_cu = 8;
+  d.causal = d.causal ? 1 : 0;
+  d.deterministic = d.deterministic ? 1 : 0;
+  if (d.kind != FI_KIND_APPEND) d.causal = 0;
+  if (d.kind != FI_KIND_CASCADE) d.num_prefix_groups = 0;
+  return FI_OK;
+}
+
+static fi_status validate_table(const char* what, int32_t n, const int32_t* indptr,
+                                const int32_t* len, int32_t ps) {
+  if (n == 0) return FI_OK;
+  if (!indptr || !len) return set_error(FI_ERR_INVALID_ARG, "%s arrays are NULL", what);
+  if (indptr[0] != 0) return set_error(FI_ERR_INVALID_ARG, "%s indptr[0] = %d", what, indptr[0]);
+  for (int32_t r = 0; r < n; ++r) {
+    if (len[r] < 0) return set_error(FI_ERR_INVALID_ARG, "%s len[%d] = %d", what, r, len[r]);
+    const int64_t pages = (int64_t)indptr[r + 1] - indptr[r];
+    if (pages != ceil_div(len[r], ps))
+      return set_error(FI_ERR_INVALID_ARG,
+                       "%s entry %d: %lld pages for %d tokens at page size %d", what, r,
+                       (long long)pages, len[r], ps);
+  }
+  return FI_OK;
+}
+
+static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const int32_t* kv_len,
+                       const int32_t* qo_indptr, const int32_t* prefix_indptr,
+                       const int32_t* prefix_len, const int32_t* req_group, HostPlan& hp) {
+  const int32_t B = d.batch, Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
+  const int32_t ps = d.page_size;
+  fi_status st = validate_table("kv", B, kv_indptr, kv_len, ps);
+  if (st != FI_OK) return st;
+  if (d.kind == FI_KIND_APPEND && B > 0) {
+    if (!qo_indptr) return set_error(FI_ERR_INVALID_ARG, "append plan needs qo_indptr");
+    if (qo_indptr[0] != 0) return set_error(FI_ERR_INVALID_ARG, "qo_indptr[0] != 0");
+    for (int32_t r = 0; r < B; ++r) {
+      const int32_t nq = qo_indptr[r + 1] - qo_indptr[r];
+      if (nq < 0 || nq > kv_len[r])
+        return set_error(FI_ERR_INVALID_ARG, "request %d: qo %d not in [0, kv_len %d]", r, nq,
+                         kv_len[r]);
+    }
+  }
+  const int32_t NG = d.num_prefix_groups;
+  if (d.kind == FI_KIND_CASCADE) {
+    st = validate_table("prefix", NG, prefix_indptr, prefix_len, ps);
+    if (st != FI_OK) return st;
+    if (B > 0 && !req_group)
+      return set_error(FI_ERR_INVALID_ARG, "cascade plan needs req_prefix_group");
+    for (int32_t r = 0; r < B; ++r)
+      if (req_group[r] < -1 || req_group[r] >= NG)
+        return set_error(FI_ERR_INVALID_ARG, "request %d: prefix group %d of %d", r,
+                         req_group[r], NG);
+  }
+  const int32_t S = hp.num_workers;
+  int32_t next_row = 0;
+  if (d.kind == FI_KIND_CASCADE) {
+    hp.num_levels = 2;
+    hp.level[0].rows_per_block = ROWS_PREFIX;
+    hp.level[1].rows_per_block = ROWS_DECODE;
+    std::vector<Unit> pu;
+    std::vector<int32_t> group_off(NG, -1);
+    for (int32_t grp = 0; grp < NG; ++grp) {
+      std::vector<int32_t> members;
+      for (int32_t r = 0; r < B; ++r)
+        if (req_group[r] == grp) members.push_back(r);
+      if (members.empty() || prefix_len[grp] == 0) continue;
+      const int32_t off = (int32_t)hp.qlist.size();
+      group_off[grp] = off;
+      hp.qlist.insert(hp.qlist.end(), members.begin(), members.end());
+      const int64_t rows = (int64_t)members.size() * G;
+      for (int64_t b = 0; b < ceil_div(rows, ROWS_PREFIX); ++b) {
+        const int32_t r0 = (int32_t)(b * ROWS_PREFIX);
+        const int32_t r1 = (int32_t)std::min<int64_t>(rows, (b + 1) * ROWS_PREFIX);
+        for (int32_t g = 0; g < Hkv; ++g) {
+          Unit u;
+          u.unit = grp;
+          u.q_base = off;
+          u.row0 = r0;
+          u.n_rows = r1 - r0;
+          u.g = g;
+          u.page_off = prefix_indptr[grp];
+          u.t_lim = prefix_len[grp];
+          u.n_pages = (int32_t)ceil_div(prefix_len[grp], ps);
+          u.q_pos0 = 0;
+          u.flags = FLAG_LIST_Q | FLAG_PREFIX;
+          pu.push_back(u);
+        }
+      }
+    }
+    std::vector<Unit> su;
+    request_units(su, B, G, Hkv, ps, ROWS_DECODE, kv_indptr, kv_len, nullptr, false);
+    LevelBuild lbp, lbs;
+    build_level(pu, d, S, true, next_row, lbp, hp.level[0]);
+    build_level(su, d, S, true, next_row, lbs, hp.level[1]);
+    // prefix partial rows of (request, kv head)
+    std::vector<std::vector<int32_t>> pref((size_t)B * Hkv);
+    for (size_t ui = 0; ui < pu.size(); ++ui) {
+      const Unit& u = pu[ui];
+      const std::vector<int32_t>& dsts = lbp.chunks[ui].second;
+      for (int32_t local = 0; local < u.n_rows; local += G) {
+        const int32_t r = hp.qlist[u.q_base + (u.row0 + local) / G];
+        std::vector<int32_t>& v = pref[(size_t)r * Hkv + u.g];
+        for (int32_t dd : dsts) v.push_back(dd + local);
+      }
+    }
+    for (size_t ui = 0; ui < su.size(); ++ui) {
+      const Unit& u = su[ui];
+      const std::vector<int32_t>& pl = pref[(size_t)u.unit * Hkv + u.g];
+      const std::vector<int32_t>& dsts = lbs.chunks[ui].second;
+      const int32_t n = (int32_t)(pl.size() + dsts.size());
+      const int32_t rec[MERGE_INTS] = {u.unit, u.g * G, G, (int32_t)hp.parts.size(), n};
+      hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
+      hp.parts.insert(hp.parts.end(), pl.begin(), pl.end());
+      hp.parts.insert(hp.parts.end(), dsts.begin(), dsts.end());
+    }
+  } else {
+    hp.num_levels = 1;
+    const bool append = d.kind == FI_KIND_APPEND;
+    const int32_t rpb = append ? ROWS_APPEND : ROWS_DECODE;
+    hp.level[0].rows_per_block = rpb;
+    std::vector<Unit> units;
+    request_units(units, B, G, Hkv, ps, rpb, kv_indptr, kv_len, append ? qo_indptr : nullptr,
+                  append && d.causal);
+    LevelBuild lb;
+    build_level(units, d, S, false, next_row, lb, hp.level[0]);
+    for (size_t ui = 0; ui < units.size(); ++ui) {
+      const Unit& u = units[ui];
+      const int32_t k = lb.chunks[ui].first;
+      if (k == 1) continue;
+      const std::vector<int32_t>& dsts = lb.chunks[ui].second;
+      const int32_t r0 = u.row0, r1 = u.row0 + u.n_rows;
+      for (int32_t i = r0 / G; i <= (r1 - 1) / G; ++i) {
+        const int32_t a = std::max(r0, i * G), b = std::min(r1, (i + 1) * G);
+        const int32_t rec[MERGE_INTS] = {u.q_base + i, u.g * G + (a - i * G), b - a,
+                                         (int32_t)hp.parts.size(), (int32_t)dsts.size()};
+        hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
+        for (int32_t dd : dsts) hp.parts.push_back(dd + (a - r0));
+      }
+    }
+    if (append) {
+      for (int32_t r = 0; r < B; ++r) {
+        const int32_t nq = qo_indptr[r + 1] - qo_indptr[r];
+        for (int32_t i = 0; i < nq; ++i) {
+          const int32_t pos = kv_len[r] - nq + i;
+          hp.scatter.push_back(kv_indptr[r] + pos / ps);
+          hp.scatter.push_back(pos % ps);
+        }
+      }
+    }
+  }
+  hp.num_part_rows = next_row;
+  return FI_OK;
+}
+
+// ---------------------------------------------------------------- upload sync
+
+// One event per pinned staging buffer: the next plan into the same buffer
+// waits for the previous upload to have read it.
+static std::mutex g_upload_mu;
+static std::map<void*, hipEvent_t> g_upload_events;
+
+}  // namespace fi
+
+using namespace fi;
+
+extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_pages,
+                                       int64_t max_qo_tokens, int64_t max_prefix_pages,
+                                       size_t* dev_bytes, size_t* host_bytes) {
+  clear_error();
+  fi_plan_desc d;
+  fi_status st = fill_defaults(desc, d);
+  if (st != FI_OK) return st;
+  if (!dev_bytes || !host_bytes) return set_error(FI_ERR_INVALID_ARG, "NULL output pointer");
+  if (max_kv_pages < 0 || max_qo_tokens < 0 || max_prefix_pages < 0)
+    return set_error(FI_ERR_INVALID_ARG, "negative size bound");
+  int32_t num_cus = d.num_cus;
+  if (num_cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess)
+      return set_error(FI_ERR_HIP, "could not query the device's compute units");
+  }
+  const int64_t S = (int64_t)num_cus * d.workers_per_cu;
+  const int64_t B = d.batch, Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
+  const int64_t c_det = std::max(1, d.det_chunk_pages);
+  size_t n_items[2] = {0, 0};
+  int64_t part_rows = 0, merges = 0;
+  auto level_bound = [&](int64_t units, int64_t pages_sum, int64_t rpb, bool all_partial) {
+    // balanced: items <= S + units; deterministic: items <= pages/c + units
+    int64_t items = d.deterministic ? pages_sum / c_det + units : S + units;
+    (void)all_partial;
+    part_rows += items * rpb;
+    return items;
+  };
+  if (d.kind == FI_KIND_CASCADE) {
+    const int64_t NG = d.num_prefix_groups;
+    const int64_t blocks = ceil_div(B * G, ROWS_PREFIX) + NG;
+    n_items[0] = (size_t)level_bound(blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_PREFIX,
+                                     true);
+    n_items[1] = (size_t)level_bound(B * Hkv, Hkv * max_kv_pages, ROWS_DECODE, true);
+    merges = B * Hkv;
+  } else if (d.kind == FI_KIND_APPEND) {
+    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_APPEND) + B;
+    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_APPEND) + 1;
+    n_items[0] = (size_t)level_bound(blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
+                                     ROWS_APPEND, false);
+    merges = part_rows + blocks * Hkv * 2;
+  } else {
+    const int64_t blocks = B * ceil_div(G, ROWS_DECODE);
+    n_items[0] = (size_t)level_bound(blocks * Hkv, Hkv * ceil_div(G, ROWS_DECODE) * max_kv_pages,
+                                     ROWS_DECODE, false);
+    merges = part_rows + blocks * Hkv * 2;
+  }
+  const size_t n_scatter = d.kind == FI_KIND_APPEND ? (size_t)max_qo_tokens : 0;
+  Layout L = layout_for((int32_t)S, n_items, (size_t)merges, (size_t)part_rows, (size_t)B,
+                        n_scatter, (size_t)part_rows, d.head_dim);
+  *dev_bytes = L.dev_bytes;
+  *host_bytes = L.blob_bytes;
+  return FI_OK;
+}
+
+extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_h,
+                             const int32_t* kv_len_h, const int32_t* qo_indptr_h,
+                             const int32_t* prefix_indptr_h, const int32_t* prefix_len_h,
+                             const int32_t* req_prefix_group_h, void* ws_dev,
+                             size_t ws_dev_bytes, void* ws_host, size_t ws_host_bytes,
+                             void* stream, fi_plan_t** out) {
+  clear_error();
+  if (!out) return set_error(FI_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  fi_plan_desc d;
+  fi_status st = fill_defaults(desc, d);
+  if (st != FI_OK) return st;
+  if (ws_dev && !ws_host)
+    return set_error(FI_ERR_INVALID_ARG, "a device plan needs a pinned host staging buffer");
+  if (d.num_cus == 0) {
+    if (!ws_dev)
+      return set_error(FI_ERR_INVALID_ARG, "a host-only plan needs num_cus > 0");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return set_error(FI_ERR_HIP, "device query: %s", hipGetErrorString(e));
+    d.num_cus = cus;
+  }
+  fi_plan_t* p = new fi_plan_t();
+  p->hp.desc = d;
+  p->hp.num_workers = d.num_cus * d.workers_per_cu;
+  st = build(d, kv_indptr_h, kv_len_h, qo_indptr_h, prefix_indptr_h, prefix_len_h,
+             req_prefix_group_h, p->hp);
+  if (st != FI_OK) {
+    delete p;
+    return st;
+  }
+  HostPlan& hp = p->hp;
+  size_t n_items[2] = {(size_t)hp.level[0].num_items(), (size_t)hp.level[1].num_items()};
+  p->lay = layout_for(hp.num_workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
+                      hp.qlist.size(), hp.scatter.size() / 2, (size_t)hp.num_part_rows,
+                      d.head_dim);
+  const Layout& L = p->lay;
+  if (ws_dev) {
+    if (ws_dev_bytes < L.dev_bytes || ws_host_bytes < L.blob_bytes) {
+      delete p;
+      return set_error(FI_ERR_WORKSPACE,
+                       "workspace too small: need %zu device / %zu host bytes, got %zu / %zu",
+                       L.dev_bytes, L.blob_bytes, ws_dev_bytes, ws_host_bytes);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t ev = nullptr;
+    {
+      std::lock_guard<std::mutex> lk(g_upload_mu);
+      auto itv = g_upload_events.find(ws_host);
+      if (itv != g_upload_events.end()) ev = itv->second;
+    }
+    hipError_t e = hipSuccess;
+    if (ev) e = hipEventSynchronize(ev);
+    if (e != hipSuccess) {
+      delete p;
+      return set_error(FI_ERR_HIP, "waiting for the previous upload: %s", hipGetErrorString(e));
+    }
+    char* h = (char*)ws_host;
+    for (int l = 0; l < 2; ++l) {
+      if (!hp.level[l].items.empty())
+        memcpy(h + L.items[l], hp.level[l].items.data(), hp.level[l].items.size() * 4);
+      if (!hp.level[l].worker_indptr.empty())
+        memcpy(h + L.windptr[l], hp.level[l].worker_indptr.data(),
+               hp.level[l].worker_indptr.size() * 4);
+    }
+    if (!hp.merges.empty()) memcpy(h + L.merges, hp.merges.data(), hp.merges.size() * 4);
+    if (!hp.parts.empty()) memcpy(h + L.parts, hp.parts.data(), hp.parts.size() * 4);
+    if (!hp.qlist.empty()) memcpy(h + L.qlist, hp.qlist.data(), hp.qlist.size() * 4);
+    if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
+    e = hipMemcpyAsync(ws_dev, ws_host, L.blob_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) {
+      if (!ev) {
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) {
+          std::lock_guard<std::mutex> lk(g_upload_mu);
+          g_upload_events[ws_host] = ev;
+        }
+      }
+      if (e == hipSuccess) e = hipEventRecord(ev, s);
+    }
+    if (e != hipSuccess) {
+      delete p;
+      return set_error(FI_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
+    }
+    p->on_device = true;
+    p->dev_base = (char*)ws_dev;
+  }
+  *out = p;
+  return FI_OK;
+}
+
+extern "C" void fi_plan_destroy(fi_plan_t* plan) { delete plan; }
+
+extern "C" fi_status fi_plan_get_info(const fi_plan_t* p, fi_plan_info* info) {
+  clear_error();
+  if (!p || !info) return set_error(FI_ERR_INVALID_ARG, "NULL plan or info");
+  memset(info, 0, sizeof(*info));
+  const HostPlan& hp = p->hp;
+  info->kind = hp.desc.kind;
+  info->num_levels = hp.num_levels;
+  info->num_workers = hp.num_workers;
+  for (int l = 0; l < 2; ++l) {
+    info->rows_per_block[l] = hp.level[l].rows_per_block;
+    info->chunk_pages[l] = hp.level[l].chunk_pages;
+    info->num_items[l] = hp.level[l].num_items();
+    info->items[l] = hp.level[l].items.data();
+    info->worker_indptr[l] = hp.level[l].worker_indptr.data();
+  }
+  info->num_merges = (int32_t)(hp.merges.size() / MERGE_INTS);
+  info->merges = hp.merges.data();
+  info->num_parts = (int32_t)hp.parts.size();
+  info->parts = hp.parts.data();
+  info->num_qlist = (int32_t)hp.qlist.size();
+  info->qlist = hp.qlist.data();
+  info->num_part_rows = hp.num_part_rows;
+  info->num_scatter = (int32_t)(hp.scatter.size() / 2);
+  info->dev_bytes_used = p->lay.dev_bytes;
+  info->host_bytes_used = p->lay.blob_bytes;
+  return FI_OK;
+}
+
+extern "C" const char* fi_last_error(void) { return fi::g_last_error.c_str(); }

@@ -1,0 +1,258 @@
+"""CPU tests of the C ABI: the library loads and exports every declared symbol,
+the C++ planner equals the reference plan rule element for element, the
+workspace bound covers every plan, and host-detectable errors are reported
+with their codes before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_attention_amd as fi
+from paged_kv_attention_amd import _lib as L
+from oracle.plan_ref import plan_ref
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "fi.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fi_\w+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fi.load()
+    names = declared_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), f"libfi.so does not export {n}"
+    assert set(names) == set(L.SIGNATURES), "binding and header disagree"
+
+
+def _indptr(counts):
+    return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+def _decode_host(lens, ps):
+    return _indptr([-(-int(x) // ps) for x in lens]), np.asarray(lens, dtype=np.int32)
+
+
+def host_plan(kind, indptr, lens, Hq, Hkv, D, ps, **kw):
+    return fi.Plan(kind, indptr, lens, Hq, Hkv, D, ps, device=None, **kw)
+
+
+def compare(info, ref):
+    assert len(info["levels"]) == len(ref["levels"])
+    for lv, rl in zip(info["levels"], ref["levels"]):
+        items = np.array(rl["items"], dtype=np.int32).reshape(-1, L.FI_ITEM_INTS)
+        assert np.array_equal(lv["items"], items)
+        assert np.array_equal(lv["worker_indptr"], np.array(rl["worker_indptr"], dtype=np.int32))
+    assert np.array_equal(info["merges"],
+                          np.array(ref["merges"], dtype=np.int32).reshape(-1, L.FI_MERGE_INTS))
+    assert np.array_equal(info["parts"], np.array(ref["parts"], dtype=np.int32))
+    assert np.array_equal(info["qlist"], np.array(ref["qlist"], dtype=np.int32))
+    assert info["num_part_rows"] == ref["n_part_rows"]
+
+
+@pytest.mark.parametrize("det", [False, True])
+@pytest.mark.parametrize("ps,Hq,Hkv", [(16, 32, 8), (8, 8, 2), (32, 4, 4), (16, 40, 2)])
+def test_decode_plan_matches_reference(det, ps, Hq, Hkv):
+    rng = np.random.default_rng(ps * 100 + Hq)
+    lens = list(rng.integers(0, 3000, 40)) + [0, 1, ps, 32768]
+    indptr, L_ = _decode_host(lens, ps)
+    kw = dict(deterministic=det, det_chunk_pages=16, min_chunk_pages=4, num_cus=7,
+              workers_per_cu=5)
+    p = host_plan("decode", indptr, L_, Hq, Hkv, 128, ps, **kw)
+    info = p.info()
+    ref = plan_ref("decode", Hq, Hkv, ps, indptr, L_, 35, [info["levels"][0]["rows_per_block"]],
+                   deterministic=det, det_chunk_pages=16, min_chunk_pages=4)
+    compare(info, ref)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("det", [False, True])
+def test_append_plan_matches_reference(causal, det):
+    rng = np.random.default_rng(7)
+    ps = 16
+    prefix = rng.integers(0, 2000, 12)
+    qo = rng.integers(0, 130, 12)
+    qo[3] = 0
+    lens = prefix + qo
+    indptr, L_ = _decode_host(lens, ps)
+    qo_indptr = _indptr(qo)
+    p = host_plan("append", indptr, L_, 32, 8, 128, ps, qo_indptr=qo_indptr, causal=causal,
+                  deterministic=det, det_chunk_pages=8, num_cus=4, workers_per_cu=8)
+    info = p.info()
+    ref = plan_ref("append", 32, 8, ps, indptr, L_, 32, [info["levels"][0]["rows_per_block"]],
+                   deterministic=det, det_chunk_pages=8, min_chunk_pages=8, qo_indptr=qo_indptr,
+                   causal=causal)
+    compare(info, ref)
+    assert info["num_scatter"] == int(qo.sum())
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_cascade_plan_matches_reference(det):
+    rng = np.random.default_rng(11)
+    ps = 16
+    suf = list(rng.integers(0, 900, 30)) + [0]
+    groups = list(rng.integers(-1, 3, 31))
+    pref = [8192, 100, 0]
+    indptr, L_ = _decode_host(suf, ps)
+    pindptr, PL = _decode_host(pref, ps)
+    p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
+                  req_prefix_group=groups, deterministic=det, num_cus=16, workers_per_cu=4)
+    info = p.info()
+    rpb = [lv["rows_per_block"] for lv in info["levels"]]
+    ref = plan_ref("cascade", 32, 8, ps, indptr, L_, 64, rpb, deterministic=det,
+                   det_chunk_pages=64, min_chunk_pages=8, prefix_indptr=pindptr, prefix_len=PL,
+                   req_group=groups)
+    compare(info, ref)
+
+
+def test_workspace_bound_covers_plans():
+    rng = np.random.default_rng(3)
+    for trial in range(20):
+        ps = int(rng.choice([8, 16, 32]))
+        B = int(rng.integers(1, 60))
+        kind = ["decode", "append", "cascade"][trial % 3]
+        det = bool(trial % 2)
+        lens = rng.integers(0, 5000, B)
+        qo = np.minimum(lens, rng.integers(0, 100, B))
+        if kind == "append":
+            pass
+        indptr, L_ = _decode_host(lens, ps)
+        kw = dict(deterministic=det, det_chunk_pages=int(rng.integers(1, 80)), num_cus=9,
+                  workers_per_cu=3)
+        n_q = 0
+        n_p = 0
+        if kind == "append":
+            kw.update(qo_indptr=_indptr(qo), causal=True)
+            n_q = int(qo.sum())
+        if kind == "cascade":
+            pref = [int(x) for x in rng.integers(0, 4000, 2)]
+            pi, pl = _decode_host(pref, ps)
+            kw.update(prefix_indptr=pi, prefix_len=pl,
+                      req_prefix_group=rng.integers(-1, 2, B))
+            n_p = int(pi[-1])
+        p = host_plan(kind, indptr, L_, 32, 8, 128, ps, **kw)
+        info = p.info()
+        desc = L.PlanDesc(kind={"decode": 0, "append": 1, "cascade": 2}[kind], batch=B,
+                          num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=ps,
+                          causal=1, deterministic=int(det), det_chunk_pages=kw["det_chunk_pages"],
+                          num_cus=9, workers_per_cu=3,
+                          num_prefix_groups=2 if kind == "cascade" else 0)
+        dev, host = fi.Workspace.bound(desc, int(indptr[-1]), n_q, n_p)
+        assert dev >= info["dev_bytes_used"], (trial, kind)
+        assert host >= info["host_bytes_used"], (trial, kind)
+
+
+# ---------------------------------------------------------------------------
+# host-detectable errors
+
+
+def _raw_plan(desc, indptr, lens, qo=None, pindptr=None, plen=None, grp=None):
+    lib = fi.load()
+    h = ctypes.c_void_p()
+    arr = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.int32)  # noqa: E731
+    keep = [arr(x) for x in (indptr, lens, qo, pindptr, plen, grp)]
+    ptrs = [None if a is None else a.ctypes.data_as(L.I32P) for a in keep]
+    st = lib.fi_plan(ctypes.byref(desc), *ptrs, None, 0, None, 0, None, ctypes.byref(h))
+    if st == 0:
+        lib.fi_plan_destroy(h)
+    return st, lib.fi_last_error().decode()
+
+
+def _desc(**kw):
+    base = dict(kind=0, batch=2, num_qo_heads=8, num_kv_heads=2, head_dim=128, page_size=16,
+                num_cus=4)
+    base.update(kw)
+    return L.PlanDesc(**base)
+
+
+GOOD_INDPTR = [0, 1, 3]
+GOOD_LENS = [10, 20]
+
+
+@pytest.mark.parametrize("desc_kw,code", [
+    (dict(head_dim=96), L.FI_ERR_UNSUPPORTED),
+    (dict(page_size=12), L.FI_ERR_UNSUPPORTED),
+    (dict(page_size=4), L.FI_ERR_UNSUPPORTED),
+    (dict(num_qo_heads=6, num_kv_heads=4), L.FI_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), L.FI_ERR_INVALID_ARG),
+    (dict(kind=7), L.FI_ERR_INVALID_ARG),
+    (dict(batch=-1), L.FI_ERR_INVALID_ARG),
+    (dict(num_cus=0), L.FI_ERR_INVALID_ARG),       # host-only plan needs num_cus
+    (dict(det_chunk_pages=-2), L.FI_ERR_INVALID_ARG),
+])
+def test_plan_rejects_bad_desc(desc_kw, code):
+    st, msg = _raw_plan(_desc(**desc_kw), GOOD_INDPTR, GOOD_LENS)
+    assert st == code, msg
+    assert msg
+
+
+@pytest.mark.parametrize("indptr,lens", [
+    ([1, 2, 4], [10, 20]),        # indptr[0] != 0
+    ([0, 1, 2], [10, 20]),        # 20 tokens need 2 pages
+    ([0, 2, 4], [10, 20]),        # 10 tokens need 1 page
+    ([0, 1, 3], [10, -1]),        # negative length
+])
+def test_plan_rejects_inconsistent_tables(indptr, lens):
+    st, msg = _raw_plan(_desc(), indptr, lens)
+    assert st == L.FI_ERR_INVALID_ARG, msg
+
+
+def test_append_rejects_qo_longer_than_kv():
+    st, msg = _raw_plan(_desc(kind=1), GOOD_INDPTR, GOOD_LENS, qo=[0, 11, 32])
+    assert st == L.FI_ERR_INVALID_ARG and "qo" in msg
+    st, _ = _raw_plan(_desc(kind=1), GOOD_INDPTR, GOOD_LENS, qo=None)
+    assert st == L.FI_ERR_INVALID_ARG
+
+
+def test_cascade_rejects_bad_group_and_grouping():
+    d = _desc(kind=2, num_prefix_groups=1)
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS, pindptr=[0, 2], plen=[32], grp=[0, 1])
+    assert st == L.FI_ERR_INVALID_ARG, msg
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS, pindptr=[0, 2], plen=[32], grp=[0, -1])
+    assert st == L.FI_OK, msg
+    d = _desc(kind=2, num_prefix_groups=1, num_qo_heads=24, num_kv_heads=1)   # G = 24
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS, pindptr=[0, 2], plen=[32], grp=[0, -1])
+    assert st == L.FI_ERR_UNSUPPORTED, msg
+
+
+def test_run_calls_refuse_without_device_plan():
+    lib = fi.load()
+    assert lib.fi_paged_decode(None, None, None, None, None, 1.0, None, None, None) == \
+        L.FI_ERR_PLAN_MISMATCH
+    p = host_plan("decode", GOOD_INDPTR, GOOD_LENS, 8, 2, 128, 16, num_cus=2)
+    st = lib.fi_paged_decode(p.handle, None, None, None, None, 1.0, None, None, None)
+    assert st == L.FI_ERR_PLAN_MISMATCH and "host-only" in lib.fi_last_error().decode()
+    st = lib.fi_cascade(p.handle, None, None, None, None, None, 1.0, None, None, None)
+    assert st == L.FI_ERR_PLAN_MISMATCH
+
+
+def test_merge_states_rejects_bad_shapes():
+    lib = fi.load()
+    assert lib.fi_merge_states(None, 0, None, 1, 1, 1, 6, None, 0, None, None) == \
+        L.FI_ERR_UNSUPPORTED
+    assert lib.fi_merge_states(None, 3, None, 1, 1, 1, 8, None, 0, None, None) == \
+        L.FI_ERR_INVALID_ARG
+    assert lib.fi_merge_states(None, 0, None, -1, 1, 1, 8, None, 0, None, None) == \
+        L.FI_ERR_INVALID_ARG
+    # empty problem is a no-op, no launch
+    assert lib.fi_merge_states(None, 0, None, 0, 3, 4, 8, None, 0, None, None) == L.FI_OK
+
+
+def test_workspace_size_rejects_bad_input():
+    lib = fi.load()
+    dev, host = ctypes.c_size_t(), ctypes.c_size_t()
+    d = _desc()
+    assert lib.fi_workspace_size(ctypes.byref(d), -1, 0, 0, ctypes.byref(dev),
+                                 ctypes.byref(host)) == L.FI_ERR_INVALID_ARG
+    assert lib.fi_workspace_size(None, 1, 0, 0, ctypes.byref(dev), ctypes.byref(host)) == \
+        L.FI_ERR_INVALID_ARG
+    d = _desc(head_dim=256)
+    assert lib.fi_workspace_size(ctypes.byref(d), 1, 0, 0, ctypes.byref(dev),
+                                 ctypes.byref(host)) == L.FI_ERR_UNSUPPORTED

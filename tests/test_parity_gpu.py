@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Full-size configurations are compared on sampled requests (the oracle computes
+each request independently); small cases are compared in full. Every case is
+seeded; inputs are poisoned (NaN in unused pages, 1e4 in tail slots, NaN in
+not-yet-written append slots) so that a stray read shows up in the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_amd as fi
+from tests.helpers import (compare, gpu_decode, np_pools, oracle_decode, request_rows,
+                           sample_requests)
+from workloads import cascade_flat_tables, make_append, make_cascade, make_config, make_decode
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev(gpu):
+    return gpu
+
+
+@pytest.fixture(scope="module")
+def cfg1():
+    return make_config(1, poison=True)
+
+
+# ---------------------------------------------------------------- configs
+
+
+def test_tiny_decode_config(dev):
+    w = make_config(0, poison=True)
+    o, lse, _ = gpu_decode(w, dev)
+    o_ref, l_ref = oracle_decode(w)
+    compare(o, lse, o_ref, l_ref, what="tiny_decode")
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_llama_decode_config_sampled(dev, cfg1, det):
+    w = cfg1
+    o, lse, p = gpu_decode(w, dev, deterministic=det)
+    rng = np.random.default_rng(1)
+    reqs = sample_requests(w.batch, 10, rng, must=[int(torch.argmax(w.kv_len))])
+    o_ref, l_ref = oracle_decode(w, requests=reqs)
+    compare(o, lse, o_ref, l_ref, rows=request_rows(reqs), what=f"llama_decode det={det}")
+
+
+def test_skewed_decode_config_sampled(dev):
+    w = make_config(2, poison=True)
+    o, lse, p = gpu_decode(w, dev)
+    long = [int(i) for i in torch.nonzero(w.kv_len == 32768).flatten()]
+    assert len(long) >= 4
+    rng = np.random.default_rng(2)
+    reqs = sample_requests(w.batch, 6, rng, must=long + [int(torch.argmin(w.kv_len))])
+    o_ref, l_ref = oracle_decode(w, requests=reqs)
+    compare(o, lse, o_ref, l_ref, rows=request_rows(reqs), what="skewed_decode")
+    assert max(p.info()["levels"][0]["items"][:, 11]) > 0, "long requests were not split"
+
+
+def _cascade_run(w, dev, **kw):
+    p = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                w.page_size, prefix_indptr=w.prefix_indptr, prefix_len=w.prefix_len,
+                req_prefix_group=w.req_prefix_group, device=dev, **kw)
+    g = w.to(dev)
+    o, lse = fi.cascade(p, g.q, g.k_cache, g.v_cache, g.prefix_indices, g.kv_indices, w.sm_scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _oracle_cascade(w, reqs):
+    kp, vp = np_pools(w)
+    return oracle.cascade_flat(w.q.double().numpy(), kp, vp, w.prefix_indptr.numpy(),
+                               w.prefix_indices.numpy(), w.prefix_len.numpy(),
+                               w.req_prefix_group.numpy(), w.kv_indptr.numpy(),
+                               w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size, w.sm_scale,
+                               requests=reqs)
+
+
+def test_cascade_config_sampled(dev):
+    w = make_config(3, poison=True)
+    o, lse = _cascade_run(w, dev)
+    rng = np.random.default_rng(3)
+    reqs = sample_requests(w.batch, 8, rng)
+    o_ref, l_ref = _oracle_cascade(w, reqs)
+    compare(o, lse, o_ref, l_ref, rows=request_rows(reqs), what="cascade")
+    # cascade equals flat decode over the concatenated table (both on the GPU)
+    ip, ix, ln = cascade_flat_tables(w)
+    p = fi.Plan("decode", ip, ln, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                device=dev)
+    g = w.to(dev)
+    of, lf = fi.paged_decode(p, g.q, g.k_cache, g.v_cache, ix.to(dev), w.sm_scale)
+    compare(of, lf, o_ref, l_ref, rows=request_rows(reqs), what="flat decode of cascade input")
+
+
+def test_append_config_sampled(dev):
+    w = make_config(4, poison=True)
+    p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev)
+    g = w.to(dev)
+    o, lse = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale,
+                             k_new=g.k_new, v_new=g.v_new)
+    torch.cuda.synchronize()
+    kp, vp = np_pools(w)
+    kp2, vp2 = oracle.scatter_new_kv(kp, vp, w.k_new.float().numpy(), w.v_new.float().numpy(),
+                                     w.qo_indptr.numpy(), w.kv_indptr.numpy(),
+                                     w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size)
+    # scatter is a bit-exact copy; every other pool byte is unchanged
+    assert np.array_equal(g.k_cache.float().cpu().numpy(), kp2, equal_nan=True)
+    assert np.array_equal(g.v_cache.float().cpu().numpy(), vp2, equal_nan=True)
+    rng = np.random.default_rng(4)
+    reqs = sample_requests(w.batch, 4, rng, must=[int(torch.argmax(w.qo_indptr.diff()))])
+    o_ref, l_ref = oracle.paged_append(w.q.double().numpy(), w.qo_indptr.numpy(), kp2, vp2,
+                                       w.kv_indptr.numpy(), w.kv_indices.numpy(),
+                                       w.kv_len.numpy(), w.page_size, w.sm_scale, causal=True,
+                                       requests=reqs)
+    rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in reqs])
+    compare(o, lse, o_ref, l_ref, rows=rows, what="append")
+
+
+# ---------------------------------------------------------------- small sweeps
+
+SMALL_LENS = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 517, 1000]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("G", [1, 4, 8, 24])
+def test_decode_small_sweep(dev, D, ps, G):
+    Hkv = 2
+    w = make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=100 + D + ps + G)
+    o_ref, l_ref = oracle_decode(w)
+    plans = [dict(), dict(deterministic=True, det_chunk_pages=1),
+             dict(deterministic=True, det_chunk_pages=3), dict(min_chunk_pages=1)]
+    for kw in plans:
+        o, lse, _ = gpu_decode(w, dev, **kw)
+        compare(o, lse, o_ref, l_ref, what=f"decode D={D} ps={ps} G={G} {kw}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 2), (128, 32, 8), (64, 16, 24)])
+def test_append_small_sweep(dev, causal, D, ps, G):
+    prefix = [0, 5, 16, 40, 300, 1]
+    qo = [1, 3, 17, 40, 70, 33]
+    Hkv = 2
+    w = make_append(prefix, qo, G * Hkv, Hkv, D, ps, seed=200 + D + ps + G, causal=causal)
+    kp, vp = np_pools(w)
+    kp2, vp2 = oracle.scatter_new_kv(kp, vp, w.k_new.float().numpy(), w.v_new.float().numpy(),
+                                     w.qo_indptr.numpy(), w.kv_indptr.numpy(),
+                                     w.kv_indices.numpy(), w.kv_len.numpy(), ps)
+    o_ref, l_ref = oracle.paged_append(w.q.double().numpy(), w.qo_indptr.numpy(), kp2, vp2,
+                                       w.kv_indptr.numpy(), w.kv_indices.numpy(),
+                                       w.kv_len.numpy(), ps, w.sm_scale, causal=causal)
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+        g = w.to(dev)
+        p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, Hkv, D, ps,
+                    qo_indptr=w.qo_indptr, causal=causal, device=dev, **kw)
+        o, lse = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale,
+                                 k_new=g.k_new, v_new=g.v_new)
+        torch.cuda.synchronize()
+        compare(o, lse, o_ref, l_ref, what=f"append causal={causal} D={D} ps={ps} G={G} {kw}")
+
+
+def test_cascade_small_multi_group(dev):
+    ps = 16
+    w = make_cascade([64, 40, 0], [0, 1, 1, -1, 2, 0, 1, 0], [5, 0, 40, 33, 16, 1, 300, 17],
+                     32, 8, 128, ps, seed=300)
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+        o, lse = _cascade_run(w, dev, **kw)
+        o_ref, l_ref = _oracle_cascade(w, None)
+        compare(o, lse, o_ref, l_ref, what=f"cascade groups {kw}")
+
+
+# ---------------------------------------------------------------- invariants
+
+
+def test_pool_permutation_is_bit_identical(dev):
+    w = make_decode([700, 33, 2048, 5, 1500], 32, 8, 128, 16, seed=400)
+    o1, l1, _ = gpu_decode(w, dev, min_chunk_pages=2)
+    P = w.num_pages
+    perm = torch.randperm(P, generator=torch.Generator().manual_seed(5))
+    k2 = torch.empty_like(w.k_cache)
+    v2 = torch.empty_like(w.v_cache)
+    k2[perm] = w.k_cache
+    v2[perm] = w.v_cache
+    w2 = make_decode([1], 32, 8, 128, 16, seed=1)   # container, fields replaced below
+    w2.kv_len, w2.kv_indptr, w2.q = w.kv_len, w.kv_indptr, w.q
+    w2.kv_indices = perm[w.kv_indices.long()].to(torch.int32)
+    w2.k_cache, w2.v_cache = k2, v2
+    o2, l2, _ = gpu_decode(w2, dev, min_chunk_pages=2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_repeat_runs_are_bit_identical(dev, cfg1):
+    for det in (False, True):
+        o1, l1, _ = gpu_decode(cfg1, dev, deterministic=det)
+        o2, l2, _ = gpu_decode(cfg1, dev, deterministic=det)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), det
+
+
+def _sub_batch(w, reqs):
+    """Decode workload with the requests ``reqs`` of ``w`` (same pool)."""
+    ptr, idx = [0], []
+    for r in reqs:
+        a, b = int(w.kv_indptr[r]), int(w.kv_indptr[r + 1])
+        idx.append(w.kv_indices[a:b])
+        ptr.append(ptr[-1] + (b - a))
+    sub = make_decode([1], w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, seed=1)
+    sub.kv_len = w.kv_len[list(reqs)].clone()
+    sub.kv_indptr = torch.tensor(ptr, dtype=torch.int32)
+    sub.kv_indices = torch.cat(idx).to(torch.int32)
+    sub.q = w.q[list(reqs)].clone()
+    sub.k_cache, sub.v_cache = w.k_cache, w.v_cache
+    return sub
+
+
+def test_deterministic_mode_is_batch_invariant(dev):
+    rng = np.random.default_rng(6)
+    lens = [5000] + list(rng.integers(1, 9000, 63))
+    w = make_decode(lens, 32, 8, 128, 16, seed=500, poison=False)
+    target = 0
+    outs = []
+    for reqs in ([target], [3, target, 9, 4], [9, 5, target],
+                 list(rng.permutation(64))):
+        sub = _sub_batch(w, [int(r) for r in reqs])
+        pos = [int(r) for r in reqs].index(target)
+        o, lse, _ = gpu_decode(sub, dev, deterministic=True, det_chunk_pages=16)
+        outs.append((o[pos].clone(), lse[pos].clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    o_ref, l_ref = oracle_decode(w, requests=[target])
+    compare(outs[0][0][None], outs[0][1][None], o_ref[[target]], l_ref[[target]],
+            what="batch-invariant target vs oracle")
+
+
+@pytest.mark.parametrize("ps", [8, 16, 32])
+def test_needle_keys_are_gathered_exactly(dev, ps):
+    lens = [100, 37, 16, 300, 64]
+    w = make_decode(lens, 8, 2, 128, ps, seed=600 + ps)
+    needles = [0, 36, 15, 257, 32]        # positions across page boundaries
+    q = torch.zeros_like(w.q)
+    q[:, :, 0] = 8.0
+    w.q = q
+    for r, t in enumerate(needles):
+        page = int(w.kv_indices[int(w.kv_indptr[r]) + t // ps])
+        w.k_cache[page, :, t % ps, 0] = 100.0
+    o, lse, _ = gpu_decode(w, dev, min_chunk_pages=1)
+    o = o.cpu()
+    for r, t in enumerate(needles):
+        page = int(w.kv_indices[int(w.kv_indptr[r]) + t // ps])
+        for h in range(8):
+            assert torch.equal(o[r, h], w.v_cache[page, h // 4, t % ps]), (r, h)
+
+
+def test_append_single_query_matches_decode(dev):
+    w = make_decode([3, 40, 77, 1000, 2500], 32, 8, 128, 16, seed=700)
+    od, ld, _ = gpu_decode(w, dev)
+    p = fi.Plan("append", w.kv_indptr, w.kv_len, 32, 8, 128, 16,
+                qo_indptr=torch.arange(6, dtype=torch.int32), causal=True, device=dev)
+    g = w.to(dev)
+    oa, la = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle_decode(w)
+    compare(od, ld, o_ref, l_ref, what="decode")
+    compare(oa, la, o_ref, l_ref, what="append with one query per request")
+
+
+def test_empty_batch_and_empty_requests(dev):
+    w = make_decode([0, 0, 5, 0], 8, 2, 64, 16, seed=800)
+    o, lse, _ = gpu_decode(w, dev)
+    assert torch.all(o[[0, 1, 3]] == 0) and torch.all(torch.isneginf(lse[[0, 1, 3]]))
+    p = fi.Plan("decode", [0], [], 8, 2, 64, 16, device=dev)
+    q = torch.empty(0, 8, 64, dtype=torch.bfloat16, device=dev)
+    o, lse = fi.paged_decode(p, q, w.k_cache.to(dev), w.v_cache.to(dev),
+                             torch.zeros(1, dtype=torch.int32, device=dev), w.sm_scale)
+    torch.cuda.synchronize()
+    assert o.numel() == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_merge_states_api(dev, dtype):
+    g = torch.Generator().manual_seed(9)
+    N, S, H, D = 6, 7, 3, 128
+    v = torch.randn(N, S, H, D, generator=g).to(dtype)
+    s = torch.randn(N, S, H, generator=g) * 4
+    s[0, :, 1] = -float("inf")        # all states empty for one row
+    s[1, 2:5, 0] = -float("inf")      # some empty
+    vo, so = fi.merge_states(v.to(dev), s.to(dev), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.merge_states(v.double().numpy(), s.double().numpy())
+    assert np.allclose(vo.cpu().numpy(), o_ref, atol=2e-6, rtol=2e-6)
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(so.cpu().numpy()), ~fin)
+    assert np.allclose(so.cpu().numpy()[fin], l_ref[fin], atol=1e-5, rtol=1e-6)
+    assert torch.all(vo[0, 1] == 0)
