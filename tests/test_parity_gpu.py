@@ -35,8 +35,8 @@ def cfg1():
 def test_tiny_decode_config(dev):
     w = make_config(0, poison=True)
     o, lse, _ = gpu_decode(w, dev)
-    o_ref, l_ref = oracle_decode(w)
-    compare(o, lse, o_ref, l_ref, what="tiny_decode")
+    o_ref, l_ref, a_ref = oracle_decode(w)
+    compare(o, lse, o_ref, l_ref, a_ref, what="tiny_decode")
 
 
 @pytest.mark.parametrize("det", [False, True])
@@ -45,8 +45,8 @@ def test_llama_decode_config_sampled(dev, cfg1, det):
     o, lse, p = gpu_decode(w, dev, deterministic=det)
     rng = np.random.default_rng(1)
     reqs = sample_requests(w.batch, 10, rng, must=[int(torch.argmax(w.kv_len))])
-    o_ref, l_ref = oracle_decode(w, requests=reqs)
-    compare(o, lse, o_ref, l_ref, rows=request_rows(reqs), what=f"llama_decode det={det}")
+    o_ref, l_ref, a_ref = oracle_decode(w, requests=reqs)
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"llama_decode det={det}")
 
 
 def test_skewed_decode_config_sampled(dev):
@@ -56,8 +56,8 @@ def test_skewed_decode_config_sampled(dev):
     assert len(long) >= 4
     rng = np.random.default_rng(2)
     reqs = sample_requests(w.batch, 6, rng, must=long + [int(torch.argmin(w.kv_len))])
-    o_ref, l_ref = oracle_decode(w, requests=reqs)
-    compare(o, lse, o_ref, l_ref, rows=request_rows(reqs), what="skewed_decode")
+    o_ref, l_ref, a_ref = oracle_decode(w, requests=reqs)
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what="skewed_decode")
     assert max(p.info()["levels"][0]["items"][:, 11]) > 0, "long requests were not split"
 
 
@@ -73,11 +73,13 @@ def _cascade_run(w, dev, **kw):
 
 def _oracle_cascade(w, reqs):
     kp, vp = np_pools(w)
-    return oracle.cascade_flat(w.q.double().numpy(), kp, vp, w.prefix_indptr.numpy(),
-                               w.prefix_indices.numpy(), w.prefix_len.numpy(),
-                               w.req_prefix_group.numpy(), w.kv_indptr.numpy(),
-                               w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size, w.sm_scale,
-                               requests=reqs)
+    q = w.q.double().numpy()
+    tabs = (w.prefix_indptr.numpy(), w.prefix_indices.numpy(), w.prefix_len.numpy(),
+            w.req_prefix_group.numpy(), w.kv_indptr.numpy(), w.kv_indices.numpy(),
+            w.kv_len.numpy(), w.page_size, w.sm_scale)
+    o, lse = oracle.cascade_flat(q, kp, vp, *tabs, requests=reqs)
+    a, _ = oracle.cascade_flat(q, kp, np.abs(vp), *tabs, requests=reqs)
+    return o, lse, a
 
 
 def test_cascade_config_sampled(dev):
@@ -85,15 +87,16 @@ def test_cascade_config_sampled(dev):
     o, lse = _cascade_run(w, dev)
     rng = np.random.default_rng(3)
     reqs = sample_requests(w.batch, 8, rng)
-    o_ref, l_ref = _oracle_cascade(w, reqs)
-    compare(o, lse, o_ref, l_ref, rows=request_rows(reqs), what="cascade")
+    o_ref, l_ref, a_ref = _oracle_cascade(w, reqs)
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what="cascade")
     # cascade equals flat decode over the concatenated table (both on the GPU)
     ip, ix, ln = cascade_flat_tables(w)
     p = fi.Plan("decode", ip, ln, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
                 device=dev)
     g = w.to(dev)
     of, lf = fi.paged_decode(p, g.q, g.k_cache, g.v_cache, ix.to(dev), w.sm_scale)
-    compare(of, lf, o_ref, l_ref, rows=request_rows(reqs), what="flat decode of cascade input")
+    compare(of, lf, o_ref, l_ref, a_ref, rows=request_rows(reqs),
+            what="flat decode of cascade input")
 
 
 def test_append_config_sampled(dev):
@@ -113,12 +116,20 @@ def test_append_config_sampled(dev):
     assert np.array_equal(g.v_cache.float().cpu().numpy(), vp2, equal_nan=True)
     rng = np.random.default_rng(4)
     reqs = sample_requests(w.batch, 4, rng, must=[int(torch.argmax(w.qo_indptr.diff()))])
-    o_ref, l_ref = oracle.paged_append(w.q.double().numpy(), w.qo_indptr.numpy(), kp2, vp2,
-                                       w.kv_indptr.numpy(), w.kv_indices.numpy(),
-                                       w.kv_len.numpy(), w.page_size, w.sm_scale, causal=True,
-                                       requests=reqs)
+    o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, True, reqs)
     rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in reqs])
-    compare(o, lse, o_ref, l_ref, rows=rows, what="append")
+    compare(o, lse, o_ref, l_ref, a_ref, rows=rows, what="append")
+
+
+def _oracle_append(w, kp2, vp2, causal, reqs=None):
+    q = w.q.double().numpy()
+    tabs = (w.kv_indptr.numpy(), w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size,
+            w.sm_scale)
+    o, lse = oracle.paged_append(q, w.qo_indptr.numpy(), kp2, vp2, *tabs, causal=causal,
+                                 requests=reqs)
+    a, _ = oracle.paged_append(q, w.qo_indptr.numpy(), kp2, np.abs(vp2), *tabs, causal=causal,
+                               requests=reqs)
+    return o, lse, a
 
 
 # ---------------------------------------------------------------- small sweeps
@@ -132,12 +143,12 @@ SMALL_LENS = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 517, 1000]
 def test_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
     w = make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=100 + D + ps + G)
-    o_ref, l_ref = oracle_decode(w)
+    o_ref, l_ref, a_ref = oracle_decode(w)
     plans = [dict(), dict(deterministic=True, det_chunk_pages=1),
              dict(deterministic=True, det_chunk_pages=3), dict(min_chunk_pages=1)]
     for kw in plans:
         o, lse, _ = gpu_decode(w, dev, **kw)
-        compare(o, lse, o_ref, l_ref, what=f"decode D={D} ps={ps} G={G} {kw}")
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"decode D={D} ps={ps} G={G} {kw}")
 
 
 @pytest.mark.parametrize("causal", [True, False])
@@ -151,9 +162,7 @@ def test_append_small_sweep(dev, causal, D, ps, G):
     kp2, vp2 = oracle.scatter_new_kv(kp, vp, w.k_new.float().numpy(), w.v_new.float().numpy(),
                                      w.qo_indptr.numpy(), w.kv_indptr.numpy(),
                                      w.kv_indices.numpy(), w.kv_len.numpy(), ps)
-    o_ref, l_ref = oracle.paged_append(w.q.double().numpy(), w.qo_indptr.numpy(), kp2, vp2,
-                                       w.kv_indptr.numpy(), w.kv_indices.numpy(),
-                                       w.kv_len.numpy(), ps, w.sm_scale, causal=causal)
+    o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, causal)
     for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
         g = w.to(dev)
         p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, Hkv, D, ps,
@@ -161,7 +170,8 @@ def test_append_small_sweep(dev, causal, D, ps, G):
         o, lse = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale,
                                  k_new=g.k_new, v_new=g.v_new)
         torch.cuda.synchronize()
-        compare(o, lse, o_ref, l_ref, what=f"append causal={causal} D={D} ps={ps} G={G} {kw}")
+        compare(o, lse, o_ref, l_ref, a_ref,
+                what=f"append causal={causal} D={D} ps={ps} G={G} {kw}")
 
 
 def test_cascade_small_multi_group(dev):
@@ -170,8 +180,8 @@ def test_cascade_small_multi_group(dev):
                      32, 8, 128, ps, seed=300)
     for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
         o, lse = _cascade_run(w, dev, **kw)
-        o_ref, l_ref = _oracle_cascade(w, None)
-        compare(o, lse, o_ref, l_ref, what=f"cascade groups {kw}")
+        o_ref, l_ref, a_ref = _oracle_cascade(w, None)
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"cascade groups {kw}")
 
 
 # ---------------------------------------------------------------- invariants
@@ -231,9 +241,9 @@ def test_deterministic_mode_is_batch_invariant(dev):
         outs.append((o[pos].clone(), lse[pos].clone()))
     for o, l in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
-    o_ref, l_ref = oracle_decode(w, requests=[target])
+    o_ref, l_ref, a_ref = oracle_decode(w, requests=[target])
     compare(outs[0][0][None], outs[0][1][None], o_ref[[target]], l_ref[[target]],
-            what="batch-invariant target vs oracle")
+            a_ref[[target]], what="batch-invariant target vs oracle")
 
 
 @pytest.mark.parametrize("ps", [8, 16, 32])
@@ -263,9 +273,9 @@ def test_append_single_query_matches_decode(dev):
     g = w.to(dev)
     oa, la = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale)
     torch.cuda.synchronize()
-    o_ref, l_ref = oracle_decode(w)
-    compare(od, ld, o_ref, l_ref, what="decode")
-    compare(oa, la, o_ref, l_ref, what="append with one query per request")
+    o_ref, l_ref, a_ref = oracle_decode(w)
+    compare(od, ld, o_ref, l_ref, a_ref, what="decode")
+    compare(oa, la, o_ref, l_ref, a_ref, what="append with one query per request")
 
 
 def test_empty_batch_and_empty_requests(dev):
