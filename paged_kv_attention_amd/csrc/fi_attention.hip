@@ -5,27 +5,35 @@
 // token range of one sequence, reading K/V through the block table (research
 // note "flashinfer-backend-selection", "Arithmetic intensity": decode reads a
 // gathered block table instead of a dense cache). Each wavefront is one
-// persistent worker that runs the items the plan gave it, in order.
+// persistent worker that runs the items the plan gave it, in order, as one
+// continuous stream of 32-token steps: the loads of step n+1 (possibly the
+// first step of the next item) are in flight while step n is computed.
 //
-// Tiling. One step covers 32 tokens. Both contractions run on the bf16 MFMA
-// v_mfma_f32_16x16x32_bf16 with fp32 accumulation:
+// Tiling. Both contractions run on the bf16 MFMA v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation:
 //   S^T[token][row] = K[token][:] . Q[row][:]    A = K tile, B = Q^T
 //   O^T[d][row]    += V^T[d][token] . P^T[token][row]
 // With both outputs transposed, the query row sits in lane%16 of every
 // accumulator, so the softmax statistics and the rescale of O stay in-lane;
 // only the row max and the final row sum cross the four 16-lane groups.
-// Lane l loads K of token 16*blk + l%16 (64 contiguous bytes per 4 lanes) and
-// V of 8 tokens (a full 16-lane row of 256 B per instruction). The V rows are
-// transposed in registers with v_perm_b32 into the MFMA A layout; the token
-// order inside a lane group (4g..4g+3, 16+4g..16+4g+3) is the same one the
-// S^T accumulator hands to P, so P needs no shuffle at all.
+// Lane l loads K of token 16*blk + l%16 (4 lanes read 64 contiguous bytes of a
+// row) and V of 8 tokens (16 lanes read a full 256-byte row per instruction).
+// The V rows are transposed in registers with v_perm_b32 into the MFMA A
+// layout; the token order inside a lane group (4g..4g+3, 16+4g..16+4g+3) is the
+// one the S^T accumulator hands to P, so P needs no shuffle.
+//
+// Pages. NP = pages one 32-token step touches (4 for page size 8, 2 for 16, 1
+// for >= 32). The step's page ids are wave-uniform scalars; which of them a
+// lane's token uses is fixed at compile time up to one lane bit, so every
+// load is a uniform 64-bit page-tile base plus a 32-bit lane offset. Pages
+// past the item's last page are clamped to it, so every address is valid and
+// the loads are unconditional; V of tokens past the end is zeroed by a
+// select, and their logits are masked to -inf.
 //
 // Softmax is online (running max m, running sum l, O rescaled by
 // exp2(m_old - m_new)) with logits pre-scaled by sm_scale*log2(e); the LSE is
 // returned in natural log. P is rounded to bf16 for the P.V MFMA; l sums the
-// fp32 P. Keys past the item's end (tail slots of the last page) and, under
-// the causal mask, keys after a query's position are masked to -inf and their
-// K/V are never loaded.
+// fp32 P. Under the causal mask a key after a query's position gets -inf.
 
 #include <hip/hip_runtime.h>
 #include <limits.h>
@@ -66,193 +74,253 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-template <int D, int MB>
-__device__ __forceinline__ void run_item(const AttnArgs& a, const int32_t* __restrict__ it,
-                                         const int lane) {
-  constexpr int KJ = D / 32;    // 32-dim k-slices of the q.K contraction
-  constexpr int DPL = D / 16;   // V dims per lane = P.V MFMAs per step
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Plan records and page tables are never written while a kernel runs; reading
+// them through the constant address space lets wave-uniform reads become
+// scalar loads, which do not queue behind the in-flight K/V vector loads.
+typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
+  return uniform(((const_i32p)p)[i]);
+}
+
+// Work item fields, all wave-uniform.
+struct Item {
+  int q_base, row0, n_rows, g, flags, t_begin, t_end, q_pos0, dst, nsteps;
+  const int32_t* plist;
+};
+
+__device__ __forceinline__ Item load_item(const AttnArgs& a, int i) {
+  const int32_t* it = a.items + (int64_t)i * ITEM_INTS;
+  Item r;
+  r.q_base = ld_uniform(it, F_Q_BASE);
+  r.row0 = ld_uniform(it, F_ROW0);
+  r.n_rows = ld_uniform(it, F_NROWS);
+  r.g = ld_uniform(it, F_KVHEAD);
+  r.flags = ld_uniform(it, F_FLAGS);
+  r.t_begin = ld_uniform(it, F_TBEGIN);
+  r.t_end = ld_uniform(it, F_TEND);
+  r.q_pos0 = ld_uniform(it, F_QPOS0);
+  r.dst = ld_uniform(it, F_DST);
+  r.nsteps = (r.t_end - r.t_begin + 31) >> 5;
+  r.plist = ((r.flags & FLAG_PREFIX) ? a.prefix_indices : a.kv_indices) + ld_uniform(it, F_PAGEOFF);
+  return r;
+}
+
+template <int D>
+struct Cfg {
+  static constexpr int KJ = D / 32;    // 32-dim k-slices of the q.K contraction
+  static constexpr int DPL = D / 16;   // V dims per lane = P.V MFMAs per step
   typedef typename RowVec<DPL / 2>::T vrow_t;
+};
 
-  const int q_base = it[F_Q_BASE], row0 = it[F_ROW0], n_rows = it[F_NROWS];
-  const int g = it[F_KVHEAD], page_off = it[F_PAGEOFF], flags = it[F_FLAGS];
-  const int t_begin = it[F_TBEGIN], t_end = it[F_TEND], q_pos0 = it[F_QPOS0];
-  const int dst = it[F_DST];
+template <int D>
+struct Tile {
+  u32x4 k[2][Cfg<D>::KJ];
+  typename Cfg<D>::vrow_t v[8];
+};
 
-  const int G = a.group, Hq = a.num_qo_heads, Hkv = a.num_kv_heads;
-  const int sh = a.page_shift, ps = a.page_size;
-  const int col = lane & 15;   // query row within a 16-row block
-  const int grp = lane >> 4;   // 16-lane group
-  const bool causal = (flags & FLAG_CAUSAL) != 0;
-  const int32_t* __restrict__ plist =
-      ((flags & FLAG_PREFIX) ? a.prefix_indices : a.kv_indices) + page_off;
+// Issue the loads of step s of item it into T.
+template <int D, int NP>
+__device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, int s, Tile<D>& T,
+                                           int col, int grp) {
+  constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL;
+  typedef typename Cfg<D>::vrow_t vrow_t;
+  const int sh = a.page_shift;
+  const int T0 = it.t_begin + 32 * s;
+  const int pb = T0 >> sh;
+  const int plast = (it.t_end - 1) >> sh;
+  const int64_t tile_elems = (int64_t)a.page_size * D;
+  const char* kb[NP];
+  const char* vb[NP];
+#pragma unroll
+  for (int n = 0; n < NP; ++n) {
+    const int pid = ld_uniform(it.plist, min(pb + n, plast));
+    const int64_t off = ((int64_t)pid * a.num_kv_heads + it.g) * tile_elems * 2;
+    kb[n] = (const char*)a.k_cache + off;
+    vb[n] = (const char*)a.v_cache + off;
+  }
+  const int slot0 = (NP == 1) ? (T0 & (a.page_size - 1)) : 0;
+  // K: token 16*blk + col
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const char* base;
+    int slot;
+    if (NP == 1) {
+      base = kb[0];
+      slot = slot0 + 16 * blk + col;
+    } else if (NP == 2) {
+      base = kb[blk];
+      slot = col;
+    } else {
+      base = (col >> 3) ? kb[2 * blk + 1] : kb[2 * blk];
+      slot = col & 7;
+    }
+    const uint32_t off = (uint32_t)(slot * D + grp * 8) * 2u;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) T.k[blk][j] = *(const u32x4*)(base + off + 64u * j);
+  }
+  // V: tokens 4*grp + i (i < 4) and 16 + 4*grp + (i - 4) (i >= 4)
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int tl = (i < 4) ? 4 * grp + i : 16 + 4 * grp + (i - 4);
+    const char* base;
+    int slot;
+    if (NP == 1) {
+      base = vb[0];
+      slot = slot0 + tl;
+    } else if (NP == 2) {
+      base = vb[i >> 2];
+      slot = tl & 15;
+    } else {
+      base = (grp >> 1) ? vb[2 * (i >> 2) + 1] : vb[2 * (i >> 2)];
+      slot = tl & 7;
+    }
+    const uint32_t off = (uint32_t)(slot * D + DPL * col) * 2u;
+    T.v[i] = *(const vrow_t*)(base + off);
+  }
+}
 
-  // ---- query rows of this item (B operand of the q.K MFMAs)
-  u32x4 qf[MB][KJ];
-  int qlim[MB];
+template <int D, int MB>
+__device__ __forceinline__ void load_q(const AttnArgs& a, const Item& it, u32x4 (&qf)[MB][Cfg<D>::KJ],
+                                       int col, int grp) {
+  const int G = a.group;
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    const int rl = mb * 16 + col;
-    const int rho = row0 + rl;
+    // Rows past n_rows (tile padding) read the item's first row: their
+    // results are never stored and MFMA rows do not mix.
+    const int rl = mb * 16 + col < it.n_rows ? mb * 16 + col : 0;
+    const int rho = it.row0 + rl;
     const int qi = rho / G, h = rho - qi * G;
-    const bool ok = rl < n_rows;
-    int tok = 0;
-    if (ok) tok = (flags & FLAG_LIST_Q) ? a.qlist[q_base + qi] : q_base + qi;
-    const uint16_t* qp = a.q + ((int64_t)tok * Hq + g * G + h) * D + grp * 8;
+    const int tok = (it.flags & FLAG_LIST_Q) ? a.qlist[it.q_base + qi] : it.q_base + qi;
+    const uint16_t* qp = a.q + ((int64_t)tok * a.num_qo_heads + it.g * G + h) * D + grp * 8;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *(const u32x4*)(qp + 32 * j);
-      qf[mb][j] = v;
-    }
-    qlim[mb] = causal ? q_pos0 + qi : INT_MAX;
+    for (int j = 0; j < Cfg<D>::KJ; ++j) qf[mb][j] = *(const u32x4*)(qp + 32 * j);
   }
+}
 
-  f32x4 acc[MB][DPL];
-  float m_run[MB], l_run[MB];
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    m_run[mb] = neg_inf();
-    l_run[mb] = 0.f;
-#pragma unroll
-    for (int m = 0; m < DPL; ++m) acc[mb][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
-  const int np = (32 >> sh) > 1 ? (32 >> sh) : 1;   // pages touched by one step
-  const int plast = (t_end - 1) >> sh;
-
-  auto load_step = [&](int s, u32x4 (&kf)[2][KJ], vrow_t (&vf)[8]) {
-    const int T0 = t_begin + 32 * s;
-    const int pbase = T0 >> sh;
-    int pid[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      pid[n] = 0;
-      if (n < np) pid[n] = plist[min(pbase + n, plast)];
-    }
-    auto page_of = [&](int t) {
-      const int rel = (t >> sh) - pbase;
-      return rel == 0 ? pid[0] : rel == 1 ? pid[1] : rel == 2 ? pid[2] : pid[3];
-    };
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int t = T0 + 16 * blk + col;
-      const int64_t tile = ((int64_t)page_of(t) * Hkv + g) * ps + (t & (ps - 1));
-      const uint16_t* kp = a.k_cache + tile * D + grp * 8;
-#pragma unroll
-      for (int j = 0; j < KJ; ++j) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (t < t_end) v = *(const u32x4*)(kp + 32 * j);
-        kf[blk][j] = v;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = T0 + (i < 4 ? 4 * grp + i : 16 + 4 * grp + (i - 4));
-      const int64_t tile = ((int64_t)page_of(t) * Hkv + g) * ps + (t & (ps - 1));
-      vrow_t v = {};
-      if (t < t_end) v = *(const vrow_t*)(a.v_cache + tile * D + DPL * col);
-      vf[i] = v;
-    }
-  };
-
-  auto compute = [&](int s, const u32x4 (&kf)[2][KJ], const vrow_t (&vf)[8]) {
-    const int T0 = t_begin + 32 * s;
-    // V^T operands: for MFMA m, lane supplies dim DPL*col+m of its 8 tokens.
-    u32x4 vt[DPL];
-#pragma unroll
-    for (int m = 0; m < DPL; ++m) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t lo = vf[2 * jj][m >> 1], hi = vf[2 * jj + 1][m >> 1];
-        vt[m][jj] = __builtin_amdgcn_perm(hi, lo, (m & 1) ? 0x07060302u : 0x05040100u);
-      }
-    }
+template <int D, int MB>
+struct State {
+  f32x4 acc[MB][Cfg<D>::DPL];
+  float m[MB], l[MB];
+  __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+      m[mb] = neg_inf();
+      l[mb] = 0.f;
 #pragma unroll
-      for (int j = 0; j < KJ; ++j) {
-        s0 = mfma_bf16(kf[0][j], qf[mb][j], s0);
-        s1 = mfma_bf16(kf[1][j], qf[mb][j], s1);
-      }
-      float x[8];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t0 = T0 + 4 * grp + r, t1 = t0 + 16;
-        x[r] = (t0 < t_end && t0 <= qlim[mb]) ? s0[r] * a.scale_log2 : neg_inf();
-        x[4 + r] = (t1 < t_end && t1 <= qlim[mb]) ? s1[r] * a.scale_log2 : neg_inf();
-      }
-      float mx = x[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[mb], mx);
-      const float base = (m_new == neg_inf()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run[mb] - base);
-      float p[8], psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = __builtin_amdgcn_exp2f(x[i] - base);
-        psum += p[i];
-      }
-      l_run[mb] = l_run[mb] * alpha + psum;
-      m_run[mb] = m_new;
-      const u32x4 pb = {pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]),
-                        pack2(p[6], p[7])};
-#pragma unroll
-      for (int m = 0; m < DPL; ++m) acc[mb][m] = mfma_bf16(vt[m], pb, acc[mb][m] * alpha);
-    }
-  };
-
-  const int nsteps = (t_end - t_begin + 31) >> 5;
-  u32x4 kA[2][KJ], kB[2][KJ];
-  vrow_t vA[8], vB[8];
-  if (nsteps > 0) load_step(0, kA, vA);
-  for (int s = 0; s < nsteps; s += 2) {
-    if (s + 1 < nsteps) load_step(s + 1, kB, vB);
-    compute(s, kA, vA);
-    if (s + 1 < nsteps) {
-      if (s + 2 < nsteps) load_step(s + 2, kA, vA);
-      compute(s + 1, kB, vB);
+      for (int d = 0; d < Cfg<D>::DPL; ++d) acc[mb][d] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
+};
 
-  // ---- finalize: o = acc / l, lse = (m + log2 l) * ln 2
+template <int D, int MB>
+__device__ __forceinline__ void compute_step(const AttnArgs& a, const Item& it, int s,
+                                             const Tile<D>& T, const u32x4 (&qf)[MB][Cfg<D>::KJ],
+                                             State<D, MB>& st, int col, int grp) {
+  constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL;
+  typedef typename Cfg<D>::vrow_t vrow_t;
+  const int T0 = it.t_begin + 32 * s;
+  const bool causal = (it.flags & FLAG_CAUSAL) != 0;
+  // V rows of tokens past the item's end hold whatever the clamped page has
+  // there (even NaN): zero them so that p = 0 cancels them exactly.
+  vrow_t vv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vv[i] = T.v[i];
+  if (T0 + 32 > it.t_end) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tl = (i < 4) ? 4 * grp + i : 16 + 4 * grp + (i - 4);
+      if (T0 + tl >= it.t_end) vv[i] = vrow_t{};
+    }
+  }
+  // V^T operands: for MFMA m, the lane supplies dim DPL*col+m of its 8 tokens.
+  u32x4 vt[DPL];
+#pragma unroll
+  for (int m = 0; m < DPL; ++m) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t lo = vv[2 * jj][m >> 1], hi = vv[2 * jj + 1][m >> 1];
+      vt[m][jj] = __builtin_amdgcn_perm(hi, lo, (m & 1) ? 0x07060302u : 0x05040100u);
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
-    float lt = l_run[mb];
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+      s0 = mfma_bf16(T.k[0][j], qf[mb][j], s0);
+      s1 = mfma_bf16(T.k[1][j], qf[mb][j], s1);
+    }
+    // last visible token for this lane's row
+    int lim = it.t_end - 1;
+    if (causal) lim = min(lim, it.q_pos0 + (it.row0 + mb * 16 + col) / a.group);
+    float x[8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t0 = T0 + 4 * grp + r;
+      x[r] = (t0 <= lim) ? s0[r] * a.scale_log2 : neg_inf();
+      x[4 + r] = (t0 + 16 <= lim) ? s1[r] * a.scale_log2 : neg_inf();
+    }
+    float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(st.m[mb], mx);
+    const float base = (m_new == neg_inf()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(st.m[mb] - base);
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - base);
+    st.l[mb] = st.l[mb] * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+    st.m[mb] = m_new;
+    const u32x4 pb = {pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
+#pragma unroll
+    for (int m = 0; m < DPL; ++m) st.acc[mb][m] = mfma_bf16(vt[m], pb, st.acc[mb][m] * alpha);
+  }
+}
+
+template <int D, int MB>
+__device__ __forceinline__ void finalize(const AttnArgs& a, const Item& it, const State<D, MB>& st,
+                                         int col, int grp) {
+  constexpr int DPL = Cfg<D>::DPL;
+  typedef typename Cfg<D>::vrow_t vrow_t;
+  const int G = a.group;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    float lt = st.l[mb];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     const int rl = mb * 16 + col;
-    if (rl >= n_rows) continue;
+    if (rl >= it.n_rows) continue;
     const bool live = lt > 0.f;
     const float inv = live ? 1.f / lt : 0.f;
-    const float lse_v = live ? (m_run[mb] + log2f(lt)) * kLn2 : neg_inf();
-    if (flags & FLAG_PARTIAL) {
-      float* op = a.part_o + (int64_t)(dst + rl) * D;
+    const float lse_v = live ? (st.m[mb] + log2f(lt)) * kLn2 : neg_inf();
+    if (it.flags & FLAG_PARTIAL) {
+      float* op = a.part_o + (int64_t)(it.dst + rl) * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float* d0 = op + DPL * (4 * grp + r);
 #pragma unroll
         for (int m = 0; m < DPL; m += 4) {
-          f32x4 v = {acc[mb][m][r] * inv, acc[mb][m + 1][r] * inv, acc[mb][m + 2][r] * inv,
-                     acc[mb][m + 3][r] * inv};
+          f32x4 v = {st.acc[mb][m][r] * inv, st.acc[mb][m + 1][r] * inv,
+                     st.acc[mb][m + 2][r] * inv, st.acc[mb][m + 3][r] * inv};
           *(f32x4*)(d0 + m) = v;
         }
       }
-      if (grp == 0) a.part_lse[dst + rl] = lse_v;
+      if (grp == 0) a.part_lse[it.dst + rl] = lse_v;
     } else {
-      const int rho = row0 + rl;
+      const int rho = it.row0 + rl;
       const int qi = rho / G, h = rho - qi * G;
-      const int tok = (flags & FLAG_LIST_Q) ? a.qlist[q_base + qi] : q_base + qi;
-      const int64_t orow = (int64_t)tok * Hq + g * G + h;
+      const int tok = (it.flags & FLAG_LIST_Q) ? a.qlist[it.q_base + qi] : it.q_base + qi;
+      const int64_t orow = (int64_t)tok * a.num_qo_heads + it.g * G + h;
       uint16_t* op = a.o + orow * D;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         vrow_t v;
 #pragma unroll
-        for (int m = 0; m < DPL; m += 2) v[m >> 1] = pack2(acc[mb][m][r] * inv, acc[mb][m + 1][r] * inv);
+        for (int m = 0; m < DPL; m += 2)
+          v[m >> 1] = pack2(st.acc[mb][m][r] * inv, st.acc[mb][m + 1][r] * inv);
         *(vrow_t*)(op + DPL * (4 * grp + r)) = v;
       }
       if (grp == 0 && a.lse) a.lse[orow] = lse_v;
@@ -260,25 +328,86 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const int32_t* __res
   }
 }
 
-template <int D, int MB>
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+template <int D, int MB, int NP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 2 : 1))) void attention_kernel(AttnArgs a) {
+  constexpr int KJ = Cfg<D>::KJ;
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int w = blockIdx.x * WAVES_PER_BLOCK + wave;
+  const int col = lane & 15, grp = lane >> 4;
+  const int w = blockIdx.x * WAVES_PER_BLOCK + uniform(threadIdx.x >> 6);
   if (w >= a.num_workers) return;
-  const int i0 = a.worker_indptr[w], i1 = a.worker_indptr[w + 1];
-  for (int i = i0; i < i1; ++i) run_item<D, MB>(a, a.items + (int64_t)i * ITEM_INTS, lane);
+  const int i_end = ld_uniform(a.worker_indptr, w + 1);
+  int i = ld_uniform(a.worker_indptr, w);
+  if (i >= i_end) return;
+
+  Item cur = load_item(a, i);
+  u32x4 q_cur[MB][KJ];
+  load_q<D, MB>(a, cur, q_cur, col, grp);
+  Tile<D> TA, TB;
+  issue_step<D, NP>(a, cur, 0, TA, col, grp);
+  State<D, MB> st;
+  st.reset();
+  int s = 0;
+  u32x4 q_nxt[MB][KJ];
+
+  // One stream step: compute step s of `cur` from X while Y receives the
+  // next step. Every call issues the same loads (next item's fields and Q,
+  // one step of K/V; at the end of the stream an in-bounds re-load of the
+  // current step), so the wait for X is the same count on every path.
+  auto advance = [&](Tile<D>& X, Tile<D>& Y) -> bool {
+    const bool last = s + 1 >= cur.nsteps;
+    const bool more = !last || i + 1 < i_end;
+    const Item nx = load_item(a, min(i + 1, i_end - 1));
+    load_q<D, MB>(a, nx, q_nxt, col, grp);
+    if (!more) {
+      issue_step<D, NP>(a, cur, s, Y, col, grp);
+    } else if (last) {
+      issue_step<D, NP>(a, nx, 0, Y, col, grp);
+    } else {
+      issue_step<D, NP>(a, cur, s + 1, Y, col, grp);
+    }
+    compute_step<D, MB>(a, cur, s, X, q_cur, st, col, grp);
+    if (last) {
+      finalize<D, MB>(a, cur, st, col, grp);
+      st.reset();
+      cur = nx;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) q_cur[mb][j] = q_nxt[mb][j];
+      ++i;
+      s = 0;
+    } else {
+      ++s;
+    }
+    return more;
+  };
+
+  while (true) {
+    if (!advance(TA, TB)) break;
+    if (!advance(TB, TA)) break;
+  }
+}
+
+template <int D, int MB>
+hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  if (a.page_size == 8) {
+    hipLaunchKernelGGL((attention_kernel<D, MB, 4>), grid, dim3(256), 0, s, a);
+  } else if (a.page_size == 16) {
+    hipLaunchKernelGGL((attention_kernel<D, MB, 2>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attention_kernel<D, MB, 1>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int rows_per_block, dim3 grid, hipStream_t s) {
   switch (rows_per_block) {
-    case 16: hipLaunchKernelGGL((attention_kernel<D, 1>), grid, dim3(256), 0, s, a); break;
-    case 32: hipLaunchKernelGGL((attention_kernel<D, 2>), grid, dim3(256), 0, s, a); break;
-    case 64: hipLaunchKernelGGL((attention_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
+    case 16: return launch_np<D, 1>(a, grid, s);
+    case 32: return launch_np<D, 2>(a, grid, s);
+    case 64: return launch_np<D, 4>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace

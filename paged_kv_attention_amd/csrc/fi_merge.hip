@@ -35,30 +35,58 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
 
-// One wavefront per merge record; each lane owns 4 consecutive outputs.
+// Part lists are never written while a kernel runs: reading them through the
+// constant address space makes the wave-uniform reads scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+__device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
+  return __builtin_amdgcn_readfirstlane(((const_i32p)p)[i]);
+}
+
+constexpr int kBatch = 8;   // partial states whose loads are in flight together
+
+// One wavefront per merge record; each lane owns 4 consecutive outputs. The
+// loads of kBatch partial states are issued together; the fold itself runs
+// j = 0, 1, ... in order, so batching does not change any rounding.
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * WAVES_PER_BLOCK + (threadIdx.x >> 6);
+  const int e = blockIdx.x * WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (e >= a.num_merges) return;
   const int32_t* m = a.merges + (int64_t)e * MERGE_INTS;
-  const int q_tok = m[M_QTOK], head0 = m[M_HEAD0], nh = m[M_NHEADS];
-  const int off = m[M_OFF], n = m[M_N];
+  const int q_tok = ld_uniform(m, M_QTOK), head0 = ld_uniform(m, M_HEAD0);
+  const int nh = ld_uniform(m, M_NHEADS), off = ld_uniform(m, M_OFF), n = ld_uniform(m, M_N);
+  const int32_t* parts = a.parts + off;
   const int D = a.head_dim;
   const int total = nh * D;
   for (int e0 = lane * 4; e0 < total; e0 += 256) {
     const int h = e0 / D, d = e0 - h * D;
     float M = neg_inf();
-    for (int j = 0; j < n; ++j) M = fmaxf(M, a.part_lse[a.parts[off + j] + h]);
+    for (int j0 = 0; j0 < n; j0 += kBatch) {
+      float l[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) l[u] = a.part_lse[ld_uniform(parts, min(j0 + u, n - 1)) + h];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) M = fmaxf(M, l[u]);
+    }
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float z = 0.f;
     if (M != neg_inf()) {
-      for (int j = 0; j < n; ++j) {
-        const int row = a.parts[off + j] + h;
-        const float lj = a.part_lse[row];
-        const float w = (lj == neg_inf()) ? 0.f : expf(lj - M);
-        z += w;
-        const f32x4 v = *(const f32x4*)(a.part_o + (int64_t)row * D + d);
-        acc += w * v;
+      for (int j0 = 0; j0 < n; j0 += kBatch) {
+        float l[kBatch];
+        f32x4 v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int row = ld_uniform(parts, min(j0 + u, n - 1)) + h;
+          l[u] = a.part_lse[row];
+          v[u] = *(const f32x4*)(a.part_o + (int64_t)row * D + d);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          if (j0 + u < n) {
+            const float w = (l[u] == neg_inf()) ? 0.f : expf(l[u] - M);
+            z += w;
+            acc += w * v[u];
+          }
+        }
       }
     }
     const float inv = z > 0.f ? 1.f / z : 0.f;
