@@ -82,7 +82,7 @@ typedef struct fi_plan_desc {
   int32_t det_chunk_pages;   /* deterministic chunk size in pages (default 64) */
   int32_t min_chunk_pages;   /* balanced mode lower bound on chunk pages (default 8) */
   int32_t num_cus;           /* compute units to plan for (0 = current device) */
-  int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 8) */
+  int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 4) */
   int32_t num_prefix_groups; /* cascade: number of shared prefixes             */
 } fi_plan_desc;
 

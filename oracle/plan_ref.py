@@ -17,20 +17,23 @@ be compared with it element for element:
 2. Key range. A unit sees tokens [0, t_lim): t_lim = kv_len, or under the
    causal mask min(kv_len, kv_len - qo + i_last + 1) with i_last the last
    query token in the block. It spans n = ceil(t_lim / ps) pages.
-3. Chunk size. Deterministic mode: c = det_chunk_pages, a constant, so chunk
-   boundaries depend on the request alone. Balanced mode: c = max(1,
-   min_chunk_pages, ceil(W / S)) with W the level's total unit pages and S the
-   number of persistent workers.
-4. Chunks. k = ceil(n / c) chunks; chunk j covers pages
-   [floor(j*n/k), floor((j+1)*n/k)).
-5. Outputs. A unit with k == 1 writes its final rows directly; k > 1 writes
-   fp32 partial rows (allocated in enumeration order) that a merge folds in
-   chunk order. Cascade writes partials for everything and merges the prefix
-   chunk(s) first, then the suffix chunks.
-6. Placement. Longest-processing-time-first (Graham): items sorted by
-   (cost descending, enumeration index), cost = pages + 1, each given to the
-   worker with the smallest load, ties to the lowest worker index. A worker
-   runs its items in the order they were given to it.
+3. Balanced mode (even split). The units' pages are laid end to end in
+   enumeration order (W pages in all) and cut into consecutive quotas of
+   c = max(1, min_chunk_pages, ceil(W / S)) pages, S = number of persistent
+   workers; quota w goes to worker w. A unit's pieces, in order, are its
+   chunks, so each worker reads c pages (the last one fewer) and runs its
+   pieces in page order.
+4. Deterministic mode. A unit of n pages has k = ceil(n / c) chunks with
+   c = det_chunk_pages, chunk j covering pages [floor(j*n/k),
+   floor((j+1)*n/k)): boundaries depend on the request alone. Chunks are
+   placed longest-processing-time-first (Graham): sorted by (cost
+   descending, enumeration index), cost = pages + 1, each given to the
+   worker with the smallest load, ties to the lowest worker index; a worker
+   runs its chunks in the order it received them.
+5. Outputs. A unit with one chunk writes its final rows directly; otherwise
+   each chunk writes fp32 partial rows (allocated in enumeration order) that a
+   merge folds in chunk order. Cascade writes partials for everything and
+   merges the prefix chunk(s) first, then the suffix chunks.
 """
 
 from __future__ import annotations
@@ -50,13 +53,6 @@ def _ceil_div(a, b):
     return -(-a // b)
 
 
-def _chunk_size(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages):
-    if deterministic:
-        return max(1, int(det_chunk_pages))
-    W = sum(u["n_pages"] for u in units)
-    return max(1, int(min_chunk_pages), _ceil_div(W, num_workers))
-
-
 def _lpt(items, num_workers):
     order = sorted(range(len(items)),
                    key=lambda i: (-(items[i]["t_pages"] + 1), i))
@@ -71,6 +67,33 @@ def _lpt(items, num_workers):
         flat.extend(per_worker[w])
         indptr.append(len(flat))
     return flat, indptr
+
+
+def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages):
+    """Per unit: list of (p0, p1, worker) page pieces in order; and c."""
+    pieces = []
+    if deterministic:
+        c = max(1, int(det_chunk_pages))
+        for u in units:
+            n = u["n_pages"]
+            k = _ceil_div(n, c) if n > 0 else 0
+            pieces.append([((j * n) // k, ((j + 1) * n) // k, None) for j in range(k)])
+        return pieces, c
+    W = sum(u["n_pages"] for u in units)
+    c = max(1, int(min_chunk_pages), _ceil_div(W, num_workers))
+    g = 0
+    for u in units:
+        n = u["n_pages"]
+        lst = []
+        p = 0
+        while p < n:
+            w = (g + p) // c
+            e = min(n, (w + 1) * c - g)
+            lst.append((p, e, w))
+            p = e
+        pieces.append(lst)
+        g += n
+    return pieces, c
 
 
 def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
@@ -141,18 +164,17 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     all_partial = kind == "cascade"
     next_row = 0
     levels = []
-    unit_chunks = []    # per level: per unit list of (dst_row) for partial chunks, or "final"
+    unit_chunks = []    # per level: per unit (k, [partial dst rows])
     for units in levels_units:
-        c = _chunk_size(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages)
+        pieces, c = _unit_pieces(units, num_workers, deterministic, det_chunk_pages,
+                                 min_chunk_pages)
         items = []
         chunks_of = []
-        for u in units:
-            n = u["n_pages"]
-            k = _ceil_div(n, c) if n > 0 else 0
+        for u, lst in zip(units, pieces):
+            k = len(lst)
             partial = all_partial or k > 1
             dsts = []
-            for j in range(k):
-                p0, p1 = (j * n) // k, ((j + 1) * n) // k
+            for j, (p0, p1, w) in enumerate(lst):
                 dst = -1
                 if partial:
                     dst = next_row
@@ -162,11 +184,20 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                     q_base=u["q_base"], row0=u["row0"], n_rows=u["n_rows"], kv_head=u["g"],
                     page_off=u["page_off"], flags=u["flags"] | (FLAG_PARTIAL if partial else 0),
                     t_begin=p0 * ps, t_end=min(p1 * ps, u["t_lim"]), q_pos0=u["q_pos0"],
-                    dst=dst, unit=u["unit"], chunk=j, t_pages=p1 - p0))
+                    dst=dst, unit=u["unit"], chunk=j, t_pages=p1 - p0, worker=w))
             chunks_of.append((k, dsts))
-        order, indptr = _lpt(items, num_workers)
+        if deterministic:
+            order, indptr = _lpt(items, num_workers)
+        else:
+            per = [[] for _ in range(num_workers)]
+            for i, it in enumerate(items):
+                per[it["worker"]].append(i)
+            order, indptr = [], [0]
+            for w in range(num_workers):
+                order.extend(per[w])
+                indptr.append(len(order))
         levels.append(dict(items=[tuple(items[i][f] for f in ITEM_FIELDS) for i in order],
-                           worker_indptr=indptr))
+                           worker_indptr=indptr, chunk_pages=c))
         unit_chunks.append(chunks_of)
 
     merges, parts = [], []

@@ -114,7 +114,7 @@ extern "C" fi_status fi_paged_decode(const fi_plan_t* p, const void* q, const vo
   const AttnArgs a =
       attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
   TimerScope t(s);
-  st = hip_status(launch_attention(a, p->hp.desc.head_dim, p->hp.level[0].rows_per_block, s),
+  st = hip_status(launch_attention(a, p->hp.desc.head_dim, p->hp.level[0].rows_per_block, false, s),
                   "attention launch");
   t.done();
   if (st != FI_OK) return st;
@@ -153,7 +153,7 @@ extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const vo
   const AttnArgs a =
       attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
   TimerScope t(s);
-  st = hip_status(launch_attention(a, d.head_dim, p->hp.level[0].rows_per_block, s),
+  st = hip_status(launch_attention(a, d.head_dim, p->hp.level[0].rows_per_block, false, s),
                   "attention launch");
   t.done();
   if (st != FI_OK) return st;
@@ -178,7 +178,7 @@ extern "C" fi_status fi_cascade(const fi_plan_t* p, const void* q, const void* k
   for (int l = 0; l < 2; ++l) {
     const AttnArgs a =
         attn_args(p, l, q, k_cache, v_cache, kv_indices, prefix_indices, sm_scale, o, lse);
-    st = hip_status(launch_attention(a, D, p->hp.level[l].rows_per_block, s), "attention launch");
+    st = hip_status(launch_attention(a, D, p->hp.level[l].rows_per_block, l == 0, s), "attention launch");
     if (st != FI_OK) return st;
   }
   t.done();

@@ -50,6 +50,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kRescaleSlack = 8.f;
 
 template <int W> struct RowVec;
 template <> struct RowVec<4> { typedef u32x4 T; };
@@ -57,16 +58,12 @@ template <> struct RowVec<2> { typedef u32x2 T; };
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return bf16_bits(lo) | (bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
@@ -114,16 +111,19 @@ struct Cfg {
   typedef typename RowVec<DPL / 2>::T vrow_t;
 };
 
-template <int D>
+// One step's registers: K and V of 32 tokens, and (first step of an item
+// only) the item's Q.
+template <int D, int MB>
 struct Tile {
   u32x4 k[2][Cfg<D>::KJ];
   typename Cfg<D>::vrow_t v[8];
+  u32x4 q[MB][Cfg<D>::KJ];
 };
 
 // Issue the loads of step s of item it into T.
-template <int D, int NP>
-__device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, int s, Tile<D>& T,
-                                           int col, int grp) {
+template <int D, int MB, int NP>
+__device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, int s,
+                                           Tile<D, MB>& T, int col, int grp) {
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL;
   typedef typename Cfg<D>::vrow_t vrow_t;
   const int sh = a.page_shift;
@@ -181,7 +181,7 @@ __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, in
   }
 }
 
-template <int D, int MB>
+template <int D, int MB, bool LQ>
 __device__ __forceinline__ void load_q(const AttnArgs& a, const Item& it, u32x4 (&qf)[MB][Cfg<D>::KJ],
                                        int col, int grp) {
   const int G = a.group;
@@ -192,7 +192,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, const Item& it, u32x4 
     const int rl = mb * 16 + col < it.n_rows ? mb * 16 + col : 0;
     const int rho = it.row0 + rl;
     const int qi = rho / G, h = rho - qi * G;
-    const int tok = (it.flags & FLAG_LIST_Q) ? a.qlist[it.q_base + qi] : it.q_base + qi;
+    const int tok = LQ ? a.qlist[it.q_base + qi] : it.q_base + qi;
     const uint16_t* qp = a.q + ((int64_t)tok * a.num_qo_heads + it.g * G + h) * D + grp * 8;
 #pragma unroll
     for (int j = 0; j < Cfg<D>::KJ; ++j) qf[mb][j] = *(const u32x4*)(qp + 32 * j);
@@ -216,7 +216,8 @@ struct State {
 
 template <int D, int MB>
 __device__ __forceinline__ void compute_step(const AttnArgs& a, const Item& it, int s,
-                                             const Tile<D>& T, const u32x4 (&qf)[MB][Cfg<D>::KJ],
+                                             const Tile<D, MB>& T,
+                                             const u32x4 (&qf)[MB][Cfg<D>::KJ],
                                              State<D, MB>& st, int col, int grp) {
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL;
   typedef typename Cfg<D>::vrow_t vrow_t;
@@ -252,35 +253,52 @@ __device__ __forceinline__ void compute_step(const AttnArgs& a, const Item& it, 
       s0 = mfma_bf16(T.k[0][j], qf[mb][j], s0);
       s1 = mfma_bf16(T.k[1][j], qf[mb][j], s1);
     }
-    // last visible token for this lane's row
-    int lim = it.t_end - 1;
-    if (causal) lim = min(lim, it.q_pos0 + (it.row0 + mb * 16 + col) / a.group);
     float x[8];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t0 = T0 + 4 * grp + r;
-      x[r] = (t0 <= lim) ? s0[r] * a.scale_log2 : neg_inf();
-      x[4 + r] = (t0 + 16 <= lim) ? s1[r] * a.scale_log2 : neg_inf();
+      x[r] = s0[r] * a.scale_log2;
+      x[4 + r] = s1[r] * a.scale_log2;
+    }
+    if (T0 + 32 > it.t_end || causal) {
+      // last visible token for this lane's row
+      int lim = it.t_end - 1;
+      if (causal) lim = min(lim, it.q_pos0 + (it.row0 + mb * 16 + col) / a.group);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t0 = T0 + 4 * grp + r;
+        if (t0 > lim) x[r] = neg_inf();
+        if (t0 + 16 > lim) x[4 + r] = neg_inf();
+      }
     }
     float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                      fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(st.m[mb], mx);
-    const float base = (m_new == neg_inf()) ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m[mb] - base);
+    // The base m that P is taken against only moves when a row's max exceeds
+    // it by more than kRescaleSlack (log2 units): until then p <= 2^slack,
+    // which fp32 and bf16 hold exactly as well, and O and l (both relative to
+    // the same m) need no rescale. The result is the same exact quotient.
+    if (__any(mx > st.m[mb] + kRescaleSlack)) {
+      const float m_new = fmaxf(st.m[mb], mx);
+      const float alpha =
+          (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[mb] - m_new);
+      st.l[mb] *= alpha;
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) st.acc[mb][m] *= alpha;
+      st.m[mb] = m_new;
+    }
+    const float base = (st.m[mb] == neg_inf()) ? 0.f : st.m[mb];
     float p[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - base);
-    st.l[mb] = st.l[mb] * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-    st.m[mb] = m_new;
+    st.l[mb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
     const u32x4 pb = {pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
 #pragma unroll
-    for (int m = 0; m < DPL; ++m) st.acc[mb][m] = mfma_bf16(vt[m], pb, st.acc[mb][m] * alpha);
+    for (int m = 0; m < DPL; ++m) st.acc[mb][m] = mfma_bf16(vt[m], pb, st.acc[mb][m]);
   }
 }
 
-template <int D, int MB>
+template <int D, int MB, bool LQ>
 __device__ __forceinline__ void finalize(const AttnArgs& a, const Item& it, const State<D, MB>& st,
                                          int col, int grp) {
   constexpr int DPL = Cfg<D>::DPL;
@@ -312,7 +330,7 @@ __device__ __forceinline__ void finalize(const AttnArgs& a, const Item& it, cons
     } else {
       const int rho = it.row0 + rl;
       const int qi = rho / G, h = rho - qi * G;
-      const int tok = (it.flags & FLAG_LIST_Q) ? a.qlist[it.q_base + qi] : it.q_base + qi;
+      const int tok = LQ ? a.qlist[it.q_base + qi] : it.q_base + qi;
       const int64_t orow = (int64_t)tok * a.num_qo_heads + it.g * G + h;
       uint16_t* op = a.o + orow * D;
 #pragma unroll
@@ -328,97 +346,114 @@ __device__ __forceinline__ void finalize(const AttnArgs& a, const Item& it, cons
   }
 }
 
-template <int D, int MB, int NP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MB == 1 ? 2 : 1))) void attention_kernel(AttnArgs a) {
+// Tiles in the ring: R-1 steps are in flight while one is computed.
+template <int MB> struct Ring { static constexpr int R = MB == 1 ? 4 : 2; };
+
+// LQ: query rows come through the member list (cascade prefix level only).
+template <int D, int MB, int NP, bool LQ>
+__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   constexpr int KJ = Cfg<D>::KJ;
+  constexpr int R = Ring<MB>::R;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int w = blockIdx.x * WAVES_PER_BLOCK + uniform(threadIdx.x >> 6);
   if (w >= a.num_workers) return;
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
-  int i = ld_uniform(a.worker_indptr, w);
-  if (i >= i_end) return;
+  const int i_begin = ld_uniform(a.worker_indptr, w);
+  if (i_begin >= i_end) return;
 
-  Item cur = load_item(a, i);
+  // Two cursors over the worker's stream of steps: the issue cursor (ii, is)
+  // runs R-1 steps ahead of the compute cursor (ci, cs), across item
+  // boundaries. Tiles are filled and consumed in the same order.
+  int ci = i_begin, cs = 0;
+  Item citem = load_item(a, ci);
+  int ii = i_begin, is = 0;
+  Item iitem = citem;
+  Tile<D, MB> T[R];
   u32x4 q_cur[MB][KJ];
-  load_q<D, MB>(a, cur, q_cur, col, grp);
-  Tile<D> TA, TB;
-  issue_step<D, NP>(a, cur, 0, TA, col, grp);
   State<D, MB> st;
   st.reset();
-  int s = 0;
-  u32x4 q_nxt[MB][KJ];
 
-  // One stream step: compute step s of `cur` from X while Y receives the
-  // next step. Every call issues the same loads (next item's fields and Q,
-  // one step of K/V; at the end of the stream an in-bounds re-load of the
-  // current step), so the wait for X is the same count on every path.
-  auto advance = [&](Tile<D>& X, Tile<D>& Y) -> bool {
-    const bool last = s + 1 >= cur.nsteps;
-    const bool more = !last || i + 1 < i_end;
-    const Item nx = load_item(a, min(i + 1, i_end - 1));
-    load_q<D, MB>(a, nx, q_nxt, col, grp);
-    if (!more) {
-      issue_step<D, NP>(a, cur, s, Y, col, grp);
-    } else if (last) {
-      issue_step<D, NP>(a, nx, 0, Y, col, grp);
-    } else {
-      issue_step<D, NP>(a, cur, s + 1, Y, col, grp);
+  auto issue = [&](Tile<D, MB>& Y) {
+    const bool valid = ii < i_end;
+    if (valid && is == 0) load_q<D, MB, LQ>(a, iitem, Y.q, col, grp);
+    // past the end of the stream: an in-bounds re-load of the current step
+    issue_step<D, MB, NP>(a, valid ? iitem : citem, valid ? is : cs, Y, col, grp);
+    if (valid && ++is >= iitem.nsteps) {
+      ++ii;
+      is = 0;
+      if (ii < i_end) iitem = load_item(a, ii);
     }
-    compute_step<D, MB>(a, cur, s, X, q_cur, st, col, grp);
-    if (last) {
-      finalize<D, MB>(a, cur, st, col, grp);
-      st.reset();
-      cur = nx;
+  };
+
+  // Refill Y (the tile computed last), then compute X.
+  auto advance = [&](Tile<D, MB>& X, Tile<D, MB>& Y) -> bool {
+    issue(Y);
+    if (cs == 0) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) q_cur[mb][j] = q_nxt[mb][j];
-      ++i;
-      s = 0;
-    } else {
-      ++s;
+        for (int j = 0; j < KJ; ++j) q_cur[mb][j] = X.q[mb][j];
     }
-    return more;
+    compute_step<D, MB>(a, citem, cs, X, q_cur, st, col, grp);
+    if (cs + 1 >= citem.nsteps) {
+      finalize<D, MB, LQ>(a, citem, st, col, grp);
+      st.reset();
+      if (++ci >= i_end) return false;
+      cs = 0;
+      citem = load_item(a, ci);
+    } else {
+      ++cs;
+    }
+    return true;
   };
 
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r) issue(T[r]);
   while (true) {
-    if (!advance(TA, TB)) break;
-    if (!advance(TB, TA)) break;
+    if (!advance(T[0], T[R - 1])) break;
+#pragma unroll
+    for (int r = 1; r < R; ++r)
+      if (!advance(T[r], T[r - 1])) goto done;
   }
+done:;
 }
 
-template <int D, int MB>
+template <int D, int MB, bool LQ>
 hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    hipLaunchKernelGGL((attention_kernel<D, MB, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attention_kernel<D, MB, 4, LQ>), grid, dim3(256), 0, s, a);
   } else if (a.page_size == 16) {
-    hipLaunchKernelGGL((attention_kernel<D, MB, 2>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attention_kernel<D, MB, 2, LQ>), grid, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attention_kernel<D, MB, 1>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attention_kernel<D, MB, 1, LQ>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(const AttnArgs& a, int rows_per_block, dim3 grid, hipStream_t s) {
+hipError_t launch_d(const AttnArgs& a, int rows_per_block, bool list_q, dim3 grid,
+                    hipStream_t s) {
+  if (list_q) {
+    if (rows_per_block == 64) return launch_np<D, 4, true>(a, grid, s);
+    return hipErrorInvalidValue;
+  }
   switch (rows_per_block) {
-    case 16: return launch_np<D, 1>(a, grid, s);
-    case 32: return launch_np<D, 2>(a, grid, s);
-    case 64: return launch_np<D, 4>(a, grid, s);
+    case 16: return launch_np<D, 1, false>(a, grid, s);
+    case 32: return launch_np<D, 2, false>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, int head_dim, int rows_per_block,
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int rows_per_block, bool list_q,
                             hipStream_t stream) {
   const int blocks = (a.num_workers + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   if (blocks == 0) return hipSuccess;
   const dim3 grid(blocks);
-  if (head_dim == 128) return launch_d<128>(a, rows_per_block, grid, stream);
-  if (head_dim == 64) return launch_d<64>(a, rows_per_block, grid, stream);
+  if (head_dim == 128) return launch_d<128>(a, rows_per_block, list_q, grid, stream);
+  if (head_dim == 64) return launch_d<64>(a, rows_per_block, list_q, grid, stream);
   return hipErrorInvalidValue;
 }
 

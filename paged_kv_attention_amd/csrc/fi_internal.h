@@ -96,7 +96,8 @@ struct MergeStatesArgs {
   float* s_out;
 };
 
-hipError_t launch_attention(const AttnArgs& a, int head_dim, int rows_per_block,
+// list_q: the level's query rows come through the member list (cascade prefix).
+hipError_t launch_attention(const AttnArgs& a, int head_dim, int rows_per_block, bool list_q,
                             hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);

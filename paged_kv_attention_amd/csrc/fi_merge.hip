@@ -24,11 +24,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
@@ -91,8 +92,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
     const float inv = z > 0.f ? 1.f / z : 0.f;
     const int64_t orow = (int64_t)q_tok * a.num_qo_heads + head0 + h;
-    u32x2 packed = {bf16_bits(acc[0] * inv) | (bf16_bits(acc[1] * inv) << 16),
-                    bf16_bits(acc[2] * inv) | (bf16_bits(acc[3] * inv) << 16)};
+    u32x2 packed = {pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv)};
     *(u32x2*)(a.o + orow * D + d) = packed;
     if (d == 0 && a.lse) a.lse[orow] = z > 0.f ? M + logf(z) : neg_inf();
   }
@@ -133,8 +133,7 @@ __global__ __launch_bounds__(256) void merge_states_kernel(MergeStatesArgs a) {
     if (a.out_f32) {
       *(f32x4*)((float*)a.v_out + obase) = o;
     } else {
-      u32x2 packed = {bf16_bits(o[0]) | (bf16_bits(o[1]) << 16),
-                      bf16_bits(o[2]) | (bf16_bits(o[3]) << 16)};
+      u32x2 packed = {pack2(o[0], o[1]), pack2(o[2], o[3])};
       *(u32x2*)((uint16_t*)a.v_out + obase) = packed;
     }
     if (d == 0 && a.s_out) a.s_out[n * H + h] = z > 0.f ? M + logf(z) : neg_inf();

@@ -10,14 +10,17 @@
 //             kv head) over the member requests' rows
 //   key range of a unit: [0, t_lim), t_lim = kv_len, or min(kv_len,
 //             kv_len - qo + i_last + 1) under the bottom-right causal mask
-//   chunk c : deterministic -> det_chunk_pages; balanced -> max(1,
-//             min_chunk_pages, ceil(W / S)), W = level's total unit pages,
-//             S = num_cus * workers_per_cu
-//   chunks  : k = ceil(n / c), chunk j = pages [floor(jn/k), floor((j+1)n/k))
-//   outputs : k == 1 final rows, else fp32 partial rows + merge (cascade: all
-//             partial, merged prefix first)
-//   placing : Graham's longest-processing-time rule, cost = pages + 1, ties to
-//             the lower enumeration index and to the lower worker index.
+//   balanced: the level's unit pages laid end to end (W pages) are cut into
+//             quotas of c = max(1, min_chunk_pages, ceil(W / S)) pages,
+//             S = num_cus * workers_per_cu; quota w is worker w's, so every
+//             worker reads the same number of pages (even split)
+//   deterministic: c = det_chunk_pages; a unit of n pages has k = ceil(n/c)
+//             chunks [floor(jn/k), floor((j+1)n/k)), boundaries depending on
+//             the request alone, placed by Graham's longest-processing-time
+//             rule (cost = pages + 1, ties to the lower enumeration index and
+//             the lower worker index)
+//   outputs : one chunk -> final rows, else fp32 partial rows + merge
+//             (cascade: all partial, merged prefix first)
 // The grid is always S workers, whatever the batch, so a captured graph is
 // re-pointed at a new batch by re-planning into the same workspace.
 
@@ -141,25 +144,45 @@ struct LevelBuild {
 
 void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, int32_t S,
                  bool all_partial, int32_t& next_row, LevelBuild& lb, Level& lv) {
+  const int32_t ps = d.page_size;
+  // Per unit: its pieces (page range and, in balanced mode, the worker).
+  struct Piece { int64_t p0, p1; int32_t worker; };
+  std::vector<std::vector<Piece>> pieces(units.size());
   int64_t c;
   if (d.deterministic) {
     c = std::max(1, d.det_chunk_pages);
+    for (size_t ui = 0; ui < units.size(); ++ui) {
+      const int64_t n = units[ui].n_pages;
+      const int64_t k = n > 0 ? ceil_div(n, c) : 0;
+      for (int64_t j = 0; j < k; ++j) pieces[ui].push_back({(j * n) / k, ((j + 1) * n) / k, -1});
+    }
   } else {
     int64_t W = 0;
     for (const Unit& u : units) W += u.n_pages;
     c = std::max<int64_t>({1, d.min_chunk_pages, ceil_div(W, S)});
+    int64_t g = 0;   // global page offset of the unit
+    for (size_t ui = 0; ui < units.size(); ++ui) {
+      const int64_t n = units[ui].n_pages;
+      for (int64_t p = 0; p < n;) {
+        const int64_t w = (g + p) / c;
+        const int64_t e = std::min(n, (w + 1) * c - g);
+        pieces[ui].push_back({p, e, (int32_t)w});
+        p = e;
+      }
+      g += n;
+    }
   }
   lv.chunk_pages = (int32_t)c;
-  const int32_t ps = d.page_size;
   lb.items.clear();
   lb.chunks.clear();
-  for (const Unit& u : units) {
-    const int64_t n = u.n_pages;
-    const int64_t k = n > 0 ? ceil_div(n, c) : 0;
+  std::vector<int32_t> item_worker;
+  for (size_t ui = 0; ui < units.size(); ++ui) {
+    const Unit& u = units[ui];
+    const int32_t k = (int32_t)pieces[ui].size();
     const bool partial = all_partial || k > 1;
     std::vector<int32_t> dsts;
-    for (int64_t j = 0; j < k; ++j) {
-      const int64_t p0 = (j * n) / k, p1 = ((j + 1) * n) / k;
+    for (int32_t j = 0; j < k; ++j) {
+      const Piece& pc = pieces[ui][j];
       int32_t dst = -1;
       if (partial) {
         dst = next_row;
@@ -173,33 +196,38 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, int32_t 
       it.f[F_KVHEAD] = u.g;
       it.f[F_PAGEOFF] = u.page_off;
       it.f[F_FLAGS] = u.flags | (partial ? FLAG_PARTIAL : 0);
-      it.f[F_TBEGIN] = (int32_t)(p0 * ps);
-      it.f[F_TEND] = (int32_t)std::min<int64_t>(p1 * ps, u.t_lim);
+      it.f[F_TBEGIN] = (int32_t)(pc.p0 * ps);
+      it.f[F_TEND] = (int32_t)std::min<int64_t>(pc.p1 * ps, u.t_lim);
       it.f[F_QPOS0] = u.q_pos0;
       it.f[F_DST] = dst;
       it.f[F_UNIT] = u.unit;
-      it.f[F_CHUNK] = (int32_t)j;
-      it.pages = (int32_t)(p1 - p0);
+      it.f[F_CHUNK] = j;
+      it.pages = (int32_t)(pc.p1 - pc.p0);
       lb.items.push_back(it);
+      item_worker.push_back(pc.worker);
     }
-    lb.chunks.emplace_back((int32_t)k, std::move(dsts));
+    lb.chunks.emplace_back(k, std::move(dsts));
   }
-  // Longest processing time first: stable sort keeps enumeration order on ties.
   const size_t n = lb.items.size();
-  std::vector<int32_t> order(n);
-  std::iota(order.begin(), order.end(), 0);
-  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
-    return lb.items[a].pages > lb.items[b].pages;
-  });
-  typedef std::pair<int64_t, int32_t> LoadW;
-  std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> heap;
-  for (int32_t w = 0; w < S; ++w) heap.push(LoadW(0, w));
   std::vector<std::vector<int32_t>> per(S);
-  for (int32_t i : order) {
-    LoadW top = heap.top();
-    heap.pop();
-    per[top.second].push_back(i);
-    heap.push(LoadW(top.first + lb.items[i].pages + 1, top.second));
+  if (d.deterministic) {
+    // Longest processing time first: stable sort keeps enumeration order on ties.
+    std::vector<int32_t> order(n);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) {
+      return lb.items[a].pages > lb.items[b].pages;
+    });
+    typedef std::pair<int64_t, int32_t> LoadW;
+    std::priority_queue<LoadW, std::vector<LoadW>, std::greater<LoadW>> heap;
+    for (int32_t w = 0; w < S; ++w) heap.push(LoadW(0, w));
+    for (int32_t i : order) {
+      LoadW top = heap.top();
+      heap.pop();
+      per[top.second].push_back(i);
+      heap.push(LoadW(top.first + lb.items[i].pages + 1, top.second));
+    }
+  } else {
+    for (size_t i = 0; i < n; ++i) per[item_worker[i]].push_back((int32_t)i);
   }
   lv.items.clear();
   lv.items.reserve(n * ITEM_INTS);
@@ -238,7 +266,7 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
     return set_error(FI_ERR_INVALID_ARG, "negative tuning field in desc");
   if (d.det_chunk_pages == 0) d.det_chunk_pages = 64;
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
-  if (d.workers_per_cu == 0) d.workers_per_cu = 8;
+  if (d.workers_per_cu == 0) d.workers_per_cu = 4;
   d.causal = d.causal ? 1 : 0;
   d.deterministic = d.deterministic ? 1 : 0;
   if (d.kind != FI_KIND_APPEND) d.causal = 0;

@@ -140,12 +140,38 @@ def test_deterministic_chunks_independent_of_batch():
             assert chunks_of(lens, pos) == alone
 
 
-def test_lpt_balances_a_skewed_batch():
+def _worker_pages(lv, S, ps):
+    out = []
+    for w in range(S):
+        its = lv["items"][lv["worker_indptr"][w]:lv["worker_indptr"][w + 1]]
+        out.append(sum(-(-(x[F["t_end"]] - x[F["t_begin"]]) // ps) for x in its))
+    return np.array(out)
+
+
+@pytest.mark.parametrize("lens", [[32768] * 4 + [1024] * 124, list(range(500, 4600, 64)),
+                                  [1, 2, 3, 17, 0, 5000]])
+def test_balanced_mode_splits_pages_evenly(lens):
+    """Every used worker reads exactly c pages, except the last used one."""
+    ps = 16
+    indptr, L = _decode_inputs(lens, ps)
+    S = 97
+    p = plan_ref("decode", 32, 8, ps, indptr, L, S, [16], min_chunk_pages=2)
+    lv = p["levels"][0]
+    c = lv["chunk_pages"]
+    W = 8 * sum(-(-x // ps) for x in lens)
+    pages = _worker_pages(lv, S, ps)
+    used = -(-W // c)
+    assert pages.sum() == W
+    assert np.all(pages[:used - 1] == c) and 0 < pages[used - 1] <= c
+    assert np.all(pages[used:] == 0)
+
+
+def test_lpt_balances_deterministic_chunks():
     ps = 16
     lens = [32768] * 4 + [1024] * 124
     indptr, L = _decode_inputs(lens, ps)
     S = 2048
-    p = plan_ref("decode", 32, 8, ps, indptr, L, S, [16])
+    p = plan_ref("decode", 32, 8, ps, indptr, L, S, [16], deterministic=True, det_chunk_pages=16)
     lv = p["levels"][0]
     loads = []
     for w in range(S):
