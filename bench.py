@@ -95,6 +95,61 @@ def cpu_baseline(w, budget_s: float):
                       f"{dt:.1f} s wall, KV bytes of the sample / wall time"}
 
 
+def explore(args, dev):
+    """Timing of one call on another configuration (decode, cascade or
+    append), for the design notes; prints its own JSON line."""
+    import torch
+    import paged_kv_attention_amd as fi
+    from workloads import CONFIG_NAMES, make_config
+    w = make_config(args.config, poison=False)
+    g = w.to(dev)
+    kw = dict(deterministic=args.mode == "deterministic", workers_per_cu=args.workers_per_cu,
+              min_chunk_pages=args.min_chunk_pages)
+    if w.kind == "decode":
+        plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
+                       w.head_dim, w.page_size, device=dev, **kw)
+        call = lambda: fi.paged_decode(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
+                                       w.sm_scale)
+        flops = 4 * w.head_dim * w.num_qo_heads * int(w.kv_len.sum())
+    elif w.kind == "cascade":
+        plan = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
+                       w.head_dim, w.page_size, prefix_indptr=w.prefix_indptr,
+                       prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group,
+                       device=dev, **kw)
+        call = lambda: fi.cascade(plan, g.q, g.k_cache, g.v_cache, g.prefix_indices,  # noqa
+                                  g.kv_indices, w.sm_scale)
+        per_req = w.kv_len.long() + w.prefix_len[0].long()
+        flops = 4 * w.head_dim * w.num_qo_heads * int(per_req.sum())
+    else:
+        plan = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
+                       w.head_dim, w.page_size, qo_indptr=w.qo_indptr, causal=True,
+                       device=dev, **kw)
+        call = lambda: fi.paged_append(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
+                                       w.sm_scale, k_new=g.k_new, v_new=g.v_new)
+        qo = (w.qo_indptr[1:] - w.qo_indptr[:-1]).long()
+        pre = w.kv_len.long() - qo
+        flops = 4 * w.head_dim * w.num_qo_heads * int((qo * pre + qo * (qo + 1) // 2).sum())
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with fi.KernelTimer(args.steps) as kt:
+        ev0.record()
+        for _ in range(args.steps):
+            call()
+        ev1.record()
+        torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    kern_ms = kt.total_ms / max(1, kt.calls)
+    kv = w.kv_bytes()
+    print(json.dumps({"workload": CONFIG_NAMES[args.config], "mode": args.mode,
+                      "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
+                      "kv_bytes": kv, "kv_GBps": round(kv / ms / 1e6, 1),
+                      "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
+                      "flops": flops, "TFLOPs": round(flops / ms / 1e9, 1),
+                      "pct_mfma_peak": round(100 * flops / ms / 1e9 / 2500.0, 2)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +162,8 @@ def main():
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--config", type=int, default=CONFIG_INDEX,
+                    help="other configurations print an exploratory line (not the bench line)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -120,6 +177,9 @@ def main():
 
     dev = torch.device("cuda:0")
     fi.load()
+    if args.config != CONFIG_INDEX:
+        explore(args, dev)
+        return
     print(f"bench: generating {CONFIG_NAMES[CONFIG_INDEX]}", file=sys.stderr, flush=True)
     w = make_config(CONFIG_INDEX, poison=False)
     g = w.to(dev)

@@ -96,7 +96,9 @@ typedef struct fi_plan fi_plan_t;
 typedef struct fi_plan_info {
   int32_t kind;
   int32_t num_levels;            /* 2 for cascade (prefix, suffix), else 1 */
-  int32_t num_workers;
+  int32_t num_workers[2];        /* per level: wavefronts (16-row levels) or
+                                    4-wave workgroups (128-row levels) */
+  int32_t min_chunk_pages[2];
   int32_t rows_per_block[2];
   int32_t chunk_pages[2];
   int32_t num_items[2];

@@ -103,11 +103,17 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     """Return the plan as plain lists.
 
     ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
-    with one entry per level (cascade: [prefix, suffix]; otherwise one).
+    with one entry per level (cascade: [prefix, suffix]; otherwise one);
+    ``num_workers`` and ``min_chunk_pages`` are a number (all levels) or such a
+    list.
     Result: ``{"levels": [{"items": [...12-tuples...], "worker_indptr": [...]}],
     "merges": [(q_tok, head0, n_heads, parts_off, n_parts)], "parts": [...],
     "qlist": [...], "n_part_rows": int}``.
     """
+    nlev = len(rows_per_block)
+    workers = list(num_workers) if isinstance(num_workers, (list, tuple)) else [num_workers] * nlev
+    min_chunk = (list(min_chunk_pages) if isinstance(min_chunk_pages, (list, tuple))
+                 else [min_chunk_pages] * nlev)
     B = len(kv_len)
     G = num_qo_heads // num_kv_heads
     ps = page_size
@@ -165,9 +171,9 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     next_row = 0
     levels = []
     unit_chunks = []    # per level: per unit (k, [partial dst rows])
-    for units in levels_units:
-        pieces, c = _unit_pieces(units, num_workers, deterministic, det_chunk_pages,
-                                 min_chunk_pages)
+    for lev, units in enumerate(levels_units):
+        S = workers[lev]
+        pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev])
         items = []
         chunks_of = []
         for u, lst in zip(units, pieces):
@@ -187,13 +193,13 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                     dst=dst, unit=u["unit"], chunk=j, t_pages=p1 - p0, worker=w))
             chunks_of.append((k, dsts))
         if deterministic:
-            order, indptr = _lpt(items, num_workers)
+            order, indptr = _lpt(items, S)
         else:
-            per = [[] for _ in range(num_workers)]
+            per = [[] for _ in range(S)]
             for i, it in enumerate(items):
                 per[it["worker"]].append(i)
             order, indptr = [], [0]
-            for w in range(num_workers):
+            for w in range(S):
                 order.extend(per[w])
                 indptr.append(len(order))
         levels.append(dict(items=[tuple(items[i][f] for f in ITEM_FIELDS) for i in order],

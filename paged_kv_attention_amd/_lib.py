@@ -31,8 +31,8 @@ I32P = POINTER(c_int32)
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [
-        ("kind", c_int32), ("num_levels", c_int32), ("num_workers", c_int32),
-        ("rows_per_block", c_int32 * 2), ("chunk_pages", c_int32 * 2),
+        ("kind", c_int32), ("num_levels", c_int32), ("num_workers", c_int32 * 2),
+        ("min_chunk_pages", c_int32 * 2), ("rows_per_block", c_int32 * 2), ("chunk_pages", c_int32 * 2),
         ("num_items", c_int32 * 2), ("items", I32P * 2), ("worker_indptr", I32P * 2),
         ("num_merges", c_int32), ("merges", I32P), ("num_parts", c_int32), ("parts", I32P),
         ("num_qlist", c_int32), ("qlist", I32P), ("num_part_rows", c_int32),

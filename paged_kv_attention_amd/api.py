@@ -137,9 +137,10 @@ class Plan:
         for l in range(inf.num_levels):
             levels.append(dict(
                 rows_per_block=inf.rows_per_block[l], chunk_pages=inf.chunk_pages[l],
+                num_workers=inf.num_workers[l], min_chunk_pages=inf.min_chunk_pages[l],
                 items=arr(inf.items[l], inf.num_items[l] * L.FI_ITEM_INTS).reshape(-1, L.FI_ITEM_INTS),
-                worker_indptr=arr(inf.worker_indptr[l], inf.num_workers + 1)))
-        return dict(kind=inf.kind, num_workers=inf.num_workers, levels=levels,
+                worker_indptr=arr(inf.worker_indptr[l], inf.num_workers[l] + 1)))
+        return dict(kind=inf.kind, levels=levels,
                     merges=arr(inf.merges, inf.num_merges * L.FI_MERGE_INTS).reshape(-1, L.FI_MERGE_INTS),
                     parts=arr(inf.parts, inf.num_parts), qlist=arr(inf.qlist, inf.num_qlist),
                     num_part_rows=inf.num_part_rows, num_scatter=inf.num_scatter,

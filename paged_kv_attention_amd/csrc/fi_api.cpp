@@ -65,7 +65,7 @@ AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, 
   AttnArgs a;
   a.items = at<int32_t>(p, p->lay.items[level]);
   a.worker_indptr = at<int32_t>(p, p->lay.windptr[level]);
-  a.num_workers = p->hp.level[level].num_items() > 0 ? p->hp.num_workers : 0;
+  a.num_workers = p->hp.level[level].num_items() > 0 ? p->hp.level[level].num_workers : 0;
   a.qlist = at<int32_t>(p, p->lay.qlist);
   a.q = (const uint16_t*)q;
   a.k_cache = (const uint16_t*)k;
@@ -83,6 +83,13 @@ AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, 
   a.page_size = d.page_size;
   a.page_shift = __builtin_ctz((unsigned)d.page_size);
   return a;
+}
+
+hipError_t launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStream_t s) {
+  const int D = p->hp.desc.head_dim;
+  if (p->hp.level[level].rows_per_block == ROWS_WIDE)
+    return launch_wide(a, D, p->hp.desc.kind == FI_KIND_CASCADE && level == 0, s);
+  return launch_decode(a, D, s);
 }
 
 fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
@@ -114,8 +121,7 @@ extern "C" fi_status fi_paged_decode(const fi_plan_t* p, const void* q, const vo
   const AttnArgs a =
       attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
   TimerScope t(s);
-  st = hip_status(launch_attention(a, p->hp.desc.head_dim, p->hp.level[0].rows_per_block, false, s),
-                  "attention launch");
+  st = hip_status(launch_level(p, 0, a, s), "attention launch");
   t.done();
   if (st != FI_OK) return st;
   return run_merge(p, o, lse, s);
@@ -153,8 +159,7 @@ extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const vo
   const AttnArgs a =
       attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
   TimerScope t(s);
-  st = hip_status(launch_attention(a, d.head_dim, p->hp.level[0].rows_per_block, false, s),
-                  "attention launch");
+  st = hip_status(launch_level(p, 0, a, s), "attention launch");
   t.done();
   if (st != FI_OK) return st;
   return run_merge(p, o, lse, s);
@@ -173,12 +178,11 @@ extern "C" fi_status fi_cascade(const fi_plan_t* p, const void* q, const void* k
   if (p->hp.level[0].num_items() > 0 && !prefix_indices)
     return set_error(FI_ERR_INVALID_ARG, "fi_cascade: NULL prefix_indices");
   hipStream_t s = (hipStream_t)stream;
-  const int D = p->hp.desc.head_dim;
   TimerScope t(s);
   for (int l = 0; l < 2; ++l) {
     const AttnArgs a =
         attn_args(p, l, q, k_cache, v_cache, kv_indices, prefix_indices, sm_scale, o, lse);
-    st = hip_status(launch_attention(a, D, p->hp.level[l].rows_per_block, l == 0, s), "attention launch");
+    st = hip_status(launch_level(p, l, a, s), "attention launch");
     if (st != FI_OK) return st;
   }
   t.done();

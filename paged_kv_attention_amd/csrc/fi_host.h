@@ -18,6 +18,8 @@ void clear_error();
 
 struct Level {
   int32_t rows_per_block = 0;
+  int32_t num_workers = 0;      // waves (decode-style) or workgroups (wide)
+  int32_t min_chunk_pages = 0;
   int32_t chunk_pages = 0;
   std::vector<int32_t> items;          // ITEM_INTS per item, grouped by worker
   std::vector<int32_t> worker_indptr;  // num_workers + 1
@@ -26,7 +28,6 @@ struct Level {
 
 struct HostPlan {
   fi_plan_desc desc{};     // defaults filled in
-  int32_t num_workers = 0;
   int32_t num_levels = 0;
   Level level[2];
   std::vector<int32_t> merges;   // MERGE_INTS per entry
@@ -45,7 +46,7 @@ struct Layout {
   size_t dev_bytes = 0;      // blob + fp32 partial states
 };
 
-Layout layout_for(int32_t num_workers, const size_t n_items[2], size_t n_merges,
+Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t n_merges,
                   size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
                   int32_t head_dim);
 

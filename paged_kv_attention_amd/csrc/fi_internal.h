@@ -33,11 +33,15 @@ enum ItemField {
 enum MergeField { M_QTOK = 0, M_HEAD0, M_NHEADS, M_OFF, M_N, MERGE_INTS };
 enum ItemFlag { FLAG_LIST_Q = 1, FLAG_PARTIAL = 2, FLAG_CAUSAL = 4, FLAG_PREFIX = 8 };
 
-// Query rows one wavefront carries through the MFMA tiles: 16 per row block.
-constexpr int ROWS_DECODE = 16;   // decode and cascade suffix: 1 block
-constexpr int ROWS_APPEND = 32;   // append: 2 blocks
-constexpr int ROWS_PREFIX = 64;   // cascade prefix: 4 blocks
+// Query rows per work item. Decode-style levels (decode, cascade suffix): one
+// 16-row MFMA block per wavefront worker. Wide levels (append, cascade
+// prefix): 128 rows per 4-wave workgroup worker sharing K/V through LDS.
+constexpr int ROWS_DECODE = 16;
+constexpr int ROWS_WIDE = 128;
 constexpr int WAVES_PER_BLOCK = 4;
+// A wide level plans num_cus * max(1, workers_per_cu / 2) workgroups and
+// chunks of at least WIDE_CHUNK_FACTOR * min_chunk_pages pages.
+constexpr int WIDE_CHUNK_FACTOR = 8;
 
 struct AttnArgs {
   const int32_t* items;
@@ -96,9 +100,11 @@ struct MergeStatesArgs {
   float* s_out;
 };
 
-// list_q: the level's query rows come through the member list (cascade prefix).
-hipError_t launch_attention(const AttnArgs& a, int head_dim, int rows_per_block, bool list_q,
-                            hipStream_t stream);
+// Decode-style level: one wavefront per worker (a.num_workers waves).
+hipError_t launch_decode(const AttnArgs& a, int head_dim, hipStream_t stream);
+// Wide level: one 4-wave workgroup per worker (a.num_workers workgroups);
+// list_q: query rows come through the member list (cascade prefix).
+hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream);

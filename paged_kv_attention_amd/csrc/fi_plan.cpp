@@ -61,7 +61,7 @@ void clear_error() { g_last_error.clear(); }
 
 static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-Layout layout_for(int32_t num_workers, const size_t n_items[2], size_t n_merges,
+Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t n_merges,
                   size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
                   int32_t head_dim) {
   Layout L;
@@ -73,7 +73,7 @@ Layout layout_for(int32_t num_workers, const size_t n_items[2], size_t n_merges,
   };
   for (int l = 0; l < 2; ++l) {
     L.items[l] = take(n_items[l] * ITEM_INTS);
-    L.windptr[l] = take((size_t)num_workers + 1);
+    L.windptr[l] = take((size_t)num_workers[l] + 1);
   }
   L.merges = take(n_merges * MERGE_INTS);
   L.parts = take(n_parts);
@@ -142,9 +142,10 @@ struct LevelBuild {
   std::vector<std::pair<int32_t, std::vector<int32_t>>> chunks;  // per unit: k, partial dsts
 };
 
-void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, int32_t S,
-                 bool all_partial, int32_t& next_row, LevelBuild& lb, Level& lv) {
+void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all_partial,
+                 int32_t& next_row, LevelBuild& lb, Level& lv) {
   const int32_t ps = d.page_size;
+  const int32_t S = lv.num_workers;
   // Per unit: its pieces (page range and, in balanced mode, the worker).
   struct Piece { int64_t p0, p1; int32_t worker; };
   std::vector<std::vector<Piece>> pieces(units.size());
@@ -159,7 +160,7 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, int32_t 
   } else {
     int64_t W = 0;
     for (const Unit& u : units) W += u.n_pages;
-    c = std::max<int64_t>({1, d.min_chunk_pages, ceil_div(W, S)});
+    c = std::max<int64_t>({1, lv.min_chunk_pages, ceil_div(W, S)});
     int64_t g = 0;   // global page offset of the unit
     for (size_t ui = 0; ui < units.size(); ++ui) {
       const int64_t n = units[ui].n_pages;
@@ -258,7 +259,7 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
     return set_error(FI_ERR_UNSUPPORTED, "page_size %d (supported: powers of two 8..256)",
                      d.page_size);
   const int32_t G = d.num_qo_heads / d.num_kv_heads;
-  if (d.kind == FI_KIND_CASCADE && (G > ROWS_DECODE || ROWS_PREFIX % G))
+  if (d.kind == FI_KIND_CASCADE && (G > ROWS_DECODE || ROWS_WIDE % G))
     return set_error(FI_ERR_UNSUPPORTED, "cascade needs a head group size dividing 16, got %d",
                      G);
   if (d.det_chunk_pages < 0 || d.min_chunk_pages < 0 || d.workers_per_cu < 0 ||
@@ -318,12 +319,21 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
         return set_error(FI_ERR_INVALID_ARG, "request %d: prefix group %d of %d", r,
                          req_group[r], NG);
   }
-  const int32_t S = hp.num_workers;
   int32_t next_row = 0;
+  auto decode_level = [&](Level& lv) {
+    lv.rows_per_block = ROWS_DECODE;
+    lv.num_workers = d.num_cus * d.workers_per_cu;
+    lv.min_chunk_pages = d.min_chunk_pages;
+  };
+  auto wide_level = [&](Level& lv) {
+    lv.rows_per_block = ROWS_WIDE;
+    lv.num_workers = d.num_cus * std::max(1, d.workers_per_cu / 2);
+    lv.min_chunk_pages = WIDE_CHUNK_FACTOR * d.min_chunk_pages;
+  };
   if (d.kind == FI_KIND_CASCADE) {
     hp.num_levels = 2;
-    hp.level[0].rows_per_block = ROWS_PREFIX;
-    hp.level[1].rows_per_block = ROWS_DECODE;
+    wide_level(hp.level[0]);
+    decode_level(hp.level[1]);
     std::vector<Unit> pu;
     std::vector<int32_t> group_off(NG, -1);
     for (int32_t grp = 0; grp < NG; ++grp) {
@@ -335,9 +345,9 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
       group_off[grp] = off;
       hp.qlist.insert(hp.qlist.end(), members.begin(), members.end());
       const int64_t rows = (int64_t)members.size() * G;
-      for (int64_t b = 0; b < ceil_div(rows, ROWS_PREFIX); ++b) {
-        const int32_t r0 = (int32_t)(b * ROWS_PREFIX);
-        const int32_t r1 = (int32_t)std::min<int64_t>(rows, (b + 1) * ROWS_PREFIX);
+      for (int64_t b = 0; b < ceil_div(rows, ROWS_WIDE); ++b) {
+        const int32_t r0 = (int32_t)(b * ROWS_WIDE);
+        const int32_t r1 = (int32_t)std::min<int64_t>(rows, (b + 1) * ROWS_WIDE);
         for (int32_t g = 0; g < Hkv; ++g) {
           Unit u;
           u.unit = grp;
@@ -357,8 +367,8 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
     std::vector<Unit> su;
     request_units(su, B, G, Hkv, ps, ROWS_DECODE, kv_indptr, kv_len, nullptr, false);
     LevelBuild lbp, lbs;
-    build_level(pu, d, S, true, next_row, lbp, hp.level[0]);
-    build_level(su, d, S, true, next_row, lbs, hp.level[1]);
+    build_level(pu, d, true, next_row, lbp, hp.level[0]);
+    build_level(su, d, true, next_row, lbs, hp.level[1]);
     // prefix partial rows of (request, kv head)
     std::vector<std::vector<int32_t>> pref((size_t)B * Hkv);
     for (size_t ui = 0; ui < pu.size(); ++ui) {
@@ -383,13 +393,13 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
   } else {
     hp.num_levels = 1;
     const bool append = d.kind == FI_KIND_APPEND;
-    const int32_t rpb = append ? ROWS_APPEND : ROWS_DECODE;
-    hp.level[0].rows_per_block = rpb;
+    if (append) wide_level(hp.level[0]); else decode_level(hp.level[0]);
+    const int32_t rpb = hp.level[0].rows_per_block;
     std::vector<Unit> units;
     request_units(units, B, G, Hkv, ps, rpb, kv_indptr, kv_len, append ? qo_indptr : nullptr,
                   append && d.causal);
     LevelBuild lb;
-    build_level(units, d, S, false, next_row, lb, hp.level[0]);
+    build_level(units, d, false, next_row, lb, hp.level[0]);
     for (size_t ui = 0; ui < units.size(); ++ui) {
       const Unit& u = units[ui];
       const int32_t k = lb.chunks[ui].first;
@@ -448,39 +458,44 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
             hipSuccess)
       return set_error(FI_ERR_HIP, "could not query the device's compute units");
   }
-  const int64_t S = (int64_t)num_cus * d.workers_per_cu;
+  const int64_t S_dec = (int64_t)num_cus * d.workers_per_cu;
+  const int64_t S_wide = (int64_t)num_cus * std::max(1, d.workers_per_cu / 2);
   const int64_t B = d.batch, Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
   const int64_t c_det = std::max(1, d.det_chunk_pages);
   size_t n_items[2] = {0, 0};
+  int32_t workers[2] = {0, 0};
   int64_t part_rows = 0, merges = 0;
-  auto level_bound = [&](int64_t units, int64_t pages_sum, int64_t rpb, bool all_partial) {
-    // balanced: items <= S + units; deterministic: items <= pages/c + units
-    int64_t items = d.deterministic ? pages_sum / c_det + units : S + units;
-    (void)all_partial;
+  // balanced: items <= S + units (every piece boundary is a quota or a unit
+  // boundary); deterministic: items <= pages / c + units
+  auto level_bound = [&](int64_t S, int64_t units, int64_t pages_sum, int64_t rpb) {
+    const int64_t items = d.deterministic ? pages_sum / c_det + units : S + units;
     part_rows += items * rpb;
     return items;
   };
   if (d.kind == FI_KIND_CASCADE) {
     const int64_t NG = d.num_prefix_groups;
-    const int64_t blocks = ceil_div(B * G, ROWS_PREFIX) + NG;
-    n_items[0] = (size_t)level_bound(blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_PREFIX,
-                                     true);
-    n_items[1] = (size_t)level_bound(B * Hkv, Hkv * max_kv_pages, ROWS_DECODE, true);
+    const int64_t blocks = ceil_div(B * G, ROWS_WIDE) + NG;
+    n_items[0] = (size_t)level_bound(S_wide, blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_WIDE);
+    n_items[1] = (size_t)level_bound(S_dec, B * Hkv, Hkv * max_kv_pages, ROWS_DECODE);
+    workers[0] = (int32_t)S_wide;
+    workers[1] = (int32_t)S_dec;
     merges = B * Hkv;
   } else if (d.kind == FI_KIND_APPEND) {
-    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_APPEND) + B;
-    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_APPEND) + 1;
-    n_items[0] = (size_t)level_bound(blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
-                                     ROWS_APPEND, false);
+    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;
+    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + 1;
+    n_items[0] = (size_t)level_bound(S_wide, blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
+                                     ROWS_WIDE);
+    workers[0] = (int32_t)S_wide;
     merges = part_rows + blocks * Hkv * 2;
   } else {
     const int64_t blocks = B * ceil_div(G, ROWS_DECODE);
-    n_items[0] = (size_t)level_bound(blocks * Hkv, Hkv * ceil_div(G, ROWS_DECODE) * max_kv_pages,
-                                     ROWS_DECODE, false);
+    n_items[0] = (size_t)level_bound(S_dec, blocks * Hkv,
+                                     Hkv * ceil_div(G, ROWS_DECODE) * max_kv_pages, ROWS_DECODE);
+    workers[0] = (int32_t)S_dec;
     merges = part_rows + blocks * Hkv * 2;
   }
   const size_t n_scatter = d.kind == FI_KIND_APPEND ? (size_t)max_qo_tokens : 0;
-  Layout L = layout_for((int32_t)S, n_items, (size_t)merges, (size_t)part_rows, (size_t)B,
+  Layout L = layout_for(workers, n_items, (size_t)merges, (size_t)part_rows, (size_t)B,
                         n_scatter, (size_t)part_rows, d.head_dim);
   *dev_bytes = L.dev_bytes;
   *host_bytes = L.blob_bytes;
@@ -512,7 +527,6 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
   }
   fi_plan_t* p = new fi_plan_t();
   p->hp.desc = d;
-  p->hp.num_workers = d.num_cus * d.workers_per_cu;
   st = build(d, kv_indptr_h, kv_len_h, qo_indptr_h, prefix_indptr_h, prefix_len_h,
              req_prefix_group_h, p->hp);
   if (st != FI_OK) {
@@ -521,7 +535,8 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
   }
   HostPlan& hp = p->hp;
   size_t n_items[2] = {(size_t)hp.level[0].num_items(), (size_t)hp.level[1].num_items()};
-  p->lay = layout_for(hp.num_workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
+  const int32_t workers[2] = {hp.level[0].num_workers, hp.level[1].num_workers};
+  p->lay = layout_for(workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
                       hp.qlist.size(), hp.scatter.size() / 2, (size_t)hp.num_part_rows,
                       d.head_dim);
   const Layout& L = p->lay;
@@ -588,8 +603,9 @@ extern "C" fi_status fi_plan_get_info(const fi_plan_t* p, fi_plan_info* info) {
   const HostPlan& hp = p->hp;
   info->kind = hp.desc.kind;
   info->num_levels = hp.num_levels;
-  info->num_workers = hp.num_workers;
   for (int l = 0; l < 2; ++l) {
+    info->num_workers[l] = hp.level[l].num_workers;
+    info->min_chunk_pages[l] = hp.level[l].min_chunk_pages;
     info->rows_per_block[l] = hp.level[l].rows_per_block;
     info->chunk_pages[l] = hp.level[l].chunk_pages;
     info->num_items[l] = hp.level[l].num_items();

@@ -1,0 +1,221 @@
+// fi_wide.hip -- multi-row paged attention for gfx950: append (prefill and
+// mixed batches, optionally causal) and the shared-prefix level of cascade.
+//
+// A work item is (up to 128 query rows, kv head g, token range of one
+// sequence). One 4-wave workgroup runs an item: every 32-token step of K and V
+// is copied once into LDS and consumed by all 128 rows (32 per wave), so the
+// bytes read from HBM per query row drop by the row count (backend-selection
+// note, "Arithmetic intensity": cascade reads a shared prefix once and reuses
+// it across requests; a prefill tile does the same within one request).
+//
+// Staging. Three LDS stages of (K, V) per step; the loads are global->LDS
+// direct copies (global_load_lds_dwordx4: each lane's 16 bytes land at
+// base + 16*lane), so staging costs no VGPRs and two further steps stay in
+// flight while one is computed. The wait for a step is an explicit vmcnt
+// count of this wave's own copies issued after it, followed by a bare
+// s_barrier (no fence, which would drain every outstanding load). K rows are
+// stored with their 16-byte chunks XOR-swizzled by the token (chunk c of
+// token t at slot c ^ (t mod D/8)), so the MFMA operand reads -- 16 lanes
+// reading the same chunk of 16 different tokens -- hit distinct banks. V rows
+// are stored as they are: the operand reads already cover whole rows.
+//
+// Compute per wave and step: the same transposed-output MFMA tiling as the
+// decode kernel (S^T = K.Q^T, O^T += V^T.P^T on v_mfma_f32_16x16x32_bf16) for
+// two 16-row blocks. Masks (sequence tail, bottom-right causal) are applied
+// only on steps that need them.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fi_device.h"
+
+namespace fi {
+namespace {
+
+using namespace dev;
+
+constexpr int kStages = 3;
+constexpr int kRowsPerWave = 32;   // two 16-row MFMA blocks
+
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef const __attribute__((address_space(1))) void* global_vptr;
+
+// s_waitcnt vmcnt(n) with no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int D>
+struct Lds {
+  static constexpr int ROW = D * 2;           // bytes per K/V row
+  static constexpr int AREA = 32 * ROW;       // K (or V) of one step
+  static constexpr int STAGE = 2 * AREA;
+  static constexpr int NK = (32 * Cfg<D>::CH) / 256;   // copies per wave per area
+};
+
+// Copy step s of item it into LDS stage st (this wave's share: NK 1-KiB
+// copies for K and NK for V).
+template <int D, int NP>
+__device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, int s, char* stage,
+                                           int wave, int lane) {
+  constexpr int CH = Cfg<D>::CH, NK = Lds<D>::NK, ROW = Lds<D>::ROW;
+  const int sh = a.page_shift;
+  const int T0 = it.t_begin + 32 * s;
+  const int pb = T0 >> sh;
+  const int plast = (it.t_end - 1) >> sh;
+  const int64_t tile_bytes = (int64_t)a.page_size * ROW;
+  int64_t poff[NP];
+#pragma unroll
+  for (int n = 0; n < NP; ++n) {
+    const int pid = ld_uniform(it.plist, min(pb + n, plast));
+    poff[n] = ((int64_t)pid * a.num_kv_heads + it.g) * tile_bytes;
+  }
+  const int slot0 = (NP == 1) ? (T0 & (a.page_size - 1)) : 0;
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int blk = wave * NK + k;           // 1-KiB block of the area
+    const int p = blk * 64 + lane;           // 16-byte slot in the area
+    const int t = p / CH, cs = p % CH;       // token of the step, stored chunk slot
+    int64_t off;
+    if (NP == 1) {
+      off = poff[0] + (int64_t)(slot0 + t) * ROW;
+    } else if (NP == 2) {
+      off = (t >> 4 ? poff[1] : poff[0]) + (int64_t)(t & 15) * ROW;
+    } else {
+      const int rel = t >> 3;
+      off = (rel == 0 ? poff[0] : rel == 1 ? poff[1] : rel == 2 ? poff[2] : poff[3]) +
+            (int64_t)(t & 7) * ROW;
+    }
+    const int kc = cs ^ (t % CH);            // K: swizzled chunk
+    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.k_cache + off + kc * 16),
+                                     (lds_vptr)(stage + blk * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.v_cache + off + cs * 16),
+                                     (lds_vptr)(stage + Lds<D>::AREA + blk * 1024), 16, 0, 0);
+  }
+}
+
+// One step of a workgroup item: copy step s+2 into `next` (if any), then, for
+// s >= 0, read step s's K/V fragments from `cur` and compute. Every copy of the
+// item goes through this one call site and the two stage pointers are
+// __restrict__: the compiler then knows the copies into `next` cannot alias
+// the reads from `cur` and adds no wait of its own; the ordering across steps
+// is the explicit vmcnt wait plus barrier in the caller.
+template <int D, int NP>
+__device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int s, bool issue,
+                                          char* __restrict__ next, const char* __restrict__ cur,
+                                          const u32x4 (&qf)[2][Cfg<D>::KJ], State<D, 2>& st,
+                                          int rl0, int wave, int lane) {
+  constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL, CH = Cfg<D>::CH, ROW = Lds<D>::ROW;
+  typedef typename Cfg<D>::vrow_t vrow_t;
+  const int col = lane & 15, grp = lane >> 4;
+  if (issue) issue_step<D, NP>(a, it, s + 2, next, wave, lane);
+  if (s < 0) return;
+  const char* vst = cur + Lds<D>::AREA;
+  const int T0 = it.t_begin + 32 * s;
+  const bool tail = T0 + 32 > it.t_end;
+  u32x4 kf[2][KJ];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int t = 16 * blk + col;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+      kf[blk][j] = *(const u32x4*)(cur + t * ROW + ((4 * j + grp) ^ (t % CH)) * 16);
+  }
+  vrow_t vv[8];
+#pragma unroll
+  for (int ii = 0; ii < 8; ++ii) {
+    const int tl = (ii < 4) ? 4 * grp + ii : 16 + 4 * grp + (ii - 4);
+    vv[ii] = *(const vrow_t*)(vst + tl * ROW + col * DPL * 2);
+    if (tail && T0 + tl >= it.t_end) vv[ii] = vrow_t{};
+  }
+  u32x4 vt[DPL];
+  transpose_v<D>(vv, vt);
+  const bool causal = (it.flags & FLAG_CAUSAL) != 0;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+      s0 = mfma_bf16(kf[0][j], qf[mb][j], s0);
+      s1 = mfma_bf16(kf[1][j], qf[mb][j], s1);
+    }
+    const int row_first = it.row0 + rl0 + mb * 16;
+    int lim = it.t_end - 1;
+    bool masked = tail;
+    if (causal) {
+      masked = masked || T0 + 31 > it.q_pos0 + row_first / a.group;
+      lim = min(lim, it.q_pos0 + (row_first + col) / a.group);
+    }
+    softmax_pv<D, 2>(st, mb, s0, s1, vt, a.scale_log2, masked, T0, lim, grp);
+  }
+}
+
+template <int D, int NP, bool LQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wide_kernel(AttnArgs a) {
+  constexpr int KJ = Cfg<D>::KJ, NK = Lds<D>::NK;
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * Lds<D>::STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, grp = lane >> 4;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int wg = blockIdx.x;
+  if (wg >= a.num_workers) return;
+  const int i_end = ld_uniform(a.worker_indptr, wg + 1);
+  const int rl0 = wave * kRowsPerWave;
+
+  for (int i = ld_uniform(a.worker_indptr, wg); i < i_end; ++i) {
+    const Item it = load_item(a, i);
+    u32x4 qf[2][KJ];
+    load_q_rows<D, 2, LQ>(a, it, rl0, qf, col, grp);
+    State<D, 2> st;
+    st.reset();
+    const int n = it.nsteps;
+    int stage_c = 1;                          // stage of step s: s mod 3 (s = -2 -> 1)
+    for (int s = -2; s < n; ++s) {
+      if (s >= 0) {
+        // this wave's copies of step s are done when at most those of step s+1
+        // are outstanding; the barrier then publishes every wave's copies, and
+        // tells every wave that step s-1's stage (which step s+2 reuses) has
+        // been read by all
+        if (s + 1 < n) wait_vmcnt<2 * NK>(); else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      const int st2 = stage_c >= 1 ? stage_c - 1 : stage_c + 2;   // (s + 2) mod 3
+      wide_step<D, NP>(a, it, s, s + 2 < n, lds + st2 * Lds<D>::STAGE,
+                       lds + stage_c * Lds<D>::STAGE, qf, st, rl0, wave, lane);
+      stage_c = stage_c == 2 ? 0 : stage_c + 1;
+    }
+    finalize_rows<D, 2, LQ>(a, it, st, rl0, col, grp);
+    __builtin_amdgcn_s_barrier();   // every wave is done with the stages
+    asm volatile("" ::: "memory");
+  }
+}
+
+template <int D, bool LQ>
+hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  if (a.page_size == 8) {
+    hipLaunchKernelGGL((wide_kernel<D, 4, LQ>), grid, dim3(256), 0, s, a);
+  } else if (a.page_size == 16) {
+    hipLaunchKernelGGL((wide_kernel<D, 2, LQ>), grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((wide_kernel<D, 1, LQ>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream) {
+  if (a.num_workers == 0) return hipSuccess;
+  const dim3 grid(a.num_workers);
+  if (head_dim == 128)
+    return list_q ? launch_np<128, true>(a, grid, stream) : launch_np<128, false>(a, grid, stream);
+  if (head_dim == 64)
+    return list_q ? launch_np<64, true>(a, grid, stream) : launch_np<64, false>(a, grid, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fi

@@ -44,6 +44,14 @@ def host_plan(kind, indptr, lens, Hq, Hkv, D, ps, **kw):
     return fi.Plan(kind, indptr, lens, Hq, Hkv, D, ps, device=None, **kw)
 
 
+def level_params(info):
+    """Per-level workers, rows per block and minimum chunk, as plan_ref takes them."""
+    lv = info["levels"]
+    return dict(num_workers=[x["num_workers"] for x in lv],
+                rows_per_block=[x["rows_per_block"] for x in lv],
+                min_chunk_pages=[x["min_chunk_pages"] for x in lv])
+
+
 def compare(info, ref):
     assert len(info["levels"]) == len(ref["levels"])
     for lv, rl in zip(info["levels"], ref["levels"]):
@@ -67,8 +75,9 @@ def test_decode_plan_matches_reference(det, ps, Hq, Hkv):
               workers_per_cu=5)
     p = host_plan("decode", indptr, L_, Hq, Hkv, 128, ps, **kw)
     info = p.info()
-    ref = plan_ref("decode", Hq, Hkv, ps, indptr, L_, 35, [info["levels"][0]["rows_per_block"]],
-                   deterministic=det, det_chunk_pages=16, min_chunk_pages=4)
+    assert info["levels"][0]["num_workers"] == 35
+    ref = plan_ref("decode", Hq, Hkv, ps, indptr, L_, **level_params(info),
+                   deterministic=det, det_chunk_pages=16)
     compare(info, ref)
 
 
@@ -86,9 +95,9 @@ def test_append_plan_matches_reference(causal, det):
     p = host_plan("append", indptr, L_, 32, 8, 128, ps, qo_indptr=qo_indptr, causal=causal,
                   deterministic=det, det_chunk_pages=8, num_cus=4, workers_per_cu=8)
     info = p.info()
-    ref = plan_ref("append", 32, 8, ps, indptr, L_, 32, [info["levels"][0]["rows_per_block"]],
-                   deterministic=det, det_chunk_pages=8, min_chunk_pages=8, qo_indptr=qo_indptr,
-                   causal=causal)
+    assert info["levels"][0]["rows_per_block"] == 128 and info["levels"][0]["num_workers"] == 16
+    ref = plan_ref("append", 32, 8, ps, indptr, L_, **level_params(info),
+                   deterministic=det, det_chunk_pages=8, qo_indptr=qo_indptr, causal=causal)
     compare(info, ref)
     assert info["num_scatter"] == int(qo.sum())
 
@@ -105,10 +114,8 @@ def test_cascade_plan_matches_reference(det):
     p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
                   req_prefix_group=groups, deterministic=det, num_cus=16, workers_per_cu=4)
     info = p.info()
-    rpb = [lv["rows_per_block"] for lv in info["levels"]]
-    ref = plan_ref("cascade", 32, 8, ps, indptr, L_, 64, rpb, deterministic=det,
-                   det_chunk_pages=64, min_chunk_pages=8, prefix_indptr=pindptr, prefix_len=PL,
-                   req_group=groups)
+    ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info), deterministic=det,
+                   det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups)
     compare(info, ref)
 
 
