@@ -103,6 +103,7 @@ fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
   m.lse = lse;
   m.num_qo_heads = p->hp.desc.num_qo_heads;
   m.head_dim = p->hp.desc.head_dim;
+  m.group = p->hp.desc.num_qo_heads / p->hp.desc.num_kv_heads;
   return hip_status(launch_merge(m, s), "merge launch");
 }
 

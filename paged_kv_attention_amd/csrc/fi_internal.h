@@ -41,7 +41,7 @@ constexpr int ROWS_WIDE = 128;
 constexpr int WAVES_PER_BLOCK = 4;
 // A wide level plans num_cus * max(1, workers_per_cu / 2) workgroups and
 // chunks of at least WIDE_CHUNK_FACTOR * min_chunk_pages pages.
-constexpr int WIDE_CHUNK_FACTOR = 8;
+constexpr int WIDE_CHUNK_FACTOR = 2;
 
 struct AttnArgs {
   const int32_t* items;
@@ -75,6 +75,7 @@ struct MergeArgs {
   float* lse;
   int32_t num_qo_heads;
   int32_t head_dim;
+  int32_t group;   // q heads per kv head: no record has more rows
 };
 
 struct ScatterArgs {

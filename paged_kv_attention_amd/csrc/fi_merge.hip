@@ -43,59 +43,131 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int i) {
   return __builtin_amdgcn_readfirstlane(((const_i32p)p)[i]);
 }
 
-constexpr int kBatch = 8;   // partial states whose loads are in flight together
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
 
-// One wavefront per merge record; each lane owns 4 consecutive outputs. The
-// loads of kBatch partial states are issued together; the fold itself runs
-// j = 0, 1, ... in order, so batching does not change any rounding.
+__device__ __forceinline__ float readlane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+
+template <int N> struct FVec { typedef float T __attribute__((ext_vector_type(N))); };
+template <> struct FVec<1> { typedef float T; };
+
+// One wavefront per RPW rows of a merge record (RPW = 1, 2 or 4: fewer,
+// fuller waves when there are many records). Lane j holds part j's row index
+// and the lse of each of the wave's rows (64 parts per pass), the wave
+// reduces each row's max, and each lane folds FPL consecutive outputs of one
+// row over the parts, its weight broadcast by readlane. Loads of up to kFold
+// parts (32 floats a lane) are in flight together (only parts that exist are loaded); the fold
+// itself runs j = 0, 1, ... in order (z and acc each a plain left fold), so no
+// rounding depends on the batching or on which wave runs it.
+template <int D, int RPW>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  constexpr int LPR = 64 / RPW;   // lanes per row
+  constexpr int FPL = D / LPR;    // outputs per lane
+  constexpr int kFold = FPL >= 8 ? 4 : FPL == 4 ? 8 : 16;   // parts in flight (32 floats)
+  typedef typename FVec<FPL>::T vec;
   const int lane = threadIdx.x & 63;
-  const int e = blockIdx.x * WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wv = blockIdx.x * WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int groups = (a.group + RPW - 1) / RPW;
+  const int e = wv / groups;
+  const int h0 = (wv - e * groups) * RPW;
   if (e >= a.num_merges) return;
   const int32_t* m = a.merges + (int64_t)e * MERGE_INTS;
+  const int nh = ld_uniform(m, M_NHEADS);
+  if (h0 >= nh) return;
+  const int rows = min(RPW, nh - h0);
   const int q_tok = ld_uniform(m, M_QTOK), head0 = ld_uniform(m, M_HEAD0);
-  const int nh = ld_uniform(m, M_NHEADS), off = ld_uniform(m, M_OFF), n = ld_uniform(m, M_N);
+  const int off = ld_uniform(m, M_OFF), n = ld_uniform(m, M_N);
   const int32_t* parts = a.parts + off;
-  const int D = a.head_dim;
-  const int total = nh * D;
-  for (int e0 = lane * 4; e0 < total; e0 += 256) {
-    const int h = e0 / D, d = e0 - h * D;
-    float M = neg_inf();
-    for (int j0 = 0; j0 < n; j0 += kBatch) {
-      float l[kBatch];
+  const int rl = lane / LPR;                 // this lane's row within the wave
+  const int rlc = min(rl, rows - 1);         // clamped to a real row for loads
+  const int col = (lane % LPR) * FPL;
+
+  // parts 0..63 stay in registers; longer lists are re-read per pass
+  int prow0 = 0;
+  float l0[RPW];
+  if (lane < n) prow0 = parts[lane] + h0;
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) l[u] = a.part_lse[ld_uniform(parts, min(j0 + u, n - 1)) + h];
+  for (int r = 0; r < RPW; ++r) l0[r] = (lane < n && r < rows) ? a.part_lse[prow0 + r] : neg_inf();
+  float M[RPW];
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) M = fmaxf(M, l[u]);
+  for (int r = 0; r < RPW; ++r) M[r] = l0[r];
+  for (int j0 = 64; j0 < n; j0 += 64) {
+    if (j0 + lane < n) {
+      const int pr = parts[j0 + lane] + h0;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        if (r < rows) M[r] = fmaxf(M[r], a.part_lse[pr + r]);
     }
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    float z = 0.f;
-    if (M != neg_inf()) {
-      for (int j0 = 0; j0 < n; j0 += kBatch) {
-        float l[kBatch];
-        f32x4 v[kBatch];
+  }
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          const int row = ld_uniform(parts, min(j0 + u, n - 1)) + h;
-          l[u] = a.part_lse[row];
-          v[u] = *(const f32x4*)(a.part_o + (int64_t)row * D + d);
-        }
+  for (int r = 0; r < RPW; ++r) M[r] = wave_max(M[r]);
+
+  vec acc = vec{};
+  float z = 0.f;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    int prow = prow0;
+    float l[RPW];
 #pragma unroll
-        for (int u = 0; u < kBatch; ++u) {
-          if (j0 + u < n) {
-            const float w = (l[u] == neg_inf()) ? 0.f : expf(l[u] - M);
-            z += w;
-            acc += w * v[u];
+    for (int r = 0; r < RPW; ++r) l[r] = l0[r];
+    if (j0 > 0) {
+      prow = 0;
+      if (j0 + lane < n) prow = parts[j0 + lane] + h0;
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        l[r] = (j0 + lane < n && r < rows) ? a.part_lse[prow + r] : neg_inf();
+    }
+    float w[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) w[r] = (l[r] == neg_inf()) ? 0.f : expf(l[r] - M[r]);
+    const int cnt = min(64, n - j0);
+    for (int b = 0; b < cnt; b += kFold) {
+      vec v[kFold];
+      float wb[kFold];
+#pragma unroll
+      for (int u = 0; u < kFold; ++u) {
+        if (b + u < cnt) {
+          const int r0 = __builtin_amdgcn_readlane(prow, b + u);
+          float ws = readlane_f(w[0], b + u);
+#pragma unroll
+          for (int r = 1; r < RPW; ++r) {
+            const float wr = readlane_f(w[r], b + u);
+            ws = (rl == r) ? wr : ws;
           }
+          wb[u] = ws;
+          v[u] = *(const vec*)(a.part_o + (int64_t)(r0 + rlc) * D + col);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kFold; ++u) {
+        if (b + u < cnt) {
+          z += wb[u];
+          acc += wb[u] * v[u];
         }
       }
     }
-    const float inv = z > 0.f ? 1.f / z : 0.f;
-    const int64_t orow = (int64_t)q_tok * a.num_qo_heads + head0 + h;
-    u32x2 packed = {pack2(acc[0] * inv, acc[1] * inv), pack2(acc[2] * inv, acc[3] * inv)};
-    *(u32x2*)(a.o + orow * D + d) = packed;
-    if (d == 0 && a.lse) a.lse[orow] = z > 0.f ? M + logf(z) : neg_inf();
   }
+  if (rl >= rows) return;
+  float mr = M[0];
+#pragma unroll
+  for (int r = 1; r < RPW; ++r) mr = (rl == r) ? M[r] : mr;
+  const float inv = z > 0.f ? 1.f / z : 0.f;
+  const int64_t orow = (int64_t)q_tok * a.num_qo_heads + head0 + h0 + rl;
+  uint16_t* op = a.o + orow * D + col;
+  if constexpr (FPL == 1) {
+    *op = (uint16_t)(pack2(acc * inv, 0.f) & 0xffffu);
+  } else {
+    typedef uint32_t packed_t __attribute__((ext_vector_type(FPL / 2)));
+    packed_t pk;
+#pragma unroll
+    for (int i = 0; i < FPL / 2; ++i) pk[i] = pack2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    *(packed_t*)op = pk;
+  }
+  if (col == 0 && a.lse) a.lse[orow] = z > 0.f ? mr + logf(z) : neg_inf();
 }
 
 // One wavefront per (n, h) row of fi_merge_states.
@@ -157,13 +229,32 @@ __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
   *(u32x4*)(a.v_cache + dst) = *(const u32x4*)(a.v_new + src);
 }
 
+template <int D>
+hipError_t launch_merge_d(const MergeArgs& a, hipStream_t stream) {
+  // Rows per wave: one while that keeps the wave count within about four per
+  // SIMD of a 256-CU chip, else 2 or 4 (each wave's time is mostly load
+  // latency, so fewer, fuller waves win once there are many records).
+  const int64_t rows = (int64_t)a.num_merges * a.group;
+  const int rpw = rows <= 4096 ? 1 : rows <= 8192 ? 2 : 4;
+  const int64_t waves = (int64_t)a.num_merges * ((a.group + rpw - 1) / rpw);
+  const dim3 grid((unsigned)((waves + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));
+  if (rpw == 1) {
+    hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(256), 0, stream, a);
+  } else if (rpw == 2) {
+    hipLaunchKernelGGL((merge_kernel<D, 2>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL((merge_kernel<D, 4>), grid, dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   if (a.num_merges == 0) return hipSuccess;
-  const int blocks = (a.num_merges + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
-  hipLaunchKernelGGL(merge_kernel, dim3(blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  if (a.head_dim == 128) return launch_merge_d<128>(a, stream);
+  if (a.head_dim == 64) return launch_merge_d<64>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream) {

@@ -151,6 +151,21 @@ def test_decode_small_sweep(dev, D, ps, G):
         compare(o, lse, o_ref, l_ref, a_ref, what=f"decode D={D} ps={ps} G={G} {kw}")
 
 
+@pytest.mark.parametrize("B,D,rows_min,rows_max", [(150, 128, 4097, 8192), (300, 64, 8193, None),
+                                                   (300, 128, 8193, None)])
+def test_decode_many_merge_records(dev, B, D, rows_min, rows_max):
+    """One-page chunks split every request, so the merge runs with many
+    records: two and four rows per merge wave."""
+    Hkv, G, ps = 8, 4, 16
+    lens = torch.randint(17, 121, (B,), generator=torch.Generator().manual_seed(B + D)).tolist()
+    w = make_decode(lens, G * Hkv, Hkv, D, ps, seed=300 + B + D)
+    o, lse, p = gpu_decode(w, dev, deterministic=True, det_chunk_pages=1)
+    rows = len(p.info()["merges"]) * G
+    assert rows >= rows_min and (rows_max is None or rows <= rows_max), rows
+    o_ref, l_ref, a_ref = oracle_decode(w)
+    compare(o, lse, o_ref, l_ref, a_ref, what=f"decode many merges B={B} D={D}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 2), (128, 32, 8), (64, 16, 24)])
 def test_append_small_sweep(dev, causal, D, ps, G):
