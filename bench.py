@@ -104,7 +104,7 @@ def explore(args, dev):
     w = make_config(args.config, poison=False)
     g = w.to(dev)
     kw = dict(deterministic=args.mode == "deterministic", workers_per_cu=args.workers_per_cu,
-              min_chunk_pages=args.min_chunk_pages)
+              min_chunk_pages=args.min_chunk_pages, engine=args.engine)
     if w.kind == "decode":
         plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, device=dev, **kw)
@@ -146,6 +146,7 @@ def explore(args, dev):
     kern_ms = kt.total_ms / max(1, kt.calls)
     kv = w.kv_bytes()
     print(json.dumps({"workload": CONFIG_NAMES[args.config], "mode": args.mode,
+                      "engine": args.engine,
                       "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
                       "kv_bytes": kv, "kv_GBps": round(kv / ms / 1e6, 1),
                       "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
@@ -161,6 +162,8 @@ def main():
     ap.add_argument("--mode", choices=("balanced", "deterministic"), default="balanced")
     ap.add_argument("--workers-per-cu", type=int, default=0)
     ap.add_argument("--min-chunk-pages", type=int, default=0)
+    ap.add_argument("--engine", choices=("default", "mfma", "valu"), default="default",
+                    help="units for the decode-style levels")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -189,7 +192,8 @@ def main():
     nbytes = algorithmic_bytes(w)
 
     plan_kw = dict(deterministic=args.mode == "deterministic",
-                   workers_per_cu=args.workers_per_cu, min_chunk_pages=args.min_chunk_pages)
+                   workers_per_cu=args.workers_per_cu, min_chunk_pages=args.min_chunk_pages,
+                   engine=args.engine)
     t0 = time.perf_counter()
     plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                    w.page_size, device=dev, **plan_kw)
@@ -259,7 +263,7 @@ def main():
         "config": {"workload": CONFIG_NAMES[CONFIG_INDEX], "batch": w.batch,
                    "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads,
                    "head_dim": w.head_dim, "page_size": w.page_size,
-                   "kv_len": "uniform [512, 4096]", "seed": w.seed, "mode": args.mode,
+                   "kv_len": "uniform [512, 4096]", "seed": w.seed, "mode": args.mode, "engine": args.engine,
                    "kv_tokens": int(w.kv_len.sum())},
         "us_per_call": round(ms_per_step * 1e3, 2),
         "pct_of_peak": round(100 * gbs / HBM_PEAK_GBS, 2),

@@ -69,6 +69,17 @@ typedef enum fi_kind {
 
 typedef enum fi_dtype { FI_DTYPE_BF16 = 0, FI_DTYPE_F32 = 1 } fi_dtype;
 
+/* Which units run the decode-style levels (decode, and the per-request suffix
+ * level of cascade). Both give the same result within the stated tolerance;
+ * the choice is a measured speed question (the research note's "Arithmetic
+ * intensity" places decode in the memory-bound regime, where either unit can
+ * keep up with HBM). */
+typedef enum fi_engine {
+  FI_ENGINE_DEFAULT = 0, /* the engine measured faster on gfx950 (see fi_plan)   */
+  FI_ENGINE_MFMA = 1,    /* bf16 matrix cores, v_mfma_f32_16x16x32_bf16           */
+  FI_ENGINE_VALU = 2     /* vector ALU only, v_dot2_f32_bf16; head group <= 8     */
+} fi_engine;
+
 /* Plan description. Zero in an optional field selects its default. */
 typedef struct fi_plan_desc {
   int32_t kind;              /* fi_kind                                        */
@@ -84,6 +95,7 @@ typedef struct fi_plan_desc {
   int32_t num_cus;           /* compute units to plan for (0 = current device) */
   int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 4) */
   int32_t num_prefix_groups; /* cascade: number of shared prefixes             */
+  int32_t decode_engine;     /* fi_engine for decode-style levels (default 0)  */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;

@@ -17,6 +17,7 @@ import torch
 from . import _lib as L
 
 _KINDS = {"decode": L.FI_KIND_DECODE, "append": L.FI_KIND_APPEND, "cascade": L.FI_KIND_CASCADE}
+_ENGINES = {"default": L.FI_ENGINE_DEFAULT, "mfma": L.FI_ENGINE_MFMA, "valu": L.FI_ENGINE_VALU}
 
 
 def _host_i32(x) -> Optional[np.ndarray]:
@@ -66,7 +67,8 @@ class Plan:
                  head_dim: int, page_size: int, *, qo_indptr=None, causal: bool = False,
                  prefix_indptr=None, prefix_len=None, req_prefix_group=None,
                  deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
-                 num_cus: int = 0, workers_per_cu: int = 0, device="cuda",
+                 num_cus: int = 0, workers_per_cu: int = 0, engine: str = "default",
+                 device="cuda",
                  workspace: Optional[Workspace] = None):
         lib = L.load()
         self.kind = kind
@@ -82,7 +84,7 @@ class Plan:
                                deterministic=int(deterministic),
                                det_chunk_pages=det_chunk_pages, min_chunk_pages=min_chunk_pages,
                                num_cus=num_cus, workers_per_cu=workers_per_cu,
-                               num_prefix_groups=ng)
+                               num_prefix_groups=ng, decode_engine=_ENGINES[engine])
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim, self.page_size, self.batch = head_dim, page_size, B
         self.device = None if device is None else torch.device(device)

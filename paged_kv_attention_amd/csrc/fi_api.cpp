@@ -89,6 +89,7 @@ hipError_t launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStr
   const int D = p->hp.desc.head_dim;
   if (p->hp.level[level].rows_per_block == ROWS_WIDE)
     return launch_wide(a, D, p->hp.desc.kind == FI_KIND_CASCADE && level == 0, s);
+  if (p->hp.desc.decode_engine == FI_ENGINE_VALU) return launch_decode_valu(a, D, s);
   return launch_decode(a, D, s);
 }
 

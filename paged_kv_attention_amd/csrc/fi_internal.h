@@ -103,6 +103,7 @@ struct MergeStatesArgs {
 
 // Decode-style level: one wavefront per worker (a.num_workers waves).
 hipError_t launch_decode(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_valu(const AttnArgs& a, int head_dim, hipStream_t stream);
 // Wide level: one 4-wave workgroup per worker (a.num_workers workgroups);
 // list_q: query rows come through the member list (cascade prefix).
 hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream);

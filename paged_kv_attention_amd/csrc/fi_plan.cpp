@@ -242,6 +242,10 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
 
 }  // namespace
 
+// Engine for decode-style levels when the caller leaves the choice open: the
+// one that measured faster for decode on MI355X.
+static constexpr int32_t kDefaultEngine = FI_ENGINE_MFMA;
+
 static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (!din) return set_error(FI_ERR_INVALID_ARG, "desc is NULL");
   d = *din;
@@ -265,6 +269,12 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.det_chunk_pages < 0 || d.min_chunk_pages < 0 || d.workers_per_cu < 0 ||
       d.num_cus < 0 || d.num_prefix_groups < 0)
     return set_error(FI_ERR_INVALID_ARG, "negative tuning field in desc");
+  if (d.decode_engine < FI_ENGINE_DEFAULT || d.decode_engine > FI_ENGINE_VALU)
+    return set_error(FI_ERR_INVALID_ARG, "decode_engine %d", d.decode_engine);
+  if (d.decode_engine == FI_ENGINE_DEFAULT) d.decode_engine = kDefaultEngine;
+  if (d.decode_engine == FI_ENGINE_VALU && G > 8)
+    return set_error(FI_ERR_UNSUPPORTED, "the VALU decode engine takes head groups <= 8, got %d",
+                     G);
   if (d.det_chunk_pages == 0) d.det_chunk_pages = 64;
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
   if (d.workers_per_cu == 0) d.workers_per_cu = 4;

@@ -229,6 +229,21 @@ def test_cascade_rejects_bad_group_and_grouping():
     assert st == L.FI_ERR_UNSUPPORTED, msg
 
 
+def test_decode_engine_field():
+    d = _desc(decode_engine=L.FI_ENGINE_VALU)                       # G = 4
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS)
+    assert st == L.FI_OK, msg
+    d = _desc(decode_engine=L.FI_ENGINE_VALU, num_qo_heads=32, num_kv_heads=2)   # G = 16
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS)
+    assert st == L.FI_ERR_UNSUPPORTED and "VALU" in msg, msg
+    d = _desc(decode_engine=L.FI_ENGINE_MFMA, num_qo_heads=32, num_kv_heads=2)
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS)
+    assert st == L.FI_OK, msg
+    for bad in (-1, 3):
+        st, msg = _raw_plan(_desc(decode_engine=bad), GOOD_INDPTR, GOOD_LENS)
+        assert st == L.FI_ERR_INVALID_ARG, msg
+
+
 def test_run_calls_refuse_without_device_plan():
     lib = fi.load()
     assert lib.fi_paged_decode(None, None, None, None, None, 1.0, None, None, None) == \

@@ -321,3 +321,44 @@ def test_merge_states_api(dev, dtype):
     assert np.array_equal(np.isneginf(so.cpu().numpy()), ~fin)
     assert np.allclose(so.cpu().numpy()[fin], l_ref[fin], atol=1e-5, rtol=1e-6)
     assert torch.all(vo[0, 1] == 0)
+
+
+# ---------------------------------------------------------------- VALU engine
+
+
+def test_valu_engine_configs(dev, cfg1):
+    w = make_config(0, poison=True)
+    o, lse, _ = gpu_decode(w, dev, engine="valu")
+    o_ref, l_ref, a_ref = oracle_decode(w)
+    compare(o, lse, o_ref, l_ref, a_ref, what="tiny_decode valu")
+    w = cfg1
+    rng = np.random.default_rng(11)
+    reqs = sample_requests(w.batch, 10, rng, must=[int(torch.argmax(w.kv_len))])
+    o_ref, l_ref, a_ref = oracle_decode(w, requests=reqs)
+    for det in (False, True):
+        o, lse, _ = gpu_decode(w, dev, engine="valu", deterministic=det)
+        compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs),
+                what=f"llama_decode valu det={det}")
+    o2, lse2, _ = gpu_decode(w, dev, engine="valu", deterministic=True)
+    assert torch.equal(o, o2) and torch.equal(lse, lse2), "VALU runs differ"
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("G", [1, 3, 4, 8])
+def test_valu_decode_small_sweep(dev, D, ps, G):
+    Hkv = 2
+    w = make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=400 + D + ps + G)
+    o_ref, l_ref, a_ref = oracle_decode(w)
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+        o, lse, _ = gpu_decode(w, dev, engine="valu", **kw)
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"valu decode D={D} ps={ps} G={G} {kw}")
+
+
+def test_valu_engine_cascade(dev):
+    w = make_config(3, poison=True)
+    o, lse = _cascade_run(w, dev, engine="valu")
+    rng = np.random.default_rng(13)
+    reqs = sample_requests(w.batch, 6, rng)
+    o_ref, l_ref, a_ref = _oracle_cascade(w, reqs)
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what="cascade valu")
