@@ -98,6 +98,12 @@ struct State {
   }
 };
 
+// Max over the four 16-lane groups (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_across_groups(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
 // Softmax update and P.V for one 16-row block and one 32-token step, given
 // its S^T accumulators s0 (tokens 0..15) and s1 (16..31) and the V^T operands.
 // T0: first token of the step; lim: last token visible to this lane's row
@@ -123,8 +129,7 @@ __device__ __forceinline__ void softmax_pv(State<D, MB>& st, int mb, f32x4 s0, f
   }
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                    fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  mx = max_across_groups(mx);
   if (__any(mx > st.m[mb] + kRescaleSlack)) {
     const float m_new = fmaxf(st.m[mb], mx);
     const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[mb] - m_new);

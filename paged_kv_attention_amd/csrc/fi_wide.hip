@@ -133,14 +133,22 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
   u32x4 vt[DPL];
   transpose_v<D>(vv, vt);
   const bool causal = (it.flags & FLAG_CAUSAL) != 0;
+  // both row blocks' logits first: the second block's MFMAs then run under
+  // the first block's softmax
+  f32x4 sa[2][2];
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
-    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+    sa[mb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+    sa[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
-      s0 = mfma_bf16(kf[0][j], qf[mb][j], s0);
-      s1 = mfma_bf16(kf[1][j], qf[mb][j], s1);
+      sa[mb][0] = mfma_bf16(kf[0][j], qf[mb][j], sa[mb][0]);
+      sa[mb][1] = mfma_bf16(kf[1][j], qf[mb][j], sa[mb][1]);
     }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const f32x4 s0 = sa[mb][0], s1 = sa[mb][1];
     const int row_first = it.row0 + rl0 + mb * 16;
     int lim = it.t_end - 1;
     bool masked = tail;
