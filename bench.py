@@ -27,7 +27,9 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention µs/call and achieved KV HBM GB/s (% of peak), 1 GPU"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 CONFIG_INDEX = 1               # the Llama-3-8B-like decode batch
-KERNEL_SOURCES = ("paged_kv_attention_amd/csrc/fi_attention.hip",)
+KERNEL_SOURCES = ("paged_kv_attention_amd/csrc/fi_attention.hip",
+                  "paged_kv_attention_amd/csrc/fi_device.h",
+                  "paged_kv_attention_amd/csrc/fi_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_decode.json")
 
 
