@@ -55,6 +55,31 @@ struct Lds {
   static constexpr int NK = (32 * Cfg<D>::CH) / 256;   // copies per wave per area
 };
 
+// V rows: chunk c of token t is stored at chunk slot c ^ v_swizzle(t). The
+// XOR is even, so each 32-byte run of 16 dims (chunks 2m, 2m+1) stays
+// contiguous, and the runs of the tokens read together by one transposed
+// read (below) fall on distinct banks: for D = 128 a row is one 256-byte bank
+// line and tokens t mod 8 pick distinct runs; for D = 64 two rows share a line
+// and (t mod 2, (t / 2) mod 4) pick distinct runs.
+template <int D>
+__device__ __forceinline__ int v_swizzle(int t) {
+  constexpr int RP = 256 / (2 * D);       // rows per 256-byte bank line
+  constexpr int RUNS = D / 16;            // 32-byte runs per row
+  return 2 * ((t / RP) % RUNS);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4* lds_s16x4p;
+
+// ds_read_b64_tr_b16: within each 16-lane block, result lane j element r is
+// source lane 4r + j/4, element j % 4 (measured on gfx950). With source lane
+// L pointing at dims 16m + 4(L % 4) .. +3 of token L / 4 of a 4-token group,
+// lane j receives dim 16m + j of the group's 4 tokens, in token order: a
+// column of V, which is the V^T MFMA operand's k-slots.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4p)p));
+}
+
 // Copy step s of item it into LDS stage st (this wave's share: NK 1-KiB
 // copies for K and NK for V).
 template <int D, int NP>
@@ -89,9 +114,10 @@ __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, in
             (int64_t)(t & 7) * ROW;
     }
     const int kc = cs ^ (t % CH);            // K: swizzled chunk
+    const int vc = cs ^ v_swizzle<D>(t);     // V: swizzled chunk
     __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.k_cache + off + kc * 16),
                                      (lds_vptr)(stage + blk * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.v_cache + off + cs * 16),
+    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.v_cache + off + vc * 16),
                                      (lds_vptr)(stage + Lds<D>::AREA + blk * 1024), 16, 0, 0);
   }
 }
@@ -108,7 +134,6 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
                                           const u32x4 (&qf)[2][Cfg<D>::KJ], State<D, 2>& st,
                                           int rl0, int wave, int lane) {
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL, CH = Cfg<D>::CH, ROW = Lds<D>::ROW;
-  typedef typename Cfg<D>::vrow_t vrow_t;
   const int col = lane & 15, grp = lane >> 4;
   if (issue) issue_step<D, NP>(a, it, s + 2, next, wave, lane);
   if (s < 0) return;
@@ -123,15 +148,31 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
     for (int j = 0; j < KJ; ++j)
       kf[blk][j] = *(const u32x4*)(cur + t * ROW + ((4 * j + grp) ^ (t % CH)) * 16);
   }
-  vrow_t vv[8];
-#pragma unroll
-  for (int ii = 0; ii < 8; ++ii) {
-    const int tl = (ii < 4) ? 4 * grp + ii : 16 + 4 * grp + (ii - 4);
-    vv[ii] = *(const vrow_t*)(vst + tl * ROW + col * DPL * 2);
-    if (tail && T0 + tl >= it.t_end) vv[ii] = vrow_t{};
-  }
+  // V^T operand of MFMA m: dims 16m + col, the lane group's tokens 4g..4g+3
+  // and 16+4g..16+4g+3 (the token order of the S^T accumulator), read
+  // transposed from LDS. Tokens past the item's end are zeroed (they may hold
+  // anything, even NaN) so that p = 0 cancels them.
+  const int tk = col >> 2, dq = col & 3;   // the token and dim quad this lane points at
+  const int t0 = 4 * grp + tk, t1 = 16 + 4 * grp + tk;
   u32x4 vt[DPL];
-  transpose_v<D>(vv, vt);
+#pragma unroll
+  for (int m = 0; m < DPL; ++m) {
+    const u32x2 lo = lds_read_tr(vst + t0 * ROW + 32 * (m ^ (v_swizzle<D>(t0) >> 1)) + 8 * dq);
+    const u32x2 hi = lds_read_tr(vst + t1 * ROW + 32 * (m ^ (v_swizzle<D>(t1) >> 1)) + 8 * dq);
+    vt[m] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+  }
+  if (tail) {
+    uint32_t keep[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const int tb = (h < 2 ? 4 * grp : 16 + 4 * grp) + 2 * (h & 1);   // tokens tb, tb+1
+      keep[h] = (T0 + tb < it.t_end ? 0x0000ffffu : 0u) | (T0 + tb + 1 < it.t_end ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int m = 0; m < DPL; ++m)
+#pragma unroll
+      for (int h = 0; h < 4; ++h) vt[m][h] &= keep[h];
+  }
   const bool causal = (it.flags & FLAG_CAUSAL) != 0;
   // both row blocks' logits first: the second block's MFMAs then run under
   // the first block's softmax
@@ -157,6 +198,44 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
       lim = min(lim, it.q_pos0 + (row_first + col) / a.group);
     }
     softmax_pv<D, 2>(st, mb, s0, s1, vt, a.scale_log2, masked, T0, lim, grp);
+  }
+}
+
+// o = acc / l and lse for the wave's two 16-row blocks. Accumulator m holds
+// dims 16m + 4*grp + r (r = 0..3) of row col: four consecutive dims per m.
+template <int D, bool LQ>
+__device__ __forceinline__ void finalize_wide(const AttnArgs& a, const Item& it,
+                                              const State<D, 2>& st, int rl0, int col, int grp) {
+  constexpr int DPL = Cfg<D>::DPL;
+  const int G = a.group;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    float lt = st.l[mb];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int rl = rl0 + mb * 16 + col;
+    if (rl >= it.n_rows) continue;
+    const bool live = lt > 0.f;
+    const float inv = live ? 1.f / lt : 0.f;
+    const float lse_v = live ? (st.m[mb] + log2f(lt)) * kLn2 : neg_inf();
+    if (it.flags & FLAG_PARTIAL) {
+      float* op = a.part_o + (int64_t)(it.dst + rl) * D + 4 * grp;
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) *(f32x4*)(op + 16 * m) = st.acc[mb][m] * inv;
+      if (grp == 0) a.part_lse[it.dst + rl] = lse_v;
+    } else {
+      const int rho = it.row0 + rl;
+      const int qi = rho / G, h = rho - qi * G;
+      const int tok = LQ ? a.qlist[it.q_base + qi] : it.q_base + qi;
+      const int64_t orow = (int64_t)tok * a.num_qo_heads + it.g * G + h;
+      uint16_t* op = a.o + orow * D + 4 * grp;
+#pragma unroll
+      for (int m = 0; m < DPL; ++m) {
+        const f32x4 v = st.acc[mb][m] * inv;
+        *(u32x2*)(op + 16 * m) = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+      }
+      if (grp == 0 && a.lse) a.lse[orow] = lse_v;
+    }
   }
 }
 
@@ -196,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
                        lds + stage_c * Lds<D>::STAGE, qf, st, rl0, wave, lane);
       stage_c = stage_c == 2 ? 0 : stage_c + 1;
     }
-    finalize_rows<D, 2, LQ>(a, it, st, rl0, col, grp);
+    finalize_wide<D, LQ>(a, it, st, rl0, col, grp);
     __builtin_amdgcn_s_barrier();   // every wave is done with the stages
     asm volatile("" ::: "memory");
   }
