@@ -127,11 +127,14 @@ __device__ __forceinline__ void softmax_pv(State<D, MB>& st, int mb, f32x4 s0, f
       if (t0 + 16 > lim) x[4 + r] = neg_inf();
     }
   }
-  float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                   fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  mx = max_across_groups(mx);
+  // The base m (equal in the four lane groups of a row) only moves when some
+  // logit exceeds it by more than the slack; the lane-local max decides that,
+  // and only then is the row max taken across the groups, so the common step
+  // needs no cross-lane exchange.
+  const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
   if (__any(mx > st.m[mb] + kRescaleSlack)) {
-    const float m_new = fmaxf(st.m[mb], mx);
+    const float m_new = fmaxf(st.m[mb], max_across_groups(mx));
     const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[mb] - m_new);
     st.l[mb] *= alpha;
 #pragma unroll
