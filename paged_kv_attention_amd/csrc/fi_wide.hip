@@ -259,8 +259,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
     State<D, 2> st;
     st.reset();
     const int n = it.nsteps;
-    int stage_c = 1;                          // stage of step s: s mod 3 (s = -2 -> 1)
-    for (int s = -2; s < n; ++s) {
+    // Step s lives in stage s mod 3; the loop is unrolled by the three stages
+    // so every stage address is a compile-time offset of `lds`.
+    auto body = [&](int s, char* next, const char* cur) -> bool {
+      if (s >= n) return false;
       if (s >= 0) {
         // this wave's copies of step s are done when at most those of step s+1
         // are outstanding; the barrier then publishes every wave's copies, and
@@ -270,10 +272,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
-      const int st2 = stage_c >= 1 ? stage_c - 1 : stage_c + 2;   // (s + 2) mod 3
-      wide_step<D, NP>(a, it, s, s + 2 < n, lds + st2 * Lds<D>::STAGE,
-                       lds + stage_c * Lds<D>::STAGE, qf, st, rl0, wave, lane);
-      stage_c = stage_c == 2 ? 0 : stage_c + 1;
+      wide_step<D, NP>(a, it, s, s + 2 < n, next, cur, qf, st, rl0, wave, lane);
+      return true;
+    };
+    constexpr int SB = Lds<D>::STAGE;
+    for (int s = -2;; s += 3) {   // stages of s, s+1, s+2: 1, 2, 0
+      if (!body(s, lds + 0 * SB, lds + 1 * SB)) break;
+      if (!body(s + 1, lds + 1 * SB, lds + 2 * SB)) break;
+      if (!body(s + 2, lds + 2 * SB, lds + 0 * SB)) break;
     }
     finalize_wide<D, LQ>(a, it, st, rl0, col, grp);
     __builtin_amdgcn_s_barrier();   // every wave is done with the stages
