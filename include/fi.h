@@ -167,6 +167,12 @@ void fi_plan_destroy(fi_plan_t* plan);
 
 fi_status fi_plan_get_info(const fi_plan_t* plan, fi_plan_info* info);
 
+/* Common to the three run calls: the logits are sm_scale * q.k, and sm_scale
+ * must be finite and > 0 (FI_ERR_INVALID_ARG otherwise, checked first); the
+ * call enqueues its kernels on `stream`, never allocates and never
+ * synchronises; a plan of another kind, or a host-only plan, gives
+ * FI_ERR_PLAN_MISMATCH. */
+
 /* Decode attention over the paged cache (research note "flashinfer-backend-
  * selection", "Arithmetic intensity": decode through a gathered block table).
  * Plan kind FI_KIND_DECODE. q [B][Hq][D] bf16 -> o [B][Hq][D] bf16 and lse

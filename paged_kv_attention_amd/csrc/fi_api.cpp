@@ -114,9 +114,10 @@ extern "C" fi_status fi_paged_decode(const fi_plan_t* p, const void* q, const vo
                                      const void* v_cache, const int32_t* kv_indices,
                                      float sm_scale, void* o, float* lse, void* stream) {
   clear_error();
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return set_error(FI_ERR_INVALID_ARG, "fi_paged_decode: sm_scale must be finite and > 0, got %g", (double)sm_scale);
   fi_status st = check_plan(p, FI_KIND_DECODE, "fi_paged_decode");
   if (st != FI_OK) return st;
-  if (!isfinite(sm_scale)) return set_error(FI_ERR_INVALID_ARG, "sm_scale is not finite");
   if (p->hp.desc.batch > 0 && (!q || !k_cache || !v_cache || !kv_indices || !o))
     return set_error(FI_ERR_INVALID_ARG, "fi_paged_decode: NULL tensor pointer");
   hipStream_t s = (hipStream_t)stream;
@@ -134,9 +135,10 @@ extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const vo
                                      const int32_t* kv_indices, float sm_scale, void* o,
                                      float* lse, void* stream) {
   clear_error();
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return set_error(FI_ERR_INVALID_ARG, "fi_paged_append: sm_scale must be finite and > 0, got %g", (double)sm_scale);
   fi_status st = check_plan(p, FI_KIND_APPEND, "fi_paged_append");
   if (st != FI_OK) return st;
-  if (!isfinite(sm_scale)) return set_error(FI_ERR_INVALID_ARG, "sm_scale is not finite");
   if ((k_new == nullptr) != (v_new == nullptr))
     return set_error(FI_ERR_INVALID_ARG, "fi_paged_append: give both k_new and v_new or neither");
   if (p->hp.desc.batch > 0 && (!q || !k_cache || !v_cache || !kv_indices || !o))
@@ -172,9 +174,10 @@ extern "C" fi_status fi_cascade(const fi_plan_t* p, const void* q, const void* k
                                 const int32_t* kv_indices, float sm_scale, void* o, float* lse,
                                 void* stream) {
   clear_error();
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return set_error(FI_ERR_INVALID_ARG, "fi_cascade: sm_scale must be finite and > 0, got %g", (double)sm_scale);
   fi_status st = check_plan(p, FI_KIND_CASCADE, "fi_cascade");
   if (st != FI_OK) return st;
-  if (!isfinite(sm_scale)) return set_error(FI_ERR_INVALID_ARG, "sm_scale is not finite");
   if (p->hp.desc.batch > 0 && (!q || !k_cache || !v_cache || !kv_indices || !o))
     return set_error(FI_ERR_INVALID_ARG, "fi_cascade: NULL tensor pointer");
   if (p->hp.level[0].num_items() > 0 && !prefix_indices)

@@ -106,6 +106,8 @@ __device__ __forceinline__ float max_across_groups(float x) {
 
 // Softmax update and P.V for one 16-row block and one 32-token step, given
 // its S^T accumulators s0 (tokens 0..15) and s1 (16..31) and the V^T operands.
+// scale_log2 = sm_scale * log2(e) must be > 0 (the run calls check sm_scale);
+// p = 2^(s * scale_log2 - m) is one fma and one exp per logit.
 // T0: first token of the step; lim: last token visible to this lane's row
 // (only read when `masked`).
 template <int D, int MB>
@@ -113,11 +115,12 @@ __device__ __forceinline__ void softmax_pv(State<D, MB>& st, int mb, f32x4 s0, f
                                            const u32x4 (&vt)[Cfg<D>::DPL], float scale_log2,
                                            bool masked, int T0, int lim, int grp) {
   constexpr int DPL = Cfg<D>::DPL;
+  // raw logits; scale_log2 > 0, so their max is the max of the scaled ones
   float x[8];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    x[r] = s0[r] * scale_log2;
-    x[4 + r] = s1[r] * scale_log2;
+    x[r] = s0[r];
+    x[4 + r] = s1[r];
   }
   if (masked) {
 #pragma unroll
@@ -132,7 +135,7 @@ __device__ __forceinline__ void softmax_pv(State<D, MB>& st, int mb, f32x4 s0, f
   // and only then is the row max taken across the groups, so the common step
   // needs no cross-lane exchange.
   const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
-                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+                         fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) * scale_log2;
   if (__any(mx > st.m[mb] + kRescaleSlack)) {
     const float m_new = fmaxf(st.m[mb], max_across_groups(mx));
     const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[mb] - m_new);
@@ -141,10 +144,10 @@ __device__ __forceinline__ void softmax_pv(State<D, MB>& st, int mb, f32x4 s0, f
     for (int m = 0; m < DPL; ++m) st.acc[mb][m] *= alpha;
     st.m[mb] = m_new;
   }
-  const float base = (st.m[mb] == neg_inf()) ? 0.f : st.m[mb];
+  const float nbase = (st.m[mb] == neg_inf()) ? 0.f : -st.m[mb];
   float p[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(x[i] - base);
+  for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(x[i], scale_log2, nbase));
   st.l[mb] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
   const u32x4 pb = {pack2(p[0], p[1]), pack2(p[2], p[3]), pack2(p[4], p[5]), pack2(p[6], p[7])};
 #pragma unroll

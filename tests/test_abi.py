@@ -244,6 +244,18 @@ def test_decode_engine_field():
         assert st == L.FI_ERR_INVALID_ARG, msg
 
 
+def test_run_calls_reject_non_positive_scale():
+    lib = fi.load()
+    for bad in (0.0, -0.125, float("nan"), float("inf")):
+        assert lib.fi_paged_decode(None, None, None, None, None, bad, None, None, None) == \
+            L.FI_ERR_INVALID_ARG
+        assert lib.fi_cascade(None, None, None, None, None, None, bad, None, None, None) == \
+            L.FI_ERR_INVALID_ARG
+        assert lib.fi_paged_append(None, None, None, None, None, None, None, bad, None, None,
+                                   None) == L.FI_ERR_INVALID_ARG
+        assert "sm_scale" in lib.fi_last_error().decode()
+
+
 def test_run_calls_refuse_without_device_plan():
     lib = fi.load()
     assert lib.fi_paged_decode(None, None, None, None, None, 1.0, None, None, None) == \
