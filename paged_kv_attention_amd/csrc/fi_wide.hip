@@ -136,7 +136,10 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL, CH = Cfg<D>::CH, ROW = Lds<D>::ROW;
   const int col = lane & 15, grp = lane >> 4;
   if (issue) issue_step<D, NP>(a, it, s + 2, next, wave, lane);
-  if (s < 0) return;
+  // row blocks of this wave that hold real rows (0, 1 or 2): a wave or block
+  // of padding rows only takes part in the copies and barriers
+  const int nmb = min(2, max(0, (it.n_rows - rl0 + 15) >> 4));
+  if (s < 0 || nmb == 0) return;
   const char* vst = cur + Lds<D>::AREA;
   const int T0 = it.t_begin + 32 * s;
   const bool tail = T0 + 32 > it.t_end;
@@ -181,6 +184,7 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
   for (int mb = 0; mb < 2; ++mb) {
     sa[mb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
     sa[mb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mb >= nmb) continue;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
       sa[mb][0] = mfma_bf16(kf[0][j], qf[mb][j], sa[mb][0]);
@@ -189,6 +193,7 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
   }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
+    if (mb >= nmb) continue;
     const f32x4 s0 = sa[mb][0], s1 = sa[mb][1];
     const int row_first = it.row0 + rl0 + mb * 16;
     int lim = it.t_end - 1;
