@@ -97,6 +97,88 @@ def cpu_baseline(w, budget_s: float):
                       f"{dt:.1f} s wall, KV bytes of the sample / wall time"}
 
 
+def _pct(xs, q):
+    xs = sorted(xs)
+    return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
+
+
+def measure_variants(args, w, g, plan, step, dev):
+    """Context for the main number, measured after the timed region:
+    HIP-graph replays, cold-cache calls, and the deterministic-mode plan."""
+    import torch
+    import paged_kv_attention_amd as fi
+    res = {}
+    # (1) HIP graph of 10 calls, replayed; per-call time of each replay
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(10):
+            step()
+    for _ in range(5):
+        graph.replay()
+    torch.cuda.synchronize()
+    samples = []
+    for _ in range(max(10, args.steps // 10)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        e1.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e3 / 10)
+    res["graph_replay_us"] = {"replays": len(samples), "calls_per_replay": 10,
+                              "median": round(_pct(samples, 0.5), 2),
+                              "p10": round(_pct(samples, 0.1), 2),
+                              "p90": round(_pct(samples, 0.9), 2)}
+    del graph
+    # (2) cold cache: reading 1 GiB between calls evicts L2 and the 256 MB
+    # Infinity Cache (a read, so no dirty lines are left to be written back
+    # during the call); the scrub's own time is measured alone and subtracted
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    n = 50
+
+    def loop(with_call):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            torch.sum(scrub, dim=0, out=sink)
+            if with_call:
+                step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    loop(True)
+    both = [loop(True) for _ in range(3)]
+    alone = [loop(False) for _ in range(3)]
+    res["cold_us_per_call"] = round(min(both) - min(alone), 2)
+    del scrub
+    # (3) deterministic-mode plan (chunks fixed per request) on the same batch
+    dplan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                    w.page_size, device=dev, deterministic=True, engine=args.engine)
+    out = torch.empty_like(g.q)
+
+    def dstep():
+        fi.paged_decode(dplan, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale, out=out)
+    for _ in range(args.warmup):
+        dstep()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dstep()
+    e1.record()
+    torch.cuda.synchronize()
+    res["deterministic_us_per_call"] = round(e0.elapsed_time(e1) * 1e3 / args.steps, 2)
+    return res
+
+
 def explore(args, dev):
     """Timing of one call on another configuration (decode, cascade or
     append), for the design notes; prints its own JSON line."""
@@ -170,6 +252,8 @@ def main():
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--no-variants", dest="variants", action="store_false",
+                    help="skip the graph-replay, cold-cache and deterministic-mode context")
     ap.add_argument("--config", type=int, default=CONFIG_INDEX,
                     help="other configurations print an exploratory line (not the bench line)")
     args = ap.parse_args()
@@ -242,6 +326,8 @@ def main():
         torch.cuda.synchronize()
     kern_ms = kt.total_ms / max(1, kt.calls)
 
+    extra = measure_variants(args, w, g, plan, step, dev) if args.variants else None
+
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -272,6 +358,8 @@ def main():
         "plan_host_us": round(plan_us, 1), "plan_first_ms": round(plan_ms_first, 2),
         "roofline": roof,
     }
+    if extra:
+        res["context"] = extra
     if args.cpu_budget > 0:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

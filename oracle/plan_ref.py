@@ -17,12 +17,15 @@ be compared with it element for element:
 2. Key range. A unit sees tokens [0, t_lim): t_lim = kv_len, or under the
    causal mask min(kv_len, kv_len - qo + i_last + 1) with i_last the last
    query token in the block. It spans n = ceil(t_lim / ps) pages.
-3. Balanced mode (even split). The units' pages are laid end to end in
-   enumeration order (W pages in all) and cut into consecutive quotas of
-   c = max(1, min_chunk_pages, ceil(W / S)) pages, S = number of persistent
-   workers; quota w goes to worker w. A unit's pieces, in order, are its
-   chunks, so each worker reads c pages (the last one fewer) and runs its
-   pieces in page order.
+3. Balanced mode (even split). The kernels walk a unit in 32-token steps,
+   so the split is counted in steps: a unit of n pages is s = ceil(n / gp)
+   steps, gp = max(1, 32 / ps) pages each. The units' steps are laid end to
+   end in enumeration order (W steps in all) and cut into consecutive quotas
+   of c = max(1, ceil(min_chunk_pages / gp), ceil(W / S)) steps, S = number of
+   persistent workers; quota w goes to worker w. A unit's pieces, in order,
+   are its chunks (page ranges: step boundaries times gp, the last clipped to
+   n), so each worker runs c steps (the last one fewer) in page order, and no
+   chunk boundary falls inside a step. The reported chunk size is c*gp pages.
 4. Deterministic mode. A unit of n pages has k = ceil(n / c) chunks with
    c = det_chunk_pages, chunk j covering pages [floor(j*n/k),
    floor((j+1)*n/k)): boundaries depend on the request alone. Chunks are
@@ -69,8 +72,9 @@ def _lpt(items, num_workers):
     return flat, indptr
 
 
-def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages):
-    """Per unit: list of (p0, p1, worker) page pieces in order; and c."""
+def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages,
+                 page_size):
+    """Per unit: list of (p0, p1, worker) page pieces in order; and c in pages."""
     pieces = []
     if deterministic:
         c = max(1, int(det_chunk_pages))
@@ -79,21 +83,25 @@ def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_p
             k = _ceil_div(n, c) if n > 0 else 0
             pieces.append([((j * n) // k, ((j + 1) * n) // k, None) for j in range(k)])
         return pieces, c
-    W = sum(u["n_pages"] for u in units)
-    c = max(1, int(min_chunk_pages), _ceil_div(W, num_workers))
+    # balanced: quotas counted in 32-token steps (gp pages each), so that no
+    # chunk boundary falls inside a step
+    gp = max(1, 32 // page_size)
+    steps = [_ceil_div(u["n_pages"], gp) for u in units]
+    W = sum(steps)
+    c = max(1, _ceil_div(int(min_chunk_pages), gp), _ceil_div(W, num_workers))
     g = 0
-    for u in units:
+    for u, ns in zip(units, steps):
         n = u["n_pages"]
         lst = []
         p = 0
-        while p < n:
+        while p < ns:
             w = (g + p) // c
-            e = min(n, (w + 1) * c - g)
-            lst.append((p, e, w))
+            e = min(ns, (w + 1) * c - g)
+            lst.append((p * gp, min(n, e * gp), w))
             p = e
         pieces.append(lst)
-        g += n
-    return pieces, c
+        g += ns
+    return pieces, c * gp
 
 
 def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
@@ -173,7 +181,8 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     unit_chunks = []    # per level: per unit (k, [partial dst rows])
     for lev, units in enumerate(levels_units):
         S = workers[lev]
-        pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev])
+        pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev],
+                                 page_size)
         items = []
         chunks_of = []
         for u, lst in zip(units, pieces):

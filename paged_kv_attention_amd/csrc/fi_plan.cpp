@@ -10,10 +10,11 @@
 //             kv head) over the member requests' rows
 //   key range of a unit: [0, t_lim), t_lim = kv_len, or min(kv_len,
 //             kv_len - qo + i_last + 1) under the bottom-right causal mask
-//   balanced: the level's unit pages laid end to end (W pages) are cut into
-//             quotas of c = max(1, min_chunk_pages, ceil(W / S)) pages,
-//             S = num_cus * workers_per_cu; quota w is worker w's, so every
-//             worker reads the same number of pages (even split)
+//   balanced: the level's units, counted in 32-token steps of gp =
+//             max(1, 32 / page_size) pages, laid end to end (W steps), are cut
+//             into quotas of c = max(1, ceil(min_chunk_pages / gp), ceil(W / S))
+//             steps, S = num_cus * workers_per_cu; quota w is worker w's, so
+//             every worker runs the same number of steps (even split)
 //   deterministic: c = det_chunk_pages; a unit of n pages has k = ceil(n/c)
 //             chunks [floor(jn/k), floor((j+1)n/k)), boundaries depending on
 //             the request alone, placed by Graham's longest-processing-time
@@ -158,19 +159,23 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
       for (int64_t j = 0; j < k; ++j) pieces[ui].push_back({(j * n) / k, ((j + 1) * n) / k, -1});
     }
   } else {
+    // Quotas are counted in 32-token steps of gp pages, the granule the
+    // kernels walk a unit in, so that no chunk boundary falls inside a step.
+    const int64_t gp = std::max(1, 32 / ps);
     int64_t W = 0;
-    for (const Unit& u : units) W += u.n_pages;
-    c = std::max<int64_t>({1, lv.min_chunk_pages, ceil_div(W, S)});
-    int64_t g = 0;   // global page offset of the unit
+    for (const Unit& u : units) W += ceil_div(u.n_pages, gp);
+    const int64_t cs = std::max<int64_t>({1, ceil_div(lv.min_chunk_pages, gp), ceil_div(W, S)});
+    c = cs * gp;
+    int64_t g = 0;   // global step offset of the unit
     for (size_t ui = 0; ui < units.size(); ++ui) {
-      const int64_t n = units[ui].n_pages;
-      for (int64_t p = 0; p < n;) {
-        const int64_t w = (g + p) / c;
-        const int64_t e = std::min(n, (w + 1) * c - g);
-        pieces[ui].push_back({p, e, (int32_t)w});
+      const int64_t n = units[ui].n_pages, ns = ceil_div(n, gp);
+      for (int64_t p = 0; p < ns;) {
+        const int64_t w = (g + p) / cs;
+        const int64_t e = std::min(ns, (w + 1) * cs - g);
+        pieces[ui].push_back({p * gp, std::min(n, e * gp), (int32_t)w});
         p = e;
       }
-      g += n;
+      g += ns;
     }
   }
   lv.chunk_pages = (int32_t)c;

@@ -362,3 +362,61 @@ def test_valu_engine_cascade(dev):
     reqs = sample_requests(w.batch, 6, rng)
     o_ref, l_ref, a_ref = _oracle_cascade(w, reqs)
     compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what="cascade valu")
+
+
+# ---------------------------------------------------------------- HIP graphs
+
+
+def _capture(fn):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn()
+    return graph
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4])
+def test_graph_replay_matches_eager(dev, cfg):
+    """A captured run call (no allocation, no memset inside) replays to the
+    eager bits, replay after replay, with other eager work in between."""
+    w = make_config(cfg, poison=False)
+    g = w.to(dev)
+    T = g.q.shape[0]
+    out = torch.empty_like(g.q)
+    lse = torch.empty(T, w.num_qo_heads, dtype=torch.float32, device=dev)
+    if w.kind == "decode":
+        p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                    w.page_size, device=dev)
+        call = lambda o, l: fi.paged_decode(p, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
+                                            w.sm_scale, out=o, lse=l)
+    elif w.kind == "cascade":
+        p = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
+                    w.head_dim, w.page_size, prefix_indptr=w.prefix_indptr,
+                    prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group, device=dev)
+        call = lambda o, l: fi.cascade(p, g.q, g.k_cache, g.v_cache, g.prefix_indices,  # noqa
+                                       g.kv_indices, w.sm_scale, out=o, lse=l)
+    else:
+        p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                    w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev)
+        call = lambda o, l: fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
+                                            w.sm_scale, k_new=g.k_new, v_new=g.v_new, out=o,
+                                            lse=l)
+    ref_o, ref_l = torch.empty_like(out), torch.empty_like(lse)
+    call(ref_o, ref_l)
+    torch.cuda.synchronize()
+    graph = _capture(lambda: call(out, lse))
+    for rep in range(3):
+        out.fill_(7.0)
+        lse.fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(lse, ref_l), f"config {cfg} replay {rep}"
+        other_o, other_l = torch.empty_like(out), torch.empty_like(lse)
+        call(other_o, other_l)          # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(other_o, ref_o)

@@ -150,20 +150,26 @@ def _worker_pages(lv, S, ps):
 
 @pytest.mark.parametrize("lens", [[32768] * 4 + [1024] * 124, list(range(500, 4600, 64)),
                                   [1, 2, 3, 17, 0, 5000]])
-def test_balanced_mode_splits_pages_evenly(lens):
-    """Every used worker reads exactly c pages, except the last used one."""
-    ps = 16
-    indptr, L = _decode_inputs(lens, ps)
-    S = 97
-    p = plan_ref("decode", 32, 8, ps, indptr, L, S, [16], min_chunk_pages=2)
-    lv = p["levels"][0]
-    c = lv["chunk_pages"]
-    W = 8 * sum(-(-x // ps) for x in lens)
-    pages = _worker_pages(lv, S, ps)
-    used = -(-W // c)
-    assert pages.sum() == W
-    assert np.all(pages[:used - 1] == c) and 0 < pages[used - 1] <= c
-    assert np.all(pages[used:] == 0)
+def test_balanced_mode_splits_steps_evenly(lens):
+    """Every used worker runs exactly c 32-token steps, except the last used
+    one; chunk boundaries fall on step boundaries (the kernels' granule)."""
+    for ps in (8, 16, 64):
+        gp = max(1, 32 // ps)
+        indptr, L = _decode_inputs(lens, ps)
+        S = 97
+        p = plan_ref("decode", 32, 8, ps, indptr, L, S, [16], min_chunk_pages=2)
+        lv = p["levels"][0]
+        c = lv["chunk_pages"] // gp
+        W = 8 * sum(-(-(-(-x // ps)) // gp) for x in lens)
+        steps = np.zeros(S, dtype=np.int64)
+        for w in range(S):
+            for it in lv["items"][lv["worker_indptr"][w]:lv["worker_indptr"][w + 1]]:
+                assert it[F["t_begin"]] % (gp * ps) == 0
+                steps[w] += -(-(it[F["t_end"]] - it[F["t_begin"]]) // (gp * ps))
+        used = -(-W // c)
+        assert steps.sum() == W
+        assert np.all(steps[:used - 1] == c) and 0 < steps[used - 1] <= c
+        assert np.all(steps[used:] == 0)
 
 
 def test_lpt_balances_deterministic_chunks():
