@@ -186,14 +186,23 @@ def explore(args, dev):
     import paged_kv_attention_amd as fi
     from workloads import CONFIG_NAMES, make_config
     w = make_config(args.config, poison=False)
+    if args.kv == "fp8":
+        if w.kind != "decode":
+            raise SystemExit("bench.py: --kv fp8 applies to the decode configurations")
+        from workloads import to_fp8_cache
+        w = to_fp8_cache(w, poison=False)
     g = w.to(dev)
     kw = dict(deterministic=args.mode == "deterministic", workers_per_cu=args.workers_per_cu,
               min_chunk_pages=args.min_chunk_pages, engine=args.engine)
     if w.kind == "decode":
         plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, device=dev, **kw)
-        call = lambda: fi.paged_decode(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
-                                       w.sm_scale)
+        if args.kv == "fp8":
+            call = lambda: fi.paged_decode_fp8(plan, g.q, g.k_fp8, g.v_fp8, g.k_scale,  # noqa
+                                               g.v_scale, g.kv_indices, w.sm_scale)
+        else:
+            call = lambda: fi.paged_decode(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
+                                           w.sm_scale)
         flops = 4 * w.head_dim * w.num_qo_heads * int(w.kv_len.sum())
     elif w.kind == "cascade":
         plan = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
@@ -228,9 +237,9 @@ def explore(args, dev):
             call()
         torch.cuda.synchronize()
     kern_ms = kt.total_ms / max(1, kt.calls)
-    kv = w.kv_bytes()
+    kv = w.kv_bytes_fp8() if args.kv == "fp8" else w.kv_bytes()
     print(json.dumps({"workload": CONFIG_NAMES[args.config], "mode": args.mode,
-                      "engine": args.engine,
+                      "engine": args.engine, "kv": args.kv,
                       "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
                       "kv_bytes": kv, "kv_GBps": round(kv / ms / 1e6, 1),
                       "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
@@ -252,6 +261,8 @@ def main():
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+                    help="KV cache format for the exploratory decode lines (--config)")
     ap.add_argument("--no-variants", dest="variants", action="store_false",
                     help="skip the graph-replay, cold-cache and deterministic-mode context")
     ap.add_argument("--config", type=int, default=CONFIG_INDEX,
@@ -269,7 +280,7 @@ def main():
 
     dev = torch.device("cuda:0")
     fi.load()
-    if args.config != CONFIG_INDEX:
+    if args.config != CONFIG_INDEX or args.kv != "bf16":
         explore(args, dev)
         return
     print(f"bench: generating {CONFIG_NAMES[CONFIG_INDEX]}", file=sys.stderr, flush=True)

@@ -182,6 +182,19 @@ fi_status fi_paged_decode(const fi_plan_t* plan, const void* q, const void* k_ca
                           const void* v_cache, const int32_t* kv_indices,
                           float sm_scale, void* o, float* lse, void* stream);
 
+/* Decode attention over an FP8 KV cache (v0.7.4 article, TL;DR: decoding
+ * from a low-precision KV cache). Plan kind FI_KIND_DECODE on the matrix-core
+ * engine (FI_ERR_UNSUPPORTED on the VALU engine). k_cache and v_cache hold
+ * FP8 E4M3 codes (OCP 8-bit floating point: bias 7, no infinities, 0x7F and
+ * 0xFF are NaN) in the bf16 layout [pages][Hkv][page_size][D], one byte per
+ * element; k_scale and v_scale are fp32 [pages][Hkv], device memory, and the
+ * element of page p, kv head g is decode(code) * scale[p][g]. Scales must be
+ * finite (they are not checked). q, o, lse as in fi_paged_decode. */
+fi_status fi_paged_decode_fp8(const fi_plan_t* plan, const void* q, const void* k_cache,
+                              const void* v_cache, const float* k_scale, const float* v_scale,
+                              const int32_t* kv_indices, float sm_scale, void* o, float* lse,
+                              void* stream);
+
 /* Append / prefill attention for a mixed batch (research note, "Arithmetic
  * intensity": prefill and decode rows of one batch). Plan kind
  * FI_KIND_APPEND. If k_new and v_new ([sum qo][Hkv][D] bf16) are non-NULL,

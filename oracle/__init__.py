@@ -18,6 +18,10 @@ Sources (the pages this follows; cited by title and section):
 * FlashInfer PR #4038 "split-K, occupancy, and m=1 stream-GEMV decode
   tactics", section *What it does*: split partials kept in fp32 and reduced in
   a fixed order so results are deterministic.
+* "FlashInfer v0.7.4 Adds Rubin MoE Kernels and a Batch-Invariant Mode",
+  *TL;DR*: decoding from a low-precision KV cache. The FP8 format itself is the
+  OCP 8-bit floating-point E4M3 definition (a published standard, not one of
+  the pages).
 
 Parity status of each function is stated in its docstring ("pinned by" lists
 the tests in ``tests/test_oracle.py`` that tie it to something other than
@@ -30,6 +34,8 @@ from .attention import (  # noqa: F401
     attend,
     gather_tokens,
     paged_decode,
+    paged_decode_fp8,
+    e4m3_values,
     paged_append,
     scatter_new_kv,
     merge_states,

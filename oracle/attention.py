@@ -114,6 +114,50 @@ def paged_decode(q, k_pool, v_pool, kv_indptr, kv_indices, kv_len, page_size: in
     return o, lse
 
 
+def e4m3_values():
+    """Value of every FP8 E4M3 code (index = code), float64, NaN for the two
+    NaN codes. The format is the OCP 8-bit floating-point E4M3 definition:
+    sign bit, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 is
+    subnormal, m/8 * 2^-6; exponent 15 with mantissa 7 is NaN; there are no
+    infinities (largest finite 448). Pinned by: all 256 codes against torch's
+    float8_e4m3fn conversion; closed forms (1, 448, 2^-9, 2^-6, signs)."""
+    out = np.empty(256)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 0xF, c & 0x7
+        if e == 15 and m == 7:
+            out[c] = np.nan
+        elif e == 0:
+            out[c] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            out[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def paged_decode_fp8(q, k_codes, v_codes, k_scale, v_scale, kv_indptr, kv_indices, kv_len,
+                     page_size: int, sm_scale: float, requests=None):
+    """Decode attention over an FP8 cache (v0.7.4 article, TL;DR: decoding from
+    a low-precision KV cache): the element of page p, kv head g is
+    e4m3_values()[code] * scale[p, g] in fp64, and the result is exactly
+    paged_decode over those values. Only the pages of the selected requests
+    are decoded. Pinned by: equality with paged_decode over pools dequantized
+    by torch's float8_e4m3fn conversion (an independent route)."""
+    B = q.shape[0]
+    reqs = _req_list(B, requests)
+    pages = np.unique(np.concatenate(
+        [np.asarray(kv_indices[int(kv_indptr[r]):int(kv_indptr[r + 1])]) for r in reqs]
+        + [np.zeros(0, dtype=np.int64)]).astype(np.int64))
+    table = e4m3_values()
+    ks = np.asarray(k_scale, dtype=np.float64)[pages][:, :, None, None]
+    vs = np.asarray(v_scale, dtype=np.float64)[pages][:, :, None, None]
+    kp = table[np.asarray(k_codes)[pages]] * ks
+    vp = table[np.asarray(v_codes)[pages]] * vs
+    remap = np.zeros(int(np.asarray(k_codes).shape[0]), dtype=np.int64)
+    remap[pages] = np.arange(pages.size)
+    idx = remap[np.asarray(kv_indices, dtype=np.int64)]
+    return paged_decode(q, kp, vp, kv_indptr, idx, kv_len, page_size, sm_scale, requests=reqs)
+
+
 def paged_append(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
                  page_size: int, sm_scale: float, causal: bool = True, requests=None):
     """Attention for ``qo`` new query tokens per request over ``kv_len`` keys

@@ -1,5 +1,5 @@
-"""MI355X-native paged-KV attention: plan, paged decode, append, cascade and
-state merge, backed by hand-written HIP kernels for gfx950 in libfi.so.
+"""MI355X-native paged-KV attention: plan, paged decode (bf16 or FP8 KV),
+append, cascade and state merge, backed by hand-written HIP kernels for gfx950 in libfi.so.
 
 The shared library is required: importing works without it, but every call
 raises until it is built (``python -m paged_kv_attention_amd.build``).
@@ -14,4 +14,5 @@ from .api import (  # noqa: F401
     merge_states,
     paged_append,
     paged_decode,
+    paged_decode_fp8,
 )

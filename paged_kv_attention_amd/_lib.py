@@ -51,6 +51,9 @@ SIGNATURES = {
     "fi_plan_get_info": (c_int32, [c_void_p, POINTER(PlanInfo)]),
     "fi_paged_decode": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                                   c_void_p, c_void_p, c_void_p]),
+    "fi_paged_decode_fp8": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                      c_void_p]),
     "fi_paged_append": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_float, c_void_p, c_void_p, c_void_p]),
     "fi_cascade": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

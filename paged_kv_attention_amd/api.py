@@ -206,6 +206,33 @@ def paged_decode(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, o
     return out, lse
 
 
+def paged_decode_fp8(plan: Plan, q, k_cache, v_cache, k_scale, v_scale, kv_indices,
+                     sm_scale: float, out=None, lse=None, return_lse: bool = True):
+    """fi_paged_decode_fp8: K/V pools of FP8 E4M3 codes (uint8, same shape as
+    the bf16 pools) with fp32 scales [pages, Hkv]; q, out, lse as paged_decode."""
+    _check_run(plan, "decode")
+    _check_tensor(q, "q", torch.bfloat16, plan.device,
+                  (plan.batch, plan.num_qo_heads, plan.head_dim))
+    _check_tensor(k_cache, "k_cache", torch.uint8, plan.device)
+    _check_tensor(v_cache, "v_cache", torch.uint8, plan.device, k_cache.shape)
+    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (plan.num_kv_heads, plan.page_size,
+                                                          plan.head_dim):
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match the plan "
+                         f"[P, {plan.num_kv_heads}, {plan.page_size}, {plan.head_dim}]")
+    P = k_cache.shape[0]
+    _check_tensor(k_scale, "k_scale", torch.float32, plan.device, (P, plan.num_kv_heads))
+    _check_tensor(v_scale, "v_scale", torch.float32, plan.device, (P, plan.num_kv_heads))
+    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    if lse is None and return_lse:
+        lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
+    out, lse = _outputs(plan, q, out, lse)
+    L.check(L.load().fi_paged_decode_fp8(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(k_scale), _ptr(v_scale), _ptr(kv_indices),
+                                         float(sm_scale), _ptr(out), _ptr(lse),
+                                         _stream(plan.device)), "fi_paged_decode_fp8")
+    return out, lse
+
+
 def paged_append(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, k_new=None,
                  v_new=None, out=None, lse=None, return_lse: bool = True):
     """fi_paged_append: q [sum qo, Hq, D]; optional k_new/v_new [sum qo, Hkv, D]

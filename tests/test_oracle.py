@@ -406,7 +406,8 @@ def _mut_merge_sign(o1, l1, o2, l2):
     return o, l
 
 
-_ORIG = {n: getattr(A, n) for n in ("gather_tokens", "attend", "merge_two", "paged_append")}
+_ORIG = {n: getattr(A, n) for n in ("gather_tokens", "attend", "merge_two", "paged_append",
+                                    "paged_decode_fp8", "e4m3_values")}
 
 
 def _mut_append_top_left(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
@@ -429,6 +430,73 @@ def _mut_append_top_left(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv
     return o, lse
 
 
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) cache
+
+
+def test_e4m3_values_match_torch_for_every_code():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).double().numpy()
+    got = A.e4m3_values()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))   # -0 at 0x80
+
+
+def test_e4m3_closed_forms():
+    v = A.e4m3_values()
+    assert v[0x38] == 1.0 and v[0x40] == 2.0 and v[0xC0] == -2.0
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0            # largest finite
+    assert v[0x08] == 2.0 ** -6                                # smallest normal
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9    # subnormals
+    assert v[0x00] == 0.0 and np.signbit(v[0x80])
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.isnan(v).sum() == 2
+
+
+def fp8_case(seed=3, ps=16, D=64, Hq=8, Hkv=2, lens=(1, 17, 40, 100)):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    n = [-(-L // ps) for L in lens]
+    P = sum(n) + 3
+    perm = rng.permutation(P)
+    indptr = np.concatenate([[0], np.cumsum(n)])
+    indices = perm[:sum(n)]
+    kc = rng.integers(0, 256, (P, Hkv, ps, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, (P, Hkv, ps, D), dtype=np.uint8)
+    for c in (kc, vc):                      # no NaN codes in used slots
+        c[(c & 0x7F) == 0x7F] = 0x3C
+    ks = rng.uniform(0.01, 0.1, (P, Hkv)).astype(np.float32)
+    vs = rng.uniform(0.1, 2.0, (P, Hkv)).astype(np.float32)
+    q = rng.standard_normal((B, Hq, D))
+    return q, kc, vc, ks, vs, indptr, indices, np.array(lens), ps
+
+
+def test_fp8_decode_equals_decode_of_torch_dequantized_pools():
+    q, kc, vc, ks, vs, indptr, indices, L, ps = fp8_case()
+    deq = lambda c, s: (torch.from_numpy(c).view(torch.float8_e4m3fn).double().numpy()  # noqa
+                        * s.astype(np.float64)[:, :, None, None])
+    kp, vp = deq(kc, ks), deq(vc, vs)
+    scale = 0.125
+    o_ref, l_ref = A.paged_decode(q, kp, vp, indptr, indices, L, ps, scale)
+    o, lse = A.paged_decode_fp8(q, kc, vc, ks, vs, indptr, indices, L, ps, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, l_ref, rtol=1e-14, atol=0)
+    # a subset of requests decodes only their pages and leaves the rest NaN
+    o2, l2 = A.paged_decode_fp8(q, kc, vc, ks, vs, indptr, indices, L, ps, scale, requests=[1, 3])
+    np.testing.assert_array_equal(o2[[1, 3]], o[[1, 3]])
+    assert np.isnan(o2[[0, 2]]).all()
+
+
+def _mut_fp8_swap_scales(q, kc, vc, ks, vs, *rest, **kw):
+    return _ORIG["paged_decode_fp8"](q, kc, vc, vs, ks, *rest, **kw)
+
+
+def _mut_e4m3_bias8():
+    return _ORIG["e4m3_values"]() / 2.0
+
+
 MUTATIONS = {
     "gather_reverse_pages": ("gather_tokens", _mut_gather_reverse_pages,
                              lambda: check_decode_vs_sdpa(16, 4)),
@@ -439,6 +507,9 @@ MUTATIONS = {
     "attend_transposed_v": ("attend", _mut_attend_transposed_v, test_two_keys_closed_form),
     "merge_sign": ("merge_two", _mut_merge_sign, lambda: test_split_and_merge_equals_whole([5])),
     "append_top_left": ("paged_append", _mut_append_top_left, check_append_vs_sdpa),
+    "fp8_scales_swapped": ("paged_decode_fp8", _mut_fp8_swap_scales,
+                           test_fp8_decode_equals_decode_of_torch_dequantized_pools),
+    "e4m3_bias_8": ("e4m3_values", _mut_e4m3_bias8, test_e4m3_values_match_torch_for_every_code),
 }
 
 
@@ -453,5 +524,5 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 def test_oracle_exports():
     for n in ("attend", "paged_decode", "paged_append", "merge_states", "cascade_flat",
-              "plan_ref"):
+              "plan_ref", "paged_decode_fp8", "e4m3_values"):
         assert hasattr(oracle, n)

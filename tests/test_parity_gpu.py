@@ -14,7 +14,8 @@ import oracle
 import paged_kv_attention_amd as fi
 from tests.helpers import (compare, gpu_decode, np_pools, oracle_decode, request_rows,
                            sample_requests)
-from workloads import cascade_flat_tables, make_append, make_cascade, make_config, make_decode
+from workloads import (cascade_flat_tables, make_append, make_cascade, make_config, make_decode,
+                       to_fp8_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -420,3 +421,56 @@ def test_graph_replay_matches_eager(dev, cfg):
         call(other_o, other_l)          # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(other_o, ref_o)
+
+
+# ---------------------------------------------------------------- FP8 cache
+
+
+def _fp8_oracle(w, requests=None):
+    args = (w.kv_indptr.numpy(), w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size,
+            w.sm_scale)
+    q = w.q.double().numpy()
+    kc, vc = w.k_fp8.numpy(), w.v_fp8.numpy()
+    ks, vs = w.k_scale.numpy(), w.v_scale.numpy()
+    o, lse = oracle.paged_decode_fp8(q, kc, vc, ks, vs, *args, requests=requests)
+    a, _ = oracle.paged_decode_fp8(q, kc, vc & 0x7F, ks, vs, *args, requests=requests)   # |V|
+    return o, lse, a
+
+
+def _fp8_run(w, dev, **kw):
+    p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                w.page_size, device=dev, **kw)
+    g = w.to(dev)
+    o, lse = fi.paged_decode_fp8(p, g.q, g.k_fp8, g.v_fp8, g.k_scale, g.v_scale, g.kv_indices,
+                                 w.sm_scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_fp8_llama_decode_sampled(dev):
+    w = to_fp8_cache(make_config(1, poison=False), poison=True)
+    rng = np.random.default_rng(21)
+    reqs = sample_requests(w.batch, 8, rng, must=[int(torch.argmax(w.kv_len))])
+    o_ref, l_ref, a_ref = _fp8_oracle(w, reqs)
+    for det in (False, True):
+        o, lse = _fp8_run(w, dev, deterministic=det)
+        compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"fp8 llama det={det}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_fp8_decode_small_sweep(dev, D, ps, G):
+    Hkv = 2
+    w = to_fp8_cache(make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=500 + D + ps + G,
+                                 poison=False), poison=True)
+    o_ref, l_ref, a_ref = _fp8_oracle(w)
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+        o, lse = _fp8_run(w, dev, **kw)
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"fp8 decode D={D} ps={ps} G={G} {kw}")
+
+
+def test_fp8_decode_refuses_the_valu_engine(dev):
+    w = to_fp8_cache(make_decode([40, 7], 8, 2, 64, 16, seed=9, poison=False), poison=True)
+    with pytest.raises(fi.FIError, match="matrix-core"):
+        _fp8_run(w, dev, engine="valu")

@@ -16,4 +16,5 @@ from .synth import (  # noqa: F401
     make_cascade,
     cascade_flat_tables,
     fp32_scale,
+    to_fp8_cache,
 )

@@ -76,6 +76,10 @@ class Workload:
     prefix_indices: Optional[torch.Tensor] = None
     prefix_len: Optional[torch.Tensor] = None
     req_prefix_group: Optional[torch.Tensor] = None
+    k_fp8: Optional[torch.Tensor] = None      # FP8 E4M3 codes, uint8, pool layout
+    v_fp8: Optional[torch.Tensor] = None
+    k_scale: Optional[torch.Tensor] = None    # fp32 [P, Hkv]
+    v_scale: Optional[torch.Tensor] = None
 
     @property
     def batch(self) -> int:
@@ -94,6 +98,10 @@ class Workload:
                 v = v.to(device)
             kw[f.name] = v
         return Workload(**kw)
+
+    def kv_bytes_fp8(self) -> int:
+        """K+V bytes of one pass over the FP8 cache (one byte per element)."""
+        return self.kv_bytes() // 2
 
     def kv_bytes(self) -> int:
         """Algorithmic K+V bytes one pass reads: exactly kv_len tokens per
@@ -182,6 +190,37 @@ def make_decode(lengths: Sequence[int], num_qo_heads: int, num_kv_heads: int,
                     sm_scale=fp32_scale(head_dim), seed=seed,
                     kv_len=L.to(torch.int32), kv_indptr=indptr, kv_indices=indices,
                     q=q, k_cache=k, v_cache=v)
+
+
+def to_fp8_cache(w: Workload, poison: bool = True) -> Workload:
+    """``w`` plus an FP8 copy of its K/V pools: for every (page, kv head) tile,
+    scale = max |x| / 448 over the slots the batch uses (448 is the largest
+    finite E4M3 value; a tile with no used slot or all zeros gets scale 1), and
+    codes = torch's round-to-nearest-even E4M3 (``float8_e4m3fn``) of x / scale.
+    ``w`` should be built without poison; with ``poison`` the codes of unused
+    pages and of slots past each sequence's end are the NaN code 0x7F."""
+    P, Hkv, ps, D = w.k_cache.shape
+    used = torch.zeros(P, ps, dtype=torch.bool)      # (page, slot) holds a token
+    for r in range(w.batch):
+        a, L = int(w.kv_indptr[r]), int(w.kv_len[r])
+        for j in range(-(-L // ps)):
+            page = int(w.kv_indices[a + j])
+            used[page, :min(ps, L - j * ps)] = True
+
+    def quant(pool):
+        x = pool.float()
+        m = (x.abs() * used[:, None, :, None]).amax(dim=(2, 3))
+        scale = torch.where(m > 0, m / 448.0, torch.ones_like(m)).to(torch.float32)
+        codes = (x / scale[:, :, None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        if poison:
+            codes = torch.where(used[:, None, :, None], codes, torch.full_like(codes, 0x7F))
+        return codes.contiguous(), scale.contiguous()
+
+    kc, ksc = quant(w.k_cache)
+    vc, vsc = quant(w.v_cache)
+    kw = {f.name: getattr(w, f.name) for f in fields(w)}
+    kw.update(k_fp8=kc, v_fp8=vc, k_scale=ksc, v_scale=vsc, name=w.name + "_fp8")
+    return Workload(**kw)
 
 
 def make_append(prefix_lens: Sequence[int], qo_lens: Sequence[int], num_qo_heads: int,
