@@ -26,6 +26,11 @@ be compared with it element for element:
    are its chunks (page ranges: step boundaries times gp, the last clipped to
    n), so each worker runs c steps (the last one fewer) in page order, and no
    chunk boundary falls inside a step. The reported chunk size is c*gp pages.
+   Exception for small batches: if there are no more units than workers and
+   the longest unit has fewer than NO_SPLIT_STEPS = 12 steps more than c,
+   every unit stays whole on worker = its enumeration index (splitting would
+   save fewer steps than the merge it needs costs); the reported chunk size
+   is then the longest unit's steps times gp.
 4. Deterministic mode. A unit of n pages has k = ceil(n / c) chunks with
    c = det_chunk_pages, chunk j covering pages [floor(j*n/k),
    floor((j+1)*n/k)): boundaries depend on the request alone. Chunks are
@@ -43,6 +48,7 @@ from __future__ import annotations
 
 import heapq
 
+NO_SPLIT_STEPS = 12  # balanced mode keeps units whole if splitting saves fewer steps
 FLAG_LIST_Q = 1     # query rows come from the member list (cascade prefix)
 FLAG_PARTIAL = 2    # write fp32 partial rows instead of final rows
 FLAG_CAUSAL = 4     # bottom-right causal mask
@@ -89,6 +95,11 @@ def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_p
     steps = [_ceil_div(u["n_pages"], gp) for u in units]
     W = sum(steps)
     c = max(1, _ceil_div(int(min_chunk_pages), gp), _ceil_div(W, num_workers))
+    longest = max(steps, default=0)
+    if len(units) <= num_workers and longest - c < NO_SPLIT_STEPS:
+        # small batch: splitting would save fewer steps than a merge costs
+        return [[(0, u["n_pages"], i)] if u["n_pages"] > 0 else []
+                for i, u in enumerate(units)], max(1, longest) * gp
     g = 0
     for u, ns in zip(units, steps):
         n = u["n_pages"]

@@ -15,6 +15,10 @@
 //             into quotas of c = max(1, ceil(min_chunk_pages / gp), ceil(W / S))
 //             steps, S = num_cus * workers_per_cu; quota w is worker w's, so
 //             every worker runs the same number of steps (even split)
+//             small batches: with no more units than workers and the longest
+//             unit under kNoSplitSteps steps longer than c, every unit stays
+//             whole on worker = its index (a split would save fewer steps
+//             than its merge launch costs)
 //   deterministic: c = det_chunk_pages; a unit of n pages has k = ceil(n/c)
 //             chunks [floor(jn/k), floor((j+1)n/k)), boundaries depending on
 //             the request alone, placed by Graham's longest-processing-time
@@ -143,6 +147,9 @@ struct LevelBuild {
   std::vector<std::pair<int32_t, std::vector<int32_t>>> chunks;  // per unit: k, partial dsts
 };
 
+// Balanced mode keeps every unit whole when a split would save fewer steps.
+constexpr int64_t kNoSplitSteps = 12;
+
 void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all_partial,
                  int32_t& next_row, LevelBuild& lb, Level& lv) {
   const int32_t ps = d.page_size;
@@ -166,8 +173,14 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
     for (const Unit& u : units) W += ceil_div(u.n_pages, gp);
     const int64_t cs = std::max<int64_t>({1, ceil_div(lv.min_chunk_pages, gp), ceil_div(W, S)});
     c = cs * gp;
+    int64_t longest = 0;
+    for (const Unit& u : units) longest = std::max<int64_t>(longest, ceil_div(u.n_pages, gp));
+    const bool whole = (int64_t)units.size() <= S && longest - cs < kNoSplitSteps;
+    if (whole) c = std::max<int64_t>(1, longest) * gp;
     int64_t g = 0;   // global step offset of the unit
-    for (size_t ui = 0; ui < units.size(); ++ui) {
+    for (size_t ui = 0; whole && ui < units.size(); ++ui)
+      if (units[ui].n_pages > 0) pieces[ui].push_back({0, units[ui].n_pages, (int32_t)ui});
+    for (size_t ui = 0; !whole && ui < units.size(); ++ui) {
       const int64_t n = units[ui].n_pages, ns = ceil_div(n, gp);
       for (int64_t p = 0; p < ns;) {
         const int64_t w = (g + p) / cs;

@@ -187,3 +187,27 @@ def test_lpt_balances_deterministic_chunks():
     # Graham's LPT bound: max load <= mean + largest item
     largest = max(-(-(x[F["t_end"]] - x[F["t_begin"]]) // ps) + 1 for x in lv["items"])
     assert max(loads) <= total / S + largest
+
+
+def test_small_batch_keeps_units_whole():
+    """Balanced mode: when splitting would save fewer than NO_SPLIT_STEPS steps,
+    each unit is one item on worker = its enumeration index, and nothing merges."""
+    ps, S = 16, 1024
+    lens = [37, 300, 120, 5, 0]
+    indptr, L = _decode_inputs(lens, ps)
+    p = plan_ref("decode", 8, 2, ps, indptr, L, S, [16])
+    lv = p["levels"][0]
+    # only the empty request's zero-part records (they write o = 0, lse = -inf)
+    assert all(m[4] == 0 for m in p["merges"]) and len(p["merges"]) == 2
+    units = [(r, g) for r in range(len(lens)) for g in range(2)]
+    for i, (r, g) in enumerate(units):
+        its = lv["items"][lv["worker_indptr"][i]:lv["worker_indptr"][i + 1]]
+        if lens[r] == 0:
+            assert len(its) == 0
+            continue
+        assert len(its) == 1 and its[0][F["t_begin"]] == 0 and its[0][F["t_end"]] == lens[r]
+    # one long request: a split saves many steps, so it still happens
+    lens2 = [37, 300, 4096]
+    indptr2, L2 = _decode_inputs(lens2, ps)
+    p2 = plan_ref("decode", 8, 2, ps, indptr2, L2, S, [16])
+    assert any(m[4] > 1 for m in p2["merges"])
