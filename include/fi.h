@@ -96,6 +96,9 @@ typedef struct fi_plan_desc {
   int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 4) */
   int32_t num_prefix_groups; /* cascade: number of shared prefixes             */
   int32_t decode_engine;     /* fi_engine for decode-style levels (default 0)  */
+  int32_t max_prefix_depth;  /* cascade: longest chain of nested shared prefixes
+                                a request may have (default 1; bounds the
+                                workspace and is checked by fi_plan)          */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;
@@ -146,7 +149,13 @@ fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_pages,
  *     qo_r <= kv_len_h[r]; kv_len counts the new tokens;
  *   prefix_indptr_h [NG+1], prefix_len_h [NG], req_prefix_group_h [B]
  *     (cascade only, else NULL): each group's prefix pages and tokens, and the
- *     group of each request (-1 = none).
+ *     group of each request (-1 = none);
+ *   prefix_parent_h [NG] (cascade, optional): the group whose prefix comes
+ *     before this group's (-1 = none), with parent index < group index. A
+ *     request of group g then attends to the prefixes of g's chain, root
+ *     first, then its own suffix: a tree of shared prefixes (research note,
+ *     "Arithmetic intensity": every shared prefix is read once for all the
+ *     requests under it). NULL: every group is a root.
  * The plan splits each request's KV range into chunks (deterministic mode:
  * det_chunk_pages each; balanced: about equal total work per worker), places
  * chunks on num_cus*workers_per_cu persistent workers (longest first), and
@@ -159,8 +168,8 @@ fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_pages,
 fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_h,
                   const int32_t* kv_len_h, const int32_t* qo_indptr_h,
                   const int32_t* prefix_indptr_h, const int32_t* prefix_len_h,
-                  const int32_t* req_prefix_group_h, void* ws_dev,
-                  size_t ws_dev_bytes, void* ws_host, size_t ws_host_bytes,
+                  const int32_t* req_prefix_group_h, const int32_t* prefix_parent_h,
+                  void* ws_dev, size_t ws_dev_bytes, void* ws_host, size_t ws_host_bytes,
                   void* stream, fi_plan_t** out);
 
 void fi_plan_destroy(fi_plan_t* plan);

@@ -256,11 +256,19 @@ def merge_states(v, s):
     return o, l
 
 
+def _chain(req_group, prefix_parent, r):
+    """Request r's prefix groups, root first (own group last)."""
+    out, h = [], int(req_group[r])
+    while h >= 0:
+        out.append(h)
+        h = -1 if prefix_parent is None else int(prefix_parent[h])
+    return out[::-1]
+
+
 def _cascade_kv(k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len, req_group,
-                kv_indptr, kv_indices, kv_len, page_size, r, g):
-    grp = int(req_group[r])
+                kv_indptr, kv_indices, kv_len, page_size, r, g, prefix_parent=None):
     parts_k, parts_v = [], []
-    if grp >= 0:
+    for grp in _chain(req_group, prefix_parent, r):
         a, L = int(prefix_indptr[grp]), int(prefix_len[grp])
         parts_k.append(gather_tokens(k_pool, prefix_indices, a, L, page_size, g))
         parts_v.append(gather_tokens(v_pool, prefix_indices, a, L, page_size, g))
@@ -272,12 +280,14 @@ def _cascade_kv(k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len, req_g
 
 def cascade_flat(q, k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len, req_group,
                  kv_indptr, kv_indices, kv_len, page_size: int, sm_scale: float,
-                 requests=None):
+                 requests=None, prefix_parent=None):
     """The definition of the cascade result: decode attention of each request
-    over the concatenation (its group's shared prefix) || (its own suffix)
-    (backend-selection note, *Arithmetic intensity*: the prefix is read once and
-    reused across requests; the result is the same attention). Pinned by:
-    equality with the two-level form, and with plain decode over a flat table.
+    over the concatenation (its groups' shared prefixes, root first) || (its own
+    suffix) (backend-selection note, *Arithmetic intensity*: a shared prefix is
+    read once and reused across requests; the result is the same attention).
+    ``prefix_parent[g]`` (optional) is the group whose prefix precedes g's, so
+    the groups form a tree. Pinned by: equality with the level-by-level form,
+    and with plain decode over a flat table.
     """
     B, Hq, D = q.shape
     Hkv = k_pool.shape[1]
@@ -288,7 +298,7 @@ def cascade_flat(q, k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len, r
         for g in range(Hkv):
             pk, pv, sk, sv = _cascade_kv(k_pool, v_pool, prefix_indptr, prefix_indices,
                                          prefix_len, req_group, kv_indptr, kv_indices,
-                                         kv_len, page_size, r, g)
+                                         kv_len, page_size, r, g, prefix_parent)
             K = np.concatenate(pk + [sk]) if pk else sk
             V = np.concatenate(pv + [sv]) if pv else sv
             hs = _heads_of(g, G)
@@ -298,9 +308,10 @@ def cascade_flat(q, k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len, r
 
 def cascade_two_level(q, k_pool, v_pool, prefix_indptr, prefix_indices, prefix_len,
                       req_group, kv_indptr, kv_indices, kv_len, page_size: int,
-                      sm_scale: float, requests=None):
-    """Two-level form: (attention over the prefix) merged with (attention over
-    the suffix), prefix first. Must equal ``cascade_flat``."""
+                      sm_scale: float, requests=None, prefix_parent=None):
+    """Level-by-level form: one attention state per prefix of the request's
+    chain and one for its suffix, folded root first with ``merge_two``. Must
+    equal ``cascade_flat``."""
     B, Hq, D = q.shape
     Hkv = k_pool.shape[1]
     G = Hq // Hkv
@@ -310,12 +321,12 @@ def cascade_two_level(q, k_pool, v_pool, prefix_indptr, prefix_indices, prefix_l
         for g in range(Hkv):
             pk, pv, sk, sv = _cascade_kv(k_pool, v_pool, prefix_indptr, prefix_indices,
                                          prefix_len, req_group, kv_indptr, kv_indices,
-                                         kv_len, page_size, r, g)
+                                         kv_len, page_size, r, g, prefix_parent)
             hs = _heads_of(g, G)
-            if pk:
-                op, lp = attend(q[r, hs], pk[0], pv[0], sm_scale)
-            else:
-                op, lp = np.zeros((G, D)), np.full(G, NEG_INF)
+            oc, lc = np.zeros((G, D)), np.full(G, NEG_INF)
+            for kk, vv in zip(pk, pv):
+                op, lp = attend(q[r, hs], kk, vv, sm_scale)
+                oc, lc = merge_two(oc, lc, op, lp)
             os_, ls = attend(q[r, hs], sk, sv, sm_scale)
-            o[r, hs], lse[r, hs] = merge_two(op, lp, os_, ls)
+            o[r, hs], lse[r, hs] = merge_two(oc, lc, os_, ls)
     return o, lse

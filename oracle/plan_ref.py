@@ -13,7 +13,11 @@ be compared with it element for element:
    row = i*G + h) are cut into blocks of ``rows_per_block`` rows. A unit is
    (request, block, kv head), enumerated in that nesting order. For the
    cascade prefix level a unit is (group, block, kv head) over the rows of the
-   group's member requests (ascending request index).
+   group's member requests (ascending request index); with a tree of prefixes
+   (``prefix_parent``, parent index < group index) a group's members are the
+   requests whose chain of groups (own group, its parent, ...) passes through
+   it, and each request's prefix parts are merged in group index order, root
+   first.
 2. Key range. A unit sees tokens [0, t_lim): t_lim = kv_len, or under the
    causal mask min(kv_len, kv_len - qo + i_last + 1) with i_last the last
    query token in the block. It spans n = ceil(t_lim / ps) pages.
@@ -118,7 +122,7 @@ def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_p
 def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
              num_workers, rows_per_block, deterministic=False, det_chunk_pages=64,
              min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
-             prefix_len=None, req_group=None):
+             prefix_len=None, req_group=None, prefix_parent=None):
     """Return the plan as plain lists.
 
     ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
@@ -162,8 +166,15 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
         NG = len(prefix_len)
         pu = []
         rpb = rows_per_block[0]
+        def chain(r):           # request r's groups, own first, then parents
+            out, h = [], int(req_group[r])
+            while h >= 0:
+                out.append(h)
+                h = -1 if prefix_parent is None else int(prefix_parent[h])
+            return out
+        chains = [chain(r) for r in range(B)]
         for grp in range(NG):
-            members = [r for r in range(B) if int(req_group[r]) == grp]
+            members = [r for r in range(B) if grp in chains[r]]
             PL = int(prefix_len[grp])
             if not members or PL == 0:
                 continue
@@ -237,7 +248,8 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
             members = qlist[u["q_base"]:]
             for local in range(0, u["n_rows"], G):
                 r = members[(u["row0"] + local) // G]
-                pref[(r, u["g"])] = [d + local for d in dsts]
+                # groups come in index order (parents first): root prefix first
+                pref.setdefault((r, u["g"]), []).extend(d + local for d in dsts)
         for ui, u in enumerate(su):
             r, g = u["unit"], u["g"]
             k, dsts = schunks[ui]

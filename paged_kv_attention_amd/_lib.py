@@ -24,7 +24,7 @@ class PlanDesc(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "kind", "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "causal",
         "deterministic", "det_chunk_pages", "min_chunk_pages", "num_cus", "workers_per_cu",
-        "num_prefix_groups", "decode_engine")]
+        "num_prefix_groups", "decode_engine", "max_prefix_depth")]
 
 
 I32P = POINTER(c_int32)
@@ -45,7 +45,7 @@ class PlanInfo(ctypes.Structure):
 SIGNATURES = {
     "fi_workspace_size": (c_int32, [POINTER(PlanDesc), c_int64, c_int64, c_int64,
                                     POINTER(c_size_t), POINTER(c_size_t)]),
-    "fi_plan": (c_int32, [POINTER(PlanDesc), I32P, I32P, I32P, I32P, I32P, I32P, c_void_p,
+    "fi_plan": (c_int32, [POINTER(PlanDesc), I32P, I32P, I32P, I32P, I32P, I32P, I32P, c_void_p,
                           c_size_t, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
     "fi_plan_destroy": (None, [c_void_p]),
     "fi_plan_get_info": (c_int32, [c_void_p, POINTER(PlanInfo)]),

@@ -59,13 +59,26 @@ class Workspace:
         return dev.value, host.value
 
 
+def _prefix_depth(parent, ng: int) -> int:
+    """Longest chain of nested prefix groups (1 without parents). Invalid
+    parents are left for fi_plan to report."""
+    if parent is None or ng == 0:
+        return 1
+    depth = [1] * ng
+    for g in range(ng):
+        p = int(parent[g])
+        if 0 <= p < g:
+            depth[g] = depth[p] + 1
+    return max(depth)
+
+
 class Plan:
     """A work plan for one batch (fi_plan). ``device=None`` builds it on the
     host only (needs ``num_cus``), which the run calls refuse."""
 
     def __init__(self, kind: str, kv_indptr, kv_len, num_qo_heads: int, num_kv_heads: int,
                  head_dim: int, page_size: int, *, qo_indptr=None, causal: bool = False,
-                 prefix_indptr=None, prefix_len=None, req_prefix_group=None,
+                 prefix_indptr=None, prefix_len=None, req_prefix_group=None, prefix_parent=None,
                  deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
                  num_cus: int = 0, workers_per_cu: int = 0, engine: str = "default",
                  device="cuda",
@@ -75,7 +88,8 @@ class Plan:
         self._ha = dict(kv_indptr=_host_i32(kv_indptr), kv_len=_host_i32(kv_len),
                         qo_indptr=_host_i32(qo_indptr), prefix_indptr=_host_i32(prefix_indptr),
                         prefix_len=_host_i32(prefix_len),
-                        req_prefix_group=_host_i32(req_prefix_group))
+                        req_prefix_group=_host_i32(req_prefix_group),
+                        prefix_parent=_host_i32(prefix_parent))
         B = int(self._ha["kv_len"].size)
         ng = 0 if prefix_len is None else int(self._ha["prefix_len"].size)
         self.desc = L.PlanDesc(kind=_KINDS[kind], batch=B, num_qo_heads=num_qo_heads,
@@ -84,7 +98,8 @@ class Plan:
                                deterministic=int(deterministic),
                                det_chunk_pages=det_chunk_pages, min_chunk_pages=min_chunk_pages,
                                num_cus=num_cus, workers_per_cu=workers_per_cu,
-                               num_prefix_groups=ng, decode_engine=_ENGINES[engine])
+                               num_prefix_groups=ng, decode_engine=_ENGINES[engine],
+                               max_prefix_depth=_prefix_depth(self._ha["prefix_parent"], ng))
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim, self.page_size, self.batch = head_dim, page_size, B
         self.device = None if device is None else torch.device(device)
@@ -107,7 +122,8 @@ class Plan:
         a = self._ha
         L.check(lib.fi_plan(ctypes.byref(self.desc), _p(a["kv_indptr"]), _p(a["kv_len"]),
                             _p(a["qo_indptr"]), _p(a["prefix_indptr"]), _p(a["prefix_len"]),
-                            _p(a["req_prefix_group"]), ws_dev, dev_b, ws_host, host_b, stream,
+                            _p(a["req_prefix_group"]), _p(a["prefix_parent"]), ws_dev, dev_b,
+                            ws_host, host_b, stream,
                             ctypes.byref(h)), "fi_plan")
         self._h = h
         self.num_q_tokens = B if qo_indptr is None else int(self._ha["qo_indptr"][-1])

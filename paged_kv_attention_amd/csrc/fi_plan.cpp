@@ -7,7 +7,10 @@
 // valid; PR #4038, "What it does": fp32 partials reduced in a fixed order) but
 // give no algorithm. The rule implemented here:
 //   units   : (request, row block, kv head); cascade prefix: (group, row block,
-//             kv head) over the member requests' rows
+//             kv head) over the member requests' rows, a group's members being
+//             the requests whose chain of groups (own, parent, ...) passes
+//             through it; groups in index order, so a request's prefix parts
+//             come root first
 //   key range of a unit: [0, t_lim), t_lim = kv_len, or min(kv_len,
 //             kv_len - qo + i_last + 1) under the bottom-right causal mask
 //   balanced: the level's units, counted in 32-token steps of gp =
@@ -293,6 +296,8 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.decode_engine == FI_ENGINE_VALU && G > 8)
     return set_error(FI_ERR_UNSUPPORTED, "the VALU decode engine takes head groups <= 8, got %d",
                      G);
+  if (d.max_prefix_depth < 0) return set_error(FI_ERR_INVALID_ARG, "negative max_prefix_depth");
+  if (d.max_prefix_depth == 0) d.max_prefix_depth = 1;
   if (d.det_chunk_pages == 0) d.det_chunk_pages = 64;
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
   if (d.workers_per_cu == 0) d.workers_per_cu = 4;
@@ -321,7 +326,8 @@ static fi_status validate_table(const char* what, int32_t n, const int32_t* indp
 
 static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const int32_t* kv_len,
                        const int32_t* qo_indptr, const int32_t* prefix_indptr,
-                       const int32_t* prefix_len, const int32_t* req_group, HostPlan& hp) {
+                       const int32_t* prefix_len, const int32_t* req_group,
+                       const int32_t* prefix_parent, HostPlan& hp) {
   const int32_t B = d.batch, Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
   const int32_t ps = d.page_size;
   fi_status st = validate_table("kv", B, kv_indptr, kv_len, ps);
@@ -346,6 +352,11 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
       if (req_group[r] < -1 || req_group[r] >= NG)
         return set_error(FI_ERR_INVALID_ARG, "request %d: prefix group %d of %d", r,
                          req_group[r], NG);
+    for (int32_t grp = 0; prefix_parent && grp < NG; ++grp)
+      if (prefix_parent[grp] < -1 || prefix_parent[grp] >= grp)
+        return set_error(FI_ERR_INVALID_ARG,
+                         "prefix group %d: parent %d (need -1 or a lower group index)", grp,
+                         prefix_parent[grp]);
   }
   int32_t next_row = 0;
   auto decode_level = [&](Level& lv) {
@@ -363,14 +374,23 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
     wide_level(hp.level[0]);
     decode_level(hp.level[1]);
     std::vector<Unit> pu;
-    std::vector<int32_t> group_off(NG, -1);
+    // members of a group: the requests whose chain (own group, its parent,
+    // ...) passes through it, in request order
+    std::vector<std::vector<int32_t>> in_group(NG);
+    for (int32_t r = 0; r < B; ++r) {
+      int32_t depth = 0;
+      for (int32_t h = req_group[r]; h >= 0; h = prefix_parent ? prefix_parent[h] : -1) {
+        in_group[h].push_back(r);
+        ++depth;
+      }
+      if (depth > d.max_prefix_depth)
+        return set_error(FI_ERR_INVALID_ARG, "request %d has %d nested prefixes, max_prefix_depth %d",
+                         r, depth, d.max_prefix_depth);
+    }
     for (int32_t grp = 0; grp < NG; ++grp) {
-      std::vector<int32_t> members;
-      for (int32_t r = 0; r < B; ++r)
-        if (req_group[r] == grp) members.push_back(r);
+      const std::vector<int32_t>& members = in_group[grp];
       if (members.empty() || prefix_len[grp] == 0) continue;
       const int32_t off = (int32_t)hp.qlist.size();
-      group_off[grp] = off;
       hp.qlist.insert(hp.qlist.end(), members.begin(), members.end());
       const int64_t rows = (int64_t)members.size() * G;
       for (int64_t b = 0; b < ceil_div(rows, ROWS_WIDE); ++b) {
@@ -502,7 +522,7 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
   };
   if (d.kind == FI_KIND_CASCADE) {
     const int64_t NG = d.num_prefix_groups;
-    const int64_t blocks = ceil_div(B * G, ROWS_WIDE) + NG;
+    const int64_t blocks = ceil_div(B * G * d.max_prefix_depth, ROWS_WIDE) + NG;
     n_items[0] = (size_t)level_bound(S_wide, blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_WIDE);
     n_items[1] = (size_t)level_bound(S_dec, B * Hkv, Hkv * max_kv_pages, ROWS_DECODE);
     workers[0] = (int32_t)S_wide;
@@ -523,7 +543,8 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
     merges = part_rows + blocks * Hkv * 2;
   }
   const size_t n_scatter = d.kind == FI_KIND_APPEND ? (size_t)max_qo_tokens : 0;
-  Layout L = layout_for(workers, n_items, (size_t)merges, (size_t)part_rows, (size_t)B,
+  const size_t n_qlist = (size_t)B * (d.kind == FI_KIND_CASCADE ? d.max_prefix_depth : 1);
+  Layout L = layout_for(workers, n_items, (size_t)merges, (size_t)part_rows, n_qlist,
                         n_scatter, (size_t)part_rows, d.head_dim);
   *dev_bytes = L.dev_bytes;
   *host_bytes = L.blob_bytes;
@@ -533,7 +554,8 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
 extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_h,
                              const int32_t* kv_len_h, const int32_t* qo_indptr_h,
                              const int32_t* prefix_indptr_h, const int32_t* prefix_len_h,
-                             const int32_t* req_prefix_group_h, void* ws_dev,
+                             const int32_t* req_prefix_group_h,
+                             const int32_t* prefix_parent_h, void* ws_dev,
                              size_t ws_dev_bytes, void* ws_host, size_t ws_host_bytes,
                              void* stream, fi_plan_t** out) {
   clear_error();
@@ -556,7 +578,7 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
   fi_plan_t* p = new fi_plan_t();
   p->hp.desc = d;
   st = build(d, kv_indptr_h, kv_len_h, qo_indptr_h, prefix_indptr_h, prefix_len_h,
-             req_prefix_group_h, p->hp);
+             req_prefix_group_h, d.kind == FI_KIND_CASCADE ? prefix_parent_h : nullptr, p->hp);
   if (st != FI_OK) {
     delete p;
     return st;

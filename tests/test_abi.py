@@ -119,6 +119,46 @@ def test_cascade_plan_matches_reference(det):
     compare(info, ref)
 
 
+@pytest.mark.parametrize("det", [False, True])
+def test_cascade_tree_plan_matches_reference(det):
+    """A tree of shared prefixes: 0 is the root, 1 and 2 extend it, 3 extends 1,
+    4 is a second root; requests hang off any node or none."""
+    rng = np.random.default_rng(12)
+    ps = 16
+    suf = list(rng.integers(0, 900, 40)) + [0]
+    groups = list(rng.integers(-1, 5, 41))
+    pref = [4096, 512, 0, 1000, 300]
+    parent = [-1, 0, 0, 1, -1]
+    indptr, L_ = _decode_host(suf, ps)
+    pindptr, PL = _decode_host(pref, ps)
+    p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
+                  req_prefix_group=groups, prefix_parent=parent, deterministic=det, num_cus=16,
+                  workers_per_cu=4)
+    info = p.info()
+    ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info), deterministic=det,
+                   det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
+                   prefix_parent=parent)
+    compare(info, ref)
+    # a request of group 3 merges the prefixes of 0, 1, 3 (root first), then its suffix
+    r = groups.index(3)
+    m = [x for x in info["merges"] if x[0] == r][0]
+    assert m[4] >= 3
+
+
+def test_cascade_tree_errors():
+    d = _desc(kind=2, num_prefix_groups=2)
+    kw = dict(pindptr=[0, 2, 3], plen=[32, 10], grp=[1, 0])
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS, par=[-1, 1], **kw)      # own index
+    assert st == L.FI_ERR_INVALID_ARG and "parent" in msg, msg
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS, par=[1, -1], **kw)      # forward
+    assert st == L.FI_ERR_INVALID_ARG and "parent" in msg, msg
+    st, msg = _raw_plan(d, GOOD_INDPTR, GOOD_LENS, par=[-1, 0], **kw)      # depth 2 > 1
+    assert st == L.FI_ERR_INVALID_ARG and "max_prefix_depth" in msg, msg
+    d2 = _desc(kind=2, num_prefix_groups=2, max_prefix_depth=2)
+    st, msg = _raw_plan(d2, GOOD_INDPTR, GOOD_LENS, par=[-1, 0], **kw)
+    assert st == L.FI_OK, msg
+
+
 def test_workspace_bound_covers_plans():
     rng = np.random.default_rng(3)
     for trial in range(20):
@@ -138,11 +178,15 @@ def test_workspace_bound_covers_plans():
         if kind == "append":
             kw.update(qo_indptr=_indptr(qo), causal=True)
             n_q = int(qo.sum())
+        depth = 1
         if kind == "cascade":
             pref = [int(x) for x in rng.integers(0, 4000, 2)]
             pi, pl = _decode_host(pref, ps)
             kw.update(prefix_indptr=pi, prefix_len=pl,
                       req_prefix_group=rng.integers(-1, 2, B))
+            if trial % 4 == 2:
+                kw.update(prefix_parent=[-1, 0])
+                depth = 2
             n_p = int(pi[-1])
         p = host_plan(kind, indptr, L_, 32, 8, 128, ps, **kw)
         info = p.info()
@@ -150,7 +194,8 @@ def test_workspace_bound_covers_plans():
                           num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=ps,
                           causal=1, deterministic=int(det), det_chunk_pages=kw["det_chunk_pages"],
                           num_cus=9, workers_per_cu=3,
-                          num_prefix_groups=2 if kind == "cascade" else 0)
+                          num_prefix_groups=2 if kind == "cascade" else 0,
+                          max_prefix_depth=depth)
         dev, host = fi.Workspace.bound(desc, int(indptr[-1]), n_q, n_p)
         assert dev >= info["dev_bytes_used"], (trial, kind)
         assert host >= info["host_bytes_used"], (trial, kind)
@@ -160,13 +205,15 @@ def test_workspace_bound_covers_plans():
 # host-detectable errors
 
 
-def _raw_plan(desc, indptr, lens, qo=None, pindptr=None, plen=None, grp=None):
+def _raw_plan(desc, indptr, lens, qo=None, pindptr=None, plen=None, grp=None, par=None):
     lib = fi.load()
     h = ctypes.c_void_p()
     arr = lambda a: None if a is None else np.ascontiguousarray(a, dtype=np.int32)  # noqa: E731
     keep = [arr(x) for x in (indptr, lens, qo, pindptr, plen, grp)]
     ptrs = [None if a is None else a.ctypes.data_as(L.I32P) for a in keep]
-    st = lib.fi_plan(ctypes.byref(desc), *ptrs, None, 0, None, 0, None, ctypes.byref(h))
+    par_arr = arr(par)
+    parent = None if par_arr is None else par_arr.ctypes.data_as(L.I32P)
+    st = lib.fi_plan(ctypes.byref(desc), *ptrs, parent, None, 0, None, 0, None, ctypes.byref(h))
     if st == 0:
         lib.fi_plan_destroy(h)
     return st, lib.fi_last_error().decode()

@@ -308,6 +308,52 @@ def test_cascade_flat_equals_two_level_and_flat_decode():
     assert np.array_equal(od, of) and np.array_equal(ld, lf)
 
 
+def check_cascade_tree():
+    """Tree of prefixes 0 <- 1 <- 3 and 0 <- 2: flat definition == level by
+    level == plain decode over the flat table built here by walking parents."""
+    rng = np.random.default_rng(18)
+    ps, Hq, Hkv, D = 8, 4, 2, 16
+    pref_lens = [32, 24, 16, 8]
+    parent = [-1, 0, 0, 1]
+    suf_lens = [5, 0, 17, 9, 30, 3, 11]
+    groups = [0, 1, 2, -1, 3, 3, 1]
+    dk = [rng.standard_normal((Hkv, L, D)) for L in pref_lens + suf_lens]
+    dv = [rng.standard_normal((Hkv, L, D)) for L in pref_lens + suf_lens]
+    kp, ip, ix, _ = paginate(dk, ps, np.random.default_rng(2))
+    vp, _, _, _ = paginate(dv, ps, np.random.default_rng(2))
+    npf = len(pref_lens)
+    prefix_indptr, kv_indptr = ip[:npf + 1], ip[npf:]
+    q = rng.standard_normal((len(suf_lens), Hq, D))
+    args = (q, kp, vp, prefix_indptr, ix, np.array(pref_lens), np.array(groups), kv_indptr, ix,
+            np.array(suf_lens), ps, 0.25)
+    of, lf = A.cascade_flat(*args, prefix_parent=np.array(parent))
+    o2, l2 = A.cascade_two_level(*args, prefix_parent=np.array(parent))
+    np.testing.assert_allclose(of, o2, atol=1e-12)
+    np.testing.assert_allclose(lf, l2, atol=1e-12)
+    fl_indptr, fl_idx, fl_len = [0], [], []
+    for r, g in enumerate(groups):
+        chain = []
+        while g >= 0:
+            chain.insert(0, g)
+            g = parent[g]
+        pages, L = [], suf_lens[r]
+        for h in chain:
+            pages += list(ix[prefix_indptr[h]:prefix_indptr[h + 1]])
+            L += pref_lens[h]
+        pages += list(ix[kv_indptr[r]:kv_indptr[r + 1]])
+        fl_idx += pages
+        fl_indptr.append(len(fl_idx))
+        fl_len.append(L)
+    od, ld = A.paged_decode(q, kp, vp, np.array(fl_indptr), np.array(fl_idx), np.array(fl_len),
+                            ps, 0.25)
+    np.testing.assert_allclose(od, of, atol=1e-12)
+    np.testing.assert_allclose(ld, lf, atol=1e-12)
+
+
+def test_cascade_tree_flat_equals_levels_and_flat_decode():
+    check_cascade_tree()
+
+
 def test_append_single_query_equals_decode():
     rng = np.random.default_rng(9)
     q, dk, dv, kp, vp, indptr, indices, L = decode_case(3, 8, 2, 16, 16, [3, 40, 77], rng)
@@ -407,7 +453,7 @@ def _mut_merge_sign(o1, l1, o2, l2):
 
 
 _ORIG = {n: getattr(A, n) for n in ("gather_tokens", "attend", "merge_two", "paged_append",
-                                    "paged_decode_fp8", "e4m3_values")}
+                                    "paged_decode_fp8", "e4m3_values", "_chain")}
 
 
 def _mut_append_top_left(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
@@ -489,6 +535,10 @@ def test_fp8_decode_equals_decode_of_torch_dequantized_pools():
     assert np.isnan(o2[[0, 2]]).all()
 
 
+def _mut_chain_own_group_only(req_group, prefix_parent, r):
+    return _ORIG["_chain"](req_group, None, r)
+
+
 def _mut_fp8_swap_scales(q, kc, vc, ks, vs, *rest, **kw):
     return _ORIG["paged_decode_fp8"](q, kc, vc, vs, ks, *rest, **kw)
 
@@ -510,6 +560,7 @@ MUTATIONS = {
     "fp8_scales_swapped": ("paged_decode_fp8", _mut_fp8_swap_scales,
                            test_fp8_decode_equals_decode_of_torch_dequantized_pools),
     "e4m3_bias_8": ("e4m3_values", _mut_e4m3_bias8, test_e4m3_values_match_torch_for_every_code),
+    "cascade_no_parents": ("_chain", _mut_chain_own_group_only, check_cascade_tree),
 }
 
 

@@ -65,7 +65,8 @@ def test_skewed_decode_config_sampled(dev):
 def _cascade_run(w, dev, **kw):
     p = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                 w.page_size, prefix_indptr=w.prefix_indptr, prefix_len=w.prefix_len,
-                req_prefix_group=w.req_prefix_group, device=dev, **kw)
+                req_prefix_group=w.req_prefix_group, prefix_parent=w.prefix_parent, device=dev,
+                **kw)
     g = w.to(dev)
     o, lse = fi.cascade(p, g.q, g.k_cache, g.v_cache, g.prefix_indices, g.kv_indices, w.sm_scale)
     torch.cuda.synchronize()
@@ -78,8 +79,9 @@ def _oracle_cascade(w, reqs):
     tabs = (w.prefix_indptr.numpy(), w.prefix_indices.numpy(), w.prefix_len.numpy(),
             w.req_prefix_group.numpy(), w.kv_indptr.numpy(), w.kv_indices.numpy(),
             w.kv_len.numpy(), w.page_size, w.sm_scale)
-    o, lse = oracle.cascade_flat(q, kp, vp, *tabs, requests=reqs)
-    a, _ = oracle.cascade_flat(q, kp, np.abs(vp), *tabs, requests=reqs)
+    par = None if w.prefix_parent is None else w.prefix_parent.numpy()
+    o, lse = oracle.cascade_flat(q, kp, vp, *tabs, requests=reqs, prefix_parent=par)
+    a, _ = oracle.cascade_flat(q, kp, np.abs(vp), *tabs, requests=reqs, prefix_parent=par)
     return o, lse, a
 
 
@@ -474,3 +476,32 @@ def test_fp8_decode_refuses_the_valu_engine(dev):
     w = to_fp8_cache(make_decode([40, 7], 8, 2, 64, 16, seed=9, poison=False), poison=True)
     with pytest.raises(fi.FIError, match="matrix-core"):
         _fp8_run(w, dev, engine="valu")
+
+
+# ---------------------------------------------------------------- prefix trees
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_cascade_tree(dev, det):
+    """Nested shared prefixes: 0 (root) <- 1 <- 3, 0 <- 2, and a second root 4;
+    requests on every node and on none. Each prefix is read once for every
+    request under it; the result is attention over the chain || suffix."""
+    parent = [-1, 0, 0, 1, -1]
+    pref = [2048, 512, 256, 128, 1008]
+    rng = np.random.default_rng(31)
+    B = 40
+    groups = [int(x) for x in rng.integers(-1, 5, B)]
+    suf = [int(x) for x in rng.integers(0, 700, B)]
+    w = make_cascade(pref, groups, suf, 32, 8, 128, 16, seed=32, poison=True,
+                     prefix_parent=parent)
+    o, lse = _cascade_run(w, dev, deterministic=det)
+    o_ref, l_ref, a_ref = _oracle_cascade(w, None)
+    compare(o, lse, o_ref, l_ref, a_ref, what=f"cascade tree det={det}")
+    # the same batch as plain decode over the flattened tables (GPU vs GPU)
+    ip, ix, ln = cascade_flat_tables(w)
+    p = fi.Plan("decode", ip, ln, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                device=dev)
+    g = w.to(dev)
+    of, lf = fi.paged_decode(p, g.q, g.k_cache, g.v_cache, ix.to(dev), w.sm_scale)
+    torch.cuda.synchronize()
+    compare(of, lf, o_ref, l_ref, a_ref, what="flat decode of the tree")

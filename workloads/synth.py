@@ -76,6 +76,7 @@ class Workload:
     prefix_indices: Optional[torch.Tensor] = None
     prefix_len: Optional[torch.Tensor] = None
     req_prefix_group: Optional[torch.Tensor] = None
+    prefix_parent: Optional[torch.Tensor] = None   # cascade tree: parent group (-1 = root)
     k_fp8: Optional[torch.Tensor] = None      # FP8 E4M3 codes, uint8, pool layout
     v_fp8: Optional[torch.Tensor] = None
     k_scale: Optional[torch.Tensor] = None    # fp32 [P, Hkv]
@@ -272,9 +273,12 @@ def make_append(prefix_lens: Sequence[int], qo_lens: Sequence[int], num_qo_heads
 def make_cascade(prefix_lens: Sequence[int], req_group: Sequence[int],
                  suffix_lens: Sequence[int], num_qo_heads: int, num_kv_heads: int,
                  head_dim: int, page_size: int, seed: int, poison: bool = True,
-                 name: str = "cascade", _gen: Optional[torch.Generator] = None) -> Workload:
+                 name: str = "cascade", _gen: Optional[torch.Generator] = None,
+                 prefix_parent: Optional[Sequence[int]] = None) -> Workload:
     """Decode queries over (shared prefix of group ``req_group[r]``) || (own suffix).
-    Each prefix is stored once in the pool; ``req_group[r] = -1`` means no prefix."""
+    Each prefix is stored once in the pool; ``req_group[r] = -1`` means no prefix.
+    With ``prefix_parent`` (parent index < group index, -1 = root) the groups
+    form a tree and a request's prefix is the chain root .. own group."""
     gen = _gen if _gen is not None else torch.Generator().manual_seed(seed)
     PL = torch.as_tensor(list(prefix_lens), dtype=torch.int64)
     S = torch.as_tensor(list(suffix_lens), dtype=torch.int64)
@@ -304,23 +308,29 @@ def make_cascade(prefix_lens: Sequence[int], req_group: Sequence[int],
                     kv_len=S.to(torch.int32), kv_indptr=indptr, kv_indices=indices,
                     q=q, k_cache=k, v_cache=v,
                     prefix_indptr=prefix_indptr, prefix_indices=prefix_indices,
-                    prefix_len=PL.to(torch.int32), req_prefix_group=grp.to(torch.int32))
+                    prefix_len=PL.to(torch.int32), req_prefix_group=grp.to(torch.int32),
+                    prefix_parent=None if prefix_parent is None else
+                    torch.as_tensor(list(prefix_parent), dtype=torch.int32))
 
 
 def cascade_flat_tables(w: Workload):
-    """(kv_indptr, kv_indices, kv_len) of the flat table prefix || suffix per
-    request. Only defined when every prefix length is a multiple of the page
-    size, so the flat page list is the plain concatenation of the two lists."""
+    """(kv_indptr, kv_indices, kv_len) of the flat table (prefixes of the
+    request's chain, root first) || suffix per request. Only defined when every
+    prefix length is a multiple of the page size, so the flat page list is the
+    plain concatenation of the lists."""
     assert w.kind == "cascade"
     ps = w.page_size
     assert all(int(x) % ps == 0 for x in w.prefix_len), "prefix not page aligned"
     idx, counts, lens = [], [], []
     for r in range(w.batch):
-        g = int(w.req_prefix_group[r])
+        chain, g = [], int(w.req_prefix_group[r])
+        while g >= 0:
+            chain.append(g)
+            g = -1 if w.prefix_parent is None else int(w.prefix_parent[g])
         a, b = int(w.kv_indptr[r]), int(w.kv_indptr[r + 1])
         pages = []
         L = int(w.kv_len[r])
-        if g >= 0:
+        for g in reversed(chain):
             pa, pb = int(w.prefix_indptr[g]), int(w.prefix_indptr[g + 1])
             pages.append(w.prefix_indices[pa:pb])
             L += int(w.prefix_len[g])
