@@ -28,6 +28,7 @@ METRIC = "paged decode attention µs/call and achieved KV HBM GB/s (% of peak), 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 CONFIG_INDEX = 1               # the Llama-3-8B-like decode batch
 KERNEL_SOURCES = ("paged_kv_attention_amd/csrc/fi_attention.hip",
+                  "paged_kv_attention_amd/csrc/fi_decode_body.h",
                   "paged_kv_attention_amd/csrc/fi_device.h",
                   "paged_kv_attention_amd/csrc/fi_internal.h")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_llama3_8b_decode.json")
@@ -184,8 +185,11 @@ def explore(args, dev):
     append), for the design notes; prints its own JSON line."""
     import torch
     import paged_kv_attention_amd as fi
-    from workloads import CONFIG_NAMES, make_config
-    w = make_config(args.config, poison=False)
+    from workloads import CONFIG_NAMES, POD_MIX_NAME, make_config, make_pod_mix
+    if args.pod_mix:
+        w, name = make_pod_mix(poison=False), POD_MIX_NAME
+    else:
+        w, name = make_config(args.config, poison=False), CONFIG_NAMES[args.config]
     if args.kv == "fp8":
         if w.kind != "decode":
             raise SystemExit("bench.py: --kv fp8 applies to the decode configurations")
@@ -216,7 +220,7 @@ def explore(args, dev):
     else:
         plan = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, qo_indptr=w.qo_indptr, causal=True,
-                       device=dev, **kw)
+                       device=dev, pod=args.pod, pod_wide_blocks=args.pod_wide_blocks, **kw)
         call = lambda: fi.paged_append(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
                                        w.sm_scale, k_new=g.k_new, v_new=g.v_new)
         qo = (w.qo_indptr[1:] - w.qo_indptr[:-1]).long()
@@ -238,8 +242,11 @@ def explore(args, dev):
         torch.cuda.synchronize()
     kern_ms = kt.total_ms / max(1, kt.calls)
     kv = w.kv_bytes_fp8() if args.kv == "fp8" else w.kv_bytes()
-    print(json.dumps({"workload": CONFIG_NAMES[args.config], "mode": args.mode,
-                      "engine": args.engine, "kv": args.kv,
+    extra = {}
+    if w.kind == "append":
+        extra = {"pod": bool(args.pod), "pod_wide_blocks": plan.info()["pod_wide_blocks"]}
+    print(json.dumps({"workload": name, "mode": args.mode,
+                      "engine": args.engine, "kv": args.kv, **extra,
                       "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
                       "kv_bytes": kv, "kv_GBps": round(kv / ms / 1e6, 1),
                       "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
@@ -267,6 +274,13 @@ def main():
                     help="skip the graph-replay, cold-cache and deterministic-mode context")
     ap.add_argument("--config", type=int, default=CONFIG_INDEX,
                     help="other configurations print an exploratory line (not the bench line)")
+    ap.add_argument("--pod-mix", action="store_true",
+                    help="exploratory line on the chunked-prefill mixed batch (64 decode "
+                         "requests beside two 512-token prefill chunks)")
+    ap.add_argument("--pod", action="store_true",
+                    help="append workloads: plan the fused mixed-batch launch")
+    ap.add_argument("--pod-wide-blocks", type=int, default=0,
+                    help="with --pod: workgroups of the wide role (0 = the plan's choice)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -280,7 +294,7 @@ def main():
 
     dev = torch.device("cuda:0")
     fi.load()
-    if args.config != CONFIG_INDEX or args.kv != "bf16":
+    if args.config != CONFIG_INDEX or args.kv != "bf16" or args.pod_mix:
         explore(args, dev)
         return
     print(f"bench: generating {CONFIG_NAMES[CONFIG_INDEX]}", file=sys.stderr, flush=True)

@@ -99,6 +99,9 @@ typedef struct fi_plan_desc {
   int32_t max_prefix_depth;  /* cascade: longest chain of nested shared prefixes
                                 a request may have (default 1; bounds the
                                 workspace and is checked by fi_plan)          */
+  int32_t pod;               /* append: 1 = fused mixed batch (see below)      */
+  int32_t pod_wide_blocks;   /* pod: workgroups given to the multi-query
+                                requests (0 = sized by the plan's cost model) */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;
@@ -129,6 +132,8 @@ typedef struct fi_plan_info {
   int32_t num_scatter;
   size_t dev_bytes_used;
   size_t host_bytes_used;
+  int32_t pod_wide_blocks;       /* pod plans: workgroups of the wide role (the
+                                    rest run the decode role), else 0 */
 } fi_plan_info;
 
 /* Upper bound on the device and pinned-host workspace bytes of any plan with
@@ -210,7 +215,17 @@ fi_status fi_paged_decode_fp8(const fi_plan_t* plan, const void* q, const void* 
  * first writes them into the cache slots of the new tokens (positions
  * kv_len-qo .. kv_len-1 of each request); then query i of request r (global
  * row qo_indptr[r]+i) attends to keys 0..kv_len-qo+i (causal plan) or to all
- * kv_len keys. Both or neither of k_new/v_new. */
+ * kv_len keys. Both or neither of k_new/v_new.
+ * Fused mixed batch (desc.pod = 1; research note, "Arithmetic intensity":
+ * POD attention runs the prefill and the decode rows of one batch in one
+ * kernel): a request whose query rows (qo * Hq/Hkv) fit one 16-row block runs
+ * in the decode role (one wavefront per worker, K/V streamed through
+ * registers), every other request in the wide role (a workgroup sharing K/V
+ * through LDS); one launch of num_cus * max(1, workers_per_cu / 2)
+ * workgroups (two per CU by default, so both roles share every CU) covers
+ * both, the plan giving pod_wide_blocks of them to the wide role by estimated
+ * cost.
+ * Same results as the unfused plan, up to rounding. */
 fi_status fi_paged_append(const fi_plan_t* plan, const void* q, const void* k_new,
                           const void* v_new, void* k_cache, void* v_cache,
                           const int32_t* kv_indices, float sm_scale, void* o,

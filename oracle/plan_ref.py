@@ -46,6 +46,20 @@ be compared with it element for element:
    each chunk writes fp32 partial rows (allocated in enumeration order) that a
    merge folds in chunk order. Cascade writes partials for everything and
    merges the prefix chunk(s) first, then the suffix chunks.
+6. Fused mixed batch (append, research note *Arithmetic intensity*: POD
+   attention runs a batch's prefill and decode rows in one kernel). A request
+   whose query rows (qo * G) fit one 16-row block belongs to the decode role
+   (level 1, 16-row units), every other request to the wide role (level 0,
+   128-row units). The launch has P workgroups; with W_w and W_d the two
+   roles' steps (as in 3), the wide role gets n_w = P if there are no decode
+   steps, 0 if there are no wide steps, else the override if one is given
+   (capped at P - 1), else round-half-up(P * c_w / (c_w + c_d)) clamped to
+   [1, P - 1], with c_w = 2 W_w and c_d = W_d (a wide workgroup step takes
+   about twice as long as a decode wavefront step; four of those run side by
+   side in a decode workgroup). Each role is planned as in
+   3-4 over its own workers (n_w workgroups; 4 (P - n_w) wavefronts), then
+   its worker list is padded with empty workers to P (wide) and 4P (decode).
+   Partial rows are allocated wide role first; merges likewise.
 """
 
 from __future__ import annotations
@@ -53,6 +67,9 @@ from __future__ import annotations
 import heapq
 
 NO_SPLIT_STEPS = 12  # balanced mode keeps units whole if splitting saves fewer steps
+POD_WIDE_STEP = 2    # fused mixed batch: time of a wide workgroup step ...
+POD_DECODE_STEP = 1  # ... and of a decode wavefront step
+POD_DECODE_ROWS = 16  # query rows of a request that runs in the decode role
 FLAG_LIST_Q = 1     # query rows come from the member list (cascade prefix)
 FLAG_PARTIAL = 2    # write fp32 partial rows instead of final rows
 FLAG_CAUSAL = 4     # bottom-right causal mask
@@ -122,7 +139,8 @@ def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_p
 def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
              num_workers, rows_per_block, deterministic=False, det_chunk_pages=64,
              min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
-             prefix_len=None, req_group=None, prefix_parent=None):
+             prefix_len=None, req_group=None, prefix_parent=None, pod_blocks=None,
+             pod_wide_blocks=0):
     """Return the plan as plain lists.
 
     ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
@@ -132,6 +150,9 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     Result: ``{"levels": [{"items": [...12-tuples...], "worker_indptr": [...]}],
     "merges": [(q_tok, head0, n_heads, parts_off, n_parts)], "parts": [...],
     "qlist": [...], "n_part_rows": int}``.
+    ``pod_blocks`` (append only): plan a fused mixed batch over that many
+    workgroups (rule 6; ``rows_per_block`` and ``min_chunk_pages`` then name
+    the wide and the decode role); the result also holds ``pod_wide_blocks``.
     """
     nlev = len(rows_per_block)
     workers = list(num_workers) if isinstance(num_workers, (list, tuple)) else [num_workers] * nlev
@@ -143,9 +164,11 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     kv_len = [int(x) for x in kv_len]
     kv_indptr = [int(x) for x in kv_indptr]
 
-    def request_units(rpb, qo_of, qtok_of, is_causal):
+    def request_units(rpb, qo_of, qtok_of, is_causal, take=lambda r: True):
         units = []
         for r in range(B):
+            if not take(r):
+                continue
             nq, L = qo_of(r), kv_len[r]
             rows = nq * G
             for b in range(_ceil_div(rows, rpb)):
@@ -192,8 +215,28 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
         levels_units.append(request_units(rows_per_block[1], lambda r: 1, lambda r: r, False))
     elif kind == "append":
         qo = [int(qo_indptr[r + 1]) - int(qo_indptr[r]) for r in range(B)]
-        levels_units.append(request_units(rows_per_block[0], lambda r: qo[r],
-                                          lambda r: int(qo_indptr[r]), bool(causal)))
+        if pod_blocks is None:
+            levels_units.append(request_units(rows_per_block[0], lambda r: qo[r],
+                                              lambda r: int(qo_indptr[r]), bool(causal)))
+        else:
+            P = int(pod_blocks)
+            small = [qo[r] * G <= POD_DECODE_ROWS for r in range(B)]
+            for lev, role in ((0, False), (1, True)):
+                levels_units.append(request_units(
+                    rows_per_block[lev], lambda r: qo[r], lambda r: int(qo_indptr[r]),
+                    bool(causal), take=lambda r, role=role: small[r] == role))
+            gp = max(1, 32 // ps)
+            w_steps = [sum(_ceil_div(u["n_pages"], gp) for u in lu) for lu in levels_units]
+            if w_steps[1] == 0:
+                n_w = P
+            elif w_steps[0] == 0:
+                n_w = 0
+            elif pod_wide_blocks > 0:
+                n_w = min(int(pod_wide_blocks), P - 1)
+            else:
+                cw, cd = POD_WIDE_STEP * w_steps[0], POD_DECODE_STEP * w_steps[1]
+                n_w = max(1, min(P - 1, (2 * P * cw + cw + cd) // (2 * (cw + cd))))
+            workers = [n_w, 4 * (P - n_w)]
     else:
         levels_units.append(request_units(rows_per_block[0], lambda r: 1, lambda r: r, False))
 
@@ -203,6 +246,11 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     unit_chunks = []    # per level: per unit (k, [partial dst rows])
     for lev, units in enumerate(levels_units):
         S = workers[lev]
+        if S == 0:      # a fused role with no workgroups (and no units)
+            assert not units
+            levels.append(dict(items=[], worker_indptr=[0], chunk_pages=0))
+            unit_chunks.append([])
+            continue
         pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev],
                                  page_size)
         items = []
@@ -257,16 +305,23 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
             merges.append((r, g * G, G, len(parts), len(plist)))
             parts.extend(plist)
     else:
-        units, (chunks_of) = levels_units[0], unit_chunks[0]
-        for ui, u in enumerate(units):
-            k, dsts = chunks_of[ui]
-            if k == 1:
-                continue
-            r0, r1 = u["row0"], u["row0"] + u["n_rows"]
-            for i in range(r0 // G, (r1 - 1) // G + 1):
-                a, b = max(r0, i * G), min(r1, (i + 1) * G)
-                plist = [d + (a - r0) for d in dsts]
-                merges.append((u["q_base"] + i, u["g"] * G + (a - i * G), b - a,
-                               len(parts), len(plist)))
-                parts.extend(plist)
-    return dict(levels=levels, merges=merges, parts=parts, qlist=qlist, n_part_rows=next_row)
+        for units, chunks_of in zip(levels_units, unit_chunks):
+            for ui, u in enumerate(units):
+                k, dsts = chunks_of[ui]
+                if k == 1:
+                    continue
+                r0, r1 = u["row0"], u["row0"] + u["n_rows"]
+                for i in range(r0 // G, (r1 - 1) // G + 1):
+                    a, b = max(r0, i * G), min(r1, (i + 1) * G)
+                    plist = [d + (a - r0) for d in dsts]
+                    merges.append((u["q_base"] + i, u["g"] * G + (a - i * G), b - a,
+                                   len(parts), len(plist)))
+                    parts.extend(plist)
+    out = dict(levels=levels, merges=merges, parts=parts, qlist=qlist, n_part_rows=next_row)
+    if kind == "append" and pod_blocks is not None:
+        P = int(pod_blocks)
+        for lev, total in ((0, P), (1, 4 * P)):
+            ind = levels[lev]["worker_indptr"]
+            ind.extend([ind[-1]] * (total + 1 - len(ind)))
+        out["pod_wide_blocks"] = workers[0]
+    return out

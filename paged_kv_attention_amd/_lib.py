@@ -24,7 +24,7 @@ class PlanDesc(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "kind", "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "causal",
         "deterministic", "det_chunk_pages", "min_chunk_pages", "num_cus", "workers_per_cu",
-        "num_prefix_groups", "decode_engine", "max_prefix_depth")]
+        "num_prefix_groups", "decode_engine", "max_prefix_depth", "pod", "pod_wide_blocks")]
 
 
 I32P = POINTER(c_int32)
@@ -38,6 +38,7 @@ class PlanInfo(ctypes.Structure):
         ("num_merges", c_int32), ("merges", I32P), ("num_parts", c_int32), ("parts", I32P),
         ("num_qlist", c_int32), ("qlist", I32P), ("num_part_rows", c_int32),
         ("num_scatter", c_int32), ("dev_bytes_used", c_size_t), ("host_bytes_used", c_size_t),
+        ("pod_wide_blocks", c_int32),
     ]
 
 

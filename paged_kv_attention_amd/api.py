@@ -81,7 +81,7 @@ class Plan:
                  prefix_indptr=None, prefix_len=None, req_prefix_group=None, prefix_parent=None,
                  deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
                  num_cus: int = 0, workers_per_cu: int = 0, engine: str = "default",
-                 device="cuda",
+                 pod: bool = False, pod_wide_blocks: int = 0, device="cuda",
                  workspace: Optional[Workspace] = None):
         lib = L.load()
         self.kind = kind
@@ -99,7 +99,8 @@ class Plan:
                                det_chunk_pages=det_chunk_pages, min_chunk_pages=min_chunk_pages,
                                num_cus=num_cus, workers_per_cu=workers_per_cu,
                                num_prefix_groups=ng, decode_engine=_ENGINES[engine],
-                               max_prefix_depth=_prefix_depth(self._ha["prefix_parent"], ng))
+                               max_prefix_depth=_prefix_depth(self._ha["prefix_parent"], ng),
+                               pod=int(pod), pod_wide_blocks=pod_wide_blocks)
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim, self.page_size, self.batch = head_dim, page_size, B
         self.device = None if device is None else torch.device(device)
@@ -162,7 +163,8 @@ class Plan:
                     merges=arr(inf.merges, inf.num_merges * L.FI_MERGE_INTS).reshape(-1, L.FI_MERGE_INTS),
                     parts=arr(inf.parts, inf.num_parts), qlist=arr(inf.qlist, inf.num_qlist),
                     num_part_rows=inf.num_part_rows, num_scatter=inf.num_scatter,
-                    dev_bytes_used=inf.dev_bytes_used, host_bytes_used=inf.host_bytes_used)
+                    dev_bytes_used=inf.dev_bytes_used, host_bytes_used=inf.host_bytes_used,
+                    pod_wide_blocks=inf.pod_wide_blocks)
 
 
 def _check_tensor(t, name, dtype, device, shape=None):

@@ -188,10 +188,19 @@ extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const vo
     st = hip_status(launch_scatter(sa, s), "scatter launch");
     if (st != FI_OK) return st;
   }
-  const AttnArgs a =
-      attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
+  AttnArgs a = attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
   TimerScope t(s);
-  st = hip_status(launch_level(p, 0, a, s), "attention launch");
+  if (p->hp.pod) {
+    // one launch of a fixed shape: every worker slot of both roles, whatever
+    // this batch's split
+    AttnArgs da = attn_args(p, 1, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
+    a.num_workers = p->hp.level[0].num_workers;
+    da.num_workers = p->hp.level[1].num_workers;
+    st = hip_status(launch_pod(a, da, at<int32_t>(p, p->lay.meta), d.head_dim, s),
+                    "attention launch");
+  } else {
+    st = hip_status(launch_level(p, 0, a, s), "attention launch");
+  }
   t.done();
   if (st != FI_OK) return st;
   return run_merge(p, o, lse, s);

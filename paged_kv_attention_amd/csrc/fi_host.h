@@ -35,12 +35,17 @@ struct HostPlan {
   std::vector<int32_t> qlist;
   std::vector<int32_t> scatter;  // 2 per new token (append)
   int32_t num_part_rows = 0;
+  // fused mixed batch: level 0 (wide role) runs on workgroups
+  // [0, pod_wide_blocks) of one launch, level 1 (decode role) on the rest
+  bool pod = false;
+  int32_t pod_wide_blocks = 0;
 };
 
 // Byte offsets of each section inside the workspace blob.
 struct Layout {
   size_t items[2] = {0, 0}, windptr[2] = {0, 0};
   size_t merges = 0, parts = 0, qlist = 0, scatter = 0;
+  size_t meta = 0;           // int32 [0]: the pod split (workgroups of the wide role)
   size_t blob_bytes = 0;     // int32 sections (host staging size)
   size_t part_o = 0, part_lse = 0;
   size_t dev_bytes = 0;      // blob + fp32 partial states

@@ -87,6 +87,7 @@ Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t 
   L.parts = take(n_parts);
   L.qlist = take(n_qlist);
   L.scatter = take(n_scatter * 2);
+  L.meta = take(1);
   L.blob_bytes = off;
   L.part_o = off;
   off = align_up(off + n_part_rows * (size_t)head_dim * 4, 256);
@@ -113,10 +114,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Units of a level whose rows are request query tokens (decode, append,
 // cascade suffix). Enumeration order: request, row block, kv head.
+// take: if given, only the requests r with take[r] != 0.
 void request_units(std::vector<Unit>& out, int32_t B, int32_t G, int32_t Hkv, int32_t ps,
                    int32_t rpb, const int32_t* kv_indptr, const int32_t* kv_len,
-                   const int32_t* qo_indptr, bool causal) {
+                   const int32_t* qo_indptr, bool causal, const uint8_t* take = nullptr) {
   for (int32_t r = 0; r < B; ++r) {
+    if (take && !take[r]) continue;
     const int32_t nq = qo_indptr ? qo_indptr[r + 1] - qo_indptr[r] : 1;
     const int32_t qtok = qo_indptr ? qo_indptr[r] : r;
     const int32_t L = kv_len[r];
@@ -152,6 +155,11 @@ struct LevelBuild {
 
 // Balanced mode keeps every unit whole when a split would save fewer steps.
 constexpr int64_t kNoSplitSteps = 12;
+// Fused mixed batch: relative time of a wide-role workgroup step (up to 128
+// rows through MFMA) and of a decode-role wavefront step (a workgroup runs
+// four such wavefronts side by side).
+constexpr int64_t kPodWideStep = 2;
+constexpr int64_t kPodDecodeStep = 1;
 
 void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all_partial,
                  int32_t& next_row, LevelBuild& lb, Level& lv) {
@@ -298,6 +306,9 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
                      G);
   if (d.max_prefix_depth < 0) return set_error(FI_ERR_INVALID_ARG, "negative max_prefix_depth");
   if (d.max_prefix_depth == 0) d.max_prefix_depth = 1;
+  if (d.pod_wide_blocks < 0) return set_error(FI_ERR_INVALID_ARG, "negative pod_wide_blocks");
+  d.pod = (d.kind == FI_KIND_APPEND && d.pod) ? 1 : 0;
+  if (!d.pod) d.pod_wide_blocks = 0;
   if (d.det_chunk_pages == 0) d.det_chunk_pages = 64;
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
   if (d.workers_per_cu == 0) d.workers_per_cu = 4;
@@ -439,27 +450,86 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
       hp.parts.insert(hp.parts.end(), dsts.begin(), dsts.end());
     }
   } else {
-    hp.num_levels = 1;
     const bool append = d.kind == FI_KIND_APPEND;
-    if (append) wide_level(hp.level[0]); else decode_level(hp.level[0]);
-    const int32_t rpb = hp.level[0].rows_per_block;
-    std::vector<Unit> units;
-    request_units(units, B, G, Hkv, ps, rpb, kv_indptr, kv_len, append ? qo_indptr : nullptr,
-                  append && d.causal);
-    LevelBuild lb;
-    build_level(units, d, false, next_row, lb, hp.level[0]);
-    for (size_t ui = 0; ui < units.size(); ++ui) {
-      const Unit& u = units[ui];
-      const int32_t k = lb.chunks[ui].first;
-      if (k == 1) continue;
-      const std::vector<int32_t>& dsts = lb.chunks[ui].second;
-      const int32_t r0 = u.row0, r1 = u.row0 + u.n_rows;
-      for (int32_t i = r0 / G; i <= (r1 - 1) / G; ++i) {
-        const int32_t a = std::max(r0, i * G), b = std::min(r1, (i + 1) * G);
-        const int32_t rec[MERGE_INTS] = {u.q_base + i, u.g * G + (a - i * G), b - a,
-                                         (int32_t)hp.parts.size(), (int32_t)dsts.size()};
-        hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
-        for (int32_t dd : dsts) hp.parts.push_back(dd + (a - r0));
+    const bool causal = append && d.causal;
+    std::vector<Unit> units[2];
+    LevelBuild lb[2];
+    if (append && d.pod) {
+      // Fused mixed batch: requests whose query rows fit one decode row block
+      // go to the decode role (level 1), the others to the wide role (level
+      // 0); the launch's P workgroups (as many as a wide level has) are split
+      // between the roles by cost.
+      hp.num_levels = 2;
+      hp.pod = true;
+      wide_level(hp.level[0]);
+      decode_level(hp.level[1]);
+      const int32_t P = d.num_cus * std::max(1, d.workers_per_cu / 2);
+      std::vector<uint8_t> small(B);
+      for (int32_t r = 0; r < B; ++r) small[r] = (int64_t)(qo_indptr[r + 1] - qo_indptr[r]) * G <= ROWS_DECODE;
+      std::vector<uint8_t> big(B);
+      for (int32_t r = 0; r < B; ++r) big[r] = !small[r];
+      request_units(units[0], B, G, Hkv, ps, ROWS_WIDE, kv_indptr, kv_len, qo_indptr, causal,
+                    big.data());
+      request_units(units[1], B, G, Hkv, ps, ROWS_DECODE, kv_indptr, kv_len, qo_indptr, causal,
+                    small.data());
+      const int64_t gp = std::max(1, 32 / ps);
+      int64_t steps[2] = {0, 0};
+      for (int l = 0; l < 2; ++l)
+        for (const Unit& u : units[l]) steps[l] += ceil_div(u.n_pages, gp);
+      int32_t nw;
+      if (steps[1] == 0) {
+        nw = P;
+      } else if (steps[0] == 0) {
+        nw = 0;
+      } else if (d.pod_wide_blocks > 0) {
+        nw = std::min(d.pod_wide_blocks, P - 1);
+      } else {
+        // wide: kPodWideStep per workgroup step; decode: kPodDecodeStep per
+        // wavefront step, four wavefronts to a workgroup; rounded half up
+        const int64_t cw = kPodWideStep * steps[0], cd = kPodDecodeStep * steps[1];
+        nw = (int32_t)((2 * (int64_t)P * cw + (cw + cd)) / (2 * (cw + cd)));
+        nw = std::max(1, std::min(P - 1, nw));
+      }
+      if (P < 2 && steps[0] > 0 && steps[1] > 0)
+        return set_error(FI_ERR_INVALID_ARG, "a fused mixed batch needs at least 2 workgroups");
+      hp.pod_wide_blocks = nw;
+      hp.level[0].num_workers = nw;
+      hp.level[1].num_workers = WAVES_PER_BLOCK * (P - nw);
+      for (int l = 0; l < 2; ++l) {
+        if (hp.level[l].num_workers > 0) {
+          build_level(units[l], d, false, next_row, lb[l], hp.level[l]);
+        } else {
+          hp.level[l].chunk_pages = 0;
+          hp.level[l].worker_indptr.assign(1, 0);
+        }
+      }
+      // every role sees the whole launch: workers past its share have no items
+      hp.level[0].worker_indptr.resize((size_t)P + 1, hp.level[0].worker_indptr.back());
+      hp.level[1].worker_indptr.resize((size_t)WAVES_PER_BLOCK * P + 1,
+                                       hp.level[1].worker_indptr.back());
+      hp.level[0].num_workers = P;
+      hp.level[1].num_workers = WAVES_PER_BLOCK * P;
+    } else {
+      hp.num_levels = 1;
+      if (append) wide_level(hp.level[0]); else decode_level(hp.level[0]);
+      request_units(units[0], B, G, Hkv, ps, hp.level[0].rows_per_block, kv_indptr, kv_len,
+                    append ? qo_indptr : nullptr, causal);
+      build_level(units[0], d, false, next_row, lb[0], hp.level[0]);
+    }
+    for (int l = 0; l < hp.num_levels; ++l) {
+      for (size_t ui = 0; ui < units[l].size(); ++ui) {
+        const Unit& u = units[l][ui];
+        const int32_t k = lb[l].chunks[ui].first;
+        if (k == 1) continue;
+        const std::vector<int32_t>& dsts = lb[l].chunks[ui].second;
+        const int32_t r0 = u.row0, r1 = u.row0 + u.n_rows;
+        for (int32_t i = r0 / G; i <= (r1 - 1) / G; ++i) {
+          const int32_t a = std::max(r0, i * G), b = std::min(r1, (i + 1) * G);
+          const int32_t rec[MERGE_INTS] = {u.q_base + i, u.g * G + (a - i * G), b - a,
+                                           (int32_t)hp.parts.size(), (int32_t)dsts.size()};
+          hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
+          for (int32_t dd : dsts) hp.parts.push_back(dd + (a - r0));
+        }
       }
     }
     if (append) {
@@ -528,6 +598,18 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
     workers[0] = (int32_t)S_wide;
     workers[1] = (int32_t)S_dec;
     merges = B * Hkv;
+  } else if (d.kind == FI_KIND_APPEND && d.pod) {
+    // wide role: at most P workgroups; decode role: at most 4P wavefronts
+    const int64_t P = S_wide;
+    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;
+    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + 1;
+    n_items[0] = (size_t)level_bound(P, blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
+                                     ROWS_WIDE);
+    n_items[1] = (size_t)level_bound(WAVES_PER_BLOCK * P, B * Hkv, Hkv * max_kv_pages,
+                                     ROWS_DECODE);
+    workers[0] = (int32_t)P;
+    workers[1] = (int32_t)(WAVES_PER_BLOCK * P);
+    merges = part_rows + (blocks + B) * Hkv * 2;
   } else if (d.kind == FI_KIND_APPEND) {
     const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;
     const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + 1;
@@ -622,6 +704,7 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
     if (!hp.parts.empty()) memcpy(h + L.parts, hp.parts.data(), hp.parts.size() * 4);
     if (!hp.qlist.empty()) memcpy(h + L.qlist, hp.qlist.data(), hp.qlist.size() * 4);
     if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
+    memcpy(h + L.meta, &hp.pod_wide_blocks, 4);
     e = hipMemcpyAsync(ws_dev, ws_host, L.blob_bytes, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) {
       if (!ev) {
@@ -672,6 +755,7 @@ extern "C" fi_status fi_plan_get_info(const fi_plan_t* p, fi_plan_info* info) {
   info->num_scatter = (int32_t)(hp.scatter.size() / 2);
   info->dev_bytes_used = p->lay.dev_bytes;
   info->host_bytes_used = p->lay.blob_bytes;
+  info->pod_wide_blocks = hp.pod ? hp.pod_wide_blocks : 0;
   return FI_OK;
 }
 

@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fi_decode_body.h"
 #include "fi_device.h"
 
 namespace fi {
@@ -244,15 +245,15 @@ __device__ __forceinline__ void finalize_wide(const AttnArgs& a, const Item& it,
   }
 }
 
+// The items of workgroup worker wg (the whole 4-wave block).
 template <int D, int NP, bool LQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wide_kernel(AttnArgs a) {
+__device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
   constexpr int KJ = Cfg<D>::KJ, NK = Lds<D>::NK;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * Lds<D>::STAGE];
 
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
   const int wave = uniform(threadIdx.x >> 6);
-  const int wg = blockIdx.x;
   if (wg >= a.num_workers) return;
   const int i_end = ld_uniform(a.worker_indptr, wg + 1);
   const int rl0 = wave * kRowsPerWave;
@@ -292,6 +293,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
   }
 }
 
+template <int D, int NP, bool LQ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wide_kernel(AttnArgs a) {
+  wide_worker<D, NP, LQ>(a, blockIdx.x);
+}
+
+// Mixed batch in one launch (POD attention: prefill and decode rows of one
+// batch in one kernel). Workgroups [0, n_wide) run the wide items (one
+// workgroup worker each), the others the decode items (four wavefront workers
+// each); n_wide comes from the plan in device memory, so the launch shape
+// does not depend on the batch. The decode role keeps a ring of two register
+// tiles, so a wavefront of either role needs at most half a SIMD's registers
+// and two workgroups share a CU: a CU holding one of each overlaps the matrix
+// work of the wide role with the HBM streaming of the decode role.
+template <int D, int NP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pod_kernel(
+    AttnArgs wa, AttnArgs da, const int32_t* __restrict__ meta) {
+  const int n_wide = ld_uniform(meta, 0);
+  if ((int)blockIdx.x < n_wide) {
+    wide_worker<D, NP, false>(wa, blockIdx.x);
+  } else {
+    dec::decode_worker<D, NP, true, 2>(da, ((int)blockIdx.x - n_wide) * WAVES_PER_BLOCK +
+                                      uniform(threadIdx.x >> 6));
+  }
+}
+
 template <int D, bool LQ>
 hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
@@ -304,7 +330,29 @@ hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_pod_d(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, dim3 grid,
+                        hipStream_t s) {
+  if (wa.page_size == 8) {
+    hipLaunchKernelGGL((pod_kernel<D, 4>), grid, dim3(256), 0, s, wa, da, meta);
+  } else if (wa.page_size == 16) {
+    hipLaunchKernelGGL((pod_kernel<D, 2>), grid, dim3(256), 0, s, wa, da, meta);
+  } else {
+    hipLaunchKernelGGL((pod_kernel<D, 1>), grid, dim3(256), 0, s, wa, da, meta);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_pod(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, int head_dim,
+                      hipStream_t stream) {
+  if (wa.num_workers == 0) return hipSuccess;
+  const dim3 grid(wa.num_workers);
+  if (head_dim == 128) return launch_pod_d<128>(wa, da, meta, grid, stream);
+  if (head_dim == 64) return launch_pod_d<64>(wa, da, meta, grid, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream) {
   if (a.num_workers == 0) return hipSuccess;

@@ -102,6 +102,74 @@ def test_append_plan_matches_reference(causal, det):
     assert info["num_scatter"] == int(qo.sum())
 
 
+def _pod_batch(rng, n_small, n_big, ps, G):
+    """Requests of a few query tokens (rows fit one 16-row block) mixed with
+    prefill chunks; kv lengths include the new tokens."""
+    small_q = rng.integers(0, 16 // G + 1, n_small)
+    big_q = rng.integers(16 // G + 1, 300, n_big)
+    qo = np.concatenate([small_q, big_q])
+    rng.shuffle(qo)
+    lens = rng.integers(0, 3000, qo.size) + qo
+    indptr, L_ = _decode_host(lens, ps)
+    return indptr, L_, _indptr(qo), qo
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("det", [False, True])
+@pytest.mark.parametrize("mix,force", [((20, 4), 0), ((30, 0), 0), ((0, 6), 0), ((12, 3), 5),
+                                       ((12, 3), 40)])
+def test_pod_plan_matches_reference(causal, det, mix, force):
+    rng = np.random.default_rng(17 + mix[0] + force)
+    ps, Hq, Hkv = 16, 32, 8
+    indptr, L_, qo_indptr, qo = _pod_batch(rng, mix[0], mix[1], ps, Hq // Hkv)
+    p = host_plan("append", indptr, L_, Hq, Hkv, 128, ps, qo_indptr=qo_indptr, causal=causal,
+                  deterministic=det, det_chunk_pages=8, num_cus=6, workers_per_cu=8, pod=True,
+                  pod_wide_blocks=force)
+    info = p.info()
+    P = 6 * (8 // 2)     # two workgroups per CU per two workers
+    lv = info["levels"]
+    assert [x["num_workers"] for x in lv] == [P, 4 * P]
+    assert [x["rows_per_block"] for x in lv] == [128, 16]
+    ref = plan_ref("append", Hq, Hkv, ps, indptr, L_, **level_params(info), deterministic=det,
+                   det_chunk_pages=8, qo_indptr=qo_indptr, causal=causal, pod_blocks=P,
+                   pod_wide_blocks=force)
+    compare(info, ref)
+    n_w = info["pod_wide_blocks"]
+    assert n_w == ref["pod_wide_blocks"]
+    if mix[1] == 0:
+        assert n_w == 0
+    elif mix[0] == 0:
+        assert n_w == P
+    else:
+        assert 1 <= n_w <= P - 1
+        if force:
+            assert n_w == min(force, P - 1)
+    # the decode role holds exactly the requests whose rows fit 16, each row
+    # block whole: a request's items sit in one role
+    G = Hq // Hkv
+    for role, items in ((0, lv[0]["items"]), (1, lv[1]["items"])):
+        for q_base in np.unique(items[:, 0]) if len(items) else []:
+            r = int(np.searchsorted(qo_indptr, q_base, side="right")) - 1
+            assert (qo[r] * G <= 16) == (role == 1)
+    # wide workers past n_w and decode workers past 4 (P - n_w) are empty
+    wi, di = lv[0]["worker_indptr"], lv[1]["worker_indptr"]
+    assert np.all(wi[n_w:] == wi[-1]) and np.all(di[4 * (P - n_w):] == di[-1])
+    assert info["num_scatter"] == int(qo.sum())
+
+
+def test_pod_plan_off_for_other_kinds_and_unfused_by_default():
+    rng = np.random.default_rng(3)
+    indptr, L_, qo_indptr, qo = _pod_batch(rng, 8, 2, 16, 4)
+    p = host_plan("append", indptr, L_, 32, 8, 128, 16, qo_indptr=qo_indptr, num_cus=4)
+    assert len(p.info()["levels"]) == 1 and p.info()["pod_wide_blocks"] == 0
+    d_indptr, d_len = _decode_host([100, 200], 16)
+    p = host_plan("decode", d_indptr, d_len, 32, 8, 128, 16, num_cus=4, pod=True)
+    assert len(p.info()["levels"]) == 1 and p.info()["pod_wide_blocks"] == 0
+    with pytest.raises(fi.FIError):
+        host_plan("append", indptr, L_, 32, 8, 128, 16, qo_indptr=qo_indptr, num_cus=4,
+                  pod=True, pod_wide_blocks=-1)
+
+
 @pytest.mark.parametrize("det", [False, True])
 def test_cascade_plan_matches_reference(det):
     rng = np.random.default_rng(11)
@@ -161,22 +229,23 @@ def test_cascade_tree_errors():
 
 def test_workspace_bound_covers_plans():
     rng = np.random.default_rng(3)
-    for trial in range(20):
+    for trial in range(30):
         ps = int(rng.choice([8, 16, 32]))
         B = int(rng.integers(1, 60))
         kind = ["decode", "append", "cascade"][trial % 3]
         det = bool(trial % 2)
+        pod = kind == "append" and trial % 4 == 1
         lens = rng.integers(0, 5000, B)
         qo = np.minimum(lens, rng.integers(0, 100, B))
-        if kind == "append":
-            pass
+        if pod:   # mostly requests of one to four query tokens
+            qo = np.minimum(lens, np.where(rng.random(B) < 0.8, rng.integers(1, 5, B), qo))
         indptr, L_ = _decode_host(lens, ps)
         kw = dict(deterministic=det, det_chunk_pages=int(rng.integers(1, 80)), num_cus=9,
                   workers_per_cu=3)
         n_q = 0
         n_p = 0
         if kind == "append":
-            kw.update(qo_indptr=_indptr(qo), causal=True)
+            kw.update(qo_indptr=_indptr(qo), causal=True, pod=pod)
             n_q = int(qo.sum())
         depth = 1
         if kind == "cascade":
@@ -195,7 +264,8 @@ def test_workspace_bound_covers_plans():
                           causal=1, deterministic=int(det), det_chunk_pages=kw["det_chunk_pages"],
                           num_cus=9, workers_per_cu=3,
                           num_prefix_groups=2 if kind == "cascade" else 0,
-                          max_prefix_depth=depth)
+                          max_prefix_depth=depth, pod=int(pod))
+        assert len(info["levels"]) == (2 if pod or kind == "cascade" else 1)
         dev, host = fi.Workspace.bound(desc, int(indptr[-1]), n_q, n_p)
         assert dev >= info["dev_bytes_used"], (trial, kind)
         assert host >= info["host_bytes_used"], (trial, kind)

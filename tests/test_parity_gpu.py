@@ -15,7 +15,7 @@ import paged_kv_attention_amd as fi
 from tests.helpers import (compare, gpu_decode, np_pools, oracle_decode, request_rows,
                            sample_requests)
 from workloads import (cascade_flat_tables, make_append, make_cascade, make_config, make_decode,
-                       to_fp8_cache)
+                       make_pod_mix, to_fp8_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -367,6 +367,82 @@ def test_valu_engine_cascade(dev):
     compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what="cascade valu")
 
 
+# ---------------------------------------------------------------- fused mixed batch
+
+
+def _append_run(w, dev, causal=True, **kw):
+    p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                w.page_size, qo_indptr=w.qo_indptr, causal=causal, device=dev, **kw)
+    g = w.to(dev)
+    o, lse = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale,
+                             k_new=g.k_new, v_new=g.v_new)
+    torch.cuda.synchronize()
+    return o, lse, p
+
+
+def _scattered_pools(w):
+    kp, vp = np_pools(w)
+    return oracle.scatter_new_kv(kp, vp, w.k_new.float().numpy(), w.v_new.float().numpy(),
+                                 w.qo_indptr.numpy(), w.kv_indptr.numpy(), w.kv_indices.numpy(),
+                                 w.kv_len.numpy(), w.page_size)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 2), (128, 32, 8), (64, 16, 1),
+                                    (128, 64, 16)])
+def test_pod_small_sweep(dev, causal, D, ps, G):
+    """Mixed batches in one fused launch: requests whose rows fit 16 run in the
+    decode role (with the causal mask over their few query tokens), the rest
+    in the wide role; every plan variant against the oracle."""
+    prefix = [0, 5, 16, 40, 300, 1, 700, 33, 1000, 2, 7]
+    qo = [1, 3, 17, 1, 70, 2, 1, 4, 1, 40, 0]
+    Hkv = 2
+    w = make_append(prefix, qo, G * Hkv, Hkv, D, ps, seed=600 + D + ps + G, causal=causal)
+    kp2, vp2 = _scattered_pools(w)
+    o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, causal)
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
+               dict(pod_wide_blocks=1), dict(num_cus=3)]:
+        o, lse, p = _append_run(w, dev, causal, pod=True, **kw)
+        info = p.info()
+        assert len(info["levels"][1]["items"]) > 0
+        compare(o, lse, o_ref, l_ref, a_ref,
+                what=f"pod causal={causal} D={D} ps={ps} G={G} {kw} n_w={info['pod_wide_blocks']}")
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_pod_mixed_sampled(dev, det):
+    """The chunked-prefill serving step (64 decode requests beside two
+    512-token prefill chunks) through the fused launch: sampled requests of
+    both roles against the oracle, and the whole batch against the unfused
+    plan."""
+    w = make_pod_mix(poison=True)
+    o, lse, p = _append_run(w, dev, pod=True, deterministic=det)
+    info = p.info()
+    assert 1 <= info["pod_wide_blocks"] < info["levels"][0]["num_workers"]
+    qo = w.qo_indptr.diff()
+    pre = [int(i) for i in torch.nonzero(qo > 1).flatten()]
+    rng = np.random.default_rng(31)
+    dec = [int(i) for i in rng.choice(torch.nonzero(qo == 1).flatten().numpy(), 6, replace=False)]
+    reqs = sorted(pre[:1] + dec)
+    kp2, vp2 = _scattered_pools(w)
+    o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, True, reqs)
+    rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in reqs])
+    compare(o, lse, o_ref, l_ref, a_ref, rows=rows, what=f"pod mixed det={det}")
+    o2, lse2, _ = _append_run(w, dev, deterministic=det)
+    assert float((o2.float() - o.float()).abs().max()) <= 2e-2
+    assert float(((lse2 - lse).abs() / lse.abs().clamp(min=1)).max()) <= 2e-3
+
+
+def test_pod_deterministic_bits_independent_of_split(dev):
+    """Deterministic mode: a request's bits do not depend on how the launch
+    is split between the roles."""
+    w = make_pod_mix(poison=False, n_decode=24, n_prefill=1, prefill_q=200)
+    outs = [_append_run(w, dev, pod=True, deterministic=True, det_chunk_pages=8,
+                        pod_wide_blocks=nw)[:2] for nw in (0, 3, 100)]
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
 # ---------------------------------------------------------------- HIP graphs
 
 
@@ -383,11 +459,11 @@ def _capture(fn):
     return graph
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 4])
+@pytest.mark.parametrize("cfg", [1, 3, 4, "pod"])
 def test_graph_replay_matches_eager(dev, cfg):
     """A captured run call (no allocation, no memset inside) replays to the
     eager bits, replay after replay, with other eager work in between."""
-    w = make_config(cfg, poison=False)
+    w = make_pod_mix(poison=False) if cfg == "pod" else make_config(cfg, poison=False)
     g = w.to(dev)
     T = g.q.shape[0]
     out = torch.empty_like(g.q)
@@ -405,7 +481,8 @@ def test_graph_replay_matches_eager(dev, cfg):
                                        g.kv_indices, w.sm_scale, out=o, lse=l)
     else:
         p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                    w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev)
+                    w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev,
+                    pod=cfg == "pod")
         call = lambda o, l: fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
                                             w.sm_scale, k_new=g.k_new, v_new=g.v_new, out=o,
                                             lse=l)

@@ -14,6 +14,8 @@ from .synth import (  # noqa: F401
     make_decode,
     make_append,
     make_cascade,
+    make_pod_mix,
+    POD_MIX_NAME,
     cascade_flat_tables,
     fp32_scale,
     to_fp8_cache,

@@ -343,6 +343,28 @@ def cascade_flat_tables(w: Workload):
             torch.tensor(lens, dtype=torch.int32))
 
 
+POD_MIX_NAME = "pod_mixed"
+
+
+def make_pod_mix(poison: bool = False, seed: Optional[int] = None, n_decode: int = 64,
+                 n_prefill: int = 2, prefill_q: int = 512) -> Workload:
+    """One step of a chunked-prefill serving batch: ``n_decode`` requests
+    decoding one token over kv U[512, 4096] (the Llama-3-8B-like decode
+    shape) beside ``n_prefill`` prefill chunks of ``prefill_q`` query tokens
+    over cached prefixes U[1024, 4096]; 32 q / 8 kv heads, D 128, page 16,
+    causal, new K/V scattered. Decode and prefill requests are interleaved."""
+    seed = BASE_SEED + 100 if seed is None else seed
+    gen = torch.Generator().manual_seed(seed)
+    dec = _lengths_uniform(gen, n_decode, 512, 4096) - 1
+    pre = _lengths_uniform(gen, n_prefill, 1024, 4096)
+    prefix = torch.cat([dec, pre])
+    qo = torch.cat([torch.ones(n_decode, dtype=torch.int64),
+                    torch.full((n_prefill,), prefill_q, dtype=torch.int64)])
+    order = torch.randperm(prefix.numel(), generator=gen)
+    return make_append(prefix[order].tolist(), qo[order].tolist(), 32, 8, 128, 16, seed, poison,
+                       True, True, POD_MIX_NAME, _gen=gen)
+
+
 def make_config(k: int, poison: bool = False, seed: Optional[int] = None) -> Workload:
     """The five benchmark configurations, by 0-based index (see CONFIG_NAMES)."""
     seed = BASE_SEED + k if seed is None else seed
