@@ -212,7 +212,7 @@ def explore(args, dev):
         plan = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, prefix_indptr=w.prefix_indptr,
                        prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group,
-                       device=dev, **kw)
+                       device=dev, pod=args.pod, pod_wide_blocks=args.pod_wide_blocks, **kw)
         call = lambda: fi.cascade(plan, g.q, g.k_cache, g.v_cache, g.prefix_indices,  # noqa
                                   g.kv_indices, w.sm_scale)
         per_req = w.kv_len.long() + w.prefix_len[0].long()
@@ -243,7 +243,7 @@ def explore(args, dev):
     kern_ms = kt.total_ms / max(1, kt.calls)
     kv = w.kv_bytes_fp8() if args.kv == "fp8" else w.kv_bytes()
     extra = {}
-    if w.kind == "append":
+    if w.kind != "decode":
         extra = {"pod": bool(args.pod), "pod_wide_blocks": plan.info()["pod_wide_blocks"]}
     print(json.dumps({"workload": name, "mode": args.mode,
                       "engine": args.engine, "kv": args.kv, **extra,
@@ -278,7 +278,7 @@ def main():
                     help="exploratory line on the chunked-prefill mixed batch (64 decode "
                          "requests beside two 512-token prefill chunks)")
     ap.add_argument("--pod", action="store_true",
-                    help="append workloads: plan the fused mixed-batch launch")
+                    help="append and cascade workloads: plan one fused launch for both roles")
     ap.add_argument("--pod-wide-blocks", type=int, default=0,
                     help="with --pod: workgroups of the wide role (0 = the plan's choice)")
     args = ap.parse_args()

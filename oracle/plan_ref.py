@@ -59,7 +59,9 @@ be compared with it element for element:
    side in a decode workgroup). Each role is planned as in
    3-4 over its own workers (n_w workgroups; 4 (P - n_w) wavefronts), then
    its worker list is padded with empty workers to P (wide) and 4P (decode).
-   Partial rows are allocated wide role first; merges likewise.
+   Partial rows are allocated wide role first; merges likewise. A cascade
+   plan may be fused the same way: its prefix level is the wide role and its
+   suffix level the decode role, split by the same rule.
 """
 
 from __future__ import annotations
@@ -150,7 +152,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     Result: ``{"levels": [{"items": [...12-tuples...], "worker_indptr": [...]}],
     "merges": [(q_tok, head0, n_heads, parts_off, n_parts)], "parts": [...],
     "qlist": [...], "n_part_rows": int}``.
-    ``pod_blocks`` (append only): plan a fused mixed batch over that many
+    ``pod_blocks`` (append and cascade): plan one fused launch of that many
     workgroups (rule 6; ``rows_per_block`` and ``min_chunk_pages`` then name
     the wide and the decode role); the result also holds ``pod_wide_blocks``.
     """
@@ -219,26 +221,29 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
             levels_units.append(request_units(rows_per_block[0], lambda r: qo[r],
                                               lambda r: int(qo_indptr[r]), bool(causal)))
         else:
-            P = int(pod_blocks)
             small = [qo[r] * G <= POD_DECODE_ROWS for r in range(B)]
             for lev, role in ((0, False), (1, True)):
                 levels_units.append(request_units(
                     rows_per_block[lev], lambda r: qo[r], lambda r: int(qo_indptr[r]),
                     bool(causal), take=lambda r, role=role: small[r] == role))
-            gp = max(1, 32 // ps)
-            w_steps = [sum(_ceil_div(u["n_pages"], gp) for u in lu) for lu in levels_units]
-            if w_steps[1] == 0:
-                n_w = P
-            elif w_steps[0] == 0:
-                n_w = 0
-            elif pod_wide_blocks > 0:
-                n_w = min(int(pod_wide_blocks), P - 1)
-            else:
-                cw, cd = POD_WIDE_STEP * w_steps[0], POD_DECODE_STEP * w_steps[1]
-                n_w = max(1, min(P - 1, (2 * P * cw + cw + cd) // (2 * (cw + cd))))
-            workers = [n_w, 4 * (P - n_w)]
     else:
         levels_units.append(request_units(rows_per_block[0], lambda r: 1, lambda r: r, False))
+
+    if pod_blocks is not None and kind != "decode":
+        # rule 6: split the launch's P workgroups between the two roles
+        P = int(pod_blocks)
+        gp = max(1, 32 // ps)
+        w_steps = [sum(_ceil_div(u["n_pages"], gp) for u in lu) for lu in levels_units]
+        if w_steps[1] == 0:
+            n_w = P
+        elif w_steps[0] == 0:
+            n_w = 0
+        elif pod_wide_blocks > 0:
+            n_w = min(int(pod_wide_blocks), P - 1)
+        else:
+            cw, cd = POD_WIDE_STEP * w_steps[0], POD_DECODE_STEP * w_steps[1]
+            n_w = max(1, min(P - 1, (2 * P * cw + cw + cd) // (2 * (cw + cd))))
+        workers = [n_w, 4 * (P - n_w)]
 
     all_partial = kind == "cascade"
     next_row = 0
@@ -246,10 +251,10 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     unit_chunks = []    # per level: per unit (k, [partial dst rows])
     for lev, units in enumerate(levels_units):
         S = workers[lev]
-        if S == 0:      # a fused role with no workgroups (and no units)
-            assert not units
+        if S == 0:      # a fused role with no workgroups (and no steps)
+            assert all(u["n_pages"] == 0 for u in units)
             levels.append(dict(items=[], worker_indptr=[0], chunk_pages=0))
-            unit_chunks.append([])
+            unit_chunks.append([(0, [])] * len(units))
             continue
         pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev],
                                  page_size)
@@ -318,7 +323,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                                    len(parts), len(plist)))
                     parts.extend(plist)
     out = dict(levels=levels, merges=merges, parts=parts, qlist=qlist, n_part_rows=next_row)
-    if kind == "append" and pod_blocks is not None:
+    if kind != "decode" and pod_blocks is not None:
         P = int(pod_blocks)
         for lev, total in ((0, P), (1, 4 * P)):
             ind = levels[lev]["worker_indptr"]

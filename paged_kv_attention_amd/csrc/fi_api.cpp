@@ -95,6 +95,19 @@ hipError_t launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStr
   return launch_decode(a, D, s);
 }
 
+// A pod plan's two levels in one launch of a fixed shape: every worker slot of
+// both roles, whatever this batch's split.
+hipError_t launch_fused(const fi_plan_t* p, const void* q, const void* k, const void* v,
+                        const int32_t* kv_indices, const int32_t* prefix_indices,
+                        float sm_scale, void* o, float* lse, hipStream_t s) {
+  AttnArgs wa = attn_args(p, 0, q, k, v, kv_indices, prefix_indices, sm_scale, o, lse);
+  AttnArgs da = attn_args(p, 1, q, k, v, kv_indices, prefix_indices, sm_scale, o, lse);
+  wa.num_workers = p->hp.level[0].num_workers;
+  da.num_workers = p->hp.level[1].num_workers;
+  return launch_pod(wa, da, at<int32_t>(p, p->lay.meta), p->hp.desc.head_dim,
+                    p->hp.desc.kind == FI_KIND_CASCADE, s);
+}
+
 fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
   MergeArgs m;
   m.merges = at<int32_t>(p, p->lay.merges);
@@ -188,17 +201,13 @@ extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const vo
     st = hip_status(launch_scatter(sa, s), "scatter launch");
     if (st != FI_OK) return st;
   }
-  AttnArgs a = attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
   TimerScope t(s);
   if (p->hp.pod) {
-    // one launch of a fixed shape: every worker slot of both roles, whatever
-    // this batch's split
-    AttnArgs da = attn_args(p, 1, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
-    a.num_workers = p->hp.level[0].num_workers;
-    da.num_workers = p->hp.level[1].num_workers;
-    st = hip_status(launch_pod(a, da, at<int32_t>(p, p->lay.meta), d.head_dim, s),
+    st = hip_status(launch_fused(p, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse, s),
                     "attention launch");
   } else {
+    const AttnArgs a =
+        attn_args(p, 0, q, k_cache, v_cache, kv_indices, nullptr, sm_scale, o, lse);
     st = hip_status(launch_level(p, 0, a, s), "attention launch");
   }
   t.done();
@@ -221,7 +230,13 @@ extern "C" fi_status fi_cascade(const fi_plan_t* p, const void* q, const void* k
     return set_error(FI_ERR_INVALID_ARG, "fi_cascade: NULL prefix_indices");
   hipStream_t s = (hipStream_t)stream;
   TimerScope t(s);
-  for (int l = 0; l < 2; ++l) {
+  if (p->hp.pod) {
+    st = hip_status(launch_fused(p, q, k_cache, v_cache, kv_indices, prefix_indices, sm_scale,
+                                 o, lse, s),
+                    "attention launch");
+    if (st != FI_OK) return st;
+  }
+  for (int l = 0; l < 2 && !p->hp.pod; ++l) {
     const AttnArgs a =
         attn_args(p, l, q, k_cache, v_cache, kv_indices, prefix_indices, sm_scale, o, lse);
     st = hip_status(launch_level(p, l, a, s), "attention launch");

@@ -110,10 +110,11 @@ hipError_t launch_decode_fp8(const AttnArgs& a, int head_dim, hipStream_t stream
 // Wide level: one 4-wave workgroup per worker (a.num_workers workgroups);
 // list_q: query rows come through the member list (cascade prefix).
 hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream);
-// Fused mixed batch: wa.num_workers workgroups; workgroup b < meta[0] is wide
-// worker b, the others hold decode workers 4 (b - meta[0]) .. +3 of da.
+// Fused launch: wa.num_workers workgroups; workgroup b < meta[0] is wide
+// worker b, the others hold decode workers 4 (b - meta[0]) .. +3 of da;
+// list_q as for launch_wide.
 hipError_t launch_pod(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, int head_dim,
-                      hipStream_t stream);
+                      bool list_q, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream);

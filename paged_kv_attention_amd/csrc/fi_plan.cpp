@@ -269,6 +269,58 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
   }
 }
 
+// Fused launch (pod plans): the launch's P workgroups are split between the
+// wide role (level 0, one workgroup per worker) and the decode role (level 1,
+// four wavefront workers per workgroup) by estimated cost; each level is
+// planned over its share, then its worker list is padded with empty workers
+// to the whole launch (P and 4P), so the launch shape does not depend on the
+// batch.
+fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
+                     bool all_partial, int32_t& next_row, LevelBuild (&lb)[2], HostPlan& hp) {
+  const int32_t P = d.num_cus * std::max(1, d.workers_per_cu / 2);
+  const int64_t gp = std::max(1, 32 / d.page_size);
+  int64_t steps[2] = {0, 0};
+  for (int l = 0; l < 2; ++l)
+    for (const Unit& u : units[l]) steps[l] += ceil_div(u.n_pages, gp);
+  if (P < 2 && steps[0] > 0 && steps[1] > 0)
+    return set_error(FI_ERR_INVALID_ARG, "a fused launch needs at least 2 workgroups");
+  int32_t nw;
+  if (steps[1] == 0) {
+    nw = P;
+  } else if (steps[0] == 0) {
+    nw = 0;
+  } else if (d.pod_wide_blocks > 0) {
+    nw = std::min(d.pod_wide_blocks, P - 1);
+  } else {
+    // wide: kPodWideStep per workgroup step; decode: kPodDecodeStep per
+    // wavefront step, four wavefronts to a workgroup; rounded half up
+    const int64_t cw = kPodWideStep * steps[0], cd = kPodDecodeStep * steps[1];
+    nw = (int32_t)((2 * (int64_t)P * cw + (cw + cd)) / (2 * (cw + cd)));
+    nw = std::max(1, std::min(P - 1, nw));
+  }
+  hp.pod = true;
+  hp.pod_wide_blocks = nw;
+  hp.level[0].num_workers = nw;
+  hp.level[1].num_workers = WAVES_PER_BLOCK * (P - nw);
+  for (int l = 0; l < 2; ++l) {
+    if (hp.level[l].num_workers > 0) {
+      build_level(units[l], d, all_partial, next_row, lb[l], hp.level[l]);
+    } else {   // a role with no workgroups has no steps: every unit is empty
+      lb[l].items.clear();
+      lb[l].chunks.assign(units[l].size(), {0, {}});
+      hp.level[l].items.clear();
+      hp.level[l].chunk_pages = 0;
+      hp.level[l].worker_indptr.assign(1, 0);
+    }
+  }
+  hp.level[0].worker_indptr.resize((size_t)P + 1, hp.level[0].worker_indptr.back());
+  hp.level[1].worker_indptr.resize((size_t)WAVES_PER_BLOCK * P + 1,
+                                   hp.level[1].worker_indptr.back());
+  hp.level[0].num_workers = P;
+  hp.level[1].num_workers = WAVES_PER_BLOCK * P;
+  return FI_OK;
+}
+
 }  // namespace
 
 // Engine for decode-style levels when the caller leaves the choice open: the
@@ -307,8 +359,10 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.max_prefix_depth < 0) return set_error(FI_ERR_INVALID_ARG, "negative max_prefix_depth");
   if (d.max_prefix_depth == 0) d.max_prefix_depth = 1;
   if (d.pod_wide_blocks < 0) return set_error(FI_ERR_INVALID_ARG, "negative pod_wide_blocks");
-  d.pod = (d.kind == FI_KIND_APPEND && d.pod) ? 1 : 0;
+  d.pod = (d.kind != FI_KIND_DECODE && d.pod) ? 1 : 0;
   if (!d.pod) d.pod_wide_blocks = 0;
+  if (d.pod && din->decode_engine == FI_ENGINE_VALU)
+    return set_error(FI_ERR_UNSUPPORTED, "a fused launch runs its decode role on the matrix cores");
   if (d.det_chunk_pages == 0) d.det_chunk_pages = 64;
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
   if (d.workers_per_cu == 0) d.workers_per_cu = 4;
@@ -425,9 +479,17 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
     }
     std::vector<Unit> su;
     request_units(su, B, G, Hkv, ps, ROWS_DECODE, kv_indptr, kv_len, nullptr, false);
-    LevelBuild lbp, lbs;
-    build_level(pu, d, true, next_row, lbp, hp.level[0]);
-    build_level(su, d, true, next_row, lbs, hp.level[1]);
+    LevelBuild lbs2[2];
+    LevelBuild& lbp = lbs2[0];
+    LevelBuild& lbs = lbs2[1];
+    if (d.pod) {
+      const std::vector<Unit> both[2] = {pu, su};
+      st = pod_levels(d, both, true, next_row, lbs2, hp);
+      if (st != FI_OK) return st;
+    } else {
+      build_level(pu, d, true, next_row, lbp, hp.level[0]);
+      build_level(su, d, true, next_row, lbs, hp.level[1]);
+    }
     // prefix partial rows of (request, kv head)
     std::vector<std::vector<int32_t>> pref((size_t)B * Hkv);
     for (size_t ui = 0; ui < pu.size(); ++ui) {
@@ -460,55 +522,19 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
       // 0); the launch's P workgroups (as many as a wide level has) are split
       // between the roles by cost.
       hp.num_levels = 2;
-      hp.pod = true;
       wide_level(hp.level[0]);
       decode_level(hp.level[1]);
-      const int32_t P = d.num_cus * std::max(1, d.workers_per_cu / 2);
-      std::vector<uint8_t> small(B);
-      for (int32_t r = 0; r < B; ++r) small[r] = (int64_t)(qo_indptr[r + 1] - qo_indptr[r]) * G <= ROWS_DECODE;
-      std::vector<uint8_t> big(B);
-      for (int32_t r = 0; r < B; ++r) big[r] = !small[r];
+      std::vector<uint8_t> small(B), big(B);
+      for (int32_t r = 0; r < B; ++r) {
+        small[r] = (int64_t)(qo_indptr[r + 1] - qo_indptr[r]) * G <= ROWS_DECODE;
+        big[r] = !small[r];
+      }
       request_units(units[0], B, G, Hkv, ps, ROWS_WIDE, kv_indptr, kv_len, qo_indptr, causal,
                     big.data());
       request_units(units[1], B, G, Hkv, ps, ROWS_DECODE, kv_indptr, kv_len, qo_indptr, causal,
                     small.data());
-      const int64_t gp = std::max(1, 32 / ps);
-      int64_t steps[2] = {0, 0};
-      for (int l = 0; l < 2; ++l)
-        for (const Unit& u : units[l]) steps[l] += ceil_div(u.n_pages, gp);
-      int32_t nw;
-      if (steps[1] == 0) {
-        nw = P;
-      } else if (steps[0] == 0) {
-        nw = 0;
-      } else if (d.pod_wide_blocks > 0) {
-        nw = std::min(d.pod_wide_blocks, P - 1);
-      } else {
-        // wide: kPodWideStep per workgroup step; decode: kPodDecodeStep per
-        // wavefront step, four wavefronts to a workgroup; rounded half up
-        const int64_t cw = kPodWideStep * steps[0], cd = kPodDecodeStep * steps[1];
-        nw = (int32_t)((2 * (int64_t)P * cw + (cw + cd)) / (2 * (cw + cd)));
-        nw = std::max(1, std::min(P - 1, nw));
-      }
-      if (P < 2 && steps[0] > 0 && steps[1] > 0)
-        return set_error(FI_ERR_INVALID_ARG, "a fused mixed batch needs at least 2 workgroups");
-      hp.pod_wide_blocks = nw;
-      hp.level[0].num_workers = nw;
-      hp.level[1].num_workers = WAVES_PER_BLOCK * (P - nw);
-      for (int l = 0; l < 2; ++l) {
-        if (hp.level[l].num_workers > 0) {
-          build_level(units[l], d, false, next_row, lb[l], hp.level[l]);
-        } else {
-          hp.level[l].chunk_pages = 0;
-          hp.level[l].worker_indptr.assign(1, 0);
-        }
-      }
-      // every role sees the whole launch: workers past its share have no items
-      hp.level[0].worker_indptr.resize((size_t)P + 1, hp.level[0].worker_indptr.back());
-      hp.level[1].worker_indptr.resize((size_t)WAVES_PER_BLOCK * P + 1,
-                                       hp.level[1].worker_indptr.back());
-      hp.level[0].num_workers = P;
-      hp.level[1].num_workers = WAVES_PER_BLOCK * P;
+      st = pod_levels(d, units, false, next_row, lb, hp);
+      if (st != FI_OK) return st;
     } else {
       hp.num_levels = 1;
       if (append) wide_level(hp.level[0]); else decode_level(hp.level[0]);
@@ -594,9 +620,11 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
     const int64_t NG = d.num_prefix_groups;
     const int64_t blocks = ceil_div(B * G * d.max_prefix_depth, ROWS_WIDE) + NG;
     n_items[0] = (size_t)level_bound(S_wide, blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_WIDE);
-    n_items[1] = (size_t)level_bound(S_dec, B * Hkv, Hkv * max_kv_pages, ROWS_DECODE);
+    // a fused launch has 4 decode wavefronts on each of its S_wide workgroups
+    const int64_t S1 = d.pod ? WAVES_PER_BLOCK * S_wide : S_dec;
+    n_items[1] = (size_t)level_bound(S1, B * Hkv, Hkv * max_kv_pages, ROWS_DECODE);
     workers[0] = (int32_t)S_wide;
-    workers[1] = (int32_t)S_dec;
+    workers[1] = (int32_t)S1;
     merges = B * Hkv;
   } else if (d.kind == FI_KIND_APPEND && d.pod) {
     // wide role: at most P workgroups; decode role: at most 4P wavefronts

@@ -306,12 +306,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 // tiles, so a wavefront of either role needs at most half a SIMD's registers
 // and two workgroups share a CU: a CU holding one of each overlaps the matrix
 // work of the wide role with the HBM streaming of the decode role.
-template <int D, int NP>
+template <int D, int NP, bool LQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pod_kernel(
     AttnArgs wa, AttnArgs da, const int32_t* __restrict__ meta) {
   const int n_wide = ld_uniform(meta, 0);
   if ((int)blockIdx.x < n_wide) {
-    wide_worker<D, NP, false>(wa, blockIdx.x);
+    wide_worker<D, NP, LQ>(wa, blockIdx.x);
   } else {
     dec::decode_worker<D, NP, true, 2>(da, ((int)blockIdx.x - n_wide) * WAVES_PER_BLOCK +
                                       uniform(threadIdx.x >> 6));
@@ -330,15 +330,15 @@ hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool LQ>
 hipError_t launch_pod_d(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, dim3 grid,
                         hipStream_t s) {
   if (wa.page_size == 8) {
-    hipLaunchKernelGGL((pod_kernel<D, 4>), grid, dim3(256), 0, s, wa, da, meta);
+    hipLaunchKernelGGL((pod_kernel<D, 4, LQ>), grid, dim3(256), 0, s, wa, da, meta);
   } else if (wa.page_size == 16) {
-    hipLaunchKernelGGL((pod_kernel<D, 2>), grid, dim3(256), 0, s, wa, da, meta);
+    hipLaunchKernelGGL((pod_kernel<D, 2, LQ>), grid, dim3(256), 0, s, wa, da, meta);
   } else {
-    hipLaunchKernelGGL((pod_kernel<D, 1>), grid, dim3(256), 0, s, wa, da, meta);
+    hipLaunchKernelGGL((pod_kernel<D, 1, LQ>), grid, dim3(256), 0, s, wa, da, meta);
   }
   return hipGetLastError();
 }
@@ -346,11 +346,15 @@ hipError_t launch_pod_d(const AttnArgs& wa, const AttnArgs& da, const int32_t* m
 }  // namespace
 
 hipError_t launch_pod(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, int head_dim,
-                      hipStream_t stream) {
+                      bool list_q, hipStream_t stream) {
   if (wa.num_workers == 0) return hipSuccess;
   const dim3 grid(wa.num_workers);
-  if (head_dim == 128) return launch_pod_d<128>(wa, da, meta, grid, stream);
-  if (head_dim == 64) return launch_pod_d<64>(wa, da, meta, grid, stream);
+  if (head_dim == 128)
+    return list_q ? launch_pod_d<128, true>(wa, da, meta, grid, stream)
+                  : launch_pod_d<128, false>(wa, da, meta, grid, stream);
+  if (head_dim == 64)
+    return list_q ? launch_pod_d<64, true>(wa, da, meta, grid, stream)
+                  : launch_pod_d<64, false>(wa, da, meta, grid, stream);
   return hipErrorInvalidValue;
 }
 

@@ -170,8 +170,9 @@ def test_pod_plan_off_for_other_kinds_and_unfused_by_default():
                   pod=True, pod_wide_blocks=-1)
 
 
+@pytest.mark.parametrize("pod", [False, True])
 @pytest.mark.parametrize("det", [False, True])
-def test_cascade_plan_matches_reference(det):
+def test_cascade_plan_matches_reference(det, pod):
     rng = np.random.default_rng(11)
     ps = 16
     suf = list(rng.integers(0, 900, 30)) + [0]
@@ -180,11 +181,36 @@ def test_cascade_plan_matches_reference(det):
     indptr, L_ = _decode_host(suf, ps)
     pindptr, PL = _decode_host(pref, ps)
     p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
-                  req_prefix_group=groups, deterministic=det, num_cus=16, workers_per_cu=4)
+                  req_prefix_group=groups, deterministic=det, num_cus=16, workers_per_cu=4,
+                  pod=pod)
     info = p.info()
     ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info), deterministic=det,
-                   det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups)
+                   det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
+                   pod_blocks=32 if pod else None)
     compare(info, ref)
+    if pod:
+        assert [x["num_workers"] for x in info["levels"]] == [32, 128]
+        assert info["pod_wide_blocks"] == ref["pod_wide_blocks"] and \
+            1 <= info["pod_wide_blocks"] <= 31
+
+
+def test_fused_cascade_edge_splits():
+    """Fused cascade plans where one role has nothing to do: all suffixes
+    empty (the wide role takes the whole launch) and no prefixes."""
+    ps = 16
+    pindptr, PL = _decode_host([700], ps)
+    for suf, groups in (([0, 0, 0], [0, 0, 0]), ([100, 30, 0], [-1, -1, -1])):
+        indptr, L_ = _decode_host(suf, ps)
+        p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr,
+                      prefix_len=PL, req_prefix_group=groups, num_cus=4, pod=True)
+        info = p.info()
+        ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info),
+                       prefix_indptr=pindptr, prefix_len=PL, req_group=groups, pod_blocks=8)
+        compare(info, ref)
+        assert info["pod_wide_blocks"] == (8 if sum(suf) == 0 else 0)
+    with pytest.raises(fi.FIError):
+        host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
+                  req_prefix_group=groups, num_cus=4, pod=True, engine="valu")
 
 
 @pytest.mark.parametrize("det", [False, True])
@@ -234,7 +260,7 @@ def test_workspace_bound_covers_plans():
         B = int(rng.integers(1, 60))
         kind = ["decode", "append", "cascade"][trial % 3]
         det = bool(trial % 2)
-        pod = kind == "append" and trial % 4 == 1
+        pod = kind != "decode" and trial % 4 in (1, 2)
         lens = rng.integers(0, 5000, B)
         qo = np.minimum(lens, rng.integers(0, 100, B))
         if pod:   # mostly requests of one to four query tokens
@@ -256,6 +282,7 @@ def test_workspace_bound_covers_plans():
             if trial % 4 == 2:
                 kw.update(prefix_parent=[-1, 0])
                 depth = 2
+            kw.update(pod=pod)
             n_p = int(pi[-1])
         p = host_plan(kind, indptr, L_, 32, 8, 128, ps, **kw)
         info = p.info()

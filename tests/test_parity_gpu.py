@@ -85,13 +85,14 @@ def _oracle_cascade(w, reqs):
     return o, lse, a
 
 
-def test_cascade_config_sampled(dev):
+@pytest.mark.parametrize("pod", [False, True])
+def test_cascade_config_sampled(dev, pod):
     w = make_config(3, poison=True)
-    o, lse = _cascade_run(w, dev)
+    o, lse = _cascade_run(w, dev, pod=pod)
     rng = np.random.default_rng(3)
     reqs = sample_requests(w.batch, 8, rng)
     o_ref, l_ref, a_ref = _oracle_cascade(w, reqs)
-    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what="cascade")
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"cascade pod={pod}")
     # cascade equals flat decode over the concatenated table (both on the GPU)
     ip, ix, ln = cascade_flat_tables(w)
     p = fi.Plan("decode", ip, ln, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
@@ -196,9 +197,11 @@ def test_cascade_small_multi_group(dev):
     ps = 16
     w = make_cascade([64, 40, 0], [0, 1, 1, -1, 2, 0, 1, 0], [5, 0, 40, 33, 16, 1, 300, 17],
                      32, 8, 128, ps, seed=300)
-    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+    o_ref, l_ref, a_ref = _oracle_cascade(w, None)
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
+               dict(pod=True), dict(pod=True, deterministic=True, det_chunk_pages=1),
+               dict(pod=True, pod_wide_blocks=1), dict(pod=True, num_cus=2)]:
         o, lse = _cascade_run(w, dev, **kw)
-        o_ref, l_ref, a_ref = _oracle_cascade(w, None)
         compare(o, lse, o_ref, l_ref, a_ref, what=f"cascade groups {kw}")
 
 
@@ -459,11 +462,12 @@ def _capture(fn):
     return graph
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 4, "pod"])
+@pytest.mark.parametrize("cfg", [1, 3, 4, "pod", "cascade_pod"])
 def test_graph_replay_matches_eager(dev, cfg):
     """A captured run call (no allocation, no memset inside) replays to the
     eager bits, replay after replay, with other eager work in between."""
-    w = make_pod_mix(poison=False) if cfg == "pod" else make_config(cfg, poison=False)
+    w = (make_pod_mix(poison=False) if cfg == "pod" else
+         make_config(3 if cfg == "cascade_pod" else cfg, poison=False))
     g = w.to(dev)
     T = g.q.shape[0]
     out = torch.empty_like(g.q)
@@ -476,7 +480,8 @@ def test_graph_replay_matches_eager(dev, cfg):
     elif w.kind == "cascade":
         p = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                     w.head_dim, w.page_size, prefix_indptr=w.prefix_indptr,
-                    prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group, device=dev)
+                    prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group, device=dev,
+                    pod=cfg == "cascade_pod")
         call = lambda o, l: fi.cascade(p, g.q, g.k_cache, g.v_cache, g.prefix_indices,  # noqa
                                        g.kv_indices, w.sm_scale, out=o, lse=l)
     else:
@@ -571,9 +576,10 @@ def test_cascade_tree(dev, det):
     suf = [int(x) for x in rng.integers(0, 700, B)]
     w = make_cascade(pref, groups, suf, 32, 8, 128, 16, seed=32, poison=True,
                      prefix_parent=parent)
-    o, lse = _cascade_run(w, dev, deterministic=det)
     o_ref, l_ref, a_ref = _oracle_cascade(w, None)
-    compare(o, lse, o_ref, l_ref, a_ref, what=f"cascade tree det={det}")
+    for pod in (False, True):
+        o, lse = _cascade_run(w, dev, deterministic=det, pod=pod)
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"cascade tree det={det} pod={pod}")
     # the same batch as plain decode over the flattened tables (GPU vs GPU)
     ip, ix, ln = cascade_flat_tables(w)
     p = fi.Plan("decode", ip, ln, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
