@@ -212,7 +212,7 @@ def explore(args, dev):
         plan = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, prefix_indptr=w.prefix_indptr,
                        prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group,
-                       device=dev, pod=args.pod, pod_wide_blocks=args.pod_wide_blocks, **kw)
+                       device=dev, launch=args.launch, pod_wide_blocks=args.pod_wide_blocks, **kw)
         call = lambda: fi.cascade(plan, g.q, g.k_cache, g.v_cache, g.prefix_indices,  # noqa
                                   g.kv_indices, w.sm_scale)
         per_req = w.kv_len.long() + w.prefix_len[0].long()
@@ -220,7 +220,7 @@ def explore(args, dev):
     else:
         plan = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, qo_indptr=w.qo_indptr, causal=True,
-                       device=dev, pod=args.pod, pod_wide_blocks=args.pod_wide_blocks, **kw)
+                       device=dev, launch=args.launch, pod_wide_blocks=args.pod_wide_blocks, **kw)
         call = lambda: fi.paged_append(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
                                        w.sm_scale, k_new=g.k_new, v_new=g.v_new)
         qo = (w.qo_indptr[1:] - w.qo_indptr[:-1]).long()
@@ -244,7 +244,7 @@ def explore(args, dev):
     kv = w.kv_bytes_fp8() if args.kv == "fp8" else w.kv_bytes()
     extra = {}
     if w.kind != "decode":
-        extra = {"pod": bool(args.pod), "pod_wide_blocks": plan.info()["pod_wide_blocks"]}
+        extra = {"launch": args.launch, "pod_wide_blocks": plan.info()["pod_wide_blocks"]}
     print(json.dumps({"workload": name, "mode": args.mode,
                       "engine": args.engine, "kv": args.kv, **extra,
                       "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
@@ -277,10 +277,11 @@ def main():
     ap.add_argument("--pod-mix", action="store_true",
                     help="exploratory line on the chunked-prefill mixed batch (64 decode "
                          "requests beside two 512-token prefill chunks)")
-    ap.add_argument("--pod", action="store_true",
-                    help="append and cascade workloads: plan one fused launch for both roles")
+    ap.add_argument("--launch", choices=("default", "pod", "separate"), default="default",
+                    help="append and cascade workloads: one POD launch for both kinds of rows, "
+                         "or one launch per kind")
     ap.add_argument("--pod-wide-blocks", type=int, default=0,
-                    help="with --pod: workgroups of the wide role (0 = the plan's choice)")
+                    help="POD launch: workgroups of the wide role (0 = the plan's choice)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:

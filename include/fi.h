@@ -80,6 +80,17 @@ typedef enum fi_engine {
   FI_ENGINE_VALU = 2     /* vector ALU only, v_dot2_f32_bf16; head group <= 8     */
 } fi_engine;
 
+/* How a plan with two kinds of rows is launched: append plans (multi-query
+ * requests and requests of a few query tokens) and cascade plans (shared
+ * prefixes and per-request suffixes). POD attention (research note,
+ * "Arithmetic intensity": prefill and decode rows of one batch in one
+ * kernel) runs both kinds in one launch whose workgroups share every CU. */
+typedef enum fi_launch {
+  FI_LAUNCH_DEFAULT = 0,  /* POD, except with the VALU decode engine          */
+  FI_LAUNCH_POD = 1,      /* one fused launch (matrix-core engine only)       */
+  FI_LAUNCH_SEPARATE = 2  /* one launch per kind of rows                      */
+} fi_launch;
+
 /* Plan description. Zero in an optional field selects its default. */
 typedef struct fi_plan_desc {
   int32_t kind;              /* fi_kind                                        */
@@ -99,9 +110,9 @@ typedef struct fi_plan_desc {
   int32_t max_prefix_depth;  /* cascade: longest chain of nested shared prefixes
                                 a request may have (default 1; bounds the
                                 workspace and is checked by fi_plan)          */
-  int32_t pod;               /* append: 1 = fused mixed batch (see below)      */
-  int32_t pod_wide_blocks;   /* pod: workgroups given to the multi-query
-                                requests (0 = sized by the plan's cost model) */
+  int32_t launch;            /* fi_launch, append and cascade (default 0)      */
+  int32_t pod_wide_blocks;   /* POD launch: workgroups of the wide role (0 =
+                                sized by the plan's cost model)              */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;
@@ -132,7 +143,7 @@ typedef struct fi_plan_info {
   int32_t num_scatter;
   size_t dev_bytes_used;
   size_t host_bytes_used;
-  int32_t pod_wide_blocks;       /* pod plans: workgroups of the wide role (the
+  int32_t pod_wide_blocks;       /* POD plans: workgroups of the wide role (the
                                     rest run the decode role), else 0 */
 } fi_plan_info;
 
@@ -216,16 +227,15 @@ fi_status fi_paged_decode_fp8(const fi_plan_t* plan, const void* q, const void* 
  * kv_len-qo .. kv_len-1 of each request); then query i of request r (global
  * row qo_indptr[r]+i) attends to keys 0..kv_len-qo+i (causal plan) or to all
  * kv_len keys. Both or neither of k_new/v_new.
- * Fused mixed batch (desc.pod = 1; research note, "Arithmetic intensity":
- * POD attention runs the prefill and the decode rows of one batch in one
- * kernel): a request whose query rows (qo * Hq/Hkv) fit one 16-row block runs
- * in the decode role (one wavefront per worker, K/V streamed through
- * registers), every other request in the wide role (a workgroup sharing K/V
- * through LDS); one launch of num_cus * max(1, workers_per_cu / 2)
- * workgroups (two per CU by default, so both roles share every CU) covers
- * both, the plan giving pod_wide_blocks of them to the wide role by estimated
- * cost.
- * Same results as the unfused plan, up to rounding. */
+ * POD launch (the default): a request whose query rows (qo * Hq/Hkv) fit one
+ * 16-row block runs in the decode role (one wavefront per worker, K/V
+ * streamed through registers), every other request in the wide role (a
+ * workgroup sharing K/V through LDS); one launch of
+ * num_cus * max(1, workers_per_cu / 2) workgroups (two per CU by default, so
+ * both roles share every CU) covers both, the plan giving pod_wide_blocks of
+ * them to the wide role by estimated cost. FI_LAUNCH_SEPARATE runs every
+ * request on the wide kernel instead. Same results either way, up to
+ * rounding. */
 fi_status fi_paged_append(const fi_plan_t* plan, const void* q, const void* k_new,
                           const void* v_new, void* k_cache, void* v_cache,
                           const int32_t* kv_indices, float sm_scale, void* o,
@@ -236,7 +246,10 @@ fi_status fi_paged_append(const fi_plan_t* plan, const void* q, const void* k_ne
  * FI_KIND_CASCADE. Level 0 attends all member queries of a group to the
  * group's prefix pages (prefix_indices), level 1 each request to its own
  * suffix (kv_indices); the two states are merged prefix first. The result is
- * attention over prefix || suffix. */
+ * attention over prefix || suffix. By default (FI_LAUNCH_POD) both levels run
+ * in one launch, the prefix level as the wide role and the suffix level as
+ * the decode role, so the prefix's matrix work and the suffixes' HBM reads
+ * overlap on every CU; FI_LAUNCH_SEPARATE runs them one after the other. */
 fi_status fi_cascade(const fi_plan_t* plan, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* prefix_indices,
                      const int32_t* kv_indices, float sm_scale, void* o, float* lse,

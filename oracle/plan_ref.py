@@ -53,10 +53,14 @@ be compared with it element for element:
    128-row units). The launch has P workgroups; with W_w and W_d the two
    roles' steps (as in 3), the wide role gets n_w = P if there are no decode
    steps, 0 if there are no wide steps, else the override if one is given
-   (capped at P - 1), else round-half-up(P * c_w / (c_w + c_d)) clamped to
-   [1, P - 1], with c_w = 2 W_w and c_d = W_d (a wide workgroup step takes
-   about twice as long as a decode wavefront step; four of those run side by
-   side in a decode workgroup). Each role is planned as in
+   (capped at P - 1), else the n in [1, P - 1] that minimises, in order,
+   max(T_w, T_d), then T_w, then n. With c_w = max(m_w, ceil(W_w / n)) and
+   c_d = max(m_d, ceil(W_d / (4 (P - n)))) the two roles' quotas under rule 3
+   (m: a role's minimum chunk in steps), T_d = 7 c_d and T_w = 4 (c_w + 2 k),
+   k the most items any wide quota holds (1 + the unit ends strictly inside
+   it): a decode wavefront step takes about 7/4 of a wide workgroup step when
+   the two roles share the chip, and a wide item costs about two steps to
+   start. Each role is planned as in
    3-4 over its own workers (n_w workgroups; 4 (P - n_w) wavefronts), then
    its worker list is padded with empty workers to P (wide) and 4P (decode).
    Partial rows are allocated wide role first; merges likewise. A cascade
@@ -69,8 +73,9 @@ from __future__ import annotations
 import heapq
 
 NO_SPLIT_STEPS = 12  # balanced mode keeps units whole if splitting saves fewer steps
-POD_WIDE_STEP = 2    # fused mixed batch: time of a wide workgroup step ...
-POD_DECODE_STEP = 1  # ... and of a decode wavefront step
+POD_WIDE_STEP = 4        # fused launch: time of a wide workgroup step ...
+POD_DECODE_STEP = 7      # ... and of a decode wavefront step
+POD_WIDE_ITEM_STEPS = 2  # starting a wide item, in wide steps
 POD_DECODE_ROWS = 16  # query rows of a request that runs in the decode role
 FLAG_LIST_Q = 1     # query rows come from the member list (cascade prefix)
 FLAG_PARTIAL = 2    # write fp32 partial rows instead of final rows
@@ -241,8 +246,25 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
         elif pod_wide_blocks > 0:
             n_w = min(int(pod_wide_blocks), P - 1)
         else:
-            cw, cd = POD_WIDE_STEP * w_steps[0], POD_DECODE_STEP * w_steps[1]
-            n_w = max(1, min(P - 1, (2 * P * cw + cw + cd) // (2 * (cw + cd))))
+            cmin = [max(1, _ceil_div(int(m), gp)) for m in min_chunk]
+            ends, acc = [], 0
+            for u in levels_units[0]:
+                ns = _ceil_div(u["n_pages"], gp)
+                if ns > 0:
+                    acc += ns
+                    ends.append(acc)
+
+            def busiest(c):
+                # items of the quota holding most unit ends strictly inside it
+                inside = [e // c for e in ends[:-1] if e % c]
+                return 1 + max((inside.count(q) for q in set(inside)), default=0)
+
+            def cost(n):
+                cw = max(cmin[0], _ceil_div(w_steps[0], n))
+                tw = POD_WIDE_STEP * (cw + POD_WIDE_ITEM_STEPS * busiest(cw))
+                td = POD_DECODE_STEP * max(cmin[1], _ceil_div(w_steps[1], 4 * (P - n)))
+                return (max(tw, td), tw, n)
+            n_w = min(range(1, P), key=cost)
         workers = [n_w, 4 * (P - n_w)]
 
     all_partial = kind == "cascade"

@@ -14,6 +14,7 @@ FI_OK, FI_ERR_INVALID_ARG, FI_ERR_UNSUPPORTED, FI_ERR_WORKSPACE, FI_ERR_PLAN_MIS
 FI_KIND_DECODE, FI_KIND_APPEND, FI_KIND_CASCADE = range(3)
 FI_DTYPE_BF16, FI_DTYPE_F32 = 0, 1
 FI_ENGINE_DEFAULT, FI_ENGINE_MFMA, FI_ENGINE_VALU = range(3)
+FI_LAUNCH_DEFAULT, FI_LAUNCH_POD, FI_LAUNCH_SEPARATE = range(3)
 FI_ITEM_INTS, FI_MERGE_INTS = 12, 5
 
 STATUS_NAMES = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
@@ -24,7 +25,7 @@ class PlanDesc(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "kind", "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "causal",
         "deterministic", "det_chunk_pages", "min_chunk_pages", "num_cus", "workers_per_cu",
-        "num_prefix_groups", "decode_engine", "max_prefix_depth", "pod", "pod_wide_blocks")]
+        "num_prefix_groups", "decode_engine", "max_prefix_depth", "launch", "pod_wide_blocks")]
 
 
 I32P = POINTER(c_int32)

@@ -18,6 +18,8 @@ from . import _lib as L
 
 _KINDS = {"decode": L.FI_KIND_DECODE, "append": L.FI_KIND_APPEND, "cascade": L.FI_KIND_CASCADE}
 _ENGINES = {"default": L.FI_ENGINE_DEFAULT, "mfma": L.FI_ENGINE_MFMA, "valu": L.FI_ENGINE_VALU}
+_LAUNCHES = {"default": L.FI_LAUNCH_DEFAULT, "pod": L.FI_LAUNCH_POD,
+             "separate": L.FI_LAUNCH_SEPARATE}
 
 
 def _host_i32(x) -> Optional[np.ndarray]:
@@ -81,7 +83,7 @@ class Plan:
                  prefix_indptr=None, prefix_len=None, req_prefix_group=None, prefix_parent=None,
                  deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
                  num_cus: int = 0, workers_per_cu: int = 0, engine: str = "default",
-                 pod: bool = False, pod_wide_blocks: int = 0, device="cuda",
+                 launch: str = "default", pod_wide_blocks: int = 0, device="cuda",
                  workspace: Optional[Workspace] = None):
         lib = L.load()
         self.kind = kind
@@ -100,7 +102,7 @@ class Plan:
                                num_cus=num_cus, workers_per_cu=workers_per_cu,
                                num_prefix_groups=ng, decode_engine=_ENGINES[engine],
                                max_prefix_depth=_prefix_depth(self._ha["prefix_parent"], ng),
-                               pod=int(pod), pod_wide_blocks=pod_wide_blocks)
+                               launch=_LAUNCHES[launch], pod_wide_blocks=pod_wide_blocks)
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim, self.page_size, self.batch = head_dim, page_size, B
         self.device = None if device is None else torch.device(device)

@@ -155,11 +155,13 @@ struct LevelBuild {
 
 // Balanced mode keeps every unit whole when a split would save fewer steps.
 constexpr int64_t kNoSplitSteps = 12;
-// Fused mixed batch: relative time of a wide-role workgroup step (up to 128
-// rows through MFMA) and of a decode-role wavefront step (a workgroup runs
-// four such wavefronts side by side).
-constexpr int64_t kPodWideStep = 2;
-constexpr int64_t kPodDecodeStep = 1;
+// Fused launch: relative time of a wide-role workgroup step (up to 128 rows
+// through MFMA) and of a decode-role wavefront step, with the two roles
+// sharing the chip (a decode workgroup runs four wavefronts side by side),
+// and the start of a wide item counted in wide steps.
+constexpr int64_t kPodWideStep = 4;
+constexpr int64_t kPodDecodeStep = 7;
+constexpr int64_t kPodWideItemSteps = 2;
 
 void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all_partial,
                  int32_t& next_row, LevelBuild& lb, Level& lv) {
@@ -292,11 +294,47 @@ fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
   } else if (d.pod_wide_blocks > 0) {
     nw = std::min(d.pod_wide_blocks, P - 1);
   } else {
-    // wide: kPodWideStep per workgroup step; decode: kPodDecodeStep per
-    // wavefront step, four wavefronts to a workgroup; rounded half up
-    const int64_t cw = kPodWideStep * steps[0], cd = kPodDecodeStep * steps[1];
-    nw = (int32_t)((2 * (int64_t)P * cw + (cw + cd)) / (2 * (cw + cd)));
-    nw = std::max(1, std::min(P - 1, nw));
+    // The split whose slower role finishes first. A role's time is its step
+    // cost times its quota c of steps (as build_level cuts it), plus for the
+    // wide role kPodWideItemSteps per item of its busiest quota (a unit
+    // boundary inside a quota adds an item). Ties go to the faster wide
+    // role, then to fewer wide workgroups.
+    const int64_t cmin[2] = {std::max<int64_t>(1, ceil_div(hp.level[0].min_chunk_pages, gp)),
+                             std::max<int64_t>(1, ceil_div(hp.level[1].min_chunk_pages, gp))};
+    std::vector<int64_t> bounds;   // wide unit ends on the steps laid end to end
+    for (const Unit& u : units[0]) {
+      const int64_t ns = ceil_div(u.n_pages, gp);
+      if (ns > 0) bounds.push_back((bounds.empty() ? 0 : bounds.back()) + ns);
+    }
+    std::map<int64_t, int64_t> items_at;   // quota c -> items of the busiest quota
+    auto max_items = [&](int64_t c) {
+      auto f = items_at.find(c);
+      if (f != items_at.end()) return f->second;
+      int64_t best = 1, run = 1, q = -1;
+      for (size_t i = 0; i + 1 < bounds.size(); ++i) {
+        if (bounds[i] % c == 0) continue;
+        const int64_t qi = bounds[i] / c;
+        run = (qi == q) ? run + 1 : 2;
+        q = qi;
+        best = std::max(best, run);
+      }
+      items_at[c] = best;
+      return best;
+    };
+    int64_t best_t = -1, best_w = 0;
+    nw = 1;
+    for (int32_t n = 1; n < P; ++n) {
+      const int64_t cw = std::max(cmin[0], ceil_div(steps[0], n));
+      const int64_t tw = kPodWideStep * (cw + kPodWideItemSteps * max_items(cw));
+      const int64_t td =
+          kPodDecodeStep * std::max(cmin[1], ceil_div(steps[1], (int64_t)WAVES_PER_BLOCK * (P - n)));
+      const int64_t t = std::max(tw, td);
+      if (best_t < 0 || t < best_t || (t == best_t && tw < best_w)) {
+        best_t = t;
+        best_w = tw;
+        nw = n;
+      }
+    }
   }
   hp.pod = true;
   hp.pod_wide_blocks = nw;
@@ -359,10 +397,18 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.max_prefix_depth < 0) return set_error(FI_ERR_INVALID_ARG, "negative max_prefix_depth");
   if (d.max_prefix_depth == 0) d.max_prefix_depth = 1;
   if (d.pod_wide_blocks < 0) return set_error(FI_ERR_INVALID_ARG, "negative pod_wide_blocks");
-  d.pod = (d.kind != FI_KIND_DECODE && d.pod) ? 1 : 0;
-  if (!d.pod) d.pod_wide_blocks = 0;
-  if (d.pod && din->decode_engine == FI_ENGINE_VALU)
-    return set_error(FI_ERR_UNSUPPORTED, "a fused launch runs its decode role on the matrix cores");
+  if (d.launch < FI_LAUNCH_DEFAULT || d.launch > FI_LAUNCH_SEPARATE)
+    return set_error(FI_ERR_INVALID_ARG, "launch %d", d.launch);
+  if (d.kind == FI_KIND_DECODE) {
+    d.launch = FI_LAUNCH_SEPARATE;
+  } else if (d.decode_engine == FI_ENGINE_VALU) {
+    if (d.launch == FI_LAUNCH_POD)
+      return set_error(FI_ERR_UNSUPPORTED, "a POD launch runs its decode role on the matrix cores");
+    d.launch = FI_LAUNCH_SEPARATE;
+  } else if (d.launch == FI_LAUNCH_DEFAULT) {
+    d.launch = FI_LAUNCH_POD;   // measured faster on the cascade and mixed batches
+  }
+  if (d.launch != FI_LAUNCH_POD) d.pod_wide_blocks = 0;
   if (d.det_chunk_pages == 0) d.det_chunk_pages = 64;
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
   if (d.workers_per_cu == 0) d.workers_per_cu = 4;
@@ -482,7 +528,7 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
     LevelBuild lbs2[2];
     LevelBuild& lbp = lbs2[0];
     LevelBuild& lbs = lbs2[1];
-    if (d.pod) {
+    if (d.launch == FI_LAUNCH_POD) {
       const std::vector<Unit> both[2] = {pu, su};
       st = pod_levels(d, both, true, next_row, lbs2, hp);
       if (st != FI_OK) return st;
@@ -516,7 +562,7 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
     const bool causal = append && d.causal;
     std::vector<Unit> units[2];
     LevelBuild lb[2];
-    if (append && d.pod) {
+    if (append && d.launch == FI_LAUNCH_POD) {
       // Fused mixed batch: requests whose query rows fit one decode row block
       // go to the decode role (level 1), the others to the wide role (level
       // 0); the launch's P workgroups (as many as a wide level has) are split
@@ -621,12 +667,12 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
     const int64_t blocks = ceil_div(B * G * d.max_prefix_depth, ROWS_WIDE) + NG;
     n_items[0] = (size_t)level_bound(S_wide, blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_WIDE);
     // a fused launch has 4 decode wavefronts on each of its S_wide workgroups
-    const int64_t S1 = d.pod ? WAVES_PER_BLOCK * S_wide : S_dec;
+    const int64_t S1 = d.launch == FI_LAUNCH_POD ? WAVES_PER_BLOCK * S_wide : S_dec;
     n_items[1] = (size_t)level_bound(S1, B * Hkv, Hkv * max_kv_pages, ROWS_DECODE);
     workers[0] = (int32_t)S_wide;
     workers[1] = (int32_t)S1;
     merges = B * Hkv;
-  } else if (d.kind == FI_KIND_APPEND && d.pod) {
+  } else if (d.kind == FI_KIND_APPEND && d.launch == FI_LAUNCH_POD) {
     // wide role: at most P workgroups; decode role: at most 4P wavefronts
     const int64_t P = S_wide;
     const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;

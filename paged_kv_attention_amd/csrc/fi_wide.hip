@@ -36,6 +36,7 @@ namespace {
 using namespace dev;
 
 constexpr int kStages = 3;
+constexpr int kAhead = kStages - 1;   // steps in flight ahead of the computed one
 constexpr int kRowsPerWave = 32;   // two 16-row MFMA blocks
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
@@ -46,6 +47,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until at most k steps' copies (NKS per step) of this wave are
+// outstanding, k in [0, kAhead - 1].
+template <int NKS>
+__device__ __forceinline__ void wait_steps(int k) {
+  static_assert(kAhead <= 4, "wait_steps covers up to three outstanding steps");
+  if (k >= 3) wait_vmcnt<3 * NKS>();
+  else if (k == 2) wait_vmcnt<2 * NKS>();
+  else if (k == 1) wait_vmcnt<NKS>();
+  else wait_vmcnt<0>();
 }
 
 template <int D>
@@ -123,7 +135,7 @@ __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, in
   }
 }
 
-// One step of a workgroup item: copy step s+2 into `next` (if any), then, for
+// One step of a workgroup item: copy step s+kAhead into `next` (if any), then, for
 // s >= 0, read step s's K/V fragments from `cur` and compute. Every copy of the
 // item goes through this one call site and the two stage pointers are
 // __restrict__: the compiler then knows the copies into `next` cannot alias
@@ -136,7 +148,7 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
                                           int rl0, int wave, int lane) {
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL, CH = Cfg<D>::CH, ROW = Lds<D>::ROW;
   const int col = lane & 15, grp = lane >> 4;
-  if (issue) issue_step<D, NP>(a, it, s + 2, next, wave, lane);
+  if (issue) issue_step<D, NP>(a, it, s + kAhead, next, wave, lane);
   // row blocks of this wave that hold real rows (0, 1 or 2): a wave or block
   // of padding rows only takes part in the copies and barriers
   const int nmb = min(2, max(0, (it.n_rows - rl0 + 15) >> 4));
@@ -265,27 +277,31 @@ __device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
     State<D, 2> st;
     st.reset();
     const int n = it.nsteps;
-    // Step s lives in stage s mod 3; the loop is unrolled by the three stages
+    // Step s lives in stage s mod kStages; the loop is unrolled by the stages
     // so every stage address is a compile-time offset of `lds`.
     auto body = [&](int s, char* next, const char* cur) -> bool {
       if (s >= n) return false;
       if (s >= 0) {
-        // this wave's copies of step s are done when at most those of step s+1
-        // are outstanding; the barrier then publishes every wave's copies, and
-        // tells every wave that step s-1's stage (which step s+2 reuses) has
-        // been read by all
-        if (s + 1 < n) wait_vmcnt<2 * NK>(); else wait_vmcnt<0>();
+        // this wave's copies of step s are done when at most those of the
+        // steps after it are outstanding; the barrier then publishes every
+        // wave's copies, and tells every wave that step s-1's stage (which
+        // step s+kAhead reuses) has been read by all
+        wait_steps<2 * NK>(min(kAhead - 1, n - 1 - s));
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
-      wide_step<D, NP>(a, it, s, s + 2 < n, next, cur, qf, st, rl0, wave, lane);
+      wide_step<D, NP>(a, it, s, s + kAhead < n, next, cur, qf, st, rl0, wave, lane);
       return true;
     };
     constexpr int SB = Lds<D>::STAGE;
-    for (int s = -2;; s += 3) {   // stages of s, s+1, s+2: 1, 2, 0
-      if (!body(s, lds + 0 * SB, lds + 1 * SB)) break;
-      if (!body(s + 1, lds + 1 * SB, lds + 2 * SB)) break;
-      if (!body(s + 2, lds + 2 * SB, lds + 0 * SB)) break;
+    // from s = -kAhead (= 1 mod kStages), body j computes stage (1+j) mod
+    // kStages and fills stage j
+    bool more = true;
+    for (int s = -kAhead; more; s += kStages) {
+#pragma unroll
+      for (int j = 0; j < kStages; ++j) {
+        if (more) more = body(s + j, lds + j * SB, lds + ((1 + j) % kStages) * SB);
+      }
     }
     finalize_wide<D, LQ>(a, it, st, rl0, col, grp);
     __builtin_amdgcn_s_barrier();   // every wave is done with the stages

@@ -93,7 +93,8 @@ def test_append_plan_matches_reference(causal, det):
     indptr, L_ = _decode_host(lens, ps)
     qo_indptr = _indptr(qo)
     p = host_plan("append", indptr, L_, 32, 8, 128, ps, qo_indptr=qo_indptr, causal=causal,
-                  deterministic=det, det_chunk_pages=8, num_cus=4, workers_per_cu=8)
+                  deterministic=det, det_chunk_pages=8, num_cus=4, workers_per_cu=8,
+                  launch="separate")
     info = p.info()
     assert info["levels"][0]["rows_per_block"] == 128 and info["levels"][0]["num_workers"] == 16
     ref = plan_ref("append", 32, 8, ps, indptr, L_, **level_params(info),
@@ -123,7 +124,7 @@ def test_pod_plan_matches_reference(causal, det, mix, force):
     ps, Hq, Hkv = 16, 32, 8
     indptr, L_, qo_indptr, qo = _pod_batch(rng, mix[0], mix[1], ps, Hq // Hkv)
     p = host_plan("append", indptr, L_, Hq, Hkv, 128, ps, qo_indptr=qo_indptr, causal=causal,
-                  deterministic=det, det_chunk_pages=8, num_cus=6, workers_per_cu=8, pod=True,
+                  deterministic=det, det_chunk_pages=8, num_cus=6, workers_per_cu=8, launch="pod",
                   pod_wide_blocks=force)
     info = p.info()
     P = 6 * (8 // 2)     # two workgroups per CU per two workers
@@ -157,17 +158,29 @@ def test_pod_plan_matches_reference(causal, det, mix, force):
     assert info["num_scatter"] == int(qo.sum())
 
 
-def test_pod_plan_off_for_other_kinds_and_unfused_by_default():
+def test_launch_defaults():
+    """POD by default for append and cascade; decode plans ignore the field;
+    the VALU decode engine runs separate launches."""
     rng = np.random.default_rng(3)
     indptr, L_, qo_indptr, qo = _pod_batch(rng, 8, 2, 16, 4)
-    p = host_plan("append", indptr, L_, 32, 8, 128, 16, qo_indptr=qo_indptr, num_cus=4)
+    kw = dict(qo_indptr=qo_indptr, num_cus=4)
+    p = host_plan("append", indptr, L_, 32, 8, 128, 16, **kw)
+    q = host_plan("append", indptr, L_, 32, 8, 128, 16, launch="pod", **kw)
+    compare(p.info(), dict(levels=[dict(items=x["items"], worker_indptr=x["worker_indptr"])
+                                   for x in q.info()["levels"]],
+                           merges=q.info()["merges"], parts=q.info()["parts"],
+                           qlist=q.info()["qlist"], n_part_rows=q.info()["num_part_rows"]))
+    assert p.info()["pod_wide_blocks"] == q.info()["pod_wide_blocks"] > 0
+    p = host_plan("append", indptr, L_, 32, 8, 128, 16, launch="separate", **kw)
+    assert len(p.info()["levels"]) == 1 and p.info()["pod_wide_blocks"] == 0
+    p = host_plan("append", indptr, L_, 32, 8, 128, 16, engine="valu", **kw)
     assert len(p.info()["levels"]) == 1 and p.info()["pod_wide_blocks"] == 0
     d_indptr, d_len = _decode_host([100, 200], 16)
-    p = host_plan("decode", d_indptr, d_len, 32, 8, 128, 16, num_cus=4, pod=True)
+    p = host_plan("decode", d_indptr, d_len, 32, 8, 128, 16, num_cus=4, launch="pod")
     assert len(p.info()["levels"]) == 1 and p.info()["pod_wide_blocks"] == 0
     with pytest.raises(fi.FIError):
         host_plan("append", indptr, L_, 32, 8, 128, 16, qo_indptr=qo_indptr, num_cus=4,
-                  pod=True, pod_wide_blocks=-1)
+                  launch="pod", pod_wide_blocks=-1)
 
 
 @pytest.mark.parametrize("pod", [False, True])
@@ -182,7 +195,7 @@ def test_cascade_plan_matches_reference(det, pod):
     pindptr, PL = _decode_host(pref, ps)
     p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
                   req_prefix_group=groups, deterministic=det, num_cus=16, workers_per_cu=4,
-                  pod=pod)
+                  launch="pod" if pod else "separate")
     info = p.info()
     ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info), deterministic=det,
                    det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
@@ -202,7 +215,7 @@ def test_fused_cascade_edge_splits():
     for suf, groups in (([0, 0, 0], [0, 0, 0]), ([100, 30, 0], [-1, -1, -1])):
         indptr, L_ = _decode_host(suf, ps)
         p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr,
-                      prefix_len=PL, req_prefix_group=groups, num_cus=4, pod=True)
+                      prefix_len=PL, req_prefix_group=groups, num_cus=4, launch="pod")
         info = p.info()
         ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info),
                        prefix_indptr=pindptr, prefix_len=PL, req_group=groups, pod_blocks=8)
@@ -210,7 +223,7 @@ def test_fused_cascade_edge_splits():
         assert info["pod_wide_blocks"] == (8 if sum(suf) == 0 else 0)
     with pytest.raises(fi.FIError):
         host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
-                  req_prefix_group=groups, num_cus=4, pod=True, engine="valu")
+                  req_prefix_group=groups, num_cus=4, launch="pod", engine="valu")
 
 
 @pytest.mark.parametrize("det", [False, True])
@@ -227,7 +240,7 @@ def test_cascade_tree_plan_matches_reference(det):
     pindptr, PL = _decode_host(pref, ps)
     p = host_plan("cascade", indptr, L_, 32, 8, 128, ps, prefix_indptr=pindptr, prefix_len=PL,
                   req_prefix_group=groups, prefix_parent=parent, deterministic=det, num_cus=16,
-                  workers_per_cu=4)
+                  workers_per_cu=4, launch="separate")
     info = p.info()
     ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info), deterministic=det,
                    det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
@@ -271,7 +284,7 @@ def test_workspace_bound_covers_plans():
         n_q = 0
         n_p = 0
         if kind == "append":
-            kw.update(qo_indptr=_indptr(qo), causal=True, pod=pod)
+            kw.update(qo_indptr=_indptr(qo), causal=True, launch="pod" if pod else "separate")
             n_q = int(qo.sum())
         depth = 1
         if kind == "cascade":
@@ -282,7 +295,7 @@ def test_workspace_bound_covers_plans():
             if trial % 4 == 2:
                 kw.update(prefix_parent=[-1, 0])
                 depth = 2
-            kw.update(pod=pod)
+            kw.update(launch="pod" if pod else "separate")
             n_p = int(pi[-1])
         p = host_plan(kind, indptr, L_, 32, 8, 128, ps, **kw)
         info = p.info()
@@ -291,7 +304,7 @@ def test_workspace_bound_covers_plans():
                           causal=1, deterministic=int(det), det_chunk_pages=kw["det_chunk_pages"],
                           num_cus=9, workers_per_cu=3,
                           num_prefix_groups=2 if kind == "cascade" else 0,
-                          max_prefix_depth=depth, pod=int(pod))
+                          max_prefix_depth=depth, launch=1 if pod else 2)
         assert len(info["levels"]) == (2 if pod or kind == "cascade" else 1)
         dev, host = fi.Workspace.bound(desc, int(indptr[-1]), n_q, n_p)
         assert dev >= info["dev_bytes_used"], (trial, kind)

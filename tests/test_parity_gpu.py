@@ -85,14 +85,14 @@ def _oracle_cascade(w, reqs):
     return o, lse, a
 
 
-@pytest.mark.parametrize("pod", [False, True])
-def test_cascade_config_sampled(dev, pod):
+@pytest.mark.parametrize("launch", ["pod", "separate"])
+def test_cascade_config_sampled(dev, launch):
     w = make_config(3, poison=True)
-    o, lse = _cascade_run(w, dev, pod=pod)
+    o, lse = _cascade_run(w, dev, launch=launch)
     rng = np.random.default_rng(3)
     reqs = sample_requests(w.batch, 8, rng)
     o_ref, l_ref, a_ref = _oracle_cascade(w, reqs)
-    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"cascade pod={pod}")
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"cascade {launch}")
     # cascade equals flat decode over the concatenated table (both on the GPU)
     ip, ix, ln = cascade_flat_tables(w)
     p = fi.Plan("decode", ip, ln, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
@@ -103,10 +103,11 @@ def test_cascade_config_sampled(dev, pod):
             what="flat decode of cascade input")
 
 
-def test_append_config_sampled(dev):
+@pytest.mark.parametrize("launch", ["pod", "separate"])
+def test_append_config_sampled(dev, launch):
     w = make_config(4, poison=True)
     p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev)
+                w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev, launch=launch)
     g = w.to(dev)
     o, lse = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale,
                              k_new=g.k_new, v_new=g.v_new)
@@ -122,7 +123,7 @@ def test_append_config_sampled(dev):
     reqs = sample_requests(w.batch, 4, rng, must=[int(torch.argmax(w.qo_indptr.diff()))])
     o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, True, reqs)
     rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in reqs])
-    compare(o, lse, o_ref, l_ref, a_ref, rows=rows, what="append")
+    compare(o, lse, o_ref, l_ref, a_ref, rows=rows, what=f"append {launch}")
 
 
 def _oracle_append(w, kp2, vp2, causal, reqs=None):
@@ -182,7 +183,9 @@ def test_append_small_sweep(dev, causal, D, ps, G):
                                      w.qo_indptr.numpy(), w.kv_indptr.numpy(),
                                      w.kv_indices.numpy(), w.kv_len.numpy(), ps)
     o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, causal)
-    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
+               dict(launch="separate"),
+               dict(launch="separate", deterministic=True, det_chunk_pages=1)]:
         g = w.to(dev)
         p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, Hkv, D, ps,
                     qo_indptr=w.qo_indptr, causal=causal, device=dev, **kw)
@@ -199,8 +202,9 @@ def test_cascade_small_multi_group(dev):
                      32, 8, 128, ps, seed=300)
     o_ref, l_ref, a_ref = _oracle_cascade(w, None)
     for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
-               dict(pod=True), dict(pod=True, deterministic=True, det_chunk_pages=1),
-               dict(pod=True, pod_wide_blocks=1), dict(pod=True, num_cus=2)]:
+               dict(launch="separate"),
+               dict(launch="separate", deterministic=True, det_chunk_pages=1),
+               dict(pod_wide_blocks=1), dict(num_cus=2)]:
         o, lse = _cascade_run(w, dev, **kw)
         compare(o, lse, o_ref, l_ref, a_ref, what=f"cascade groups {kw}")
 
@@ -405,7 +409,7 @@ def test_pod_small_sweep(dev, causal, D, ps, G):
     o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, causal)
     for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
                dict(pod_wide_blocks=1), dict(num_cus=3)]:
-        o, lse, p = _append_run(w, dev, causal, pod=True, **kw)
+        o, lse, p = _append_run(w, dev, causal, launch="pod", **kw)
         info = p.info()
         assert len(info["levels"][1]["items"]) > 0
         compare(o, lse, o_ref, l_ref, a_ref,
@@ -419,7 +423,7 @@ def test_pod_mixed_sampled(dev, det):
     both roles against the oracle, and the whole batch against the unfused
     plan."""
     w = make_pod_mix(poison=True)
-    o, lse, p = _append_run(w, dev, pod=True, deterministic=det)
+    o, lse, p = _append_run(w, dev, launch="pod", deterministic=det)
     info = p.info()
     assert 1 <= info["pod_wide_blocks"] < info["levels"][0]["num_workers"]
     qo = w.qo_indptr.diff()
@@ -431,7 +435,7 @@ def test_pod_mixed_sampled(dev, det):
     o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, True, reqs)
     rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in reqs])
     compare(o, lse, o_ref, l_ref, a_ref, rows=rows, what=f"pod mixed det={det}")
-    o2, lse2, _ = _append_run(w, dev, deterministic=det)
+    o2, lse2, _ = _append_run(w, dev, launch="separate", deterministic=det)
     assert float((o2.float() - o.float()).abs().max()) <= 2e-2
     assert float(((lse2 - lse).abs() / lse.abs().clamp(min=1)).max()) <= 2e-3
 
@@ -440,7 +444,7 @@ def test_pod_deterministic_bits_independent_of_split(dev):
     """Deterministic mode: a request's bits do not depend on how the launch
     is split between the roles."""
     w = make_pod_mix(poison=False, n_decode=24, n_prefill=1, prefill_q=200)
-    outs = [_append_run(w, dev, pod=True, deterministic=True, det_chunk_pages=8,
+    outs = [_append_run(w, dev, launch="pod", deterministic=True, det_chunk_pages=8,
                         pod_wide_blocks=nw)[:2] for nw in (0, 3, 100)]
     for o, lse in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
@@ -481,13 +485,13 @@ def test_graph_replay_matches_eager(dev, cfg):
         p = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                     w.head_dim, w.page_size, prefix_indptr=w.prefix_indptr,
                     prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group, device=dev,
-                    pod=cfg == "cascade_pod")
+                    launch="pod" if cfg == "cascade_pod" else "separate")
         call = lambda o, l: fi.cascade(p, g.q, g.k_cache, g.v_cache, g.prefix_indices,  # noqa
                                        g.kv_indices, w.sm_scale, out=o, lse=l)
     else:
         p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                     w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev,
-                    pod=cfg == "pod")
+                    launch="pod" if cfg == "pod" else "separate")
         call = lambda o, l: fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
                                             w.sm_scale, k_new=g.k_new, v_new=g.v_new, out=o,
                                             lse=l)
@@ -578,7 +582,8 @@ def test_cascade_tree(dev, det):
                      prefix_parent=parent)
     o_ref, l_ref, a_ref = _oracle_cascade(w, None)
     for pod in (False, True):
-        o, lse = _cascade_run(w, dev, deterministic=det, pod=pod)
+        o, lse = _cascade_run(w, dev, deterministic=det,
+                              launch="pod" if pod else "separate")
         compare(o, lse, o_ref, l_ref, a_ref, what=f"cascade tree det={det} pod={pod}")
     # the same batch as plain decode over the flattened tables (GPU vs GPU)
     ip, ix, ln = cascade_flat_tables(w)
