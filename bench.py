@@ -103,6 +103,35 @@ def _pct(xs, q):
     return xs[min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))]
 
 
+def cold_us_per_call(step, dev, n=50):
+    """Time of one call with nothing of its inputs cached: reading 1 GiB
+    between calls evicts L2 and the 256 MB Infinity Cache (a read, so no
+    dirty lines are left to be written back during the call); the scrub's own
+    time is measured alone and subtracted. A serving step reads each layer's
+    KV once, so this is the time a model sees; the plain loop re-reads the
+    same KV and can hit the Infinity Cache when it fits."""
+    import torch
+    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def loop(with_call):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            torch.sum(scrub, dim=0, out=sink)
+            if with_call:
+                step()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+    loop(True)
+    both = [loop(True) for _ in range(3)]
+    alone = [loop(False) for _ in range(3)]
+    del scrub
+    return round(min(both) - min(alone), 2)
+
+
 def measure_variants(args, w, g, plan, step, dev):
     """Context for the main number, measured after the timed region:
     HIP-graph replays, cold-cache calls, and the deterministic-mode plan."""
@@ -137,29 +166,8 @@ def measure_variants(args, w, g, plan, step, dev):
                               "p10": round(_pct(samples, 0.1), 2),
                               "p90": round(_pct(samples, 0.9), 2)}
     del graph
-    # (2) cold cache: reading 1 GiB between calls evicts L2 and the 256 MB
-    # Infinity Cache (a read, so no dirty lines are left to be written back
-    # during the call); the scrub's own time is measured alone and subtracted
-    scrub = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    sink = torch.empty((), dtype=torch.float32, device=dev)
-    n = 50
-
-    def loop(with_call):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(n):
-            torch.sum(scrub, dim=0, out=sink)
-            if with_call:
-                step()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n
-    loop(True)
-    both = [loop(True) for _ in range(3)]
-    alone = [loop(False) for _ in range(3)]
-    res["cold_us_per_call"] = round(min(both) - min(alone), 2)
-    del scrub
+    # (2) cold cache
+    res["cold_us_per_call"] = cold_us_per_call(step, dev)
     # (3) deterministic-mode plan (chunks fixed per request) on the same batch
     dplan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                     w.page_size, device=dev, deterministic=True, engine=args.engine)
@@ -241,6 +249,7 @@ def explore(args, dev):
             call()
         torch.cuda.synchronize()
     kern_ms = kt.total_ms / max(1, kt.calls)
+    cold_us = cold_us_per_call(call, dev)
     kv = w.kv_bytes_fp8() if args.kv == "fp8" else w.kv_bytes()
     extra = {}
     if w.kind != "decode":
@@ -248,6 +257,7 @@ def explore(args, dev):
     print(json.dumps({"workload": name, "mode": args.mode,
                       "engine": args.engine, "kv": args.kv, **extra,
                       "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
+                      "cold_us_per_call": cold_us,
                       "kv_bytes": kv, "kv_GBps": round(kv / ms / 1e6, 1),
                       "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
                       "flops": flops, "TFLOPs": round(flops / ms / 1e9, 1),

@@ -56,11 +56,11 @@ be compared with it element for element:
    (capped at P - 1), else the n in [1, P - 1] that minimises, in order,
    max(T_w, T_d), then T_w, then n. With c_w = max(m_w, ceil(W_w / n)) and
    c_d = max(m_d, ceil(W_d / (4 (P - n)))) the two roles' quotas under rule 3
-   (m: a role's minimum chunk in steps), T_d = 7 c_d and T_w = 4 (c_w + 2 k),
+   (m: a role's minimum chunk in steps), T_d = 9 c_d and T_w = 4 (c_w + 2 k),
    k the most items any wide quota holds (1 + the unit ends strictly inside
-   it): a decode wavefront step takes about 7/4 of a wide workgroup step when
-   the two roles share the chip, and a wide item costs about two steps to
-   start. Each role is planned as in
+   it): a decode wavefront step takes about 9/4 of a wide workgroup step when
+   the two roles share the chip and the KV comes from HBM, and a wide item
+   costs about two steps to start. Each role is planned as in
    3-4 over its own workers (n_w workgroups; 4 (P - n_w) wavefronts), then
    its worker list is padded with empty workers to P (wide) and 4P (decode).
    Partial rows are allocated wide role first; merges likewise. A cascade
@@ -74,7 +74,7 @@ import heapq
 
 NO_SPLIT_STEPS = 12  # balanced mode keeps units whole if splitting saves fewer steps
 POD_WIDE_STEP = 4        # fused launch: time of a wide workgroup step ...
-POD_DECODE_STEP = 7      # ... and of a decode wavefront step
+POD_DECODE_STEP = 9      # ... and of a decode wavefront step
 POD_WIDE_ITEM_STEPS = 2  # starting a wide item, in wide steps
 POD_DECODE_ROWS = 16  # query rows of a request that runs in the decode role
 FLAG_LIST_Q = 1     # query rows come from the member list (cascade prefix)

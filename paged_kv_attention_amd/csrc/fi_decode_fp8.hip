@@ -122,7 +122,8 @@ __device__ __forceinline__ void issue_step8(const AttnArgs& a, const Item& it, i
     }
     const uint32_t off = (uint32_t)(slot * D + grp * (D / 4));
 #pragma unroll
-    for (int i = 0; i < KV4; ++i) T.k[blk][i] = *(const u32x4*)(base + off + 16u * i);
+    for (int i = 0; i < KV4; ++i)   // K and V are read once: nontemporal loads
+      T.k[blk][i] = __builtin_nontemporal_load((const u32x4*)(base + off + 16u * i));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {   // V: tokens 4*grp + i and 16 + 4*grp + (i - 4)
@@ -139,7 +140,7 @@ __device__ __forceinline__ void issue_step8(const AttnArgs& a, const Item& it, i
       base = (grp >> 1) ? vb[2 * (i >> 2) + 1] : vb[2 * (i >> 2)];
       slot = tl & 7;
     }
-    T.v[i] = *(const vraw_t*)(base + (uint32_t)(slot * D + DPL * col));
+    T.v[i] = __builtin_nontemporal_load((const vraw_t*)(base + (uint32_t)(slot * D + DPL * col)));
   }
 }
 

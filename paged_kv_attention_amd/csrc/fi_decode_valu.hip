@@ -96,8 +96,8 @@ __device__ __forceinline__ void issue_step_v(const AttnArgs& a, const Item& it, 
     const int n = (NP == 1) ? 0 : (TPI * i) / kPS;
     const int slot = slot0 + ((NP == 1) ? TPI * i : (TPI * i) % kPS) + grp;
     const uint32_t off = (uint32_t)(slot * D + 8 * c) * 2u;
-    T.k[i] = *(const u32x4*)(kb[n] + off);
-    T.v[i] = *(const u32x4*)(vb[n] + off);
+    T.k[i] = __builtin_nontemporal_load((const u32x4*)(kb[n] + off));   // read once: nontemporal
+    T.v[i] = __builtin_nontemporal_load((const u32x4*)(vb[n] + off));
   }
 }
 

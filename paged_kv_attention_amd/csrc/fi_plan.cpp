@@ -157,10 +157,10 @@ struct LevelBuild {
 constexpr int64_t kNoSplitSteps = 12;
 // Fused launch: relative time of a wide-role workgroup step (up to 128 rows
 // through MFMA) and of a decode-role wavefront step, with the two roles
-// sharing the chip (a decode workgroup runs four wavefronts side by side),
-// and the start of a wide item counted in wide steps.
+// sharing the chip and the KV coming from HBM (a decode workgroup runs four
+// wavefronts side by side), and the start of a wide item in wide steps.
 constexpr int64_t kPodWideStep = 4;
-constexpr int64_t kPodDecodeStep = 7;
+constexpr int64_t kPodDecodeStep = 9;
 constexpr int64_t kPodWideItemSteps = 2;
 
 void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all_partial,
