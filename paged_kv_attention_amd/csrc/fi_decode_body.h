@@ -156,8 +156,11 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
     if constexpr (QT) {
       if (valid && is == 0) load_q_rows<D, 1, false>(a, iitem, 0, Y.q, col, grp);
     }
-    // past the end of the stream: an in-bounds re-load of the current step
-    issue_tile<D, NP, QT>(a, valid ? iitem : citem, valid ? is : cs, Y, col, grp);
+    // past the end of the stream: an in-bounds re-load of the current step,
+    // every lane at lane 0's addresses (one line per load, so the extra
+    // loads of the ring's last steps add next to no HBM traffic)
+    issue_tile<D, NP, QT>(a, valid ? iitem : citem, valid ? is : cs, Y, valid ? col : 0,
+                          valid ? grp : 0);
     if (valid && ++is >= iitem.nsteps) {
       ++ii;
       is = 0;

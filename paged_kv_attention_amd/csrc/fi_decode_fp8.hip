@@ -281,8 +281,10 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(AttnArgs a) {
   auto issue = [&](Tile8<D>& Y) {
     const bool valid = ii < i_end;
     if (valid && is == 0) load_q8<D>(a, iitem, Y.q, col, grp);
-    // past the end of the stream: an in-bounds re-load of the current step
-    issue_step8<D, NP>(a, valid ? iitem : citem, valid ? is : cs, Y, col, grp);
+    // past the end of the stream: an in-bounds re-load of the current step,
+    // every lane at lane 0's addresses (next to no HBM traffic)
+    issue_step8<D, NP>(a, valid ? iitem : citem, valid ? is : cs, Y, valid ? col : 0,
+                       valid ? grp : 0);
     if (valid && ++is >= iitem.nsteps) {
       ++ii;
       is = 0;

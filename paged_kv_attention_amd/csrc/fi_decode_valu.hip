@@ -277,8 +277,10 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(AttnArgs a) {
   auto issue = [&](VTile<D, GM>& Y) {
     const bool valid = ii < i_end;
     if (valid && is == 0) load_q_v<D, GM>(a, iitem, Y.q, c);
-    // past the end of the stream: an in-bounds re-load of the current step
-    issue_step_v<D, NP, GM>(a, valid ? iitem : citem, valid ? is : cs, Y, c, grp);
+    // past the end of the stream: an in-bounds re-load of the current step,
+    // every lane at lane 0's addresses (next to no HBM traffic)
+    issue_step_v<D, NP, GM>(a, valid ? iitem : citem, valid ? is : cs, Y, valid ? c : 0,
+                            valid ? grp : 0);
     if (valid && ++is >= iitem.nsteps) {
       ++ii;
       is = 0;
