@@ -170,7 +170,8 @@ def measure_variants(args, w, g, plan, step, dev):
     res["cold_us_per_call"] = cold_us_per_call(step, dev)
     # (3) deterministic-mode plan (chunks fixed per request) on the same batch
     dplan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                    w.page_size, device=dev, deterministic=True, engine=args.engine)
+                    w.page_size, device=dev, deterministic=True, engine=args.engine,
+                    det_chunk_pages=args.det_chunk_pages)
     out = torch.empty_like(g.q)
 
     def dstep():
@@ -205,7 +206,8 @@ def explore(args, dev):
         w = to_fp8_cache(w, poison=False)
     g = w.to(dev)
     kw = dict(deterministic=args.mode == "deterministic", workers_per_cu=args.workers_per_cu,
-              min_chunk_pages=args.min_chunk_pages, engine=args.engine)
+              min_chunk_pages=args.min_chunk_pages, det_chunk_pages=args.det_chunk_pages,
+              engine=args.engine)
     if w.kind == "decode":
         plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, device=dev, **kw)
@@ -249,7 +251,7 @@ def explore(args, dev):
             call()
         torch.cuda.synchronize()
     kern_ms = kt.total_ms / max(1, kt.calls)
-    cold_us = cold_us_per_call(call, dev)
+    cold_us = cold_us_per_call(call, dev) if args.variants else None
     kv = w.kv_bytes_fp8() if args.kv == "fp8" else w.kv_bytes()
     extra = {}
     if w.kind != "decode":
@@ -272,6 +274,8 @@ def main():
     ap.add_argument("--mode", choices=("balanced", "deterministic"), default="balanced")
     ap.add_argument("--workers-per-cu", type=int, default=0)
     ap.add_argument("--min-chunk-pages", type=int, default=0)
+    ap.add_argument("--det-chunk-pages", type=int, default=0,
+                    help="deterministic mode: chunk size in pages (0 = the library default)")
     ap.add_argument("--engine", choices=("default", "mfma", "valu"), default="default",
                     help="units for the decode-style levels")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -281,7 +285,8 @@ def main():
     ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
                     help="KV cache format for the exploratory decode lines (--config)")
     ap.add_argument("--no-variants", dest="variants", action="store_false",
-                    help="skip the graph-replay, cold-cache and deterministic-mode context")
+                    help="skip the graph-replay, cold-cache and deterministic-mode context "
+                         "(exploratory lines: the cold-cache time)")
     ap.add_argument("--config", type=int, default=CONFIG_INDEX,
                     help="other configurations print an exploratory line (not the bench line)")
     ap.add_argument("--pod-mix", action="store_true",
@@ -315,7 +320,7 @@ def main():
 
     plan_kw = dict(deterministic=args.mode == "deterministic",
                    workers_per_cu=args.workers_per_cu, min_chunk_pages=args.min_chunk_pages,
-                   engine=args.engine)
+                   det_chunk_pages=args.det_chunk_pages, engine=args.engine)
     t0 = time.perf_counter()
     plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                    w.page_size, device=dev, **plan_kw)

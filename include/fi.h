@@ -101,7 +101,7 @@ typedef struct fi_plan_desc {
   int32_t page_size;         /* tokens per page: power of two in [8, 256]      */
   int32_t causal;            /* append: 1 = bottom-right causal mask           */
   int32_t deterministic;     /* 1 = chunk boundaries depend on the request only */
-  int32_t det_chunk_pages;   /* deterministic chunk size in pages (default 64) */
+  int32_t det_chunk_pages;   /* deterministic chunk size in pages (default 48) */
   int32_t min_chunk_pages;   /* balanced mode lower bound on chunk pages (default 8) */
   int32_t num_cus;           /* compute units to plan for (0 = current device) */
   int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 4) */

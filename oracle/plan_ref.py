@@ -144,7 +144,7 @@ def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_p
 
 
 def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
-             num_workers, rows_per_block, deterministic=False, det_chunk_pages=64,
+             num_workers, rows_per_block, deterministic=False, det_chunk_pages=48,
              min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
              prefix_len=None, req_group=None, prefix_parent=None, pod_blocks=None,
              pod_wide_blocks=0):

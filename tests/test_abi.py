@@ -198,7 +198,7 @@ def test_cascade_plan_matches_reference(det, pod):
                   launch="pod" if pod else "separate")
     info = p.info()
     ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info), deterministic=det,
-                   det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
+                   det_chunk_pages=48, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
                    pod_blocks=32 if pod else None)
     compare(info, ref)
     if pod:
@@ -243,7 +243,7 @@ def test_cascade_tree_plan_matches_reference(det):
                   workers_per_cu=4, launch="separate")
     info = p.info()
     ref = plan_ref("cascade", 32, 8, ps, indptr, L_, **level_params(info), deterministic=det,
-                   det_chunk_pages=64, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
+                   det_chunk_pages=48, prefix_indptr=pindptr, prefix_len=PL, req_group=groups,
                    prefix_parent=parent)
     compare(info, ref)
     # a request of group 3 merges the prefixes of 0, 1, 3 (root first), then its suffix
