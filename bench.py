@@ -197,6 +197,9 @@ def explore(args, dev):
     from workloads import CONFIG_NAMES, POD_MIX_NAME, make_config, make_pod_mix
     if args.pod_mix:
         w, name = make_pod_mix(poison=False), POD_MIX_NAME
+    elif args.sparse_video:
+        from workloads import SPARSE_VIDEO_NAME, make_sparse_video
+        w, name = make_sparse_video(poison=False), SPARSE_VIDEO_NAME
     else:
         w, name = make_config(args.config, poison=False), CONFIG_NAMES[args.config]
     if args.kv == "fp8":
@@ -227,6 +230,19 @@ def explore(args, dev):
                                   g.kv_indices, w.sm_scale)
         per_req = w.kv_len.long() + w.prefix_len[0].long()
         flops = 4 * w.head_dim * w.num_qo_heads * int(per_req.sum())
+    elif w.kind == "block_sparse":
+        plan = fi.BlockSparsePlan(w.q.shape[0], int(w.kv_len[0]), w.row_block_sz,
+                                  w.col_block_sz, w.block_mask, w.kv_indices, w.num_qo_heads,
+                                  w.num_kv_heads, w.head_dim, w.page_size, device=dev,
+                                  launch=args.launch, pod_wide_blocks=args.pod_wide_blocks,
+                                  **{k: v for k, v in kw.items() if k != "engine"})
+        call = lambda: fi.block_sparse_attention(plan, g.q, g.k_cache, g.v_cache,  # noqa
+                                                 w.sm_scale)
+        # attended (query, key) pairs, every q head: 4 D flops each
+        G = w.num_qo_heads // w.num_kv_heads
+        pairs = (w.block_mask.double() * w.row_block_sz[:, :, None].double()
+                 * w.col_block_sz[:, None, :].double()).sum()
+        flops = int(4 * w.head_dim * G * float(pairs))
     else:
         plan = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, qo_indptr=w.qo_indptr, causal=True,
@@ -292,6 +308,9 @@ def main():
     ap.add_argument("--pod-mix", action="store_true",
                     help="exploratory line on the chunked-prefill mixed batch (64 decode "
                          "requests beside two 512-token prefill chunks)")
+    ap.add_argument("--sparse-video", action="store_true",
+                    help="exploratory line on the video-shaped variable block-sparse "
+                         "self-attention (8192 tokens, 16 heads, 64 blocks per head)")
     ap.add_argument("--launch", choices=("default", "pod", "separate"), default="default",
                     help="append and cascade workloads: one POD launch for both kinds of rows, "
                          "or one launch per kind")
@@ -310,7 +329,7 @@ def main():
 
     dev = torch.device("cuda:0")
     fi.load()
-    if args.config != CONFIG_INDEX or args.kv != "bf16" or args.pod_mix:
+    if args.config != CONFIG_INDEX or args.kv != "bf16" or args.pod_mix or args.sparse_video:
         explore(args, dev)
         return
     print(f"bench: generating {CONFIG_NAMES[CONFIG_INDEX]}", file=sys.stderr, flush=True)

@@ -64,7 +64,8 @@ typedef enum fi_status {
 typedef enum fi_kind {
   FI_KIND_DECODE = 0,   /* one query token per request                      */
   FI_KIND_APPEND = 1,   /* qo_r query tokens per request, optional causal   */
-  FI_KIND_CASCADE = 2   /* decode over (shared prefix) || (own suffix)      */
+  FI_KIND_CASCADE = 2,  /* decode over (shared prefix) || (own suffix)      */
+  FI_KIND_BLOCK_SPARSE = 3  /* one sequence, a block mask per kv head (below) */
 } fi_kind;
 
 typedef enum fi_dtype { FI_DTYPE_BF16 = 0, FI_DTYPE_F32 = 1 } fi_dtype;
@@ -145,6 +146,8 @@ typedef struct fi_plan_info {
   size_t host_bytes_used;
   int32_t pod_wide_blocks;       /* POD plans: workgroups of the wide role (the
                                     rest run the decode role), else 0 */
+  int32_t num_plist;             /* block-sparse plans: the page lists the plan */
+  const int32_t* plist;          /* built (items' page offsets index it)        */
 } fi_plan_info;
 
 /* Upper bound on the device and pinned-host workspace bytes of any plan with
@@ -240,6 +243,45 @@ fi_status fi_paged_append(const fi_plan_t* plan, const void* q, const void* k_ne
                           const void* v_new, void* k_cache, void* v_cache,
                           const int32_t* kv_indices, float sm_scale, void* o,
                           float* lse, void* stream);
+
+/* Variable block-sparse attention over one sequence (research note,
+ * "Arithmetic intensity": block-sparse and variable block-sparse plans; Ye et
+ * al. record, "summary": composable block-sparse KV representations). For kv
+ * head g, the qo_len query tokens are cut into num_row_blocks row blocks of
+ * sizes row_block_sz[g][a] (host int32 [Hkv][num_row_blocks], each row sums
+ * to qo_len) and the kv_len keys into num_col_blocks column blocks of sizes
+ * col_block_sz[g][b] (host int32 [Hkv][num_col_blocks], each row sums to
+ * kv_len, every non-empty block starting on a page boundary, so only the
+ * sequence's last block may end inside a page); block_mask (host uint8 [Hkv][num_row_blocks]
+ * [num_col_blocks], nonzero = attend) says which column blocks the rows of a
+ * row block see. Query i of q head h (kv head g = h / (Hq/Hkv)) attends to
+ * the keys of the selected column blocks of its row block, no causal mask; a
+ * row with no selected key gets o = 0, lse = -inf. Block sizes may differ per
+ * kv head and per block; zero-size blocks are allowed. The sequence's keys
+ * are token t in page seq_pages_h[t / page_size] (host int32,
+ * ceil(kv_len / page_size) page ids), slot t % page_size, of the usual pools.
+ * Plan kind FI_KIND_BLOCK_SPARSE (desc.batch is ignored, desc.causal must be
+ * 0): every (kv head, row block) becomes a unit over the page list of its
+ * selected column blocks, stored in the plan's workspace, and is planned and
+ * launched like an append batch (POD launch by default). Workspace bound from
+ * fi_workspace_size_block_sparse. Errors as fi_plan, FI_ERR_INVALID_ARG for
+ * sizes that do not add up or blocks off page boundaries. */
+fi_status fi_workspace_size_block_sparse(const fi_plan_desc* desc, int32_t qo_len,
+                                         int32_t kv_len, int32_t num_row_blocks,
+                                         int32_t num_col_blocks, size_t* dev_bytes,
+                                         size_t* host_bytes);
+fi_status fi_plan_block_sparse(const fi_plan_desc* desc, int32_t qo_len, int32_t kv_len,
+                               int32_t num_row_blocks, const int32_t* row_block_sz_h,
+                               int32_t num_col_blocks, const int32_t* col_block_sz_h,
+                               const uint8_t* block_mask_h, const int32_t* seq_pages_h,
+                               void* ws_dev, size_t ws_dev_bytes, void* ws_host,
+                               size_t ws_host_bytes, void* stream, fi_plan_t** out);
+/* Run a block-sparse plan: q [qo_len][Hq][D] bf16 -> o [qo_len][Hq][D] bf16,
+ * lse [qo_len][Hq] fp32 (NULL to skip); k_cache, v_cache the pools the plan's
+ * seq_pages index. The page lists come from the plan's workspace. */
+fi_status fi_block_sparse_attention(const fi_plan_t* plan, const void* q, const void* k_cache,
+                                    const void* v_cache, float sm_scale, void* o, float* lse,
+                                    void* stream);
 
 /* Cascade decode (research note, "Arithmetic intensity": a shared prefix's KV
  * is read once and reused by every request that shares it). Plan kind

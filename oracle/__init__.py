@@ -37,6 +37,7 @@ from .attention import (  # noqa: F401
     paged_decode_fp8,
     e4m3_values,
     paged_append,
+    block_sparse,
     scatter_new_kv,
     merge_states,
     merge_two,

@@ -194,6 +194,49 @@ def paged_append(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
     return o, lse
 
 
+def block_sparse(q, k_pool, v_pool, seq_pages, kv_len: int, page_size: int, row_sz, col_sz,
+                 mask, sm_scale: float, rows=None):
+    """Variable block-sparse attention of one sequence (research note,
+    *Arithmetic intensity*: block-sparse and variable block-sparse plans; Ye
+    et al. record, *summary*: composable block-sparse KV representations).
+
+    For kv head g the ``qo_len`` queries are cut into consecutive row blocks
+    of sizes ``row_sz[g]`` and the ``kv_len`` keys into consecutive column
+    blocks of sizes ``col_sz[g]``; query i sees key t iff ``mask[g][a][b]``
+    for the row block a holding i and the column block b holding t. Each q
+    head h uses the partition and mask of its kv head h // (Hq/Hkv). No causal
+    mask; a row that sees no key gets o = 0, lse = -inf. ``q [qo_len, Hq, D]``;
+    keys are gathered through ``seq_pages``. Returns ``o [qo_len, Hq, D]``,
+    ``lse [qo_len, Hq]``; with ``rows`` (query indices) only those rows are
+    computed and the others are NaN. Pinned by: brute force over explicit
+    per-row key lists on tiny inputs, the all-ones mask equal to unmasked
+    attention, a block-diagonal mask equal to independent attention per
+    block (torch SDPA), and rows with no selected block.
+    """
+    T, Hq, D = q.shape
+    Hkv = k_pool.shape[1]
+    G = Hq // Hkv
+    sel = np.arange(T) if rows is None else np.asarray(sorted(rows), dtype=np.int64)
+    o = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    for g in range(Hkv):
+        K = gather_tokens(k_pool, seq_pages, 0, kv_len, page_size, g)
+        V = gather_tokens(v_pool, seq_pages, 0, kv_len, page_size, g)
+        rs = np.asarray(row_sz[g], dtype=np.int64)
+        cs = np.asarray(col_sz[g], dtype=np.int64)
+        assert rs.sum() == T and cs.sum() == kv_len, "blocks must cover the sequence"
+        row_block = np.repeat(np.arange(rs.size), rs)          # query -> its row block
+        col_block = np.repeat(np.arange(cs.size), cs)          # key -> its column block
+        m = np.asarray(mask[g], dtype=bool)
+        vis_tok = m[row_block[sel][:, None], col_block[None, :]]    # [rows, kv_len]
+        hs = _heads_of(g, G)
+        qr = np.asarray(q[sel][:, hs], dtype=np.float64).reshape(sel.size * G, D)
+        ob, lb = attend(qr, K, V, sm_scale, np.repeat(vis_tok, G, axis=0))
+        o[sel, hs] = ob.reshape(sel.size, G, D)
+        lse[sel, hs] = lb.reshape(sel.size, G)
+    return o, lse
+
+
 def scatter_new_kv(k_pool, v_pool, k_new, v_new, qo_indptr, kv_indptr, kv_indices,
                    kv_len, page_size: int):
     """Copies of the pools with the new tokens' K/V written into their slots.

@@ -66,6 +66,16 @@ be compared with it element for element:
    Partial rows are allocated wide role first; merges likewise. A cascade
    plan may be fused the same way: its prefix level is the wide role and its
    suffix level the decode role, split by the same rule.
+7. Variable block-sparse (one sequence; research note *Arithmetic intensity*:
+   block-sparse and variable block-sparse plans). For kv head g and row
+   block a (rows = a's query tokens times G), the page list is the pages of
+   a's selected non-empty column blocks in column order (a block of c keys
+   starting at key c0 covers pages c0/ps .. ceil((c0+c)/ps)-1 of the
+   sequence), appended to ``plist``; t_lim = the selected keys. Units are
+   enumerated g, a, row block (128 rows; in a POD plan a row block of at most
+   16 rows is one decode-role unit), with q_base = a's first query token and
+   page_off = the list's offset; no causal mask. Levels, merges (a unit with
+   no keys gets empty records: o = 0, lse = -inf) as in 3-6.
 """
 
 from __future__ import annotations
@@ -147,7 +157,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
              num_workers, rows_per_block, deterministic=False, det_chunk_pages=48,
              min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
              prefix_len=None, req_group=None, prefix_parent=None, pod_blocks=None,
-             pod_wide_blocks=0):
+             pod_wide_blocks=0, block_sparse=None):
     """Return the plan as plain lists.
 
     ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
@@ -157,9 +167,13 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     Result: ``{"levels": [{"items": [...12-tuples...], "worker_indptr": [...]}],
     "merges": [(q_tok, head0, n_heads, parts_off, n_parts)], "parts": [...],
     "qlist": [...], "n_part_rows": int}``.
-    ``pod_blocks`` (append and cascade): plan one fused launch of that many
-    workgroups (rule 6; ``rows_per_block`` and ``min_chunk_pages`` then name
-    the wide and the decode role); the result also holds ``pod_wide_blocks``.
+    ``pod_blocks`` (append, cascade, block_sparse): plan one fused launch of
+    that many workgroups (rule 6; ``rows_per_block`` and ``min_chunk_pages``
+    then name the wide and the decode role); the result also holds
+    ``pod_wide_blocks``. ``kind="block_sparse"`` takes ``block_sparse =
+    (qo_len, row_sz [Hkv][MB], col_sz [Hkv][NB], mask [Hkv][MB][NB],
+    seq_pages)`` (rule 7; ``kv_indptr`` and ``kv_len`` are then unused) and
+    the result also holds ``plist``.
     """
     nlev = len(rows_per_block)
     workers = list(num_workers) if isinstance(num_workers, (list, tuple)) else [num_workers] * nlev
@@ -191,6 +205,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
         return units
 
     qlist = []
+    page_list = []      # block_sparse: the units' page lists
     levels_units = []
     if kind == "cascade":
         NG = len(prefix_len)
@@ -231,6 +246,31 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                 levels_units.append(request_units(
                     rows_per_block[lev], lambda r: qo[r], lambda r: int(qo_indptr[r]),
                     bool(causal), take=lambda r, role=role: small[r] == role))
+    elif kind == "block_sparse":
+        qo_len, row_sz, col_sz, mask, seq_pages = block_sparse
+        wide, small = [], []
+        for g in range(num_kv_heads):
+            q0 = 0
+            for a, nq in enumerate(int(x) for x in row_sz[g]):
+                off, t_lim, c0 = len(page_list), 0, 0
+                for b, c in enumerate(int(x) for x in col_sz[g]):
+                    if c > 0 and mask[g][a][b]:
+                        page_list.extend(int(seq_pages[pg]) for pg in
+                                     range(c0 // ps, _ceil_div(c0 + c, ps)))
+                        t_lim += c
+                    c0 += c
+                rows = nq * G
+                to_small = pod_blocks is not None and rows <= POD_DECODE_ROWS
+                rpb = rows_per_block[1] if to_small else rows_per_block[0]
+                for blk in range(_ceil_div(rows, rpb)):
+                    (small if to_small else wide).append(dict(
+                        unit=g * len(row_sz[g]) + a, q_base=q0, row0=blk * rpb,
+                        n_rows=min(rows - blk * rpb, rpb), g=g, page_off=off, t_lim=t_lim,
+                        n_pages=_ceil_div(t_lim, ps), q_pos0=0, flags=0, nq=nq))
+                q0 += nq
+        levels_units.append(wide)
+        if pod_blocks is not None:
+            levels_units.append(small)
     else:
         levels_units.append(request_units(rows_per_block[0], lambda r: 1, lambda r: r, False))
 
@@ -344,7 +384,8 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                     merges.append((u["q_base"] + i, u["g"] * G + (a - i * G), b - a,
                                    len(parts), len(plist)))
                     parts.extend(plist)
-    out = dict(levels=levels, merges=merges, parts=parts, qlist=qlist, n_part_rows=next_row)
+    out = dict(levels=levels, merges=merges, parts=parts, qlist=qlist, n_part_rows=next_row,
+               plist=page_list)
     if kind != "decode" and pod_blocks is not None:
         P = int(pod_blocks)
         for lev, total in ((0, P), (1, 4 * P)):

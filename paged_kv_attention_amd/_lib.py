@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(HERE, "libfi.so")
 
 FI_OK, FI_ERR_INVALID_ARG, FI_ERR_UNSUPPORTED, FI_ERR_WORKSPACE, FI_ERR_PLAN_MISMATCH, \
     FI_ERR_HIP = range(6)
-FI_KIND_DECODE, FI_KIND_APPEND, FI_KIND_CASCADE = range(3)
+FI_KIND_DECODE, FI_KIND_APPEND, FI_KIND_CASCADE, FI_KIND_BLOCK_SPARSE = range(4)
 FI_DTYPE_BF16, FI_DTYPE_F32 = 0, 1
 FI_ENGINE_DEFAULT, FI_ENGINE_MFMA, FI_ENGINE_VALU = range(3)
 FI_LAUNCH_DEFAULT, FI_LAUNCH_POD, FI_LAUNCH_SEPARATE = range(3)
@@ -39,7 +39,7 @@ class PlanInfo(ctypes.Structure):
         ("num_merges", c_int32), ("merges", I32P), ("num_parts", c_int32), ("parts", I32P),
         ("num_qlist", c_int32), ("qlist", I32P), ("num_part_rows", c_int32),
         ("num_scatter", c_int32), ("dev_bytes_used", c_size_t), ("host_bytes_used", c_size_t),
-        ("pod_wide_blocks", c_int32),
+        ("pod_wide_blocks", c_int32), ("num_plist", c_int32), ("plist", I32P),
     ]
 
 
@@ -60,6 +60,14 @@ SIGNATURES = {
                                   c_void_p, c_float, c_void_p, c_void_p, c_void_p]),
     "fi_cascade": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                              c_float, c_void_p, c_void_p, c_void_p]),
+    "fi_workspace_size_block_sparse": (c_int32, [POINTER(PlanDesc), c_int32, c_int32, c_int32,
+                                                 c_int32, POINTER(c_size_t),
+                                                 POINTER(c_size_t)]),
+    "fi_plan_block_sparse": (c_int32, [POINTER(PlanDesc), c_int32, c_int32, c_int32, I32P,
+                                       c_int32, I32P, c_void_p, I32P, c_void_p, c_size_t,
+                                       c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+    "fi_block_sparse_attention": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_float,
+                                            c_void_p, c_void_p, c_void_p]),
     "fi_merge_states": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,
                                   c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
     "fi_last_error": (c_char_p, []),

@@ -166,7 +166,65 @@ class Plan:
                     parts=arr(inf.parts, inf.num_parts), qlist=arr(inf.qlist, inf.num_qlist),
                     num_part_rows=inf.num_part_rows, num_scatter=inf.num_scatter,
                     dev_bytes_used=inf.dev_bytes_used, host_bytes_used=inf.host_bytes_used,
-                    pod_wide_blocks=inf.pod_wide_blocks)
+                    pod_wide_blocks=inf.pod_wide_blocks, plist=arr(inf.plist, inf.num_plist))
+
+
+class BlockSparsePlan(Plan):
+    """A variable block-sparse plan over one sequence (fi_plan_block_sparse).
+    ``row_block_sz [Hkv, MB]`` and ``col_block_sz [Hkv, NB]`` cut the qo_len
+    queries and the kv_len keys per kv head, ``block_mask [Hkv, MB, NB]``
+    selects the (row block, column block) pairs, and ``seq_pages`` holds the
+    sequence's page ids (token t in page seq_pages[t // page_size])."""
+
+    def __init__(self, qo_len: int, kv_len: int, row_block_sz, col_block_sz, block_mask,
+                 seq_pages, num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                 page_size: int, *, deterministic: bool = False, det_chunk_pages: int = 0,
+                 min_chunk_pages: int = 0, num_cus: int = 0, workers_per_cu: int = 0,
+                 launch: str = "default", pod_wide_blocks: int = 0, device="cuda",
+                 workspace: Optional[Workspace] = None):
+        lib = L.load()
+        self.kind = "block_sparse"
+        rs = _host_i32(row_block_sz).reshape(num_kv_heads, -1)
+        cs = _host_i32(col_block_sz).reshape(num_kv_heads, -1)
+        mb, nb = rs.shape[1], cs.shape[1]
+        mask = block_mask.detach().cpu().numpy() if isinstance(block_mask, torch.Tensor) \
+            else np.asarray(block_mask)
+        mask = np.ascontiguousarray(mask.astype(np.uint8).reshape(num_kv_heads, mb, nb))
+        pages = _host_i32(seq_pages)
+        self._ha = dict(row=np.ascontiguousarray(rs), col=np.ascontiguousarray(cs), mask=mask,
+                        pages=pages if pages is not None else np.zeros(0, np.int32))
+        self.desc = L.PlanDesc(kind=L.FI_KIND_BLOCK_SPARSE, batch=1, num_qo_heads=num_qo_heads,
+                               num_kv_heads=num_kv_heads, head_dim=head_dim,
+                               page_size=page_size, deterministic=int(deterministic),
+                               det_chunk_pages=det_chunk_pages, min_chunk_pages=min_chunk_pages,
+                               num_cus=num_cus, workers_per_cu=workers_per_cu,
+                               launch=_LAUNCHES[launch], pod_wide_blocks=pod_wide_blocks)
+        self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
+        self.head_dim, self.page_size, self.batch = head_dim, page_size, 1
+        self.num_q_tokens = int(qo_len)
+        self.device = None if device is None else torch.device(device)
+        self.workspace = workspace
+        ws_dev = ws_host = None
+        dev_b = host_b = 0
+        stream = None
+        if self.device is not None:
+            if self.workspace is None:
+                db, hb = ctypes.c_size_t(), ctypes.c_size_t()
+                L.check(lib.fi_workspace_size_block_sparse(
+                    ctypes.byref(self.desc), int(qo_len), int(kv_len), mb, nb,
+                    ctypes.byref(db), ctypes.byref(hb)), "fi_workspace_size_block_sparse")
+                self.workspace = Workspace(db.value, hb.value, self.device)
+            ws_dev, ws_host = _ptr(self.workspace.dev), _ptr(self.workspace.host)
+            dev_b, host_b = self.workspace.dev.numel(), self.workspace.host.numel()
+            stream = _stream(self.device)
+        h = ctypes.c_void_p()
+        a = self._ha
+        L.check(lib.fi_plan_block_sparse(ctypes.byref(self.desc), int(qo_len), int(kv_len), mb,
+                                         _p(a["row"]), nb, _p(a["col"]),
+                                         a["mask"].ctypes.data_as(ctypes.c_void_p),
+                                         _p(a["pages"]), ws_dev, dev_b, ws_host, host_b, stream,
+                                         ctypes.byref(h)), "fi_plan_block_sparse")
+        self._h = h
 
 
 def _check_tensor(t, name, dtype, device, shape=None):
@@ -293,6 +351,23 @@ def cascade(plan: Plan, q, k_cache, v_cache, prefix_indices, kv_indices, sm_scal
     L.check(L.load().fi_cascade(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                 _ptr(prefix_indices), _ptr(kv_indices), float(sm_scale),
                                 _ptr(out), _ptr(lse), _stream(plan.device)), "fi_cascade")
+    return out, lse
+
+
+def block_sparse_attention(plan: BlockSparsePlan, q, k_cache, v_cache, sm_scale: float,
+                           out=None, lse=None, return_lse: bool = True):
+    """fi_block_sparse_attention: q [qo_len, Hq, D] bf16 -> (out, lse [qo_len, Hq])."""
+    _check_run(plan, "block_sparse")
+    T = plan.num_q_tokens
+    _check_tensor(q, "q", torch.bfloat16, plan.device, (T, plan.num_qo_heads, plan.head_dim))
+    _check_cache(plan, k_cache, v_cache)
+    if lse is None and return_lse:
+        lse = torch.empty(T, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
+    out, lse = _outputs(plan, q, out, lse)
+    L.check(L.load().fi_block_sparse_attention(plan.handle, _ptr(q), _ptr(k_cache),
+                                               _ptr(v_cache), float(sm_scale), _ptr(out),
+                                               _ptr(lse), _stream(plan.device)),
+            "fi_block_sparse_attention")
     return out, lse
 
 

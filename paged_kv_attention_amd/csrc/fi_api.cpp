@@ -215,6 +215,35 @@ extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const vo
   return run_merge(p, o, lse, s);
 }
 
+extern "C" fi_status fi_block_sparse_attention(const fi_plan_t* p, const void* q,
+                                               const void* k_cache, const void* v_cache,
+                                               float sm_scale, void* o, float* lse,
+                                               void* stream) {
+  clear_error();
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return set_error(FI_ERR_INVALID_ARG,
+                     "fi_block_sparse_attention: sm_scale must be finite and > 0, got %g",
+                     (double)sm_scale);
+  fi_status st = check_plan(p, FI_KIND_BLOCK_SPARSE, "fi_block_sparse_attention");
+  if (st != FI_OK) return st;
+  if (!p->hp.merges.empty() || p->hp.level[0].num_items() > 0 || p->hp.level[1].num_items() > 0)
+    if (!q || !k_cache || !v_cache || !o)
+      return set_error(FI_ERR_INVALID_ARG, "fi_block_sparse_attention: NULL tensor pointer");
+  hipStream_t s = (hipStream_t)stream;
+  const int32_t* plist = at<int32_t>(p, p->lay.plist);   // the plan's own page lists
+  TimerScope t(s);
+  if (p->hp.pod) {
+    st = hip_status(launch_fused(p, q, k_cache, v_cache, plist, nullptr, sm_scale, o, lse, s),
+                    "attention launch");
+  } else {
+    const AttnArgs a = attn_args(p, 0, q, k_cache, v_cache, plist, nullptr, sm_scale, o, lse);
+    st = hip_status(launch_level(p, 0, a, s), "attention launch");
+  }
+  t.done();
+  if (st != FI_OK) return st;
+  return run_merge(p, o, lse, s);
+}
+
 extern "C" fi_status fi_cascade(const fi_plan_t* p, const void* q, const void* k_cache,
                                 const void* v_cache, const int32_t* prefix_indices,
                                 const int32_t* kv_indices, float sm_scale, void* o, float* lse,

@@ -39,6 +39,7 @@ struct HostPlan {
   // [0, pod_wide_blocks) of one launch, level 1 (decode role) on the rest
   bool pod = false;
   int32_t pod_wide_blocks = 0;
+  std::vector<int32_t> plist;    // block-sparse: the units' page lists
 };
 
 // Byte offsets of each section inside the workspace blob.
@@ -46,6 +47,7 @@ struct Layout {
   size_t items[2] = {0, 0}, windptr[2] = {0, 0};
   size_t merges = 0, parts = 0, qlist = 0, scatter = 0;
   size_t meta = 0;           // int32 [0]: the pod split (workgroups of the wide role)
+  size_t plist = 0;          // block-sparse page lists
   size_t blob_bytes = 0;     // int32 sections (host staging size)
   size_t part_o = 0, part_lse = 0;
   size_t dev_bytes = 0;      // blob + fp32 partial states
@@ -53,7 +55,7 @@ struct Layout {
 
 Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t n_merges,
                   size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
-                  int32_t head_dim);
+                  int32_t head_dim, size_t n_plist = 0);
 
 }  // namespace fi
 

@@ -71,7 +71,7 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t n_merges,
                   size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
-                  int32_t head_dim) {
+                  int32_t head_dim, size_t n_plist) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t n_int32) {
@@ -88,6 +88,7 @@ Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t 
   L.qlist = take(n_qlist);
   L.scatter = take(n_scatter * 2);
   L.meta = take(1);
+  L.plist = take(n_plist);
   L.blob_bytes = off;
   L.part_o = off;
   off = align_up(off + n_part_rows * (size_t)head_dim * 4, 256);
@@ -359,6 +360,27 @@ fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
   return FI_OK;
 }
 
+// Merge records of a level whose units write final rows unless split: a unit
+// of k != 1 chunks gets, per query token of its rows, a record over its
+// chunks' partial rows in chunk order (k = 0, no keys: an empty record, which
+// writes o = 0 and lse = -inf).
+void unit_merges(const std::vector<Unit>& units, const LevelBuild& lb, int32_t G, HostPlan& hp) {
+  for (size_t ui = 0; ui < units.size(); ++ui) {
+    const Unit& u = units[ui];
+    const int32_t k = lb.chunks[ui].first;
+    if (k == 1) continue;
+    const std::vector<int32_t>& dsts = lb.chunks[ui].second;
+    const int32_t r0 = u.row0, r1 = u.row0 + u.n_rows;
+    for (int32_t i = r0 / G; i <= (r1 - 1) / G; ++i) {
+      const int32_t a = std::max(r0, i * G), b = std::min(r1, (i + 1) * G);
+      const int32_t rec[MERGE_INTS] = {u.q_base + i, u.g * G + (a - i * G), b - a,
+                                       (int32_t)hp.parts.size(), (int32_t)dsts.size()};
+      hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
+      for (int32_t dd : dsts) hp.parts.push_back(dd + (a - r0));
+    }
+  }
+}
+
 }  // namespace
 
 // Engine for decode-style levels when the caller leaves the choice open: the
@@ -368,8 +390,12 @@ static constexpr int32_t kDefaultEngine = FI_ENGINE_MFMA;
 static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (!din) return set_error(FI_ERR_INVALID_ARG, "desc is NULL");
   d = *din;
-  if (d.kind < FI_KIND_DECODE || d.kind > FI_KIND_CASCADE)
+  if (d.kind < FI_KIND_DECODE || d.kind > FI_KIND_BLOCK_SPARSE)
     return set_error(FI_ERR_INVALID_ARG, "unknown plan kind %d", d.kind);
+  if (d.kind == FI_KIND_BLOCK_SPARSE) {
+    if (d.causal) return set_error(FI_ERR_INVALID_ARG, "a block-sparse plan takes no causal mask");
+    d.batch = 1;
+  }
   if (d.batch < 0) return set_error(FI_ERR_INVALID_ARG, "batch %d < 0", d.batch);
   if (d.num_qo_heads < 1 || d.num_kv_heads < 1)
     return set_error(FI_ERR_INVALID_ARG, "head counts must be >= 1");
@@ -414,7 +440,7 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.workers_per_cu == 0) d.workers_per_cu = 4;
   d.causal = d.causal ? 1 : 0;
   d.deterministic = d.deterministic ? 1 : 0;
-  if (d.kind != FI_KIND_APPEND) d.causal = 0;
+  if (d.kind != FI_KIND_APPEND) d.causal = 0;   // (block-sparse: refused above if set)
   if (d.kind != FI_KIND_CASCADE) d.num_prefix_groups = 0;
   return FI_OK;
 }
@@ -588,22 +614,7 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
                     append ? qo_indptr : nullptr, causal);
       build_level(units[0], d, false, next_row, lb[0], hp.level[0]);
     }
-    for (int l = 0; l < hp.num_levels; ++l) {
-      for (size_t ui = 0; ui < units[l].size(); ++ui) {
-        const Unit& u = units[l][ui];
-        const int32_t k = lb[l].chunks[ui].first;
-        if (k == 1) continue;
-        const std::vector<int32_t>& dsts = lb[l].chunks[ui].second;
-        const int32_t r0 = u.row0, r1 = u.row0 + u.n_rows;
-        for (int32_t i = r0 / G; i <= (r1 - 1) / G; ++i) {
-          const int32_t a = std::max(r0, i * G), b = std::min(r1, (i + 1) * G);
-          const int32_t rec[MERGE_INTS] = {u.q_base + i, u.g * G + (a - i * G), b - a,
-                                           (int32_t)hp.parts.size(), (int32_t)dsts.size()};
-          hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
-          for (int32_t dd : dsts) hp.parts.push_back(dd + (a - r0));
-        }
-      }
-    }
+    for (int l = 0; l < hp.num_levels; ++l) unit_merges(units[l], lb[l], G, hp);
     if (append) {
       for (int32_t r = 0; r < B; ++r) {
         const int32_t nq = qo_indptr[r + 1] - qo_indptr[r];
@@ -619,6 +630,100 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
   return FI_OK;
 }
 
+// Variable block-sparse: every (kv head g, row block a) is a unit set over the
+// page list of a's selected column blocks (in column order), appended to
+// hp.plist; units in the order g, a, 128-row (or, in the decode role, 16-row)
+// block. Rows of a fit one 16-row block -> decode role of a POD launch.
+static fi_status build_block_sparse(const fi_plan_desc& d, int32_t qo_len, int32_t kv_len,
+                                    int32_t MB, const int32_t* row_sz, int32_t NB,
+                                    const int32_t* col_sz, const uint8_t* mask,
+                                    const int32_t* seq_pages, HostPlan& hp) {
+  const int32_t Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads, ps = d.page_size;
+  if (qo_len < 0 || kv_len < 0 || MB < 0 || NB < 0)
+    return set_error(FI_ERR_INVALID_ARG, "negative block-sparse size");
+  if ((MB > 0 && !row_sz) || (NB > 0 && !col_sz) || (MB > 0 && NB > 0 && !mask) ||
+      (kv_len > 0 && !seq_pages))
+    return set_error(FI_ERR_INVALID_ARG, "block-sparse arrays are NULL");
+  for (int32_t g = 0; g < Hkv; ++g) {
+    int64_t rs = 0, cs = 0;
+    for (int32_t a = 0; a < MB; ++a) {
+      if (row_sz[g * MB + a] < 0) return set_error(FI_ERR_INVALID_ARG, "negative row block size");
+      rs += row_sz[g * MB + a];
+    }
+    for (int32_t b = 0; b < NB; ++b) {
+      const int32_t c = col_sz[g * NB + b];
+      if (c < 0) return set_error(FI_ERR_INVALID_ARG, "negative column block size");
+      if (c > 0 && cs % ps)
+        return set_error(FI_ERR_INVALID_ARG,
+                         "kv head %d: column block %d starts at key %lld, not a page boundary", g,
+                         b, (long long)cs);
+      cs += c;
+    }
+    if (rs != qo_len || cs != kv_len)
+      return set_error(FI_ERR_INVALID_ARG,
+                       "kv head %d: row blocks sum to %lld (qo_len %d), column blocks to %lld "
+                       "(kv_len %d)", g, (long long)rs, qo_len, (long long)cs, kv_len);
+  }
+  const bool pod = d.launch == FI_LAUNCH_POD;
+  std::vector<Unit> units[2];
+  for (int32_t g = 0; g < Hkv; ++g) {
+    int32_t q0 = 0;
+    for (int32_t a = 0; a < MB; ++a) {
+      const int32_t nq = row_sz[g * MB + a];
+      const int32_t off = (int32_t)hp.plist.size();
+      int32_t t_lim = 0, c0 = 0;
+      for (int32_t b = 0; b < NB; ++b) {
+        const int32_t c = col_sz[g * NB + b];
+        if (c > 0 && mask[((int64_t)g * MB + a) * NB + b]) {
+          for (int32_t pg = c0 / ps; pg < (int32_t)ceil_div(c0 + c, ps); ++pg)
+            hp.plist.push_back(seq_pages[pg]);
+          t_lim += c;
+        }
+        c0 += c;
+      }
+      const int64_t rows = (int64_t)nq * G;
+      const int lvl = (pod && rows <= ROWS_DECODE) ? 1 : 0;
+      const int32_t rpb = lvl ? ROWS_DECODE : ROWS_WIDE;
+      for (int64_t blk = 0; blk < ceil_div(rows, rpb); ++blk) {
+        Unit u;
+        u.unit = g * MB + a;
+        u.q_base = q0;
+        u.row0 = (int32_t)(blk * rpb);
+        u.n_rows = (int32_t)std::min<int64_t>(rows - blk * rpb, rpb);
+        u.g = g;
+        u.page_off = off;
+        u.t_lim = t_lim;
+        u.n_pages = (int32_t)ceil_div(t_lim, ps);
+        u.q_pos0 = 0;
+        u.flags = 0;
+        units[lvl].push_back(u);
+      }
+      q0 += nq;
+    }
+  }
+  int32_t next_row = 0;
+  LevelBuild lb[2];
+  Level& l0 = hp.level[0];
+  l0.rows_per_block = ROWS_WIDE;
+  l0.num_workers = d.num_cus * std::max(1, d.workers_per_cu / 2);
+  l0.min_chunk_pages = WIDE_CHUNK_FACTOR * d.min_chunk_pages;
+  if (pod) {
+    Level& l1 = hp.level[1];
+    l1.rows_per_block = ROWS_DECODE;
+    l1.num_workers = d.num_cus * d.workers_per_cu;
+    l1.min_chunk_pages = d.min_chunk_pages;
+    hp.num_levels = 2;
+    fi_status st = pod_levels(d, units, false, next_row, lb, hp);
+    if (st != FI_OK) return st;
+  } else {
+    hp.num_levels = 1;
+    build_level(units[0], d, false, next_row, lb[0], l0);
+  }
+  for (int l = 0; l < hp.num_levels; ++l) unit_merges(units[l], lb[l], G, hp);
+  hp.num_part_rows = next_row;
+  return FI_OK;
+}
+
 // ---------------------------------------------------------------- upload sync
 
 // One event per pinned staging buffer: the next plan into the same buffer
@@ -630,6 +735,95 @@ static std::map<void*, hipEvent_t> g_upload_events;
 
 using namespace fi;
 
+// Defaults, and the device's CU count when the caller leaves it open.
+static fi_status begin_plan(const fi_plan_desc* desc, void* ws_dev, void* ws_host,
+                            fi_plan_desc& d) {
+  fi_status st = fill_defaults(desc, d);
+  if (st != FI_OK) return st;
+  if (ws_dev && !ws_host)
+    return set_error(FI_ERR_INVALID_ARG, "a device plan needs a pinned host staging buffer");
+  if (d.num_cus == 0) {
+    if (!ws_dev)
+      return set_error(FI_ERR_INVALID_ARG, "a host-only plan needs num_cus > 0");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return set_error(FI_ERR_HIP, "device query: %s", hipGetErrorString(e));
+    d.num_cus = cus;
+  }
+  return FI_OK;
+}
+
+// Lay the built plan out, check the caller's workspace, and upload (the
+// pinned staging buffer is reused only after its previous upload was read).
+static fi_status finish_plan(fi_plan_t* p, void* ws_dev, size_t ws_dev_bytes, void* ws_host,
+                             size_t ws_host_bytes, void* stream, fi_plan_t** out) {
+  HostPlan& hp = p->hp;
+  const fi_plan_desc& d = hp.desc;
+  size_t n_items[2] = {(size_t)hp.level[0].num_items(), (size_t)hp.level[1].num_items()};
+  const int32_t workers[2] = {hp.level[0].num_workers, hp.level[1].num_workers};
+  p->lay = layout_for(workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
+                      hp.qlist.size(), hp.scatter.size() / 2, (size_t)hp.num_part_rows,
+                      d.head_dim, hp.plist.size());
+  const Layout& L = p->lay;
+  if (ws_dev) {
+    if (ws_dev_bytes < L.dev_bytes || ws_host_bytes < L.blob_bytes) {
+      delete p;
+      return set_error(FI_ERR_WORKSPACE,
+                       "workspace too small: need %zu device / %zu host bytes, got %zu / %zu",
+                       L.dev_bytes, L.blob_bytes, ws_dev_bytes, ws_host_bytes);
+    }
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t ev = nullptr;
+    {
+      std::lock_guard<std::mutex> lk(g_upload_mu);
+      auto itv = g_upload_events.find(ws_host);
+      if (itv != g_upload_events.end()) ev = itv->second;
+    }
+    hipError_t e = hipSuccess;
+    if (ev) e = hipEventSynchronize(ev);
+    if (e != hipSuccess) {
+      delete p;
+      return set_error(FI_ERR_HIP, "waiting for the previous upload: %s", hipGetErrorString(e));
+    }
+    char* h = (char*)ws_host;
+    for (int l = 0; l < 2; ++l) {
+      if (!hp.level[l].items.empty())
+        memcpy(h + L.items[l], hp.level[l].items.data(), hp.level[l].items.size() * 4);
+      if (!hp.level[l].worker_indptr.empty())
+        memcpy(h + L.windptr[l], hp.level[l].worker_indptr.data(),
+               hp.level[l].worker_indptr.size() * 4);
+    }
+    if (!hp.merges.empty()) memcpy(h + L.merges, hp.merges.data(), hp.merges.size() * 4);
+    if (!hp.parts.empty()) memcpy(h + L.parts, hp.parts.data(), hp.parts.size() * 4);
+    if (!hp.qlist.empty()) memcpy(h + L.qlist, hp.qlist.data(), hp.qlist.size() * 4);
+    if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
+    memcpy(h + L.meta, &hp.pod_wide_blocks, 4);
+    if (!hp.plist.empty()) memcpy(h + L.plist, hp.plist.data(), hp.plist.size() * 4);
+    e = hipMemcpyAsync(ws_dev, ws_host, L.blob_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) {
+      if (!ev) {
+        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) {
+          std::lock_guard<std::mutex> lk(g_upload_mu);
+          g_upload_events[ws_host] = ev;
+        }
+      }
+      if (e == hipSuccess) e = hipEventRecord(ev, s);
+    }
+    if (e != hipSuccess) {
+      delete p;
+      return set_error(FI_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
+    }
+    p->on_device = true;
+    p->dev_base = (char*)ws_dev;
+  }
+  *out = p;
+  return FI_OK;
+}
+
+
+
 extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_pages,
                                        int64_t max_qo_tokens, int64_t max_prefix_pages,
                                        size_t* dev_bytes, size_t* host_bytes) {
@@ -638,6 +832,8 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
   fi_status st = fill_defaults(desc, d);
   if (st != FI_OK) return st;
   if (!dev_bytes || !host_bytes) return set_error(FI_ERR_INVALID_ARG, "NULL output pointer");
+  if (d.kind == FI_KIND_BLOCK_SPARSE)
+    return set_error(FI_ERR_INVALID_ARG, "block-sparse plans: fi_workspace_size_block_sparse");
   if (max_kv_pages < 0 || max_qo_tokens < 0 || max_prefix_pages < 0)
     return set_error(FI_ERR_INVALID_ARG, "negative size bound");
   int32_t num_cus = d.num_cus;
@@ -707,6 +903,46 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
   return FI_OK;
 }
 
+extern "C" fi_status fi_workspace_size_block_sparse(const fi_plan_desc* desc, int32_t qo_len,
+                                                    int32_t kv_len, int32_t num_row_blocks,
+                                                    int32_t num_col_blocks, size_t* dev_bytes,
+                                                    size_t* host_bytes) {
+  clear_error();
+  fi_plan_desc d;
+  fi_status st = fill_defaults(desc, d);
+  if (st != FI_OK) return st;
+  if (!dev_bytes || !host_bytes) return set_error(FI_ERR_INVALID_ARG, "NULL output pointer");
+  if (qo_len < 0 || kv_len < 0 || num_row_blocks < 0 || num_col_blocks < 0)
+    return set_error(FI_ERR_INVALID_ARG, "negative size bound");
+  int32_t num_cus = d.num_cus;
+  if (num_cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+            hipSuccess)
+      return set_error(FI_ERR_HIP, "could not query the device's compute units");
+  }
+  const int64_t Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads, MB = num_row_blocks;
+  const int64_t P = (int64_t)num_cus * std::max(1, d.workers_per_cu / 2);
+  const int64_t S1 = d.launch == FI_LAUNCH_POD ? WAVES_PER_BLOCK * P : 0;
+  const int64_t seq_pages = ceil_div(kv_len, d.page_size);
+  // units: every (kv head, row block) in blocks of at least 16 rows
+  const int64_t units = Hkv * (ceil_div((int64_t)qo_len * G, ROWS_DECODE) + MB);
+  const int64_t c_det = std::max(1, d.det_chunk_pages);
+  auto items_of = [&](int64_t S) {
+    return d.deterministic ? units * seq_pages / c_det + units : S + units;
+  };
+  size_t n_items[2] = {(size_t)items_of(P), S1 ? (size_t)items_of(S1) : 0};
+  const int32_t workers[2] = {(int32_t)P, (int32_t)S1};
+  const int64_t part_rows = ((int64_t)n_items[0] + (int64_t)n_items[1]) * ROWS_WIDE;
+  const int64_t merges = Hkv * qo_len + 2 * units;
+  Layout L = layout_for(workers, n_items, (size_t)merges, (size_t)part_rows, 0, 0,
+                        (size_t)part_rows, d.head_dim, (size_t)(Hkv * MB * seq_pages));
+  *dev_bytes = L.dev_bytes;
+  *host_bytes = L.blob_bytes;
+  return FI_OK;
+}
+
 extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_h,
                              const int32_t* kv_len_h, const int32_t* qo_indptr_h,
                              const int32_t* prefix_indptr_h, const int32_t* prefix_len_h,
@@ -718,19 +954,10 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
   if (!out) return set_error(FI_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   fi_plan_desc d;
-  fi_status st = fill_defaults(desc, d);
+  fi_status st = begin_plan(desc, ws_dev, ws_host, d);
   if (st != FI_OK) return st;
-  if (ws_dev && !ws_host)
-    return set_error(FI_ERR_INVALID_ARG, "a device plan needs a pinned host staging buffer");
-  if (d.num_cus == 0) {
-    if (!ws_dev)
-      return set_error(FI_ERR_INVALID_ARG, "a host-only plan needs num_cus > 0");
-    int dev = 0, cus = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return set_error(FI_ERR_HIP, "device query: %s", hipGetErrorString(e));
-    d.num_cus = cus;
-  }
+  if (d.kind == FI_KIND_BLOCK_SPARSE)
+    return set_error(FI_ERR_INVALID_ARG, "block-sparse plans are built by fi_plan_block_sparse");
   fi_plan_t* p = new fi_plan_t();
   p->hp.desc = d;
   st = build(d, kv_indptr_h, kv_len_h, qo_indptr_h, prefix_indptr_h, prefix_len_h,
@@ -739,66 +966,34 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
     delete p;
     return st;
   }
-  HostPlan& hp = p->hp;
-  size_t n_items[2] = {(size_t)hp.level[0].num_items(), (size_t)hp.level[1].num_items()};
-  const int32_t workers[2] = {hp.level[0].num_workers, hp.level[1].num_workers};
-  p->lay = layout_for(workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
-                      hp.qlist.size(), hp.scatter.size() / 2, (size_t)hp.num_part_rows,
-                      d.head_dim);
-  const Layout& L = p->lay;
-  if (ws_dev) {
-    if (ws_dev_bytes < L.dev_bytes || ws_host_bytes < L.blob_bytes) {
-      delete p;
-      return set_error(FI_ERR_WORKSPACE,
-                       "workspace too small: need %zu device / %zu host bytes, got %zu / %zu",
-                       L.dev_bytes, L.blob_bytes, ws_dev_bytes, ws_host_bytes);
-    }
-    hipStream_t s = (hipStream_t)stream;
-    hipEvent_t ev = nullptr;
-    {
-      std::lock_guard<std::mutex> lk(g_upload_mu);
-      auto itv = g_upload_events.find(ws_host);
-      if (itv != g_upload_events.end()) ev = itv->second;
-    }
-    hipError_t e = hipSuccess;
-    if (ev) e = hipEventSynchronize(ev);
-    if (e != hipSuccess) {
-      delete p;
-      return set_error(FI_ERR_HIP, "waiting for the previous upload: %s", hipGetErrorString(e));
-    }
-    char* h = (char*)ws_host;
-    for (int l = 0; l < 2; ++l) {
-      if (!hp.level[l].items.empty())
-        memcpy(h + L.items[l], hp.level[l].items.data(), hp.level[l].items.size() * 4);
-      if (!hp.level[l].worker_indptr.empty())
-        memcpy(h + L.windptr[l], hp.level[l].worker_indptr.data(),
-               hp.level[l].worker_indptr.size() * 4);
-    }
-    if (!hp.merges.empty()) memcpy(h + L.merges, hp.merges.data(), hp.merges.size() * 4);
-    if (!hp.parts.empty()) memcpy(h + L.parts, hp.parts.data(), hp.parts.size() * 4);
-    if (!hp.qlist.empty()) memcpy(h + L.qlist, hp.qlist.data(), hp.qlist.size() * 4);
-    if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
-    memcpy(h + L.meta, &hp.pod_wide_blocks, 4);
-    e = hipMemcpyAsync(ws_dev, ws_host, L.blob_bytes, hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) {
-      if (!ev) {
-        e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-        if (e == hipSuccess) {
-          std::lock_guard<std::mutex> lk(g_upload_mu);
-          g_upload_events[ws_host] = ev;
-        }
-      }
-      if (e == hipSuccess) e = hipEventRecord(ev, s);
-    }
-    if (e != hipSuccess) {
-      delete p;
-      return set_error(FI_ERR_HIP, "plan upload: %s", hipGetErrorString(e));
-    }
-    p->on_device = true;
-    p->dev_base = (char*)ws_dev;
+  return finish_plan(p, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes, stream, out);
+}
+
+extern "C" fi_status fi_plan_block_sparse(const fi_plan_desc* desc, int32_t qo_len,
+                                          int32_t kv_len, int32_t num_row_blocks,
+                                          const int32_t* row_block_sz_h, int32_t num_col_blocks,
+                                          const int32_t* col_block_sz_h,
+                                          const uint8_t* block_mask_h,
+                                          const int32_t* seq_pages_h, void* ws_dev,
+                                          size_t ws_dev_bytes, void* ws_host,
+                                          size_t ws_host_bytes, void* stream, fi_plan_t** out) {
+  clear_error();
+  if (!out) return set_error(FI_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  fi_plan_desc d;
+  fi_status st = begin_plan(desc, ws_dev, ws_host, d);
+  if (st != FI_OK) return st;
+  if (d.kind != FI_KIND_BLOCK_SPARSE)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan_block_sparse needs kind FI_KIND_BLOCK_SPARSE");
+  fi_plan_t* p = new fi_plan_t();
+  p->hp.desc = d;
+  st = build_block_sparse(d, qo_len, kv_len, num_row_blocks, row_block_sz_h, num_col_blocks,
+                          col_block_sz_h, block_mask_h, seq_pages_h, p->hp);
+  if (st != FI_OK) {
+    delete p;
+    return st;
   }
-  *out = p;
-  return FI_OK;
+  return finish_plan(p, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes, stream, out);
 }
 
 extern "C" void fi_plan_destroy(fi_plan_t* plan) { delete plan; }
@@ -830,6 +1025,8 @@ extern "C" fi_status fi_plan_get_info(const fi_plan_t* p, fi_plan_info* info) {
   info->dev_bytes_used = p->lay.dev_bytes;
   info->host_bytes_used = p->lay.blob_bytes;
   info->pod_wide_blocks = hp.pod ? hp.pod_wide_blocks : 0;
+  info->num_plist = (int32_t)hp.plist.size();
+  info->plist = hp.plist.data();
   return FI_OK;
 }
 

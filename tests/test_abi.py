@@ -447,3 +447,93 @@ def test_workspace_size_rejects_bad_input():
     d = _desc(head_dim=256)
     assert lib.fi_workspace_size(ctypes.byref(d), 1, 0, 0, ctypes.byref(dev),
                                  ctypes.byref(host)) == L.FI_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- block-sparse plans
+
+
+def _bs_spec(rng, Hkv, T, Lk, ps, MB, NB, p_mask=0.5):
+    def cuts(total, n, align):
+        units = -(-total // align)
+        e = np.sort(rng.integers(0, units + 1, n - 1)) * align
+        return np.diff(np.concatenate([[0], np.minimum(e, total), [total]])).astype(np.int32)
+    row = np.stack([cuts(T, MB, 1) for _ in range(Hkv)])
+    col = np.stack([cuts(Lk, NB, ps) for _ in range(Hkv)])
+    mask = (rng.random((Hkv, MB, NB)) < p_mask).astype(np.uint8)
+    pages = rng.permutation(-(-Lk // ps) + 5)[: -(-Lk // ps)].astype(np.int32)
+    return row, col, mask, pages
+
+
+@pytest.mark.parametrize("launch", ["pod", "separate"])
+@pytest.mark.parametrize("det", [False, True])
+@pytest.mark.parametrize("Hq,Hkv,ps,T,Lk,MB,NB", [(8, 2, 16, 300, 1000, 5, 7),
+                                                   (32, 8, 8, 40, 333, 3, 4),
+                                                   (4, 4, 32, 17, 64, 17, 2),
+                                                   (16, 2, 16, 1, 5000, 1, 9)])
+def test_block_sparse_plan_matches_reference(launch, det, Hq, Hkv, ps, T, Lk, MB, NB):
+    rng = np.random.default_rng(T + Lk + MB)
+    row, col, mask, pages = _bs_spec(rng, Hkv, T, Lk, ps, MB, NB)
+    p = fi.BlockSparsePlan(T, Lk, row, col, mask, pages, Hq, Hkv, 128, ps, device=None,
+                           num_cus=5, workers_per_cu=4, deterministic=det, det_chunk_pages=6,
+                           launch=launch)
+    info = p.info()
+    P = 5 * 2
+    ref = plan_ref("block_sparse", Hq, Hkv, ps, [0], [], **level_params(info),
+                   deterministic=det, det_chunk_pages=6,
+                   pod_blocks=P if launch == "pod" else None,
+                   block_sparse=(T, row, col, mask, pages))
+    compare(info, ref)
+    assert np.array_equal(info["plist"], np.array(ref["plist"], dtype=np.int32))
+    if launch == "pod":
+        assert info["pod_wide_blocks"] == ref["pod_wide_blocks"]
+    # every (kv head, query token) row is covered exactly once: by one item
+    # whose unit is unsplit, or by merge records
+    G = Hq // Hkv
+    seen = np.zeros((T, Hq), dtype=np.int64)
+    for lv in info["levels"]:
+        for it in lv["items"]:
+            if it[5] & 2:       # partial rows: covered by the merges below
+                continue
+            for rho in range(it[1], it[1] + it[2]):
+                seen[it[0] + rho // G, it[3] * G + rho % G] += 1
+    for m in info["merges"]:
+        seen[m[0], m[1]:m[1] + m[2]] += 1
+    assert np.all(seen == 1)
+    # the plan fits its workspace bound
+    d = L.PlanDesc(kind=L.FI_KIND_BLOCK_SPARSE, batch=1, num_qo_heads=Hq, num_kv_heads=Hkv,
+                   head_dim=128, page_size=ps, deterministic=int(det), det_chunk_pages=6,
+                   num_cus=5, workers_per_cu=4,
+                   launch=L.FI_LAUNCH_POD if launch == "pod" else L.FI_LAUNCH_SEPARATE)
+    db, hb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert fi.load().fi_workspace_size_block_sparse(ctypes.byref(d), T, Lk, MB, NB,
+                                                    ctypes.byref(db), ctypes.byref(hb)) == 0
+    assert db.value >= info["dev_bytes_used"] and hb.value >= info["host_bytes_used"]
+
+
+def test_block_sparse_plan_errors():
+    rng = np.random.default_rng(1)
+    row, col, mask, pages = _bs_spec(rng, 2, 20, 100, 16, 2, 3)
+    kw = dict(device=None, num_cus=4)
+    bad_col = col.copy()
+    bad_col[0, 0] += 1
+    bad_col[0, 1] -= 1                      # second block starts off a page boundary
+    if bad_col[0, 0] > 0 and bad_col[0, 1] >= 0 and bad_col[0, 1] + bad_col[0, 2] > 0:
+        with pytest.raises(fi.FIError, match="page boundary"):
+            fi.BlockSparsePlan(20, 100, row, bad_col, mask, pages, 8, 2, 64, 16, **kw)
+    bad_row = row.copy()
+    bad_row[1, 0] += 1                      # rows no longer sum to qo_len
+    with pytest.raises(fi.FIError, match="sum"):
+        fi.BlockSparsePlan(20, 100, bad_row, col, mask, pages, 8, 2, 64, 16, **kw)
+    # fi_plan and fi_workspace_size refuse the block-sparse kind
+    d = L.PlanDesc(kind=L.FI_KIND_BLOCK_SPARSE, batch=1, num_qo_heads=8, num_kv_heads=2,
+                   head_dim=64, page_size=16, num_cus=4)
+    h = ctypes.c_void_p()
+    lib = fi.load()
+    assert lib.fi_plan(ctypes.byref(d), None, None, None, None, None, None, None, None, 0, None,
+                       0, None, ctypes.byref(h)) == L.FI_ERR_INVALID_ARG
+    db, hb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.fi_workspace_size(ctypes.byref(d), 10, 0, 0, ctypes.byref(db),
+                                 ctypes.byref(hb)) == L.FI_ERR_INVALID_ARG
+    d.causal = 1
+    assert lib.fi_plan_block_sparse(ctypes.byref(d), 20, 100, 2, None, 3, None, None, None, None,
+                                    0, None, 0, None, ctypes.byref(h)) == L.FI_ERR_INVALID_ARG

@@ -453,7 +453,7 @@ def _mut_merge_sign(o1, l1, o2, l2):
 
 
 _ORIG = {n: getattr(A, n) for n in ("gather_tokens", "attend", "merge_two", "paged_append",
-                                    "paged_decode_fp8", "e4m3_values", "_chain")}
+                                    "paged_decode_fp8", "e4m3_values", "_chain", "block_sparse")}
 
 
 def _mut_append_top_left(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
@@ -535,6 +535,126 @@ def test_fp8_decode_equals_decode_of_torch_dequantized_pools():
     assert np.isnan(o2[[0, 2]]).all()
 
 
+# ---------------------------------------------------------------------------
+# variable block-sparse attention
+
+
+def _cuts(rng, total, n, align=1):
+    """n consecutive block sizes summing to total, every non-empty block
+    starting at a multiple of align (the last may end anywhere)."""
+    units = -(-total // align)
+    edges = np.sort(rng.integers(0, units + 1, n - 1)) * align
+    edges = np.concatenate([[0], np.minimum(edges, total), [total]])
+    return np.diff(edges).astype(np.int64)
+
+
+def block_sparse_case(seed, T=9, Lk=23, Hkv=2, G=2, D=4, ps=4, MB=3, NB=4, p_mask=0.5):
+    rng = np.random.default_rng(seed)
+    dk = rng.standard_normal((Hkv, Lk, D))
+    dv = rng.standard_normal((Hkv, Lk, D))
+    kp, indptr, indices, _ = paginate([dk], ps, rng)
+    vp = np.full_like(kp, np.nan)
+    for t in range(Lk):
+        vp[indices[t // ps], :, t % ps, :] = dv[:, t, :]
+    q = rng.standard_normal((T, Hkv * G, D))
+    row = np.stack([_cuts(rng, T, MB) for _ in range(Hkv)])
+    col = np.stack([_cuts(rng, Lk, NB, ps) for _ in range(Hkv)])
+    mask = rng.random((Hkv, MB, NB)) < p_mask
+    return q, dk, dv, kp, vp, indices, Lk, ps, row, col, mask
+
+
+def brute_block_sparse(q, dk, dv, row, col, mask, scale):
+    """Pure-Python loops: each row's visible keys listed one by one."""
+    T, Hq, D = q.shape
+    Hkv = dk.shape[0]
+    G = Hq // Hkv
+    o = np.zeros((T, Hq, D))
+    lse = np.full((T, Hq), -math.inf)
+    for h in range(Hq):
+        g = h // G
+        for i in range(T):
+            a, acc = 0, 0
+            while acc + row[g][a] <= i:
+                acc += row[g][a]
+                a += 1
+            keys = []
+            start = 0
+            for b, c in enumerate(col[g]):
+                if mask[g][a][b]:
+                    keys.extend(range(start, start + c))
+                start += c
+            if not keys:
+                continue
+            s = [scale * sum(q[i, h, d] * dk[g, t, d] for d in range(D)) for t in keys]
+            m = max(s)
+            w = [math.exp(x - m) for x in s]
+            z = sum(w)
+            lse[i, h] = m + math.log(z)
+            for d in range(D):
+                o[i, h, d] = sum(wj * dv[g, t, d] for wj, t in zip(w, keys)) / z
+    return o, lse
+
+
+def check_block_sparse_brute(seed=5):
+    q, dk, dv, kp, vp, idx, Lk, ps, row, col, mask = block_sparse_case(seed, MB=3, NB=3)
+    mask[:, 0, 1] = True
+    mask[:, 1, 0] = False             # asymmetric, so a transposed lookup differs
+    scale = 0.37
+    o, lse = A.block_sparse(q, kp, vp, idx, Lk, ps, row, col, mask, scale)
+    o_ref, l_ref = brute_block_sparse(q, dk, dv, row, col, mask, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(np.isinf(lse), np.isinf(l_ref))
+    fin = np.isfinite(l_ref)
+    np.testing.assert_allclose(lse[fin], l_ref[fin], rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("seed", [5, 6, 7])
+def test_block_sparse_brute_force(seed):
+    check_block_sparse_brute(seed)
+
+
+def test_block_sparse_full_mask_is_plain_attention():
+    q, dk, dv, kp, vp, idx, Lk, ps, row, col, mask = block_sparse_case(8, T=12, Lk=40, ps=8)
+    mask[:] = True
+    o, lse = A.block_sparse(q, kp, vp, idx, Lk, ps, row, col, mask, 0.5)
+    G = q.shape[1] // dk.shape[0]
+    for h in range(q.shape[1]):
+        ref = sdpa(q[:, h], dk[h // G], dv[h // G], 0.5)
+        np.testing.assert_allclose(o[:, h], ref, rtol=0, atol=1e-12)
+
+
+def test_block_sparse_block_diagonal_is_per_block_attention():
+    rng = np.random.default_rng(9)
+    q, dk, dv, kp, vp, idx, Lk, ps, _, _, _ = block_sparse_case(9, T=10, Lk=32, ps=8)
+    row = np.array([[3, 7, 0, 0], [5, 5, 0, 0]])
+    col = np.array([[8, 24, 0, 0], [16, 16, 0, 0]])
+    mask = np.zeros((2, 4, 4), dtype=bool)
+    mask[:, 0, 0] = mask[:, 1, 1] = True
+    o, lse = A.block_sparse(q, kp, vp, idx, Lk, ps, row, col, mask, 0.25)
+    G = 2
+    for h in range(q.shape[1]):
+        g = h // G
+        r0, c0 = 0, 0
+        for a in range(2):
+            r1, c1 = r0 + row[g][a], c0 + col[g][a]
+            ref = sdpa(q[r0:r1, h], dk[g, c0:c1], dv[g, c0:c1], 0.25)
+            np.testing.assert_allclose(o[r0:r1, h], ref, rtol=0, atol=1e-12)
+            r0, c0 = r1, c1
+
+
+def test_block_sparse_row_without_keys_is_zero_and_neg_inf():
+    q, dk, dv, kp, vp, idx, Lk, ps, row, col, mask = block_sparse_case(10)
+    mask[0, 1, :] = False                 # kv head 0, row block 1 sees nothing
+    o, lse = A.block_sparse(q, kp, vp, idx, Lk, ps, row, col, mask, 1.0)
+    r0, r1 = row[0][0], row[0][0] + row[0][1]
+    assert np.all(o[r0:r1, 0:2] == 0) and np.all(np.isneginf(lse[r0:r1, 0:2]))
+
+
+def _mut_block_sparse_mask_transposed(q, kp, vp, idx, Lk, ps, row, col, mask, scale):
+    return _ORIG["block_sparse"](q, kp, vp, idx, Lk, ps, row, col,
+                                 np.transpose(np.asarray(mask), (0, 2, 1)), scale)
+
+
 def _mut_chain_own_group_only(req_group, prefix_parent, r):
     return _ORIG["_chain"](req_group, None, r)
 
@@ -561,6 +681,8 @@ MUTATIONS = {
                            test_fp8_decode_equals_decode_of_torch_dequantized_pools),
     "e4m3_bias_8": ("e4m3_values", _mut_e4m3_bias8, test_e4m3_values_match_torch_for_every_code),
     "cascade_no_parents": ("_chain", _mut_chain_own_group_only, check_cascade_tree),
+    "block_sparse_mask_transposed": ("block_sparse", _mut_block_sparse_mask_transposed,
+                                     check_block_sparse_brute),
 }
 
 
@@ -575,5 +697,5 @@ def test_planted_mistake_is_caught(name, monkeypatch):
 
 def test_oracle_exports():
     for n in ("attend", "paged_decode", "paged_append", "merge_states", "cascade_flat",
-              "plan_ref", "paged_decode_fp8", "e4m3_values"):
+              "plan_ref", "paged_decode_fp8", "e4m3_values", "block_sparse"):
         assert hasattr(oracle, n)

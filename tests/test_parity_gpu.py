@@ -14,8 +14,8 @@ import oracle
 import paged_kv_attention_amd as fi
 from tests.helpers import (compare, gpu_decode, np_pools, oracle_decode, request_rows,
                            sample_requests)
-from workloads import (cascade_flat_tables, make_append, make_cascade, make_config, make_decode,
-                       make_pod_mix, to_fp8_cache)
+from workloads import (cascade_flat_tables, make_append, make_block_sparse, make_cascade,
+                       make_config, make_decode, make_pod_mix, make_sparse_video, to_fp8_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -448,6 +448,74 @@ def test_pod_deterministic_bits_independent_of_split(dev):
                         pod_wide_blocks=nw)[:2] for nw in (0, 3, 100)]
     for o, lse in outs[1:]:
         assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+
+
+# ---------------------------------------------------------------- variable block-sparse
+
+
+def _bs_run(w, dev, **kw):
+    p = fi.BlockSparsePlan(w.q.shape[0], int(w.kv_len[0]), w.row_block_sz, w.col_block_sz,
+                           w.block_mask, w.kv_indices, w.num_qo_heads, w.num_kv_heads,
+                           w.head_dim, w.page_size, device=dev, **kw)
+    g = w.to(dev)
+    o, lse = fi.block_sparse_attention(p, g.q, g.k_cache, g.v_cache, w.sm_scale)
+    torch.cuda.synchronize()
+    return o, lse, p
+
+
+def _bs_oracle(w, rows=None):
+    kp, vp = np_pools(w)
+    args = (w.kv_indices.numpy(), int(w.kv_len[0]), w.page_size, w.row_block_sz.numpy(),
+            w.col_block_sz.numpy(), w.block_mask.numpy(), w.sm_scale)
+    q = w.q.double().numpy()
+    o, lse = oracle.block_sparse(q, kp, vp, *args, rows=rows)
+    a, _ = oracle.block_sparse(q, kp, np.abs(vp), *args, rows=rows)
+    return o, lse, a
+
+
+@pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 1), (128, 32, 8), (64, 16, 2),
+                                    (128, 64, 16)])
+def test_block_sparse_small_sweep(dev, D, ps, G):
+    """Variable blocks per kv head (some empty), random masks with a row block
+    that sees nothing, every plan variant, against the oracle in full."""
+    Hkv = 2
+    w = make_block_sparse(90, 700, G * Hkv, Hkv, D, ps, 6, 9, 0.45, seed=900 + D + ps + G)
+    w.block_mask[1, 2, :] = False          # kv head 1, row block 2: no keys
+    o_ref, l_ref, a_ref = _bs_oracle(w)
+    for kw in [dict(), dict(launch="separate"), dict(deterministic=True, det_chunk_pages=1),
+               dict(launch="separate", deterministic=True, det_chunk_pages=2),
+               dict(min_chunk_pages=1), dict(pod_wide_blocks=1), dict(num_cus=3)]:
+        o, lse, p = _bs_run(w, dev, **kw)
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"block sparse D={D} ps={ps} G={G} {kw}")
+
+
+def test_block_sparse_full_mask_equals_append(dev):
+    """One row block and one column block, fully selected: the same attention
+    as a non-causal append of the whole sequence (GPU against GPU and the
+    oracle)."""
+    T, Lk, Hq, Hkv = 200, 1500, 32, 8
+    w = make_block_sparse(T, Lk, Hq, Hkv, 128, 16, 1, 1, 1.0, seed=950)
+    o, lse, _ = _bs_run(w, dev)
+    o_ref, l_ref, a_ref = _bs_oracle(w)
+    compare(o, lse, o_ref, l_ref, a_ref, what="block sparse full mask")
+    pa = fi.Plan("append", w.kv_indptr, w.kv_len, Hq, Hkv, 128, 16,
+                 qo_indptr=torch.tensor([0, T], dtype=torch.int32), causal=False, device=dev)
+    g = w.to(dev)
+    oa, la = fi.paged_append(pa, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale)
+    torch.cuda.synchronize()
+    compare(oa, la, o_ref, l_ref, a_ref, what="append over the same sequence")
+
+
+@pytest.mark.parametrize("launch", ["default", "separate"])
+def test_sparse_video_sampled(dev, launch):
+    """The video-shaped sparse self-attention batch (8192 tokens, 16 heads,
+    64 variable blocks per head): sampled query rows against the oracle."""
+    w = make_sparse_video(poison=True)
+    o, lse, p = _bs_run(w, dev, launch=launch)
+    rng = np.random.default_rng(41)
+    rows = sorted(set(rng.choice(w.q.shape[0], 48, replace=False).tolist()) | {0, 8191})
+    o_ref, l_ref, a_ref = _bs_oracle(w, rows=rows)
+    compare(o, lse, o_ref, l_ref, a_ref, rows=np.asarray(rows), what=f"sparse video {launch}")
 
 
 # ---------------------------------------------------------------- HIP graphs

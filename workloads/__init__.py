@@ -15,6 +15,9 @@ from .synth import (  # noqa: F401
     make_append,
     make_cascade,
     make_pod_mix,
+    make_block_sparse,
+    make_sparse_video,
+    SPARSE_VIDEO_NAME,
     POD_MIX_NAME,
     cascade_flat_tables,
     fp32_scale,

@@ -55,7 +55,7 @@ def fp32_scale(head_dim: int) -> float:
 @dataclass
 class Workload:
     name: str
-    kind: str                      # "decode" | "append" | "cascade"
+    kind: str                      # "decode" | "append" | "cascade" | "block_sparse"
     num_qo_heads: int
     num_kv_heads: int
     head_dim: int
@@ -81,6 +81,9 @@ class Workload:
     v_fp8: Optional[torch.Tensor] = None
     k_scale: Optional[torch.Tensor] = None    # fp32 [P, Hkv]
     v_scale: Optional[torch.Tensor] = None
+    row_block_sz: Optional[torch.Tensor] = None   # block_sparse: int32 [Hkv, MB]
+    col_block_sz: Optional[torch.Tensor] = None   # int32 [Hkv, NB]
+    block_mask: Optional[torch.Tensor] = None     # bool [Hkv, MB, NB]
 
     @property
     def batch(self) -> int:
@@ -341,6 +344,88 @@ def cascade_flat_tables(w: Workload):
         lens.append(L)
     return (_indptr(torch.tensor(counts)), torch.cat(idx).to(torch.int32),
             torch.tensor(lens, dtype=torch.int32))
+
+
+def _block_cuts(gen, total: int, n: int, align: int) -> torch.Tensor:
+    """n consecutive block sizes summing to ``total``, every non-empty block
+    starting at a multiple of ``align`` (the last may end anywhere); some
+    blocks may be empty."""
+    units = -(-total // align)
+    e = torch.sort(torch.randint(0, units + 1, (n - 1,), generator=gen)).values * align
+    e = torch.clamp(e, max=total)
+    edges = torch.cat([torch.zeros(1, dtype=torch.int64), e, torch.tensor([total])])
+    return torch.diff(edges).to(torch.int32)
+
+
+def make_block_sparse(qo_len: int, kv_len: int, num_qo_heads: int, num_kv_heads: int,
+                      head_dim: int, page_size: int, num_row_blocks: int, num_col_blocks: int,
+                      density: float, seed: int, poison: bool = True,
+                      name: str = "block_sparse", row_block_sz=None, col_block_sz=None,
+                      block_mask=None, _gen: Optional[torch.Generator] = None) -> Workload:
+    """One sequence of ``qo_len`` queries over ``kv_len`` keys with a variable
+    block partition and mask per kv head: random cut points (column cuts on
+    page boundaries), each (row block, column block) kept with probability
+    ``density``; explicit sizes or mask override the random ones. The
+    sequence's pages are placed by a seeded permutation of the pool."""
+    gen = _gen if _gen is not None else torch.Generator().manual_seed(seed)
+    Hkv = num_kv_heads
+    if row_block_sz is None:
+        row_block_sz = torch.stack([_block_cuts(gen, qo_len, num_row_blocks, 1)
+                                    for _ in range(Hkv)])
+    if col_block_sz is None:
+        col_block_sz = torch.stack([_block_cuts(gen, kv_len, num_col_blocks, page_size)
+                                    for _ in range(Hkv)])
+    row_block_sz = torch.as_tensor(row_block_sz, dtype=torch.int32).reshape(Hkv, -1)
+    col_block_sz = torch.as_tensor(col_block_sz, dtype=torch.int32).reshape(Hkv, -1)
+    MB, NB = row_block_sz.shape[1], col_block_sz.shape[1]
+    if block_mask is None:
+        block_mask = torch.rand((Hkv, MB, NB), generator=gen) < density
+    block_mask = torch.as_tensor(block_mask, dtype=torch.bool).reshape(Hkv, MB, NB)
+    n = -(-kv_len // page_size)
+    pool = _pool_size(n)
+    perm = torch.randperm(pool, generator=gen).to(torch.int32)
+    indices = perm[:n].clone()
+    q = _randn_bf16(gen, (qo_len, num_qo_heads, head_dim))
+    k = _randn_pool(gen, pool, Hkv, page_size, head_dim)
+    v = _randn_pool(gen, pool, Hkv, page_size, head_dim)
+    if poison:
+        tabs = [(indices, 0, kv_len)]
+        _poison_pool(k, indices, tabs)
+        _poison_pool(v, indices, tabs)
+    return Workload(name=name, kind="block_sparse", num_qo_heads=num_qo_heads,
+                    num_kv_heads=Hkv, head_dim=head_dim, page_size=page_size,
+                    sm_scale=fp32_scale(head_dim), seed=seed,
+                    kv_len=torch.tensor([kv_len], dtype=torch.int32),
+                    kv_indptr=torch.tensor([0, n], dtype=torch.int32), kv_indices=indices,
+                    q=q, k_cache=k, v_cache=v, row_block_sz=row_block_sz,
+                    col_block_sz=col_block_sz, block_mask=block_mask)
+
+
+SPARSE_VIDEO_NAME = "sparse_video_attention"
+
+
+def make_sparse_video(poison: bool = False, seed: Optional[int] = None) -> Workload:
+    """Block-sparse self-attention shaped like a video diffusion transformer's
+    sparse attention: 8192 tokens (queries = keys), 16 q / 16 kv heads (MHA),
+    D 128, page 16; per head the tokens are cut into 64 blocks of variable size
+    (multiples of 16 averaging 128) and a block pair is kept on the diagonal
+    band |a - b| <= 1 and with probability 0.15 elsewhere."""
+    seed = BASE_SEED + 200 if seed is None else seed
+    gen = torch.Generator().manual_seed(seed)
+    H, T, nb = 16, 8192, 64
+    sizes = []
+    for _ in range(H):
+        w = torch.randint(4, 13, (nb,), generator=gen).to(torch.float64)   # 64..192 tokens
+        edges = torch.round(torch.cumsum(w, 0) / w.sum() * (T // 16)).to(torch.int64)
+        edges = torch.cat([torch.zeros(1, dtype=torch.int64), edges])
+        sizes.append((torch.diff(edges) * 16).to(torch.int32))
+    sz = torch.stack(sizes)
+    a = torch.arange(nb)
+    band = (a[:, None] - a[None, :]).abs() <= 1
+    mask = band[None] | (torch.rand((H, nb, nb), generator=gen) < 0.15)
+    return make_block_sparse(T, T, H, H, 128, 16, nb, nb, 0.0, seed, poison,
+                             SPARSE_VIDEO_NAME, row_block_sz=sz, col_block_sz=sz,
+                             block_mask=mask, _gen=gen)
 
 
 POD_MIX_NAME = "pod_mixed"
