@@ -122,7 +122,7 @@ typedef struct fi_plan fi_plan_t;
  * pointers stay valid until fi_plan_destroy. Item and merge records are
  * FI_ITEM_INTS / FI_MERGE_INTS int32 each, field order as in fi_internal.h. */
 #define FI_ITEM_INTS 12
-#define FI_MERGE_INTS 5
+#define FI_MERGE_INTS 6
 typedef struct fi_plan_info {
   int32_t kind;
   int32_t num_levels;            /* 2 for cascade (prefix, suffix), else 1 */

@@ -44,8 +44,13 @@ be compared with it element for element:
    runs its chunks in the order it received them.
 5. Outputs. A unit with one chunk writes its final rows directly; otherwise
    each chunk writes fp32 partial rows (allocated in enumeration order) that a
-   merge folds in chunk order. Cascade writes partials for everything and
-   merges the prefix chunk(s) first, then the suffix chunks.
+   merge folds in chunk order. Merge records are ``(q_base, row0, n_rows,
+   kv_head, parts_off, n_parts)``: rows row0 .. row0+n_rows-1 of a unit (row
+   rho is query q_base + rho // G, head kv_head*G + rho % G), a unit's rows cut
+   into records of MERGE_ROWS = 16; part j of record row k is partial row
+   parts[parts_off + j] + k. Cascade writes partials for everything and
+   merges, per (request, kv head), the prefix chunk(s) first, then the suffix
+   chunks.
 6. Fused mixed batch (append, research note *Arithmetic intensity*: POD
    attention runs a batch's prefill and decode rows in one kernel). A request
    whose query rows (qo * G) fit one 16-row block belongs to the decode role
@@ -87,6 +92,7 @@ POD_WIDE_STEP = 4        # fused launch: time of a wide workgroup step ...
 POD_DECODE_STEP = 9      # ... and of a decode wavefront step
 POD_WIDE_ITEM_STEPS = 2  # starting a wide item, in wide steps
 POD_DECODE_ROWS = 16  # query rows of a request that runs in the decode role
+MERGE_ROWS = 16       # unit rows per merge record at most
 FLAG_LIST_Q = 1     # query rows come from the member list (cascade prefix)
 FLAG_PARTIAL = 2    # write fp32 partial rows instead of final rows
 FLAG_CAUSAL = 4     # bottom-right causal mask
@@ -369,7 +375,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
             r, g = u["unit"], u["g"]
             k, dsts = schunks[ui]
             plist = pref.get((r, g), []) + list(dsts)
-            merges.append((r, g * G, G, len(parts), len(plist)))
+            merges.append((r, 0, G, g, len(parts), len(plist)))
             parts.extend(plist)
     else:
         for units, chunks_of in zip(levels_units, unit_chunks):
@@ -377,13 +383,10 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                 k, dsts = chunks_of[ui]
                 if k == 1:
                     continue
-                r0, r1 = u["row0"], u["row0"] + u["n_rows"]
-                for i in range(r0 // G, (r1 - 1) // G + 1):
-                    a, b = max(r0, i * G), min(r1, (i + 1) * G)
-                    plist = [d + (a - r0) for d in dsts]
-                    merges.append((u["q_base"] + i, u["g"] * G + (a - i * G), b - a,
-                                   len(parts), len(plist)))
-                    parts.extend(plist)
+                for k0 in range(0, u["n_rows"], MERGE_ROWS):
+                    merges.append((u["q_base"], u["row0"] + k0,
+                                   min(MERGE_ROWS, u["n_rows"] - k0), u["g"], len(parts), k))
+                    parts.extend(d + k0 for d in dsts)
     out = dict(levels=levels, merges=merges, parts=parts, qlist=qlist, n_part_rows=next_row,
                plist=page_list)
     if kind != "decode" and pod_blocks is not None:

@@ -15,7 +15,7 @@ FI_KIND_DECODE, FI_KIND_APPEND, FI_KIND_CASCADE, FI_KIND_BLOCK_SPARSE = range(4)
 FI_DTYPE_BF16, FI_DTYPE_F32 = 0, 1
 FI_ENGINE_DEFAULT, FI_ENGINE_MFMA, FI_ENGINE_VALU = range(3)
 FI_LAUNCH_DEFAULT, FI_LAUNCH_POD, FI_LAUNCH_SEPARATE = range(3)
-FI_ITEM_INTS, FI_MERGE_INTS = 12, 5
+FI_ITEM_INTS, FI_MERGE_INTS = 12, 6
 
 STATUS_NAMES = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
                 3: "FI_ERR_WORKSPACE", 4: "FI_ERR_PLAN_MISMATCH", 5: "FI_ERR_HIP"}

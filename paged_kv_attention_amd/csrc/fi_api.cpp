@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 #include <utility>
 #include <vector>
@@ -120,6 +121,7 @@ fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
   m.num_qo_heads = p->hp.desc.num_qo_heads;
   m.head_dim = p->hp.desc.head_dim;
   m.group = p->hp.desc.num_qo_heads / p->hp.desc.num_kv_heads;
+  m.rows_per_record = p->hp.merge_rows;
   return hip_status(launch_merge(m, s), "merge launch");
 }
 

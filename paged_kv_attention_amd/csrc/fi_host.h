@@ -40,6 +40,7 @@ struct HostPlan {
   bool pod = false;
   int32_t pod_wide_blocks = 0;
   std::vector<int32_t> plist;    // block-sparse: the units' page lists
+  int32_t merge_rows = 0;        // the most rows of any merge record
 };
 
 // Byte offsets of each section inside the workspace blob.

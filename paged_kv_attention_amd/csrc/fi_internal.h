@@ -15,9 +15,10 @@
 //   9 dst      first fp32 partial row (FLAG_PARTIAL), else -1
 //  10 unit     request (or prefix group) id, informational
 //  11 chunk    chunk index within the unit, informational
-// Merge record (FI_MERGE_INTS = 5): q_tok, head0, n_heads, parts_off, n_parts;
-// head head0+k of token q_tok folds partial rows parts[parts_off+j]+k, j in
-// order. Scatter record (2 int32 per new token): index into kv_indices of the
+// Merge record (FI_MERGE_INTS = 6): q_base, row0, n_rows, kv_head, parts_off,
+// n_parts; row k < n_rows (at most MERGE_ROWS) is rho = row0 + k of a unit,
+// query token q_base + rho / G, head kv_head*G + rho % G, and folds partial
+// rows parts[parts_off+j]+k, j in order. Scatter record (2 int32 per new token): index into kv_indices of the
 // token's page, slot within the page.
 #pragma once
 
@@ -30,7 +31,7 @@ enum ItemField {
   F_Q_BASE = 0, F_ROW0, F_NROWS, F_KVHEAD, F_PAGEOFF, F_FLAGS,
   F_TBEGIN, F_TEND, F_QPOS0, F_DST, F_UNIT, F_CHUNK, ITEM_INTS
 };
-enum MergeField { M_QTOK = 0, M_HEAD0, M_NHEADS, M_OFF, M_N, MERGE_INTS };
+enum MergeField { M_QBASE = 0, M_ROW0, M_NROWS, M_KVHEAD, M_OFF, M_N, MERGE_INTS };
 enum ItemFlag { FLAG_LIST_Q = 1, FLAG_PARTIAL = 2, FLAG_CAUSAL = 4, FLAG_PREFIX = 8 };
 
 // Query rows per work item. Decode-style levels (decode, cascade suffix): one
@@ -39,6 +40,9 @@ enum ItemFlag { FLAG_LIST_Q = 1, FLAG_PARTIAL = 2, FLAG_CAUSAL = 4, FLAG_PREFIX 
 constexpr int ROWS_DECODE = 16;
 constexpr int ROWS_WIDE = 128;
 constexpr int WAVES_PER_BLOCK = 4;
+// Rows of a merge record at most (a unit's rows are cut into records of this
+// many).
+constexpr int MERGE_ROWS = 16;
 // A wide level plans num_cus * max(1, workers_per_cu / 2) workgroups and
 // chunks of at least WIDE_CHUNK_FACTOR * min_chunk_pages pages.
 constexpr int WIDE_CHUNK_FACTOR = 2;
@@ -77,7 +81,8 @@ struct MergeArgs {
   float* lse;
   int32_t num_qo_heads;
   int32_t head_dim;
-  int32_t group;   // q heads per kv head: no record has more rows
+  int32_t group;             // q heads per kv head
+  int32_t rows_per_record;   // the most rows any record has (<= MERGE_ROWS)
 };
 
 struct ScatterArgs {

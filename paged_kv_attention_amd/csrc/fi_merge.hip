@@ -72,15 +72,16 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   typedef typename FVec<FPL>::T vec;
   const int lane = threadIdx.x & 63;
   const int wv = blockIdx.x * WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int groups = (a.group + RPW - 1) / RPW;
+  const int groups = (a.rows_per_record + RPW - 1) / RPW;
   const int e = wv / groups;
-  const int h0 = (wv - e * groups) * RPW;
+  const int h0 = (wv - e * groups) * RPW;   // the wave's first row of the record
   if (e >= a.num_merges) return;
   const int32_t* m = a.merges + (int64_t)e * MERGE_INTS;
-  const int nh = ld_uniform(m, M_NHEADS);
+  const int nh = ld_uniform(m, M_NROWS);
   if (h0 >= nh) return;
   const int rows = min(RPW, nh - h0);
-  const int q_tok = ld_uniform(m, M_QTOK), head0 = ld_uniform(m, M_HEAD0);
+  const int q_base = ld_uniform(m, M_QBASE), row0 = ld_uniform(m, M_ROW0);
+  const int kv_head = ld_uniform(m, M_KVHEAD);
   const int off = ld_uniform(m, M_OFF), n = ld_uniform(m, M_N);
   const int32_t* parts = a.parts + off;
   const int rl = lane / LPR;                 // this lane's row within the wave
@@ -156,7 +157,9 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 #pragma unroll
   for (int r = 1; r < RPW; ++r) mr = (rl == r) ? M[r] : mr;
   const float inv = z > 0.f ? 1.f / z : 0.f;
-  const int64_t orow = (int64_t)q_tok * a.num_qo_heads + head0 + h0 + rl;
+  const int rho = row0 + h0 + rl;   // the unit row: query token and head
+  const int64_t orow = (int64_t)(q_base + rho / a.group) * a.num_qo_heads +
+                       kv_head * a.group + rho % a.group;
   uint16_t* op = a.o + orow * D + col;
   if constexpr (FPL == 1) {
     *op = (uint16_t)(pack2(acc * inv, 0.f) & 0xffffu);
@@ -234,9 +237,9 @@ hipError_t launch_merge_d(const MergeArgs& a, hipStream_t stream) {
   // Rows per wave: one while that keeps the wave count within about four per
   // SIMD of a 256-CU chip, else 2 or 4 (each wave's time is mostly load
   // latency, so fewer, fuller waves win once there are many records).
-  const int64_t rows = (int64_t)a.num_merges * a.group;
+  const int64_t rows = (int64_t)a.num_merges * a.rows_per_record;
   const int rpw = rows <= 4096 ? 1 : rows <= 8192 ? 2 : 4;
-  const int64_t waves = (int64_t)a.num_merges * ((a.group + rpw - 1) / rpw);
+  const int64_t waves = (int64_t)a.num_merges * ((a.rows_per_record + rpw - 1) / rpw);
   const dim3 grid((unsigned)((waves + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));
   if (rpw == 1) {
     hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(256), 0, stream, a);

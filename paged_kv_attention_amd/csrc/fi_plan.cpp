@@ -360,23 +360,21 @@ fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
   return FI_OK;
 }
 
-// Merge records of a level whose units write final rows unless split: a unit
-// of k != 1 chunks gets, per query token of its rows, a record over its
-// chunks' partial rows in chunk order (k = 0, no keys: an empty record, which
-// writes o = 0 and lse = -inf).
-void unit_merges(const std::vector<Unit>& units, const LevelBuild& lb, int32_t G, HostPlan& hp) {
+// Merge records of a level whose units write final rows unless split: the
+// rows of a unit of k != 1 chunks are cut into records of MERGE_ROWS rows,
+// each over its chunks' partial rows in chunk order (k = 0, no keys: empty
+// records, which write o = 0 and lse = -inf).
+void unit_merges(const std::vector<Unit>& units, const LevelBuild& lb, HostPlan& hp) {
   for (size_t ui = 0; ui < units.size(); ++ui) {
     const Unit& u = units[ui];
     const int32_t k = lb.chunks[ui].first;
     if (k == 1) continue;
     const std::vector<int32_t>& dsts = lb.chunks[ui].second;
-    const int32_t r0 = u.row0, r1 = u.row0 + u.n_rows;
-    for (int32_t i = r0 / G; i <= (r1 - 1) / G; ++i) {
-      const int32_t a = std::max(r0, i * G), b = std::min(r1, (i + 1) * G);
-      const int32_t rec[MERGE_INTS] = {u.q_base + i, u.g * G + (a - i * G), b - a,
-                                       (int32_t)hp.parts.size(), (int32_t)dsts.size()};
+    for (int32_t k0 = 0; k0 < u.n_rows; k0 += MERGE_ROWS) {
+      const int32_t rec[MERGE_INTS] = {u.q_base, u.row0 + k0, std::min(MERGE_ROWS, u.n_rows - k0),
+                                       u.g, (int32_t)hp.parts.size(), (int32_t)dsts.size()};
       hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
-      for (int32_t dd : dsts) hp.parts.push_back(dd + (a - r0));
+      for (int32_t dd : dsts) hp.parts.push_back(dd + k0);
     }
   }
 }
@@ -578,7 +576,7 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
       const std::vector<int32_t>& pl = pref[(size_t)u.unit * Hkv + u.g];
       const std::vector<int32_t>& dsts = lbs.chunks[ui].second;
       const int32_t n = (int32_t)(pl.size() + dsts.size());
-      const int32_t rec[MERGE_INTS] = {u.unit, u.g * G, G, (int32_t)hp.parts.size(), n};
+      const int32_t rec[MERGE_INTS] = {u.unit, 0, G, u.g, (int32_t)hp.parts.size(), n};
       hp.merges.insert(hp.merges.end(), rec, rec + MERGE_INTS);
       hp.parts.insert(hp.parts.end(), pl.begin(), pl.end());
       hp.parts.insert(hp.parts.end(), dsts.begin(), dsts.end());
@@ -614,7 +612,7 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
                     append ? qo_indptr : nullptr, causal);
       build_level(units[0], d, false, next_row, lb[0], hp.level[0]);
     }
-    for (int l = 0; l < hp.num_levels; ++l) unit_merges(units[l], lb[l], G, hp);
+    for (int l = 0; l < hp.num_levels; ++l) unit_merges(units[l], lb[l], hp);
     if (append) {
       for (int32_t r = 0; r < B; ++r) {
         const int32_t nq = qo_indptr[r + 1] - qo_indptr[r];
@@ -719,7 +717,7 @@ static fi_status build_block_sparse(const fi_plan_desc& d, int32_t qo_len, int32
     hp.num_levels = 1;
     build_level(units[0], d, false, next_row, lb[0], l0);
   }
-  for (int l = 0; l < hp.num_levels; ++l) unit_merges(units[l], lb[l], G, hp);
+  for (int l = 0; l < hp.num_levels; ++l) unit_merges(units[l], lb[l], hp);
   hp.num_part_rows = next_row;
   return FI_OK;
 }
@@ -760,6 +758,8 @@ static fi_status finish_plan(fi_plan_t* p, void* ws_dev, size_t ws_dev_bytes, vo
                              size_t ws_host_bytes, void* stream, fi_plan_t** out) {
   HostPlan& hp = p->hp;
   const fi_plan_desc& d = hp.desc;
+  for (size_t i = M_NROWS; i < hp.merges.size(); i += MERGE_INTS)
+    hp.merge_rows = std::max(hp.merge_rows, hp.merges[i]);
   size_t n_items[2] = {(size_t)hp.level[0].num_items(), (size_t)hp.level[1].num_items()};
   const int32_t workers[2] = {hp.level[0].num_workers, hp.level[1].num_workers};
   p->lay = layout_for(workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),

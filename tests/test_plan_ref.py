@@ -55,10 +55,11 @@ def check_outputs_once(plan, G, Hq, n_tokens):
         for rho in range(it[F["row0"]], it[F["row0"]] + it[F["n_rows"]]):
             covered[it[F["q_base"]] + rho // G, it[F["kv_head"]] * G + rho % G] += 1
     assert np.all(rows_used == 1)
-    for (qt, h0, nh, off, n) in plan["merges"]:
-        covered[qt, h0:h0 + nh] += 1
+    for (qb, row0, nr, g, off, n) in plan["merges"]:
+        for rho in range(row0, row0 + nr):
+            covered[qb + rho // G, g * G + rho % G] += 1
         for p in plan["parts"][off:off + n]:
-            assert 0 <= p and p + nh <= plan["n_part_rows"]
+            assert 0 <= p and p + nr <= plan["n_part_rows"]
     return covered
 
 
@@ -198,7 +199,7 @@ def test_small_batch_keeps_units_whole():
     p = plan_ref("decode", 8, 2, ps, indptr, L, S, [16])
     lv = p["levels"][0]
     # only the empty request's zero-part records (they write o = 0, lse = -inf)
-    assert all(m[4] == 0 for m in p["merges"]) and len(p["merges"]) == 2
+    assert all(m[5] == 0 for m in p["merges"]) and len(p["merges"]) == 2
     units = [(r, g) for r in range(len(lens)) for g in range(2)]
     for i, (r, g) in enumerate(units):
         its = lv["items"][lv["worker_indptr"][i]:lv["worker_indptr"][i + 1]]
@@ -210,4 +211,4 @@ def test_small_batch_keeps_units_whole():
     lens2 = [37, 300, 4096]
     indptr2, L2 = _decode_inputs(lens2, ps)
     p2 = plan_ref("decode", 8, 2, ps, indptr2, L2, S, [16])
-    assert any(m[4] > 1 for m in p2["merges"])
+    assert any(m[5] > 1 for m in p2["merges"])
