@@ -34,8 +34,11 @@
  * Streams: `stream` is a hipStream_t (NULL = default stream). Run calls only
  *   enqueue work and return; device faults surface at the caller's next
  *   synchronisation. Run calls neither allocate nor synchronise, so they may be
- *   captured in a HIP graph; a later fi_plan on the same workspace (same
- *   capacity) updates what a captured graph reads.
+ *   captured in a HIP graph. A captured call replays its plan; with a
+ *   graph-stable plan (fi_plan_desc.cap_batch > 0) it also serves every later
+ *   plan of the same description built into the same workspace (Ye et al.
+ *   record, "summary": load-balanced scheduling that stays valid under static
+ *   graph capture).
  * Errors: every call returns FI_OK (0) or an error code and launches nothing
  *   on error; fi_last_error() gives a thread-local message. Device-side arrays
  *   (kv_indices) are trusted to agree with the host arrays given to fi_plan.
@@ -114,6 +117,21 @@ typedef struct fi_plan_desc {
   int32_t launch;            /* fi_launch, append and cascade (default 0)      */
   int32_t pod_wide_blocks;   /* POD launch: workgroups of the wide role (0 =
                                 sized by the plan's cost model)              */
+  /* Graph-stable plan (cap_batch > 0; not for block-sparse plans): the
+   * workspace is laid out for at most cap_batch requests and these totals
+   * (the same bound fi_workspace_size gives for them, with batch =
+   * cap_batch), every launch is made and sized from these capacities, and the
+   * kernels read this batch's counts from the workspace. A run call captured
+   * in a HIP graph then serves any later plan with the same description (the
+   * batch and the number of prefix groups may change; max_prefix_depth is
+   * part of the capacity) built into the same workspace. fi_workspace_size on
+   * such a description returns that layout's size (its max_* arguments are
+   * not used). fi_plan fails with FI_ERR_INVALID_ARG if the batch exceeds a
+   * capacity. 0 = a plan laid out for its own batch. */
+  int32_t cap_batch;
+  int32_t cap_kv_pages;      /* sum of the requests' pages (suffix pages)     */
+  int32_t cap_qo_tokens;     /* append: sum of query tokens                   */
+  int32_t cap_prefix_pages;  /* cascade: sum of the groups' prefix pages      */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;

@@ -25,7 +25,8 @@ class PlanDesc(ctypes.Structure):
     _fields_ = [(n, c_int32) for n in (
         "kind", "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "causal",
         "deterministic", "det_chunk_pages", "min_chunk_pages", "num_cus", "workers_per_cu",
-        "num_prefix_groups", "decode_engine", "max_prefix_depth", "launch", "pod_wide_blocks")]
+        "num_prefix_groups", "decode_engine", "max_prefix_depth", "launch", "pod_wide_blocks", "cap_batch", "cap_kv_pages",
+        "cap_qo_tokens", "cap_prefix_pages")]
 
 
 I32P = POINTER(c_int32)

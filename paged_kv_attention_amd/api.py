@@ -76,7 +76,12 @@ def _prefix_depth(parent, ng: int) -> int:
 
 class Plan:
     """A work plan for one batch (fi_plan). ``device=None`` builds it on the
-    host only (needs ``num_cus``), which the run calls refuse."""
+    host only (needs ``num_cus``), which the run calls refuse. ``capacity =
+    (batch, kv_pages, qo_tokens, prefix_pages[, prefix_depth])`` makes it
+    graph-stable: laid out for at most those sizes (and nested prefixes at
+    most ``prefix_depth`` deep, default 1), so that a run call captured in a
+    HIP graph serves every later plan of the same kind and shape built into
+    the same ``workspace``."""
 
     def __init__(self, kind: str, kv_indptr, kv_len, num_qo_heads: int, num_kv_heads: int,
                  head_dim: int, page_size: int, *, qo_indptr=None, causal: bool = False,
@@ -84,7 +89,7 @@ class Plan:
                  deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
                  num_cus: int = 0, workers_per_cu: int = 0, engine: str = "default",
                  launch: str = "default", pod_wide_blocks: int = 0, device="cuda",
-                 workspace: Optional[Workspace] = None):
+                 workspace: Optional[Workspace] = None, capacity=None):
         lib = L.load()
         self.kind = kind
         self._ha = dict(kv_indptr=_host_i32(kv_indptr), kv_len=_host_i32(kv_len),
@@ -103,6 +108,10 @@ class Plan:
                                num_prefix_groups=ng, decode_engine=_ENGINES[engine],
                                max_prefix_depth=_prefix_depth(self._ha["prefix_parent"], ng),
                                launch=_LAUNCHES[launch], pod_wide_blocks=pod_wide_blocks)
+        if capacity is not None:
+            cap = [int(x) for x in capacity] + [1] * (5 - len(capacity))
+            (self.desc.cap_batch, self.desc.cap_kv_pages, self.desc.cap_qo_tokens,
+             self.desc.cap_prefix_pages, self.desc.max_prefix_depth) = cap
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim, self.page_size, self.batch = head_dim, page_size, B
         self.device = None if device is None else torch.device(device)
@@ -114,6 +123,7 @@ class Plan:
                 n_q = 0 if qo_indptr is None else int(self._ha["qo_indptr"][-1])
                 n_p = 0 if prefix_indptr is None else int(self._ha["prefix_indptr"][-1])
                 n_kv = int(self._ha["kv_indptr"][-1]) if B else 0
+                # (a graph-stable description sizes itself from its capacity)
                 db, hb = Workspace.bound(self.desc, n_kv, n_q, n_p)
                 self.workspace = Workspace(db, hb, self.device)
             ws_dev, ws_host = _ptr(self.workspace.dev), _ptr(self.workspace.host)

@@ -66,7 +66,9 @@ AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, 
   AttnArgs a;
   a.items = at<int32_t>(p, p->lay.items[level]);
   a.worker_indptr = at<int32_t>(p, p->lay.windptr[level]);
-  a.num_workers = p->hp.level[level].num_items() > 0 ? p->hp.level[level].num_workers : 0;
+  // a graph-stable plan launches every level whatever this batch holds
+  a.num_workers = (p->hp.stable || p->hp.level[level].num_items() > 0)
+                      ? p->hp.level[level].num_workers : 0;
   a.qlist = at<int32_t>(p, p->lay.qlist);
   a.q = (const uint16_t*)q;
   a.k_cache = (const uint16_t*)k;
@@ -112,7 +114,9 @@ hipError_t launch_fused(const fi_plan_t* p, const void* q, const void* k, const 
 fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
   MergeArgs m;
   m.merges = at<int32_t>(p, p->lay.merges);
-  m.num_merges = (int32_t)(p->hp.merges.size() / MERGE_INTS);
+  // launch sizing: the plan's records, or a graph-stable plan's capacity
+  m.num_merges = p->hp.stable ? (int32_t)p->hp.cap_merges
+                              : (int32_t)(p->hp.merges.size() / MERGE_INTS);
   m.parts = at<int32_t>(p, p->lay.parts);
   m.part_o = at<float>(p, p->lay.part_o);
   m.part_lse = at<float>(p, p->lay.part_lse);
@@ -121,7 +125,8 @@ fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
   m.num_qo_heads = p->hp.desc.num_qo_heads;
   m.head_dim = p->hp.desc.head_dim;
   m.group = p->hp.desc.num_qo_heads / p->hp.desc.num_kv_heads;
-  m.rows_per_record = p->hp.merge_rows;
+  m.rows_per_record = p->hp.stable ? MERGE_ROWS : p->hp.merge_rows;
+  m.counts = at<int32_t>(p, p->lay.meta);
   return hip_status(launch_merge(m, s), "merge launch");
 }
 
@@ -191,7 +196,9 @@ extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const vo
   if (k_new) {
     ScatterArgs sa;
     sa.scatter = at<int32_t>(p, p->lay.scatter);
-    sa.num_tokens = (int32_t)(p->hp.scatter.size() / 2);
+    sa.num_tokens = p->hp.stable ? (int32_t)p->hp.cap_scatter
+                                 : (int32_t)(p->hp.scatter.size() / 2);
+    sa.counts = at<int32_t>(p, p->lay.meta);
     sa.kv_indices = kv_indices;
     sa.k_new = (const uint16_t*)k_new;
     sa.v_new = (const uint16_t*)v_new;

@@ -41,13 +41,17 @@ struct HostPlan {
   int32_t pod_wide_blocks = 0;
   std::vector<int32_t> plist;    // block-sparse: the units' page lists
   int32_t merge_rows = 0;        // the most rows of any merge record
+  // graph-stable plan (capacity given in the description): a fixed layout,
+  // every launch made whatever the batch, sized by these capacities
+  bool stable = false;
+  int64_t cap_merges = 0, cap_scatter = 0;
 };
 
 // Byte offsets of each section inside the workspace blob.
 struct Layout {
   size_t items[2] = {0, 0}, windptr[2] = {0, 0};
   size_t merges = 0, parts = 0, qlist = 0, scatter = 0;
-  size_t meta = 0;           // int32 [0]: the pod split (workgroups of the wide role)
+  size_t meta = 0;           // int32 [META_INTS]: counts the kernels read
   size_t plist = 0;          // block-sparse page lists
   size_t blob_bytes = 0;     // int32 sections (host staging size)
   size_t part_o = 0, part_lse = 0;

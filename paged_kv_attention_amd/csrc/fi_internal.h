@@ -43,6 +43,11 @@ constexpr int WAVES_PER_BLOCK = 4;
 // Rows of a merge record at most (a unit's rows are cut into records of this
 // many).
 constexpr int MERGE_ROWS = 16;
+// Plan counts the kernels read from device memory (the plan's meta section),
+// so that a launch captured in a graph follows a later plan into the same
+// workspace: the POD split, the merge records, their most rows, and the new
+// tokens to scatter.
+enum MetaField { META_POD_WIDE = 0, META_MERGES, META_MERGE_ROWS, META_SCATTER, META_INTS };
 // A wide level plans num_cus * max(1, workers_per_cu / 2) workgroups and
 // chunks of at least WIDE_CHUNK_FACTOR * min_chunk_pages pages.
 constexpr int WIDE_CHUNK_FACTOR = 2;
@@ -82,12 +87,14 @@ struct MergeArgs {
   int32_t num_qo_heads;
   int32_t head_dim;
   int32_t group;             // q heads per kv head
-  int32_t rows_per_record;   // the most rows any record has (<= MERGE_ROWS)
+  int32_t rows_per_record;   // launch sizing: the most rows of a record (<= MERGE_ROWS)
+  const int32_t* counts;     // device meta: the record count and most rows per record
 };
 
 struct ScatterArgs {
   const int32_t* scatter;   // 2 int32 per new token
-  int32_t num_tokens;
+  int32_t num_tokens;       // launch sizing (the count itself is read from counts)
+  const int32_t* counts;    // device meta
   const int32_t* kv_indices;
   const uint16_t* k_new;
   const uint16_t* v_new;

@@ -13,10 +13,16 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "fi_internal.h"
 
 namespace fi {
 namespace {
+
+// Grid-stride kernels here launch at most this many workgroups (eight per CU
+// of a 256-CU chip); larger counts loop.
+constexpr int64_t kMaxLaunchBlocks = 2048;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -65,17 +71,11 @@ template <> struct FVec<1> { typedef float T; };
 // itself runs j = 0, 1, ... in order (z and acc each a plain left fold), so no
 // rounding depends on the batching or on which wave runs it.
 template <int D, int RPW>
-__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+__device__ __forceinline__ void merge_rows(const MergeArgs& a, int e, int h0, int lane) {
   constexpr int LPR = 64 / RPW;   // lanes per row
   constexpr int FPL = D / LPR;    // outputs per lane
   constexpr int kFold = FPL >= 8 ? 4 : FPL == 4 ? 8 : 16;   // parts in flight (32 floats)
   typedef typename FVec<FPL>::T vec;
-  const int lane = threadIdx.x & 63;
-  const int wv = blockIdx.x * WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int groups = (a.rows_per_record + RPW - 1) / RPW;
-  const int e = wv / groups;
-  const int h0 = (wv - e * groups) * RPW;   // the wave's first row of the record
-  if (e >= a.num_merges) return;
   const int32_t* m = a.merges + (int64_t)e * MERGE_INTS;
   const int nh = ld_uniform(m, M_NROWS);
   if (h0 >= nh) return;
@@ -173,6 +173,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (col == 0 && a.lse) a.lse[orow] = z > 0.f ? mr + logf(z) : neg_inf();
 }
 
+// Waves take (record, first row) pairs in turn, the record count and the most
+// rows of a record read from the plan in device memory; the grid is sized by
+// the host (from the plan, or its capacity).
+template <int D, int RPW>
+__global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int num_merges = ld_uniform(a.counts, META_MERGES);
+  const int groups = (ld_uniform(a.counts, META_MERGE_ROWS) + RPW - 1) / RPW;
+  const int64_t total = (int64_t)num_merges * groups;
+  const int64_t nw = (int64_t)gridDim.x * WAVES_PER_BLOCK;
+  for (int64_t wv = blockIdx.x * WAVES_PER_BLOCK + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+       wv < total; wv += nw) {
+    const int e = (int)(wv / groups);
+    merge_rows<D, RPW>(a, e, (int)(wv - (int64_t)e * groups) * RPW, lane);
+  }
+}
+
 // One wavefront per (n, h) row of fi_merge_states.
 __global__ __launch_bounds__(256) void merge_states_kernel(MergeStatesArgs a) {
   const int lane = threadIdx.x & 63;
@@ -215,21 +232,25 @@ __global__ __launch_bounds__(256) void merge_states_kernel(MergeStatesArgs a) {
   }
 }
 
-// One thread per 16 bytes of a new token's K (and the same bytes of V).
+// One thread per 16 bytes of a new token's K (and the same bytes of V), in a
+// grid-stride loop over the token count read from the plan.
 __global__ __launch_bounds__(256) void scatter_kernel(ScatterArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int cpr = a.head_dim / 8;                 // 16-byte chunks per head row
   const int cpt = a.num_kv_heads * cpr;           // per token
-  if (idx >= (int64_t)a.num_tokens * cpt) return;
-  const int tok = (int)(idx / cpt);
-  const int c = (int)(idx - (int64_t)tok * cpt);
-  const int g = c / cpr, dc = c - g * cpr;
-  const int page = a.kv_indices[a.scatter[2 * tok]];
-  const int slot = a.scatter[2 * tok + 1];
-  const int64_t dst = (((int64_t)page * a.num_kv_heads + g) * a.page_size + slot) * a.head_dim + dc * 8;
-  const int64_t src = ((int64_t)tok * a.num_kv_heads + g) * a.head_dim + dc * 8;
-  *(u32x4*)(a.k_cache + dst) = *(const u32x4*)(a.k_new + src);
-  *(u32x4*)(a.v_cache + dst) = *(const u32x4*)(a.v_new + src);
+  const int64_t n = (int64_t)ld_uniform(a.counts, META_SCATTER) * cpt;
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * 256) {
+    const int tok = (int)(idx / cpt);
+    const int c = (int)(idx - (int64_t)tok * cpt);
+    const int g = c / cpr, dc = c - g * cpr;
+    const int page = a.kv_indices[a.scatter[2 * tok]];
+    const int slot = a.scatter[2 * tok + 1];
+    const int64_t dst =
+        (((int64_t)page * a.num_kv_heads + g) * a.page_size + slot) * a.head_dim + dc * 8;
+    const int64_t src = ((int64_t)tok * a.num_kv_heads + g) * a.head_dim + dc * 8;
+    *(u32x4*)(a.k_cache + dst) = *(const u32x4*)(a.k_new + src);
+    *(u32x4*)(a.v_cache + dst) = *(const u32x4*)(a.v_new + src);
+  }
 }
 
 template <int D>
@@ -240,7 +261,8 @@ hipError_t launch_merge_d(const MergeArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_merges * a.rows_per_record;
   const int rpw = rows <= 4096 ? 1 : rows <= 8192 ? 2 : 4;
   const int64_t waves = (int64_t)a.num_merges * ((a.rows_per_record + rpw - 1) / rpw);
-  const dim3 grid((unsigned)((waves + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));
+  const dim3 grid((unsigned)std::min<int64_t>(kMaxLaunchBlocks,
+                                              (waves + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK));
   if (rpw == 1) {
     hipLaunchKernelGGL((merge_kernel<D, 1>), grid, dim3(256), 0, stream, a);
   } else if (rpw == 2) {
@@ -254,7 +276,7 @@ hipError_t launch_merge_d(const MergeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
-  if (a.num_merges == 0) return hipSuccess;
+  if (a.num_merges == 0 || a.rows_per_record == 0) return hipSuccess;
   if (a.head_dim == 128) return launch_merge_d<128>(a, stream);
   if (a.head_dim == 64) return launch_merge_d<64>(a, stream);
   return hipErrorInvalidValue;
@@ -271,7 +293,8 @@ hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream) {
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream) {
   const int64_t n = (int64_t)a.num_tokens * a.num_kv_heads * (a.head_dim / 8);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)std::min<int64_t>(kMaxLaunchBlocks, (n + 255) / 256)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -87,7 +87,7 @@ Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t 
   L.parts = take(n_parts);
   L.qlist = take(n_qlist);
   L.scatter = take(n_scatter * 2);
-  L.meta = take(1);
+  L.meta = take(META_INTS);
   L.plist = take(n_plist);
   L.blob_bytes = off;
   L.part_o = off;
@@ -421,6 +421,9 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.max_prefix_depth < 0) return set_error(FI_ERR_INVALID_ARG, "negative max_prefix_depth");
   if (d.max_prefix_depth == 0) d.max_prefix_depth = 1;
   if (d.pod_wide_blocks < 0) return set_error(FI_ERR_INVALID_ARG, "negative pod_wide_blocks");
+  if (d.cap_batch < 0 || d.cap_kv_pages < 0 || d.cap_qo_tokens < 0 || d.cap_prefix_pages < 0)
+    return set_error(FI_ERR_INVALID_ARG, "negative capacity");
+  if (d.kind == FI_KIND_BLOCK_SPARSE) d.cap_batch = 0;
   if (d.launch < FI_LAUNCH_DEFAULT || d.launch > FI_LAUNCH_SEPARATE)
     return set_error(FI_ERR_INVALID_ARG, "launch %d", d.launch);
   if (d.kind == FI_KIND_DECODE) {
@@ -754,17 +757,30 @@ static fi_status begin_plan(const fi_plan_desc* desc, void* ws_dev, void* ws_hos
 
 // Lay the built plan out, check the caller's workspace, and upload (the
 // pinned staging buffer is reused only after its previous upload was read).
-static fi_status finish_plan(fi_plan_t* p, void* ws_dev, size_t ws_dev_bytes, void* ws_host,
-                             size_t ws_host_bytes, void* stream, fi_plan_t** out) {
+struct Caps;
+static Layout caps_layout(const Caps& c, int32_t head_dim);
+static fi_status check_caps(const HostPlan& hp, const Caps& c);
+static fi_status finish_plan(fi_plan_t* p, const Caps* caps, void* ws_dev, size_t ws_dev_bytes,
+                             void* ws_host, size_t ws_host_bytes, void* stream,
+                             fi_plan_t** out) {
   HostPlan& hp = p->hp;
   const fi_plan_desc& d = hp.desc;
   for (size_t i = M_NROWS; i < hp.merges.size(); i += MERGE_INTS)
     hp.merge_rows = std::max(hp.merge_rows, hp.merges[i]);
   size_t n_items[2] = {(size_t)hp.level[0].num_items(), (size_t)hp.level[1].num_items()};
   const int32_t workers[2] = {hp.level[0].num_workers, hp.level[1].num_workers};
-  p->lay = layout_for(workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
-                      hp.qlist.size(), hp.scatter.size() / 2, (size_t)hp.num_part_rows,
-                      d.head_dim, hp.plist.size());
+  if (caps) {
+    const fi_status st = check_caps(hp, *caps);
+    if (st != FI_OK) {
+      delete p;
+      return st;
+    }
+    p->lay = caps_layout(*caps, d.head_dim);
+  } else {
+    p->lay = layout_for(workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
+                        hp.qlist.size(), hp.scatter.size() / 2, (size_t)hp.num_part_rows,
+                        d.head_dim, hp.plist.size());
+  }
   const Layout& L = p->lay;
   if (ws_dev) {
     if (ws_dev_bytes < L.dev_bytes || ws_host_bytes < L.blob_bytes) {
@@ -798,7 +814,10 @@ static fi_status finish_plan(fi_plan_t* p, void* ws_dev, size_t ws_dev_bytes, vo
     if (!hp.parts.empty()) memcpy(h + L.parts, hp.parts.data(), hp.parts.size() * 4);
     if (!hp.qlist.empty()) memcpy(h + L.qlist, hp.qlist.data(), hp.qlist.size() * 4);
     if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
-    memcpy(h + L.meta, &hp.pod_wide_blocks, 4);
+    const int32_t meta[META_INTS] = {hp.pod_wide_blocks,
+                                     (int32_t)(hp.merges.size() / MERGE_INTS), hp.merge_rows,
+                                     (int32_t)(hp.scatter.size() / 2)};
+    memcpy(h + L.meta, meta, sizeof(meta));
     if (!hp.plist.empty()) memcpy(h + L.plist, hp.plist.data(), hp.plist.size() * 4);
     e = hipMemcpyAsync(ws_dev, ws_host, L.blob_bytes, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) {
@@ -824,6 +843,110 @@ static fi_status finish_plan(fi_plan_t* p, void* ws_dev, size_t ws_dev_bytes, vo
 
 
 
+// Per-section capacities of any plan with this (defaults-filled) description,
+// at most d.batch requests and the given totals.
+struct Caps {
+  int32_t workers[2] = {0, 0};
+  size_t items[2] = {0, 0};
+  size_t merges = 0, parts = 0, qlist = 0, scatter = 0, part_rows = 0;
+};
+
+static void bound_counts(const fi_plan_desc& d, int32_t num_cus, int64_t max_kv_pages,
+                         int64_t max_qo_tokens, int64_t max_prefix_pages, Caps& c) {
+  const int64_t S_dec = (int64_t)num_cus * d.workers_per_cu;
+  const int64_t S_wide = (int64_t)num_cus * std::max(1, d.workers_per_cu / 2);
+  const int64_t B = d.batch, Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
+  const int64_t c_det = std::max(1, d.det_chunk_pages);
+  int64_t part_rows = 0, merges = 0;
+  // balanced: items <= S + units (every piece boundary is a quota or a unit
+  // boundary); deterministic: items <= pages / c + units
+  auto level_bound = [&](int64_t S, int64_t units, int64_t pages_sum, int64_t rpb) {
+    const int64_t items = d.deterministic ? pages_sum / c_det + units : S + units;
+    part_rows += items * rpb;
+    return items;
+  };
+  if (d.kind == FI_KIND_CASCADE) {
+    // groups with members: at most NG, and at most B * depth (each request
+    // is a member of at most depth groups; groups without members plan nothing)
+    const int64_t NG = std::min<int64_t>(d.num_prefix_groups, B * d.max_prefix_depth);
+    const int64_t blocks = ceil_div(B * G * d.max_prefix_depth, ROWS_WIDE) + NG;
+    c.items[0] = (size_t)level_bound(S_wide, blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_WIDE);
+    // a fused launch has 4 decode wavefronts on each of its S_wide workgroups
+    const int64_t S1 = d.launch == FI_LAUNCH_POD ? WAVES_PER_BLOCK * S_wide : S_dec;
+    c.items[1] = (size_t)level_bound(S1, B * Hkv, Hkv * max_kv_pages, ROWS_DECODE);
+    c.workers[0] = (int32_t)S_wide;
+    c.workers[1] = (int32_t)S1;
+    merges = B * Hkv;
+  } else if (d.kind == FI_KIND_APPEND && d.launch == FI_LAUNCH_POD) {
+    // wide role: at most P workgroups; decode role: at most 4P wavefronts
+    const int64_t P = S_wide;
+    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;
+    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + 1;
+    c.items[0] = (size_t)level_bound(P, blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
+                                     ROWS_WIDE);
+    c.items[1] = (size_t)level_bound(WAVES_PER_BLOCK * P, B * Hkv, Hkv * max_kv_pages,
+                                     ROWS_DECODE);
+    c.workers[0] = (int32_t)P;
+    c.workers[1] = (int32_t)(WAVES_PER_BLOCK * P);
+    merges = part_rows + (blocks + B) * Hkv * 2;
+  } else if (d.kind == FI_KIND_APPEND) {
+    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;
+    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + 1;
+    c.items[0] = (size_t)level_bound(S_wide, blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
+                                     ROWS_WIDE);
+    c.workers[0] = (int32_t)S_wide;
+    merges = part_rows + blocks * Hkv * 2;
+  } else {
+    const int64_t blocks = B * ceil_div(G, ROWS_DECODE);
+    c.items[0] = (size_t)level_bound(S_dec, blocks * Hkv,
+                                     Hkv * ceil_div(G, ROWS_DECODE) * max_kv_pages, ROWS_DECODE);
+    c.workers[0] = (int32_t)S_dec;
+    merges = part_rows + blocks * Hkv * 2;
+  }
+  c.merges = (size_t)merges;
+  c.parts = (size_t)part_rows;
+  c.part_rows = (size_t)part_rows;
+  c.scatter = d.kind == FI_KIND_APPEND ? (size_t)max_qo_tokens : 0;
+  c.qlist = (size_t)B * (d.kind == FI_KIND_CASCADE ? d.max_prefix_depth : 1);
+}
+
+// The capacities a graph-stable description (cap_batch > 0) lays its
+// workspace out for: cap_batch requests, the capped totals, and at most
+// cap_batch * max_prefix_depth prefix groups with members.
+static void stable_caps(const fi_plan_desc& d, int32_t num_cus, Caps& c) {
+  fi_plan_desc dc = d;
+  dc.batch = d.cap_batch;
+  dc.num_prefix_groups = d.cap_batch * d.max_prefix_depth;
+  bound_counts(dc, num_cus, d.cap_kv_pages, d.cap_qo_tokens, d.cap_prefix_pages, c);
+}
+
+static Layout caps_layout(const Caps& c, int32_t head_dim) {
+  return layout_for(c.workers, c.items, c.merges, c.parts, c.qlist, c.scatter, c.part_rows,
+                    head_dim);
+}
+
+// A built plan against the capacities of its graph-stable layout (a bound
+// that holds by construction; checked so that a broken bound is an error,
+// not an overrun).
+static fi_status check_caps(const HostPlan& hp, const Caps& c) {
+  for (int l = 0; l < 2; ++l)
+    if ((size_t)hp.level[l].num_items() > c.items[l] || hp.level[l].num_workers > c.workers[l])
+      return set_error(FI_ERR_WORKSPACE, "level %d exceeds its capacity", l);
+  if (hp.merges.size() / MERGE_INTS > c.merges || hp.parts.size() > c.parts ||
+      hp.qlist.size() > c.qlist || hp.scatter.size() / 2 > c.scatter ||
+      (size_t)hp.num_part_rows > c.part_rows)
+    return set_error(FI_ERR_WORKSPACE, "plan exceeds its capacity");
+  return FI_OK;
+}
+
+static fi_status device_cus(int32_t& num_cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return set_error(FI_ERR_HIP, "could not query the device's compute units");
+  return FI_OK;
+}
+
 extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_pages,
                                        int64_t max_qo_tokens, int64_t max_prefix_pages,
                                        size_t* dev_bytes, size_t* host_bytes) {
@@ -837,67 +960,13 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
   if (max_kv_pages < 0 || max_qo_tokens < 0 || max_prefix_pages < 0)
     return set_error(FI_ERR_INVALID_ARG, "negative size bound");
   int32_t num_cus = d.num_cus;
-  if (num_cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-            hipSuccess)
-      return set_error(FI_ERR_HIP, "could not query the device's compute units");
-  }
-  const int64_t S_dec = (int64_t)num_cus * d.workers_per_cu;
-  const int64_t S_wide = (int64_t)num_cus * std::max(1, d.workers_per_cu / 2);
-  const int64_t B = d.batch, Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
-  const int64_t c_det = std::max(1, d.det_chunk_pages);
-  size_t n_items[2] = {0, 0};
-  int32_t workers[2] = {0, 0};
-  int64_t part_rows = 0, merges = 0;
-  // balanced: items <= S + units (every piece boundary is a quota or a unit
-  // boundary); deterministic: items <= pages / c + units
-  auto level_bound = [&](int64_t S, int64_t units, int64_t pages_sum, int64_t rpb) {
-    const int64_t items = d.deterministic ? pages_sum / c_det + units : S + units;
-    part_rows += items * rpb;
-    return items;
-  };
-  if (d.kind == FI_KIND_CASCADE) {
-    const int64_t NG = d.num_prefix_groups;
-    const int64_t blocks = ceil_div(B * G * d.max_prefix_depth, ROWS_WIDE) + NG;
-    n_items[0] = (size_t)level_bound(S_wide, blocks * Hkv, blocks * Hkv * max_prefix_pages, ROWS_WIDE);
-    // a fused launch has 4 decode wavefronts on each of its S_wide workgroups
-    const int64_t S1 = d.launch == FI_LAUNCH_POD ? WAVES_PER_BLOCK * S_wide : S_dec;
-    n_items[1] = (size_t)level_bound(S1, B * Hkv, Hkv * max_kv_pages, ROWS_DECODE);
-    workers[0] = (int32_t)S_wide;
-    workers[1] = (int32_t)S1;
-    merges = B * Hkv;
-  } else if (d.kind == FI_KIND_APPEND && d.launch == FI_LAUNCH_POD) {
-    // wide role: at most P workgroups; decode role: at most 4P wavefronts
-    const int64_t P = S_wide;
-    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;
-    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + 1;
-    n_items[0] = (size_t)level_bound(P, blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
-                                     ROWS_WIDE);
-    n_items[1] = (size_t)level_bound(WAVES_PER_BLOCK * P, B * Hkv, Hkv * max_kv_pages,
-                                     ROWS_DECODE);
-    workers[0] = (int32_t)P;
-    workers[1] = (int32_t)(WAVES_PER_BLOCK * P);
-    merges = part_rows + (blocks + B) * Hkv * 2;
-  } else if (d.kind == FI_KIND_APPEND) {
-    const int64_t blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + B;
-    const int64_t per_req_blocks = ceil_div(max_qo_tokens * G, ROWS_WIDE) + 1;
-    n_items[0] = (size_t)level_bound(S_wide, blocks * Hkv, Hkv * per_req_blocks * max_kv_pages,
-                                     ROWS_WIDE);
-    workers[0] = (int32_t)S_wide;
-    merges = part_rows + blocks * Hkv * 2;
-  } else {
-    const int64_t blocks = B * ceil_div(G, ROWS_DECODE);
-    n_items[0] = (size_t)level_bound(S_dec, blocks * Hkv,
-                                     Hkv * ceil_div(G, ROWS_DECODE) * max_kv_pages, ROWS_DECODE);
-    workers[0] = (int32_t)S_dec;
-    merges = part_rows + blocks * Hkv * 2;
-  }
-  const size_t n_scatter = d.kind == FI_KIND_APPEND ? (size_t)max_qo_tokens : 0;
-  const size_t n_qlist = (size_t)B * (d.kind == FI_KIND_CASCADE ? d.max_prefix_depth : 1);
-  Layout L = layout_for(workers, n_items, (size_t)merges, (size_t)part_rows, n_qlist,
-                        n_scatter, (size_t)part_rows, d.head_dim);
+  if (num_cus == 0 && (st = device_cus(num_cus)) != FI_OK) return st;
+  Caps c;
+  if (d.cap_batch > 0)   // graph-stable: the layout its plans use, whatever the arguments
+    stable_caps(d, num_cus, c);
+  else
+    bound_counts(d, num_cus, max_kv_pages, max_qo_tokens, max_prefix_pages, c);
+  const Layout L = caps_layout(c, d.head_dim);
   *dev_bytes = L.dev_bytes;
   *host_bytes = L.blob_bytes;
   return FI_OK;
@@ -958,6 +1027,24 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
   if (st != FI_OK) return st;
   if (d.kind == FI_KIND_BLOCK_SPARSE)
     return set_error(FI_ERR_INVALID_ARG, "block-sparse plans are built by fi_plan_block_sparse");
+  const bool stable = d.cap_batch > 0;
+  Caps caps;
+  if (stable) {
+    // the batch must fit the capacity the workspace is laid out for
+    const int32_t B = d.batch;
+    const int64_t pages = B > 0 && kv_indptr_h ? kv_indptr_h[B] : 0;
+    const int64_t qo = d.kind == FI_KIND_APPEND && B > 0 && qo_indptr_h ? qo_indptr_h[B] : 0;
+    const int64_t ppages = d.kind == FI_KIND_CASCADE && d.num_prefix_groups > 0 && prefix_indptr_h
+                               ? prefix_indptr_h[d.num_prefix_groups] : 0;
+    if (B > d.cap_batch || pages > d.cap_kv_pages || qo > d.cap_qo_tokens ||
+        ppages > d.cap_prefix_pages)
+      return set_error(FI_ERR_INVALID_ARG,
+                       "batch exceeds the plan's capacity: %d requests / %lld pages / %lld "
+                       "query tokens / %lld prefix pages against %d / %d / %d / %d",
+                       B, (long long)pages, (long long)qo, (long long)ppages, d.cap_batch,
+                       d.cap_kv_pages, d.cap_qo_tokens, d.cap_prefix_pages);
+    stable_caps(d, d.num_cus, caps);
+  }
   fi_plan_t* p = new fi_plan_t();
   p->hp.desc = d;
   st = build(d, kv_indptr_h, kv_len_h, qo_indptr_h, prefix_indptr_h, prefix_len_h,
@@ -966,7 +1053,13 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
     delete p;
     return st;
   }
-  return finish_plan(p, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes, stream, out);
+  if (stable) {
+    p->hp.stable = true;
+    p->hp.cap_merges = (int64_t)caps.merges;
+    p->hp.cap_scatter = (int64_t)caps.scatter;
+  }
+  return finish_plan(p, stable ? &caps : nullptr, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes,
+                     stream, out);
 }
 
 extern "C" fi_status fi_plan_block_sparse(const fi_plan_desc* desc, int32_t qo_len,
@@ -993,7 +1086,7 @@ extern "C" fi_status fi_plan_block_sparse(const fi_plan_desc* desc, int32_t qo_l
     delete p;
     return st;
   }
-  return finish_plan(p, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes, stream, out);
+  return finish_plan(p, nullptr, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes, stream, out);
 }
 
 extern "C" void fi_plan_destroy(fi_plan_t* plan) { delete plan; }

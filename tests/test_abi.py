@@ -538,3 +538,50 @@ def test_block_sparse_plan_errors():
     d.causal = 1
     assert lib.fi_plan_block_sparse(ctypes.byref(d), 20, 100, 2, None, 3, None, None, None, None,
                                     0, None, 0, None, ctypes.byref(h)) == L.FI_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------- graph-stable plans
+
+
+@pytest.mark.parametrize("kind", ["decode", "append", "cascade"])
+def test_stable_plans_share_one_layout(kind):
+    """Plans of different batches under one capacity lay the workspace out
+    identically (the size fi_workspace_size reports for the description), so a
+    launch captured on one serves the others; a batch over a capacity is
+    refused."""
+    rng = np.random.default_rng(5)
+    ps, cap = 16, (12, 500, 600, 300)
+    sizes = set()
+    for trial in range(6):
+        B = int(rng.integers(1, 13))
+        lens = rng.integers(1, 600, B)
+        kw = dict(num_cus=6, capacity=cap)
+        if kind == "append":
+            qo = np.minimum(lens, rng.integers(1, 50, B))
+            kw.update(qo_indptr=_indptr(qo), causal=True)
+        if kind == "cascade":
+            ng = int(rng.integers(1, 4))
+            pi, pl = _decode_host([int(x) for x in rng.integers(0, 1200, ng)], ps)
+            kw.update(prefix_indptr=pi, prefix_len=pl, req_prefix_group=rng.integers(-1, ng, B))
+        indptr, L_ = _decode_host(lens, ps)
+        info = host_plan(kind, indptr, L_, 32, 8, 128, ps, **kw).info()
+        sizes.add((info["dev_bytes_used"], info["host_bytes_used"]))
+    assert len(sizes) == 1
+    d = L.PlanDesc(kind={"decode": 0, "append": 1, "cascade": 2}[kind], batch=1,
+                   num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=ps, num_cus=6,
+                   causal=int(kind == "append"), num_prefix_groups=2 if kind == "cascade" else 0,
+                   cap_batch=cap[0], cap_kv_pages=cap[1], cap_qo_tokens=cap[2],
+                   cap_prefix_pages=cap[3])
+    for args in ((0, 0, 0), (10, 20, 30)):     # the bound ignores its arguments
+        dev, host = fi.Workspace.bound(d, *args)
+        assert (dev, host) == sizes.pop() if args == (0, 0, 0) else (dev, host) == (dev0, host0)
+        dev0, host0 = dev, host
+    indptr, L_ = _decode_host([16 * 600], ps)                 # 600 pages > 500
+    kw = dict(num_cus=6, capacity=cap)
+    if kind == "append":
+        kw.update(qo_indptr=_indptr([1]))
+    if kind == "cascade":
+        pi, pl = _decode_host([16], ps)
+        kw.update(prefix_indptr=pi, prefix_len=pl, req_prefix_group=[0])
+    with pytest.raises(fi.FIError, match="capacity"):
+        host_plan(kind, indptr, L_, 32, 8, 128, ps, **kw)

@@ -579,6 +579,109 @@ def test_graph_replay_matches_eager(dev, cfg):
         assert torch.equal(other_o, ref_o)
 
 
+def _stage(buf, t):
+    """Copy t into the leading rows of a fixed buffer; return that view."""
+    v = buf[: t.shape[0]]
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("kind", ["decode", "append", "cascade"])
+def test_graph_follows_replan_into_stable_workspace(dev, kind):
+    """A run call captured once serves later batches: each batch is re-planned
+    into the same graph-stable workspace and its inputs copied into the same
+    buffers, and every replay equals the eager call on that batch, bit for
+    bit, whatever its size, split or POD role mix."""
+    Hq, Hkv, D, ps = 32, 8, 128, 16
+    if kind == "decode":
+        ws = [make_decode(L, Hq, Hkv, D, ps, seed=1000 + i, poison=False)
+              for i, L in enumerate([[700, 33, 2048, 5], [100] * 9 + [3000], [9]])]
+        cap = (10, 400, 0, 0)
+    elif kind == "append":
+        ws = [make_append(P, Q, Hq, Hkv, D, ps, seed=1100 + i, poison=False, causal=True)
+              for i, (P, Q) in enumerate([([900, 40, 2000], [1, 130, 2]),
+                                          ([50] * 6, [1] * 6),
+                                          ([3000, 10], [300, 64])])]
+        cap = (8, 400, 400, 0)
+    else:
+        ws = [make_cascade(P, grp, suf, Hq, Hkv, D, ps, seed=1200 + i, poison=False)
+              for i, (P, grp, suf) in enumerate([([1024], [0, 0, 0, -1], [100, 5, 300, 40]),
+                                                  ([2048, 64], [1, 0, 1, 0, 1, 0], [7] * 6),
+                                                  ([16], [0], [999])])]
+        cap = (8, 200, 0, 200)
+    maxP = max(w.num_pages for w in ws)
+    bufs = dict(q=torch.zeros(cap[0] * 64, Hq, D, dtype=torch.bfloat16, device=dev),
+                k=torch.zeros(maxP, Hkv, ps, D, dtype=torch.bfloat16, device=dev),
+                v=torch.zeros(maxP, Hkv, ps, D, dtype=torch.bfloat16, device=dev),
+                idx=torch.zeros(512, dtype=torch.int32, device=dev),
+                kn=torch.zeros(cap[0] * 64, Hkv, D, dtype=torch.bfloat16, device=dev),
+                vn=torch.zeros(cap[0] * 64, Hkv, D, dtype=torch.bfloat16, device=dev),
+                pidx=torch.zeros(512, dtype=torch.int32, device=dev),
+                o=torch.zeros(cap[0] * 64, Hq, D, dtype=torch.bfloat16, device=dev),
+                lse=torch.zeros(cap[0] * 64, Hq, dtype=torch.float32, device=dev))
+
+    def plan_of(w, workspace=None):
+        kw = dict(capacity=cap, device=dev, workspace=workspace)
+        if kind == "append":
+            kw.update(qo_indptr=w.qo_indptr, causal=True)
+        if kind == "cascade":
+            kw.update(prefix_indptr=w.prefix_indptr, prefix_len=w.prefix_len,
+                      req_prefix_group=w.req_prefix_group)
+        return fi.Plan(kind, w.kv_indptr, w.kv_len, Hq, Hkv, D, ps, **kw)
+
+    def stage(w):
+        g = w.to(dev)
+        q = _stage(bufs["q"], g.q)
+        bufs["k"][: w.num_pages].copy_(g.k_cache)
+        bufs["v"][: w.num_pages].copy_(g.v_cache)
+        idx = _stage(bufs["idx"], g.kv_indices)
+        pidx = _stage(bufs["pidx"], g.prefix_indices) if kind == "cascade" else None
+        new = None
+        if kind == "append":      # the new tokens' K/V, scattered by the call
+            new = (_stage(bufs["kn"], g.k_new), _stage(bufs["vn"], g.v_new))
+        return q, idx, pidx, new
+
+    def run(plan, q, idx, pidx, new):
+        T = q.shape[0]
+        o, lse = bufs["o"][:T], bufs["lse"][:T]
+        if kind == "decode":
+            fi.paged_decode(plan, q, bufs["k"], bufs["v"], idx, ws[0].sm_scale, out=o, lse=lse)
+        elif kind == "append":
+            fi.paged_append(plan, q, bufs["k"], bufs["v"], idx, ws[0].sm_scale, k_new=new[0],
+                            v_new=new[1], out=o, lse=lse)
+        else:
+            fi.cascade(plan, q, bufs["k"], bufs["v"], pidx, idx, ws[0].sm_scale, out=o, lse=lse)
+
+    p0 = plan_of(ws[0])
+    args0 = stage(ws[0])
+    graph = _capture(lambda: run(p0, *args0))
+    for rep, w in enumerate(ws[1:] + ws[:1]):
+        p = plan_of(w, workspace=p0.workspace)
+        args = stage(w)
+        T = args[0].shape[0]
+        run(p, *args)                                  # eager, on this batch
+        torch.cuda.synchronize()
+        ref_o, ref_l = bufs["o"][:T].clone(), bufs["lse"][:T].clone()
+        bufs["o"].fill_(7.0)
+        bufs["lse"].fill_(7.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs["o"][:T], ref_o), f"{kind} batch {rep}: outputs differ"
+        assert torch.equal(bufs["lse"][:T], ref_l), f"{kind} batch {rep}: lse differs"
+        o_ref, l_ref, a_ref = _stable_oracle(kind, w)
+        compare(bufs["o"][:T], bufs["lse"][:T], o_ref, l_ref, a_ref,
+                what=f"graph replay after re-plan, {kind} batch {rep}")
+
+
+def _stable_oracle(kind, w):
+    if kind == "decode":
+        return oracle_decode(w)
+    if kind == "append":
+        kp2, vp2 = _scattered_pools(w)
+        return _oracle_append(w, kp2, vp2, True)
+    return _oracle_cascade(w, None)
+
+
 # ---------------------------------------------------------------- FP8 cache
 
 
