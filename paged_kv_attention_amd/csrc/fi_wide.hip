@@ -97,44 +97,55 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4p)p));
 }
 
+// This lane's byte offsets, within a page tile, of the 16-byte slots it copies:
+// copy k of the wave (1-KiB block blk = wave*NK + k of the step's K, or V,
+// area) holds tokens blk*TPC .. +TPC-1 of the step, which share one page
+// (TPC divides a page), so a copy's page base is one scalar and the lane's
+// part (token slot in the page and swizzled chunk) is fixed for the kernel.
+template <int D, int NP>
+struct CopyLanes {
+  static constexpr int CH = Cfg<D>::CH, NK = Lds<D>::NK, ROW = Lds<D>::ROW;
+  static constexpr int TPC = 64 / CH;         // tokens per copy
+  static constexpr int TPP = 32 / NP;         // tokens of the step per page (NP > 1)
+  uint32_t k[NK], v[NK];
+  __device__ __forceinline__ CopyLanes(int wave, int lane) {
+#pragma unroll
+    for (int c = 0; c < NK; ++c) {
+      const int p = (wave * NK + c) * 64 + lane;    // 16-byte slot in the area
+      const int t = p / CH, cs = p % CH;            // token of the step, stored chunk slot
+      const int slot = t % TPP;                     // (NP = 1: plus the step's first slot)
+      k[c] = (uint32_t)(slot * ROW + (cs ^ (t % CH)) * 16);   // K: swizzled chunk
+      v[c] = (uint32_t)(slot * ROW + (cs ^ v_swizzle<D>(t)) * 16);
+    }
+  }
+};
+
 // Copy step s of item it into LDS stage st (this wave's share: NK 1-KiB
 // copies for K and NK for V).
 template <int D, int NP>
 __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, int s, char* stage,
-                                           int wave, int lane) {
-  constexpr int CH = Cfg<D>::CH, NK = Lds<D>::NK, ROW = Lds<D>::ROW;
+                                           int wave, const CopyLanes<D, NP>& cl) {
+  constexpr int NK = Lds<D>::NK, ROW = Lds<D>::ROW, TPC = CopyLanes<D, NP>::TPC;
   const int sh = a.page_shift;
   const int T0 = it.t_begin + 32 * s;
   const int pb = T0 >> sh;
   const int plast = (it.t_end - 1) >> sh;
   const int64_t tile_bytes = (int64_t)a.page_size * ROW;
-  int64_t poff[NP];
+  int pids[NP];   // the step's page ids, loaded together
 #pragma unroll
-  for (int n = 0; n < NP; ++n) {
-    const int pid = ld_uniform(it.plist, min(pb + n, plast));
-    poff[n] = ((int64_t)pid * a.num_kv_heads + it.g) * tile_bytes;
-  }
-  const int slot0 = (NP == 1) ? (T0 & (a.page_size - 1)) : 0;
+  for (int n = 0; n < NP; ++n) pids[n] = ld_uniform(it.plist, min(pb + n, plast));
 #pragma unroll
-  for (int k = 0; k < NK; ++k) {
-    const int blk = wave * NK + k;           // 1-KiB block of the area
-    const int p = blk * 64 + lane;           // 16-byte slot in the area
-    const int t = p / CH, cs = p % CH;       // token of the step, stored chunk slot
-    int64_t off;
-    if (NP == 1) {
-      off = poff[0] + (int64_t)(slot0 + t) * ROW;
-    } else if (NP == 2) {
-      off = (t >> 4 ? poff[1] : poff[0]) + (int64_t)(t & 15) * ROW;
-    } else {
-      const int rel = t >> 3;
-      off = (rel == 0 ? poff[0] : rel == 1 ? poff[1] : rel == 2 ? poff[2] : poff[3]) +
-            (int64_t)(t & 7) * ROW;
-    }
-    const int kc = cs ^ (t % CH);            // K: swizzled chunk
-    const int vc = cs ^ v_swizzle<D>(t);     // V: swizzled chunk
-    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.k_cache + off + kc * 16),
+  for (int c = 0; c < NK; ++c) {
+    const int blk = wave * NK + c;                       // 1-KiB block of the area
+    const int n = NP == 1 ? 0 : (blk * TPC) / (32 / NP);  // its page within the step
+    int pid = pids[0];
+#pragma unroll
+    for (int j = 1; j < NP; ++j) pid = (n == j) ? pids[j] : pid;
+    int64_t base = ((int64_t)pid * a.num_kv_heads + it.g) * tile_bytes;
+    if (NP == 1) base += (int64_t)(T0 & (a.page_size - 1)) * ROW;
+    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.k_cache + base + cl.k[c]),
                                      (lds_vptr)(stage + blk * 1024), 16, 0, kCopyPolicy);
-    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.v_cache + off + vc * 16),
+    __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.v_cache + base + cl.v[c]),
                                      (lds_vptr)(stage + Lds<D>::AREA + blk * 1024), 16, 0,
                                      kCopyPolicy);
   }
@@ -150,10 +161,11 @@ template <int D, int NP>
 __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int s, bool issue,
                                           char* __restrict__ next, const char* __restrict__ cur,
                                           const u32x4 (&qf)[2][Cfg<D>::KJ], State<D, 2>& st,
-                                          int rl0, int wave, int lane) {
+                                          int rl0, int wave, int lane,
+                                          const CopyLanes<D, NP>& cl) {
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL, CH = Cfg<D>::CH, ROW = Lds<D>::ROW;
   const int col = lane & 15, grp = lane >> 4;
-  if (issue) issue_step<D, NP>(a, it, s + kAhead, next, wave, lane);
+  if (issue) issue_step<D, NP>(a, it, s + kAhead, next, wave, cl);
   // row blocks of this wave that hold real rows (0, 1 or 2): a wave or block
   // of padding rows only takes part in the copies and barriers
   const int nmb = min(2, max(0, (it.n_rows - rl0 + 15) >> 4));
@@ -274,6 +286,7 @@ __device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
   if (wg >= a.num_workers) return;
   const int i_end = ld_uniform(a.worker_indptr, wg + 1);
   const int rl0 = wave * kRowsPerWave;
+  const CopyLanes<D, NP> cl(wave, lane);
 
   for (int i = ld_uniform(a.worker_indptr, wg); i < i_end; ++i) {
     const Item it = load_item(a, i);
@@ -295,7 +308,7 @@ __device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
-      wide_step<D, NP>(a, it, s, s + kAhead < n, next, cur, qf, st, rl0, wave, lane);
+      wide_step<D, NP>(a, it, s, s + kAhead < n, next, cur, qf, st, rl0, wave, lane, cl);
       return true;
     };
     constexpr int SB = Lds<D>::STAGE;
