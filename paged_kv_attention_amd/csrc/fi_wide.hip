@@ -210,6 +210,9 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
   // both row blocks' logits first: the second block's MFMAs then run under
   // the first block's softmax
   f32x4 sa[2][2];
+  // the matrix phase at raised priority, so that the SIMD's other wave (in
+  // its softmax) fills the vector unit meanwhile rather than competing
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     sa[mb][0] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -221,6 +224,7 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
       sa[mb][1] = mfma_bf16(kf[1][j], qf[mb][j], sa[mb][1]);
     }
   }
+  __builtin_amdgcn_s_setprio(0);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (mb >= nmb) continue;
