@@ -202,11 +202,14 @@ def explore(args, dev):
         w, name = make_sparse_video(poison=False), SPARSE_VIDEO_NAME
     else:
         w, name = make_config(args.config, poison=False), CONFIG_NAMES[args.config]
+    if args.kv != "bf16" and w.kind != "decode":
+        raise SystemExit(f"bench.py: --kv {args.kv} applies to the decode configurations")
     if args.kv == "fp8":
-        if w.kind != "decode":
-            raise SystemExit("bench.py: --kv fp8 applies to the decode configurations")
         from workloads import to_fp8_cache
         w = to_fp8_cache(w, poison=False)
+    elif args.kv == "mxfp4":
+        from workloads import to_mxfp4_cache
+        w = to_mxfp4_cache(w, poison=False)
     g = w.to(dev)
     kw = dict(deterministic=args.mode == "deterministic", workers_per_cu=args.workers_per_cu,
               min_chunk_pages=args.min_chunk_pages, det_chunk_pages=args.det_chunk_pages,
@@ -217,6 +220,10 @@ def explore(args, dev):
         if args.kv == "fp8":
             call = lambda: fi.paged_decode_fp8(plan, g.q, g.k_fp8, g.v_fp8, g.k_scale,  # noqa
                                                g.v_scale, g.kv_indices, w.sm_scale)
+        elif args.kv == "mxfp4":
+            call = lambda: fi.paged_decode_mxfp4(plan, g.q, g.k_fp4, g.v_fp4,  # noqa
+                                                 g.k_bscale, g.v_bscale, g.kv_indices,
+                                                 w.sm_scale)
         else:
             call = lambda: fi.paged_decode(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
                                            w.sm_scale)
@@ -268,7 +275,7 @@ def explore(args, dev):
         torch.cuda.synchronize()
     kern_ms = kt.total_ms / max(1, kt.calls)
     cold_us = cold_us_per_call(call, dev) if args.variants else None
-    kv = w.kv_bytes_fp8() if args.kv == "fp8" else w.kv_bytes()
+    kv = {"fp8": w.kv_bytes_fp8, "mxfp4": w.kv_bytes_mxfp4}.get(args.kv, w.kv_bytes)()
     extra = {}
     if w.kind != "decode":
         extra = {"launch": args.launch, "pod_wide_blocks": plan.info()["pod_wide_blocks"]}
@@ -298,7 +305,7 @@ def main():
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
-    ap.add_argument("--kv", choices=("bf16", "fp8"), default="bf16",
+    ap.add_argument("--kv", choices=("bf16", "fp8", "mxfp4"), default="bf16",
                     help="KV cache format for the exploratory decode lines (--config)")
     ap.add_argument("--no-variants", dest="variants", action="store_false",
                     help="skip the graph-replay, cold-cache and deterministic-mode context "

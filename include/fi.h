@@ -241,6 +241,20 @@ fi_status fi_paged_decode_fp8(const fi_plan_t* plan, const void* q, const void* 
                               const int32_t* kv_indices, float sm_scale, void* o, float* lse,
                               void* stream);
 
+/* Decode attention over an MXFP4 KV cache (v0.7.4 article, TL;DR: decoding
+ * from a 4-bit KV cache), gfx950's native 4-bit format: OCP microscaling FP4,
+ * E2M1 elements (0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives; sign in bit 3)
+ * with one E8M0 scale (2^(code - 127); 255 = NaN) per 32 consecutive
+ * elements of a token row. Plan kind FI_KIND_DECODE on the matrix-core
+ * engine. k_codes, v_codes: uint8 [pages][Hkv][page_size][D/2], element 2i
+ * in the low nibble of byte i; k_scales, v_scales: uint8
+ * [pages][Hkv][page_size][D/32], device memory; D = 64 or 128. The element
+ * is value(code) * 2^(scale - 127). q, o, lse as in fi_paged_decode. */
+fi_status fi_paged_decode_mxfp4(const fi_plan_t* plan, const void* q, const void* k_codes,
+                                const void* v_codes, const void* k_scales,
+                                const void* v_scales, const int32_t* kv_indices,
+                                float sm_scale, void* o, float* lse, void* stream);
+
 /* Append / prefill attention for a mixed batch (research note, "Arithmetic
  * intensity": prefill and decode rows of one batch). Plan kind
  * FI_KIND_APPEND. If k_new and v_new ([sum qo][Hkv][D] bf16) are non-NULL,

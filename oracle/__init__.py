@@ -20,8 +20,9 @@ Sources (the pages this follows; cited by title and section):
   a fixed order so results are deterministic.
 * "FlashInfer v0.7.4 Adds Rubin MoE Kernels and a Batch-Invariant Mode",
   *TL;DR*: decoding from a low-precision KV cache. The FP8 format itself is the
-  OCP 8-bit floating-point E4M3 definition (a published standard, not one of
-  the pages).
+  OCP 8-bit floating-point E4M3 definition, and the 4-bit one the OCP
+  microscaling (MX) FP4 E2M1 element with an E8M0 scale per 32 elements
+  (published standards, not among the pages).
 
 Parity status of each function is stated in its docstring ("pinned by" lists
 the tests in ``tests/test_oracle.py`` that tie it to something other than
@@ -36,6 +37,10 @@ from .attention import (  # noqa: F401
     paged_decode,
     paged_decode_fp8,
     e4m3_values,
+    e2m1_values,
+    e8m0_values,
+    mxfp4_dequantize,
+    paged_decode_mxfp4,
     paged_append,
     block_sparse,
     scatter_new_kv,

@@ -158,6 +158,64 @@ def paged_decode_fp8(q, k_codes, v_codes, k_scale, v_scale, kv_indptr, kv_indice
     return paged_decode(q, kp, vp, kv_indptr, idx, kv_len, page_size, sm_scale, requests=reqs)
 
 
+def e2m1_values():
+    """Value of every FP4 E2M1 code (index = code 0..15), float64. The format
+    is the OCP microscaling FP4 element: sign bit (bit 3), 2 exponent bits
+    (bias 1), 1 mantissa bit; exponent field 0 is subnormal, m/2; no
+    infinities or NaN (largest 6). Pinned by: the closed-form table
+    {0, 0.5, 1, 1.5, 2, 3, 4, 6} and its negatives."""
+    out = np.empty(16)
+    for c in range(16):
+        sign = -1.0 if c & 0x8 else 1.0
+        e, m = (c >> 1) & 0x3, c & 0x1
+        out[c] = sign * (m / 2.0 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1))
+    return out
+
+
+def e8m0_values():
+    """Value of every E8M0 scale code (index = code 0..255): 2^(code - 127),
+    NaN for 255 (OCP microscaling shared scale). Pinned by closed forms."""
+    out = 2.0 ** (np.arange(256, dtype=np.float64) - 127.0)
+    out[255] = np.nan
+    return out
+
+
+def mxfp4_dequantize(codes, scales):
+    """Elements of MXFP4 rows: ``codes [..., D/2]`` uint8 (element 2i in the
+    low nibble of byte i, 2i+1 in the high nibble), ``scales [..., D/32]``
+    uint8 E8M0, one per 32 consecutive elements; returns ``[..., D]`` float64,
+    value = e2m1(code) * 2^(scale - 127). Pinned by: bytes built from known
+    elements, the nibble order, and a NaN scale."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    lo, hi = codes & 0xF, codes >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    vals = e2m1_values()[nib]
+    sc = e8m0_values()[np.asarray(scales, dtype=np.uint8)]
+    return vals * np.repeat(sc, 32, axis=-1)
+
+
+def paged_decode_mxfp4(q, k_codes, v_codes, k_scales, v_scales, kv_indptr, kv_indices, kv_len,
+                       page_size: int, sm_scale: float, requests=None):
+    """Decode attention over an MXFP4 cache (v0.7.4 article, TL;DR: decoding
+    from a 4-bit KV cache): K and V elements are mxfp4_dequantize of the
+    pools' codes and scales in fp64, and the result is exactly paged_decode
+    over those values. Only the pages of the selected requests are decoded.
+    Pinned by: equality with paged_decode over pools dequantized by an
+    independent route (integer bit fields of each code), and the element
+    layout pins of mxfp4_dequantize."""
+    B = q.shape[0]
+    reqs = _req_list(B, requests)
+    pages = np.unique(np.concatenate(
+        [np.asarray(kv_indices[int(kv_indptr[r]):int(kv_indptr[r + 1])]) for r in reqs]
+        + [np.zeros(0, dtype=np.int64)]).astype(np.int64))
+    kp = mxfp4_dequantize(np.asarray(k_codes)[pages], np.asarray(k_scales)[pages])
+    vp = mxfp4_dequantize(np.asarray(v_codes)[pages], np.asarray(v_scales)[pages])
+    remap = np.zeros(int(np.asarray(k_codes).shape[0]), dtype=np.int64)
+    remap[pages] = np.arange(pages.size)
+    idx = remap[np.asarray(kv_indices, dtype=np.int64)]
+    return paged_decode(q, kp, vp, kv_indptr, idx, kv_len, page_size, sm_scale, requests=reqs)
+
+
 def paged_append(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
                  page_size: int, sm_scale: float, causal: bool = True, requests=None):
     """Attention for ``qo`` new query tokens per request over ``kv_len`` keys

@@ -17,4 +17,5 @@ from .api import (  # noqa: F401
     paged_append,
     paged_decode,
     paged_decode_fp8,
+    paged_decode_mxfp4,
 )

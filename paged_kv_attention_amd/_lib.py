@@ -57,6 +57,9 @@ SIGNATURES = {
     "fi_paged_decode_fp8": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                       c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                       c_void_p]),
+    "fi_paged_decode_mxfp4": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_float, c_void_p, c_void_p,
+                                        c_void_p]),
     "fi_paged_append": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_float, c_void_p, c_void_p, c_void_p]),
     "fi_cascade": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

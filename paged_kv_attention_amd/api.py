@@ -321,6 +321,34 @@ def paged_decode_fp8(plan: Plan, q, k_cache, v_cache, k_scale, v_scale, kv_indic
     return out, lse
 
 
+def paged_decode_mxfp4(plan: Plan, q, k_codes, v_codes, k_scales, v_scales, kv_indices,
+                       sm_scale: float, out=None, lse=None, return_lse: bool = True):
+    """fi_paged_decode_mxfp4: K/V as MXFP4 codes (uint8 [P, Hkv, ps, D/2], two
+    E2M1 elements per byte, low nibble first) with E8M0 scales (uint8
+    [P, Hkv, ps, D/32], one per 32 elements); q, out, lse as paged_decode."""
+    _check_run(plan, "decode")
+    _check_tensor(q, "q", torch.bfloat16, plan.device,
+                  (plan.batch, plan.num_qo_heads, plan.head_dim))
+    D = plan.head_dim
+    _check_tensor(k_codes, "k_codes", torch.uint8, plan.device)
+    P = k_codes.shape[0]
+    _check_tensor(k_codes, "k_codes", torch.uint8, plan.device,
+                  (P, plan.num_kv_heads, plan.page_size, D // 2))
+    _check_tensor(v_codes, "v_codes", torch.uint8, plan.device, k_codes.shape)
+    sshape = (P, plan.num_kv_heads, plan.page_size, D // 32)
+    _check_tensor(k_scales, "k_scales", torch.uint8, plan.device, sshape)
+    _check_tensor(v_scales, "v_scales", torch.uint8, plan.device, sshape)
+    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    if lse is None and return_lse:
+        lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
+    out, lse = _outputs(plan, q, out, lse)
+    L.check(L.load().fi_paged_decode_mxfp4(plan.handle, _ptr(q), _ptr(k_codes), _ptr(v_codes),
+                                           _ptr(k_scales), _ptr(v_scales), _ptr(kv_indices),
+                                           float(sm_scale), _ptr(out), _ptr(lse),
+                                           _stream(plan.device)), "fi_paged_decode_mxfp4")
+    return out, lse
+
+
 def paged_append(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, k_new=None,
                  v_new=None, out=None, lse=None, return_lse: bool = True):
     """fi_paged_append: q [sum qo, Hq, D]; optional k_new/v_new [sum qo, Hkv, D]

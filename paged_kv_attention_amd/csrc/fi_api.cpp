@@ -81,6 +81,8 @@ AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, 
   a.part_lse = at<float>(p, p->lay.part_lse);
   a.k_scale = nullptr;
   a.v_scale = nullptr;
+  a.k_bscale = nullptr;
+  a.v_bscale = nullptr;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.num_qo_heads = d.num_qo_heads;
   a.num_kv_heads = d.num_kv_heads;
@@ -173,6 +175,33 @@ extern "C" fi_status fi_paged_decode_fp8(const fi_plan_t* p, const void* q, cons
   a.v_scale = v_scale;
   TimerScope t(s);
   st = hip_status(launch_decode_fp8(a, p->hp.desc.head_dim, s), "attention launch");
+  t.done();
+  if (st != FI_OK) return st;
+  return run_merge(p, o, lse, s);
+}
+
+extern "C" fi_status fi_paged_decode_mxfp4(const fi_plan_t* p, const void* q, const void* k_codes,
+                                           const void* v_codes, const void* k_scales,
+                                           const void* v_scales, const int32_t* kv_indices,
+                                           float sm_scale, void* o, float* lse, void* stream) {
+  clear_error();
+  if (!(sm_scale > 0.f) || !isfinite(sm_scale))
+    return set_error(FI_ERR_INVALID_ARG,
+                     "fi_paged_decode_mxfp4: sm_scale must be finite and > 0, got %g",
+                     (double)sm_scale);
+  fi_status st = check_plan(p, FI_KIND_DECODE, "fi_paged_decode_mxfp4");
+  if (st != FI_OK) return st;
+  if (p->hp.desc.decode_engine != FI_ENGINE_MFMA)
+    return set_error(FI_ERR_UNSUPPORTED, "fi_paged_decode_mxfp4 runs on the matrix-core engine");
+  if (p->hp.desc.batch > 0 &&
+      (!q || !k_codes || !v_codes || !k_scales || !v_scales || !kv_indices || !o))
+    return set_error(FI_ERR_INVALID_ARG, "fi_paged_decode_mxfp4: NULL tensor pointer");
+  hipStream_t s = (hipStream_t)stream;
+  AttnArgs a = attn_args(p, 0, q, k_codes, v_codes, kv_indices, nullptr, sm_scale, o, lse);
+  a.k_bscale = (const uint8_t*)k_scales;
+  a.v_bscale = (const uint8_t*)v_scales;
+  TimerScope t(s);
+  st = hip_status(launch_decode_mxfp4(a, p->hp.desc.head_dim, s), "attention launch");
   t.done();
   if (st != FI_OK) return st;
   return run_merge(p, o, lse, s);

@@ -68,6 +68,8 @@ struct AttnArgs {
   float* part_lse;
   const float* k_scale;    // FP8 cache only: [pages][Hkv] fp32 scale of each K tile
   const float* v_scale;    // FP8 cache only: the same for V
+  const uint8_t* k_bscale; // MXFP4 cache only: E8M0 scale per 32 elements of a K row
+  const uint8_t* v_bscale; // MXFP4 cache only: the same for V
   float scale_log2;        // sm_scale * log2(e): logits are kept in base 2
   int32_t num_qo_heads;
   int32_t num_kv_heads;
@@ -119,6 +121,7 @@ struct MergeStatesArgs {
 hipError_t launch_decode(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_valu(const AttnArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_fp8(const AttnArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_mxfp4(const AttnArgs& a, int head_dim, hipStream_t stream);
 // Wide level: one 4-wave workgroup per worker (a.num_workers workgroups);
 // list_q: query rows come through the member list (cascade prefix).
 hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream);

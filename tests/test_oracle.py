@@ -536,6 +536,105 @@ def test_fp8_decode_equals_decode_of_torch_dequantized_pools():
 
 
 # ---------------------------------------------------------------------------
+# MXFP4 (E2M1 elements, E8M0 block scales) cache
+
+
+def test_e2m1_closed_forms():
+    """The eight FP4 E2M1 magnitudes of the OCP microscaling format, in code
+    order, then the same with the sign bit (bit 3) set; no NaN or infinity."""
+    v = A.e2m1_values()
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert list(v[:8]) == mags
+    assert list(v[8:]) == [-m for m in mags]
+    assert np.signbit(v[8]) and not np.signbit(v[0])
+    assert np.isfinite(v).all()
+
+
+def test_e8m0_values_match_torch_for_every_code():
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).double().numpy()
+    got = A.e8m0_values()
+    assert np.isnan(got[255]) and np.isnan(ref[255]) and np.isnan(got).sum() == 1
+    assert np.array_equal(got[:255], ref[:255])
+    assert got[127] == 1.0 and got[128] == 2.0 and got[0] == 2.0 ** -127
+    assert got[254] == 2.0 ** 127
+
+
+def test_mxfp4_dequantize_nibble_order_and_scale_blocks():
+    # byte 0x21: element 0 = code 1 (0.5), element 1 = code 2 (1.0)
+    codes = np.zeros((1, 32), dtype=np.uint8)
+    codes[0, 0] = 0x21
+    codes[0, 17] = 0xF7          # element 34 = code 7 (6), element 35 = code 15 (-6)
+    scales = np.array([[127, 130]], dtype=np.uint8)     # 1 for dims 0..31, 8 for 32..63
+    d = A.mxfp4_dequantize(codes, scales)
+    assert d.shape == (1, 64)
+    want = np.zeros(64)
+    want[0], want[1], want[34], want[35] = 0.5, 1.0, 48.0, -48.0
+    assert np.array_equal(d[0], want)
+    # the scale of element i is block i // 32 (not i % n_blocks)
+    codes[0, :] = 0x22           # every element 1.0
+    d = A.mxfp4_dequantize(codes, scales)
+    assert np.array_equal(d[0, :32], np.ones(32)) and np.array_equal(d[0, 32:], np.full(32, 8.0))
+    # a NaN scale poisons exactly its 32 elements
+    d = A.mxfp4_dequantize(codes, np.array([[255, 127]], dtype=np.uint8))
+    assert np.isnan(d[0, :32]).all() and np.array_equal(d[0, 32:], np.ones(32))
+
+
+def mxfp4_case(seed=4, ps=16, D=64, Hq=8, Hkv=2, lens=(1, 17, 40, 100)):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    n = [-(-L // ps) for L in lens]
+    P = sum(n) + 3
+    indptr = np.concatenate([[0], np.cumsum(n)])
+    indices = rng.permutation(P)[:sum(n)]
+    kc = rng.integers(0, 256, (P, Hkv, ps, D // 2), dtype=np.uint8)
+    vc = rng.integers(0, 256, (P, Hkv, ps, D // 2), dtype=np.uint8)
+    ks = rng.integers(120, 128, (P, Hkv, ps, D // 32), dtype=np.uint8)
+    vs = rng.integers(124, 134, (P, Hkv, ps, D // 32), dtype=np.uint8)
+    q = rng.standard_normal((B, Hq, D))
+    return q, kc, vc, ks, vs, indptr, indices, np.array(lens), ps
+
+
+def _dequantize_by_fields(codes, scales):
+    """Element by element from the integer bit fields of each code: sign bit 3,
+    exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0 is m * 2^-1."""
+    P, H, ps, nb = codes.shape
+    D = 2 * nb
+    out = np.empty((P, H, ps, D))
+    for idx in np.ndindex(P, H, ps):
+        for i in range(D):
+            c = (int(codes[idx][i // 2]) >> (4 * (i % 2))) & 0xF
+            e, m = (c >> 1) & 3, c & 1
+            mag = m * 0.5 if e == 0 else (2 + m) * 2.0 ** (e - 2)
+            out[idx][i] = (-mag if c & 8 else mag) * math.ldexp(1.0, int(scales[idx][i // 32]) - 127)
+    return out
+
+
+def test_mxfp4_decode_equals_decode_of_field_dequantized_pools():
+    q, kc, vc, ks, vs, indptr, indices, L, ps = mxfp4_case()
+    kp, vp = _dequantize_by_fields(kc, ks), _dequantize_by_fields(vc, vs)
+    scale = 0.125
+    o_ref, l_ref = A.paged_decode(q, kp, vp, indptr, indices, L, ps, scale)
+    o, lse = A.paged_decode_mxfp4(q, kc, vc, ks, vs, indptr, indices, L, ps, scale)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, l_ref, rtol=1e-14, atol=0)
+    o2, l2 = A.paged_decode_mxfp4(q, kc, vc, ks, vs, indptr, indices, L, ps, scale,
+                                  requests=[0, 2])
+    np.testing.assert_array_equal(o2[[0, 2]], o[[0, 2]])
+    assert np.isnan(o2[[1, 3]]).all()
+
+
+def test_mxfp4_planted_mistakes_fail_the_pins():
+    """A nibble swap or an off-by-one scale bias in the dequantization is seen
+    by the field-by-field route."""
+    q, kc, vc, ks, vs, indptr, indices, L, ps = mxfp4_case(seed=6)
+    kp = _dequantize_by_fields(kc, ks)
+    swapped = ((kc & 0xF) << 4) | (kc >> 4)
+    assert not np.array_equal(A.mxfp4_dequantize(swapped, ks), kp)
+    assert not np.array_equal(A.mxfp4_dequantize(kc, ks + 1), kp)
+    assert np.array_equal(A.mxfp4_dequantize(kc, ks), kp)
+
+
+# ---------------------------------------------------------------------------
 # variable block-sparse attention
 
 

@@ -6,6 +6,8 @@ seeded; inputs are poisoned (NaN in unused pages, 1e4 in tail slots, NaN in
 not-yet-written append slots) so that a stray read shows up in the output.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -15,7 +17,8 @@ import paged_kv_attention_amd as fi
 from tests.helpers import (compare, gpu_decode, np_pools, oracle_decode, request_rows,
                            sample_requests)
 from workloads import (cascade_flat_tables, make_append, make_block_sparse, make_cascade,
-                       make_config, make_decode, make_pod_mix, make_sparse_video, to_fp8_cache)
+                       make_config, make_decode, make_pod_mix, make_sparse_video, to_fp8_cache,
+                       to_mxfp4_cache)
 
 pytestmark = pytest.mark.gpu
 
@@ -733,6 +736,78 @@ def test_fp8_decode_refuses_the_valu_engine(dev):
     w = to_fp8_cache(make_decode([40, 7], 8, 2, 64, 16, seed=9, poison=False), poison=True)
     with pytest.raises(fi.FIError, match="matrix-core"):
         _fp8_run(w, dev, engine="valu")
+
+
+# ---------------------------------------------------------------- MXFP4 cache
+
+
+def _fp4_oracle(w, requests=None):
+    args = (w.kv_indptr.numpy(), w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size,
+            w.sm_scale)
+    q = w.q.double().numpy()
+    kc, vc = w.k_fp4.numpy(), w.v_fp4.numpy()
+    ks, vs = w.k_bscale.numpy(), w.v_bscale.numpy()
+    o, lse = oracle.paged_decode_mxfp4(q, kc, vc, ks, vs, *args, requests=requests)
+    a, _ = oracle.paged_decode_mxfp4(q, kc, vc & 0x77, ks, vs, *args, requests=requests)  # |V|
+    return o, lse, a
+
+
+def _fp4_run(w, dev, **kw):
+    p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                w.page_size, device=dev, **kw)
+    g = w.to(dev)
+    o, lse = fi.paged_decode_mxfp4(p, g.q, g.k_fp4, g.v_fp4, g.k_bscale, g.v_bscale,
+                                   g.kv_indices, w.sm_scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_mxfp4_llama_decode_sampled(dev):
+    w = to_mxfp4_cache(make_config(1, poison=False), poison=True)
+    rng = np.random.default_rng(22)
+    reqs = sample_requests(w.batch, 8, rng, must=[int(torch.argmax(w.kv_len))])
+    o_ref, l_ref, a_ref = _fp4_oracle(w, reqs)
+    for det in (False, True):
+        o, lse = _fp4_run(w, dev, deterministic=det)
+        compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs),
+                what=f"mxfp4 llama det={det}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_mxfp4_decode_small_sweep(dev, D, ps, G):
+    Hkv = 2
+    w = to_mxfp4_cache(make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=600 + D + ps + G,
+                                   poison=False), poison=True)
+    o_ref, l_ref, a_ref = _fp4_oracle(w)
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+        o, lse = _fp4_run(w, dev, **kw)
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"mxfp4 decode D={D} ps={ps} G={G} {kw}")
+
+
+def test_mxfp4_decode_extreme_scales(dev):
+    """Block scales spread far from 1 and different in every 32-element block
+    of a row (K 2^-9 .. 2^0, V 2^-27 .. 2^23): each block's elements must take
+    their own scale, exactly. Outputs are compared after division by one
+    power of two (exact on both sides) so the absolute bar stays meaningful."""
+    w = to_mxfp4_cache(make_decode([70, 33, 5], 8, 2, 128, 16, seed=61, poison=False),
+                       poison=True)
+    gen = torch.Generator().manual_seed(62)
+    kb = torch.randint(118, 128, w.k_bscale.shape, generator=gen, dtype=torch.int32)
+    vb = torch.randint(100, 151, w.v_bscale.shape, generator=gen, dtype=torch.int32)
+    w.k_bscale = torch.where(w.k_bscale != 255, kb.to(torch.uint8), w.k_bscale)
+    w.v_bscale = torch.where(w.v_bscale != 255, vb.to(torch.uint8), w.v_bscale)
+    o_ref, l_ref, a_ref = _fp4_oracle(w)
+    o, lse = _fp4_run(w, dev)
+    c = 2.0 ** math.ceil(math.log2(np.abs(a_ref).max()))
+    compare(o.double() / c, lse, o_ref / c, l_ref, a_ref / c, what="mxfp4 extreme scales")
+
+
+def test_mxfp4_decode_refuses_the_valu_engine(dev):
+    w = to_mxfp4_cache(make_decode([40, 7], 8, 2, 64, 16, seed=9, poison=False), poison=True)
+    with pytest.raises(fi.FIError, match="matrix-core"):
+        _fp4_run(w, dev, engine="valu")
 
 
 # ---------------------------------------------------------------- prefix trees

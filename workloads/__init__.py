@@ -22,4 +22,5 @@ from .synth import (  # noqa: F401
     cascade_flat_tables,
     fp32_scale,
     to_fp8_cache,
+    to_mxfp4_cache,
 )

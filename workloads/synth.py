@@ -81,6 +81,10 @@ class Workload:
     v_fp8: Optional[torch.Tensor] = None
     k_scale: Optional[torch.Tensor] = None    # fp32 [P, Hkv]
     v_scale: Optional[torch.Tensor] = None
+    k_fp4: Optional[torch.Tensor] = None      # MXFP4 E2M1 codes, uint8 [P, Hkv, ps, D/2]
+    v_fp4: Optional[torch.Tensor] = None
+    k_bscale: Optional[torch.Tensor] = None   # E8M0 block scales, uint8 [P, Hkv, ps, D/32]
+    v_bscale: Optional[torch.Tensor] = None
     row_block_sz: Optional[torch.Tensor] = None   # block_sparse: int32 [Hkv, MB]
     col_block_sz: Optional[torch.Tensor] = None   # int32 [Hkv, NB]
     block_mask: Optional[torch.Tensor] = None     # bool [Hkv, MB, NB]
@@ -106,6 +110,11 @@ class Workload:
     def kv_bytes_fp8(self) -> int:
         """K+V bytes of one pass over the FP8 cache (one byte per element)."""
         return self.kv_bytes() // 2
+
+    def kv_bytes_mxfp4(self) -> int:
+        """K+V bytes of one pass over the MXFP4 cache: D/2 code bytes and
+        D/32 scale bytes per token row, i.e. 17/64 of the bf16 bytes."""
+        return self.kv_bytes() * 17 // 64
 
     def kv_bytes(self) -> int:
         """Algorithmic K+V bytes one pass reads: exactly kv_len tokens per
@@ -203,13 +212,7 @@ def to_fp8_cache(w: Workload, poison: bool = True) -> Workload:
     codes = torch's round-to-nearest-even E4M3 (``float8_e4m3fn``) of x / scale.
     ``w`` should be built without poison; with ``poison`` the codes of unused
     pages and of slots past each sequence's end are the NaN code 0x7F."""
-    P, Hkv, ps, D = w.k_cache.shape
-    used = torch.zeros(P, ps, dtype=torch.bool)      # (page, slot) holds a token
-    for r in range(w.batch):
-        a, L = int(w.kv_indptr[r]), int(w.kv_len[r])
-        for j in range(-(-L // ps)):
-            page = int(w.kv_indices[a + j])
-            used[page, :min(ps, L - j * ps)] = True
+    used = _used_slots(w)                            # (page, slot) holds a token
 
     def quant(pool):
         x = pool.float()
@@ -224,6 +227,67 @@ def to_fp8_cache(w: Workload, poison: bool = True) -> Workload:
     vc, vsc = quant(w.v_cache)
     kw = {f.name: getattr(w, f.name) for f in fields(w)}
     kw.update(k_fp8=kc, v_fp8=vc, k_scale=ksc, v_scale=vsc, name=w.name + "_fp8")
+    return Workload(**kw)
+
+
+def _used_slots(w: Workload) -> torch.Tensor:
+    """bool [pages, page_size]: the (page, slot) pairs that hold a token of
+    some request of ``w``."""
+    P, _, ps, _ = w.k_cache.shape
+    used = torch.zeros(P, ps, dtype=torch.bool)
+    for r in range(w.batch):
+        a, L = int(w.kv_indptr[r]), int(w.kv_len[r])
+        for j in range(-(-L // ps)):
+            page = int(w.kv_indices[a + j])
+            used[page, :min(ps, L - j * ps)] = True
+    return used
+
+
+# Midpoints between consecutive E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+_E2M1_CUTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+def to_mxfp4_cache(w: Workload, poison: bool = True, pages_per_chunk: int = 4096) -> Workload:
+    """``w`` plus an MXFP4 copy of its K/V pools. Each token row of D elements
+    is cut into D/32 blocks of 32; a block with max |x| = m > 0 gets the E8M0
+    scale code 127 + s with s the smallest integer such that m / 2^s <= 6 (6
+    is the largest E2M1 magnitude; code 127, scale 1, for an all-zero block),
+    and each element the E2M1 code of the magnitude nearest to |x| / 2^s (ties
+    to the smaller one) with the sign of x in bit 3. Codes are packed two per
+    byte, element 2i in the low nibble. ``w`` should be built without poison;
+    with ``poison`` the scale of every unused slot is 255 (NaN) and its codes
+    0xFF."""
+    P, Hkv, ps, D = w.k_cache.shape
+    used = _used_slots(w)
+    cuts = torch.tensor(_E2M1_CUTS, dtype=torch.float32)
+
+    def quant(pool):
+        codes = torch.empty(P, Hkv, ps, D // 2, dtype=torch.uint8)
+        scales = torch.empty(P, Hkv, ps, D // 32, dtype=torch.uint8)
+        for p0 in range(0, P, pages_per_chunk):
+            p1 = min(P, p0 + pages_per_chunk)
+            x = pool[p0:p1].float().reshape(p1 - p0, Hkv, ps, D // 32, 32)
+            m = x.abs().amax(dim=-1).double()
+            mant, ex = torch.frexp(m / 6.0)               # m / 6 = mant * 2^ex, mant in [0.5, 1)
+            s = torch.where(mant == 0.5, ex - 1, ex).to(torch.int64)
+            s = torch.where(m > 0, s, torch.zeros_like(s)).clamp(-127, 127)
+            mag = (x.abs() * torch.pow(2.0, -s.to(torch.float32))[..., None]).clamp(max=6.0)
+            c = torch.bucketize(mag, cuts).to(torch.uint8) | ((x < 0).to(torch.uint8) << 3)
+            c = c.reshape(p1 - p0, Hkv, ps, D)
+            cb = c[..., 0::2] | (c[..., 1::2] << 4)
+            sc = (s + 127).to(torch.uint8)
+            if poison:
+                u = used[p0:p1, None, :, None]
+                cb = torch.where(u, cb, torch.full_like(cb, 0xFF))
+                sc = torch.where(u, sc, torch.full_like(sc, 255))
+            codes[p0:p1] = cb
+            scales[p0:p1] = sc
+        return codes, scales
+
+    kc, ks = quant(w.k_cache)
+    vc, vs = quant(w.v_cache)
+    kw = {f.name: getattr(w, f.name) for f in fields(w)}
+    kw.update(k_fp4=kc, v_fp4=vc, k_bscale=ks, v_bscale=vs, name=w.name + "_mxfp4")
     return Workload(**kw)
 
 
