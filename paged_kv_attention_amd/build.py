@@ -36,9 +36,18 @@ COMMON = [
 ]
 
 
+# Per-file extras. The MXFP4 decode kernel keeps its MFMA accumulators in
+# ordinary VGPRs: in the AGPR form the compiler copies all 32 of them between
+# the two register files on every step (the lazy rescale multiplies them on
+# the VALU), which that ALU-bound kernel cannot afford.
+EXTRA = {
+    "fi_decode_fp4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -767,10 +767,10 @@ def test_mxfp4_llama_decode_sampled(dev):
     rng = np.random.default_rng(22)
     reqs = sample_requests(w.batch, 8, rng, must=[int(torch.argmax(w.kv_len))])
     o_ref, l_ref, a_ref = _fp4_oracle(w, reqs)
-    for det in (False, True):
-        o, lse = _fp4_run(w, dev, deterministic=det)
+    for kw in (dict(), dict(deterministic=True), dict(workers_per_cu=8)):
+        o, lse = _fp4_run(w, dev, **kw)
         compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs),
-                what=f"mxfp4 llama det={det}")
+                what=f"mxfp4 llama {kw}")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -781,7 +781,8 @@ def test_mxfp4_decode_small_sweep(dev, D, ps, G):
     w = to_mxfp4_cache(make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=600 + D + ps + G,
                                    poison=False), poison=True)
     o_ref, l_ref, a_ref = _fp4_oracle(w)
-    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
+               dict(workers_per_cu=8, min_chunk_pages=1), dict(workers_per_cu=12)]:
         o, lse = _fp4_run(w, dev, **kw)
         compare(o, lse, o_ref, l_ref, a_ref, what=f"mxfp4 decode D={D} ps={ps} G={G} {kw}")
 
