@@ -216,7 +216,7 @@ def explore(args, dev):
               engine=args.engine)
     if w.kind == "decode":
         plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
-                       w.head_dim, w.page_size, device=dev, **kw)
+                       w.head_dim, w.page_size, device=dev, kv_format=args.kv, **kw)
         if args.kv == "fp8":
             call = lambda: fi.paged_decode_fp8(plan, g.q, g.k_fp8, g.v_fp8, g.k_scale,  # noqa
                                                g.v_scale, g.kv_indices, w.sm_scale)

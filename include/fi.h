@@ -95,6 +95,16 @@ typedef enum fi_launch {
   FI_LAUNCH_SEPARATE = 2  /* one launch per kind of rows                      */
 } fi_launch;
 
+/* KV cache format that a decode plan's run calls will read. It only picks
+ * the default launch shape (workers_per_cu): results do not depend on it,
+ * and any decode plan may be run with any of the decode calls. */
+typedef enum fi_kv_format {
+  FI_KV_BF16 = 0,   /* fi_paged_decode: 4 workers per CU (one wave per SIMD)  */
+  FI_KV_FP8 = 1,    /* fi_paged_decode_fp8: 4                                 */
+  FI_KV_MXFP4 = 2   /* fi_paged_decode_mxfp4: 12 (three waves per SIMD; that
+                       kernel is bound by ALU work and latency, not by HBM)   */
+} fi_kv_format;
+
 /* Plan description. Zero in an optional field selects its default. */
 typedef struct fi_plan_desc {
   int32_t kind;              /* fi_kind                                        */
@@ -108,7 +118,8 @@ typedef struct fi_plan_desc {
   int32_t det_chunk_pages;   /* deterministic chunk size in pages (default 48) */
   int32_t min_chunk_pages;   /* balanced mode lower bound on chunk pages (default 8) */
   int32_t num_cus;           /* compute units to plan for (0 = current device) */
-  int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 4) */
+  int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 4;
+                                12 for a decode plan of format FI_KV_MXFP4) */
   int32_t num_prefix_groups; /* cascade: number of shared prefixes             */
   int32_t decode_engine;     /* fi_engine for decode-style levels (default 0)  */
   int32_t max_prefix_depth;  /* cascade: longest chain of nested shared prefixes
@@ -132,6 +143,7 @@ typedef struct fi_plan_desc {
   int32_t cap_kv_pages;      /* sum of the requests' pages (suffix pages)     */
   int32_t cap_qo_tokens;     /* append: sum of query tokens                   */
   int32_t cap_prefix_pages;  /* cascade: sum of the groups' prefix pages      */
+  int32_t kv_format;         /* decode: fi_kv_format (default FI_KV_BF16)     */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;
@@ -250,10 +262,10 @@ fi_status fi_paged_decode_fp8(const fi_plan_t* plan, const void* q, const void* 
  * in the low nibble of byte i; k_scales, v_scales: uint8
  * [pages][Hkv][page_size][D/32], device memory; D = 64 or 128. The element
  * is value(code) * 2^(scale - 127). q, o, lse as in fi_paged_decode.
- * This kernel is bound by ALU work and latency more than by HBM: a plan with
- * workers_per_cu = 12 (three waves per SIMD) runs it about 1.2x faster than
- * the default plan (4, one wave per SIMD); any plan gives the same results
- * up to rounding. */
+ * This kernel is bound by ALU work and latency more than by HBM: a plan of
+ * kv_format FI_KV_MXFP4 (default workers_per_cu 12, three waves per SIMD)
+ * runs it about 1.2x faster than a bf16 plan (4, one wave per SIMD); any
+ * decode plan gives the same results up to rounding. */
 fi_status fi_paged_decode_mxfp4(const fi_plan_t* plan, const void* q, const void* k_codes,
                                 const void* v_codes, const void* k_scales,
                                 const void* v_scales, const int32_t* kv_indices,

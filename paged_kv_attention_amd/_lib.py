@@ -15,6 +15,7 @@ FI_KIND_DECODE, FI_KIND_APPEND, FI_KIND_CASCADE, FI_KIND_BLOCK_SPARSE = range(4)
 FI_DTYPE_BF16, FI_DTYPE_F32 = 0, 1
 FI_ENGINE_DEFAULT, FI_ENGINE_MFMA, FI_ENGINE_VALU = range(3)
 FI_LAUNCH_DEFAULT, FI_LAUNCH_POD, FI_LAUNCH_SEPARATE = range(3)
+FI_KV_BF16, FI_KV_FP8, FI_KV_MXFP4 = range(3)
 FI_ITEM_INTS, FI_MERGE_INTS = 12, 6
 
 STATUS_NAMES = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
@@ -26,7 +27,7 @@ class PlanDesc(ctypes.Structure):
         "kind", "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "causal",
         "deterministic", "det_chunk_pages", "min_chunk_pages", "num_cus", "workers_per_cu",
         "num_prefix_groups", "decode_engine", "max_prefix_depth", "launch", "pod_wide_blocks", "cap_batch", "cap_kv_pages",
-        "cap_qo_tokens", "cap_prefix_pages")]
+        "cap_qo_tokens", "cap_prefix_pages", "kv_format")]
 
 
 I32P = POINTER(c_int32)

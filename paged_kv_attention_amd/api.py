@@ -20,6 +20,7 @@ _KINDS = {"decode": L.FI_KIND_DECODE, "append": L.FI_KIND_APPEND, "cascade": L.F
 _ENGINES = {"default": L.FI_ENGINE_DEFAULT, "mfma": L.FI_ENGINE_MFMA, "valu": L.FI_ENGINE_VALU}
 _LAUNCHES = {"default": L.FI_LAUNCH_DEFAULT, "pod": L.FI_LAUNCH_POD,
              "separate": L.FI_LAUNCH_SEPARATE}
+_KV_FORMATS = {"bf16": L.FI_KV_BF16, "fp8": L.FI_KV_FP8, "mxfp4": L.FI_KV_MXFP4}
 
 
 def _host_i32(x) -> Optional[np.ndarray]:
@@ -76,7 +77,9 @@ def _prefix_depth(parent, ng: int) -> int:
 
 class Plan:
     """A work plan for one batch (fi_plan). ``device=None`` builds it on the
-    host only (needs ``num_cus``), which the run calls refuse. ``capacity =
+    host only (needs ``num_cus``), which the run calls refuse. ``kv_format``
+    ("bf16", "fp8" or "mxfp4") names the cache a decode plan will be run on:
+    it only picks the default ``workers_per_cu`` (12 for "mxfp4", else 4). ``capacity =
     (batch, kv_pages, qo_tokens, prefix_pages[, prefix_depth])`` makes it
     graph-stable: laid out for at most those sizes (and nested prefixes at
     most ``prefix_depth`` deep, default 1), so that a run call captured in a
@@ -88,8 +91,8 @@ class Plan:
                  prefix_indptr=None, prefix_len=None, req_prefix_group=None, prefix_parent=None,
                  deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
                  num_cus: int = 0, workers_per_cu: int = 0, engine: str = "default",
-                 launch: str = "default", pod_wide_blocks: int = 0, device="cuda",
-                 workspace: Optional[Workspace] = None, capacity=None):
+                 launch: str = "default", pod_wide_blocks: int = 0, kv_format: str = "bf16",
+                 device="cuda", workspace: Optional[Workspace] = None, capacity=None):
         lib = L.load()
         self.kind = kind
         self._ha = dict(kv_indptr=_host_i32(kv_indptr), kv_len=_host_i32(kv_len),
@@ -107,7 +110,8 @@ class Plan:
                                num_cus=num_cus, workers_per_cu=workers_per_cu,
                                num_prefix_groups=ng, decode_engine=_ENGINES[engine],
                                max_prefix_depth=_prefix_depth(self._ha["prefix_parent"], ng),
-                               launch=_LAUNCHES[launch], pod_wide_blocks=pod_wide_blocks)
+                               launch=_LAUNCHES[launch], pod_wide_blocks=pod_wide_blocks,
+                               kv_format=_KV_FORMATS[kv_format])
         if capacity is not None:
             cap = [int(x) for x in capacity] + [1] * (5 - len(capacity))
             (self.desc.cap_batch, self.desc.cap_kv_pages, self.desc.cap_qo_tokens,

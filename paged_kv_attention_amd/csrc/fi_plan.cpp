@@ -438,7 +438,12 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.launch != FI_LAUNCH_POD) d.pod_wide_blocks = 0;
   if (d.det_chunk_pages == 0) d.det_chunk_pages = 48;   // fastest of 8..64 on the five batches
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
-  if (d.workers_per_cu == 0) d.workers_per_cu = 4;
+  if (d.kv_format < FI_KV_BF16 || d.kv_format > FI_KV_MXFP4)
+    return set_error(FI_ERR_INVALID_ARG, "kv_format %d", d.kv_format);
+  if (d.kind != FI_KIND_DECODE) d.kv_format = FI_KV_BF16;
+  // one wave per SIMD for the register-ring decode kernels; three for the
+  // MXFP4 kernel, which staging through LDS leaves ALU- and latency-bound
+  if (d.workers_per_cu == 0) d.workers_per_cu = d.kv_format == FI_KV_MXFP4 ? 12 : 4;
   d.causal = d.causal ? 1 : 0;
   d.deterministic = d.deterministic ? 1 : 0;
   if (d.kind != FI_KIND_APPEND) d.causal = 0;   // (block-sparse: refused above if set)

@@ -183,6 +183,36 @@ def test_launch_defaults():
                   launch="pod", pod_wide_blocks=-1)
 
 
+def test_kv_format_picks_the_default_worker_count():
+    """A decode plan for an MXFP4 cache defaults to 12 workers per CU, bf16
+    and FP8 plans to 4; an explicit count wins; other plan kinds ignore the
+    field; an unknown format is refused."""
+    d_indptr, d_len = _decode_host([100, 2000, 37], 16)
+    for fmt, wpc in (("bf16", 4), ("fp8", 4), ("mxfp4", 12)):
+        p = host_plan("decode", d_indptr, d_len, 32, 8, 128, 16, num_cus=5, kv_format=fmt)
+        assert p.info()["levels"][0]["num_workers"] == 5 * wpc
+    p = host_plan("decode", d_indptr, d_len, 32, 8, 128, 16, num_cus=5, kv_format="mxfp4",
+                  workers_per_cu=6)
+    assert p.info()["levels"][0]["num_workers"] == 30
+    rng = np.random.default_rng(4)
+    indptr, L_, qo_indptr, qo = _pod_batch(rng, 8, 2, 16, 4)
+    a = host_plan("append", indptr, L_, 32, 8, 128, 16, qo_indptr=qo_indptr, num_cus=4,
+                  kv_format="mxfp4")
+    b = host_plan("append", indptr, L_, 32, 8, 128, 16, qo_indptr=qo_indptr, num_cus=4)
+    assert [lv["num_workers"] for lv in a.info()["levels"]] == \
+        [lv["num_workers"] for lv in b.info()["levels"]]
+    d = L.PlanDesc(kind=0, batch=3, num_qo_heads=32, num_kv_heads=8, head_dim=128,
+                   page_size=16, num_cus=5, kv_format=3)
+    h = ctypes.c_void_p()
+    ind = np.asarray(d_indptr, dtype=np.int32)
+    ln = np.asarray(d_len, dtype=np.int32)
+    st = fi.load().fi_plan(ctypes.byref(d), ind.ctypes.data_as(L.I32P), ln.ctypes.data_as(L.I32P),
+                           None, None, None, None, None,   # qo, prefixes, groups, parents
+                           None, 0, None, 0, None, ctypes.byref(h))
+    assert st == L.FI_ERR_INVALID_ARG
+    assert b"kv_format" in fi.load().fi_last_error()
+
+
 @pytest.mark.parametrize("pod", [False, True])
 @pytest.mark.parametrize("det", [False, True])
 def test_cascade_plan_matches_reference(det, pod):

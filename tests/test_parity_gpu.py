@@ -767,7 +767,8 @@ def test_mxfp4_llama_decode_sampled(dev):
     rng = np.random.default_rng(22)
     reqs = sample_requests(w.batch, 8, rng, must=[int(torch.argmax(w.kv_len))])
     o_ref, l_ref, a_ref = _fp4_oracle(w, reqs)
-    for kw in (dict(), dict(deterministic=True), dict(workers_per_cu=8)):
+    for kw in (dict(), dict(deterministic=True), dict(workers_per_cu=8),
+               dict(kv_format="mxfp4"), dict(kv_format="mxfp4", deterministic=True)):
         o, lse = _fp4_run(w, dev, **kw)
         compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs),
                 what=f"mxfp4 llama {kw}")
