@@ -78,12 +78,19 @@ def cpu_baseline(w, budget_s: float):
     kp, vp = w.k_cache.float().numpy(), w.v_cache.float().numpy()
     q = w.q.double().numpy()
     args = (w.kv_indptr.numpy(), w.kv_indices.numpy(), w.kv_len.numpy(), w.page_size, w.sm_scale)
-    # size the sample: time one request, then take enough requests for the budget
+    # size the sample by KV tokens: time the first few requests, then take
+    # requests in order (and whole-batch repeats) for about budget_s seconds
+    lens = [int(x) for x in w.kv_len]
+    probe = list(range(min(4, w.batch)))
+    oracle.paged_decode(q, kp, vp, *args, requests=probe[:1])   # first-call costs
     t0 = time.perf_counter()
-    oracle.paged_decode(q, kp, vp, *args, requests=[0])
-    per_req = max(1e-3, time.perf_counter() - t0)
-    n_req = max(1, min(w.batch, int(budget_s / per_req)))
-    reps = max(1, int(budget_s / (per_req * n_req)))
+    oracle.paged_decode(q, kp, vp, *args, requests=probe)
+    per_tok = (time.perf_counter() - t0) / max(1, sum(lens[r] for r in probe))
+    n_req, toks = 0, 0
+    while n_req < w.batch and (n_req == 0 or (toks + lens[n_req]) * per_tok <= budget_s):
+        toks += lens[n_req]
+        n_req += 1
+    reps = max(1, int(budget_s / max(1e-9, toks * per_tok)))
     reqs = list(range(n_req))
     t0 = time.perf_counter()
     for _ in range(reps):
@@ -301,7 +308,7 @@ def main():
                     help="deterministic mode: chunk size in pages (0 = the library default)")
     ap.add_argument("--engine", choices=("default", "mfma", "valu"), default="default",
                     help="units for the decode-style levels")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")

@@ -806,6 +806,30 @@ def test_mxfp4_decode_extreme_scales(dev):
     compare(o.double() / c, lse, o_ref / c, l_ref, a_ref / c, what="mxfp4 extreme scales")
 
 
+def test_mxfp4_deterministic_mode_is_batch_invariant(dev):
+    """Deterministic MXFP4 decode: a request's output bits do not depend on
+    the rest of the batch nor on the plan's workers per CU (which picks the
+    kernel's LDS ring depth: 8, 4 or 3 stages)."""
+    rng = np.random.default_rng(16)
+    lens = [4100] + list(rng.integers(1, 6000, 31))
+    w = to_mxfp4_cache(make_decode(lens, 32, 8, 128, 16, seed=520, poison=False), poison=True)
+    target = 0
+    outs = []
+    for reqs, wpc in (([target], 0), ([3, target, 9, 4], 4), ([9, 5, target], 8),
+                      (list(rng.permutation(32)), 12)):
+        sub = _sub_batch(w, [int(r) for r in reqs])
+        for f in ("k_fp4", "v_fp4", "k_bscale", "v_bscale"):
+            setattr(sub, f, getattr(w, f))
+        pos = [int(r) for r in reqs].index(target)
+        o, lse = _fp4_run(sub, dev, deterministic=True, det_chunk_pages=16, workers_per_cu=wpc)
+        outs.append((o[pos].clone(), lse[pos].clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    o_ref, l_ref, a_ref = _fp4_oracle(w, requests=[target])
+    compare(outs[0][0][None], outs[0][1][None], o_ref[[target]], l_ref[[target]],
+            a_ref[[target]], what="mxfp4 batch-invariant target vs oracle")
+
+
 def test_mxfp4_decode_refuses_the_valu_engine(dev):
     w = to_mxfp4_cache(make_decode([40, 7], 8, 2, 64, 16, seed=9, poison=False), poison=True)
     with pytest.raises(fi.FIError, match="matrix-core"):
