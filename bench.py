@@ -333,8 +333,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build measures one GPU only; --gpus must be 1 "
-              "(the path's multi-GPU sharding is a design note, not a run).", file=sys.stderr)
+        print("bench.py: the library runs on one GPU; --gpus must be 1 (sharding the path "
+              "across GPUs is designed, not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -25,7 +25,7 @@ struct Tile {
 };
 
 // Issue the loads of step s of item it into T. K and V are read once per call,
-// so the loads are nontemporal (on the box they stream from HBM ~13% faster
+// so the loads are nontemporal (on MI355X they stream from HBM ~13% faster
 // than default-policy loads).
 template <int D, int NP, bool QT>
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, int s,

@@ -11,7 +11,7 @@
 //
 // Every element value (an E2M1 value times a power of two) is exact in bf16,
 // so codes are widened to bf16 with v_cvt_scalef32_pk_bf16_fp4, the scale
-// applied by the instruction (measured on the box for every byte, selector
+// applied by the instruction (measured on MI355X for every byte, selector
 // and scale code: exact, bf16 overflow to infinity, scale 255 -> NaN), and the
 // bf16 MFMA tiling of the bf16 decode kernel is reused unchanged: no scale is
 // folded into the softmax.

@@ -15,7 +15,7 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def gpu():
     """The GPU tests fail loudly (never skip) when no device is present, so a
-    broken box can not pass as green."""
+    machine without a working GPU cannot pass as green."""
     import torch
     if not torch.cuda.is_available():
         pytest.fail("GPU test run without a visible GPU (run with -m 'not gpu' on CPU)")
