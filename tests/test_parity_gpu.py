@@ -537,17 +537,33 @@ def _capture(fn):
     return graph
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 4, "pod", "cascade_pod"])
+@pytest.mark.parametrize("cfg", [1, 3, 4, "pod", "cascade_pod", "fp8", "mxfp4"])
 def test_graph_replay_matches_eager(dev, cfg):
     """A captured run call (no allocation, no memset inside) replays to the
     eager bits, replay after replay, with other eager work in between."""
     w = (make_pod_mix(poison=False) if cfg == "pod" else
-         make_config(3 if cfg == "cascade_pod" else cfg, poison=False))
+         make_config(3 if cfg == "cascade_pod" else 1 if cfg in ("fp8", "mxfp4") else cfg,
+                     poison=False))
+    if cfg == "fp8":
+        w = to_fp8_cache(w, poison=False)
+    elif cfg == "mxfp4":
+        w = to_mxfp4_cache(w, poison=False)
     g = w.to(dev)
     T = g.q.shape[0]
     out = torch.empty_like(g.q)
     lse = torch.empty(T, w.num_qo_heads, dtype=torch.float32, device=dev)
-    if w.kind == "decode":
+    if cfg in ("fp8", "mxfp4"):
+        p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                    w.page_size, device=dev, kv_format=cfg)
+        if cfg == "fp8":
+            call = lambda o, l: fi.paged_decode_fp8(p, g.q, g.k_fp8, g.v_fp8, g.k_scale,  # noqa
+                                                    g.v_scale, g.kv_indices, w.sm_scale,
+                                                    out=o, lse=l)
+        else:
+            call = lambda o, l: fi.paged_decode_mxfp4(p, g.q, g.k_fp4, g.v_fp4,  # noqa
+                                                      g.k_bscale, g.v_bscale, g.kv_indices,
+                                                      w.sm_scale, out=o, lse=l)
+    elif w.kind == "decode":
         p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                     w.page_size, device=dev)
         call = lambda o, l: fi.paged_decode(p, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
