@@ -737,7 +737,7 @@ def test_fp8_llama_decode_sampled(dev):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("ps", [8, 16, 32, 64])
-@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("G", [1, 4, 8, 16, 24])
 def test_fp8_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
     w = to_fp8_cache(make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=500 + D + ps + G,
@@ -792,7 +792,7 @@ def test_mxfp4_llama_decode_sampled(dev):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("ps", [8, 16, 32, 64])
-@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("G", [1, 4, 8, 16, 24])
 def test_mxfp4_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
     w = to_mxfp4_cache(make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=600 + D + ps + G,
