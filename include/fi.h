@@ -271,6 +271,21 @@ fi_status fi_paged_decode_mxfp4(const fi_plan_t* plan, const void* q, const void
                                 const void* v_scales, const int32_t* kv_indices,
                                 float sm_scale, void* o, float* lse, void* stream);
 
+/* Debug check of the device page tables that a run call with this plan
+ * will read. The run calls trust them (the ABI conventions above); this call
+ * lets a caller verify them while debugging. Counts the page ids outside
+ * [0, num_pages) among the first kv_indptr[B] entries of kv_indices (the
+ * entries the plan's host table covers) and, if prefix_indices is not NULL
+ * (cascade plans), among the first prefix_indptr[num_prefix_groups] entries of
+ * prefix_indices, and writes the count to *bad_count (one int32 in device
+ * memory, overwritten; the write is ordered on `stream`, so read it after the
+ * stream). Decode, append and cascade plans (FI_ERR_INVALID_ARG for a
+ * block-sparse plan, whose page lists are copied from the host at plan
+ * time); num_pages >= 1. */
+fi_status fi_check_page_tables(const fi_plan_t* plan, const int32_t* kv_indices,
+                               const int32_t* prefix_indices, int32_t num_pages,
+                               int32_t* bad_count, void* stream);
+
 /* Append / prefill attention for a mixed batch (research note, "Arithmetic
  * intensity": prefill and decode rows of one batch). Plan kind
  * FI_KIND_APPEND. If k_new and v_new ([sum qo][Hkv][D] bf16) are non-NULL,

@@ -13,6 +13,7 @@ from .api import (  # noqa: F401
     Workspace,
     block_sparse_attention,
     cascade,
+    check_page_tables,
     merge_states,
     paged_append,
     paged_decode,

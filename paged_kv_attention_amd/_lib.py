@@ -61,6 +61,8 @@ SIGNATURES = {
     "fi_paged_decode_mxfp4": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                         c_void_p]),
+    "fi_check_page_tables": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                       c_void_p]),
     "fi_paged_append": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                   c_void_p, c_float, c_void_p, c_void_p, c_void_p]),
     "fi_cascade": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

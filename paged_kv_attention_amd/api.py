@@ -353,6 +353,22 @@ def paged_decode_mxfp4(plan: Plan, q, k_codes, v_codes, k_scales, v_scales, kv_i
     return out, lse
 
 
+def check_page_tables(plan: Plan, kv_indices, num_pages: int, prefix_indices=None) -> int:
+    """fi_check_page_tables (debugging aid): the number of page ids outside
+    [0, num_pages) in the entries of ``kv_indices`` (and ``prefix_indices``)
+    that run calls with ``plan`` read. Synchronises the stream to return it."""
+    if plan.device is None:
+        raise ValueError("host-only plan: the check runs on the plan's device")
+    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    if prefix_indices is not None:
+        _check_tensor(prefix_indices, "prefix_indices", torch.int32, plan.device)
+    count = torch.empty(1, dtype=torch.int32, device=plan.device)
+    L.check(L.load().fi_check_page_tables(plan.handle, _ptr(kv_indices), _ptr(prefix_indices),
+                                          int(num_pages), _ptr(count), _stream(plan.device)),
+            "fi_check_page_tables")
+    return int(count.item())
+
+
 def paged_append(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, k_new=None,
                  v_new=None, out=None, lse=None, return_lse: bool = True):
     """fi_paged_append: q [sum qo, Hq, D]; optional k_new/v_new [sum qo, Hkv, D]

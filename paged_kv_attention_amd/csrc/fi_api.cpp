@@ -207,6 +207,28 @@ extern "C" fi_status fi_paged_decode_mxfp4(const fi_plan_t* p, const void* q, co
   return run_merge(p, o, lse, s);
 }
 
+extern "C" fi_status fi_check_page_tables(const fi_plan_t* p, const int32_t* kv_indices,
+                                          const int32_t* prefix_indices, int32_t num_pages,
+                                          int32_t* bad_count, void* stream) {
+  clear_error();
+  if (!p) return set_error(FI_ERR_PLAN_MISMATCH, "fi_check_page_tables: plan is NULL");
+  if (!p->on_device)
+    return set_error(FI_ERR_PLAN_MISMATCH,
+                     "fi_check_page_tables: host-only plan (built without a device workspace)");
+  if (p->hp.desc.kind == FI_KIND_BLOCK_SPARSE)
+    return set_error(FI_ERR_INVALID_ARG,
+                     "fi_check_page_tables: a block-sparse plan reads no caller page table");
+  if (num_pages < 1)
+    return set_error(FI_ERR_INVALID_ARG, "fi_check_page_tables: num_pages %d < 1", num_pages);
+  if (!bad_count) return set_error(FI_ERR_INVALID_ARG, "fi_check_page_tables: bad_count is NULL");
+  if (p->hp.kv_entries > 0 && !kv_indices)
+    return set_error(FI_ERR_INVALID_ARG, "fi_check_page_tables: kv_indices is NULL");
+  return hip_status(launch_check_page_ids(kv_indices, p->hp.kv_entries, prefix_indices,
+                                          prefix_indices ? p->hp.prefix_entries : 0, num_pages,
+                                          bad_count, (hipStream_t)stream),
+                    "page table check launch");
+}
+
 extern "C" fi_status fi_paged_append(const fi_plan_t* p, const void* q, const void* k_new,
                                      const void* v_new, void* k_cache, void* v_cache,
                                      const int32_t* kv_indices, float sm_scale, void* o,

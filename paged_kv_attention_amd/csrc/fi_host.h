@@ -45,6 +45,9 @@ struct HostPlan {
   // every launch made whatever the batch, sized by these capacities
   bool stable = false;
   int64_t cap_merges = 0, cap_scatter = 0;
+  // entries of the device page tables the run calls read (kv_indptr[B] and,
+  // for cascade, prefix_indptr[num_prefix_groups]; 0 for block-sparse plans)
+  int64_t kv_entries = 0, prefix_entries = 0;
 };
 
 // Byte offsets of each section inside the workspace blob.
@@ -61,6 +64,12 @@ struct Layout {
 Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t n_merges,
                   size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
                   int32_t head_dim, size_t n_plist = 0);
+
+// Debug check of device page tables (fi_check.hip): zeroes *count, then adds
+// the number of ids outside [0, num_pages) in each non-NULL table.
+hipError_t launch_check_page_ids(const int32_t* kv_ids, int64_t n_kv, const int32_t* prefix_ids,
+                                 int64_t n_prefix, int32_t num_pages, int32_t* count,
+                                 hipStream_t stream);
 
 }  // namespace fi
 

@@ -1063,6 +1063,9 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
     p->hp.cap_merges = (int64_t)caps.merges;
     p->hp.cap_scatter = (int64_t)caps.scatter;
   }
+  p->hp.kv_entries = d.batch > 0 ? kv_indptr_h[d.batch] : 0;
+  p->hp.prefix_entries = d.kind == FI_KIND_CASCADE && d.num_prefix_groups > 0
+                             ? prefix_indptr_h[d.num_prefix_groups] : 0;
   return finish_plan(p, stable ? &caps : nullptr, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes,
                      stream, out);
 }

@@ -183,6 +183,18 @@ def test_launch_defaults():
                   launch="pod", pod_wide_blocks=-1)
 
 
+def test_page_table_check_refuses_bad_plans_before_any_launch():
+    lib = fi.load()
+    cnt = ctypes.c_int32(0)
+    assert lib.fi_check_page_tables(None, None, None, 10, ctypes.byref(cnt), None) == \
+        L.FI_ERR_PLAN_MISMATCH
+    d_indptr, d_len = _decode_host([100, 20], 16)
+    p = host_plan("decode", d_indptr, d_len, 8, 2, 64, 16, num_cus=4)
+    assert lib.fi_check_page_tables(p.handle, None, None, 10, ctypes.byref(cnt), None) == \
+        L.FI_ERR_PLAN_MISMATCH                        # host-only plan
+    assert b"host-only" in lib.fi_last_error()
+
+
 def test_kv_format_picks_the_default_worker_count():
     """A decode plan for an MXFP4 cache defaults to 12 workers per CU, bf16
     and FP8 plans to 4; an explicit count wins; other plan kinds ignore the

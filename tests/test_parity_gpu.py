@@ -318,6 +318,32 @@ def test_empty_batch_and_empty_requests(dev):
     assert o.numel() == 0
 
 
+def test_page_table_check_counts_out_of_range_ids(dev):
+    """fi_check_page_tables counts the ids outside [0, num_pages) among the
+    entries the plan covers (planted in a copy of the table), not beyond
+    them, and checks a cascade plan's prefix table when given."""
+    w = make_decode([100, 37, 300, 16], 8, 2, 64, 16, seed=77)
+    p = fi.Plan("decode", w.kv_indptr, w.kv_len, 8, 2, 64, 16, device=dev)
+    P = w.num_pages
+    n = int(w.kv_indptr[-1])
+    idx = torch.cat([w.kv_indices, torch.tensor([-5, P + 9], dtype=torch.int32)]).to(dev)
+    assert fi.check_page_tables(p, idx, P) == 0          # entries past kv_indptr[B] ignored
+    bad = idx.clone()
+    bad[0], bad[7], bad[n - 1] = -1, P, 2 ** 30
+    assert fi.check_page_tables(p, bad, P) == 3
+    assert fi.check_page_tables(p, idx, int(idx[:n].max())) == 1   # the largest id is now out
+    c = make_cascade([64, 32], [0, 1, -1], [40, 7, 100], 8, 2, 64, 16, seed=78)
+    pc = fi.Plan("cascade", c.kv_indptr, c.kv_len, 8, 2, 64, 16, prefix_indptr=c.prefix_indptr,
+                 prefix_len=c.prefix_len, req_prefix_group=c.req_prefix_group, device=dev)
+    gi, gp = c.kv_indices.to(dev), c.prefix_indices.to(dev).clone()
+    assert fi.check_page_tables(pc, gi, c.num_pages, gp) == 0
+    gp[1] = -3
+    assert fi.check_page_tables(pc, gi, c.num_pages, gp) == 1
+    assert fi.check_page_tables(pc, gi, c.num_pages) == 0     # prefix table not given
+    with pytest.raises(fi.FIError):
+        fi.check_page_tables(p, idx, 0)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_merge_states_api(dev, dtype):
     g = torch.Generator().manual_seed(9)
