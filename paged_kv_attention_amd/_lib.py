@@ -7,7 +7,10 @@ import os
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int32, c_int64, c_size_t, c_void_p
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libfi.so")
+# FI_LIB_PATH selects another build of the same library (the CPU tests run the
+# ABI tests once more against a build whose host code carries AddressSanitizer
+# and UBSan checks).
+LIB_PATH = os.environ.get("FI_LIB_PATH") or os.path.join(HERE, "libfi.so")
 
 FI_OK, FI_ERR_INVALID_ARG, FI_ERR_UNSUPPORTED, FI_ERR_WORKSPACE, FI_ERR_PLAN_MISMATCH, \
     FI_ERR_HIP = range(6)

@@ -45,29 +45,54 @@ EXTRA = {
 }
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+# Host-sanitizer build (libfi_san.so, for the CPU tests): host code with
+# AddressSanitizer and UBSan, device code unchanged.
+SAN_LIB = os.path.join(HERE, "libfi_san.so")
+SAN_BUILD = os.path.join(HERE, "_build_san")
+SAN_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def _compile(src: str, sanitize: bool = False) -> str:
+    obj = os.path.join(SAN_BUILD if sanitize else BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc()] + COMMON + EXTRA.get(os.path.basename(src), []) + \
+        (SAN_HOST if sanitize else []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, sanitize: bool = False) -> str:
+    """Compile every source and link the library (``sanitize``: the
+    host-sanitizer build, libfi_san.so, which needs the sanitizer runtime
+    preloaded into the process that loads it)."""
+    out_dir, lib = (SAN_BUILD, SAN_LIB) if sanitize else (BUILD, LIB)
+    os.makedirs(out_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, sanitize), srcs))
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if sanitize:
+        cmd += SAN_HOST + ["-shared-libsan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB} from {len(srcs)} sources")
-    return LIB
+        print(f"built {lib} from {len(srcs)} sources")
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """Path of the AddressSanitizer runtime the sanitizer build links."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True)
+    path = r.stdout.strip()
+    if r.returncode != 0 or not os.path.isabs(path) or not os.path.exists(path):
+        raise RuntimeError("AddressSanitizer runtime not found next to hipcc's clang")
+    return path
 
 
 if __name__ == "__main__":
