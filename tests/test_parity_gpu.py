@@ -146,7 +146,7 @@ SMALL_LENS = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 517, 1000]
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64, 256])
 @pytest.mark.parametrize("G", [1, 4, 8, 24])
 def test_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
@@ -383,7 +383,7 @@ def test_valu_engine_configs(dev, cfg1):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64, 256])
 @pytest.mark.parametrize("G", [1, 3, 4, 8])
 def test_valu_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
@@ -762,7 +762,7 @@ def test_fp8_llama_decode_sampled(dev):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64, 256])
 @pytest.mark.parametrize("G", [1, 4, 8, 16, 24])
 def test_fp8_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
@@ -817,7 +817,7 @@ def test_mxfp4_llama_decode_sampled(dev):
 
 
 @pytest.mark.parametrize("D", [64, 128])
-@pytest.mark.parametrize("ps", [8, 16, 32, 64])
+@pytest.mark.parametrize("ps", [8, 16, 32, 64, 256])
 @pytest.mark.parametrize("G", [1, 4, 8, 16, 24])
 def test_mxfp4_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
