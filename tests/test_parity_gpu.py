@@ -175,7 +175,8 @@ def test_decode_many_merge_records(dev, B, D, rows_min, rows_max):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 2), (128, 32, 8), (64, 16, 24)])
+@pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 2), (128, 32, 8), (64, 16, 24),
+                                    (128, 256, 4)])
 def test_append_small_sweep(dev, causal, D, ps, G):
     prefix = [0, 5, 16, 40, 300, 1]
     qo = [1, 3, 17, 40, 70, 33]
@@ -425,7 +426,7 @@ def _scattered_pools(w):
 
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 2), (128, 32, 8), (64, 16, 1),
-                                    (128, 64, 16)])
+                                    (128, 64, 16), (64, 256, 4)])
 def test_pod_small_sweep(dev, causal, D, ps, G):
     """Mixed batches in one fused launch: requests whose rows fit 16 run in the
     decode role (with the causal mask over their few query tokens), the rest
@@ -503,7 +504,7 @@ def _bs_oracle(w, rows=None):
 
 
 @pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 1), (128, 32, 8), (64, 16, 2),
-                                    (128, 64, 16)])
+                                    (128, 64, 16), (128, 256, 4)])
 def test_block_sparse_small_sweep(dev, D, ps, G):
     """Variable blocks per kv head (some empty), random masks with a row block
     that sees nothing, every plan variant, against the oracle in full."""
