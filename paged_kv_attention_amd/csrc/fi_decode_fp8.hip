@@ -185,17 +185,26 @@ __device__ __forceinline__ void compute_step8(const AttnArgs& a, const Item& it,
   }
   // V rows: tokens past the item's end are zeroed as codes (0 is +0), the
   // rest widened to bf16 rows, then transposed to the V^T operand
+  // (only tail steps hold such tokens: the selects are made there alone)
+  typename C8<D>::vraw_t vraw[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) vraw[i] = T.v[i];
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int tl = (i < 4) ? 4 * grp + i : 16 + 4 * grp + (i - 4);
+      if (T0 + tl >= it.t_end) vraw[i] = typename C8<D>::vraw_t{};
+    }
+  }
   vrow_t vv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int tl = (i < 4) ? 4 * grp + i : 16 + 4 * grp + (i - 4);
-    const bool ok = T0 + tl < it.t_end;
     if constexpr (DPL == 8) {
-      const u32x2 raw = ok ? T.v[i] : u32x2{0u, 0u};
+      const u32x2 raw = vraw[i];
       vv[i] = vrow_t{widen2<false>(raw[0]), widen2<true>(raw[0]), widen2<false>(raw[1]),
                      widen2<true>(raw[1])};
     } else {
-      const uint32_t raw = ok ? T.v[i] : 0u;
+      const uint32_t raw = vraw[i];
       vv[i] = vrow_t{widen2<false>(raw), widen2<true>(raw)};
     }
   }
