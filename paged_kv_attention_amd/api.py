@@ -274,6 +274,17 @@ def _outputs(plan: Plan, q, out, lse):
     return out, lse
 
 
+def _check_table(plan: Plan, t, name: str, key: str):
+    """A device page table must hold at least the entries the plan's host
+    table covers (``plan._ha[key][-1]``): the kernels read that many ids
+    unchecked, so a shorter table would be read past its end."""
+    _check_tensor(t, name, torch.int32, plan.device)
+    ptr = plan._ha.get(key)
+    need = int(ptr[-1]) if ptr is not None and ptr.size else 0
+    if t.numel() < need:
+        raise ValueError(f"{name} has {t.numel()} entries, the plan's table needs {need}")
+
+
 def _check_run(plan: Plan, kind: str):
     if plan.kind != kind:
         raise ValueError(f"plan kind is {plan.kind}, not {kind}")
@@ -288,7 +299,7 @@ def paged_decode(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, o
     _check_tensor(q, "q", torch.bfloat16, plan.device,
                   (plan.batch, plan.num_qo_heads, plan.head_dim))
     _check_cache(plan, k_cache, v_cache)
-    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    _check_table(plan, kv_indices, "kv_indices", "kv_indptr")
     if lse is None and return_lse:
         lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
     out, lse = _outputs(plan, q, out, lse)
@@ -314,7 +325,7 @@ def paged_decode_fp8(plan: Plan, q, k_cache, v_cache, k_scale, v_scale, kv_indic
     P = k_cache.shape[0]
     _check_tensor(k_scale, "k_scale", torch.float32, plan.device, (P, plan.num_kv_heads))
     _check_tensor(v_scale, "v_scale", torch.float32, plan.device, (P, plan.num_kv_heads))
-    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    _check_table(plan, kv_indices, "kv_indices", "kv_indptr")
     if lse is None and return_lse:
         lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
     out, lse = _outputs(plan, q, out, lse)
@@ -342,7 +353,7 @@ def paged_decode_mxfp4(plan: Plan, q, k_codes, v_codes, k_scales, v_scales, kv_i
     sshape = (P, plan.num_kv_heads, plan.page_size, D // 32)
     _check_tensor(k_scales, "k_scales", torch.uint8, plan.device, sshape)
     _check_tensor(v_scales, "v_scales", torch.uint8, plan.device, sshape)
-    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    _check_table(plan, kv_indices, "kv_indices", "kv_indptr")
     if lse is None and return_lse:
         lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
     out, lse = _outputs(plan, q, out, lse)
@@ -359,9 +370,9 @@ def check_page_tables(plan: Plan, kv_indices, num_pages: int, prefix_indices=Non
     that run calls with ``plan`` read. Synchronises the stream to return it."""
     if plan.device is None:
         raise ValueError("host-only plan: the check runs on the plan's device")
-    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    _check_table(plan, kv_indices, "kv_indices", "kv_indptr")
     if prefix_indices is not None:
-        _check_tensor(prefix_indices, "prefix_indices", torch.int32, plan.device)
+        _check_table(plan, prefix_indices, "prefix_indices", "prefix_indptr")
     count = torch.empty(1, dtype=torch.int32, device=plan.device)
     L.check(L.load().fi_check_page_tables(plan.handle, _ptr(kv_indices), _ptr(prefix_indices),
                                           int(num_pages), _ptr(count), _stream(plan.device)),
@@ -377,7 +388,7 @@ def paged_append(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, k
     T = plan.num_q_tokens
     _check_tensor(q, "q", torch.bfloat16, plan.device, (T, plan.num_qo_heads, plan.head_dim))
     _check_cache(plan, k_cache, v_cache)
-    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    _check_table(plan, kv_indices, "kv_indices", "kv_indptr")
     if (k_new is None) != (v_new is None):
         raise ValueError("give both k_new and v_new, or neither")
     if k_new is not None:
@@ -401,8 +412,8 @@ def cascade(plan: Plan, q, k_cache, v_cache, prefix_indices, kv_indices, sm_scal
     _check_tensor(q, "q", torch.bfloat16, plan.device,
                   (plan.batch, plan.num_qo_heads, plan.head_dim))
     _check_cache(plan, k_cache, v_cache)
-    _check_tensor(prefix_indices, "prefix_indices", torch.int32, plan.device)
-    _check_tensor(kv_indices, "kv_indices", torch.int32, plan.device)
+    _check_table(plan, prefix_indices, "prefix_indices", "prefix_indptr")
+    _check_table(plan, kv_indices, "kv_indices", "kv_indptr")
     if lse is None and return_lse:
         lse = torch.empty(plan.batch, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
     out, lse = _outputs(plan, q, out, lse)

@@ -229,15 +229,18 @@ __device__ __forceinline__ void compute_step8(const AttnArgs& a, const Item& it,
   }
   const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  // lazy rescale, decided on the lane-local max (the base is equal across a
-  // row's lane groups and only moves here)
+  // lazy rescale: a wave-wide vote on the lane-local max gates it, and each
+  // row (the base is equal across a row's lane groups) moves its base only on
+  // its own max, so a row's bits never depend on the block's other rows
   if (__any(mx > st.m[0] + kRescaleSlack)) {
-    const float m_new = fmaxf(st.m[0], max_across_groups(mx));
-    const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[0] - m_new);
-    st.l[0] *= alpha;
+    const float rmax = max_across_groups(mx);
+    if (rmax > st.m[0] + kRescaleSlack) {
+      const float alpha = (st.m[0] == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[0] - rmax);
+      st.l[0] *= alpha;
 #pragma unroll
-    for (int m = 0; m < DPL; ++m) st.acc[0][m] *= alpha;
-    st.m[0] = m_new;
+      for (int m = 0; m < DPL; ++m) st.acc[0][m] *= alpha;
+      st.m[0] = rmax;
+    }
   }
   const float base = (st.m[0] == neg_inf()) ? 0.f : st.m[0];
   float p[8];

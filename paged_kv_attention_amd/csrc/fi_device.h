@@ -131,18 +131,24 @@ __device__ __forceinline__ void softmax_pv(State<D, MB>& st, int mb, f32x4 s0, f
     }
   }
   // The base m (equal in the four lane groups of a row) only moves when some
-  // logit exceeds it by more than the slack; the lane-local max decides that,
-  // and only then is the row max taken across the groups, so the common step
-  // needs no cross-lane exchange.
+  // logit of the row exceeds it by more than the slack. A wave-wide vote on
+  // the lane-local max gates the cross-lane exchange, so the common step
+  // needs none; inside, each row decides from its own max alone, so a row's
+  // base -- and with it the rounding of its p, l and O -- never depends on
+  // the other rows of the block (which may belong to other requests, as on a
+  // shared prefix).
   const float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
                          fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]))) * scale_log2;
   if (__any(mx > st.m[mb] + kRescaleSlack)) {
-    const float m_new = fmaxf(st.m[mb], max_across_groups(mx));
-    const float alpha = (m_new == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[mb] - m_new);
-    st.l[mb] *= alpha;
+    const float rmax = max_across_groups(mx);
+    if (rmax > st.m[mb] + kRescaleSlack) {
+      const float m_new = rmax;   // > m, finite or +inf only if a logit is
+      const float alpha = (st.m[mb] == neg_inf()) ? 1.f : __builtin_amdgcn_exp2f(st.m[mb] - m_new);
+      st.l[mb] *= alpha;
 #pragma unroll
-    for (int m = 0; m < DPL; ++m) st.acc[mb][m] *= alpha;
-    st.m[mb] = m_new;
+      for (int m = 0; m < DPL; ++m) st.acc[mb][m] *= alpha;
+      st.m[mb] = m_new;
+    }
   }
   const float nbase = (st.m[mb] == neg_inf()) ? 0.f : -st.m[mb];
   float p[8];

@@ -3,7 +3,9 @@
 Full-size configurations are compared on sampled requests (the oracle computes
 each request independently); small cases are compared in full. Every case is
 seeded; inputs are poisoned (NaN in unused pages, 1e4 in tail slots, NaN in
-not-yet-written append slots) so that a stray read shows up in the output.
+not-yet-written append slots) so that a stray read shows up in the output; the
+small sweeps put NaN in the tail slots as well, so a tail V row that reaches
+the P.V product unzeroed turns the output into NaN.
 """
 
 import math
@@ -53,15 +55,16 @@ def test_llama_decode_config_sampled(dev, cfg1, det):
     compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"llama_decode det={det}")
 
 
-def test_skewed_decode_config_sampled(dev):
+@pytest.mark.parametrize("det", [False, True])
+def test_skewed_decode_config_sampled(dev, det):
     w = make_config(2, poison=True)
-    o, lse, p = gpu_decode(w, dev)
+    o, lse, p = gpu_decode(w, dev, deterministic=det)
     long = [int(i) for i in torch.nonzero(w.kv_len == 32768).flatten()]
     assert len(long) >= 4
     rng = np.random.default_rng(2)
     reqs = sample_requests(w.batch, 6, rng, must=long + [int(torch.argmin(w.kv_len))])
     o_ref, l_ref, a_ref = oracle_decode(w, requests=reqs)
-    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what="skewed_decode")
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"skewed_decode det={det}")
     assert max(p.info()["levels"][0]["items"][:, 11]) > 0, "long requests were not split"
 
 
@@ -88,14 +91,16 @@ def _oracle_cascade(w, reqs):
     return o, lse, a
 
 
+@pytest.mark.parametrize("det", [False, True])
 @pytest.mark.parametrize("launch", ["pod", "separate"])
-def test_cascade_config_sampled(dev, launch):
+def test_cascade_config_sampled(dev, launch, det):
+    """The cascade batch, every one of its 64 requests against the oracle."""
     w = make_config(3, poison=True)
-    o, lse = _cascade_run(w, dev, launch=launch)
-    rng = np.random.default_rng(3)
-    reqs = sample_requests(w.batch, 8, rng)
+    o, lse = _cascade_run(w, dev, launch=launch, deterministic=det)
+    reqs = list(range(w.batch))
     o_ref, l_ref, a_ref = _oracle_cascade(w, reqs)
-    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"cascade {launch}")
+    compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs),
+            what=f"cascade {launch} det={det}")
     # cascade equals flat decode over the concatenated table (both on the GPU)
     ip, ix, ln = cascade_flat_tables(w)
     p = fi.Plan("decode", ip, ln, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
@@ -106,11 +111,15 @@ def test_cascade_config_sampled(dev, launch):
             what="flat decode of cascade input")
 
 
+@pytest.mark.parametrize("det", [False, True])
 @pytest.mark.parametrize("launch", ["pod", "separate"])
-def test_append_config_sampled(dev, launch):
+def test_append_config_sampled(dev, launch, det):
+    """The mixed append batch: the scatter bit for bit, and all 16 requests'
+    query rows against the oracle."""
     w = make_config(4, poison=True)
     p = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev, launch=launch)
+                w.page_size, qo_indptr=w.qo_indptr, causal=True, device=dev, launch=launch,
+                deterministic=det)
     g = w.to(dev)
     o, lse = fi.paged_append(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale,
                              k_new=g.k_new, v_new=g.v_new)
@@ -122,11 +131,8 @@ def test_append_config_sampled(dev, launch):
     # scatter is a bit-exact copy; every other pool byte is unchanged
     assert np.array_equal(g.k_cache.float().cpu().numpy(), kp2, equal_nan=True)
     assert np.array_equal(g.v_cache.float().cpu().numpy(), vp2, equal_nan=True)
-    rng = np.random.default_rng(4)
-    reqs = sample_requests(w.batch, 4, rng, must=[int(torch.argmax(w.qo_indptr.diff()))])
-    o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, True, reqs)
-    rows = np.concatenate([np.arange(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])) for r in reqs])
-    compare(o, lse, o_ref, l_ref, a_ref, rows=rows, what=f"append {launch}")
+    o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, True)
+    compare(o, lse, o_ref, l_ref, a_ref, what=f"append {launch} det={det}")
 
 
 def _oracle_append(w, kp2, vp2, causal, reqs=None):
@@ -150,7 +156,7 @@ SMALL_LENS = [0, 1, 7, 8, 9, 15, 16, 17, 31, 32, 33, 100, 517, 1000]
 @pytest.mark.parametrize("G", [1, 4, 8, 24])
 def test_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
-    w = make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=100 + D + ps + G)
+    w = make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=100 + D + ps + G, poison="nan")
     o_ref, l_ref, a_ref = oracle_decode(w)
     plans = [dict(), dict(deterministic=True, det_chunk_pages=1),
              dict(deterministic=True, det_chunk_pages=3), dict(min_chunk_pages=1)]
@@ -181,7 +187,8 @@ def test_append_small_sweep(dev, causal, D, ps, G):
     prefix = [0, 5, 16, 40, 300, 1]
     qo = [1, 3, 17, 40, 70, 33]
     Hkv = 2
-    w = make_append(prefix, qo, G * Hkv, Hkv, D, ps, seed=200 + D + ps + G, causal=causal)
+    w = make_append(prefix, qo, G * Hkv, Hkv, D, ps, seed=200 + D + ps + G, causal=causal,
+                    poison="nan")
     kp, vp = np_pools(w)
     kp2, vp2 = oracle.scatter_new_kv(kp, vp, w.k_new.float().numpy(), w.v_new.float().numpy(),
                                      w.qo_indptr.numpy(), w.kv_indptr.numpy(),
@@ -203,7 +210,7 @@ def test_append_small_sweep(dev, causal, D, ps, G):
 def test_cascade_small_multi_group(dev):
     ps = 16
     w = make_cascade([64, 40, 0], [0, 1, 1, -1, 2, 0, 1, 0], [5, 0, 40, 33, 16, 1, 300, 17],
-                     32, 8, 128, ps, seed=300)
+                     32, 8, 128, ps, seed=300, poison="nan")
     o_ref, l_ref, a_ref = _oracle_cascade(w, None)
     for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
                dict(launch="separate"),
@@ -388,7 +395,7 @@ def test_valu_engine_configs(dev, cfg1):
 @pytest.mark.parametrize("G", [1, 3, 4, 8])
 def test_valu_decode_small_sweep(dev, D, ps, G):
     Hkv = 2
-    w = make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=400 + D + ps + G)
+    w = make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=400 + D + ps + G, poison="nan")
     o_ref, l_ref, a_ref = oracle_decode(w)
     for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
         o, lse, _ = gpu_decode(w, dev, engine="valu", **kw)
@@ -434,7 +441,8 @@ def test_pod_small_sweep(dev, causal, D, ps, G):
     prefix = [0, 5, 16, 40, 300, 1, 700, 33, 1000, 2, 7]
     qo = [1, 3, 17, 1, 70, 2, 1, 4, 1, 40, 0]
     Hkv = 2
-    w = make_append(prefix, qo, G * Hkv, Hkv, D, ps, seed=600 + D + ps + G, causal=causal)
+    w = make_append(prefix, qo, G * Hkv, Hkv, D, ps, seed=600 + D + ps + G, causal=causal,
+                    poison="nan")
     kp2, vp2 = _scattered_pools(w)
     o_ref, l_ref, a_ref = _oracle_append(w, kp2, vp2, causal)
     for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
@@ -509,7 +517,8 @@ def test_block_sparse_small_sweep(dev, D, ps, G):
     """Variable blocks per kv head (some empty), random masks with a row block
     that sees nothing, every plan variant, against the oracle in full."""
     Hkv = 2
-    w = make_block_sparse(90, 700, G * Hkv, Hkv, D, ps, 6, 9, 0.45, seed=900 + D + ps + G)
+    w = make_block_sparse(90, 700, G * Hkv, Hkv, D, ps, 6, 9, 0.45, seed=900 + D + ps + G,
+                          poison="nan")
     w.block_mask[1, 2, :] = False          # kv head 1, row block 2: no keys
     o_ref, l_ref, a_ref = _bs_oracle(w)
     for kw in [dict(), dict(launch="separate"), dict(deterministic=True, det_chunk_pages=1),

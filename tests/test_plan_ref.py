@@ -212,3 +212,192 @@ def test_small_batch_keeps_units_whole():
     indptr2, L2 = _decode_inputs(lens2, ps)
     p2 = plan_ref("decode", 8, 2, ps, indptr2, L2, S, [16])
     assert any(m[5] > 1 for m in p2["merges"])
+
+
+# ---------------------------------------------------------------- rule 6 (fused launch)
+
+
+def _append_inputs(prefix, qo, ps):
+    L = np.asarray(prefix) + np.asarray(qo)
+    indptr, _ = _decode_inputs(list(L), ps)
+    return indptr, L, np.concatenate([[0], np.cumsum(qo)]).astype(int)
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_pod_roles_rows_and_padding(det):
+    """Rule 6: a request whose rows (qo * G) fit 16 has all its items in the
+    decode role (level 1) and none in the wide role, every other request the
+    reverse; every query row is written exactly once across both roles; the
+    worker lists are padded to P and 4P, with the padding workers empty."""
+    ps, G, Hq, Hkv, P = 16, 4, 32, 8, 40
+    rng = np.random.default_rng(60)
+    qo = [int(x) for x in rng.choice([1, 2, 3, 4, 5, 17, 60, 200, 0], 30)]
+    prefix = [int(x) for x in rng.integers(0, 2500, 30)]
+    indptr, L, qo_indptr = _append_inputs(prefix, qo, ps)
+    p = plan_ref("append", Hq, Hkv, ps, indptr, L, None, [128, 16], deterministic=det,
+                 det_chunk_pages=6, min_chunk_pages=[4, 2], qo_indptr=qo_indptr, causal=True,
+                 pod_blocks=P)
+    n_w = p["pod_wide_blocks"]
+    assert 1 <= n_w <= P - 1
+    small = [q * G <= 16 for q in qo]
+    for lev, role_small in ((0, False), (1, True)):
+        for it in p["levels"][lev]["items"]:
+            assert small[it[F["unit"]]] == role_small
+            assert it[F["n_rows"]] <= (16 if role_small else 128)
+    cov = check_outputs_once(p, G, Hq, int(qo_indptr[-1]))
+    assert np.all(cov == 1)
+    w0, w1 = p["levels"][0]["worker_indptr"], p["levels"][1]["worker_indptr"]
+    assert len(w0) == P + 1 and len(w1) == 4 * P + 1
+    assert w0[-1] == len(p["levels"][0]["items"]) and w1[-1] == len(p["levels"][1]["items"])
+    assert all(w0[w] == w0[w + 1] for w in range(n_w, P))
+    assert all(w1[w] == w1[w + 1] for w in range(4 * (P - n_w), 4 * P))
+
+
+def test_pod_split_follows_the_work():
+    """Rule 6's split: only wide work gives every workgroup to the wide role,
+    only decode work none; an override is capped at P - 1; and as the decode
+    role's work grows against fixed wide work, the wide role's share never
+    grows."""
+    ps, G, P = 16, 4, 64
+    prefill = ([3000, 2000], [300, 129])
+
+    def n_w(prefix, qo, **kw):
+        indptr, L, qo_indptr = _append_inputs(prefix, qo, ps)
+        return plan_ref("append", 32, 8, ps, indptr, L, None, [128, 16], qo_indptr=qo_indptr,
+                        causal=True, min_chunk_pages=[16, 8], pod_blocks=P, **kw)["pod_wide_blocks"]
+
+    assert n_w(*prefill) == P
+    assert n_w([500] * 10, [1] * 10) == 0
+    assert n_w(prefill[0] + [500], prefill[1] + [1], pod_wide_blocks=10 ** 6) == P - 1
+    shares = []
+    for n_dec in (1, 8, 32, 128, 512):
+        shares.append(n_w(prefill[0] + [4000] * n_dec, prefill[1] + [1] * n_dec))
+    assert all(a >= b for a, b in zip(shares, shares[1:])), shares
+    assert shares[0] > shares[-1]
+
+
+# ---------------------------------------------------------------- rule 7 (block-sparse)
+
+
+@pytest.mark.parametrize("pod", [None, 24])
+def test_block_sparse_units_address_the_selected_keys(pod):
+    """Rule 7: token t of a (kv head, row block) unit must be the t-th key of
+    its selected set, in key order. For every unit, the plan's page list at
+    the unit's offset, read the way the kernels read it (page t // ps of the
+    list, slot t % ps), addresses the same pool slot as that key does through
+    the sequence's own page table; the unit's key count is the selected
+    count, and its rows are the row block's."""
+    rng = np.random.default_rng(70)
+    ps, Hq, Hkv = 16, 8, 2
+    G = Hq // Hkv
+    T, Lk, MB, NB = 120, 900, 5, 7
+    row_sz = np.array([[30, 2, 0, 50, 38], [1, 60, 59, 0, 0]])
+    col_sz = []
+    for g in range(Hkv):
+        cuts = np.sort(rng.choice(np.arange(1, -(-Lk // ps)), NB - 1, replace=False)) * ps
+        col_sz.append(np.diff(np.concatenate([[0], np.minimum(cuts, Lk), [Lk]])))
+    col_sz = np.array(col_sz)
+    col_sz[1, 2] = 0                                   # an empty column block
+    mask = rng.random((Hkv, MB, NB)) < 0.5
+    mask[0, 1, :] = False                               # a row block with no keys
+    seq_pages = rng.permutation(200)[:-(-Lk // ps)]
+    p = plan_ref("block_sparse", Hq, Hkv, ps, [0], [0], 31 if pod is None else None,
+                 [128] if pod is None else [128, 16], min_chunk_pages=1,
+                 block_sparse=(T, row_sz, col_sz, mask, seq_pages), pod_blocks=pod)
+    plist = p["plist"]
+    seen = {}
+    for lv in p["levels"]:
+        for it in lv["items"]:
+            g, unit = it[F["kv_head"]], it[F["unit"]]
+            a = unit - g * MB
+            assert 0 <= a < MB
+            keys = [c0 + t for b, (c0, c) in enumerate(zip(np.cumsum(col_sz[g]) - col_sz[g],
+                                                           col_sz[g]))
+                    if mask[g, a, b] for t in range(c)]
+            assert it[F["q_base"]] == int(row_sz[g, :a].sum())
+            assert it[F["row0"]] + it[F["n_rows"]] <= row_sz[g, a] * G
+            for t in range(it[F["t_begin"]], it[F["t_end"]]):
+                k = keys[t]
+                assert plist[it[F["page_off"]] + t // ps] == seq_pages[k // ps]
+                assert t % ps == k % ps
+            seen.setdefault((g, a, it[F["row0"]]), []).append((it[F["t_begin"]], it[F["t_end"]]))
+            assert it[F["t_end"]] <= len(keys)
+    for g in range(Hkv):
+        for a in range(MB):
+            nsel = sum(int(c) for b, c in enumerate(col_sz[g]) if mask[g, a, b])
+            for r0 in range(0, int(row_sz[g, a]) * G,
+                            16 if pod and row_sz[g, a] * G <= 16 else 128):
+                spans = sorted(seen.get((g, a, r0), []))
+                covered = sum(e - b for b, e in spans)
+                assert covered == nsel, (g, a, r0, covered, nsel)
+    cov = check_outputs_once(p, G, Hq, T)
+    assert np.all(cov == 1)
+
+
+# ---------------------------------------------------------------- prefix trees
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_prefix_tree_parts_fold_root_first(det):
+    """Rule 1 and 5 for a tree of prefixes: a request's merge folds the
+    prefix parts of its chain in chain order from the root down, each
+    prefix's chunks in chunk order, then its own suffix chunks in order; a
+    group's units are over exactly the requests whose chain passes through
+    it."""
+    ps, Hq, Hkv = 16, 8, 2
+    G = Hq // Hkv
+    parent = [-1, 0, 1, 0, -1]
+    pref = [300, 160, 96, 500, 64]
+    groups = [2, 1, 0, 3, -1, 4, 2, 0, 1]
+    suf = [40, 0, 700, 17, 33, 5, 90, 300, 1]
+    indptr, L = _decode_inputs(suf, ps)
+    pindptr, PL = _decode_inputs(pref, ps)
+    p = plan_ref("cascade", Hq, Hkv, ps, indptr, L, [5, 11], [128, 16], deterministic=det,
+                 det_chunk_pages=3, min_chunk_pages=1, prefix_indptr=pindptr, prefix_len=PL,
+                 req_group=groups, prefix_parent=parent)
+
+    def chain_root_first(r):
+        c, h = [], groups[r]
+        while h >= 0:
+            c.append(h)
+            h = parent[h]
+        return c[::-1]
+
+    # who wrote each partial row: (level, group or request, chunk), row offset
+    owner = {}
+    for lev, lv in enumerate(p["levels"]):
+        for it in lv["items"]:
+            for k in range(it[F["n_rows"]]):
+                owner[it[F["dst"]] + k] = (lev, it[F["unit"]], it[F["chunk"]], it[F["kv_head"]],
+                                          it[F["q_base"]], it[F["row0"]] + k)
+    qlist = p["qlist"]
+    assert len(p["merges"]) == len(suf) * Hkv
+    for (r, row0, nr, g, off, n) in p["merges"]:
+        assert row0 == 0 and nr == G
+        seq = [owner[x] for x in p["parts"][off:off + n]]
+        for lev, unit, chunk, kvh, qb, rho in seq:
+            assert kvh == g
+            if lev == 0:       # a prefix part: its row is this request's first head
+                assert qlist[qb + rho // G] == r and rho % G == 0
+            else:
+                assert unit == r and rho == 0
+        got = [(lev, unit, chunk) for lev, unit, chunk, *_ in seq]
+        want = []
+        for grp in chain_root_first(r):
+            its = [it for it in p["levels"][0]["items"]
+                   if it[F["unit"]] == grp and it[F["kv_head"]] == g]
+            m = qlist.index(r, its[0][F["q_base"]]) - its[0][F["q_base"]]   # member index
+            k = sum(1 for it in its if it[F["row0"]] <= m * G < it[F["row0"]] + it[F["n_rows"]])
+            want.extend((0, grp, j) for j in range(k))
+        ks = sum(1 for it in p["levels"][1]["items"]
+                 if it[F["unit"]] == r and it[F["kv_head"]] == g)
+        want.extend((1, r, j) for j in range(ks))
+        assert got == want, (r, g, got, want)
+    for grp in range(len(pref)):
+        members = sorted(r for r in range(len(suf)) if grp in chain_root_first(r))
+        its = [it for it in p["levels"][0]["items"] if it[F["unit"]] == grp]
+        if not members:
+            assert not its
+            continue
+        qb = its[0][F["q_base"]]
+        assert qlist[qb:qb + len(members)] == members

@@ -22,7 +22,9 @@ Token ``t`` of a sequence sits in page ``indices[indptr[r] + t // ps]`` at slot
 ``t % ps``. With ``poison=True`` the pages no request uses are NaN, the slots
 past a request's length in its last page hold 1e4, and (append) the slots the
 new tokens will occupy hold NaN until the kernel scatters them: a kernel that
-reads a byte it should not shows up in the output.
+reads a byte it should not shows up in the output. ``poison="nan"`` puts NaN
+in the tail slots too, so that a tail V row reaching the P.V product with
+p = 0 (rather than being zeroed first) turns the output into NaN.
 """
 
 from __future__ import annotations
@@ -156,8 +158,16 @@ def _pool_size(used_pages: int) -> int:
     return max(1, int(math.ceil(used_pages * (1.0 + POOL_SLACK))))
 
 
-def _poison_pool(pool: torch.Tensor, used: torch.Tensor, tables) -> None:
-    """NaN in unused pages; TAIL_POISON in slots past each sequence's end.
+def _tail_value(poison) -> float:
+    """Value of the slots past a sequence's end under ``poison``: True gives
+    the finite TAIL_POISON (a stray read of K or V shows up as a huge logit or
+    value), ``"nan"`` gives NaN (a kernel that lets a p = 0 multiply such a V
+    row, instead of zeroing it, turns the output into NaN)."""
+    return float("nan") if poison == "nan" else TAIL_POISON
+
+
+def _poison_pool(pool: torch.Tensor, used: torch.Tensor, tables, tail: float = TAIL_POISON) -> None:
+    """NaN in unused pages; ``tail`` in slots past each sequence's end.
     ``tables`` is a list of (indices, start, length) for every sequence."""
     ps = pool.shape[2]
     mask = torch.ones(pool.shape[0], dtype=torch.bool)
@@ -166,7 +176,7 @@ def _poison_pool(pool: torch.Tensor, used: torch.Tensor, tables) -> None:
     for indices, start, length in tables:
         if length % ps:
             last = int(indices[start + (length - 1) // ps])
-            pool[last, :, length % ps:, :] = TAIL_POISON
+            pool[last, :, length % ps:, :] = tail
 
 
 def _lengths_uniform(gen, n, lo, hi) -> torch.Tensor:
@@ -196,8 +206,8 @@ def make_decode(lengths: Sequence[int], num_qo_heads: int, num_kv_heads: int,
     v = _randn_pool(gen, pool, num_kv_heads, page_size, head_dim)
     if poison:
         tabs = [(indices, int(indptr[r]), int(L[r])) for r in range(B)]
-        _poison_pool(k, indices, tabs)
-        _poison_pool(v, indices, tabs)
+        _poison_pool(k, indices, tabs, _tail_value(poison))
+        _poison_pool(v, indices, tabs, _tail_value(poison))
     return Workload(name=name, kind="decode", num_qo_heads=num_qo_heads,
                     num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
                     sm_scale=fp32_scale(head_dim), seed=seed,
@@ -321,8 +331,8 @@ def make_append(prefix_lens: Sequence[int], qo_lens: Sequence[int], num_qo_heads
         v_new = _randn_bf16(gen, (T, num_kv_heads, head_dim))
     if poison:
         tabs = [(indices, int(indptr[r]), int(L[r])) for r in range(B)]
-        _poison_pool(k, indices, tabs)
-        _poison_pool(v, indices, tabs)
+        _poison_pool(k, indices, tabs, _tail_value(poison))
+        _poison_pool(v, indices, tabs, _tail_value(poison))
         if with_new_kv:
             for r in range(B):
                 for t in range(int(P[r]), int(L[r])):
@@ -367,8 +377,8 @@ def make_cascade(prefix_lens: Sequence[int], req_group: Sequence[int],
         used = perm[:tot_pf + tot_s]
         tabs = [(prefix_indices, int(prefix_indptr[g]), int(PL[g])) for g in range(PL.numel())]
         tabs += [(indices, int(indptr[r]), int(S[r])) for r in range(B)]
-        _poison_pool(k, used, tabs)
-        _poison_pool(v, used, tabs)
+        _poison_pool(k, used, tabs, _tail_value(poison))
+        _poison_pool(v, used, tabs, _tail_value(poison))
     return Workload(name=name, kind="cascade", num_qo_heads=num_qo_heads,
                     num_kv_heads=num_kv_heads, head_dim=head_dim, page_size=page_size,
                     sm_scale=fp32_scale(head_dim), seed=seed,
@@ -454,8 +464,8 @@ def make_block_sparse(qo_len: int, kv_len: int, num_qo_heads: int, num_kv_heads:
     v = _randn_pool(gen, pool, Hkv, page_size, head_dim)
     if poison:
         tabs = [(indices, 0, kv_len)]
-        _poison_pool(k, indices, tabs)
-        _poison_pool(v, indices, tabs)
+        _poison_pool(k, indices, tabs, _tail_value(poison))
+        _poison_pool(v, indices, tabs, _tail_value(poison))
     return Workload(name=name, kind="block_sparse", num_qo_heads=num_qo_heads,
                     num_kv_heads=Hkv, head_dim=head_dim, page_size=page_size,
                     sm_scale=fp32_scale(head_dim), seed=seed,
