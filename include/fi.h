@@ -271,6 +271,32 @@ fi_status fi_paged_decode_mxfp4(const fi_plan_t* plan, const void* q, const void
                                 const void* v_scales, const int32_t* kv_indices,
                                 float sm_scale, void* o, float* lse, void* stream);
 
+/* Bytes of the library's static device scratch (per GPU), which
+ * fi_paged_decode_noalloc uses in place of a plan workspace. */
+#define FI_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* Decode attention that allocates nothing and needs no caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Same computation,
+ * kernels and results, bit for bit, as fi_paged_decode on a plan of the same
+ * description and batch. `plan` must be a host-only decode plan (fi_plan with
+ * ws_dev = NULL and num_cus > 0, normally the device's CU count): the call
+ * uploads the plan's arrays with one hipMemcpyAsync on `stream` from the
+ * plan's own host memory into a static device array of the library, of
+ * FI_NOALLOC_SCRATCH_BYTES per GPU, which also holds the split partial states;
+ * then it launches the attention and merge kernels on `stream`. It calls no
+ * allocator. The array is shared by every call on a GPU and keeps the last
+ * call's contents: calls that overlap on one GPU (other streams, other
+ * threads) race on it and must be serialised by the caller. The plan handle
+ * must stay alive until the call returns (the upload reads its host memory).
+ * Errors: FI_ERR_PLAN_MISMATCH (not a host-only decode plan), FI_ERR_WORKSPACE
+ * (the plan needs more than FI_NOALLOC_SCRATCH_BYTES of workspace, as
+ * fi_plan_info.dev_bytes_used reports), FI_ERR_INVALID_ARG and FI_ERR_HIP as
+ * fi_paged_decode; nothing is launched on error. */
+fi_status fi_paged_decode_noalloc(const fi_plan_t* plan, const void* q, const void* k_cache,
+                                  const void* v_cache, const int32_t* kv_indices,
+                                  float sm_scale, void* o, float* lse, void* stream);
+
 /* Debug check of the device page tables that a run call with this plan
  * will read. The run calls trust them (the ABI conventions above); this call
  * lets a caller verify them while debugging. Counts the page ids outside

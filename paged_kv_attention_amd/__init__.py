@@ -19,4 +19,5 @@ from .api import (  # noqa: F401
     paged_decode,
     paged_decode_fp8,
     paged_decode_mxfp4,
+    paged_decode_noalloc,
 )

@@ -20,6 +20,7 @@ FI_ENGINE_DEFAULT, FI_ENGINE_MFMA, FI_ENGINE_VALU = range(3)
 FI_LAUNCH_DEFAULT, FI_LAUNCH_POD, FI_LAUNCH_SEPARATE = range(3)
 FI_KV_BF16, FI_KV_FP8, FI_KV_MXFP4 = range(3)
 FI_ITEM_INTS, FI_MERGE_INTS = 12, 6
+FI_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 STATUS_NAMES = {0: "FI_OK", 1: "FI_ERR_INVALID_ARG", 2: "FI_ERR_UNSUPPORTED",
                 3: "FI_ERR_WORKSPACE", 4: "FI_ERR_PLAN_MISMATCH", 5: "FI_ERR_HIP"}
@@ -64,6 +65,8 @@ SIGNATURES = {
     "fi_paged_decode_mxfp4": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_void_p, c_float, c_void_p, c_void_p,
                                         c_void_p]),
+    "fi_paged_decode_noalloc": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                          c_float, c_void_p, c_void_p, c_void_p]),
     "fi_check_page_tables": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                        c_void_p]),
     "fi_paged_append": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,

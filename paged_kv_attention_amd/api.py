@@ -309,6 +309,38 @@ def paged_decode(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, o
     return out, lse
 
 
+def paged_decode_noalloc(plan: Plan, q, k_cache, v_cache, kv_indices, sm_scale: float, out,
+                         lse=None):
+    """fi_paged_decode_noalloc: the decode of ``paged_decode`` with the plan's
+    workspace in the library's static device scratch, for callers that cannot
+    allocate. ``plan`` is a host-only decode plan (``device=None`` and
+    ``num_cus`` given); ``out`` (and ``lse``, if given) are caller buffers,
+    since this call allocates nothing; tensors on the current device. Calls
+    that overlap on one GPU race on the shared scratch."""
+    if plan.kind != "decode":
+        raise ValueError(f"plan kind is {plan.kind}, not decode")
+    if plan.device is not None:
+        raise ValueError("fi_paged_decode_noalloc takes a host-only plan (device=None)")
+    dev = q.device
+    _check_tensor(q, "q", torch.bfloat16, dev, (plan.batch, plan.num_qo_heads, plan.head_dim))
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _check_tensor(t, n, torch.bfloat16, dev)
+        if t.dim() != 4 or tuple(t.shape[1:]) != (plan.num_kv_heads, plan.page_size,
+                                                  plan.head_dim):
+            raise ValueError(f"{n} shape {tuple(t.shape)} does not match the plan")
+    _check_tensor(kv_indices, "kv_indices", torch.int32, dev)
+    need = int(plan._ha["kv_indptr"][-1]) if plan._ha["kv_indptr"].size else 0
+    if kv_indices.numel() < need:
+        raise ValueError(f"kv_indices has {kv_indices.numel()} entries, the plan needs {need}")
+    _check_tensor(out, "out", torch.bfloat16, dev, (plan.batch, plan.num_qo_heads, plan.head_dim))
+    if lse is not None:
+        _check_tensor(lse, "lse", torch.float32, dev, (plan.batch, plan.num_qo_heads))
+    L.check(L.load().fi_paged_decode_noalloc(plan.handle, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(kv_indices), float(sm_scale), _ptr(out),
+                                             _ptr(lse), _stream(dev)), "fi_paged_decode_noalloc")
+    return out, lse
+
+
 def paged_decode_fp8(plan: Plan, q, k_cache, v_cache, k_scale, v_scale, kv_indices,
                      sm_scale: float, out=None, lse=None, return_lse: bool = True):
     """fi_paged_decode_fp8: K/V pools of FP8 E4M3 codes (uint8, same shape as

@@ -23,22 +23,6 @@ bool g_timer_on = false;
 int32_t g_timer_used = 0;
 std::vector<std::pair<hipEvent_t, hipEvent_t>> g_timer_events;
 
-struct TimerScope {
-  hipStream_t s;
-  hipEvent_t stop = nullptr;
-  explicit TimerScope(hipStream_t st) : s(st) {
-    std::lock_guard<std::mutex> lk(g_timer_mu);
-    if (g_timer_on && g_timer_used < (int32_t)g_timer_events.size()) {
-      auto& pr = g_timer_events[g_timer_used++];
-      if (hipEventRecord(pr.first, s) == hipSuccess) stop = pr.second;
-    }
-  }
-  void done() {
-    if (stop) (void)hipEventRecord(stop, s);
-    stop = nullptr;
-  }
-};
-
 template <typename T>
 T* at(const fi_plan_t* p, size_t off) {
   return (T*)(p->dev_base + off);
@@ -62,14 +46,43 @@ fi_status hip_status(hipError_t e, const char* what) {
 AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, const void* v,
                    const int32_t* kv_indices, const int32_t* prefix_indices, float sm_scale,
                    void* o, float* lse) {
+  return plan_attn_args(p, p->dev_base, level, q, k, v, kv_indices, prefix_indices, sm_scale,
+                        o, lse);
+}
+
+hipError_t launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStream_t s) {
+  return plan_launch_level(p, level, a, s);
+}
+
+}  // namespace
+
+namespace fi {
+
+TimerScope::TimerScope(hipStream_t st) : s(st) {
+  std::lock_guard<std::mutex> lk(g_timer_mu);
+  if (g_timer_on && g_timer_used < (int32_t)g_timer_events.size()) {
+    auto& pr = g_timer_events[g_timer_used++];
+    if (hipEventRecord(pr.first, s) == hipSuccess) stop = pr.second;
+  }
+}
+
+void TimerScope::done() {
+  if (stop) (void)hipEventRecord(stop, s);
+  stop = nullptr;
+}
+
+AttnArgs plan_attn_args(const fi_plan_t* p, const char* base, int level, const void* q,
+                        const void* k, const void* v, const int32_t* kv_indices,
+                        const int32_t* prefix_indices, float sm_scale, void* o, float* lse) {
   const fi_plan_desc& d = p->hp.desc;
+  auto at = [&](size_t off) { return (const int32_t*)(base + off); };
   AttnArgs a;
-  a.items = at<int32_t>(p, p->lay.items[level]);
-  a.worker_indptr = at<int32_t>(p, p->lay.windptr[level]);
+  a.items = at(p->lay.items[level]);
+  a.worker_indptr = at(p->lay.windptr[level]);
   // a graph-stable plan launches every level whatever this batch holds
   a.num_workers = (p->hp.stable || p->hp.level[level].num_items() > 0)
                       ? p->hp.level[level].num_workers : 0;
-  a.qlist = at<int32_t>(p, p->lay.qlist);
+  a.qlist = at(p->lay.qlist);
   a.q = (const uint16_t*)q;
   a.k_cache = (const uint16_t*)k;
   a.v_cache = (const uint16_t*)v;
@@ -77,8 +90,8 @@ AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, 
   a.prefix_indices = prefix_indices;
   a.o = (uint16_t*)o;
   a.lse = lse;
-  a.part_o = at<float>(p, p->lay.part_o);
-  a.part_lse = at<float>(p, p->lay.part_lse);
+  a.part_o = (float*)(base + p->lay.part_o);
+  a.part_lse = (float*)(base + p->lay.part_lse);
   a.k_scale = nullptr;
   a.v_scale = nullptr;
   a.k_bscale = nullptr;
@@ -92,13 +105,37 @@ AttnArgs attn_args(const fi_plan_t* p, int level, const void* q, const void* k, 
   return a;
 }
 
-hipError_t launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStream_t s) {
+hipError_t plan_launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStream_t s) {
   const int D = p->hp.desc.head_dim;
   if (p->hp.level[level].rows_per_block == ROWS_WIDE)
     return launch_wide(a, D, p->hp.desc.kind == FI_KIND_CASCADE && level == 0, s);
   if (p->hp.desc.decode_engine == FI_ENGINE_VALU) return launch_decode_valu(a, D, s);
   return launch_decode(a, D, s);
 }
+
+hipError_t plan_launch_merge(const fi_plan_t* p, const char* base, void* o, float* lse,
+                             hipStream_t s) {
+  MergeArgs m;
+  m.merges = (const int32_t*)(base + p->lay.merges);
+  // launch sizing: the plan's records, or a graph-stable plan's capacity
+  m.num_merges = p->hp.stable ? (int32_t)p->hp.cap_merges
+                              : (int32_t)(p->hp.merges.size() / MERGE_INTS);
+  m.parts = (const int32_t*)(base + p->lay.parts);
+  m.part_o = (const float*)(base + p->lay.part_o);
+  m.part_lse = (const float*)(base + p->lay.part_lse);
+  m.o = (uint16_t*)o;
+  m.lse = lse;
+  m.num_qo_heads = p->hp.desc.num_qo_heads;
+  m.head_dim = p->hp.desc.head_dim;
+  m.group = p->hp.desc.num_qo_heads / p->hp.desc.num_kv_heads;
+  m.rows_per_record = p->hp.stable ? MERGE_ROWS : p->hp.merge_rows;
+  m.counts = (const int32_t*)(base + p->lay.meta);
+  return launch_merge(m, s);
+}
+
+}  // namespace fi
+
+namespace {
 
 // A pod plan's two levels in one launch of a fixed shape: every worker slot of
 // both roles, whatever this batch's split.
@@ -114,22 +151,7 @@ hipError_t launch_fused(const fi_plan_t* p, const void* q, const void* k, const 
 }
 
 fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
-  MergeArgs m;
-  m.merges = at<int32_t>(p, p->lay.merges);
-  // launch sizing: the plan's records, or a graph-stable plan's capacity
-  m.num_merges = p->hp.stable ? (int32_t)p->hp.cap_merges
-                              : (int32_t)(p->hp.merges.size() / MERGE_INTS);
-  m.parts = at<int32_t>(p, p->lay.parts);
-  m.part_o = at<float>(p, p->lay.part_o);
-  m.part_lse = at<float>(p, p->lay.part_lse);
-  m.o = (uint16_t*)o;
-  m.lse = lse;
-  m.num_qo_heads = p->hp.desc.num_qo_heads;
-  m.head_dim = p->hp.desc.head_dim;
-  m.group = p->hp.desc.num_qo_heads / p->hp.desc.num_kv_heads;
-  m.rows_per_record = p->hp.stable ? MERGE_ROWS : p->hp.merge_rows;
-  m.counts = at<int32_t>(p, p->lay.meta);
-  return hip_status(launch_merge(m, s), "merge launch");
+  return hip_status(plan_launch_merge(p, p->dev_base, o, lse, s), "merge launch");
 }
 
 }  // namespace

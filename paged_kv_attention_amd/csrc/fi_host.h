@@ -78,4 +78,28 @@ struct fi_plan {
   fi::Layout lay;
   bool on_device = false;
   char* dev_base = nullptr;   // caller's device workspace
+  std::vector<char> host_blob;   // host-only plans: the int32 sections as laid out
 };
+
+namespace fi {
+
+// Kernel arguments of level `level` of plan p, whose workspace sits at device
+// address `base` (the caller's workspace, or the library's static scratch).
+AttnArgs plan_attn_args(const fi_plan_t* p, const char* base, int level, const void* q,
+                        const void* k, const void* v, const int32_t* kv_indices,
+                        const int32_t* prefix_indices, float sm_scale, void* o, float* lse);
+// The attention launch of a single-level plan (decode engines or wide kernel).
+hipError_t plan_launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStream_t s);
+// The merge launch of plan p with its workspace at `base`.
+hipError_t plan_launch_merge(const fi_plan_t* p, const char* base, void* o, float* lse,
+                             hipStream_t s);
+
+// Kernel timer hooks (no-ops unless fi_timer_begin enabled them).
+struct TimerScope {
+  hipStream_t s;
+  hipEvent_t stop = nullptr;
+  explicit TimerScope(hipStream_t st);
+  void done();
+};
+
+}  // namespace fi

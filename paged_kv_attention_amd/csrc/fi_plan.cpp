@@ -760,6 +760,27 @@ static fi_status begin_plan(const fi_plan_desc* desc, void* ws_dev, void* ws_hos
   return FI_OK;
 }
 
+// The plan's int32 sections at their layout offsets (L.blob_bytes bytes at h;
+// the bytes between sections are left as they are).
+static void fill_blob(const HostPlan& hp, const Layout& L, char* h) {
+  for (int l = 0; l < 2; ++l) {
+    if (!hp.level[l].items.empty())
+      memcpy(h + L.items[l], hp.level[l].items.data(), hp.level[l].items.size() * 4);
+    if (!hp.level[l].worker_indptr.empty())
+      memcpy(h + L.windptr[l], hp.level[l].worker_indptr.data(),
+             hp.level[l].worker_indptr.size() * 4);
+  }
+  if (!hp.merges.empty()) memcpy(h + L.merges, hp.merges.data(), hp.merges.size() * 4);
+  if (!hp.parts.empty()) memcpy(h + L.parts, hp.parts.data(), hp.parts.size() * 4);
+  if (!hp.qlist.empty()) memcpy(h + L.qlist, hp.qlist.data(), hp.qlist.size() * 4);
+  if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
+  const int32_t meta[META_INTS] = {hp.pod_wide_blocks,
+                                   (int32_t)(hp.merges.size() / MERGE_INTS), hp.merge_rows,
+                                   (int32_t)(hp.scatter.size() / 2)};
+  memcpy(h + L.meta, meta, sizeof(meta));
+  if (!hp.plist.empty()) memcpy(h + L.plist, hp.plist.data(), hp.plist.size() * 4);
+}
+
 // Lay the built plan out, check the caller's workspace, and upload (the
 // pinned staging buffer is reused only after its previous upload was read).
 struct Caps;
@@ -807,23 +828,7 @@ static fi_status finish_plan(fi_plan_t* p, const Caps* caps, void* ws_dev, size_
       delete p;
       return set_error(FI_ERR_HIP, "waiting for the previous upload: %s", hipGetErrorString(e));
     }
-    char* h = (char*)ws_host;
-    for (int l = 0; l < 2; ++l) {
-      if (!hp.level[l].items.empty())
-        memcpy(h + L.items[l], hp.level[l].items.data(), hp.level[l].items.size() * 4);
-      if (!hp.level[l].worker_indptr.empty())
-        memcpy(h + L.windptr[l], hp.level[l].worker_indptr.data(),
-               hp.level[l].worker_indptr.size() * 4);
-    }
-    if (!hp.merges.empty()) memcpy(h + L.merges, hp.merges.data(), hp.merges.size() * 4);
-    if (!hp.parts.empty()) memcpy(h + L.parts, hp.parts.data(), hp.parts.size() * 4);
-    if (!hp.qlist.empty()) memcpy(h + L.qlist, hp.qlist.data(), hp.qlist.size() * 4);
-    if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
-    const int32_t meta[META_INTS] = {hp.pod_wide_blocks,
-                                     (int32_t)(hp.merges.size() / MERGE_INTS), hp.merge_rows,
-                                     (int32_t)(hp.scatter.size() / 2)};
-    memcpy(h + L.meta, meta, sizeof(meta));
-    if (!hp.plist.empty()) memcpy(h + L.plist, hp.plist.data(), hp.plist.size() * 4);
+    fill_blob(hp, L, (char*)ws_host);
     e = hipMemcpyAsync(ws_dev, ws_host, L.blob_bytes, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) {
       if (!ev) {
@@ -841,6 +846,11 @@ static fi_status finish_plan(fi_plan_t* p, const Caps* caps, void* ws_dev, size_
     }
     p->on_device = true;
     p->dev_base = (char*)ws_dev;
+  } else {
+    // a host-only plan keeps its int32 sections laid out as on the device, so
+    // that a run call can upload them itself (fi_paged_decode_noalloc)
+    p->host_blob.assign(L.blob_bytes, 0);
+    fill_blob(hp, L, p->host_blob.data());
   }
   *out = p;
   return FI_OK;
