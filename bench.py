@@ -223,7 +223,8 @@ def explore(args, dev):
               engine=args.engine)
     if w.kind == "decode":
         plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
-                       w.head_dim, w.page_size, device=dev, kv_format=args.kv, **kw)
+                       w.head_dim, w.page_size, device=dev, kv_format=args.kv, merge=args.merge,
+                       **kw)
         if args.kv == "fp8":
             call = lambda: fi.paged_decode_fp8(plan, g.q, g.k_fp8, g.v_fp8, g.k_scale,  # noqa
                                                g.v_scale, g.kv_indices, w.sm_scale)
@@ -286,6 +287,8 @@ def explore(args, dev):
     extra = {}
     if w.kind != "decode":
         extra = {"launch": args.launch, "pod_wide_blocks": plan.info()["pod_wide_blocks"]}
+    else:
+        extra = {"merge": "fused" if plan.info()["fused_merge"] else "separate"}
     print(json.dumps({"workload": name, "mode": args.mode,
                       "engine": args.engine, "kv": args.kv, **extra,
                       "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
@@ -319,6 +322,8 @@ def main():
                          "(exploratory lines: the cold-cache time)")
     ap.add_argument("--config", type=int, default=CONFIG_INDEX,
                     help="other configurations print an exploratory line (not the bench line)")
+    ap.add_argument("--explore", action="store_true",
+                    help="print the exploratory line for the headline configuration too")
     ap.add_argument("--pod-mix", action="store_true",
                     help="exploratory line on the chunked-prefill mixed batch (64 decode "
                          "requests beside two 512-token prefill chunks)")
@@ -328,6 +333,9 @@ def main():
     ap.add_argument("--launch", choices=("default", "pod", "separate"), default="default",
                     help="append and cascade workloads: one POD launch for both kinds of rows, "
                          "or one launch per kind")
+    ap.add_argument("--merge", choices=("default", "fused", "separate"), default="default",
+                    help="decode: fold split units in the attention kernel (default) or in a "
+                         "merge launch after it")
     ap.add_argument("--pod-wide-blocks", type=int, default=0,
                     help="POD launch: workgroups of the wide role (0 = the plan's choice)")
     args = ap.parse_args()
@@ -343,7 +351,8 @@ def main():
 
     dev = torch.device("cuda:0")
     fi.load()
-    if args.config != CONFIG_INDEX or args.kv != "bf16" or args.pod_mix or args.sparse_video:
+    if (args.config != CONFIG_INDEX or args.kv != "bf16" or args.pod_mix or args.sparse_video
+            or args.explore):
         explore(args, dev)
         return
     print(f"bench: generating {CONFIG_NAMES[CONFIG_INDEX]}", file=sys.stderr, flush=True)
@@ -353,7 +362,7 @@ def main():
 
     plan_kw = dict(deterministic=args.mode == "deterministic",
                    workers_per_cu=args.workers_per_cu, min_chunk_pages=args.min_chunk_pages,
-                   det_chunk_pages=args.det_chunk_pages, engine=args.engine)
+                   det_chunk_pages=args.det_chunk_pages, engine=args.engine, merge=args.merge)
     t0 = time.perf_counter()
     plan = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                    w.page_size, device=dev, **plan_kw)
@@ -391,9 +400,9 @@ def main():
     torch.cuda.synchronize()
     ms_total = ev0.elapsed_time(ev1)
     ms_per_step = ms_total / args.steps
-    # The attention kernel's own duration: the same calls again, each launch
-    # bracketed by HIP events on its stream (the events add a few us per call,
-    # which is why they stay out of the region above).
+    # The attention kernel's own duration: the same calls again, each attention
+    # launch recording a HIP event pair in its dispatch packet on its stream
+    # (the start and end of the kernel's execution, as a kernel trace sees it).
     with fi.KernelTimer(args.steps) as kt:
         for _ in range(args.steps):
             step()
@@ -415,8 +424,9 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(nbytes["total"]),
             "kernel": "decode_kernel<128,2>", "algorithmic_bytes_per_launch": nbytes["total"],
             "avg_launch_us": round(kern_ms * 1e3, 2),
-            "timing": "avg of per-launch HIP events on the launch stream, a second pass of the "
-                      "same steps"}
+            "timing": "avg over a second pass of the same steps of each attention kernel's "
+                      "execution, HIP events recorded in its dispatch (hipExtLaunchKernel) on "
+                      "the launch stream"}
     res = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),

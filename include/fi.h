@@ -105,6 +105,23 @@ typedef enum fi_kv_format {
                        kernel is bound by ALU work and latency, not by HBM)   */
 } fi_kv_format;
 
+/* Where a decode plan's split units are merged (PR #4038, "What it does":
+ * fp32 partials reduced in a fixed order). By default a merge kernel runs
+ * after the attention kernel. FI_MERGE_FUSED (decode plans on the matrix-core
+ * engine) folds them inside the attention kernel instead: when a wave's items
+ * are done, each partial item counts in at its unit's merge record (a vector
+ * atomic at agent scope after a release of its partial rows), and the wave
+ * whose count completes the record folds it in part order with the merge
+ * kernel's arithmetic, so the bits are the same. It saves the merge launch
+ * but measured slower on MI355X: the release and acquire write back and
+ * invalidate an XCD's L2 for every wave. Other plans ignore the field. */
+typedef enum fi_merge_mode {
+  FI_MERGE_DEFAULT = 0,   /* a merge launch after the attention kernel          */
+  FI_MERGE_FUSED = 1,     /* folded in the decode kernels (decode plans, matrix
+                             cores; the VALU engine uses the merge launch)     */
+  FI_MERGE_SEPARATE = 2   /* a merge launch (the default)                       */
+} fi_merge_mode;
+
 /* Plan description. Zero in an optional field selects its default. */
 typedef struct fi_plan_desc {
   int32_t kind;              /* fi_kind                                        */
@@ -144,6 +161,7 @@ typedef struct fi_plan_desc {
   int32_t cap_qo_tokens;     /* append: sum of query tokens                   */
   int32_t cap_prefix_pages;  /* cascade: sum of the groups' prefix pages      */
   int32_t kv_format;         /* decode: fi_kv_format (default FI_KV_BF16)     */
+  int32_t merge_mode;        /* fi_merge_mode (default 0)                     */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;
@@ -178,6 +196,11 @@ typedef struct fi_plan_info {
                                     rest run the decode role), else 0 */
   int32_t num_plist;             /* block-sparse plans: the page lists the plan */
   const int32_t* plist;          /* built (items' page offsets index it)        */
+  int32_t fused_merge;           /* 1: split units are folded in the kernel    */
+  const int32_t* item_rec;       /* fused: per level-0 item, its merge record
+                                    (-1 for an item writing final rows)        */
+  int32_t num_empty_recs;        /* fused: records of units with no keys, which */
+  const int32_t* empty_recs;     /* the kernel's workers write at start        */
 } fi_plan_info;
 
 /* Upper bound on the device and pinned-host workspace bytes of any plan with

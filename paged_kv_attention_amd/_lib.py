@@ -19,6 +19,7 @@ FI_DTYPE_BF16, FI_DTYPE_F32 = 0, 1
 FI_ENGINE_DEFAULT, FI_ENGINE_MFMA, FI_ENGINE_VALU = range(3)
 FI_LAUNCH_DEFAULT, FI_LAUNCH_POD, FI_LAUNCH_SEPARATE = range(3)
 FI_KV_BF16, FI_KV_FP8, FI_KV_MXFP4 = range(3)
+FI_MERGE_DEFAULT, FI_MERGE_FUSED, FI_MERGE_SEPARATE = range(3)
 FI_ITEM_INTS, FI_MERGE_INTS = 12, 6
 FI_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -31,7 +32,7 @@ class PlanDesc(ctypes.Structure):
         "kind", "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "causal",
         "deterministic", "det_chunk_pages", "min_chunk_pages", "num_cus", "workers_per_cu",
         "num_prefix_groups", "decode_engine", "max_prefix_depth", "launch", "pod_wide_blocks", "cap_batch", "cap_kv_pages",
-        "cap_qo_tokens", "cap_prefix_pages", "kv_format")]
+        "cap_qo_tokens", "cap_prefix_pages", "kv_format", "merge_mode")]
 
 
 I32P = POINTER(c_int32)
@@ -46,6 +47,8 @@ class PlanInfo(ctypes.Structure):
         ("num_qlist", c_int32), ("qlist", I32P), ("num_part_rows", c_int32),
         ("num_scatter", c_int32), ("dev_bytes_used", c_size_t), ("host_bytes_used", c_size_t),
         ("pod_wide_blocks", c_int32), ("num_plist", c_int32), ("plist", I32P),
+        ("fused_merge", c_int32), ("item_rec", I32P), ("num_empty_recs", c_int32),
+        ("empty_recs", I32P),
     ]
 
 

@@ -21,6 +21,8 @@ _ENGINES = {"default": L.FI_ENGINE_DEFAULT, "mfma": L.FI_ENGINE_MFMA, "valu": L.
 _LAUNCHES = {"default": L.FI_LAUNCH_DEFAULT, "pod": L.FI_LAUNCH_POD,
              "separate": L.FI_LAUNCH_SEPARATE}
 _KV_FORMATS = {"bf16": L.FI_KV_BF16, "fp8": L.FI_KV_FP8, "mxfp4": L.FI_KV_MXFP4}
+_MERGES = {"default": L.FI_MERGE_DEFAULT, "fused": L.FI_MERGE_FUSED,
+           "separate": L.FI_MERGE_SEPARATE}
 
 
 def _host_i32(x) -> Optional[np.ndarray]:
@@ -79,7 +81,11 @@ class Plan:
     """A work plan for one batch (fi_plan). ``device=None`` builds it on the
     host only (needs ``num_cus``), which the run calls refuse. ``kv_format``
     ("bf16", "fp8" or "mxfp4") names the cache a decode plan will be run on:
-    it only picks the default ``workers_per_cu`` (12 for "mxfp4", else 4). ``capacity =
+    it only picks the default ``workers_per_cu`` (12 for "mxfp4", else 4). ``merge``
+    ("default", "fused" or "separate") says where a decode plan's split units
+    are merged: by a merge launch after the attention kernel (the default and
+    "separate") or inside the decode kernels ("fused", matrix-core engine;
+    same bits, measured slower on MI355X). ``capacity =
     (batch, kv_pages, qo_tokens, prefix_pages[, prefix_depth])`` makes it
     graph-stable: laid out for at most those sizes (and nested prefixes at
     most ``prefix_depth`` deep, default 1), so that a run call captured in a
@@ -92,7 +98,8 @@ class Plan:
                  deterministic: bool = False, det_chunk_pages: int = 0, min_chunk_pages: int = 0,
                  num_cus: int = 0, workers_per_cu: int = 0, engine: str = "default",
                  launch: str = "default", pod_wide_blocks: int = 0, kv_format: str = "bf16",
-                 device="cuda", workspace: Optional[Workspace] = None, capacity=None):
+                 merge: str = "default", device="cuda", workspace: Optional[Workspace] = None,
+                 capacity=None):
         lib = L.load()
         self.kind = kind
         self._ha = dict(kv_indptr=_host_i32(kv_indptr), kv_len=_host_i32(kv_len),
@@ -111,7 +118,7 @@ class Plan:
                                num_prefix_groups=ng, decode_engine=_ENGINES[engine],
                                max_prefix_depth=_prefix_depth(self._ha["prefix_parent"], ng),
                                launch=_LAUNCHES[launch], pod_wide_blocks=pod_wide_blocks,
-                               kv_format=_KV_FORMATS[kv_format])
+                               kv_format=_KV_FORMATS[kv_format], merge_mode=_MERGES[merge])
         if capacity is not None:
             cap = [int(x) for x in capacity] + [1] * (5 - len(capacity))
             (self.desc.cap_batch, self.desc.cap_kv_pages, self.desc.cap_qo_tokens,
@@ -180,7 +187,10 @@ class Plan:
                     parts=arr(inf.parts, inf.num_parts), qlist=arr(inf.qlist, inf.num_qlist),
                     num_part_rows=inf.num_part_rows, num_scatter=inf.num_scatter,
                     dev_bytes_used=inf.dev_bytes_used, host_bytes_used=inf.host_bytes_used,
-                    pod_wide_blocks=inf.pod_wide_blocks, plist=arr(inf.plist, inf.num_plist))
+                    pod_wide_blocks=inf.pod_wide_blocks, plist=arr(inf.plist, inf.num_plist),
+                    fused_merge=bool(inf.fused_merge),
+                    item_rec=arr(inf.item_rec, inf.num_items[0] if inf.fused_merge else 0),
+                    empty_recs=arr(inf.empty_recs, inf.num_empty_recs))
 
 
 class BlockSparsePlan(Plan):

@@ -58,16 +58,31 @@ hipError_t launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStr
 
 namespace fi {
 
+LaunchTiming& launch_timing() {
+  static thread_local LaunchTiming t;
+  return t;
+}
+
+// The scope hands its event pair to the launches in it (launch_timed); if it
+// launched nothing, the pair is recorded around nothing, so that every pair
+// the timer hands out has been recorded.
 TimerScope::TimerScope(hipStream_t st) : s(st) {
   std::lock_guard<std::mutex> lk(g_timer_mu);
   if (g_timer_on && g_timer_used < (int32_t)g_timer_events.size()) {
     auto& pr = g_timer_events[g_timer_used++];
-    if (hipEventRecord(pr.first, s) == hipSuccess) stop = pr.second;
+    stop = pr.second;
+    launch_timing() = LaunchTiming{pr.first, pr.second};
   }
 }
 
 void TimerScope::done() {
-  if (stop) (void)hipEventRecord(stop, s);
+  if (!stop) return;
+  LaunchTiming& t = launch_timing();
+  if (t.start) {   // no kernel took the events
+    (void)hipEventRecord(t.start, s);
+    (void)hipEventRecord(stop, s);
+  }
+  t = LaunchTiming{};
   stop = nullptr;
 }
 
@@ -79,8 +94,11 @@ AttnArgs plan_attn_args(const fi_plan_t* p, const char* base, int level, const v
   AttnArgs a;
   a.items = at(p->lay.items[level]);
   a.worker_indptr = at(p->lay.windptr[level]);
-  // a graph-stable plan launches every level whatever this batch holds
-  a.num_workers = (p->hp.stable || p->hp.level[level].num_items() > 0)
+  // a graph-stable plan launches every level whatever this batch holds, and
+  // a fused-merge plan whenever it has records to write (units with no keys)
+  const bool fused = p->hp.fused && level == 0;
+  a.num_workers = (p->hp.stable || p->hp.level[level].num_items() > 0 ||
+                   (fused && !p->hp.empty_recs.empty()))
                       ? p->hp.level[level].num_workers : 0;
   a.qlist = at(p->lay.qlist);
   a.q = (const uint16_t*)q;
@@ -96,6 +114,12 @@ AttnArgs plan_attn_args(const fi_plan_t* p, const char* base, int level, const v
   a.v_scale = nullptr;
   a.k_bscale = nullptr;
   a.v_bscale = nullptr;
+  a.item_rec = fused ? at(p->lay.item_rec) : nullptr;
+  a.counters = fused ? (int32_t*)(base + p->lay.counters) : nullptr;
+  a.merges = at(p->lay.merges);
+  a.parts = at(p->lay.parts);
+  a.empty_recs = at(p->lay.empty_recs);
+  a.meta = at(p->lay.meta);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.num_qo_heads = d.num_qo_heads;
   a.num_kv_heads = d.num_kv_heads;
@@ -151,6 +175,7 @@ hipError_t launch_fused(const fi_plan_t* p, const void* q, const void* k, const 
 }
 
 fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {
+  if (p->hp.fused) return FI_OK;   // the attention kernel folded its split units
   return hip_status(plan_launch_merge(p, p->dev_base, o, lse, s), "merge launch");
 }
 

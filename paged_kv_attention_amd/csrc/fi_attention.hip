@@ -51,11 +51,11 @@ __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
 template <int D>
 hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    hipLaunchKernelGGL((decode_kernel<D, 4>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_kernel<D, 4>), grid, dim3(256), s, a);
   } else if (a.page_size == 16) {
-    hipLaunchKernelGGL((decode_kernel<D, 2>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_kernel<D, 2>), grid, dim3(256), s, a);
   } else {
-    hipLaunchKernelGGL((decode_kernel<D, 1>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_kernel<D, 1>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }

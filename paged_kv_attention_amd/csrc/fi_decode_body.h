@@ -136,6 +136,7 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
   if (w >= a.num_workers) return;
+  fused_merge_start<D>(a, w, lane);
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
   const int i_begin = ld_uniform(a.worker_indptr, w);
   if (i_begin >= i_end) return;
@@ -207,6 +208,7 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
     while (advance(TA, TB) && advance(TB, TA)) {
     }
   }
+  fused_merge_end<D>(a, i_begin, i_end, lane);
 }
 
 }  // namespace dec

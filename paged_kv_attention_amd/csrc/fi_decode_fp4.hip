@@ -290,6 +290,7 @@ __global__ __launch_bounds__(256) void decode_mxfp4_kernel(AttnArgs a) {
   const int wave = uniform(threadIdx.x >> 6);
   const int w = blockIdx.x * kWaves4 + wave;
   if (w >= a.num_workers) return;
+  fused_merge_start<D>(a, w, lane);
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
   const int i_begin = ld_uniform(a.worker_indptr, w);
   if (i_begin >= i_end) return;
@@ -368,16 +369,17 @@ __global__ __launch_bounds__(256) void decode_mxfp4_kernel(AttnArgs a) {
   }
   // drain this wave's copies before it exits (the stages are its own)
   wait_vmcnt<0>();
+  fused_merge_end<D>(a, i_begin, i_end, lane);
 }
 
 template <int D, int R>
 hipError_t launch_f4(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    hipLaunchKernelGGL((decode_mxfp4_kernel<D, 4, R>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_mxfp4_kernel<D, 4, R>), grid, dim3(256), s, a);
   } else if (a.page_size == 16) {
-    hipLaunchKernelGGL((decode_mxfp4_kernel<D, 2, R>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_mxfp4_kernel<D, 2, R>), grid, dim3(256), s, a);
   } else {
-    hipLaunchKernelGGL((decode_mxfp4_kernel<D, 1, R>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_mxfp4_kernel<D, 1, R>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }

@@ -275,6 +275,7 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(AttnArgs a) {
   const int col = lane & 15, grp = lane >> 4;
   const int w = blockIdx.x * WAVES_PER_BLOCK + uniform(threadIdx.x >> 6);
   if (w >= a.num_workers) return;
+  fused_merge_start<D>(a, w, lane);
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
   const int i_begin = ld_uniform(a.worker_indptr, w);
   if (i_begin >= i_end) return;
@@ -333,16 +334,17 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(AttnArgs a) {
   while (advance(TA, TF) && advance(TB, TA) && advance(TC, TB) && advance(TD, TC) &&
          advance(TE, TD) && advance(TF, TE)) {
   }
+  fused_merge_end<D>(a, i_begin, i_end, lane);
 }
 
 template <int D>
 hipError_t launch_f8(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    hipLaunchKernelGGL((decode_fp8_kernel<D, 4>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_fp8_kernel<D, 4>), grid, dim3(256), s, a);
   } else if (a.page_size == 16) {
-    hipLaunchKernelGGL((decode_fp8_kernel<D, 2>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_fp8_kernel<D, 2>), grid, dim3(256), s, a);
   } else {
-    hipLaunchKernelGGL((decode_fp8_kernel<D, 1>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_fp8_kernel<D, 1>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }

@@ -318,11 +318,11 @@ __global__ __launch_bounds__(256) void decode_valu_kernel(AttnArgs a) {
 template <int D, int GM>
 hipError_t launch_v(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    hipLaunchKernelGGL((decode_valu_kernel<D, 4, GM>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_valu_kernel<D, 4, GM>), grid, dim3(256), s, a);
   } else if (a.page_size == 16) {
-    hipLaunchKernelGGL((decode_valu_kernel<D, 2, GM>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_valu_kernel<D, 2, GM>), grid, dim3(256), s, a);
   } else {
-    hipLaunchKernelGGL((decode_valu_kernel<D, 1, GM>), grid, dim3(256), 0, s, a);
+    launch_timed((decode_valu_kernel<D, 1, GM>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }

@@ -245,5 +245,124 @@ __device__ __forceinline__ void load_q_rows(const AttnArgs& a, const Item& it, i
   }
 }
 
+// ---------------------------------------------------------------- fused merge
+
+// Per element of a merge: acc = fma(w, v, acc), z = z + w, in part order;
+// o = acc * (1 / z), lse = M + ln z (M the parts' max lse). The merge kernel
+// (fi_merge.hip) and the fused fold below run exactly these operations, so a
+// row's bits do not depend on which of them merged it.
+
+// Fold merge record e into the final rows (16 lanes per row, four rows per
+// pass): row k < n_rows of the record is unit row row0 + k, query q_base +
+// (row0 + k) / G, head kv_head * G + (row0 + k) % G; its parts are partial
+// rows parts[off + j] + k, j = 0..n-1. With n = 0 the rows get o = 0,
+// lse = -inf.
+template <int D>
+__device__ __forceinline__ void fold_record(const AttnArgs& a, int e, int lane) {
+  constexpr int FPL = D / 16;   // outputs per lane
+  constexpr int kBatch = 4;     // parts loaded together
+  typedef float vec __attribute__((ext_vector_type(FPL)));
+  typedef uint32_t packed __attribute__((ext_vector_type(FPL / 2)));
+  const int32_t* m = a.merges + (int64_t)e * MERGE_INTS;
+  const int q_base = ld_uniform(m, M_QBASE), row0 = ld_uniform(m, M_ROW0);
+  const int nh = ld_uniform(m, M_NROWS), kv_head = ld_uniform(m, M_KVHEAD);
+  const int off = ld_uniform(m, M_OFF), n = ld_uniform(m, M_N);
+  const int G = a.group;
+  const int col = (lane & 15) * FPL;
+  for (int h0 = 0; h0 < nh; h0 += 4) {
+    const int row = h0 + (lane >> 4);
+    const int rowc = row < nh ? row : h0;     // lanes past the rows load a real row
+    float M = neg_inf();
+    for (int j0 = 0; j0 < n; j0 += 2 * kBatch) {
+      float l[2 * kBatch];
+#pragma unroll
+      for (int u = 0; u < 2 * kBatch; ++u)
+        l[u] = j0 + u < n ? a.part_lse[ld_uniform(a.parts, off + j0 + u) + rowc] : neg_inf();
+#pragma unroll
+      for (int u = 0; u < 2 * kBatch; ++u) M = fmaxf(M, l[u]);
+    }
+    float z = 0.f;
+    vec acc = vec{};
+    for (int j0 = 0; j0 < n; j0 += kBatch) {
+      float l[kBatch];
+      vec v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j0 + u < n) {
+          const int pr = ld_uniform(a.parts, off + j0 + u) + rowc;
+          l[u] = a.part_lse[pr];
+          v[u] = *(const vec*)(a.part_o + (int64_t)pr * D + col);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (j0 + u < n) {
+          const float w = (l[u] == neg_inf()) ? 0.f : expf(l[u] - M);
+          z += w;
+#pragma unroll
+          for (int i = 0; i < FPL; ++i) acc[i] = __builtin_fmaf(w, v[u][i], acc[i]);
+        }
+      }
+    }
+    if (row >= nh) continue;
+    const float inv = z > 0.f ? 1.f / z : 0.f;
+    const int rho = row0 + row;
+    const int64_t orow = (int64_t)(q_base + rho / G) * a.num_qo_heads + kv_head * G + rho % G;
+    packed pk;
+#pragma unroll
+    for (int i = 0; i < FPL / 2; ++i) pk[i] = pack2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+    *(packed*)(a.o + orow * D + col) = pk;
+    if ((lane & 15) == 0 && a.lse) a.lse[orow] = z > 0.f ? M + logf(z) : neg_inf();
+  }
+}
+
+// At a worker's start: write the records of units with no keys, spread over
+// the workers.
+template <int D>
+__device__ __forceinline__ void fused_merge_start(const AttnArgs& a, int w, int lane) {
+  if (!a.item_rec) return;
+  const int n_empty = ld_uniform(a.meta, META_EMPTY);
+  for (int k = w; k < n_empty; k += a.num_workers) fold_record<D>(a, ld_uniform(a.empty_recs, k), lane);
+}
+
+// At the end of a worker's stream (so that the release below, which waits for
+// every load and store of the wave, drains no prefetch): count in each of its
+// partial items at the item's record -- one lane per item, all at once -- and
+// fold every record this wave completed.
+template <int D>
+__device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, int i_end,
+                                                int lane) {
+  if (!a.item_rec) return;
+  // the partial rows written by this wave become visible at agent scope (to
+  // a folding wave on another XCD) before any count that announces them
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  for (int i0 = i_begin; i0 < i_end; i0 += 64) {
+    const int i = i0 + lane;
+    int rec = -1;
+    bool last = false;
+    if (i < i_end) {
+      rec = a.item_rec[i];
+      if (rec >= 0) {
+        const int n = a.merges[(int64_t)rec * MERGE_INTS + M_N];
+        const int before =
+            __hip_atomic_fetch_add(a.counters + rec, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = before == n - 1;
+        // every chunk of the record has counted in: reset for the next call
+        if (last) __hip_atomic_store(a.counters + rec, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    uint64_t done = __ballot(last);
+    if (done) {
+      // the other chunks' partial rows, released before their counts
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      while (done) {
+        const int l = __builtin_ctzll(done);
+        done &= done - 1;
+        fold_record<D>(a, __builtin_amdgcn_readlane(rec, l), lane);
+      }
+    }
+  }
+}
+
 }  // namespace dev
 }  // namespace fi

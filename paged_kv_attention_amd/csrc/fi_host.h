@@ -23,6 +23,7 @@ struct Level {
   int32_t chunk_pages = 0;
   std::vector<int32_t> items;          // ITEM_INTS per item, grouped by worker
   std::vector<int32_t> worker_indptr;  // num_workers + 1
+  std::vector<int32_t> item_unit;      // per item (in items' order): its unit's index
   int32_t num_items() const { return (int32_t)(items.size() / ITEM_INTS); }
 };
 
@@ -41,6 +42,10 @@ struct HostPlan {
   int32_t pod_wide_blocks = 0;
   std::vector<int32_t> plist;    // block-sparse: the units' page lists
   int32_t merge_rows = 0;        // the most rows of any merge record
+  // fused merge (decode plans on the matrix cores): per level-0 item its
+  // merge record (-1: final rows), and the records of units with no keys
+  bool fused = false;
+  std::vector<int32_t> item_rec, empty_recs;
   // graph-stable plan (capacity given in the description): a fixed layout,
   // every launch made whatever the batch, sized by these capacities
   bool stable = false;
@@ -56,6 +61,7 @@ struct Layout {
   size_t merges = 0, parts = 0, qlist = 0, scatter = 0;
   size_t meta = 0;           // int32 [META_INTS]: counts the kernels read
   size_t plist = 0;          // block-sparse page lists
+  size_t item_rec = 0, counters = 0, empty_recs = 0;   // fused merge
   size_t blob_bytes = 0;     // int32 sections (host staging size)
   size_t part_o = 0, part_lse = 0;
   size_t dev_bytes = 0;      // blob + fp32 partial states
@@ -63,7 +69,7 @@ struct Layout {
 
 Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t n_merges,
                   size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
-                  int32_t head_dim, size_t n_plist = 0);
+                  int32_t head_dim, size_t n_plist = 0, bool fused = false);
 
 // Debug check of device page tables (fi_check.hip): zeroes *count, then adds
 // the number of ids outside [0, num_pages) in each non-NULL table.
@@ -99,6 +105,7 @@ struct TimerScope {
   hipStream_t s;
   hipEvent_t stop = nullptr;
   explicit TimerScope(hipStream_t st);
+  ~TimerScope() { done(); }
   void done();
 };
 

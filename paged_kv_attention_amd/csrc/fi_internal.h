@@ -22,10 +22,33 @@
 // token's page, slot within the page.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace fi {
+
+// Kernel timer (fi_timer_begin): while a run call is timed, its attention
+// launches record the timer's events in their own dispatch (the start event
+// on the first launch, the stop event on each), so the interval is the
+// kernels' execution, as a profiler's kernel trace measures it.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+LaunchTiming& launch_timing();   // this thread's
+
+// Launch an attention kernel (errors are left for hipGetLastError).
+template <typename K, typename... Args>
+inline void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  LaunchTiming& t = launch_timing();
+  if (t.stop) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args...);
+    t.start = nullptr;
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+  }
+}
 
 enum ItemField {
   F_Q_BASE = 0, F_ROW0, F_NROWS, F_KVHEAD, F_PAGEOFF, F_FLAGS,
@@ -47,7 +70,9 @@ constexpr int MERGE_ROWS = 16;
 // so that a launch captured in a graph follows a later plan into the same
 // workspace: the POD split, the merge records, their most rows, and the new
 // tokens to scatter.
-enum MetaField { META_POD_WIDE = 0, META_MERGES, META_MERGE_ROWS, META_SCATTER, META_INTS };
+enum MetaField {
+  META_POD_WIDE = 0, META_MERGES, META_MERGE_ROWS, META_SCATTER, META_EMPTY, META_INTS
+};
 // A wide level plans num_cus * max(1, workers_per_cu / 2) workgroups and
 // chunks of at least WIDE_CHUNK_FACTOR * min_chunk_pages pages.
 constexpr int WIDE_CHUNK_FACTOR = 2;
@@ -70,6 +95,18 @@ struct AttnArgs {
   const float* v_scale;    // FP8 cache only: the same for V
   const uint8_t* k_bscale; // MXFP4 cache only: E8M0 scale per 32 elements of a K row
   const uint8_t* v_bscale; // MXFP4 cache only: the same for V
+  // Fused merge (decode plans; item_rec == NULL: the merge kernel runs after).
+  // When a wave's stream of items ends, each of its partial items counts in at
+  // its merge record, and the wave that brings a record's count to its part
+  // count folds the record's rows in part order (the merge kernel's
+  // arithmetic); it then resets the count to 0 for the next call. Records of
+  // units with no keys are written (o = 0, lse = -inf) by the workers at start.
+  const int32_t* item_rec; // per item of the level: its merge record, or -1
+  int32_t* counters;       // per merge record: the level's chunks counted in
+  const int32_t* merges;
+  const int32_t* parts;
+  const int32_t* empty_recs;
+  const int32_t* meta;     // META_EMPTY: the number of empty_recs
   float scale_log2;        // sm_scale * log2(e): logits are kept in base 2
   int32_t num_qo_heads;
   int32_t num_kv_heads;

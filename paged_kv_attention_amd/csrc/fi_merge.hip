@@ -62,6 +62,11 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 template <int N> struct FVec { typedef float T __attribute__((ext_vector_type(N))); };
 template <> struct FVec<1> { typedef float T; };
 
+// Per element: acc = fma(w_j, v_j, acc) and z = z + w_j for j = 0, 1, ...;
+// o = acc * (1 / z); lse = M + ln z -- the same operations, in the same order,
+// as the fused fold at the end of the decode kernel (fold_record), so a row's
+// bits do not depend on which of the two merged it.
+//
 // One wavefront per RPW rows of a merge record (RPW = 1, 2 or 4: fewer,
 // fuller waves when there are many records). Lane j holds part j's row index
 // and the lse of each of the wave's rows (64 parts per pass), the wave
@@ -147,7 +152,12 @@ __device__ __forceinline__ void merge_rows(const MergeArgs& a, int e, int h0, in
       for (int u = 0; u < kFold; ++u) {
         if (b + u < cnt) {
           z += wb[u];
-          acc += wb[u] * v[u];
+          if constexpr (FPL == 1) {
+            acc = __builtin_fmaf(wb[u], v[u], acc);
+          } else {
+#pragma unroll
+            for (int i = 0; i < FPL; ++i) acc[i] = __builtin_fmaf(wb[u], v[u][i], acc[i]);
+          }
         }
       }
     }

@@ -10,9 +10,10 @@
 // that device current, and is what the kernels, the copy and the merge get.
 // Every call on a GPU reuses that GPU's array and leaves the last call's
 // contents there: calls that overlap on one GPU (two streams, or two threads)
-// race on it. Nothing in it needs to start at zero: each call uploads every
-// plan section the kernels read, and the attention kernel writes every
-// partial row before the merge reads it, both ordered on the call's stream.
+// race on it. Each call uploads every plan section the kernels read (the
+// fused merge's arrival counts among them, as zeros), and the attention
+// kernel writes every partial row before it is merged, both ordered on the
+// call's stream.
 
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -98,7 +99,7 @@ extern "C" fi_status fi_paged_decode_noalloc(const fi_plan_t* p, const void* q,
   if (e != hipSuccess)
     return set_error(FI_ERR_HIP, "fi_paged_decode_noalloc: attention launch: %s",
                      hipGetErrorString(e));
-  e = plan_launch_merge(p, base, o, lse, s);
+  if (!p->hp.fused) e = plan_launch_merge(p, base, o, lse, s);
   if (e != hipSuccess)
     return set_error(FI_ERR_HIP, "fi_paged_decode_noalloc: merge launch: %s",
                      hipGetErrorString(e));

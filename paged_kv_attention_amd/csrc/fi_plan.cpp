@@ -71,7 +71,7 @@ static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t n_merges,
                   size_t n_parts, size_t n_qlist, size_t n_scatter, size_t n_part_rows,
-                  int32_t head_dim, size_t n_plist) {
+                  int32_t head_dim, size_t n_plist, bool fused) {
   Layout L;
   size_t off = 0;
   auto take = [&](size_t n_int32) {
@@ -89,6 +89,11 @@ Layout layout_for(const int32_t num_workers[2], const size_t n_items[2], size_t 
   L.scatter = take(n_scatter * 2);
   L.meta = take(META_INTS);
   L.plist = take(n_plist);
+  // fused merge: per level-0 item its record, a count per record, and the
+  // list of records of units with no keys (at most one per record)
+  L.item_rec = take(fused ? n_items[0] : 0);
+  L.counters = take(fused ? n_merges : 0);
+  L.empty_recs = take(fused ? n_merges : 0);
   L.blob_bytes = off;
   L.part_o = off;
   off = align_up(off + n_part_rows * (size_t)head_dim * 4, 256);
@@ -208,7 +213,7 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
   lv.chunk_pages = (int32_t)c;
   lb.items.clear();
   lb.chunks.clear();
-  std::vector<int32_t> item_worker;
+  std::vector<int32_t> item_worker, item_unit;
   for (size_t ui = 0; ui < units.size(); ++ui) {
     const Unit& u = units[ui];
     const int32_t k = (int32_t)pieces[ui].size();
@@ -238,6 +243,7 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
       it.pages = (int32_t)(pc.p1 - pc.p0);
       lb.items.push_back(it);
       item_worker.push_back(pc.worker);
+      item_unit.push_back((int32_t)ui);
     }
     lb.chunks.emplace_back(k, std::move(dsts));
   }
@@ -264,10 +270,14 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
   }
   lv.items.clear();
   lv.items.reserve(n * ITEM_INTS);
+  lv.item_unit.clear();
+  lv.item_unit.reserve(n);
   lv.worker_indptr.assign(1, 0);
   for (int32_t w = 0; w < S; ++w) {
-    for (int32_t i : per[w])
+    for (int32_t i : per[w]) {
       lv.items.insert(lv.items.end(), lb.items[i].f, lb.items[i].f + ITEM_INTS);
+      lv.item_unit.push_back(item_unit[i]);
+    }
     lv.worker_indptr.push_back((int32_t)(lv.items.size() / ITEM_INTS));
   }
 }
@@ -348,6 +358,7 @@ fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
       lb[l].items.clear();
       lb[l].chunks.assign(units[l].size(), {0, {}});
       hp.level[l].items.clear();
+      hp.level[l].item_unit.clear();
       hp.level[l].chunk_pages = 0;
       hp.level[l].worker_indptr.assign(1, 0);
     }
@@ -364,11 +375,14 @@ fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
 // rows of a unit of k != 1 chunks are cut into records of MERGE_ROWS rows,
 // each over its chunks' partial rows in chunk order (k = 0, no keys: empty
 // records, which write o = 0 and lse = -inf).
-void unit_merges(const std::vector<Unit>& units, const LevelBuild& lb, HostPlan& hp) {
+std::vector<int32_t> unit_merges(const std::vector<Unit>& units, const LevelBuild& lb,
+                                 HostPlan& hp) {
+  std::vector<int32_t> first_rec(units.size(), -1);   // per unit: its first record
   for (size_t ui = 0; ui < units.size(); ++ui) {
     const Unit& u = units[ui];
     const int32_t k = lb.chunks[ui].first;
     if (k == 1) continue;
+    first_rec[ui] = (int32_t)(hp.merges.size() / MERGE_INTS);
     const std::vector<int32_t>& dsts = lb.chunks[ui].second;
     for (int32_t k0 = 0; k0 < u.n_rows; k0 += MERGE_ROWS) {
       const int32_t rec[MERGE_INTS] = {u.q_base, u.row0 + k0, std::min(MERGE_ROWS, u.n_rows - k0),
@@ -377,6 +391,7 @@ void unit_merges(const std::vector<Unit>& units, const LevelBuild& lb, HostPlan&
       for (int32_t dd : dsts) hp.parts.push_back(dd + k0);
     }
   }
+  return first_rec;
 }
 
 }  // namespace
@@ -440,6 +455,8 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.min_chunk_pages == 0) d.min_chunk_pages = 8;
   if (d.kv_format < FI_KV_BF16 || d.kv_format > FI_KV_MXFP4)
     return set_error(FI_ERR_INVALID_ARG, "kv_format %d", d.kv_format);
+  if (d.merge_mode < FI_MERGE_DEFAULT || d.merge_mode > FI_MERGE_SEPARATE)
+    return set_error(FI_ERR_INVALID_ARG, "merge_mode %d", d.merge_mode);
   if (d.kind != FI_KIND_DECODE) d.kv_format = FI_KV_BF16;
   // one wave per SIMD for the register-ring decode kernels; three for the
   // MXFP4 kernel, which staging through LDS leaves ALU- and latency-bound
@@ -449,6 +466,17 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.kind != FI_KIND_APPEND) d.causal = 0;   // (block-sparse: refused above if set)
   if (d.kind != FI_KIND_CASCADE) d.num_prefix_groups = 0;
   return FI_OK;
+}
+
+// FI_MERGE_FUSED decode plans on the matrix cores fold their split units at
+// the end of the attention kernel (its decode kernels count chunks in and the
+// last folds); every other plan launches the merge kernel after it. Separate
+// is the default: on MI355X the fused fold's agent-scope release and acquire
+// (an L2 write-back and invalidate of the XCD per wave) cost more than the
+// merge launch they save (Llama-like batch: 121 against 89 us per call).
+static bool fused_merge(const fi_plan_desc& d) {
+  return d.kind == FI_KIND_DECODE && d.decode_engine == FI_ENGINE_MFMA &&
+         d.merge_mode == FI_MERGE_FUSED;
 }
 
 static fi_status validate_table(const char* what, int32_t n, const int32_t* indptr,
@@ -473,6 +501,7 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
                        const int32_t* prefix_parent, HostPlan& hp) {
   const int32_t B = d.batch, Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
   const int32_t ps = d.page_size;
+  hp.fused = fused_merge(d);
   fi_status st = validate_table("kv", B, kv_indptr, kv_len, ps);
   if (st != FI_OK) return st;
   if (d.kind == FI_KIND_APPEND && B > 0) {
@@ -620,7 +649,16 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
                     append ? qo_indptr : nullptr, causal);
       build_level(units[0], d, false, next_row, lb[0], hp.level[0]);
     }
-    for (int l = 0; l < hp.num_levels; ++l) unit_merges(units[l], lb[l], hp);
+    std::vector<int32_t> first_rec[2];
+    for (int l = 0; l < hp.num_levels; ++l) first_rec[l] = unit_merges(units[l], lb[l], hp);
+    if (!append && hp.fused) {
+      // decode units have at most MERGE_ROWS rows: one record each
+      const Level& lv = hp.level[0];
+      hp.item_rec.resize(lv.item_unit.size());
+      for (size_t i = 0; i < lv.item_unit.size(); ++i) hp.item_rec[i] = first_rec[0][lv.item_unit[i]];
+      for (size_t e = 0; e < hp.merges.size() / MERGE_INTS; ++e)
+        if (hp.merges[e * MERGE_INTS + M_N] == 0) hp.empty_recs.push_back((int32_t)e);
+    }
     if (append) {
       for (int32_t r = 0; r < B; ++r) {
         const int32_t nq = qo_indptr[r + 1] - qo_indptr[r];
@@ -776,9 +814,17 @@ static void fill_blob(const HostPlan& hp, const Layout& L, char* h) {
   if (!hp.scatter.empty()) memcpy(h + L.scatter, hp.scatter.data(), hp.scatter.size() * 4);
   const int32_t meta[META_INTS] = {hp.pod_wide_blocks,
                                    (int32_t)(hp.merges.size() / MERGE_INTS), hp.merge_rows,
-                                   (int32_t)(hp.scatter.size() / 2)};
+                                   (int32_t)(hp.scatter.size() / 2),
+                                   (int32_t)hp.empty_recs.size()};
   memcpy(h + L.meta, meta, sizeof(meta));
   if (!hp.plist.empty()) memcpy(h + L.plist, hp.plist.data(), hp.plist.size() * 4);
+  if (hp.fused) {
+    if (!hp.item_rec.empty()) memcpy(h + L.item_rec, hp.item_rec.data(), hp.item_rec.size() * 4);
+    // every count starts at 0; the kernel's last arrival resets its own
+    memset(h + L.counters, 0, hp.merges.size() / MERGE_INTS * 4);
+    if (!hp.empty_recs.empty())
+      memcpy(h + L.empty_recs, hp.empty_recs.data(), hp.empty_recs.size() * 4);
+  }
 }
 
 // Lay the built plan out, check the caller's workspace, and upload (the
@@ -805,7 +851,7 @@ static fi_status finish_plan(fi_plan_t* p, const Caps* caps, void* ws_dev, size_
   } else {
     p->lay = layout_for(workers, n_items, hp.merges.size() / MERGE_INTS, hp.parts.size(),
                         hp.qlist.size(), hp.scatter.size() / 2, (size_t)hp.num_part_rows,
-                        d.head_dim, hp.plist.size());
+                        d.head_dim, hp.plist.size(), hp.fused);
   }
   const Layout& L = p->lay;
   if (ws_dev) {
@@ -864,6 +910,7 @@ struct Caps {
   int32_t workers[2] = {0, 0};
   size_t items[2] = {0, 0};
   size_t merges = 0, parts = 0, qlist = 0, scatter = 0, part_rows = 0;
+  bool fused = false;
 };
 
 static void bound_counts(const fi_plan_desc& d, int32_t num_cus, int64_t max_kv_pages,
@@ -923,6 +970,7 @@ static void bound_counts(const fi_plan_desc& d, int32_t num_cus, int64_t max_kv_
   c.part_rows = (size_t)part_rows;
   c.scatter = d.kind == FI_KIND_APPEND ? (size_t)max_qo_tokens : 0;
   c.qlist = (size_t)B * (d.kind == FI_KIND_CASCADE ? d.max_prefix_depth : 1);
+  c.fused = fused_merge(d);
 }
 
 // The capacities a graph-stable description (cap_batch > 0) lays its
@@ -937,7 +985,7 @@ static void stable_caps(const fi_plan_desc& d, int32_t num_cus, Caps& c) {
 
 static Layout caps_layout(const Caps& c, int32_t head_dim) {
   return layout_for(c.workers, c.items, c.merges, c.parts, c.qlist, c.scatter, c.part_rows,
-                    head_dim);
+                    head_dim, 0, c.fused);
 }
 
 // A built plan against the capacities of its graph-stable layout (a bound
@@ -1138,6 +1186,10 @@ extern "C" fi_status fi_plan_get_info(const fi_plan_t* p, fi_plan_info* info) {
   info->pod_wide_blocks = hp.pod ? hp.pod_wide_blocks : 0;
   info->num_plist = (int32_t)hp.plist.size();
   info->plist = hp.plist.data();
+  info->fused_merge = hp.fused ? 1 : 0;
+  info->item_rec = hp.item_rec.data();
+  info->num_empty_recs = (int32_t)hp.empty_recs.size();
+  info->empty_recs = hp.empty_recs.data();
   return FI_OK;
 }
 

@@ -359,11 +359,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 template <int D, bool LQ>
 hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    hipLaunchKernelGGL((wide_kernel<D, 4, LQ>), grid, dim3(256), 0, s, a);
+    launch_timed((wide_kernel<D, 4, LQ>), grid, dim3(256), s, a);
   } else if (a.page_size == 16) {
-    hipLaunchKernelGGL((wide_kernel<D, 2, LQ>), grid, dim3(256), 0, s, a);
+    launch_timed((wide_kernel<D, 2, LQ>), grid, dim3(256), s, a);
   } else {
-    hipLaunchKernelGGL((wide_kernel<D, 1, LQ>), grid, dim3(256), 0, s, a);
+    launch_timed((wide_kernel<D, 1, LQ>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }
@@ -372,11 +372,11 @@ template <int D, bool LQ>
 hipError_t launch_pod_d(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, dim3 grid,
                         hipStream_t s) {
   if (wa.page_size == 8) {
-    hipLaunchKernelGGL((pod_kernel<D, 4, LQ>), grid, dim3(256), 0, s, wa, da, meta);
+    launch_timed((pod_kernel<D, 4, LQ>), grid, dim3(256), s, wa, da, meta);
   } else if (wa.page_size == 16) {
-    hipLaunchKernelGGL((pod_kernel<D, 2, LQ>), grid, dim3(256), 0, s, wa, da, meta);
+    launch_timed((pod_kernel<D, 2, LQ>), grid, dim3(256), s, wa, da, meta);
   } else {
-    hipLaunchKernelGGL((pod_kernel<D, 1, LQ>), grid, dim3(256), 0, s, wa, da, meta);
+    launch_timed((pod_kernel<D, 1, LQ>), grid, dim3(256), s, wa, da, meta);
   }
   return hipGetLastError();
 }

@@ -627,3 +627,44 @@ def test_stable_plans_share_one_layout(kind):
         kw.update(prefix_indptr=pi, prefix_len=pl, req_prefix_group=[0])
     with pytest.raises(fi.FIError, match="capacity"):
         host_plan(kind, indptr, L_, 32, 8, 128, ps, **kw)
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_fused_merge_records(det):
+    """A merge="fused" decode plan on the matrix cores folds its split units
+    in the kernel:
+    each item that writes partial rows points at the merge record whose part
+    list holds its rows (the record of its own unit: same query and kv head),
+    items writing final rows point nowhere, every split record is pointed at
+    by exactly its part count of items, and the records of units with no keys
+    are listed for the kernel to write. The VALU engine, merge="separate" and
+    default plans launch the merge kernel instead."""
+    ps = 16
+    rng = np.random.default_rng(31)
+    lens = list(rng.integers(0, 5000, 37)) + [0, 1, 0, 32768]
+    indptr, L_ = _decode_host(lens, ps)
+    p = host_plan("decode", indptr, L_, 32, 8, 128, ps, deterministic=det, det_chunk_pages=16,
+                  num_cus=5, workers_per_cu=4, merge="fused")
+    info = p.info()
+    assert info["fused_merge"]
+    items = info["levels"][0]["items"]
+    rec = info["item_rec"]
+    assert rec.shape == (len(items),)
+    hits = np.zeros(len(info["merges"]), dtype=int)
+    for it, e in zip(items, rec):
+        partial = bool(it[5] & 2)
+        assert (e >= 0) == partial
+        if not partial:
+            continue
+        q_base, row0, n_rows, g, off, n = info["merges"][e]
+        assert (q_base, g, row0, n_rows) == (it[0], it[3], it[1], it[2])
+        assert it[9] in info["parts"][off:off + n]
+        hits[e] += 1
+    assert np.array_equal(hits, info["merges"][:, 5])
+    assert list(info["empty_recs"]) == [e for e in range(len(info["merges"]))
+                                       if info["merges"][e, 5] == 0]
+    assert len(info["empty_recs"]) == 8 * 2          # two empty requests, 8 kv heads
+    for kw in (dict(engine="valu", merge="fused"), dict(merge="separate"), dict()):
+        q = host_plan("decode", indptr, L_, 32, 8, 128, ps, deterministic=det,
+                      det_chunk_pages=16, num_cus=5, workers_per_cu=4, **kw).info()
+        assert not q["fused_merge"] and len(q["item_rec"]) == 0

@@ -240,6 +240,40 @@ def test_pool_permutation_is_bit_identical(dev):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_fused_merge_bits_equal_merge_kernel(dev, cfg):
+    """merge="fused" decode plans fold their split units inside the attention
+    kernel; the bits equal those of the merge kernel (the default launch), on
+    every decode kernel, in both modes, and stay the same over repeated calls
+    on one plan (the arrival counts reset themselves)."""
+    w = make_config(cfg, poison=True)
+    if cfg == 1:
+        w = to_mxfp4_cache(to_fp8_cache(w, poison=True), poison=True)
+    g = w.to(dev)
+    kernels = ["bf16"] + (["fp8", "mxfp4"] if cfg == 1 else [])
+    for det in (False, True):
+        for kern in kernels:
+            outs = []
+            for merge in ("fused", "default"):
+                p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
+                            w.head_dim, w.page_size, device=dev, deterministic=det, merge=merge)
+                assert p.info()["fused_merge"] == (merge == "fused")
+                for rep in range(3 if merge == "fused" else 1):
+                    if kern == "bf16":
+                        o, lse = fi.paged_decode(p, g.q, g.k_cache, g.v_cache, g.kv_indices,
+                                                 w.sm_scale)
+                    elif kern == "fp8":
+                        o, lse = fi.paged_decode_fp8(p, g.q, g.k_fp8, g.v_fp8, g.k_scale,
+                                                     g.v_scale, g.kv_indices, w.sm_scale)
+                    else:
+                        o, lse = fi.paged_decode_mxfp4(p, g.q, g.k_fp4, g.v_fp4, g.k_bscale,
+                                                       g.v_bscale, g.kv_indices, w.sm_scale)
+                    torch.cuda.synchronize()
+                    outs.append((o, lse))
+            for o, lse in outs[1:]:
+                assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1]), (kern, det)
+
+
 def test_repeat_runs_are_bit_identical(dev, cfg1):
     for det in (False, True):
         o1, l1, _ = gpu_decode(cfg1, dev, deterministic=det)
