@@ -122,6 +122,16 @@ typedef enum fi_merge_mode {
   FI_MERGE_SEPARATE = 2   /* a merge launch (the default)                       */
 } fi_merge_mode;
 
+/* Layout of the K/V a block-sparse plan reads (research note, "Arithmetic
+ * intensity": paged and ragged KV-cache layouts). PAGED: pools
+ * [num_pages][Hkv][page_size][D] and a page table. RAGGED: one contiguous
+ * tensor [tokens][Hkv][D] per K and V, sequence s holding tokens
+ * kv_indptr[s] .. kv_indptr[s+1]-1. Plans of other kinds read paged pools. */
+typedef enum fi_kv_layout {
+  FI_KV_LAYOUT_PAGED = 0,
+  FI_KV_LAYOUT_RAGGED = 1
+} fi_kv_layout;
+
 /* Plan description. Zero in an optional field selects its default. */
 typedef struct fi_plan_desc {
   int32_t kind;              /* fi_kind                                        */
@@ -162,6 +172,7 @@ typedef struct fi_plan_desc {
   int32_t cap_prefix_pages;  /* cascade: sum of the groups' prefix pages      */
   int32_t kv_format;         /* decode: fi_kv_format (default FI_KV_BF16)     */
   int32_t merge_mode;        /* fi_merge_mode (default 0)                     */
+  int32_t kv_layout;         /* fi_kv_layout: block-sparse plans (default 0)  */
 } fi_plan_desc;
 
 typedef struct fi_plan fi_plan_t;
@@ -388,9 +399,46 @@ fi_status fi_plan_block_sparse(const fi_plan_desc* desc, int32_t qo_len, int32_t
                                const uint8_t* block_mask_h, const int32_t* seq_pages_h,
                                void* ws_dev, size_t ws_dev_bytes, void* ws_host,
                                size_t ws_host_bytes, void* stream, fi_plan_t** out);
-/* Run a block-sparse plan: q [qo_len][Hq][D] bf16 -> o [qo_len][Hq][D] bf16,
- * lse [qo_len][Hq] fp32 (NULL to skip); k_cache, v_cache the pools the plan's
- * seq_pages index. The page lists come from the plan's workspace. */
+/* Variable block-sparse attention over a batch of sequences in one plan
+ * (research note, "Arithmetic intensity": block-sparse and variable
+ * block-sparse plans over paged and ragged KV layouts; Ye et al. record,
+ * "summary": composable block-sparse KV representations). Sequence s has
+ * qo_len_h[s] queries, q rows sum(qo_len_h[0..s-1]) onward, and kv_len_h[s]
+ * keys; per kv head it is cut into num_row_blocks_h[s] row blocks and
+ * num_col_blocks_h[s] column blocks with a block mask, exactly as for
+ * fi_plan_block_sparse, its arrays concatenated over the sequences:
+ * row_block_sz_h holds each sequence's [Hkv][num_row_blocks_h[s]] in turn,
+ * col_block_sz_h each [Hkv][num_col_blocks_h[s]], block_mask_h each
+ * [Hkv][num_row_blocks_h[s]][num_col_blocks_h[s]] (host memory). Keys:
+ * desc.kv_layout PAGED: token t of sequence s in page
+ * kv_indices_h[kv_indptr_h[s] + t / page_size] (kv_indptr_h[s+1] -
+ * kv_indptr_h[s] == ceil(kv_len_h[s] / page_size)) of the usual pools;
+ * RAGGED: token t of sequence s is row kv_indptr_h[s] + t of the [tokens][Hkv][D]
+ * tensors (kv_indptr_h[s+1] - kv_indptr_h[s] == kv_len_h[s]; kv_indices_h is
+ * not read), with page_size the granule of the key walk (column blocks start
+ * on multiples of it, as in the paged layout); the kernels read whole
+ * page_size-token runs, so the tensors must hold at least
+ * kv_indptr_h[num_seqs] + page_size - 1 rows (rows past a sequence's end are
+ * read and ignored). No query attends across sequences. Errors as
+ * fi_plan_block_sparse. */
+fi_status fi_workspace_size_block_sparse_batch(const fi_plan_desc* desc, int32_t num_seqs,
+                                               const int32_t* qo_len_h, const int32_t* kv_len_h,
+                                               const int32_t* num_row_blocks_h,
+                                               const int32_t* num_col_blocks_h,
+                                               size_t* dev_bytes, size_t* host_bytes);
+fi_status fi_plan_block_sparse_batch(const fi_plan_desc* desc, int32_t num_seqs,
+                                     const int32_t* qo_len_h, const int32_t* kv_len_h,
+                                     const int32_t* num_row_blocks_h,
+                                     const int32_t* row_block_sz_h,
+                                     const int32_t* num_col_blocks_h,
+                                     const int32_t* col_block_sz_h, const uint8_t* block_mask_h,
+                                     const int32_t* kv_indptr_h, const int32_t* kv_indices_h,
+                                     void* ws_dev, size_t ws_dev_bytes, void* ws_host,
+                                     size_t ws_host_bytes, void* stream, fi_plan_t** out);
+/* Run a block-sparse plan: q [T][Hq][D] bf16 -> o [T][Hq][D] bf16, lse
+ * [T][Hq] fp32 (NULL to skip), T the plan's query rows; k_cache, v_cache the
+ * pools the plan's page ids index (paged), or the [tokens][Hkv][D] tensors
+ * (ragged). The page lists come from the plan's workspace. */
 fi_status fi_block_sparse_attention(const fi_plan_t* plan, const void* q, const void* k_cache,
                                     const void* v_cache, float sm_scale, void* o, float* lse,
                                     void* stream);

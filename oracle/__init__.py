@@ -43,6 +43,8 @@ from .attention import (  # noqa: F401
     paged_decode_mxfp4,
     paged_append,
     block_sparse,
+    block_sparse_batch,
+    gather_ragged,
     scatter_new_kv,
     merge_states,
     merge_two,

@@ -252,6 +252,43 @@ def paged_append(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
     return o, lse
 
 
+def gather_ragged(kv, start: int, length: int, kv_head: int) -> np.ndarray:
+    """Tokens ``start .. start+length-1`` of a ragged ``[tokens, Hkv, D]`` K or
+    V tensor for one kv head, in token order (research note, *Arithmetic
+    intensity*: ragged KV-cache layouts, one contiguous run of tokens per
+    sequence). Pinned by: a ragged tensor scattered into a paged pool gathers
+    to the same keys, and brute force over explicit key lists."""
+    d = kv.shape[-1]
+    if length <= 0:
+        return np.zeros((0, d), dtype=np.float64)
+    return np.asarray(kv[start:start + length, kv_head], dtype=np.float64)
+
+
+def _block_sparse_seq(q, keys_of, kv_len: int, row_sz, col_sz, mask, sm_scale: float, sel,
+                      o, lse):
+    """Block-sparse attention of one sequence: ``q [T, Hq, D]`` its queries,
+    ``keys_of(g)`` its (K, V) for kv head g, ``sel`` the query indices to
+    compute; writes ``o``/``lse`` rows ``sel`` (the definition in
+    ``block_sparse``)."""
+    T, Hq, D = q.shape
+    Hkv = len(row_sz)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        K, V = keys_of(g)
+        rs = np.asarray(row_sz[g], dtype=np.int64)
+        cs = np.asarray(col_sz[g], dtype=np.int64)
+        assert rs.sum() == T and cs.sum() == kv_len, "blocks must cover the sequence"
+        row_block = np.repeat(np.arange(rs.size), rs)          # query -> its row block
+        col_block = np.repeat(np.arange(cs.size), cs)          # key -> its column block
+        m = np.asarray(mask[g], dtype=bool)
+        vis_tok = m[row_block[sel][:, None], col_block[None, :]]    # [rows, kv_len]
+        hs = _heads_of(g, G)
+        qr = np.asarray(q[sel][:, hs], dtype=np.float64).reshape(sel.size * G, D)
+        ob, lb = attend(qr, K, V, sm_scale, np.repeat(vis_tok, G, axis=0))
+        o[sel, hs] = ob.reshape(sel.size, G, D)
+        lse[sel, hs] = lb.reshape(sel.size, G)
+
+
 def block_sparse(q, k_pool, v_pool, seq_pages, kv_len: int, page_size: int, row_sz, col_sz,
                  mask, sm_scale: float, rows=None):
     """Variable block-sparse attention of one sequence (research note,
@@ -272,26 +309,54 @@ def block_sparse(q, k_pool, v_pool, seq_pages, kv_len: int, page_size: int, row_
     block (torch SDPA), and rows with no selected block.
     """
     T, Hq, D = q.shape
-    Hkv = k_pool.shape[1]
-    G = Hq // Hkv
     sel = np.arange(T) if rows is None else np.asarray(sorted(rows), dtype=np.int64)
     o = np.full((T, Hq, D), np.nan)
     lse = np.full((T, Hq), np.nan)
-    for g in range(Hkv):
-        K = gather_tokens(k_pool, seq_pages, 0, kv_len, page_size, g)
-        V = gather_tokens(v_pool, seq_pages, 0, kv_len, page_size, g)
-        rs = np.asarray(row_sz[g], dtype=np.int64)
-        cs = np.asarray(col_sz[g], dtype=np.int64)
-        assert rs.sum() == T and cs.sum() == kv_len, "blocks must cover the sequence"
-        row_block = np.repeat(np.arange(rs.size), rs)          # query -> its row block
-        col_block = np.repeat(np.arange(cs.size), cs)          # key -> its column block
-        m = np.asarray(mask[g], dtype=bool)
-        vis_tok = m[row_block[sel][:, None], col_block[None, :]]    # [rows, kv_len]
-        hs = _heads_of(g, G)
-        qr = np.asarray(q[sel][:, hs], dtype=np.float64).reshape(sel.size * G, D)
-        ob, lb = attend(qr, K, V, sm_scale, np.repeat(vis_tok, G, axis=0))
-        o[sel, hs] = ob.reshape(sel.size, G, D)
-        lse[sel, hs] = lb.reshape(sel.size, G)
+
+    def keys_of(g):
+        return (gather_tokens(k_pool, seq_pages, 0, kv_len, page_size, g),
+                gather_tokens(v_pool, seq_pages, 0, kv_len, page_size, g))
+    _block_sparse_seq(q, keys_of, kv_len, row_sz, col_sz, mask, sm_scale, sel, o, lse)
+    return o, lse
+
+
+def block_sparse_batch(q, k, v, qo_len, kv_len, row_sz, col_sz, mask, sm_scale: float,
+                       kv_indptr, kv_indices=None, page_size: int = 0, rows=None):
+    """Block-sparse attention over a batch of sequences, each with its own
+    partitions and mask (``row_sz[s]``, ``col_sz[s]``, ``mask[s]`` as in
+    ``block_sparse``); sequence s's queries are q rows ``sum(qo_len[:s])``
+    onward and see only its own keys. Keys, paged (``kv_indices`` given):
+    token t of sequence s in page ``kv_indices[kv_indptr[s] + t // page_size]``
+    of pools ``k, v [P, Hkv, ps, D]``; ragged (``kv_indices`` None): rows
+    ``kv_indptr[s] + t`` of ``k, v [tokens, Hkv, D]``. Returns
+    ``o [T, Hq, D]``, ``lse [T, Hq]`` (``rows``: only those global query rows,
+    others NaN). Pinned by: brute force over explicit per-row key lists on a
+    tiny ragged batch, equality with ``block_sparse`` per sequence, and
+    ragged equal to paged for the same keys.
+    """
+    T, Hq, D = q.shape
+    o = np.full((T, Hq, D), np.nan)
+    lse = np.full((T, Hq), np.nan)
+    want = None if rows is None else set(int(r) for r in rows)
+    q0 = 0
+    for s in range(len(qo_len)):
+        nq, L, base = int(qo_len[s]), int(kv_len[s]), int(kv_indptr[s])
+        sel = np.array([i for i in range(nq) if want is None or q0 + i in want], dtype=np.int64)
+        if sel.size:
+            if kv_indices is None:
+                def keys_of(g):
+                    return gather_ragged(k, base, L, g), gather_ragged(v, base, L, g)
+            else:
+                def keys_of(g):
+                    return (gather_tokens(k, kv_indices, base, L, page_size, g),
+                            gather_tokens(v, kv_indices, base, L, page_size, g))
+            os_ = np.full((nq, Hq, D), np.nan)
+            ls_ = np.full((nq, Hq), np.nan)
+            _block_sparse_seq(q[q0:q0 + nq], keys_of, L, row_sz[s], col_sz[s], mask[s],
+                              sm_scale, sel, os_, ls_)
+            o[q0 + sel] = os_[sel]
+            lse[q0 + sel] = ls_[sel]
+        q0 += nq
     return o, lse
 
 

@@ -71,14 +71,17 @@ be compared with it element for element:
    Partial rows are allocated wide role first; merges likewise. A cascade
    plan may be fused the same way: its prefix level is the wide role and its
    suffix level the decode role, split by the same rule.
-7. Variable block-sparse (one sequence; research note *Arithmetic intensity*:
-   block-sparse and variable block-sparse plans). For kv head g and row
-   block a (rows = a's query tokens times G), the page list is the pages of
-   a's selected non-empty column blocks in column order (a block of c keys
-   starting at key c0 covers pages c0/ps .. ceil((c0+c)/ps)-1 of the
-   sequence), appended to ``plist``; t_lim = the selected keys. Units are
-   enumerated g, a, row block (128 rows; in a POD plan a row block of at most
-   16 rows is one decode-role unit), with q_base = a's first query token and
+7. Variable block-sparse (research note *Arithmetic intensity*: block-sparse
+   and variable block-sparse plans over paged and ragged layouts). For
+   sequence s, kv head g and row block a (rows = a's query tokens times G),
+   the page list is the pages of a's selected non-empty column blocks in
+   column order (a block of c keys starting at key c0 covers pages c0/ps ..
+   ceil((c0+c)/ps)-1 of the sequence), appended to ``plist``; a paged
+   sequence lists its page ids, a ragged one (keys in rows kv_indptr[s] + t
+   of one [tokens][Hkv][D] tensor) the first token kv_indptr[s] + pg*ps of
+   each page-sized run. t_lim = the selected keys. Units are enumerated s, g,
+   a, row block (128 rows; in a POD plan a row block of at most 16 rows is one
+   decode-role unit), with q_base = a's first query row in the batch and
    page_off = the list's offset; no causal mask. Levels, merges (a unit with
    no keys gets empty records: o = 0, lse = -inf) as in 3-6.
 """
@@ -163,7 +166,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
              num_workers, rows_per_block, deterministic=False, det_chunk_pages=48,
              min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
              prefix_len=None, req_group=None, prefix_parent=None, pod_blocks=None,
-             pod_wide_blocks=0, block_sparse=None):
+             pod_wide_blocks=0, block_sparse=None, block_sparse_batch=None):
     """Return the plan as plain lists.
 
     ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
@@ -179,7 +182,10 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
     ``pod_wide_blocks``. ``kind="block_sparse"`` takes ``block_sparse =
     (qo_len, row_sz [Hkv][MB], col_sz [Hkv][NB], mask [Hkv][MB][NB],
     seq_pages)`` (rule 7; ``kv_indptr`` and ``kv_len`` are then unused) and
-    the result also holds ``plist``.
+    the result also holds ``plist``; or ``block_sparse_batch = (qo_lens,
+    row_szs, col_szs, masks, kv_indptr, kv_indices)`` for a batch of
+    sequences (per-sequence lists; ``kv_indices`` None for a ragged layout,
+    ``kv_indptr`` then in tokens).
     """
     nlev = len(rows_per_block)
     workers = list(num_workers) if isinstance(num_workers, (list, tuple)) else [num_workers] * nlev
@@ -253,27 +259,42 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                     rows_per_block[lev], lambda r: qo[r], lambda r: int(qo_indptr[r]),
                     bool(causal), take=lambda r, role=role: small[r] == role))
     elif kind == "block_sparse":
-        qo_len, row_sz, col_sz, mask, seq_pages = block_sparse
+        if block_sparse is not None:      # one paged sequence
+            qo_len, row_sz, col_sz, mask, seq_pages = block_sparse
+            n = _ceil_div(sum(int(x) for x in col_sz[0]), ps) if len(col_sz) else 0
+            seqs = ([qo_len], [row_sz], [col_sz], [mask], [0, n], list(seq_pages))
+        else:
+            seqs = block_sparse_batch
+        qo_lens, rows_s, cols_s, masks_s, kvp, kvi = seqs
         wide, small = [], []
-        for g in range(num_kv_heads):
-            q0 = 0
-            for a, nq in enumerate(int(x) for x in row_sz[g]):
-                off, t_lim, c0 = len(page_list), 0, 0
-                for b, c in enumerate(int(x) for x in col_sz[g]):
-                    if c > 0 and mask[g][a][b]:
-                        page_list.extend(int(seq_pages[pg]) for pg in
-                                     range(c0 // ps, _ceil_div(c0 + c, ps)))
-                        t_lim += c
-                    c0 += c
-                rows = nq * G
-                to_small = pod_blocks is not None and rows <= POD_DECODE_ROWS
-                rpb = rows_per_block[1] if to_small else rows_per_block[0]
-                for blk in range(_ceil_div(rows, rpb)):
-                    (small if to_small else wide).append(dict(
-                        unit=g * len(row_sz[g]) + a, q_base=q0, row0=blk * rpb,
-                        n_rows=min(rows - blk * rpb, rpb), g=g, page_off=off, t_lim=t_lim,
-                        n_pages=_ceil_div(t_lim, ps), q_pos0=0, flags=0, nq=nq))
-                q0 += nq
+        q_seq, unit_id = 0, 0
+        for sq in range(len(qo_lens)):
+            row_sz, col_sz, mask = rows_s[sq], cols_s[sq], masks_s[sq]
+            base = int(kvp[sq])
+            for g in range(num_kv_heads):
+                q0 = q_seq
+                for a, nq in enumerate(int(x) for x in row_sz[g]):
+                    off, t_lim, c0 = len(page_list), 0, 0
+                    for b, c in enumerate(int(x) for x in col_sz[g]):
+                        if c > 0 and mask[g][a][b]:
+                            # paged: the pool's page ids; ragged (kvi None):
+                            # the first token of each ps-token run
+                            page_list.extend(
+                                (base + pg * ps) if kvi is None else int(kvi[base + pg])
+                                for pg in range(c0 // ps, _ceil_div(c0 + c, ps)))
+                            t_lim += c
+                        c0 += c
+                    rows = nq * G
+                    to_small = pod_blocks is not None and rows <= POD_DECODE_ROWS
+                    rpb = rows_per_block[1] if to_small else rows_per_block[0]
+                    for blk in range(_ceil_div(rows, rpb)):
+                        (small if to_small else wide).append(dict(
+                            unit=unit_id, q_base=q0, row0=blk * rpb,
+                            n_rows=min(rows - blk * rpb, rpb), g=g, page_off=off, t_lim=t_lim,
+                            n_pages=_ceil_div(t_lim, ps), q_pos0=0, flags=0, nq=nq))
+                    q0 += nq
+                    unit_id += 1
+            q_seq += int(qo_lens[sq])
         levels_units.append(wide)
         if pod_blocks is not None:
             levels_units.append(small)

@@ -20,6 +20,7 @@ FI_ENGINE_DEFAULT, FI_ENGINE_MFMA, FI_ENGINE_VALU = range(3)
 FI_LAUNCH_DEFAULT, FI_LAUNCH_POD, FI_LAUNCH_SEPARATE = range(3)
 FI_KV_BF16, FI_KV_FP8, FI_KV_MXFP4 = range(3)
 FI_MERGE_DEFAULT, FI_MERGE_FUSED, FI_MERGE_SEPARATE = range(3)
+FI_KV_LAYOUT_PAGED, FI_KV_LAYOUT_RAGGED = range(2)
 FI_ITEM_INTS, FI_MERGE_INTS = 12, 6
 FI_NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -32,7 +33,7 @@ class PlanDesc(ctypes.Structure):
         "kind", "batch", "num_qo_heads", "num_kv_heads", "head_dim", "page_size", "causal",
         "deterministic", "det_chunk_pages", "min_chunk_pages", "num_cus", "workers_per_cu",
         "num_prefix_groups", "decode_engine", "max_prefix_depth", "launch", "pod_wide_blocks", "cap_batch", "cap_kv_pages",
-        "cap_qo_tokens", "cap_prefix_pages", "kv_format", "merge_mode")]
+        "cap_qo_tokens", "cap_prefix_pages", "kv_format", "merge_mode", "kv_layout")]
 
 
 I32P = POINTER(c_int32)
@@ -82,6 +83,13 @@ SIGNATURES = {
     "fi_plan_block_sparse": (c_int32, [POINTER(PlanDesc), c_int32, c_int32, c_int32, I32P,
                                        c_int32, I32P, c_void_p, I32P, c_void_p, c_size_t,
                                        c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+    "fi_workspace_size_block_sparse_batch": (c_int32, [POINTER(PlanDesc), c_int32, I32P, I32P,
+                                                       I32P, I32P, POINTER(c_size_t),
+                                                       POINTER(c_size_t)]),
+    "fi_plan_block_sparse_batch": (c_int32, [POINTER(PlanDesc), c_int32, I32P, I32P, I32P, I32P,
+                                             I32P, I32P, c_void_p, I32P, I32P, c_void_p,
+                                             c_size_t, c_void_p, c_size_t, c_void_p,
+                                             POINTER(c_void_p)]),
     "fi_block_sparse_attention": (c_int32, [c_void_p, c_void_p, c_void_p, c_void_p, c_float,
                                             c_void_p, c_void_p, c_void_p]),
     "fi_merge_states": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, c_int32, c_int32,

@@ -194,60 +194,94 @@ class Plan:
 
 
 class BlockSparsePlan(Plan):
-    """A variable block-sparse plan over one sequence (fi_plan_block_sparse).
-    ``row_block_sz [Hkv, MB]`` and ``col_block_sz [Hkv, NB]`` cut the qo_len
-    queries and the kv_len keys per kv head, ``block_mask [Hkv, MB, NB]``
-    selects the (row block, column block) pairs, and ``seq_pages`` holds the
-    sequence's page ids (token t in page seq_pages[t // page_size])."""
+    """A variable block-sparse plan over a batch of sequences
+    (fi_plan_block_sparse_batch). Sequence s has ``qo_len[s]`` queries (q
+    rows in sequence order) and ``kv_len[s]`` keys; ``row_block_sz[s]``
+    ``[Hkv, MB_s]`` and ``col_block_sz[s]`` ``[Hkv, NB_s]`` cut them per kv
+    head and ``block_mask[s]`` ``[Hkv, MB_s, NB_s]`` selects the block pairs.
+    ``layout="paged"``: keys through ``kv_indptr`` (pages) and ``kv_indices``
+    into pools ``[P, Hkv, ps, D]``; ``layout="ragged"``: sequence s is rows
+    ``kv_indptr[s] ..`` of K/V tensors ``[tokens, Hkv, D]`` (``kv_indices``
+    unused), ``page_size`` the granule of the key walk. A single sequence may
+    be given without the lists: ``qo_len``/``kv_len`` ints, the size and mask
+    arrays of that sequence, and ``seq_pages`` (paged) for its page ids."""
 
-    def __init__(self, qo_len: int, kv_len: int, row_block_sz, col_block_sz, block_mask,
-                 seq_pages, num_qo_heads: int, num_kv_heads: int, head_dim: int,
-                 page_size: int, *, deterministic: bool = False, det_chunk_pages: int = 0,
+    def __init__(self, qo_len, kv_len, row_block_sz, col_block_sz, block_mask,
+                 seq_pages=None, num_qo_heads: int = 0, num_kv_heads: int = 0,
+                 head_dim: int = 0, page_size: int = 0, *, kv_indptr=None, kv_indices=None,
+                 layout: str = "paged", deterministic: bool = False, det_chunk_pages: int = 0,
                  min_chunk_pages: int = 0, num_cus: int = 0, workers_per_cu: int = 0,
                  launch: str = "default", pod_wide_blocks: int = 0, device="cuda",
                  workspace: Optional[Workspace] = None):
         lib = L.load()
         self.kind = "block_sparse"
-        rs = _host_i32(row_block_sz).reshape(num_kv_heads, -1)
-        cs = _host_i32(col_block_sz).reshape(num_kv_heads, -1)
-        mb, nb = rs.shape[1], cs.shape[1]
-        mask = block_mask.detach().cpu().numpy() if isinstance(block_mask, torch.Tensor) \
-            else np.asarray(block_mask)
-        mask = np.ascontiguousarray(mask.astype(np.uint8).reshape(num_kv_heads, mb, nb))
-        pages = _host_i32(seq_pages)
-        self._ha = dict(row=np.ascontiguousarray(rs), col=np.ascontiguousarray(cs), mask=mask,
-                        pages=pages if pages is not None else np.zeros(0, np.int32))
+        Hkv, ps = num_kv_heads, page_size
+        single = np.ndim(qo_len) == 0
+        if single:
+            qo_len, kv_len = [int(qo_len)], [int(kv_len)]
+            row_block_sz, col_block_sz, block_mask = [row_block_sz], [col_block_sz], [block_mask]
+            if layout == "paged":
+                n = -(-int(kv_len[0]) // ps)
+                kv_indptr = [0, n]
+                kv_indices = seq_pages if seq_pages is not None else np.zeros(0, np.int32)
+        S = len(qo_len)
+        rows, cols, masks, nrb, ncb = [], [], [], [], []
+        for s in range(S):
+            r = _host_i32(row_block_sz[s]).reshape(Hkv, -1)
+            c = _host_i32(col_block_sz[s]).reshape(Hkv, -1)
+            m = block_mask[s]
+            m = m.detach().cpu().numpy() if isinstance(m, torch.Tensor) else np.asarray(m)
+            m = m.astype(np.uint8).reshape(Hkv, r.shape[1], c.shape[1])
+            rows.append(r.ravel()), cols.append(c.ravel()), masks.append(m.ravel())
+            nrb.append(r.shape[1]), ncb.append(c.shape[1])
+        cat = lambda xs, dt: np.ascontiguousarray(np.concatenate(xs).astype(dt)) if xs \
+            else np.zeros(0, dt)  # noqa: E731
+        self._ha = dict(qo_len=_host_i32(qo_len), kv_len=_host_i32(kv_len),
+                        nrb=_host_i32(nrb), ncb=_host_i32(ncb), row=cat(rows, np.int32),
+                        col=cat(cols, np.int32), mask=cat(masks, np.uint8),
+                        kv_indptr=_host_i32(kv_indptr),
+                        kv_indices=_host_i32(kv_indices) if layout == "paged" else None)
+        if self._ha["kv_indptr"] is None:
+            raise ValueError("kv_indptr is required")
+        self.layout = layout
         self.desc = L.PlanDesc(kind=L.FI_KIND_BLOCK_SPARSE, batch=1, num_qo_heads=num_qo_heads,
-                               num_kv_heads=num_kv_heads, head_dim=head_dim,
-                               page_size=page_size, deterministic=int(deterministic),
-                               det_chunk_pages=det_chunk_pages, min_chunk_pages=min_chunk_pages,
-                               num_cus=num_cus, workers_per_cu=workers_per_cu,
-                               launch=_LAUNCHES[launch], pod_wide_blocks=pod_wide_blocks)
-        self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
-        self.head_dim, self.page_size, self.batch = head_dim, page_size, 1
-        self.num_q_tokens = int(qo_len)
+                               num_kv_heads=Hkv, head_dim=head_dim, page_size=ps,
+                               deterministic=int(deterministic), det_chunk_pages=det_chunk_pages,
+                               min_chunk_pages=min_chunk_pages, num_cus=num_cus,
+                               workers_per_cu=workers_per_cu, launch=_LAUNCHES[launch],
+                               pod_wide_blocks=pod_wide_blocks,
+                               kv_layout=L.FI_KV_LAYOUT_RAGGED if layout == "ragged"
+                               else L.FI_KV_LAYOUT_PAGED)
+        self.num_qo_heads, self.num_kv_heads = num_qo_heads, Hkv
+        self.head_dim, self.page_size, self.batch = head_dim, ps, S
+        self.num_q_tokens = int(self._ha["qo_len"].sum()) if S else 0
+        # ragged: the kernels read whole page_size-token runs, the last of them
+        # up to page_size - 1 rows past the last sequence's end
+        self.kv_tokens = int(self._ha["kv_indptr"][-1]) + ps - 1 if layout == "ragged" and S \
+            else 0
         self.device = None if device is None else torch.device(device)
         self.workspace = workspace
         ws_dev = ws_host = None
         dev_b = host_b = 0
         stream = None
+        a = self._ha
         if self.device is not None:
             if self.workspace is None:
                 db, hb = ctypes.c_size_t(), ctypes.c_size_t()
-                L.check(lib.fi_workspace_size_block_sparse(
-                    ctypes.byref(self.desc), int(qo_len), int(kv_len), mb, nb,
-                    ctypes.byref(db), ctypes.byref(hb)), "fi_workspace_size_block_sparse")
+                L.check(lib.fi_workspace_size_block_sparse_batch(
+                    ctypes.byref(self.desc), S, _p(a["qo_len"]), _p(a["kv_len"]), _p(a["nrb"]),
+                    _p(a["ncb"]), ctypes.byref(db), ctypes.byref(hb)),
+                    "fi_workspace_size_block_sparse_batch")
                 self.workspace = Workspace(db.value, hb.value, self.device)
             ws_dev, ws_host = _ptr(self.workspace.dev), _ptr(self.workspace.host)
             dev_b, host_b = self.workspace.dev.numel(), self.workspace.host.numel()
             stream = _stream(self.device)
         h = ctypes.c_void_p()
-        a = self._ha
-        L.check(lib.fi_plan_block_sparse(ctypes.byref(self.desc), int(qo_len), int(kv_len), mb,
-                                         _p(a["row"]), nb, _p(a["col"]),
-                                         a["mask"].ctypes.data_as(ctypes.c_void_p),
-                                         _p(a["pages"]), ws_dev, dev_b, ws_host, host_b, stream,
-                                         ctypes.byref(h)), "fi_plan_block_sparse")
+        L.check(lib.fi_plan_block_sparse_batch(
+            ctypes.byref(self.desc), S, _p(a["qo_len"]), _p(a["kv_len"]), _p(a["nrb"]),
+            _p(a["row"]), _p(a["ncb"]), _p(a["col"]), a["mask"].ctypes.data_as(ctypes.c_void_p),
+            _p(a["kv_indptr"]), _p(a["kv_indices"]), ws_dev, dev_b, ws_host, host_b, stream,
+            ctypes.byref(h)), "fi_plan_block_sparse_batch")
         self._h = h
 
 
@@ -467,11 +501,21 @@ def cascade(plan: Plan, q, k_cache, v_cache, prefix_indices, kv_indices, sm_scal
 
 def block_sparse_attention(plan: BlockSparsePlan, q, k_cache, v_cache, sm_scale: float,
                            out=None, lse=None, return_lse: bool = True):
-    """fi_block_sparse_attention: q [qo_len, Hq, D] bf16 -> (out, lse [qo_len, Hq])."""
+    """fi_block_sparse_attention: q [T, Hq, D] bf16 -> (out, lse [T, Hq]), T
+    the plan's query rows; k_cache/v_cache paged pools, or [tokens, Hkv, D]
+    tensors for a ragged plan."""
     _check_run(plan, "block_sparse")
     T = plan.num_q_tokens
     _check_tensor(q, "q", torch.bfloat16, plan.device, (T, plan.num_qo_heads, plan.head_dim))
-    _check_cache(plan, k_cache, v_cache)
+    if getattr(plan, "layout", "paged") == "ragged":
+        _check_tensor(k_cache, "k", torch.bfloat16, plan.device)
+        _check_tensor(v_cache, "v", torch.bfloat16, plan.device, k_cache.shape)
+        if (k_cache.dim() != 3 or tuple(k_cache.shape[1:]) != (plan.num_kv_heads, plan.head_dim)
+                or k_cache.shape[0] < plan.kv_tokens):
+            raise ValueError(f"ragged K/V shape {tuple(k_cache.shape)} does not match the plan "
+                             f"[>= {plan.kv_tokens}, {plan.num_kv_heads}, {plan.head_dim}]")
+    else:
+        _check_cache(plan, k_cache, v_cache)
     if lse is None and return_lse:
         lse = torch.empty(T, plan.num_qo_heads, dtype=torch.float32, device=plan.device)
     out, lse = _outputs(plan, q, out, lse)

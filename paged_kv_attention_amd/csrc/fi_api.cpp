@@ -132,7 +132,8 @@ AttnArgs plan_attn_args(const fi_plan_t* p, const char* base, int level, const v
 hipError_t plan_launch_level(const fi_plan_t* p, int level, const AttnArgs& a, hipStream_t s) {
   const int D = p->hp.desc.head_dim;
   if (p->hp.level[level].rows_per_block == ROWS_WIDE)
-    return launch_wide(a, D, p->hp.desc.kind == FI_KIND_CASCADE && level == 0, s);
+    return launch_wide(a, D, p->hp.desc.kind == FI_KIND_CASCADE && level == 0,
+                       p->hp.desc.kv_layout == FI_KV_LAYOUT_RAGGED, s);
   if (p->hp.desc.decode_engine == FI_ENGINE_VALU) return launch_decode_valu(a, D, s);
   return launch_decode(a, D, s);
 }
@@ -171,7 +172,8 @@ hipError_t launch_fused(const fi_plan_t* p, const void* q, const void* k, const 
   wa.num_workers = p->hp.level[0].num_workers;
   da.num_workers = p->hp.level[1].num_workers;
   return launch_pod(wa, da, at<int32_t>(p, p->lay.meta), p->hp.desc.head_dim,
-                    p->hp.desc.kind == FI_KIND_CASCADE, s);
+                    p->hp.desc.kind == FI_KIND_CASCADE,
+                    p->hp.desc.kv_layout == FI_KV_LAYOUT_RAGGED, s);
 }
 
 fi_status run_merge(const fi_plan_t* p, void* o, float* lse, hipStream_t s) {

@@ -26,8 +26,11 @@ struct Tile {
 
 // Issue the loads of step s of item it into T. K and V are read once per call,
 // so the loads are nontemporal (on MI355X they stream from HBM ~13% faster
-// than default-policy loads).
-template <int D, int NP, bool QT>
+// than default-policy loads). Paged layout: page id pid, kv head g at tile
+// (pid * Hkv + g) of ps tokens of D elements. RAGGED layout ([tokens][Hkv][D]):
+// the page list holds the first token of each ps-token run, token stride
+// Hkv * D elements.
+template <int D, int NP, bool QT, bool RAGGED = false>
 __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, int s,
                                            Tile<D, QT>& T, int col, int grp) {
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL;
@@ -36,7 +39,8 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, in
   const int T0 = it.t_begin + 32 * s;
   const int pb = T0 >> sh;
   const int plast = (it.t_end - 1) >> sh;
-  const int64_t tile_bytes = (int64_t)a.page_size * D * 2;
+  const int64_t tile_bytes = RAGGED ? (int64_t)D * 2 : (int64_t)a.page_size * D * 2;
+  const uint32_t tok = RAGGED ? (uint32_t)(a.num_kv_heads * D * 2) : (uint32_t)(D * 2);
   const char* kb[NP];
   const char* vb[NP];
 #pragma unroll
@@ -61,7 +65,8 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, in
       base = (col >> 3) ? kb[2 * blk + 1] : kb[2 * blk];
       slot = col & 7;
     }
-    const uint32_t off = (uint32_t)(slot * D + grp * 8) * 2u;
+    const uint32_t off = RAGGED ? (uint32_t)slot * tok + (uint32_t)(grp * 16)
+                                : (uint32_t)(slot * D + grp * 8) * 2u;
 #pragma unroll
     for (int j = 0; j < KJ; ++j)
       T.k[blk][j] = __builtin_nontemporal_load((const u32x4*)(base + off + 64u * j));
@@ -81,7 +86,9 @@ __device__ __forceinline__ void issue_tile(const AttnArgs& a, const Item& it, in
       base = (grp >> 1) ? vb[2 * (i >> 2) + 1] : vb[2 * (i >> 2)];
       slot = tl & 7;
     }
-    T.v[i] = __builtin_nontemporal_load((const vrow_t*)(base + (uint32_t)(slot * D + DPL * col) * 2u));
+    const uint32_t voff = RAGGED ? (uint32_t)slot * tok + (uint32_t)(DPL * col * 2)
+                                 : (uint32_t)(slot * D + DPL * col) * 2u;
+    T.v[i] = __builtin_nontemporal_load((const vrow_t*)(base + voff));
   }
 }
 
@@ -127,7 +134,7 @@ __device__ __forceinline__ void compute_step(const AttnArgs& a, const Item& it, 
 // it shares them with a second wavefront (two workgroups per CU); a ring of 2
 // keeps the query out of the tiles and loads it when an item's first step is
 // computed, ahead of the next step's loads.
-template <int D, int NP, bool CAUSAL = false, int RING = kRing>
+template <int D, int NP, bool CAUSAL = false, int RING = kRing, bool RAGGED = false>
 __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
   static_assert(RING == 2 || RING == 4, "rings of two or four tiles");
   constexpr int KJ = Cfg<D>::KJ;
@@ -160,8 +167,8 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
     // past the end of the stream: an in-bounds re-load of the current step,
     // every lane at lane 0's addresses (one line per load, so the extra
     // loads of the ring's last steps add next to no HBM traffic)
-    issue_tile<D, NP, QT>(a, valid ? iitem : citem, valid ? is : cs, Y, valid ? col : 0,
-                          valid ? grp : 0);
+    issue_tile<D, NP, QT, RAGGED>(a, valid ? iitem : citem, valid ? is : cs, Y, valid ? col : 0,
+                                  valid ? grp : 0);
     if (valid && ++is >= iitem.nsteps) {
       ++ii;
       is = 0;

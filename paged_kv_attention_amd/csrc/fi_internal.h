@@ -161,12 +161,15 @@ hipError_t launch_decode_fp8(const AttnArgs& a, int head_dim, hipStream_t stream
 hipError_t launch_decode_mxfp4(const AttnArgs& a, int head_dim, hipStream_t stream);
 // Wide level: one 4-wave workgroup per worker (a.num_workers workgroups);
 // list_q: query rows come through the member list (cascade prefix).
-hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream);
+// ragged: keys in a [tokens][Hkv][D] layout (block-sparse plans), the page
+// lists holding the first token of each page_size-token run.
+hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, bool ragged,
+                       hipStream_t stream);
 // Fused launch: wa.num_workers workgroups; workgroup b < meta[0] is wide
 // worker b, the others hold decode workers 4 (b - meta[0]) .. +3 of da;
 // list_q as for launch_wide.
 hipError_t launch_pod(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, int head_dim,
-                      bool list_q, hipStream_t stream);
+                      bool list_q, bool ragged, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_scatter(const ScatterArgs& a, hipStream_t stream);
 hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream);

@@ -409,6 +409,10 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
     if (d.causal) return set_error(FI_ERR_INVALID_ARG, "a block-sparse plan takes no causal mask");
     d.batch = 1;
   }
+  if (d.kv_layout != FI_KV_LAYOUT_PAGED && d.kv_layout != FI_KV_LAYOUT_RAGGED)
+    return set_error(FI_ERR_INVALID_ARG, "kv_layout %d", d.kv_layout);
+  if (d.kv_layout == FI_KV_LAYOUT_RAGGED && d.kind != FI_KIND_BLOCK_SPARSE)
+    return set_error(FI_ERR_UNSUPPORTED, "a ragged KV layout is read by block-sparse plans only");
   if (d.batch < 0) return set_error(FI_ERR_INVALID_ARG, "batch %d < 0", d.batch);
   if (d.num_qo_heads < 1 || d.num_kv_heads < 1)
     return set_error(FI_ERR_INVALID_ARG, "head counts must be >= 1");
@@ -674,76 +678,135 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
   return FI_OK;
 }
 
-// Variable block-sparse: every (kv head g, row block a) is a unit set over the
-// page list of a's selected column blocks (in column order), appended to
-// hp.plist; units in the order g, a, 128-row (or, in the decode role, 16-row)
-// block. Rows of a fit one 16-row block -> decode role of a POD launch.
-static fi_status build_block_sparse(const fi_plan_desc& d, int32_t qo_len, int32_t kv_len,
-                                    int32_t MB, const int32_t* row_sz, int32_t NB,
-                                    const int32_t* col_sz, const uint8_t* mask,
-                                    const int32_t* seq_pages, HostPlan& hp) {
-  const int32_t Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads, ps = d.page_size;
-  if (qo_len < 0 || kv_len < 0 || MB < 0 || NB < 0)
-    return set_error(FI_ERR_INVALID_ARG, "negative block-sparse size");
-  if ((MB > 0 && !row_sz) || (NB > 0 && !col_sz) || (MB > 0 && NB > 0 && !mask) ||
-      (kv_len > 0 && !seq_pages))
+// A batch of block-sparse sequences, as the host arrays describe it: per
+// sequence s its query and key counts, its row and column block counts, and
+// offsets of its blocks and mask in the concatenated size and mask arrays.
+struct BsBatch {
+  int32_t S = 0;
+  const int32_t *qo_len = nullptr, *kv_len = nullptr, *nrb = nullptr, *ncb = nullptr;
+  const int32_t *row_sz = nullptr, *col_sz = nullptr;
+  const uint8_t* mask = nullptr;
+  const int32_t *kv_indptr = nullptr, *kv_indices = nullptr;   // kv_indices NULL: ragged
+  std::vector<int64_t> row_off, col_off, mask_off;              // per sequence
+};
+
+// Check the batch and compute the per-sequence offsets.
+static fi_status check_bs_batch(const fi_plan_desc& d, BsBatch& bb) {
+  const int32_t Hkv = d.num_kv_heads, ps = d.page_size, S = bb.S;
+  const bool ragged = d.kv_layout == FI_KV_LAYOUT_RAGGED;
+  if (S < 0) return set_error(FI_ERR_INVALID_ARG, "negative number of sequences");
+  if (S > 0 && (!bb.qo_len || !bb.kv_len || !bb.nrb || !bb.ncb || !bb.kv_indptr))
     return set_error(FI_ERR_INVALID_ARG, "block-sparse arrays are NULL");
-  for (int32_t g = 0; g < Hkv; ++g) {
-    int64_t rs = 0, cs = 0;
-    for (int32_t a = 0; a < MB; ++a) {
-      if (row_sz[g * MB + a] < 0) return set_error(FI_ERR_INVALID_ARG, "negative row block size");
-      rs += row_sz[g * MB + a];
-    }
-    for (int32_t b = 0; b < NB; ++b) {
-      const int32_t c = col_sz[g * NB + b];
-      if (c < 0) return set_error(FI_ERR_INVALID_ARG, "negative column block size");
-      if (c > 0 && cs % ps)
-        return set_error(FI_ERR_INVALID_ARG,
-                         "kv head %d: column block %d starts at key %lld, not a page boundary", g,
-                         b, (long long)cs);
-      cs += c;
-    }
-    if (rs != qo_len || cs != kv_len)
+  if (!ragged && S > 0 && !bb.kv_indices)
+    return set_error(FI_ERR_INVALID_ARG, "a paged block-sparse plan needs kv_indices");
+  if (S > 0 && bb.kv_indptr[0] != 0)
+    return set_error(FI_ERR_INVALID_ARG, "kv_indptr[0] = %d", bb.kv_indptr[0]);
+  bb.row_off.assign(S + 1, 0);
+  bb.col_off.assign(S + 1, 0);
+  bb.mask_off.assign(S + 1, 0);
+  for (int32_t q = 0; q < S; ++q) {
+    const int32_t qo = bb.qo_len[q], L = bb.kv_len[q], MB = bb.nrb[q], NB = bb.ncb[q];
+    if (qo < 0 || L < 0 || MB < 0 || NB < 0)
+      return set_error(FI_ERR_INVALID_ARG, "sequence %d: negative block-sparse size", q);
+    const int64_t span = (int64_t)bb.kv_indptr[q + 1] - bb.kv_indptr[q];
+    const int64_t want = ragged ? L : ceil_div(L, ps);
+    if (span != want)
       return set_error(FI_ERR_INVALID_ARG,
-                       "kv head %d: row blocks sum to %lld (qo_len %d), column blocks to %lld "
-                       "(kv_len %d)", g, (long long)rs, qo_len, (long long)cs, kv_len);
+                       "sequence %d: kv_indptr spans %lld %s for %d keys", q, (long long)span,
+                       ragged ? "tokens" : "pages", L);
+    bb.row_off[q + 1] = bb.row_off[q] + (int64_t)Hkv * MB;
+    bb.col_off[q + 1] = bb.col_off[q] + (int64_t)Hkv * NB;
+    bb.mask_off[q + 1] = bb.mask_off[q] + (int64_t)Hkv * MB * NB;
   }
+  if ((bb.row_off[S] > 0 && !bb.row_sz) || (bb.col_off[S] > 0 && !bb.col_sz) ||
+      (bb.mask_off[S] > 0 && !bb.mask))
+    return set_error(FI_ERR_INVALID_ARG, "block-sparse arrays are NULL");
+  for (int32_t q = 0; q < S; ++q) {
+    const int32_t MB = bb.nrb[q], NB = bb.ncb[q];
+    const int32_t* rsz = bb.row_sz + bb.row_off[q];
+    const int32_t* csz = bb.col_sz + bb.col_off[q];
+    for (int32_t g = 0; g < Hkv; ++g) {
+      int64_t rs = 0, cs = 0;
+      for (int32_t a = 0; a < MB; ++a) {
+        if (rsz[g * MB + a] < 0) return set_error(FI_ERR_INVALID_ARG, "negative row block size");
+        rs += rsz[g * MB + a];
+      }
+      for (int32_t b = 0; b < NB; ++b) {
+        const int32_t c = csz[g * NB + b];
+        if (c < 0) return set_error(FI_ERR_INVALID_ARG, "negative column block size");
+        if (c > 0 && cs % ps)
+          return set_error(FI_ERR_INVALID_ARG,
+                           "sequence %d, kv head %d: column block %d starts at key %lld, not a "
+                           "page boundary", q, g, b, (long long)cs);
+        cs += c;
+      }
+      if (rs != bb.qo_len[q] || cs != bb.kv_len[q])
+        return set_error(FI_ERR_INVALID_ARG,
+                         "sequence %d, kv head %d: row blocks sum to %lld (qo_len %d), column "
+                         "blocks to %lld (kv_len %d)", q, g, (long long)rs, bb.qo_len[q],
+                         (long long)cs, bb.kv_len[q]);
+    }
+  }
+  return FI_OK;
+}
+
+// Variable block-sparse over a batch of sequences: every (sequence, kv head
+// g, row block a) is a unit set over the page list of a's selected column
+// blocks (in column order), appended to hp.plist; units in the order
+// sequence, g, a, 128-row (or, in the decode role, 16-row) block. Rows of a
+// fit one 16-row block -> decode role of a POD launch. A paged batch lists
+// the pool's page ids (kv_indices); a ragged one (keys k[kv_indptr[s] + t]
+// of a [tokens][Hkv][D] tensor) lists the first token of each page_size-token
+// run, which the kernels address in the ragged layout.
+static fi_status build_block_sparse(const fi_plan_desc& d, const BsBatch& bb, HostPlan& hp) {
+  const int32_t Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads, ps = d.page_size;
+  const bool ragged = d.kv_layout == FI_KV_LAYOUT_RAGGED;
   const bool pod = d.launch == FI_LAUNCH_POD;
   std::vector<Unit> units[2];
-  for (int32_t g = 0; g < Hkv; ++g) {
-    int32_t q0 = 0;
-    for (int32_t a = 0; a < MB; ++a) {
-      const int32_t nq = row_sz[g * MB + a];
-      const int32_t off = (int32_t)hp.plist.size();
-      int32_t t_lim = 0, c0 = 0;
-      for (int32_t b = 0; b < NB; ++b) {
-        const int32_t c = col_sz[g * NB + b];
-        if (c > 0 && mask[((int64_t)g * MB + a) * NB + b]) {
-          for (int32_t pg = c0 / ps; pg < (int32_t)ceil_div(c0 + c, ps); ++pg)
-            hp.plist.push_back(seq_pages[pg]);
-          t_lim += c;
+  int32_t q_seq = 0, unit_id = 0;   // first query row of the sequence; row-block counter
+  for (int32_t q = 0; q < bb.S; ++q) {
+    const int32_t MB = bb.nrb[q], NB = bb.ncb[q];
+    const int32_t* rsz = bb.row_sz + bb.row_off[q];
+    const int32_t* csz = bb.col_sz + bb.col_off[q];
+    const uint8_t* msk = bb.mask + bb.mask_off[q];
+    const int32_t base = bb.kv_indptr[q];
+    for (int32_t g = 0; g < Hkv; ++g) {
+      int32_t q0 = q_seq;
+      for (int32_t a = 0; a < MB; ++a) {
+        const int32_t nq = rsz[g * MB + a];
+        const int32_t off = (int32_t)hp.plist.size();
+        int32_t t_lim = 0, c0 = 0;
+        for (int32_t b = 0; b < NB; ++b) {
+          const int32_t c = csz[g * NB + b];
+          if (c > 0 && msk[((int64_t)g * MB + a) * NB + b]) {
+            for (int32_t pg = c0 / ps; pg < (int32_t)ceil_div(c0 + c, ps); ++pg)
+              hp.plist.push_back(ragged ? base + pg * ps : bb.kv_indices[base + pg]);
+            t_lim += c;
+          }
+          c0 += c;
         }
-        c0 += c;
+        const int64_t rows = (int64_t)nq * G;
+        const int lvl = (pod && rows <= ROWS_DECODE) ? 1 : 0;
+        const int32_t rpb = lvl ? ROWS_DECODE : ROWS_WIDE;
+        for (int64_t blk = 0; blk < ceil_div(rows, rpb); ++blk) {
+          Unit u;
+          u.unit = unit_id;
+          u.q_base = q0;
+          u.row0 = (int32_t)(blk * rpb);
+          u.n_rows = (int32_t)std::min<int64_t>(rows - blk * rpb, rpb);
+          u.g = g;
+          u.page_off = off;
+          u.t_lim = t_lim;
+          u.n_pages = (int32_t)ceil_div(t_lim, ps);
+          u.q_pos0 = 0;
+          u.flags = 0;
+          units[lvl].push_back(u);
+        }
+        q0 += nq;
+        ++unit_id;
       }
-      const int64_t rows = (int64_t)nq * G;
-      const int lvl = (pod && rows <= ROWS_DECODE) ? 1 : 0;
-      const int32_t rpb = lvl ? ROWS_DECODE : ROWS_WIDE;
-      for (int64_t blk = 0; blk < ceil_div(rows, rpb); ++blk) {
-        Unit u;
-        u.unit = g * MB + a;
-        u.q_base = q0;
-        u.row0 = (int32_t)(blk * rpb);
-        u.n_rows = (int32_t)std::min<int64_t>(rows - blk * rpb, rpb);
-        u.g = g;
-        u.page_off = off;
-        u.t_lim = t_lim;
-        u.n_pages = (int32_t)ceil_div(t_lim, ps);
-        u.q_pos0 = 0;
-        u.flags = 0;
-        units[lvl].push_back(u);
-      }
-      q0 += nq;
     }
+    q_seq += bb.qo_len[q];
   }
   int32_t next_row = 0;
   LevelBuild lb[2];
@@ -1035,44 +1098,78 @@ extern "C" fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_
   return FI_OK;
 }
 
-extern "C" fi_status fi_workspace_size_block_sparse(const fi_plan_desc* desc, int32_t qo_len,
-                                                    int32_t kv_len, int32_t num_row_blocks,
-                                                    int32_t num_col_blocks, size_t* dev_bytes,
-                                                    size_t* host_bytes) {
-  clear_error();
-  fi_plan_desc d;
-  fi_status st = fill_defaults(desc, d);
-  if (st != FI_OK) return st;
-  if (!dev_bytes || !host_bytes) return set_error(FI_ERR_INVALID_ARG, "NULL output pointer");
-  if (qo_len < 0 || kv_len < 0 || num_row_blocks < 0 || num_col_blocks < 0)
-    return set_error(FI_ERR_INVALID_ARG, "negative size bound");
-  int32_t num_cus = d.num_cus;
-  if (num_cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&num_cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-            hipSuccess)
-      return set_error(FI_ERR_HIP, "could not query the device's compute units");
-  }
-  const int64_t Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads, MB = num_row_blocks;
+// Workspace bound of a block-sparse batch (the checked batch bb).
+static void bs_layout_bound(const fi_plan_desc& d, int32_t num_cus, const BsBatch& bb,
+                            size_t* dev_bytes, size_t* host_bytes) {
+  const int64_t Hkv = d.num_kv_heads, G = d.num_qo_heads / d.num_kv_heads;
   const int64_t P = (int64_t)num_cus * std::max(1, d.workers_per_cu / 2);
   const int64_t S1 = d.launch == FI_LAUNCH_POD ? WAVES_PER_BLOCK * P : 0;
-  const int64_t seq_pages = ceil_div(kv_len, d.page_size);
-  // units: every (kv head, row block) in blocks of at least 16 rows
-  const int64_t units = Hkv * (ceil_div((int64_t)qo_len * G, ROWS_DECODE) + MB);
   const int64_t c_det = std::max(1, d.det_chunk_pages);
+  // units: every (sequence, kv head, row block) in blocks of at least 16 rows;
+  // pages: each unit's list is at most its sequence's pages
+  int64_t units = 0, unit_pages = 0, q_rows = 0, plist = 0;
+  for (int32_t q = 0; q < bb.S; ++q) {
+    const int64_t seq_pages = ceil_div(bb.kv_len[q], d.page_size);
+    const int64_t u = Hkv * (ceil_div((int64_t)bb.qo_len[q] * G, ROWS_DECODE) + bb.nrb[q]);
+    units += u;
+    unit_pages += u * seq_pages;
+    q_rows += bb.qo_len[q];
+    plist += Hkv * bb.nrb[q] * seq_pages;
+  }
   auto items_of = [&](int64_t S) {
-    return d.deterministic ? units * seq_pages / c_det + units : S + units;
+    return d.deterministic ? unit_pages / c_det + units : S + units;
   };
   size_t n_items[2] = {(size_t)items_of(P), S1 ? (size_t)items_of(S1) : 0};
   const int32_t workers[2] = {(int32_t)P, (int32_t)S1};
   const int64_t part_rows = ((int64_t)n_items[0] + (int64_t)n_items[1]) * ROWS_WIDE;
-  const int64_t merges = Hkv * qo_len + 2 * units;
+  const int64_t merges = Hkv * q_rows + 2 * units;
   Layout L = layout_for(workers, n_items, (size_t)merges, (size_t)part_rows, 0, 0,
-                        (size_t)part_rows, d.head_dim, (size_t)(Hkv * MB * seq_pages));
+                        (size_t)part_rows, d.head_dim, (size_t)plist);
   *dev_bytes = L.dev_bytes;
   *host_bytes = L.blob_bytes;
+}
+
+static fi_status bs_begin(const fi_plan_desc* desc, fi_plan_desc& d) {
+  fi_status st = fill_defaults(desc, d);
+  if (st != FI_OK) return st;
+  if (d.kind != FI_KIND_BLOCK_SPARSE)
+    return set_error(FI_ERR_INVALID_ARG, "block-sparse calls need kind FI_KIND_BLOCK_SPARSE");
   return FI_OK;
+}
+
+extern "C" fi_status fi_workspace_size_block_sparse_batch(
+    const fi_plan_desc* desc, int32_t num_seqs, const int32_t* qo_len_h, const int32_t* kv_len_h,
+    const int32_t* num_row_blocks_h, const int32_t* num_col_blocks_h, size_t* dev_bytes,
+    size_t* host_bytes) {
+  clear_error();
+  fi_plan_desc d;
+  fi_status st = bs_begin(desc, d);
+  if (st != FI_OK) return st;
+  if (!dev_bytes || !host_bytes) return set_error(FI_ERR_INVALID_ARG, "NULL output pointer");
+  if (num_seqs < 0) return set_error(FI_ERR_INVALID_ARG, "negative number of sequences");
+  if (num_seqs > 0 && (!qo_len_h || !kv_len_h || !num_row_blocks_h || !num_col_blocks_h))
+    return set_error(FI_ERR_INVALID_ARG, "block-sparse arrays are NULL");
+  BsBatch bb;
+  bb.S = num_seqs;
+  bb.qo_len = qo_len_h;
+  bb.kv_len = kv_len_h;
+  bb.nrb = num_row_blocks_h;
+  bb.ncb = num_col_blocks_h;
+  for (int32_t q = 0; q < num_seqs; ++q)
+    if (qo_len_h[q] < 0 || kv_len_h[q] < 0 || num_row_blocks_h[q] < 0 || num_col_blocks_h[q] < 0)
+      return set_error(FI_ERR_INVALID_ARG, "negative size bound");
+  int32_t num_cus = d.num_cus;
+  if (num_cus == 0 && (st = device_cus(num_cus)) != FI_OK) return st;
+  bs_layout_bound(d, num_cus, bb, dev_bytes, host_bytes);
+  return FI_OK;
+}
+
+extern "C" fi_status fi_workspace_size_block_sparse(const fi_plan_desc* desc, int32_t qo_len,
+                                                    int32_t kv_len, int32_t num_row_blocks,
+                                                    int32_t num_col_blocks, size_t* dev_bytes,
+                                                    size_t* host_bytes) {
+  return fi_workspace_size_block_sparse_batch(desc, 1, &qo_len, &kv_len, &num_row_blocks,
+                                              &num_col_blocks, dev_bytes, host_bytes);
 }
 
 extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_h,
@@ -1128,6 +1225,43 @@ extern "C" fi_status fi_plan(const fi_plan_desc* desc, const int32_t* kv_indptr_
                      stream, out);
 }
 
+extern "C" fi_status fi_plan_block_sparse_batch(
+    const fi_plan_desc* desc, int32_t num_seqs, const int32_t* qo_len_h, const int32_t* kv_len_h,
+    const int32_t* num_row_blocks_h, const int32_t* row_block_sz_h,
+    const int32_t* num_col_blocks_h, const int32_t* col_block_sz_h, const uint8_t* block_mask_h,
+    const int32_t* kv_indptr_h, const int32_t* kv_indices_h, void* ws_dev, size_t ws_dev_bytes,
+    void* ws_host, size_t ws_host_bytes, void* stream, fi_plan_t** out) {
+  clear_error();
+  if (!out) return set_error(FI_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  fi_plan_desc d;
+  fi_status st = begin_plan(desc, ws_dev, ws_host, d);
+  if (st != FI_OK) return st;
+  if (d.kind != FI_KIND_BLOCK_SPARSE)
+    return set_error(FI_ERR_INVALID_ARG, "fi_plan_block_sparse needs kind FI_KIND_BLOCK_SPARSE");
+  BsBatch bb;
+  bb.S = num_seqs;
+  bb.qo_len = qo_len_h;
+  bb.kv_len = kv_len_h;
+  bb.nrb = num_row_blocks_h;
+  bb.ncb = num_col_blocks_h;
+  bb.row_sz = row_block_sz_h;
+  bb.col_sz = col_block_sz_h;
+  bb.mask = block_mask_h;
+  bb.kv_indptr = kv_indptr_h;
+  bb.kv_indices = d.kv_layout == FI_KV_LAYOUT_RAGGED ? nullptr : kv_indices_h;
+  st = check_bs_batch(d, bb);
+  if (st != FI_OK) return st;
+  fi_plan_t* p = new fi_plan_t();
+  p->hp.desc = d;
+  st = build_block_sparse(d, bb, p->hp);
+  if (st != FI_OK) {
+    delete p;
+    return st;
+  }
+  return finish_plan(p, nullptr, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes, stream, out);
+}
+
 extern "C" fi_status fi_plan_block_sparse(const fi_plan_desc* desc, int32_t qo_len,
                                           int32_t kv_len, int32_t num_row_blocks,
                                           const int32_t* row_block_sz_h, int32_t num_col_blocks,
@@ -1137,22 +1271,17 @@ extern "C" fi_status fi_plan_block_sparse(const fi_plan_desc* desc, int32_t qo_l
                                           size_t ws_dev_bytes, void* ws_host,
                                           size_t ws_host_bytes, void* stream, fi_plan_t** out) {
   clear_error();
-  if (!out) return set_error(FI_ERR_INVALID_ARG, "out is NULL");
-  *out = nullptr;
-  fi_plan_desc d;
-  fi_status st = begin_plan(desc, ws_dev, ws_host, d);
-  if (st != FI_OK) return st;
-  if (d.kind != FI_KIND_BLOCK_SPARSE)
-    return set_error(FI_ERR_INVALID_ARG, "fi_plan_block_sparse needs kind FI_KIND_BLOCK_SPARSE");
-  fi_plan_t* p = new fi_plan_t();
-  p->hp.desc = d;
-  st = build_block_sparse(d, qo_len, kv_len, num_row_blocks, row_block_sz_h, num_col_blocks,
-                          col_block_sz_h, block_mask_h, seq_pages_h, p->hp);
-  if (st != FI_OK) {
-    delete p;
-    return st;
-  }
-  return finish_plan(p, nullptr, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes, stream, out);
+  if (desc && desc->kv_layout != FI_KV_LAYOUT_PAGED)
+    return set_error(FI_ERR_INVALID_ARG,
+                     "fi_plan_block_sparse reads a paged sequence (ragged: the batch call)");
+  if (kv_len < 0 || qo_len < 0)
+    return set_error(FI_ERR_INVALID_ARG, "negative block-sparse size");
+  const int32_t ps = desc ? desc->page_size : 0;
+  const int32_t indptr[2] = {0, ps > 0 ? (kv_len + ps - 1) / ps : 0};
+  return fi_plan_block_sparse_batch(desc, 1, &qo_len, &kv_len, &num_row_blocks, row_block_sz_h,
+                                    &num_col_blocks, col_block_sz_h, block_mask_h, indptr,
+                                    seq_pages_h, ws_dev, ws_dev_bytes, ws_host, ws_host_bytes,
+                                    stream, out);
 }
 
 extern "C" void fi_plan_destroy(fi_plan_t* plan) { delete plan; }

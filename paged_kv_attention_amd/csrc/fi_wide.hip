@@ -102,27 +102,31 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* p) {
 // area) holds tokens blk*TPC .. +TPC-1 of the step, which share one page
 // (TPC divides a page), so a copy's page base is one scalar and the lane's
 // part (token slot in the page and swizzled chunk) is fixed for the kernel.
+// tok: bytes from one token of a page to the next in global memory (D * 2 in
+// the paged layout, Hkv * D * 2 in the ragged one).
 template <int D, int NP>
 struct CopyLanes {
   static constexpr int CH = Cfg<D>::CH, NK = Lds<D>::NK, ROW = Lds<D>::ROW;
   static constexpr int TPC = 64 / CH;         // tokens per copy
   static constexpr int TPP = 32 / NP;         // tokens of the step per page (NP > 1)
   uint32_t k[NK], v[NK];
-  __device__ __forceinline__ CopyLanes(int wave, int lane) {
+  __device__ __forceinline__ CopyLanes(int wave, int lane, uint32_t tok) {
 #pragma unroll
     for (int c = 0; c < NK; ++c) {
       const int p = (wave * NK + c) * 64 + lane;    // 16-byte slot in the area
       const int t = p / CH, cs = p % CH;            // token of the step, stored chunk slot
       const int slot = t % TPP;                     // (NP = 1: plus the step's first slot)
-      k[c] = (uint32_t)(slot * ROW + (cs ^ (t % CH)) * 16);   // K: swizzled chunk
-      v[c] = (uint32_t)(slot * ROW + (cs ^ v_swizzle<D>(t)) * 16);
+      k[c] = (uint32_t)slot * tok + (uint32_t)((cs ^ (t % CH)) * 16);   // K: swizzled chunk
+      v[c] = (uint32_t)slot * tok + (uint32_t)((cs ^ v_swizzle<D>(t)) * 16);
     }
   }
 };
 
 // Copy step s of item it into LDS stage st (this wave's share: NK 1-KiB
-// copies for K and NK for V).
-template <int D, int NP>
+// copies for K and NK for V). Paged layout: page id pid, kv head g at tile
+// (pid * Hkv + g) of ps rows; RAGGED ([tokens][Hkv][D]): the page list holds
+// the first token of each ps-token run, row (token) stride Hkv * D elements.
+template <int D, int NP, bool RAGGED>
 __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, int s, char* stage,
                                            int wave, const CopyLanes<D, NP>& cl) {
   constexpr int NK = Lds<D>::NK, ROW = Lds<D>::ROW, TPC = CopyLanes<D, NP>::TPC;
@@ -130,7 +134,8 @@ __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, in
   const int T0 = it.t_begin + 32 * s;
   const int pb = T0 >> sh;
   const int plast = (it.t_end - 1) >> sh;
-  const int64_t tile_bytes = (int64_t)a.page_size * ROW;
+  const int64_t tile_bytes = RAGGED ? (int64_t)ROW : (int64_t)a.page_size * ROW;
+  const int64_t tok = RAGGED ? (int64_t)a.num_kv_heads * ROW : (int64_t)ROW;
   int pids[NP];   // the step's page ids, loaded together
 #pragma unroll
   for (int n = 0; n < NP; ++n) pids[n] = ld_uniform(it.plist, min(pb + n, plast));
@@ -142,7 +147,7 @@ __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, in
 #pragma unroll
     for (int j = 1; j < NP; ++j) pid = (n == j) ? pids[j] : pid;
     int64_t base = ((int64_t)pid * a.num_kv_heads + it.g) * tile_bytes;
-    if (NP == 1) base += (int64_t)(T0 & (a.page_size - 1)) * ROW;
+    if (NP == 1) base += (int64_t)(T0 & (a.page_size - 1)) * tok;
     __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.k_cache + base + cl.k[c]),
                                      (lds_vptr)(stage + blk * 1024), 16, 0, kCopyPolicy);
     __builtin_amdgcn_global_load_lds((global_vptr)((const char*)a.v_cache + base + cl.v[c]),
@@ -157,7 +162,7 @@ __device__ __forceinline__ void issue_step(const AttnArgs& a, const Item& it, in
 // __restrict__: the compiler then knows the copies into `next` cannot alias
 // the reads from `cur` and adds no wait of its own; the ordering across steps
 // is the explicit vmcnt wait plus barrier in the caller.
-template <int D, int NP>
+template <int D, int NP, bool RAGGED>
 __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int s, bool issue,
                                           char* __restrict__ next, const char* __restrict__ cur,
                                           const u32x4 (&qf)[2][Cfg<D>::KJ], State<D, 2>& st,
@@ -165,7 +170,7 @@ __device__ __forceinline__ void wide_step(const AttnArgs& a, const Item& it, int
                                           const CopyLanes<D, NP>& cl) {
   constexpr int KJ = Cfg<D>::KJ, DPL = Cfg<D>::DPL, CH = Cfg<D>::CH, ROW = Lds<D>::ROW;
   const int col = lane & 15, grp = lane >> 4;
-  if (issue) issue_step<D, NP>(a, it, s + kAhead, next, wave, cl);
+  if (issue) issue_step<D, NP, RAGGED>(a, it, s + kAhead, next, wave, cl);
   // row blocks of this wave that hold real rows (0, 1 or 2): a wave or block
   // of padding rows only takes part in the copies and barriers
   const int nmb = min(2, max(0, (it.n_rows - rl0 + 15) >> 4));
@@ -279,7 +284,7 @@ __device__ __forceinline__ void finalize_wide(const AttnArgs& a, const Item& it,
 }
 
 // The items of workgroup worker wg (the whole 4-wave block).
-template <int D, int NP, bool LQ>
+template <int D, int NP, bool LQ, bool RAGGED>
 __device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
   constexpr int KJ = Cfg<D>::KJ, NK = Lds<D>::NK;
   __shared__ __attribute__((aligned(1024))) char lds[kStages * Lds<D>::STAGE];
@@ -290,7 +295,8 @@ __device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
   if (wg >= a.num_workers) return;
   const int i_end = ld_uniform(a.worker_indptr, wg + 1);
   const int rl0 = wave * kRowsPerWave;
-  const CopyLanes<D, NP> cl(wave, lane);
+  const CopyLanes<D, NP> cl(wave, lane,
+                           RAGGED ? (uint32_t)(a.num_kv_heads * Lds<D>::ROW) : (uint32_t)Lds<D>::ROW);
 
   for (int i = ld_uniform(a.worker_indptr, wg); i < i_end; ++i) {
     const Item it = load_item(a, i);
@@ -312,7 +318,7 @@ __device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
-      wide_step<D, NP>(a, it, s, s + kAhead < n, next, cur, qf, st, rl0, wave, lane, cl);
+      wide_step<D, NP, RAGGED>(a, it, s, s + kAhead < n, next, cur, qf, st, rl0, wave, lane, cl);
       return true;
     };
     constexpr int SB = Lds<D>::STAGE;
@@ -331,9 +337,9 @@ __device__ __forceinline__ void wide_worker(const AttnArgs& a, int wg) {
   }
 }
 
-template <int D, int NP, bool LQ>
+template <int D, int NP, bool LQ, bool RAGGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void wide_kernel(AttnArgs a) {
-  wide_worker<D, NP, LQ>(a, blockIdx.x);
+  wide_worker<D, NP, LQ, RAGGED>(a, blockIdx.x);
 }
 
 // Mixed batch in one launch (POD attention: prefill and decode rows of one
@@ -344,65 +350,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void w
 // tiles, so a wavefront of either role needs at most half a SIMD's registers
 // and two workgroups share a CU: a CU holding one of each overlaps the matrix
 // work of the wide role with the HBM streaming of the decode role.
-template <int D, int NP, bool LQ>
+template <int D, int NP, bool LQ, bool RAGGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void pod_kernel(
     AttnArgs wa, AttnArgs da, const int32_t* __restrict__ meta) {
   const int n_wide = ld_uniform(meta, 0);
   if ((int)blockIdx.x < n_wide) {
-    wide_worker<D, NP, LQ>(wa, blockIdx.x);
+    wide_worker<D, NP, LQ, RAGGED>(wa, blockIdx.x);
   } else {
-    dec::decode_worker<D, NP, true, 2>(da, ((int)blockIdx.x - n_wide) * WAVES_PER_BLOCK +
-                                      uniform(threadIdx.x >> 6));
+    dec::decode_worker<D, NP, true, 2, RAGGED>(da, ((int)blockIdx.x - n_wide) * WAVES_PER_BLOCK +
+                                              uniform(threadIdx.x >> 6));
   }
 }
 
-template <int D, bool LQ>
+template <int D, bool LQ, bool RAGGED>
 hipError_t launch_np(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    launch_timed((wide_kernel<D, 4, LQ>), grid, dim3(256), s, a);
+    launch_timed((wide_kernel<D, 4, LQ, RAGGED>), grid, dim3(256), s, a);
   } else if (a.page_size == 16) {
-    launch_timed((wide_kernel<D, 2, LQ>), grid, dim3(256), s, a);
+    launch_timed((wide_kernel<D, 2, LQ, RAGGED>), grid, dim3(256), s, a);
   } else {
-    launch_timed((wide_kernel<D, 1, LQ>), grid, dim3(256), s, a);
+    launch_timed((wide_kernel<D, 1, LQ, RAGGED>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }
 
-template <int D, bool LQ>
+template <int D, bool LQ, bool RAGGED>
 hipError_t launch_pod_d(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, dim3 grid,
                         hipStream_t s) {
   if (wa.page_size == 8) {
-    launch_timed((pod_kernel<D, 4, LQ>), grid, dim3(256), s, wa, da, meta);
+    launch_timed((pod_kernel<D, 4, LQ, RAGGED>), grid, dim3(256), s, wa, da, meta);
   } else if (wa.page_size == 16) {
-    launch_timed((pod_kernel<D, 2, LQ>), grid, dim3(256), s, wa, da, meta);
+    launch_timed((pod_kernel<D, 2, LQ, RAGGED>), grid, dim3(256), s, wa, da, meta);
   } else {
-    launch_timed((pod_kernel<D, 1, LQ>), grid, dim3(256), s, wa, da, meta);
+    launch_timed((pod_kernel<D, 1, LQ, RAGGED>), grid, dim3(256), s, wa, da, meta);
   }
   return hipGetLastError();
+}
+
+// list_q (cascade prefix level: rows through the member list) and ragged
+// (block-sparse plans over a [tokens][Hkv][D] layout) never come together.
+template <int D>
+hipError_t launch_pod_kind(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, dim3 grid,
+                           bool list_q, bool ragged, hipStream_t s) {
+  if (list_q) return launch_pod_d<D, true, false>(wa, da, meta, grid, s);
+  if (ragged) return launch_pod_d<D, false, true>(wa, da, meta, grid, s);
+  return launch_pod_d<D, false, false>(wa, da, meta, grid, s);
+}
+
+template <int D>
+hipError_t launch_wide_kind(const AttnArgs& a, dim3 grid, bool list_q, bool ragged,
+                            hipStream_t s) {
+  if (list_q) return launch_np<D, true, false>(a, grid, s);
+  if (ragged) return launch_np<D, false, true>(a, grid, s);
+  return launch_np<D, false, false>(a, grid, s);
 }
 
 }  // namespace
 
 hipError_t launch_pod(const AttnArgs& wa, const AttnArgs& da, const int32_t* meta, int head_dim,
-                      bool list_q, hipStream_t stream) {
+                      bool list_q, bool ragged, hipStream_t stream) {
   if (wa.num_workers == 0) return hipSuccess;
+  if (list_q && ragged) return hipErrorInvalidValue;
   const dim3 grid(wa.num_workers);
-  if (head_dim == 128)
-    return list_q ? launch_pod_d<128, true>(wa, da, meta, grid, stream)
-                  : launch_pod_d<128, false>(wa, da, meta, grid, stream);
-  if (head_dim == 64)
-    return list_q ? launch_pod_d<64, true>(wa, da, meta, grid, stream)
-                  : launch_pod_d<64, false>(wa, da, meta, grid, stream);
+  if (head_dim == 128) return launch_pod_kind<128>(wa, da, meta, grid, list_q, ragged, stream);
+  if (head_dim == 64) return launch_pod_kind<64>(wa, da, meta, grid, list_q, ragged, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, hipStream_t stream) {
+hipError_t launch_wide(const AttnArgs& a, int head_dim, bool list_q, bool ragged,
+                       hipStream_t stream) {
   if (a.num_workers == 0) return hipSuccess;
+  if (list_q && ragged) return hipErrorInvalidValue;
   const dim3 grid(a.num_workers);
-  if (head_dim == 128)
-    return list_q ? launch_np<128, true>(a, grid, stream) : launch_np<128, false>(a, grid, stream);
-  if (head_dim == 64)
-    return list_q ? launch_np<64, true>(a, grid, stream) : launch_np<64, false>(a, grid, stream);
+  if (head_dim == 128) return launch_wide_kind<128>(a, grid, list_q, ragged, stream);
+  if (head_dim == 64) return launch_wide_kind<64>(a, grid, list_q, ragged, stream);
   return hipErrorInvalidValue;
 }
 

@@ -668,3 +668,108 @@ def test_fused_merge_records(det):
         q = host_plan("decode", indptr, L_, 32, 8, 128, ps, deterministic=det,
                       det_chunk_pages=16, num_cus=5, workers_per_cu=4, **kw).info()
         assert not q["fused_merge"] and len(q["item_rec"]) == 0
+
+
+def _bs_batch_spec(rng, Hkv, ps, seqs, layout):
+    """Per sequence (queries, keys, row blocks, column blocks): sizes, masks,
+    and the key table of a paged pool (page ids) or a ragged tensor (token
+    offsets with gaps between sequences)."""
+    def cuts(total, n, align):
+        if n == 0:
+            return np.zeros(0, np.int32)
+        units = -(-total // align)
+        e = np.sort(rng.integers(0, units + 1, n - 1)) * align
+        return np.diff(np.concatenate([[0], np.minimum(e, total), [total]])).astype(np.int32)
+    rows, cols, masks = [], [], []
+    for (T, Lk, MB, NB) in seqs:
+        rows.append(np.stack([cuts(T, MB, 1) for _ in range(Hkv)]).reshape(Hkv, MB))
+        cols.append(np.stack([cuts(Lk, NB, ps) for _ in range(Hkv)]).reshape(Hkv, NB))
+        masks.append((rng.random((Hkv, MB, NB)) < 0.5).astype(np.uint8))
+    if layout == "paged":
+        n = [-(-Lk // ps) for (_, Lk, _, _) in seqs]
+        indptr = _indptr(n)
+        indices = rng.permutation(int(indptr[-1]) + 7)[: int(indptr[-1])].astype(np.int32)
+    else:
+        lens = [Lk for (_, Lk, _, _) in seqs]
+        indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        indices = None
+    return rows, cols, masks, indptr, indices
+
+
+@pytest.mark.parametrize("layout", ["paged", "ragged"])
+@pytest.mark.parametrize("launch", ["pod", "separate"])
+@pytest.mark.parametrize("det", [False, True])
+def test_block_sparse_batch_plan_matches_reference(layout, launch, det):
+    """A batch of block-sparse sequences, paged or ragged: the C++ plan equals
+    plan_ref rule 7 element for element, page lists included, every query
+    row of every sequence is written exactly once, and the plan fits the
+    batch workspace bound."""
+    rng = np.random.default_rng(71 + det)
+    Hq, Hkv, ps = 16, 4, 16
+    seqs = [(300, 1000, 5, 7), (3, 64, 1, 2), (0, 200, 0, 3), (40, 333, 3, 4), (1, 17, 1, 1)]
+    rows, cols, masks, indptr, indices = _bs_batch_spec(rng, Hkv, ps, seqs, layout)
+    qo = [s[0] for s in seqs]
+    kl = [s[1] for s in seqs]
+    p = fi.BlockSparsePlan(qo, kl, rows, cols, masks, None, Hq, Hkv, 128, ps, kv_indptr=indptr,
+                           kv_indices=indices, layout=layout, device=None, num_cus=5,
+                           workers_per_cu=4, deterministic=det, det_chunk_pages=6,
+                           launch=launch)
+    info = p.info()
+    P = 5 * 2
+    ref = plan_ref("block_sparse", Hq, Hkv, ps, [0], [], **level_params(info),
+                   deterministic=det, det_chunk_pages=6,
+                   pod_blocks=P if launch == "pod" else None,
+                   block_sparse_batch=(qo, rows, cols, masks, indptr, indices))
+    compare(info, ref)
+    assert np.array_equal(info["plist"], np.array(ref["plist"], dtype=np.int32))
+    G = Hq // Hkv
+    T = sum(qo)
+    seen = np.zeros((T, Hq), dtype=np.int64)
+    for lv in info["levels"]:
+        for it in lv["items"]:
+            if it[5] & 2:
+                continue
+            for rho in range(it[1], it[1] + it[2]):
+                seen[it[0] + rho // G, it[3] * G + rho % G] += 1
+    for m in info["merges"]:
+        for rho in range(m[1], m[1] + m[2]):
+            seen[m[0] + rho // G, m[3] * G + rho % G] += 1
+    assert np.all(seen == 1)
+    d = L.PlanDesc(kind=L.FI_KIND_BLOCK_SPARSE, batch=1, num_qo_heads=Hq, num_kv_heads=Hkv,
+                   head_dim=128, page_size=ps, deterministic=int(det), det_chunk_pages=6,
+                   num_cus=5, workers_per_cu=4,
+                   launch=L.FI_LAUNCH_POD if launch == "pod" else L.FI_LAUNCH_SEPARATE,
+                   kv_layout=L.FI_KV_LAYOUT_RAGGED if layout == "ragged" else 0)
+    db, hb = ctypes.c_size_t(), ctypes.c_size_t()
+    a = p._ha
+    assert fi.load().fi_workspace_size_block_sparse_batch(
+        ctypes.byref(d), len(seqs), a["qo_len"].ctypes.data_as(L.I32P),
+        a["kv_len"].ctypes.data_as(L.I32P), a["nrb"].ctypes.data_as(L.I32P),
+        a["ncb"].ctypes.data_as(L.I32P), ctypes.byref(db), ctypes.byref(hb)) == 0
+    assert db.value >= info["dev_bytes_used"] and hb.value >= info["host_bytes_used"]
+
+
+def test_block_sparse_batch_errors():
+    rng = np.random.default_rng(3)
+    Hkv, ps = 2, 16
+    seqs = [(20, 100, 2, 3), (5, 40, 1, 2)]
+    rows, cols, masks, indptr, indices = _bs_batch_spec(rng, Hkv, ps, seqs, "ragged")
+    kw = dict(device=None, num_cus=4, layout="ragged")
+    bad = indptr.copy()
+    bad[2] += 1                             # ragged span != kv_len
+    with pytest.raises(fi.FIError, match="spans"):
+        fi.BlockSparsePlan([20, 5], [100, 40], rows, cols, masks, None, 8, 2, 64, ps,
+                           kv_indptr=bad, **kw)
+    with pytest.raises(fi.FIError, match="spans"):   # paged: spans are pages
+        fi.BlockSparsePlan([20, 5], [100, 40], rows, cols, masks, None, 8, 2, 64, ps,
+                           kv_indptr=indptr, kv_indices=np.arange(200, dtype=np.int32),
+                           device=None, num_cus=4)
+    # a ragged layout is for block-sparse plans only
+    d = L.PlanDesc(kind=L.FI_KIND_DECODE, batch=1, num_qo_heads=8, num_kv_heads=2, head_dim=64,
+                   page_size=16, num_cus=4, kv_layout=L.FI_KV_LAYOUT_RAGGED)
+    h = ctypes.c_void_p()
+    ip = np.array([0, 1], np.int32)
+    ln = np.array([5], np.int32)
+    assert fi.load().fi_plan(ctypes.byref(d), ip.ctypes.data_as(L.I32P),
+                             ln.ctypes.data_as(L.I32P), None, None, None, None, None, None, 0,
+                             None, 0, None, ctypes.byref(h)) == L.FI_ERR_UNSUPPORTED

@@ -453,7 +453,8 @@ def _mut_merge_sign(o1, l1, o2, l2):
 
 
 _ORIG = {n: getattr(A, n) for n in ("gather_tokens", "attend", "merge_two", "paged_append",
-                                    "paged_decode_fp8", "e4m3_values", "_chain", "block_sparse")}
+                                    "paged_decode_fp8", "e4m3_values", "_chain", "block_sparse",
+                                    "gather_ragged")}
 
 
 def _mut_append_top_left(q, qo_indptr, k_pool, v_pool, kv_indptr, kv_indices, kv_len,
@@ -749,6 +750,104 @@ def test_block_sparse_row_without_keys_is_zero_and_neg_inf():
     assert np.all(o[r0:r1, 0:2] == 0) and np.all(np.isneginf(lse[r0:r1, 0:2]))
 
 
+def block_sparse_batch_case(seed, seqs=((9, 23, 3, 4), (5, 8, 2, 1), (0, 12, 0, 2), (7, 1, 1, 1)),
+                            Hkv=2, G=2, D=4, ps=4, p_mask=0.5):
+    """A tiny batch: per sequence (queries, keys, row blocks, column blocks);
+    dense per-sequence keys, a ragged [tokens, Hkv, D] copy (sequences at
+    seeded gaps in the tensor: kv_indptr is not the running sum) and a paged
+    copy in a random pool."""
+    rng = np.random.default_rng(seed)
+    dks, dvs, rows, cols, masks, qo, kl = [], [], [], [], [], [], []
+    for (T, Lk, MB, NB) in seqs:
+        dks.append(rng.standard_normal((Hkv, Lk, D)))
+        dvs.append(rng.standard_normal((Hkv, Lk, D)))
+        rows.append(np.stack([_cuts(rng, T, MB) if MB else np.zeros(0, np.int64)
+                              for _ in range(Hkv)]).reshape(Hkv, MB))
+        cols.append(np.stack([_cuts(rng, Lk, NB, ps) for _ in range(Hkv)]))
+        masks.append(rng.random((Hkv, MB, NB)) < p_mask)
+        qo.append(T)
+        kl.append(Lk)
+    gaps = rng.integers(0, 5, len(seqs))
+    starts = np.cumsum(np.concatenate([[0], np.asarray(kl[:-1]) + gaps[:-1]])) + gaps[0]
+    N = int(starts[-1] + kl[-1] + 3)
+    kr = np.full((N, Hkv, D), np.nan)
+    vr = np.full((N, Hkv, D), np.nan)
+    for s, a0 in enumerate(starts):
+        kr[a0:a0 + kl[s]] = dks[s].transpose(1, 0, 2)
+        vr[a0:a0 + kl[s]] = dvs[s].transpose(1, 0, 2)
+    # paged copy: every sequence's pages at random places of one pool
+    n = [-(-L // ps) for L in kl]
+    P = sum(n) + 2
+    perm = rng.permutation(P)
+    kp = np.full((P, Hkv, ps, D), np.nan)
+    vp = np.full((P, Hkv, ps, D), np.nan)
+    pindptr = np.concatenate([[0], np.cumsum(n)])
+    pidx = perm[:sum(n)]
+    for s in range(len(seqs)):
+        for t in range(kl[s]):
+            pg = pidx[pindptr[s] + t // ps]
+            kp[pg, :, t % ps] = dks[s][:, t]
+            vp[pg, :, t % ps] = dvs[s][:, t]
+    q = rng.standard_normal((sum(qo), Hkv * G, D))
+    return dict(q=q, dks=dks, dvs=dvs, rows=rows, cols=cols, masks=masks, qo=qo, kl=kl,
+                kr=kr, vr=vr, r_indptr=np.append(starts, 0)[:-1], kp=kp, vp=vp,
+                p_indptr=pindptr, p_idx=pidx, ps=ps)
+
+
+def check_block_sparse_batch_brute(seed=11):
+    c = block_sparse_batch_case(seed)
+    for m in c["masks"]:
+        if m.shape[1] > 1 and m.shape[2] > 1:
+            m[:, 0, 1] = True
+            m[:, 1, 0] = False
+    scale = 0.41
+    o, lse = A.block_sparse_batch(c["q"], c["kr"], c["vr"], c["qo"], c["kl"], c["rows"],
+                                  c["cols"], c["masks"], scale, c["r_indptr"])
+    q0 = 0
+    for s, T in enumerate(c["qo"]):
+        if T:
+            o_ref, l_ref = brute_block_sparse(c["q"][q0:q0 + T], c["dks"][s], c["dvs"][s],
+                                              c["rows"][s], c["cols"][s], c["masks"][s], scale)
+            np.testing.assert_allclose(o[q0:q0 + T], o_ref, rtol=0, atol=1e-12)
+            np.testing.assert_array_equal(np.isinf(lse[q0:q0 + T]), np.isinf(l_ref))
+            fin = np.isfinite(l_ref)
+            np.testing.assert_allclose(lse[q0:q0 + T][fin], l_ref[fin], rtol=1e-13, atol=0)
+        q0 += T
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_block_sparse_batch_brute_force(seed):
+    """A ragged batch (sequences at gaps in the tensor, one without queries,
+    one of a single key) against pure-Python loops per sequence."""
+    check_block_sparse_batch_brute(seed)
+
+
+def test_block_sparse_batch_paged_equals_ragged_and_per_sequence():
+    """The same keys laid out paged (a permuted pool) and ragged give the same
+    result, and each sequence's rows equal block_sparse on that sequence
+    alone with its own page list."""
+    c = block_sparse_batch_case(13)
+    scale = 0.3
+    args = (c["q"], c["qo"], c["kl"], c["rows"], c["cols"], c["masks"], scale)
+    o_r, l_r = A.block_sparse_batch(c["q"], c["kr"], c["vr"], *args[1:], c["r_indptr"])
+    o_p, l_p = A.block_sparse_batch(c["q"], c["kp"], c["vp"], *args[1:], c["p_indptr"],
+                                    kv_indices=c["p_idx"], page_size=c["ps"])
+    np.testing.assert_allclose(o_p, o_r, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(l_p, l_r)
+    q0 = 0
+    for s, T in enumerate(c["qo"]):
+        pages = c["p_idx"][c["p_indptr"][s]:c["p_indptr"][s + 1]]
+        o1, l1 = A.block_sparse(c["q"][q0:q0 + T], c["kp"], c["vp"], pages, c["kl"][s], c["ps"],
+                                c["rows"][s], c["cols"][s], c["masks"][s], scale)
+        np.testing.assert_array_equal(o1, o_p[q0:q0 + T])
+        np.testing.assert_array_equal(l1, l_p[q0:q0 + T])
+        q0 += T
+
+
+def _mut_ragged_from_zero(kv, start, length, kv_head):
+    return _ORIG["gather_ragged"](kv, 0, length, kv_head)
+
+
 def _mut_block_sparse_mask_transposed(q, kp, vp, idx, Lk, ps, row, col, mask, scale):
     return _ORIG["block_sparse"](q, kp, vp, idx, Lk, ps, row, col,
                                  np.transpose(np.asarray(mask), (0, 2, 1)), scale)
@@ -782,6 +881,7 @@ MUTATIONS = {
     "cascade_no_parents": ("_chain", _mut_chain_own_group_only, check_cascade_tree),
     "block_sparse_mask_transposed": ("block_sparse", _mut_block_sparse_mask_transposed,
                                      check_block_sparse_brute),
+    "ragged_from_zero": ("gather_ragged", _mut_ragged_from_zero, check_block_sparse_batch_brute),
 }
 
 

@@ -18,9 +18,9 @@ import oracle
 import paged_kv_attention_amd as fi
 from tests.helpers import (compare, gpu_decode, np_pools, oracle_decode, request_rows,
                            sample_requests)
-from workloads import (cascade_flat_tables, make_append, make_block_sparse, make_cascade,
-                       make_config, make_decode, make_pod_mix, make_sparse_video, to_fp8_cache,
-                       to_mxfp4_cache)
+from workloads import (cascade_flat_tables, make_append, make_block_sparse,
+                       make_block_sparse_batch, make_cascade, make_config, make_decode,
+                       make_pod_mix, make_sparse_video, to_fp8_cache, to_mxfp4_cache, to_ragged)
 
 pytestmark = pytest.mark.gpu
 
@@ -951,3 +951,107 @@ def test_cascade_tree(dev, det):
     of, lf = fi.paged_decode(p, g.q, g.k_cache, g.v_cache, ix.to(dev), w.sm_scale)
     torch.cuda.synchronize()
     compare(of, lf, o_ref, l_ref, a_ref, what="flat decode of the tree")
+
+
+# ---------------------------------------------------------------- block-sparse batches
+
+
+BSB_SEQS = [(90, 700, 6, 9), (3, 64, 1, 2), (0, 100, 0, 2), (40, 333, 3, 4), (1, 17, 1, 1),
+            (130, 1000, 4, 6)]
+
+
+def _bsb_run(w, dev, layout="paged", **kw):
+    """A block-sparse batch through one plan: the paged pool, or the ragged
+    copy of the same keys."""
+    g = w.to(dev)
+    if layout == "paged":
+        p = fi.BlockSparsePlan(w.qo_lens, [int(x) for x in w.kv_len], w.row_block_szs,
+                               w.col_block_szs, w.block_masks, None, w.num_qo_heads,
+                               w.num_kv_heads, w.head_dim, w.page_size, kv_indptr=w.kv_indptr,
+                               kv_indices=w.kv_indices, device=dev, **kw)
+        k, v = g.k_cache, g.v_cache
+    else:
+        p = fi.BlockSparsePlan(w.qo_lens, [int(x) for x in w.kv_len], w.row_block_szs,
+                               w.col_block_szs, w.block_masks, None, w.num_qo_heads,
+                               w.num_kv_heads, w.head_dim, w.page_size,
+                               kv_indptr=w.ragged_indptr, layout="ragged", device=dev, **kw)
+        k, v = g.k_ragged, g.v_ragged
+    o, lse = fi.block_sparse_attention(p, g.q, k, v, w.sm_scale)
+    torch.cuda.synchronize()
+    return o, lse, p
+
+
+def _bsb_oracle(w, rows=None):
+    kp, vp = np_pools(w)
+    args = (w.qo_lens, [int(x) for x in w.kv_len], [r.numpy() for r in w.row_block_szs],
+            [c.numpy() for c in w.col_block_szs], [m.numpy() for m in w.block_masks],
+            w.sm_scale, w.kv_indptr.numpy())
+    q = w.q.double().numpy()
+    kw = dict(kv_indices=w.kv_indices.numpy(), page_size=w.page_size, rows=rows)
+    o, lse = oracle.block_sparse_batch(q, kp, vp, *args, **kw)
+    a, _ = oracle.block_sparse_batch(q, kp, np.abs(vp), *args, **kw)
+    return o, lse, a
+
+
+@pytest.mark.parametrize("D,ps,G", [(128, 16, 4), (64, 8, 1), (128, 32, 8), (64, 16, 2),
+                                    (128, 64, 16), (128, 256, 4)])
+def test_block_sparse_batch_small_sweep(dev, D, ps, G):
+    """Several sequences in one block-sparse plan, each with its own variable
+    blocks and mask (one without queries, one of a single key), through the
+    paged pool and through a ragged copy of the same keys: every plan
+    variant against the oracle, and the ragged bits equal the paged ones."""
+    Hkv = 2
+    w = to_ragged(make_block_sparse_batch(BSB_SEQS, G * Hkv, Hkv, D, ps, seed=960 + D + ps + G,
+                                          poison="nan"), poison=True)
+    o_ref, l_ref, a_ref = _bsb_oracle(w)
+    for kw in [dict(), dict(launch="separate"), dict(deterministic=True, det_chunk_pages=1),
+               dict(launch="separate", deterministic=True, det_chunk_pages=2),
+               dict(min_chunk_pages=1), dict(pod_wide_blocks=1), dict(num_cus=3)]:
+        o, lse, _ = _bsb_run(w, dev, "paged", **kw)
+        compare(o, lse, o_ref, l_ref, a_ref, what=f"bs batch paged D={D} ps={ps} G={G} {kw}")
+        o2, lse2, _ = _bsb_run(w, dev, "ragged", **kw)
+        assert torch.equal(o2, o) and torch.equal(lse2, lse), f"ragged != paged {kw}"
+
+
+@pytest.mark.parametrize("layout", ["paged", "ragged"])
+def test_block_sparse_batch_deterministic_is_batch_invariant(dev, layout):
+    """Deterministic mode: a sequence's rows keep their bits alone and in
+    batches of other sequences, at any position."""
+    Hq, Hkv, D, ps = 16, 4, 128, 16
+    seqs = [(120, 900, 5, 8), (7, 300, 2, 3), (60, 500, 3, 5), (1, 40, 1, 2)]
+    base = make_block_sparse_batch(seqs, Hq, Hkv, D, ps, seed=981, poison=True)
+    target = 0
+    outs = []
+    for order in ([0], [2, 0, 3], [1, 3, 0, 2], [3, 2, 1, 0]):
+        sub = _bsb_subset(base, order)
+        o, lse, _ = _bsb_run(to_ragged(sub) if layout == "ragged" else sub, dev, layout,
+                             deterministic=True, det_chunk_pages=4)
+        q0 = sum(sub.qo_lens[:order.index(target)])
+        outs.append((o[q0:q0 + seqs[target][0]].clone(), lse[q0:q0 + seqs[target][0]].clone()))
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+    o_ref, l_ref, a_ref = _bsb_oracle(base, rows=list(range(seqs[target][0])))
+    r = np.arange(seqs[target][0])
+    compare(outs[0][0], outs[0][1], o_ref[r], l_ref[r], a_ref[r],
+            what=f"bs batch target {layout} vs oracle")
+
+
+def _bsb_subset(w, order):
+    """The block-sparse batch of sequences ``order`` of ``w`` (same pool)."""
+    ptr, idx, qs = [0], [], []
+    q_off = np.concatenate([[0], np.cumsum(w.qo_lens)])
+    for s in order:
+        a, b = int(w.kv_indptr[s]), int(w.kv_indptr[s + 1])
+        idx.append(w.kv_indices[a:b])
+        ptr.append(ptr[-1] + (b - a))
+        qs.append(w.q[int(q_off[s]):int(q_off[s + 1])])
+    kw = {f: getattr(w, f) for f in ("name", "kind", "num_qo_heads", "num_kv_heads", "head_dim",
+                                      "page_size", "sm_scale", "seed", "k_cache", "v_cache")}
+    from workloads import Workload
+    return Workload(kv_len=w.kv_len[list(order)].clone(),
+                    kv_indptr=torch.tensor(ptr, dtype=torch.int32),
+                    kv_indices=torch.cat(idx).to(torch.int32), q=torch.cat(qs),
+                    qo_lens=[w.qo_lens[s] for s in order],
+                    row_block_szs=[w.row_block_szs[s] for s in order],
+                    col_block_szs=[w.col_block_szs[s] for s in order],
+                    block_masks=[w.block_masks[s] for s in order], **kw)

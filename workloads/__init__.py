@@ -16,6 +16,8 @@ from .synth import (  # noqa: F401
     make_cascade,
     make_pod_mix,
     make_block_sparse,
+    make_block_sparse_batch,
+    to_ragged,
     make_sparse_video,
     SPARSE_VIDEO_NAME,
     POD_MIX_NAME,

@@ -90,6 +90,18 @@ class Workload:
     row_block_sz: Optional[torch.Tensor] = None   # block_sparse: int32 [Hkv, MB]
     col_block_sz: Optional[torch.Tensor] = None   # int32 [Hkv, NB]
     block_mask: Optional[torch.Tensor] = None     # bool [Hkv, MB, NB]
+    # block-sparse batch: per sequence its queries and [Hkv, MB_s], [Hkv, NB_s],
+    # [Hkv, MB_s, NB_s] arrays (kv_len / kv_indptr / kv_indices as for decode)
+    qo_lens: Optional[list] = None
+    row_block_szs: Optional[list] = None
+    col_block_szs: Optional[list] = None
+    block_masks: Optional[list] = None
+    # ragged copy of the keys and values: [tokens, Hkv, D], sequence s in rows
+    # ragged_indptr[s] .. ragged_indptr[s+1]-1, followed by page_size - 1 (or
+    # more) rows no sequence owns
+    k_ragged: Optional[torch.Tensor] = None
+    v_ragged: Optional[torch.Tensor] = None
+    ragged_indptr: Optional[torch.Tensor] = None
 
     @property
     def batch(self) -> int:
@@ -100,7 +112,8 @@ class Workload:
         return int(self.k_cache.shape[0])
 
     def to(self, device) -> "Workload":
-        """Copy with every tensor moved to ``device``."""
+        """Copy with every tensor moved to ``device`` (the per-sequence block
+        lists stay on the host: they feed the plan)."""
         kw = {}
         for f in fields(self):
             v = getattr(self, f.name)
@@ -473,6 +486,76 @@ def make_block_sparse(qo_len: int, kv_len: int, num_qo_heads: int, num_kv_heads:
                     kv_indptr=torch.tensor([0, n], dtype=torch.int32), kv_indices=indices,
                     q=q, k_cache=k, v_cache=v, row_block_sz=row_block_sz,
                     col_block_sz=col_block_sz, block_mask=block_mask)
+
+
+def make_block_sparse_batch(seqs, num_qo_heads: int, num_kv_heads: int, head_dim: int,
+                            page_size: int, seed: int, density: float = 0.5,
+                            poison=True, name: str = "block_sparse_batch") -> Workload:
+    """A batch of block-sparse sequences in one paged pool: ``seqs`` lists
+    (queries, keys, row blocks, column blocks) per sequence; each gets its own
+    random cut points (column cuts on page boundaries; empty blocks occur)
+    and mask (block pairs kept with probability ``density``). Draw order:
+    per sequence its cuts and mask, then the page permutation, q, K pool, V
+    pool. q rows are the sequences' queries in order."""
+    gen = torch.Generator().manual_seed(seed)
+    Hkv = num_kv_heads
+    rows, cols, masks = [], [], []
+    for (T, Lk, MB, NB) in seqs:
+        r = [(_block_cuts(gen, T, MB, 1) if MB else torch.zeros(0, dtype=torch.int32))
+             for _ in range(Hkv)]
+        c = [(_block_cuts(gen, Lk, NB, page_size) if NB else torch.zeros(0, dtype=torch.int32))
+             for _ in range(Hkv)]
+        rows.append(torch.stack(r).reshape(Hkv, MB).to(torch.int32))
+        cols.append(torch.stack(c).reshape(Hkv, NB).to(torch.int32))
+        masks.append(torch.rand((Hkv, MB, NB), generator=gen) < density)
+    L = torch.tensor([s[1] for s in seqs], dtype=torch.int64)
+    n = _pages_for(L, page_size)
+    total = int(n.sum())
+    pool = _pool_size(total)
+    perm = torch.randperm(pool, generator=gen).to(torch.int32)
+    indptr = _indptr(n)
+    indices = perm[:total].clone()
+    T = sum(s[0] for s in seqs)
+    q = _randn_bf16(gen, (T, num_qo_heads, head_dim))
+    k = _randn_pool(gen, pool, Hkv, page_size, head_dim)
+    v = _randn_pool(gen, pool, Hkv, page_size, head_dim)
+    if poison:
+        tabs = [(indices, int(indptr[r]), int(L[r])) for r in range(len(seqs))]
+        _poison_pool(k, indices, tabs, _tail_value(poison))
+        _poison_pool(v, indices, tabs, _tail_value(poison))
+    return Workload(name=name, kind="block_sparse_batch", num_qo_heads=num_qo_heads,
+                    num_kv_heads=Hkv, head_dim=head_dim, page_size=page_size,
+                    sm_scale=fp32_scale(head_dim), seed=seed, kv_len=L.to(torch.int32),
+                    kv_indptr=indptr, kv_indices=indices, q=q, k_cache=k, v_cache=v,
+                    qo_lens=[s[0] for s in seqs], row_block_szs=rows, col_block_szs=cols,
+                    block_masks=masks)
+
+
+def to_ragged(w: Workload, poison: bool = True) -> Workload:
+    """``w`` plus a ragged copy of its keys and values: each sequence's
+    kv_len tokens gathered from its pages into consecutive rows of
+    ``[tokens, Hkv, D]`` tensors (token-major), sequences back to back,
+    followed by page_size - 1 rows that belong to no sequence (NaN under
+    ``poison``, else zero). Data movement only."""
+    ps, Hkv, D = w.page_size, w.num_kv_heads, w.head_dim
+    lens = [int(x) for x in w.kv_len]
+    N = sum(lens) + ps - 1
+    fill = float("nan") if poison else 0.0
+    kr = torch.full((N, Hkv, D), fill, dtype=torch.bfloat16)
+    vr = torch.full((N, Hkv, D), fill, dtype=torch.bfloat16)
+    row = 0
+    for r, Lr in enumerate(lens):
+        a = int(w.kv_indptr[r])
+        for j in range(-(-Lr // ps)):
+            t0, t1 = j * ps, min(Lr, (j + 1) * ps)
+            page = int(w.kv_indices[a + j])
+            kr[row + t0: row + t1] = w.k_cache[page, :, : t1 - t0].transpose(0, 1)
+            vr[row + t0: row + t1] = w.v_cache[page, :, : t1 - t0].transpose(0, 1)
+        row += Lr
+    kw = {f.name: getattr(w, f.name) for f in fields(w)}
+    kw.update(k_ragged=kr, v_ragged=vr, ragged_indptr=_indptr(torch.tensor(lens)),
+              name=w.name + "_ragged")
+    return Workload(**kw)
 
 
 SPARSE_VIDEO_NAME = "sparse_video_attention"
