@@ -35,6 +35,12 @@ be compared with it element for element:
    every unit stays whole on worker = its enumeration index (splitting would
    save fewer steps than the merge it needs costs); the reported chunk size
    is then the longest unit's steps times gp.
+3b. Tiny decode batches (no more steps W than workers S, on the matrix
+   cores, merge mode left to the library, not graph-stable): the split units
+   are folded inside the attention kernel, so there is no merge launch to
+   amortise: c = max(1, ceil(W / S)) steps and no whole-unit exception, so a
+   unit's steps run on several waves side by side. (``fold_tiny=False``
+   gives the plans that do not take this rule.)
 4. Deterministic mode. A unit of n pages has k = ceil(n / c) chunks with
    c = det_chunk_pages, chunk j covering pages [floor(j*n/k),
    floor((j+1)*n/k)): boundaries depend on the request alone. Chunks are
@@ -126,8 +132,10 @@ def _lpt(items, num_workers):
 
 
 def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages,
-                 page_size):
-    """Per unit: list of (p0, p1, worker) page pieces in order; and c in pages."""
+                 page_size, tiny=False):
+    """Per unit: list of (p0, p1, worker) page pieces in order; and c in pages.
+    ``tiny`` (rule 3b): quotas of max(1, ceil(W / S)) steps and no whole-unit
+    exception."""
     pieces = []
     if deterministic:
         c = max(1, int(det_chunk_pages))
@@ -141,9 +149,10 @@ def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_p
     gp = max(1, 32 // page_size)
     steps = [_ceil_div(u["n_pages"], gp) for u in units]
     W = sum(steps)
-    c = max(1, _ceil_div(int(min_chunk_pages), gp), _ceil_div(W, num_workers))
+    c = max(1, _ceil_div(W, num_workers)) if tiny else \
+        max(1, _ceil_div(int(min_chunk_pages), gp), _ceil_div(W, num_workers))
     longest = max(steps, default=0)
-    if len(units) <= num_workers and longest - c < NO_SPLIT_STEPS:
+    if not tiny and len(units) <= num_workers and longest - c < NO_SPLIT_STEPS:
         # small batch: splitting would save fewer steps than a merge costs
         return [[(0, u["n_pages"], i)] if u["n_pages"] > 0 else []
                 for i, u in enumerate(units)], max(1, longest) * gp
@@ -166,7 +175,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
              num_workers, rows_per_block, deterministic=False, det_chunk_pages=48,
              min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
              prefix_len=None, req_group=None, prefix_parent=None, pod_blocks=None,
-             pod_wide_blocks=0, block_sparse=None, block_sparse_batch=None):
+             pod_wide_blocks=0, block_sparse=None, block_sparse_batch=None, fold_tiny=True):
     """Return the plan as plain lists.
 
     ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
@@ -345,8 +354,11 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
             levels.append(dict(items=[], worker_indptr=[0], chunk_pages=0))
             unit_chunks.append([(0, [])] * len(units))
             continue
+        gp = max(1, 32 // ps)
+        tiny = (fold_tiny and kind == "decode" and not deterministic
+                and sum(_ceil_div(u["n_pages"], gp) for u in units) <= S)
         pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev],
-                                 page_size)
+                                 page_size, tiny)
         items = []
         chunks_of = []
         for u, lst in zip(units, pieces):

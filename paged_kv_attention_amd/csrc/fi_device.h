@@ -333,6 +333,12 @@ template <int D>
 __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, int i_end,
                                                 int lane) {
   if (!a.item_rec) return;
+  // waves whose items all wrote final rows have nothing to announce (and
+  // skip the fence)
+  bool any = false;
+  for (int i0 = i_begin; i0 < i_end && !any; i0 += 64)
+    any = __ballot(i0 + lane < i_end && a.item_rec[i0 + lane] >= 0) != 0;
+  if (!any) return;
   // the partial rows written by this wave become visible at agent scope (to
   // a folding wave on another XCD) before any count that announces them
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");

@@ -169,8 +169,12 @@ constexpr int64_t kPodWideStep = 4;
 constexpr int64_t kPodDecodeStep = 9;
 constexpr int64_t kPodWideItemSteps = 2;
 
+// tiny: a decode level with fewer steps than workers whose split units are
+// folded in the kernel (no merge launch to amortise): chunks of
+// max(1, ceil(W / S)) steps and no whole-unit exception, so a short unit's
+// steps run on several idle waves side by side.
 void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all_partial,
-                 int32_t& next_row, LevelBuild& lb, Level& lv) {
+                 int32_t& next_row, LevelBuild& lb, Level& lv, bool tiny = false) {
   const int32_t ps = d.page_size;
   const int32_t S = lv.num_workers;
   // Per unit: its pieces (page range and, in balanced mode, the worker).
@@ -190,11 +194,12 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
     const int64_t gp = std::max(1, 32 / ps);
     int64_t W = 0;
     for (const Unit& u : units) W += ceil_div(u.n_pages, gp);
-    const int64_t cs = std::max<int64_t>({1, ceil_div(lv.min_chunk_pages, gp), ceil_div(W, S)});
+    const int64_t cs = tiny ? std::max<int64_t>(1, ceil_div(W, S))
+                            : std::max<int64_t>({1, ceil_div(lv.min_chunk_pages, gp), ceil_div(W, S)});
     c = cs * gp;
     int64_t longest = 0;
     for (const Unit& u : units) longest = std::max<int64_t>(longest, ceil_div(u.n_pages, gp));
-    const bool whole = (int64_t)units.size() <= S && longest - cs < kNoSplitSteps;
+    const bool whole = !tiny && (int64_t)units.size() <= S && longest - cs < kNoSplitSteps;
     if (whole) c = std::max<int64_t>(1, longest) * gp;
     int64_t g = 0;   // global step offset of the unit
     for (size_t ui = 0; whole && ui < units.size(); ++ui)
@@ -474,13 +479,22 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
 
 // FI_MERGE_FUSED decode plans on the matrix cores fold their split units at
 // the end of the attention kernel (its decode kernels count chunks in and the
-// last folds); every other plan launches the merge kernel after it. Separate
-// is the default: on MI355X the fused fold's agent-scope release and acquire
-// (an L2 write-back and invalidate of the XCD per wave) cost more than the
-// merge launch they save (Llama-like batch: 121 against 89 us per call).
+// last folds); so do default-mode ones with fewer 32-token steps than
+// workers (tiny batches: few waves, so the fences are cheap, and the plan
+// then spreads each unit's steps over idle waves), except graph-stable plans,
+// whose layout is fixed by the description. Every other plan launches the
+// merge kernel after the attention kernel: on MI355X the fused fold's
+// agent-scope release and acquire (an L2 write-back and invalidate of the
+// XCD per wave) cost more than the merge launch on full batches (Llama-like
+// batch: 121 against 89 us per call).
 static bool fused_merge(const fi_plan_desc& d) {
   return d.kind == FI_KIND_DECODE && d.decode_engine == FI_ENGINE_MFMA &&
          d.merge_mode == FI_MERGE_FUSED;
+}
+
+static bool fused_tiny(const fi_plan_desc& d, int64_t steps, int64_t workers) {
+  return d.kind == FI_KIND_DECODE && d.decode_engine == FI_ENGINE_MFMA &&
+         d.merge_mode == FI_MERGE_DEFAULT && d.cap_batch == 0 && steps <= workers;
 }
 
 static fi_status validate_table(const char* what, int32_t n, const int32_t* indptr,
@@ -651,7 +665,15 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
       if (append) wide_level(hp.level[0]); else decode_level(hp.level[0]);
       request_units(units[0], B, G, Hkv, ps, hp.level[0].rows_per_block, kv_indptr, kv_len,
                     append ? qo_indptr : nullptr, causal);
-      build_level(units[0], d, false, next_row, lb[0], hp.level[0]);
+      bool tiny = false;
+      if (!append) {
+        const int64_t gp = std::max(1, 32 / ps);
+        int64_t steps = 0;
+        for (const Unit& u : units[0]) steps += ceil_div(u.n_pages, gp);
+        tiny = fused_tiny(d, steps, hp.level[0].num_workers);
+        hp.fused = hp.fused || tiny;
+      }
+      build_level(units[0], d, false, next_row, lb[0], hp.level[0], tiny && !d.deterministic);
     }
     std::vector<int32_t> first_rec[2];
     for (int l = 0; l < hp.num_levels; ++l) first_rec[l] = unit_merges(units[l], lb[l], hp);

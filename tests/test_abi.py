@@ -773,3 +773,25 @@ def test_block_sparse_batch_errors():
     assert fi.load().fi_plan(ctypes.byref(d), ip.ctypes.data_as(L.I32P),
                              ln.ctypes.data_as(L.I32P), None, None, None, None, None, None, 0,
                              None, 0, None, ctypes.byref(h)) == L.FI_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_tiny_decode_plan_folds_in_kernel(det):
+    """A decode batch with fewer steps than workers: the default plan folds
+    its split units in the kernel and (balanced) spreads each unit's steps
+    over idle workers, equal to plan_ref rule 3b; merge="separate" keeps the
+    plain rule and the merge launch."""
+    ps = 16
+    lens = [37, 300, 120, 5, 0, 64]
+    indptr, L_ = _decode_host(lens, ps)
+    kw = dict(deterministic=det, det_chunk_pages=4, num_cus=256)
+    p = host_plan("decode", indptr, L_, 8, 2, 64, ps, **kw)
+    info = p.info()
+    assert info["fused_merge"]
+    ref = plan_ref("decode", 8, 2, ps, indptr, L_, **level_params(info), deterministic=det,
+                   det_chunk_pages=4)
+    compare(info, ref)
+    q = host_plan("decode", indptr, L_, 8, 2, 64, ps, merge="separate", **kw).info()
+    assert not q["fused_merge"]
+    compare(q, plan_ref("decode", 8, 2, ps, indptr, L_, **level_params(q), deterministic=det,
+                        det_chunk_pages=4, fold_tiny=False))

@@ -196,7 +196,7 @@ def test_small_batch_keeps_units_whole():
     ps, S = 16, 1024
     lens = [37, 300, 120, 5, 0]
     indptr, L = _decode_inputs(lens, ps)
-    p = plan_ref("decode", 8, 2, ps, indptr, L, S, [16])
+    p = plan_ref("decode", 8, 2, ps, indptr, L, S, [16], fold_tiny=False)
     lv = p["levels"][0]
     # only the empty request's zero-part records (they write o = 0, lse = -inf)
     assert all(m[5] == 0 for m in p["merges"]) and len(p["merges"]) == 2
@@ -210,7 +210,7 @@ def test_small_batch_keeps_units_whole():
     # one long request: a split saves many steps, so it still happens
     lens2 = [37, 300, 4096]
     indptr2, L2 = _decode_inputs(lens2, ps)
-    p2 = plan_ref("decode", 8, 2, ps, indptr2, L2, S, [16])
+    p2 = plan_ref("decode", 8, 2, ps, indptr2, L2, S, [16], fold_tiny=False)
     assert any(m[5] > 1 for m in p2["merges"])
 
 
@@ -401,3 +401,27 @@ def test_prefix_tree_parts_fold_root_first(det):
             continue
         qb = its[0][F["q_base"]]
         assert qlist[qb:qb + len(members)] == members
+
+
+def test_tiny_decode_spreads_steps_over_idle_workers():
+    """Rule 3b: a decode batch with no more 32-token steps than workers, its
+    split units folded in the kernel, runs one step per worker (W <= S):
+    every unit of n steps is n one-step chunks on n distinct workers, in
+    order, and every output row is still written exactly once."""
+    ps, S = 16, 1024
+    lens = [37, 300, 120, 5, 0, 64]
+    indptr, L = _decode_inputs(lens, ps)
+    p = plan_ref("decode", 8, 2, ps, indptr, L, S, [16])
+    check_partition(p, ps)
+    assert np.all(check_outputs_once(p, 4, 8, len(lens)) == 1)
+    lv = p["levels"][0]
+    per_worker = np.diff(lv["worker_indptr"])
+    assert per_worker.max() == 1                     # one step each
+    W = sum(2 * -(-x // 32) for x in lens)           # 2 kv heads
+    assert per_worker.sum() == W
+    for it in lv["items"]:
+        assert it[F["t_end"]] - it[F["t_begin"]] <= 32
+    # with more steps than workers the rule does not apply
+    assert (plan_ref("decode", 8, 2, ps, indptr, L, 8, [16], min_chunk_pages=8)
+            == plan_ref("decode", 8, 2, ps, indptr, L, 8, [16], min_chunk_pages=8,
+                        fold_tiny=False))
