@@ -139,6 +139,36 @@ def cold_us_per_call(step, dev, n=50):
     return round(min(both) - min(alone), 2)
 
 
+def graph_us_per_call(call, calls=10, replays=20):
+    """Median per-call time of HIP-graph replays of ``calls`` back-to-back
+    calls: the GPU's time per call without the host's launch cost."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(calls):
+            call()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    samples = []
+    for _ in range(replays):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        e1.synchronize()
+        samples.append(e0.elapsed_time(e1) * 1e3 / calls)
+    del graph
+    return round(_pct(samples, 0.5), 2)
+
+
 def measure_variants(args, w, g, plan, step, dev):
     """Context for the main number, measured after the timed region:
     HIP-graph replays, cold-cache calls, and the deterministic-mode plan."""
@@ -226,23 +256,24 @@ def explore(args, dev):
                        w.head_dim, w.page_size, device=dev, kv_format=args.kv, merge=args.merge,
                        **kw)
         if args.kv == "fp8":
-            call = lambda: fi.paged_decode_fp8(plan, g.q, g.k_fp8, g.v_fp8, g.k_scale,  # noqa
-                                               g.v_scale, g.kv_indices, w.sm_scale)
+            call = lambda o, l: fi.paged_decode_fp8(plan, g.q, g.k_fp8, g.v_fp8, g.k_scale,  # noqa
+                                                    g.v_scale, g.kv_indices, w.sm_scale,
+                                                    out=o, lse=l)
         elif args.kv == "mxfp4":
-            call = lambda: fi.paged_decode_mxfp4(plan, g.q, g.k_fp4, g.v_fp4,  # noqa
-                                                 g.k_bscale, g.v_bscale, g.kv_indices,
-                                                 w.sm_scale)
+            call = lambda o, l: fi.paged_decode_mxfp4(plan, g.q, g.k_fp4, g.v_fp4,  # noqa
+                                                      g.k_bscale, g.v_bscale, g.kv_indices,
+                                                      w.sm_scale, out=o, lse=l)
         else:
-            call = lambda: fi.paged_decode(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
-                                           w.sm_scale)
+            call = lambda o, l: fi.paged_decode(plan, g.q, g.k_cache, g.v_cache,  # noqa
+                                                g.kv_indices, w.sm_scale, out=o, lse=l)
         flops = 4 * w.head_dim * w.num_qo_heads * int(w.kv_len.sum())
     elif w.kind == "cascade":
         plan = fi.Plan("cascade", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, prefix_indptr=w.prefix_indptr,
                        prefix_len=w.prefix_len, req_prefix_group=w.req_prefix_group,
                        device=dev, launch=args.launch, pod_wide_blocks=args.pod_wide_blocks, **kw)
-        call = lambda: fi.cascade(plan, g.q, g.k_cache, g.v_cache, g.prefix_indices,  # noqa
-                                  g.kv_indices, w.sm_scale)
+        call = lambda o, l: fi.cascade(plan, g.q, g.k_cache, g.v_cache,  # noqa
+                                       g.prefix_indices, g.kv_indices, w.sm_scale, out=o, lse=l)
         per_req = w.kv_len.long() + w.prefix_len[0].long()
         flops = 4 * w.head_dim * w.num_qo_heads * int(per_req.sum())
     elif w.kind == "block_sparse":
@@ -251,8 +282,8 @@ def explore(args, dev):
                                   w.num_kv_heads, w.head_dim, w.page_size, device=dev,
                                   launch=args.launch, pod_wide_blocks=args.pod_wide_blocks,
                                   **{k: v for k, v in kw.items() if k != "engine"})
-        call = lambda: fi.block_sparse_attention(plan, g.q, g.k_cache, g.v_cache,  # noqa
-                                                 w.sm_scale)
+        call = lambda o, l: fi.block_sparse_attention(plan, g.q, g.k_cache,  # noqa
+                                                      g.v_cache, w.sm_scale, out=o, lse=l)
         # attended (query, key) pairs, every q head: 4 D flops each
         G = w.num_qo_heads // w.num_kv_heads
         pairs = (w.block_mask.double() * w.row_block_sz[:, :, None].double()
@@ -262,11 +293,19 @@ def explore(args, dev):
         plan = fi.Plan("append", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads,
                        w.head_dim, w.page_size, qo_indptr=w.qo_indptr, causal=True,
                        device=dev, launch=args.launch, pod_wide_blocks=args.pod_wide_blocks, **kw)
-        call = lambda: fi.paged_append(plan, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
-                                       w.sm_scale, k_new=g.k_new, v_new=g.v_new)
+        call = lambda o, l: fi.paged_append(plan, g.q, g.k_cache, g.v_cache,  # noqa
+                                            g.kv_indices, w.sm_scale, k_new=g.k_new,
+                                            v_new=g.v_new, out=o, lse=l)
         qo = (w.qo_indptr[1:] - w.qo_indptr[:-1]).long()
         pre = w.kv_len.long() - qo
         flops = 4 * w.head_dim * w.num_qo_heads * int((qo * pre + qo * (qo + 1) // 2).sum())
+    # outputs preallocated, as a serving loop holds them: the timed calls
+    # allocate nothing
+    T = g.q.shape[0]
+    out = torch.empty_like(g.q)
+    lse_buf = torch.empty(T, w.num_qo_heads, dtype=torch.float32, device=dev)
+    raw_call = call
+    call = lambda: raw_call(out, lse_buf)  # noqa: E731
     for _ in range(args.warmup):
         call()
     torch.cuda.synchronize()
@@ -277,6 +316,7 @@ def explore(args, dev):
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    graph_us = graph_us_per_call(call) if args.variants else None
     with fi.KernelTimer(args.steps) as kt:
         for _ in range(args.steps):
             call()
@@ -292,7 +332,7 @@ def explore(args, dev):
     print(json.dumps({"workload": name, "mode": args.mode,
                       "engine": args.engine, "kv": args.kv, **extra,
                       "us_per_call": round(ms * 1e3, 2), "attention_us": round(kern_ms * 1e3, 2),
-                      "cold_us_per_call": cold_us,
+                      "graph_us_per_call": graph_us, "cold_us_per_call": cold_us,
                       "kv_bytes": kv, "kv_GBps": round(kv / ms / 1e6, 1),
                       "pct_hbm_peak": round(100 * kv / ms / 1e6 / HBM_PEAK_GBS, 2),
                       "flops": flops, "TFLOPs": round(flops / ms / 1e9, 1),
