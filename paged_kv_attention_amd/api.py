@@ -81,7 +81,8 @@ class Plan:
     """A work plan for one batch (fi_plan). ``device=None`` builds it on the
     host only (needs ``num_cus``), which the run calls refuse. ``kv_format``
     ("bf16", "fp8" or "mxfp4") names the cache a decode plan will be run on:
-    it only picks the default ``workers_per_cu`` (12 for "mxfp4", else 4). ``merge``
+    it only picks the default ``workers_per_cu`` (8 for "fp8", 12 for "mxfp4",
+    else 4). ``merge``
     ("default", "fused" or "separate") says where a decode plan's split units
     are merged: by a merge launch after the attention kernel (the default and
     "separate") or inside the decode kernels ("fused", matrix-core engine;

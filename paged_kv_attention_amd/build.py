@@ -42,6 +42,7 @@ COMMON = [
 # the VALU), which that ALU-bound kernel cannot afford.
 EXTRA = {
     "fi_decode_fp4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "fi_decode_fp8.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

@@ -14,16 +14,27 @@
 // a token's page into its logit's scale, the V scale into its p (the row sum
 // l uses the unscaled p); p * v_scale enters P.V as two bf16 parts.
 //
-// Lanes. K: the contraction order over the head dim is free, so lane group g
-// takes dims [g*D/4, (g+1)*D/4) of its token, D/4 contiguous bytes (two 16-byte
-// loads at D = 128), and MFMA j of q.K uses bytes 8j..8j+7 of that run; q is
-// loaded in the same dim order. V: lane col takes dims D/16*col .. +D/16 of
-// the lane group's 8 tokens (the S^T token order), widened to bf16 and
-// transposed in registers as in the bf16 kernel.
+// Staging. Each wave streams its steps through its own ring of LDS stages
+// (no sharing, no barriers between waves) with direct global->LDS copies: per
+// step the K codes (four 1-KiB copies at D = 128, two at 64), the V codes
+// (the same) and one copy of the step's page scales, each lane fetching 16
+// (scales: 4) bytes at an address of its own. The wait for a step is an
+// explicit vmcnt count of the copies issued after it. (Staged in registers
+// instead, the widening needs the codes in VGPRs while the ring overflows
+// into AGPRs, and the compiler's copies between the two files wait for loads
+// issued one step earlier: the ring drains every step.) K rows keep their
+// 16-byte chunks XOR-swizzled by the token and V rows are placed rotated
+// within groups of four tokens, so that the operand reads (16 lanes on one
+// chunk of 16 tokens; 4 lane groups on 4 different tokens) spread over the
+// banks. The page ids of a step are loaded one issue ahead, so that their
+// scalar round trip is not in front of the step's copies.
 //
-// Pages, clamping, the item stream and the prefetch ring follow the bf16
-// decode kernel; with half the bytes per step the ring is six tiles deep so
-// the bytes in flight per wave stay about the same.
+// Lanes. K: the contraction order over the head dim is free, so lane group g
+// takes dims [g*D/4, (g+1)*D/4) of its token, D/4 contiguous bytes (two
+// 16-byte chunks at D = 128), and MFMA j of q.K uses bytes 8j..8j+7 of that
+// run; q is loaded in the same dim order. V: lane col takes dims
+// D/16*col .. +D/16 of the lane group's 8 tokens (the S^T token order),
+// widened to bf16 and transposed in registers as in the bf16 kernel.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -35,7 +46,8 @@ namespace {
 
 using namespace dev;
 
-constexpr int kRing8 = 6;
+typedef __attribute__((address_space(3))) void* lds_vptr;
+typedef const __attribute__((address_space(1))) void* global_vptr;
 
 template <int W> struct Words;
 template <> struct Words<2> { typedef u32x2 T; };
@@ -44,18 +56,40 @@ template <> struct Words<1> { typedef uint32_t T; };
 template <int D>
 struct C8 {
   static constexpr int KJ = D / 32;          // q.K MFMAs per 16-token block
-  static constexpr int KV4 = D / 64;         // 16-byte K loads per lane and token
+  static constexpr int KV4 = D / 64;         // 16-byte K chunks per lane and token
   static constexpr int DPL = D / 16;         // V dims per lane = P.V MFMAs
-  typedef typename Words<DPL / 4>::T vraw_t; // DPL codes of one V row
+  static constexpr int ROW = D;              // bytes per K (or V) row
+  static constexpr int NCH = D / 16;         // 16-byte chunks per row
+  static constexpr int RPW = 256 / D;        // rows per 256-byte span of the banks
+  static constexpr int TPC = 1024 / D;       // rows per 1-KiB copy
+  static constexpr int NKC = 32 / TPC;       // copies per step of K (or V) codes
+  static constexpr int NCOPY = 2 * NKC + 1;  // copies per step in all
+  static constexpr int AREA = 32 * ROW;      // K (or V) codes of a step
+  static constexpr int SCALES = 2 * AREA;    // the step's scales: K of its pages, then V
+  static constexpr int STAGE = 2 * AREA + 256;
+  typedef typename Words<DPL / 4>::T vraw_t;
 };
 
+// One step's operands as read from its stage.
 template <int D>
-struct Tile8 {
+struct Frag8 {
   u32x4 k[2][C8<D>::KV4];
   typename C8<D>::vraw_t v[8];
   float ks[2], vs[2];     // scales of this lane's two token halves
-  u32x4 q[C8<D>::KJ];     // the item's q, on its first step only
 };
+
+// K: chunk c of token t sits at chunk slot c ^ k_swz(t) of row t; the 16
+// tokens read together then cover the 256-byte bank span once.
+template <int D>
+__device__ __forceinline__ int k_swz(int t) {
+  return (t / C8<D>::RPW) % C8<D>::NCH;
+}
+
+// V: row of token t (0..31), rotated within its group of four so that the
+// tokens 4g + i (g = 0..3) of one operand read fall in different parts of the
+// bank span; and its inverse.
+__device__ __forceinline__ int v_row_of(int t) { return (t & ~3) | ((t + (t >> 2)) & 3); }
+__device__ __forceinline__ int v_token_of(int r) { return (r & ~3) | (((r & 3) - (r >> 2)) & 3); }
 
 // Two E4M3 codes (the low or high 16 bits of w) -> two bf16 in one dword. The
 // result is only ever used as a whole dword.
@@ -64,84 +98,124 @@ __device__ __forceinline__ uint32_t widen2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-__device__ __forceinline__ float ld_uniform_f(const float* p, int64_t i) {
-  return __builtin_bit_cast(float, ld_uniform((const int32_t*)p, i));
+// s_waitcnt vmcnt(n) with no wait on the other counters (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// This lane's part of every copy of a step, fixed for the kernel: the page of
+// the step (0..NP-1) its bytes come from and their offset in that page's tile.
 template <int D, int NP>
-__device__ __forceinline__ void issue_step8(const AttnArgs& a, const Item& it, int s,
-                                            Tile8<D>& T, int col, int grp) {
-  constexpr int KV4 = C8<D>::KV4, DPL = C8<D>::DPL;
-  typedef typename C8<D>::vraw_t vraw_t;
-  const int sh = a.page_shift;
-  const int T0 = it.t_begin + 32 * s;
-  const int pb = T0 >> sh;
-  const int plast = (it.t_end - 1) >> sh;
-  const int64_t tile_bytes = (int64_t)a.page_size * D;
-  const char* kb[NP];
-  const char* vb[NP];
-  float ks[NP], vs[NP];
+struct Lanes8 {
+  static constexpr int NKC = C8<D>::NKC, NCH = C8<D>::NCH, ROW = C8<D>::ROW;
+  static constexpr int TPP = 32 / NP;          // tokens of the step per page
+  int kn[NKC], vn[NKC], sn;
+  uint32_t koff[NKC], voff[NKC];
+  bool s_is_v;
+  __device__ __forceinline__ Lanes8(int lane) {
 #pragma unroll
-  for (int n = 0; n < NP; ++n) {
-    const int pid = ld_uniform(it.plist, min(pb + n, plast));
-    const int64_t ph = (int64_t)pid * a.num_kv_heads + it.g;
-    kb[n] = (const char*)a.k_cache + ph * tile_bytes;
-    vb[n] = (const char*)a.v_cache + ph * tile_bytes;
-    ks[n] = ld_uniform_f(a.k_scale, ph);
-    vs[n] = ld_uniform_f(a.v_scale, ph);
-  }
-  // pages of this lane's tokens 4g..4g+3 and 16+4g..16+4g+3
-  if constexpr (NP == 1) {
-    T.ks[0] = T.ks[1] = ks[0];
-    T.vs[0] = T.vs[1] = vs[0];
-  } else if constexpr (NP == 2) {
-    T.ks[0] = ks[0];
-    T.ks[1] = ks[1];
-    T.vs[0] = vs[0];
-    T.vs[1] = vs[1];
-  } else {
-    T.ks[0] = (grp >> 1) ? ks[1] : ks[0];
-    T.ks[1] = (grp >> 1) ? ks[NP - 1] : ks[NP - 2];
-    T.vs[0] = (grp >> 1) ? vs[1] : vs[0];
-    T.vs[1] = (grp >> 1) ? vs[NP - 1] : vs[NP - 2];
-  }
-  const int slot0 = (NP == 1) ? (T0 & (a.page_size - 1)) : 0;
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {   // K: token 16*blk + col, bytes [grp*D/4, +D/4)
-    const char* base;
-    int slot;
-    if (NP == 1) {
-      base = kb[0];
-      slot = slot0 + 16 * blk + col;
-    } else if (NP == 2) {
-      base = kb[blk];
-      slot = col;
-    } else {
-      base = (col >> 3) ? kb[2 * blk + 1] : kb[2 * blk];
-      slot = col & 7;
+    for (int c = 0; c < NKC; ++c) {
+      const int p = c * 64 + lane;               // 16-byte slot of the area
+      const int r = p / NCH, cs = p % NCH;       // LDS row and chunk slot
+      const int tk = r, chk = cs ^ k_swz<D>(tk); // K: row = token, chunks swizzled
+      const int tv = v_token_of(r);              // V: rotated rows, chunks in order
+      kn[c] = tk / TPP;
+      vn[c] = tv / TPP;
+      koff[c] = (uint32_t)((tk % TPP) * ROW + chk * 16);
+      voff[c] = (uint32_t)((tv % TPP) * ROW + cs * 16);
     }
-    const uint32_t off = (uint32_t)(slot * D + grp * (D / 4));
+    // scales: lanes 0..NP-1 the K scale of page lane, NP..2NP-1 the V scale
+    // of page lane - NP, the rest repeat lane 0's
+    s_is_v = lane >= NP && lane < 2 * NP;
+    sn = lane < 2 * NP ? lane % NP : 0;
+  }
+};
+
+// Row sel (0..NP-1) of r0..r3, selected per lane; written as selects so that
+// no indexed array (which the compiler may move to scratch) is formed.
+template <int NP>
+__device__ __forceinline__ int64_t pick(int64_t r0, int64_t r1, int64_t r2, int64_t r3, int n) {
+  if (NP == 1) return r0;
+  if (NP == 2) return (n & 1) ? r1 : r0;
+  const int64_t lo = (n & 1) ? r1 : r0, hi = (n & 1) ? r3 : r2;
+  return (n & 2) ? hi : lo;
+}
+
+// Page ids of step s of item it (clamped to the item's last page).
+template <int NP>
+__device__ __forceinline__ void load_pids(const AttnArgs& a, const Item& it, int s,
+                                          int (&pid)[NP]) {
+  const int sh = a.page_shift;
+  const int pb = (it.t_begin + 32 * s) >> sh;
+  const int plast = (it.t_end - 1) >> sh;
 #pragma unroll
-    for (int i = 0; i < KV4; ++i)   // K and V are read once: nontemporal loads
-      T.k[blk][i] = __builtin_nontemporal_load((const u32x4*)(base + off + 16u * i));
+  for (int n = 0; n < NP; ++n) pid[n] = ld_uniform(it.plist, min(pb + n, plast));
+}
+
+// Copy step s of item it (page ids pid) into LDS stage `st`. valid = false
+// (past the end of the stream): the same number of copies, every lane at the
+// step's first bytes (in bounds, next to no HBM traffic), into a stage never
+// read again.
+template <int D, int NP>
+__device__ __forceinline__ void issue_copies8(const AttnArgs& a, const Item& it, int s,
+                                              const int (&pid)[NP], char* st,
+                                              const Lanes8<D, NP>& ln, bool valid) {
+  constexpr int NKC = C8<D>::NKC, ROW = C8<D>::ROW, AREA = C8<D>::AREA;
+  const int T0 = it.t_begin + 32 * s;
+  // (page, kv head) tile of each page of the step, and its first token row
+  auto tile = [&](int n) -> int64_t {
+    return n < NP ? (int64_t)pid[n] * a.num_kv_heads + it.g : 0;
+  };
+  const int64_t h0 = tile(0), h1 = tile(1), h2 = tile(2), h3 = tile(3);
+  int64_t r0 = h0 * a.page_size;
+  const int64_t r1 = h1 * a.page_size, r2 = h2 * a.page_size, r3 = h3 * a.page_size;
+  if (NP == 1) r0 += T0 & (a.page_size - 1);
+  const char* kc = (const char*)a.k_cache;
+  const char* vc = (const char*)a.v_cache;
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) {
+    const char* kp = kc + pick<NP>(r0, r1, r2, r3, valid ? ln.kn[c] : 0) * ROW +
+                     (valid ? ln.koff[c] : 0u);
+    __builtin_amdgcn_global_load_lds((global_vptr)kp, (lds_vptr)(st + c * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) {
+    const char* vp = vc + pick<NP>(r0, r1, r2, r3, valid ? ln.vn[c] : 0) * ROW +
+                     (valid ? ln.voff[c] : 0u);
+    __builtin_amdgcn_global_load_lds((global_vptr)vp, (lds_vptr)(st + AREA + c * 1024), 16, 0, 0);
+  }
+  const float* sbase = ln.s_is_v ? a.v_scale : a.k_scale;
+  const float* sp = sbase + pick<NP>(h0, h1, h2, h3, valid ? ln.sn : 0);
+  __builtin_amdgcn_global_load_lds((global_vptr)sp, (lds_vptr)(st + C8<D>::SCALES), 4, 0, 0);
+}
+
+// The operands of this lane from stage st.
+template <int D, int NP>
+__device__ __forceinline__ void read_frags(const char* st, Frag8<D>& T, int col, int grp) {
+  constexpr int KV4 = C8<D>::KV4, ROW = C8<D>::ROW, DPL = C8<D>::DPL, AREA = C8<D>::AREA;
+  typedef typename C8<D>::vraw_t vraw_t;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {   // K: token 16*blk + col, chunks KV4*grp ..
+    const int t = 16 * blk + col;
+#pragma unroll
+    for (int h = 0; h < KV4; ++h)
+      T.k[blk][h] = *(const u32x4*)(st + t * ROW + 16 * ((KV4 * grp + h) ^ k_swz<D>(t)));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {   // V: tokens 4*grp + i and 16 + 4*grp + (i - 4)
     const int tl = (i < 4) ? 4 * grp + i : 16 + 4 * grp + (i - 4);
-    const char* base;
-    int slot;
-    if (NP == 1) {
-      base = vb[0];
-      slot = slot0 + tl;
-    } else if (NP == 2) {
-      base = vb[i >> 2];
-      slot = tl & 15;
-    } else {
-      base = (grp >> 1) ? vb[2 * (i >> 2) + 1] : vb[2 * (i >> 2)];
-      slot = tl & 7;
-    }
-    T.v[i] = __builtin_nontemporal_load((const vraw_t*)(base + (uint32_t)(slot * D + DPL * col)));
+    T.v[i] = *(const vraw_t*)(st + AREA + v_row_of(tl) * ROW + DPL * col);
   }
+  // pages of this lane's tokens 4g..4g+3 and 16+4g..16+4g+3
+  constexpr int TPP = 32 / NP;
+  const int n0 = (4 * grp) / TPP, n1 = (16 + 4 * grp) / TPP;
+  const float* sc = (const float*)(st + C8<D>::SCALES);
+  T.ks[0] = sc[n0];
+  T.ks[1] = sc[n1];
+  T.vs[0] = sc[NP + n0];
+  T.vs[1] = sc[NP + n1];
 }
 
 template <int D>
@@ -160,7 +234,7 @@ __device__ __forceinline__ void load_q8(const AttnArgs& a, const Item& it, u32x4
 
 template <int D>
 __device__ __forceinline__ void compute_step8(const AttnArgs& a, const Item& it, int s,
-                                              const Tile8<D>& T, const u32x4 (&qf)[C8<D>::KJ],
+                                              const Frag8<D>& T, const u32x4 (&qf)[C8<D>::KJ],
                                               State<D, 1>& st, int grp) {
   constexpr int KJ = C8<D>::KJ, DPL = C8<D>::DPL;
   typedef typename Cfg<D>::vrow_t vrow_t;
@@ -268,51 +342,72 @@ __device__ __forceinline__ void compute_step8(const AttnArgs& a, const Item& it,
   }
 }
 
-template <int D, int NP>
+// R: LDS stages per wave. 4 at D = 128 (8.25 KiB a stage, 132 KiB per
+// workgroup) and 8 at D = 64 with one wave per SIMD; half that when the plan
+// gives eight or more workers per CU (two workgroups per CU).
+template <int D, int NP, int R>
 __global__ __launch_bounds__(256) void decode_fp8_kernel(AttnArgs a) {
-  constexpr int KJ = C8<D>::KJ;
+  constexpr int KJ = C8<D>::KJ, STAGE = C8<D>::STAGE, NCOPY = C8<D>::NCOPY;
+  __shared__ __attribute__((aligned(1024))) char lds[WAVES_PER_BLOCK * R * STAGE];
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  const int w = blockIdx.x * WAVES_PER_BLOCK + uniform(threadIdx.x >> 6);
+  const int wave = uniform(threadIdx.x >> 6);
+  const int w = blockIdx.x * WAVES_PER_BLOCK + wave;
   if (w >= a.num_workers) return;
   fused_merge_start<D>(a, w, lane);
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
   const int i_begin = ld_uniform(a.worker_indptr, w);
   if (i_begin >= i_end) return;
+  char* ring = lds + wave * (R * STAGE);
+  const Lanes8<D, NP> ln(lane);
 
-  // Issue cursor (ii, is) kRing8-1 steps ahead of the compute cursor (ci, cs)
-  // across item boundaries; tiles are filled and consumed in the same order.
+  // Issue cursor (ii, is) R-1 steps ahead of the compute cursor (ci, cs)
+  // across item boundaries; stages are filled and consumed in the same order.
+  // npid: the page ids of the issue cursor's step, loaded one issue ahead.
   int ci = i_begin, cs = 0;
   Item citem = load_item(a, ci);
   int ii = i_begin, is = 0;
   Item iitem = citem;
-  Tile8<D> TA, TB, TC, TD, TE, TF;   // the ring, named so it stays in registers
+  int npid[NP];
+  load_pids<NP>(a, iitem, 0, npid);
   u32x4 q_cur[KJ];
   State<D, 1> st;
   st.reset();
 
-  auto issue = [&](Tile8<D>& Y) {
+  auto issue = [&](int y) {
     const bool valid = ii < i_end;
-    if (valid && is == 0) load_q8<D>(a, iitem, Y.q, col, grp);
-    // past the end of the stream: an in-bounds re-load of the current step,
-    // every lane at lane 0's addresses (next to no HBM traffic)
-    issue_step8<D, NP>(a, valid ? iitem : citem, valid ? is : cs, Y, valid ? col : 0,
-                       valid ? grp : 0);
-    if (valid && ++is >= iitem.nsteps) {
-      ++ii;
-      is = 0;
-      if (ii < i_end) iitem = load_item(a, ii);
+    // past the end: iitem and npid still hold the stream's last step
+    issue_copies8<D, NP>(a, iitem, valid ? is : iitem.nsteps - 1, npid, ring + y * STAGE, ln,
+                         valid);
+    if (valid) {
+      if (++is >= iitem.nsteps) {
+        ++ii;
+        is = 0;
+        if (ii < i_end) iitem = load_item(a, ii);
+      }
+      if (ii < i_end) load_pids<NP>(a, iitem, is, npid);
     }
   };
 
-  // Refill Y (the tile computed last), then compute X.
-  auto advance = [&](Tile8<D>& X, Tile8<D>& Y) -> bool {
-    issue(Y);
+  // Refill stage y (computed in the previous call), then compute stage x
+  // once its copies have landed: R-1 steps' copies were issued after them
+  // (maybe also the stores of finished items, which only make the wait
+  // stricter). An item's q is loaded when its first step is computed, its
+  // wait taken on that path only (at the use after the paths join it would
+  // drain the ring on every step).
+  static_assert((R - 1) * NCOPY < 64, "vmcnt range");
+  auto advance = [&](int x, int y) -> bool {
+    asm volatile("" ::: "memory");   // stage y's reads stay before its refill
+    issue(y);
     if (cs == 0) {
+      load_q8<D>(a, citem, q_cur, col, grp);
 #pragma unroll
-      for (int j = 0; j < KJ; ++j) q_cur[j] = X.q[j];
+      for (int j = 0; j < KJ; ++j) asm volatile("" : "+v"(q_cur[j]));
     }
-    compute_step8<D>(a, citem, cs, X, q_cur, st, grp);
+    wait_vmcnt<(R - 1) * NCOPY>();
+    Frag8<D> F;
+    read_frags<D, NP>(ring + x * STAGE, F, col, grp);
+    compute_step8<D>(a, citem, cs, F, q_cur, st, grp);
     if (cs + 1 >= citem.nsteps) {
       finalize_rows<D, 1, false>(a, citem, st, 0, col, grp);
       st.reset();
@@ -325,26 +420,33 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(AttnArgs a) {
     return true;
   };
 
-  static_assert(kRing8 == 6, "the loop below is unrolled for a ring of six tiles");
-  issue(TA);
-  issue(TB);
-  issue(TC);
-  issue(TD);
-  issue(TE);
-  while (advance(TA, TF) && advance(TB, TA) && advance(TC, TB) && advance(TD, TC) &&
-         advance(TE, TD) && advance(TF, TE)) {
+  for (int k = 0; k < R - 1; ++k) issue(k);
+  // unrolled so that every stage offset is a constant
+  if constexpr (R == 8) {
+    while (advance(0, 7) && advance(1, 0) && advance(2, 1) && advance(3, 2) && advance(4, 3) &&
+           advance(5, 4) && advance(6, 5) && advance(7, 6)) {
+    }
+  } else if constexpr (R == 4) {
+    while (advance(0, 3) && advance(1, 0) && advance(2, 1) && advance(3, 2)) {
+    }
+  } else {
+    static_assert(R == 2, "rings of two, four or eight stages");
+    while (advance(0, 1) && advance(1, 0)) {
+    }
   }
+  // drain this wave's copies before it exits (the stages are its own)
+  wait_vmcnt<0>();
   fused_merge_end<D>(a, i_begin, i_end, lane);
 }
 
-template <int D>
+template <int D, int R>
 hipError_t launch_f8(const AttnArgs& a, dim3 grid, hipStream_t s) {
   if (a.page_size == 8) {
-    launch_timed((decode_fp8_kernel<D, 4>), grid, dim3(256), s, a);
+    launch_timed((decode_fp8_kernel<D, 4, R>), grid, dim3(256), s, a);
   } else if (a.page_size == 16) {
-    launch_timed((decode_fp8_kernel<D, 2>), grid, dim3(256), s, a);
+    launch_timed((decode_fp8_kernel<D, 2, R>), grid, dim3(256), s, a);
   } else {
-    launch_timed((decode_fp8_kernel<D, 1>), grid, dim3(256), s, a);
+    launch_timed((decode_fp8_kernel<D, 1, R>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }
@@ -354,8 +456,18 @@ hipError_t launch_f8(const AttnArgs& a, dim3 grid, hipStream_t s) {
 hipError_t launch_decode_fp8(const AttnArgs& a, int head_dim, hipStream_t stream) {
   const int blocks = (a.num_workers + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   if (blocks == 0) return hipSuccess;
-  if (head_dim == 128) return launch_f8<128>(a, dim3(blocks), stream);
-  if (head_dim == 64) return launch_f8<64>(a, dim3(blocks), stream);
+  // workers per CU of the plan, against this device's CU count
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int per_cu = cus > 0 ? a.num_workers / cus : 0;
+  if (head_dim == 128)
+    return per_cu >= 8 ? launch_f8<128, 2>(a, dim3(blocks), stream)
+                       : launch_f8<128, 4>(a, dim3(blocks), stream);
+  if (head_dim == 64)
+    return per_cu >= 8 ? launch_f8<64, 4>(a, dim3(blocks), stream)
+                       : launch_f8<64, 8>(a, dim3(blocks), stream);
   return hipErrorInvalidValue;
 }
 

@@ -467,9 +467,11 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
   if (d.merge_mode < FI_MERGE_DEFAULT || d.merge_mode > FI_MERGE_SEPARATE)
     return set_error(FI_ERR_INVALID_ARG, "merge_mode %d", d.merge_mode);
   if (d.kind != FI_KIND_DECODE) d.kv_format = FI_KV_BF16;
-  // one wave per SIMD for the register-ring decode kernels; three for the
-  // MXFP4 kernel, which staging through LDS leaves ALU- and latency-bound
-  if (d.workers_per_cu == 0) d.workers_per_cu = d.kv_format == FI_KV_MXFP4 ? 12 : 4;
+  // one wave per SIMD for the register-ring decode kernel; two and three
+  // for the FP8 and MXFP4 kernels, which staging through LDS leaves ALU- and
+  // latency-bound
+  if (d.workers_per_cu == 0)
+    d.workers_per_cu = d.kv_format == FI_KV_MXFP4 ? 12 : d.kv_format == FI_KV_FP8 ? 8 : 4;
   d.causal = d.causal ? 1 : 0;
   d.deterministic = d.deterministic ? 1 : 0;
   if (d.kind != FI_KIND_APPEND) d.causal = 0;   // (block-sparse: refused above if set)

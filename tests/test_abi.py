@@ -196,11 +196,11 @@ def test_page_table_check_refuses_bad_plans_before_any_launch():
 
 
 def test_kv_format_picks_the_default_worker_count():
-    """A decode plan for an MXFP4 cache defaults to 12 workers per CU, bf16
-    and FP8 plans to 4; an explicit count wins; other plan kinds ignore the
+    """A decode plan for an MXFP4 cache defaults to 12 workers per CU, FP8 to
+    8 and bf16 to 4; an explicit count wins; other plan kinds ignore the
     field; an unknown format is refused."""
     d_indptr, d_len = _decode_host([100, 2000, 37], 16)
-    for fmt, wpc in (("bf16", 4), ("fp8", 4), ("mxfp4", 12)):
+    for fmt, wpc in (("bf16", 4), ("fp8", 8), ("mxfp4", 12)):
         p = host_plan("decode", d_indptr, d_len, 32, 8, 128, 16, num_cus=5, kv_format=fmt)
         assert p.info()["levels"][0]["num_workers"] == 5 * wpc
     p = host_plan("decode", d_indptr, d_len, 32, 8, 128, 16, num_cus=5, kv_format="mxfp4",

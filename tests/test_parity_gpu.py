@@ -800,9 +800,12 @@ def test_fp8_llama_decode_sampled(dev):
     rng = np.random.default_rng(21)
     reqs = sample_requests(w.batch, 8, rng, must=[int(torch.argmax(w.kv_len))])
     o_ref, l_ref, a_ref = _fp8_oracle(w, reqs)
-    for det in (False, True):
-        o, lse = _fp8_run(w, dev, deterministic=det)
-        compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"fp8 llama det={det}")
+    # an FP8 plan (two waves per SIMD, two LDS stages per wave) and a bf16
+    # one (one wave, four stages)
+    for kw in (dict(), dict(kv_format="fp8"), dict(deterministic=True),
+               dict(deterministic=True, kv_format="fp8")):
+        o, lse = _fp8_run(w, dev, **kw)
+        compare(o, lse, o_ref, l_ref, a_ref, rows=request_rows(reqs), what=f"fp8 llama {kw}")
 
 
 @pytest.mark.parametrize("D", [64, 128])
@@ -813,7 +816,8 @@ def test_fp8_decode_small_sweep(dev, D, ps, G):
     w = to_fp8_cache(make_decode(SMALL_LENS, G * Hkv, Hkv, D, ps, seed=500 + D + ps + G,
                                  poison=False), poison=True)
     o_ref, l_ref, a_ref = _fp8_oracle(w)
-    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1)]:
+    for kw in [dict(), dict(deterministic=True, det_chunk_pages=1), dict(min_chunk_pages=1),
+               dict(kv_format="fp8", min_chunk_pages=1)]:
         o, lse = _fp8_run(w, dev, **kw)
         compare(o, lse, o_ref, l_ref, a_ref, what=f"fp8 decode D={D} ps={ps} G={G} {kw}")
 
