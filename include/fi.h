@@ -213,6 +213,9 @@ typedef struct fi_plan_info {
                                     (-1 for an item writing final rows)        */
   int32_t num_empty_recs;        /* fused: records of units with no keys, which */
   const int32_t* empty_recs;     /* the kernel's workers write at start        */
+  int32_t wg_fold;               /* fused tiny batch: unit u on the four waves of
+                                    workgroup u (workers 4u..4u+3), folded
+                                    after a workgroup barrier                   */
 } fi_plan_info;
 
 /* Upper bound on the device and pinned-host workspace bytes of any plan with

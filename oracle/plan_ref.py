@@ -41,6 +41,12 @@ be compared with it element for element:
    amortise: c = max(1, ceil(W / S)) steps and no whole-unit exception, so a
    unit's steps run on several waves side by side. (``fold_tiny=False``
    gives the plans that do not take this rule.)
+3c. Tiny batches with at most S/4 units (S a multiple of 4): unit u runs on
+   the four waves of workgroup u, workers 4u..4u+3, so that the kernel folds
+   it after a workgroup barrier: with ns = ceil(n / gp) steps and
+   k = ceil(ns / 4), chunk j covers steps [j k, min(ns, (j+1) k)) (empty
+   ones dropped) on worker 4u + j; the reported chunk size is
+   max(1, ceil(longest / 4)) * gp pages.
 4. Deterministic mode. A unit of n pages has k = ceil(n / c) chunks with
    c = det_chunk_pages, chunk j covering pages [floor(j*n/k),
    floor((j+1)*n/k)): boundaries depend on the request alone. Chunks are
@@ -132,10 +138,10 @@ def _lpt(items, num_workers):
 
 
 def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages,
-                 page_size, tiny=False):
+                 page_size, tiny=False, wg=False):
     """Per unit: list of (p0, p1, worker) page pieces in order; and c in pages.
     ``tiny`` (rule 3b): quotas of max(1, ceil(W / S)) steps and no whole-unit
-    exception."""
+    exception; ``wg`` (rule 3c): unit u on workers 4u..4u+3."""
     pieces = []
     if deterministic:
         c = max(1, int(det_chunk_pages))
@@ -152,6 +158,13 @@ def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_p
     c = max(1, _ceil_div(W, num_workers)) if tiny else \
         max(1, _ceil_div(int(min_chunk_pages), gp), _ceil_div(W, num_workers))
     longest = max(steps, default=0)
+    if wg:
+        out = []
+        for ui, (u, ns) in enumerate(zip(units, steps)):
+            n, k = u["n_pages"], _ceil_div(ns, 4)
+            out.append([(j * k * gp, min(n, min(ns, (j + 1) * k) * gp), 4 * ui + j)
+                        for j in range(4) if j * k < min(ns, (j + 1) * k)])
+        return out, max(1, _ceil_div(longest, 4)) * gp
     if not tiny and len(units) <= num_workers and longest - c < NO_SPLIT_STEPS:
         # small batch: splitting would save fewer steps than a merge costs
         return [[(0, u["n_pages"], i)] if u["n_pages"] > 0 else []
@@ -357,8 +370,9 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
         gp = max(1, 32 // ps)
         tiny = (fold_tiny and kind == "decode" and not deterministic
                 and sum(_ceil_div(u["n_pages"], gp) for u in units) <= S)
+        wg = tiny and S % 4 == 0 and 4 * len(units) <= S
         pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev],
-                                 page_size, tiny)
+                                 page_size, tiny, wg)
         items = []
         chunks_of = []
         for u, lst in zip(units, pieces):

@@ -49,7 +49,7 @@ class PlanInfo(ctypes.Structure):
         ("num_scatter", c_int32), ("dev_bytes_used", c_size_t), ("host_bytes_used", c_size_t),
         ("pod_wide_blocks", c_int32), ("num_plist", c_int32), ("plist", I32P),
         ("fused_merge", c_int32), ("item_rec", I32P), ("num_empty_recs", c_int32),
-        ("empty_recs", I32P),
+        ("empty_recs", I32P), ("wg_fold", c_int32),
     ]
 
 

@@ -191,7 +191,8 @@ class Plan:
                     pod_wide_blocks=inf.pod_wide_blocks, plist=arr(inf.plist, inf.num_plist),
                     fused_merge=bool(inf.fused_merge),
                     item_rec=arr(inf.item_rec, inf.num_items[0] if inf.fused_merge else 0),
-                    empty_recs=arr(inf.empty_recs, inf.num_empty_recs))
+                    empty_recs=arr(inf.empty_recs, inf.num_empty_recs),
+                    wg_fold=bool(inf.wg_fold))
 
 
 class BlockSparsePlan(Plan):

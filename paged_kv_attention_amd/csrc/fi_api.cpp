@@ -120,6 +120,7 @@ AttnArgs plan_attn_args(const fi_plan_t* p, const char* base, int level, const v
   a.parts = at(p->lay.parts);
   a.empty_recs = at(p->lay.empty_recs);
   a.meta = at(p->lay.meta);
+  a.wg_fold = (fused && p->hp.wg_fold) ? 1 : 0;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.num_qo_heads = d.num_qo_heads;
   a.num_kv_heads = d.num_kv_heads;

@@ -146,7 +146,10 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
   fused_merge_start<D>(a, w, lane);
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
   const int i_begin = ld_uniform(a.worker_indptr, w);
-  if (i_begin >= i_end) return;
+  if (i_begin >= i_end) {   // (a workgroup-folded plan's barrier needs every wave)
+    fused_merge_end<D>(a, i_begin, i_end, lane);
+    return;
+  }
 
   // Two cursors over the worker's stream of steps: the issue cursor (ii, is)
   // runs RING-1 steps ahead of the compute cursor (ci, cs), across item

@@ -293,7 +293,10 @@ __global__ __launch_bounds__(256) void decode_mxfp4_kernel(AttnArgs a) {
   fused_merge_start<D>(a, w, lane);
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
   const int i_begin = ld_uniform(a.worker_indptr, w);
-  if (i_begin >= i_end) return;
+  if (i_begin >= i_end) {   // (a workgroup-folded plan's barrier needs every wave)
+    fused_merge_end<D>(a, i_begin, i_end, lane);
+    return;
+  }
   char* ring = lds + wave * (kRing4 * STAGE);
   const Lanes4<D, NP> ln(lane);
 

@@ -329,10 +329,27 @@ __device__ __forceinline__ void fused_merge_start(const AttnArgs& a, int w, int 
 // every load and store of the wave, drains no prefetch): count in each of its
 // partial items at the item's record -- one lane per item, all at once -- and
 // fold every record this wave completed.
+//
+// A tiny batch's plan (wg_fold) puts each unit on the four waves of one
+// workgroup, one chunk per wave: every wave of the workgroup comes here once
+// (those with no item too), its partial rows become visible to the
+// workgroup, and after the barrier the wave holding chunk 0 folds the unit's
+// record -- no agent-scope fence and no count.
 template <int D>
 __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, int i_end,
                                                 int lane) {
   if (!a.item_rec) return;
+  if (a.wg_fold) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (i_begin < i_end) {
+      const int rec = ld_uniform(a.item_rec, i_begin);
+      if (rec >= 0 && ld_uniform(a.items, (int64_t)i_begin * ITEM_INTS + F_CHUNK) == 0)
+        fold_record<D>(a, rec, lane);
+    }
+    return;
+  }
   // waves whose items all wrote final rows have nothing to announce (and
   // skip the fence)
   bool any = false;

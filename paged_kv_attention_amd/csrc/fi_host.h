@@ -46,6 +46,9 @@ struct HostPlan {
   // merge record (-1: final rows), and the records of units with no keys
   bool fused = false;
   std::vector<int32_t> item_rec, empty_recs;
+  // fused tiny decode plan with every unit on the four waves of one
+  // workgroup (workers 4u..4u+3): the fold follows a workgroup barrier
+  bool wg_fold = false;
   // graph-stable plan (capacity given in the description): a fixed layout,
   // every launch made whatever the batch, sized by these capacities
   bool stable = false;

@@ -107,6 +107,10 @@ struct AttnArgs {
   const int32_t* parts;
   const int32_t* empty_recs;
   const int32_t* meta;     // META_EMPTY: the number of empty_recs
+  // 1: every split unit's chunks are the items of one workgroup's four waves
+  // (a tiny batch); the wave with chunk 0 folds the unit after a workgroup
+  // barrier instead of the counts above
+  int32_t wg_fold;
   float scale_log2;        // sm_scale * log2(e): logits are kept in base 2
   int32_t num_qo_heads;
   int32_t num_kv_heads;

@@ -172,9 +172,13 @@ constexpr int64_t kPodWideItemSteps = 2;
 // tiny: a decode level with fewer steps than workers whose split units are
 // folded in the kernel (no merge launch to amortise): chunks of
 // max(1, ceil(W / S)) steps and no whole-unit exception, so a short unit's
-// steps run on several idle waves side by side.
+// steps run on several idle waves side by side. wg (tiny, with at most S/4
+// units): unit u runs on the four waves of workgroup u (workers 4u..4u+3),
+// chunk c being its steps [c k, (c+1) k), k = ceil(steps / 4), so that the
+// chunks are folded after a workgroup barrier.
 void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all_partial,
-                 int32_t& next_row, LevelBuild& lb, Level& lv, bool tiny = false) {
+                 int32_t& next_row, LevelBuild& lb, Level& lv, bool tiny = false,
+                 bool wg = false) {
   const int32_t ps = d.page_size;
   const int32_t S = lv.num_workers;
   // Per unit: its pieces (page range and, in balanced mode, the worker).
@@ -201,10 +205,18 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
     for (const Unit& u : units) longest = std::max<int64_t>(longest, ceil_div(u.n_pages, gp));
     const bool whole = !tiny && (int64_t)units.size() <= S && longest - cs < kNoSplitSteps;
     if (whole) c = std::max<int64_t>(1, longest) * gp;
+    if (wg) c = std::max<int64_t>(1, ceil_div(longest, 4)) * gp;
+    for (size_t ui = 0; wg && ui < units.size(); ++ui) {
+      const int64_t n = units[ui].n_pages, ns = ceil_div(n, gp), k = ceil_div(ns, 4);
+      for (int64_t j = 0; j < 4; ++j) {
+        const int64_t s0 = j * k, s1 = std::min(ns, (j + 1) * k);
+        if (s0 < s1) pieces[ui].push_back({s0 * gp, std::min(n, s1 * gp), (int32_t)(4 * ui + j)});
+      }
+    }
     int64_t g = 0;   // global step offset of the unit
     for (size_t ui = 0; whole && ui < units.size(); ++ui)
       if (units[ui].n_pages > 0) pieces[ui].push_back({0, units[ui].n_pages, (int32_t)ui});
-    for (size_t ui = 0; !whole && ui < units.size(); ++ui) {
+    for (size_t ui = 0; !whole && !wg && ui < units.size(); ++ui) {
       const int64_t n = units[ui].n_pages, ns = ceil_div(n, gp);
       for (int64_t p = 0; p < ns;) {
         const int64_t w = (g + p) / cs;
@@ -675,7 +687,11 @@ static fi_status build(const fi_plan_desc& d, const int32_t* kv_indptr, const in
         tiny = fused_tiny(d, steps, hp.level[0].num_workers);
         hp.fused = hp.fused || tiny;
       }
-      build_level(units[0], d, false, next_row, lb[0], hp.level[0], tiny && !d.deterministic);
+      const int32_t S0 = hp.level[0].num_workers;
+      hp.wg_fold = tiny && !d.deterministic && S0 % 4 == 0 &&
+                   (int64_t)units[0].size() * 4 <= S0;
+      build_level(units[0], d, false, next_row, lb[0], hp.level[0], tiny && !d.deterministic,
+                  hp.wg_fold);
     }
     std::vector<int32_t> first_rec[2];
     for (int l = 0; l < hp.num_levels; ++l) first_rec[l] = unit_merges(units[l], lb[l], hp);
@@ -1340,6 +1356,7 @@ extern "C" fi_status fi_plan_get_info(const fi_plan_t* p, fi_plan_info* info) {
   info->num_plist = (int32_t)hp.plist.size();
   info->plist = hp.plist.data();
   info->fused_merge = hp.fused ? 1 : 0;
+  info->wg_fold = hp.wg_fold ? 1 : 0;
   info->item_rec = hp.item_rec.data();
   info->num_empty_recs = (int32_t)hp.empty_recs.size();
   info->empty_recs = hp.empty_recs.data();

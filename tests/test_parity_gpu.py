@@ -274,6 +274,38 @@ def test_fused_merge_bits_equal_merge_kernel(dev, cfg):
                 assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1]), (kern, det)
 
 
+@pytest.mark.parametrize("lens", [[37, 300, 120, 5, 0, 64], [1, 2, 33, 64, 65, 400]])
+def test_workgroup_fold_tiny_decode(dev, lens):
+    """A tiny decode batch (no more steps than workers, at most a quarter as
+    many units) runs each unit on the four waves of one workgroup and folds
+    it after a workgroup barrier: the plan says so, the bf16 result matches
+    the oracle, and every decode kernel repeats its bits over calls."""
+    w = to_mxfp4_cache(to_fp8_cache(make_decode(lens, 8, 2, 128, 16, seed=77, poison=True),
+                                    poison=True), poison=True)
+    g = w.to(dev)
+    p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                w.page_size, device=dev)
+    assert p.info()["wg_fold"] and p.info()["fused_merge"]
+    o_ref, l_ref, a_ref = oracle_decode(w)
+    for kern in ("bf16", "fp8", "mxfp4"):
+        outs = []
+        for rep in range(3):
+            if kern == "bf16":
+                o, lse = fi.paged_decode(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale)
+            elif kern == "fp8":
+                o, lse = fi.paged_decode_fp8(p, g.q, g.k_fp8, g.v_fp8, g.k_scale, g.v_scale,
+                                             g.kv_indices, w.sm_scale)
+            else:
+                o, lse = fi.paged_decode_mxfp4(p, g.q, g.k_fp4, g.v_fp4, g.k_bscale,
+                                               g.v_bscale, g.kv_indices, w.sm_scale)
+            torch.cuda.synchronize()
+            outs.append((o, lse))
+        for o, lse in outs[1:]:
+            assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1]), kern
+        if kern == "bf16":
+            compare(outs[0][0], outs[0][1], o_ref, l_ref, a_ref, what=f"wg fold {lens}")
+
+
 def test_repeat_runs_are_bit_identical(dev, cfg1):
     for det in (False, True):
         o1, l1, _ = gpu_decode(cfg1, dev, deterministic=det)

@@ -407,8 +407,9 @@ def test_tiny_decode_spreads_steps_over_idle_workers():
     """Rule 3b: a decode batch with no more 32-token steps than workers, its
     split units folded in the kernel, runs one step per worker (W <= S):
     every unit of n steps is n one-step chunks on n distinct workers, in
-    order, and every output row is still written exactly once."""
-    ps, S = 16, 1024
+    order, and every output row is still written exactly once. (Twelve
+    units on 40 workers: more than S/4, so rule 3c does not apply.)"""
+    ps, S = 16, 40
     lens = [37, 300, 120, 5, 0, 64]
     indptr, L = _decode_inputs(lens, ps)
     p = plan_ref("decode", 8, 2, ps, indptr, L, S, [16])
@@ -425,3 +426,31 @@ def test_tiny_decode_spreads_steps_over_idle_workers():
     assert (plan_ref("decode", 8, 2, ps, indptr, L, 8, [16], min_chunk_pages=8)
             == plan_ref("decode", 8, 2, ps, indptr, L, 8, [16], min_chunk_pages=8,
                         fold_tiny=False))
+
+
+def test_tiny_decode_units_on_one_workgroup_each():
+    """Rule 3c: with at most S/4 units, unit u's chunks are the items of
+    workers 4u..4u+3 (one workgroup), chunk j covering steps [j k, (j+1) k)
+    with k = ceil(steps / 4); every output row is written exactly once."""
+    ps, S = 16, 1024
+    lens = [37, 300, 120, 5, 0, 64]
+    indptr, L = _decode_inputs(lens, ps)
+    p = plan_ref("decode", 8, 2, ps, indptr, L, S, [16])
+    check_partition(p, ps)
+    assert np.all(check_outputs_once(p, 4, 8, len(lens)) == 1)
+    lv = p["levels"][0]
+    wi = np.asarray(lv["worker_indptr"])
+    assert np.diff(wi).max() == 1
+    by_worker = {w: lv["items"][wi[w]] for w in range(S) if wi[w + 1] > wi[w]}
+    u = 0
+    for r, n_tok in enumerate(lens):
+        for g in range(2):           # units: requests x kv heads, in order
+            ns = -(-n_tok // 32)
+            k = -(-ns // 4)
+            got = [(w % 4, it[F["t_begin"]], it[F["t_end"]]) for w, it in by_worker.items()
+                   if w // 4 == u]
+            want = [(j, 32 * j * k, min(n_tok, 32 * (j + 1) * k)) for j in range(4)
+                    if j * k < min(ns, (j + 1) * k)]
+            assert sorted(got) == want, (r, g, got, want)
+            u += 1
+    assert lv["chunk_pages"] == -(-(-(-300 // 32)) // 4) * 2
