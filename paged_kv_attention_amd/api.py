@@ -38,11 +38,26 @@ def _p(a: Optional[np.ndarray]):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    # the entry points declare these arguments c_void_p, so ctypes converts
+    # the integer address (and None) itself
+    return None if t is None else t.data_ptr()
 
 
-def _stream(device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+def _stream(device) -> int:
+    """The raw handle of the current torch stream on ``device`` (a CUDA
+    torch.device with an index)."""
+    return torch._C._cuda_getCurrentRawStream(device.index)
+
+
+def _device(device) -> Optional[torch.device]:
+    """torch.device with the index filled in (``"cuda"`` is the current
+    device), so that tensors compare equal to it."""
+    if device is None:
+        return None
+    d = torch.device(device)
+    if d.type == "cuda" and d.index is None:
+        d = torch.device("cuda", torch.cuda.current_device())
+    return d
 
 
 class Workspace:
@@ -126,7 +141,7 @@ class Plan:
              self.desc.cap_prefix_pages, self.desc.max_prefix_depth) = cap
         self.num_qo_heads, self.num_kv_heads = num_qo_heads, num_kv_heads
         self.head_dim, self.page_size, self.batch = head_dim, page_size, B
-        self.device = None if device is None else torch.device(device)
+        self.device = _device(device)
         self.workspace = workspace
         ws_dev = ws_host = None
         dev_b = host_b = 0
@@ -261,7 +276,7 @@ class BlockSparsePlan(Plan):
         # up to page_size - 1 rows past the last sequence's end
         self.kv_tokens = int(self._ha["kv_indptr"][-1]) + ps - 1 if layout == "ragged" and S \
             else 0
-        self.device = None if device is None else torch.device(device)
+        self.device = _device(device)
         self.workspace = workspace
         ws_dev = ws_host = None
         dev_b = host_b = 0
@@ -288,6 +303,14 @@ class BlockSparsePlan(Plan):
 
 
 def _check_tensor(t, name, dtype, device, shape=None):
+    # the common case in one expression; anything else goes through the
+    # checks below, which name what is wrong
+    try:
+        if (t.dtype is dtype and t.get_device() == device.index and t.is_contiguous()
+                and (shape is None or t.shape == shape)):
+            return
+    except AttributeError:
+        pass
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
@@ -304,8 +327,8 @@ def _check_cache(plan: Plan, k_cache, v_cache):
     dev = plan.device
     _check_tensor(k_cache, "k_cache", torch.bfloat16, dev)
     _check_tensor(v_cache, "v_cache", torch.bfloat16, dev, k_cache.shape)
-    if k_cache.dim() != 4 or tuple(k_cache.shape[1:]) != (plan.num_kv_heads, plan.page_size,
-                                                          plan.head_dim):
+    if k_cache.dim() != 4 or k_cache.shape[1:] != (plan.num_kv_heads, plan.page_size,
+                                                   plan.head_dim):
         raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match the plan "
                          f"[P, {plan.num_kv_heads}, {plan.page_size}, {plan.head_dim}]")
 
@@ -325,8 +348,11 @@ def _check_table(plan: Plan, t, name: str, key: str):
     table covers (``plan._ha[key][-1]``): the kernels read that many ids
     unchecked, so a shorter table would be read past its end."""
     _check_tensor(t, name, torch.int32, plan.device)
-    ptr = plan._ha.get(key)
-    need = int(ptr[-1]) if ptr is not None and ptr.size else 0
+    needs = plan.__dict__.setdefault("_table_need", {})
+    need = needs.get(key)
+    if need is None:
+        ptr = plan._ha.get(key)
+        need = needs[key] = int(ptr[-1]) if ptr is not None and ptr.size else 0
     if t.numel() < need:
         raise ValueError(f"{name} has {t.numel()} entries, the plan's table needs {need}")
 

@@ -795,3 +795,25 @@ def test_tiny_decode_plan_folds_in_kernel(det):
     assert not q["fused_merge"]
     compare(q, plan_ref("decode", 8, 2, ps, indptr, L_, **level_params(q), deterministic=det,
                         det_chunk_pages=4, fold_tiny=False))
+
+
+def test_binding_tensor_checks_name_the_failure():
+    # the binding's one-expression fast path must not let through what the
+    # detailed checks refuse; on the CPU every call takes the detailed path
+    import torch
+    from paged_kv_attention_amd import api
+    cpu = torch.device("cpu")
+    t = torch.zeros(4, 3, 8, dtype=torch.bfloat16)
+    api._check_tensor(t, "q", torch.bfloat16, cpu, (4, 3, 8))
+    api._check_tensor(t, "q", torch.bfloat16, cpu, t.shape)
+    with pytest.raises(TypeError, match="q must be torch.bfloat16"):
+        api._check_tensor(t.float(), "q", torch.bfloat16, cpu)
+    with pytest.raises(ValueError, match="q has shape"):
+        api._check_tensor(t, "q", torch.bfloat16, cpu, (4, 3, 9))
+    with pytest.raises(ValueError, match="contiguous"):
+        api._check_tensor(t.transpose(0, 1), "q", torch.bfloat16, cpu)
+    with pytest.raises(TypeError, match="torch.Tensor"):
+        api._check_tensor([1, 2], "q", torch.bfloat16, cpu)
+    assert api._device(None) is None
+    assert api._device("cpu") == cpu
+    assert api._ptr(None) is None and api._ptr(t) == t.data_ptr()
