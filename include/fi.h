@@ -110,11 +110,13 @@ typedef enum fi_kv_format {
  * after the attention kernel. FI_MERGE_FUSED (decode plans on the matrix-core
  * engine) folds them inside the attention kernel instead: when a wave's items
  * are done, each partial item counts in at its unit's merge record (a vector
- * atomic at agent scope after a release of its partial rows), and the wave
- * whose count completes the record folds it in part order with the merge
- * kernel's arithmetic, so the bits are the same. It saves the merge launch
- * but measured slower on MI355X: the release and acquire write back and
- * invalidate an XCD's L2 for every wave. Other plans ignore the field. */
+ * atomic at agent scope, once its partial rows, stored with agent-scope
+ * stores, have completed), and the wave whose count completes the record
+ * folds it in part order with the merge kernel's arithmetic, so the bits are
+ * the same. It saves the merge launch but measured slower on MI355X on full
+ * batches: agent-scope stores write through the XCD's L2, which costs more
+ * than the merge launch (Llama-like batch: 98 against 90 us per call). Other
+ * plans ignore the field. */
 typedef enum fi_merge_mode {
   FI_MERGE_DEFAULT = 0,   /* a merge launch after the attention kernel          */
   FI_MERGE_FUSED = 1,     /* folded in the decode kernels (decode plans, matrix

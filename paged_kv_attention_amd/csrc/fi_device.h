@@ -57,6 +57,30 @@ __device__ __forceinline__ int ld_uniform(const int32_t* p, int64_t i) {
   return uniform(((const_i32p)p)[i]);
 }
 
+// Partial rows that the fused merge folds in another workgroup, which may run
+// on another XCD (each XCD has its own L2), are stored and loaded with
+// agent-scope atomic accesses. Those are coherent at that scope by themselves
+// (gfx950 marks them sc1), so announcing them needs only this wave's own
+// stores to have completed -- not a write-back of the whole L2, which an
+// agent-scope release fence performs -- and the folding wave needs no L2
+// invalidate before it reads them.
+__device__ __forceinline__ void st_agent(float* p, f32x4 v) {
+  __hip_atomic_store((uint64_t*)p, __builtin_bit_cast(uint64_t, f32x2{v[0], v[1]}),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((uint64_t*)p + 1, __builtin_bit_cast(uint64_t, f32x2{v[2], v[3]}),
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 ld_agent2(const float* p) {
+  return __builtin_bit_cast(f32x2, __hip_atomic_load((uint64_t*)const_cast<float*>(p),
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Work item fields, all wave-uniform.
 struct Item {
   int q_base, row0, n_rows, g, flags, t_begin, t_end, q_pos0, dst, nsteps;
@@ -196,6 +220,8 @@ __device__ __forceinline__ void finalize_rows(const AttnArgs& a, const Item& it,
     const float lse_v = live ? (st.m[mb] + log2f(lt)) * kLn2 : neg_inf();
     if (it.flags & FLAG_PARTIAL) {
       float* op = a.part_o + (int64_t)(it.dst + rl) * D;
+      // rows folded by the fused merge across workgroups: agent-scope stores
+      const bool scoped = a.item_rec != nullptr && !a.wg_fold;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float* d0 = op + DPL * (4 * grp + r);
@@ -203,10 +229,14 @@ __device__ __forceinline__ void finalize_rows(const AttnArgs& a, const Item& it,
         for (int m = 0; m < DPL; m += 4) {
           f32x4 v = {st.acc[mb][m][r] * inv, st.acc[mb][m + 1][r] * inv,
                      st.acc[mb][m + 2][r] * inv, st.acc[mb][m + 3][r] * inv};
-          *(f32x4*)(d0 + m) = v;
+          if (scoped) st_agent(d0 + m, v);
+          else *(f32x4*)(d0 + m) = v;
         }
       }
-      if (grp == 0) a.part_lse[it.dst + rl] = lse_v;
+      if (grp == 0) {
+        if (scoped) st_agent(a.part_lse + it.dst + rl, lse_v);
+        else a.part_lse[it.dst + rl] = lse_v;
+      }
     } else {
       const int rho = it.row0 + rl;
       const int qi = rho / G, h = rho - qi * G;
@@ -252,12 +282,37 @@ __device__ __forceinline__ void load_q_rows(const AttnArgs& a, const Item& it, i
 // (fi_merge.hip) and the fused fold below run exactly these operations, so a
 // row's bits do not depend on which of them merged it.
 
+template <bool SCOPED>
+__device__ __forceinline__ float lse_at(const AttnArgs& a, int64_t i) {
+  return SCOPED ? ld_agent(a.part_lse + i) : a.part_lse[i];
+}
+
+// FPL = D / 16 consecutive floats of partial row pr, from column col.
+template <int D, bool SCOPED>
+__device__ __forceinline__ auto part_row(const AttnArgs& a, int pr, int col) {
+  constexpr int FPL = D / 16;
+  typedef float vec __attribute__((ext_vector_type(FPL)));
+  const float* src = a.part_o + (int64_t)pr * D + col;
+  vec v;
+  if (SCOPED) {
+#pragma unroll
+    for (int i = 0; i < FPL; i += 2) {
+      const f32x2 x = ld_agent2(src + i);
+      v[i] = x[0];
+      v[i + 1] = x[1];
+    }
+  } else {
+    v = *(const vec*)src;
+  }
+  return v;
+}
+
 // Fold merge record e into the final rows (16 lanes per row, four rows per
 // pass): row k < n_rows of the record is unit row row0 + k, query q_base +
 // (row0 + k) / G, head kv_head * G + (row0 + k) % G; its parts are partial
 // rows parts[off + j] + k, j = 0..n-1. With n = 0 the rows get o = 0,
 // lse = -inf.
-template <int D>
+template <int D, bool SCOPED>
 __device__ __forceinline__ void fold_record(const AttnArgs& a, int e, int lane) {
   constexpr int FPL = D / 16;   // outputs per lane
   constexpr int kBatch = 4;     // parts loaded together
@@ -273,25 +328,52 @@ __device__ __forceinline__ void fold_record(const AttnArgs& a, int e, int lane) 
     const int row = h0 + (lane >> 4);
     const int rowc = row < nh ? row : h0;     // lanes past the rows load a real row
     float M = neg_inf();
-    for (int j0 = 0; j0 < n; j0 += 2 * kBatch) {
+    float z = 0.f;
+    vec acc = vec{};
+    if (n <= 2 * kBatch) {
+      // every part in one round of loads (the common case; a fold at the end
+      // of the attention kernel sits on its critical path): the same max and
+      // the same multiply-adds, in the same order, as the two passes below
+      float l[2 * kBatch];
+      vec v[2 * kBatch];
+#pragma unroll
+      for (int u = 0; u < 2 * kBatch; ++u) {
+        l[u] = neg_inf();
+        if (u < n) {
+          const int pr = ld_uniform(a.parts, off + u) + rowc;
+          l[u] = lse_at<SCOPED>(a, pr);
+          v[u] = part_row<D, SCOPED>(a, pr, col);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2 * kBatch; ++u) M = fmaxf(M, l[u]);
+#pragma unroll
+      for (int u = 0; u < 2 * kBatch; ++u) {
+        if (u < n) {
+          const float w = (l[u] == neg_inf()) ? 0.f : expf(l[u] - M);
+          z += w;
+#pragma unroll
+          for (int i = 0; i < FPL; ++i) acc[i] = __builtin_fmaf(w, v[u][i], acc[i]);
+        }
+      }
+    }
+    for (int j0 = 0; j0 < n && n > 2 * kBatch; j0 += 2 * kBatch) {
       float l[2 * kBatch];
 #pragma unroll
       for (int u = 0; u < 2 * kBatch; ++u)
-        l[u] = j0 + u < n ? a.part_lse[ld_uniform(a.parts, off + j0 + u) + rowc] : neg_inf();
+        l[u] = j0 + u < n ? lse_at<SCOPED>(a, ld_uniform(a.parts, off + j0 + u) + rowc) : neg_inf();
 #pragma unroll
       for (int u = 0; u < 2 * kBatch; ++u) M = fmaxf(M, l[u]);
     }
-    float z = 0.f;
-    vec acc = vec{};
-    for (int j0 = 0; j0 < n; j0 += kBatch) {
+    for (int j0 = 0; j0 < n && n > 2 * kBatch; j0 += kBatch) {
       float l[kBatch];
       vec v[kBatch];
 #pragma unroll
       for (int u = 0; u < kBatch; ++u) {
         if (j0 + u < n) {
           const int pr = ld_uniform(a.parts, off + j0 + u) + rowc;
-          l[u] = a.part_lse[pr];
-          v[u] = *(const vec*)(a.part_o + (int64_t)pr * D + col);
+          l[u] = lse_at<SCOPED>(a, pr);
+          v[u] = part_row<D, SCOPED>(a, pr, col);
         }
       }
 #pragma unroll
@@ -322,7 +404,7 @@ template <int D>
 __device__ __forceinline__ void fused_merge_start(const AttnArgs& a, int w, int lane) {
   if (!a.item_rec) return;
   const int n_empty = ld_uniform(a.meta, META_EMPTY);
-  for (int k = w; k < n_empty; k += a.num_workers) fold_record<D>(a, ld_uniform(a.empty_recs, k), lane);
+  for (int k = w; k < n_empty; k += a.num_workers) fold_record<D, false>(a, ld_uniform(a.empty_recs, k), lane);
 }
 
 // At the end of a worker's stream (so that the release below, which waits for
@@ -346,7 +428,7 @@ __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, 
     if (i_begin < i_end) {
       const int rec = ld_uniform(a.item_rec, i_begin);
       if (rec >= 0 && ld_uniform(a.items, (int64_t)i_begin * ITEM_INTS + F_CHUNK) == 0)
-        fold_record<D>(a, rec, lane);
+        fold_record<D, false>(a, rec, lane);
     }
     return;
   }
@@ -356,9 +438,12 @@ __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, 
   for (int i0 = i_begin; i0 < i_end && !any; i0 += 64)
     any = __ballot(i0 + lane < i_end && a.item_rec[i0 + lane] >= 0) != 0;
   if (!any) return;
-  // the partial rows written by this wave become visible at agent scope (to
-  // a folding wave on another XCD) before any count that announces them
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // the partial rows written by this wave (agent-scope stores) have completed,
+  // so they are visible at agent scope -- to a folding wave on another XCD --
+  // before any count that announces them
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0), expcnt and lgkmcnt untouched
+  asm volatile("" ::: "memory");
   for (int i0 = i_begin; i0 < i_end; i0 += 64) {
     const int i = i0 + lane;
     int rec = -1;
@@ -376,12 +461,14 @@ __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, 
     }
     uint64_t done = __ballot(last);
     if (done) {
-      // the other chunks' partial rows, released before their counts
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      // the other chunks' partial rows completed before their counts, and the
+      // fold reads them with agent-scope loads, issued after the counts came
+      // back
+      asm volatile("" ::: "memory");
       while (done) {
         const int l = __builtin_ctzll(done);
         done &= done - 1;
-        fold_record<D>(a, __builtin_amdgcn_readlane(rec, l), lane);
+        fold_record<D, true>(a, __builtin_amdgcn_readlane(rec, l), lane);
       }
     }
   }

@@ -494,13 +494,12 @@ static fi_status fill_defaults(const fi_plan_desc* din, fi_plan_desc& d) {
 // FI_MERGE_FUSED decode plans on the matrix cores fold their split units at
 // the end of the attention kernel (its decode kernels count chunks in and the
 // last folds); so do default-mode ones with fewer 32-token steps than
-// workers (tiny batches: few waves, so the fences are cheap, and the plan
-// then spreads each unit's steps over idle waves), except graph-stable plans,
-// whose layout is fixed by the description. Every other plan launches the
-// merge kernel after the attention kernel: on MI355X the fused fold's
-// agent-scope release and acquire (an L2 write-back and invalidate of the
-// XCD per wave) cost more than the merge launch on full batches (Llama-like
-// batch: 121 against 89 us per call).
+// workers (tiny batches: few partial rows, and the plan then spreads each
+// unit's steps over idle waves), except graph-stable plans, whose layout is
+// fixed by the description. Every other plan launches the merge kernel after
+// the attention kernel: on MI355X the fused fold's agent-scope partial stores,
+// which write through the XCD's L2, cost more than the merge launch on full
+// batches (Llama-like batch: 98 against 90 us per call).
 static bool fused_merge(const fi_plan_desc& d) {
   return d.kind == FI_KIND_DECODE && d.decode_engine == FI_ENGINE_MFMA &&
          d.merge_mode == FI_MERGE_FUSED;
