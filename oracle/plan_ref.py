@@ -105,7 +105,7 @@ import heapq
 NO_SPLIT_STEPS = 12  # balanced mode keeps units whole if splitting saves fewer steps
 POD_WIDE_STEP = 4        # fused launch: time of a wide workgroup step ...
 POD_DECODE_STEP = 9      # ... and of a decode wavefront step
-POD_WIDE_ITEM_STEPS = 2  # starting a wide item, in wide steps
+POD_WIDE_ITEM_STEPS = 4  # starting and ending a wide item, in wide steps
 POD_DECODE_ROWS = 16  # query rows of a request that runs in the decode role
 MERGE_ROWS = 16       # unit rows per merge record at most
 FLAG_LIST_Q = 1     # query rows come from the member list (cascade prefix)

@@ -164,10 +164,13 @@ constexpr int64_t kNoSplitSteps = 12;
 // Fused launch: relative time of a wide-role workgroup step (up to 128 rows
 // through MFMA) and of a decode-role wavefront step, with the two roles
 // sharing the chip and the KV coming from HBM (a decode workgroup runs four
-// wavefronts side by side), and the start of a wide item in wide steps.
+// wavefronts side by side), and the start and end of a wide item in wide
+// steps (the query load, the pipeline fill, the output rows and the closing
+// barrier of an item took about four to five steps' time in the fused
+// launch, timed inside the kernel on the shared-prefix cascade batch).
 constexpr int64_t kPodWideStep = 4;
 constexpr int64_t kPodDecodeStep = 9;
-constexpr int64_t kPodWideItemSteps = 2;
+constexpr int64_t kPodWideItemSteps = 4;
 
 // tiny: a decode level with fewer steps than workers whose split units are
 // folded in the kernel (no merge launch to amortise): chunks of
