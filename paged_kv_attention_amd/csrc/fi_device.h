@@ -407,8 +407,8 @@ __device__ __forceinline__ void fused_merge_start(const AttnArgs& a, int w, int 
   for (int k = w; k < n_empty; k += a.num_workers) fold_record<D, false>(a, ld_uniform(a.empty_recs, k), lane);
 }
 
-// At the end of a worker's stream (so that the release below, which waits for
-// every load and store of the wave, drains no prefetch): count in each of its
+// At the end of a worker's stream (so that the wait below, for every load and
+// store of the wave, drains no prefetch): count in each of its
 // partial items at the item's record -- one lane per item, all at once -- and
 // fold every record this wave completed.
 //
@@ -433,7 +433,7 @@ __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, 
     return;
   }
   // waves whose items all wrote final rows have nothing to announce (and
-  // skip the fence)
+  // skip the wait)
   bool any = false;
   for (int i0 = i_begin; i0 < i_end && !any; i0 += 64)
     any = __ballot(i0 + lane < i_end && a.item_rec[i0 + lane] >= 0) != 0;
