@@ -73,11 +73,14 @@ be compared with it element for element:
    (capped at P - 1), else the n in [1, P - 1] that minimises, in order,
    max(T_w, T_d), then T_w, then n. With c_w = max(m_w, ceil(W_w / n)) and
    c_d = max(m_d, ceil(W_d / (4 (P - n)))) the two roles' quotas under rule 3
-   (m: a role's minimum chunk in steps), T_d = 9 c_d and T_w = 4 (c_w + 2 k),
+   (m: a role's minimum chunk in steps), T_d = 9 c_d and T_w = 4 (c_w + 4 k),
    k the most items any wide quota holds (1 + the unit ends strictly inside
    it): a decode wavefront step takes about 9/4 of a wide workgroup step when
    the two roles share the chip and the KV comes from HBM, and a wide item
-   costs about two steps to start. Each role is planned as in
+   costs about four steps to start and end. Deterministic plans (rule 4
+   chunks): with N_r a role's chunk count and L_r its longest chunk in steps,
+   T_w = 4 ceil(N_w / n) (L_w + 4) and T_d = 9 max(L_d, ceil(W_d / (4 (P -
+   n)))). Each role is planned as in
    3-4 over its own workers (n_w workgroups; 4 (P - n_w) wavefronts), then
    its worker list is padded with empty workers to P (wide) and 4P (decode).
    Partial rows are allocated wide role first; merges likewise. A cascade
@@ -348,7 +351,23 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                 inside = [e // c for e in ends[:-1] if e % c]
                 return 1 + max((inside.count(q) for q in set(inside)), default=0)
 
+            # deterministic chunks (rule 4): per role the chunk count and the
+            # longest chunk in steps
+            cdet = max(1, int(det_chunk_pages))
+            nch, longest = [0, 0], [0, 0]
+            for lev_i, lu in enumerate(levels_units):
+                for u in lu:
+                    if u["n_pages"] > 0:
+                        k = _ceil_div(u["n_pages"], cdet)
+                        nch[lev_i] += k
+                        longest[lev_i] = max(longest[lev_i],
+                                             _ceil_div(_ceil_div(u["n_pages"], k), gp))
+
             def cost(n):
+                if deterministic:
+                    tw = POD_WIDE_STEP * _ceil_div(nch[0], n) * (longest[0] + POD_WIDE_ITEM_STEPS)
+                    td = POD_DECODE_STEP * max(longest[1], _ceil_div(w_steps[1], 4 * (P - n)))
+                    return (max(tw, td), tw, n)
                 cw = max(cmin[0], _ceil_div(w_steps[0], n))
                 tw = POD_WIDE_STEP * (cw + POD_WIDE_ITEM_STEPS * busiest(cw))
                 td = POD_DECODE_STEP * max(cmin[1], _ceil_div(w_steps[1], 4 * (P - n)))

@@ -352,13 +352,34 @@ fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
       items_at[c] = best;
       return best;
     };
+    // Deterministic plans cut each unit into chunks of at most c_det pages
+    // and place them longest first: a role's time is then its chunks per
+    // worker (rounded up) times its longest chunk, or its steps per worker
+    // if larger, the wide role paying kPodWideItemSteps per chunk.
+    int64_t nch[2] = {0, 0}, longest[2] = {0, 0};
+    if (d.deterministic) {
+      const int64_t cdet = std::max(1, d.det_chunk_pages);
+      for (int l = 0; l < 2; ++l)
+        for (const Unit& u : units[l]) {
+          if (u.n_pages <= 0) continue;
+          const int64_t k = ceil_div(u.n_pages, cdet);
+          nch[l] += k;
+          longest[l] = std::max(longest[l], ceil_div(ceil_div(u.n_pages, k), gp));
+        }
+    }
     int64_t best_t = -1, best_w = 0;
     nw = 1;
     for (int32_t n = 1; n < P; ++n) {
-      const int64_t cw = std::max(cmin[0], ceil_div(steps[0], n));
-      const int64_t tw = kPodWideStep * (cw + kPodWideItemSteps * max_items(cw));
-      const int64_t td =
-          kPodDecodeStep * std::max(cmin[1], ceil_div(steps[1], (int64_t)WAVES_PER_BLOCK * (P - n)));
+      const int64_t waves = (int64_t)WAVES_PER_BLOCK * (P - n);
+      int64_t tw, td;
+      if (d.deterministic) {
+        tw = kPodWideStep * ceil_div(nch[0], n) * (longest[0] + kPodWideItemSteps);
+        td = kPodDecodeStep * std::max(longest[1], ceil_div(steps[1], waves));
+      } else {
+        const int64_t cw = std::max(cmin[0], ceil_div(steps[0], n));
+        tw = kPodWideStep * (cw + kPodWideItemSteps * max_items(cw));
+        td = kPodDecodeStep * std::max(cmin[1], ceil_div(steps[1], waves));
+      }
       const int64_t t = std::max(tw, td);
       if (best_t < 0 || t < best_t || (t == best_t && tw < best_w)) {
         best_t = t;
