@@ -639,12 +639,15 @@ def _capture(fn):
     return graph
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 4, "pod", "cascade_pod", "fp8", "mxfp4"])
+@pytest.mark.parametrize("cfg", [0, 1, 3, 4, "pod", "cascade_pod", "fp8", "mxfp4", "fused"])
 def test_graph_replay_matches_eager(dev, cfg):
     """A captured run call (no allocation, no memset inside) replays to the
-    eager bits, replay after replay, with other eager work in between."""
+    eager bits, replay after replay, with other eager work in between. The
+    tiny batch (folded after a workgroup barrier) and merge="fused" (folded
+    by arrival counts, which each call's last arrival resets) are included:
+    a count left over from a call would leave rows unfolded."""
     w = (make_pod_mix(poison=False) if cfg == "pod" else
-         make_config(3 if cfg == "cascade_pod" else 1 if cfg in ("fp8", "mxfp4") else cfg,
+         make_config(3 if cfg == "cascade_pod" else 1 if cfg in ("fp8", "mxfp4", "fused") else cfg,
                      poison=False))
     if cfg == "fp8":
         w = to_fp8_cache(w, poison=False)
@@ -667,7 +670,9 @@ def test_graph_replay_matches_eager(dev, cfg):
                                                       w.sm_scale, out=o, lse=l)
     elif w.kind == "decode":
         p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                    w.page_size, device=dev)
+                    w.page_size, device=dev, merge="fused" if cfg == "fused" else "default")
+        if cfg in (0, "fused"):
+            assert p.info()["fused_merge"]
         call = lambda o, l: fi.paged_decode(p, g.q, g.k_cache, g.v_cache, g.kv_indices,  # noqa
                                             w.sm_scale, out=o, lse=l)
     elif w.kind == "cascade":
