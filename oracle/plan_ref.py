@@ -47,9 +47,11 @@ be compared with it element for element:
    k = ceil(ns / 4), chunk j covers steps [j k, min(ns, (j+1) k)) (empty
    ones dropped) on worker 4u + j; the reported chunk size is
    max(1, ceil(longest / 4)) * gp pages.
-4. Deterministic mode. A unit of n pages has k = ceil(n / c) chunks with
-   c = det_chunk_pages, chunk j covering pages [floor(j*n/k),
-   floor((j+1)*n/k)): boundaries depend on the request alone. Chunks are
+4. Deterministic mode. A unit of n pages has k chunks, chunk j covering
+   pages [floor(j*n/k), floor((j+1)*n/k)): k = ceil(n / c) on a wide level
+   (128-row units), k = min(ceil(n / max(1, c // 2)), DET_MAX_CHUNKS = 16)
+   on a decode-style one (16-row units), c = det_chunk_pages; boundaries
+   depend on the request alone. Chunks are
    placed longest-processing-time-first (Graham): sorted by (cost
    descending, enumeration index), cost = pages + 1, each given to the
    worker with the smallest load, ties to the lowest worker index; a worker
@@ -106,6 +108,7 @@ from __future__ import annotations
 import heapq
 
 NO_SPLIT_STEPS = 12  # balanced mode keeps units whole if splitting saves fewer steps
+DET_MAX_CHUNKS = 16  # deterministic chunks of a decode-style unit at most
 POD_WIDE_STEP = 4        # fused launch: time of a wide workgroup step ...
 POD_DECODE_STEP = 9      # ... and of a decode wavefront step
 POD_WIDE_ITEM_STEPS = 4  # starting and ending a wide item, in wide steps
@@ -140,17 +143,29 @@ def _lpt(items, num_workers):
     return flat, indptr
 
 
+def _det_chunks(n, c, decode_style):
+    """Rule 4: the number of deterministic chunks of a unit of n pages."""
+    if n <= 0:
+        return 0
+    c = max(1, int(c))
+    if not decode_style:
+        return _ceil_div(n, c)
+    return min(_ceil_div(n, max(1, c // 2)), DET_MAX_CHUNKS)
+
+
 def _unit_pieces(units, num_workers, deterministic, det_chunk_pages, min_chunk_pages,
-                 page_size, tiny=False, wg=False):
+                 page_size, tiny=False, wg=False, decode_style=False):
     """Per unit: list of (p0, p1, worker) page pieces in order; and c in pages.
     ``tiny`` (rule 3b): quotas of max(1, ceil(W / S)) steps and no whole-unit
     exception; ``wg`` (rule 3c): unit u on workers 4u..4u+3."""
     pieces = []
     if deterministic:
         c = max(1, int(det_chunk_pages))
+        if decode_style:
+            c = max(1, c // 2)
         for u in units:
             n = u["n_pages"]
-            k = _ceil_div(n, c) if n > 0 else 0
+            k = _det_chunks(n, det_chunk_pages, decode_style)
             pieces.append([((j * n) // k, ((j + 1) * n) // k, None) for j in range(k)])
         return pieces, c
     # balanced: quotas counted in 32-token steps (gp pages each), so that no
@@ -353,12 +368,11 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
 
             # deterministic chunks (rule 4): per role the chunk count and the
             # longest chunk in steps
-            cdet = max(1, int(det_chunk_pages))
             nch, longest = [0, 0], [0, 0]
             for lev_i, lu in enumerate(levels_units):
                 for u in lu:
                     if u["n_pages"] > 0:
-                        k = _ceil_div(u["n_pages"], cdet)
+                        k = _det_chunks(u["n_pages"], det_chunk_pages, lev_i == 1)
                         nch[lev_i] += k
                         longest[lev_i] = max(longest[lev_i],
                                              _ceil_div(_ceil_div(u["n_pages"], k), gp))
@@ -391,7 +405,7 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                 and sum(_ceil_div(u["n_pages"], gp) for u in units) <= S)
         wg = tiny and S % 4 == 0 and 4 * len(units) <= S
         pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev],
-                                 page_size, tiny, wg)
+                                 page_size, tiny, wg, decode_style=rows_per_block[lev] == 16)
         items = []
         chunks_of = []
         for u, lst in zip(units, pieces):

@@ -23,8 +23,10 @@
 //             whole on worker = its index (a split would save fewer steps
 //             than its merge launch costs)
 //   deterministic: c = det_chunk_pages; a unit of n pages has k = ceil(n/c)
-//             chunks [floor(jn/k), floor((j+1)n/k)), boundaries depending on
-//             the request alone, placed by Graham's longest-processing-time
+//             chunks on a wide level, k = min(ceil(n/(c/2)), kDetMaxChunks)
+//             on a decode-style one, chunk j [floor(jn/k), floor((j+1)n/k)),
+//             boundaries depending on the request alone, placed by Graham's
+//             longest-processing-time
 //             rule (cost = pages + 1, ties to the lower enumeration index and
 //             the lower worker index)
 //   outputs : one chunk -> final rows, else fp32 partial rows + merge
@@ -161,6 +163,20 @@ struct LevelBuild {
 
 // Balanced mode keeps every unit whole when a split would save fewer steps.
 constexpr int64_t kNoSplitSteps = 12;
+// Deterministic chunking depends on a unit alone (so a row's bits do not
+// depend on its batch). A wide level (128-row units, an item costing about
+// four steps to start and end) cuts a unit of n pages into ceil(n / c)
+// chunks, c = det_chunk_pages; a decode-style level (16-row units, items
+// nearly free) into min(ceil(n / (c / 2)), kDetMaxChunks): half-size chunks
+// place evenly on the workers, and the cap keeps very long requests from
+// merging scores of parts.
+constexpr int64_t kDetMaxChunks = 16;
+int64_t det_chunks(int64_t n, int64_t c, bool decode_style) {
+  if (n <= 0) return 0;
+  c = std::max<int64_t>(1, c);
+  if (!decode_style) return ceil_div(n, c);
+  return std::min<int64_t>(ceil_div(n, std::max<int64_t>(1, c / 2)), kDetMaxChunks);
+}
 // Fused launch: relative time of a wide-role workgroup step (up to 128 rows
 // through MFMA) and of a decode-role wavefront step, with the two roles
 // sharing the chip and the KV coming from HBM (a decode workgroup runs four
@@ -189,10 +205,12 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
   std::vector<std::vector<Piece>> pieces(units.size());
   int64_t c;
   if (d.deterministic) {
+    const bool decode_style = lv.rows_per_block == ROWS_DECODE;
     c = std::max(1, d.det_chunk_pages);
+    if (decode_style) c = std::max<int64_t>(1, c / 2);
     for (size_t ui = 0; ui < units.size(); ++ui) {
       const int64_t n = units[ui].n_pages;
-      const int64_t k = n > 0 ? ceil_div(n, c) : 0;
+      const int64_t k = det_chunks(n, d.det_chunk_pages, decode_style);
       for (int64_t j = 0; j < k; ++j) pieces[ui].push_back({(j * n) / k, ((j + 1) * n) / k, -1});
     }
   } else {
@@ -358,11 +376,10 @@ fi_status pod_levels(const fi_plan_desc& d, const std::vector<Unit> (&units)[2],
     // if larger, the wide role paying kPodWideItemSteps per chunk.
     int64_t nch[2] = {0, 0}, longest[2] = {0, 0};
     if (d.deterministic) {
-      const int64_t cdet = std::max(1, d.det_chunk_pages);
       for (int l = 0; l < 2; ++l)
         for (const Unit& u : units[l]) {
           if (u.n_pages <= 0) continue;
-          const int64_t k = ceil_div(u.n_pages, cdet);
+          const int64_t k = det_chunks(u.n_pages, d.det_chunk_pages, l == 1);
           nch[l] += k;
           longest[l] = std::max(longest[l], ceil_div(ceil_div(u.n_pages, k), gp));
         }
@@ -1049,7 +1066,8 @@ static void bound_counts(const fi_plan_desc& d, int32_t num_cus, int64_t max_kv_
   // balanced: items <= S + units (every piece boundary is a quota or a unit
   // boundary); deterministic: items <= pages / c + units
   auto level_bound = [&](int64_t S, int64_t units, int64_t pages_sum, int64_t rpb) {
-    const int64_t items = d.deterministic ? pages_sum / c_det + units : S + units;
+    const int64_t cl = rpb == ROWS_DECODE ? std::max<int64_t>(1, c_det / 2) : c_det;
+    const int64_t items = d.deterministic ? pages_sum / cl + units : S + units;
     part_rows += items * rpb;
     return items;
   };
@@ -1179,10 +1197,11 @@ static void bs_layout_bound(const fi_plan_desc& d, int32_t num_cus, const BsBatc
     q_rows += bb.qo_len[q];
     plist += Hkv * bb.nrb[q] * seq_pages;
   }
-  auto items_of = [&](int64_t S) {
-    return d.deterministic ? unit_pages / c_det + units : S + units;
+  auto items_of = [&](int64_t S, int64_t c) {
+    return d.deterministic ? unit_pages / c + units : S + units;
   };
-  size_t n_items[2] = {(size_t)items_of(P), S1 ? (size_t)items_of(S1) : 0};
+  size_t n_items[2] = {(size_t)items_of(P, c_det),
+                       S1 ? (size_t)items_of(S1, std::max<int64_t>(1, c_det / 2)) : 0};
   const int32_t workers[2] = {(int32_t)P, (int32_t)S1};
   const int64_t part_rows = ((int64_t)n_items[0] + (int64_t)n_items[1]) * ROWS_WIDE;
   const int64_t merges = Hkv * q_rows + 2 * units;

@@ -72,15 +72,25 @@ def test_decode_plan_properties(det, ps):
     S = 37
     p = plan_ref("decode", 32, 8, ps, indptr, L, S, [16], deterministic=det, det_chunk_pages=5,
                  min_chunk_pages=2)
-    check_partition(p, ps)
+    units = check_partition(p, ps)
     cov = check_outputs_once(p, 4, 32, len(lens))
     assert np.all(cov == 1)
     lv = p["levels"][0]
     assert lv["worker_indptr"][0] == 0 and lv["worker_indptr"][-1] == len(lv["items"])
     assert len(lv["worker_indptr"]) == S + 1
-    c = 5 if det else max(2, -(-8 * sum(-(-x // ps) for x in lens) // S))
-    for it in lv["items"]:
-        assert -(-(it[F["t_end"]] - it[F["t_begin"]]) // ps) <= c
+    if det:
+        # rule 4 on a decode-style level: chunks of at most c // 2 pages, or
+        # a 16th of the unit when that cap binds; equal within a page
+        for its in units.values():
+            n = -(-its[-1][F["t_end"]] // ps)
+            k = min(-(-n // 2), 16)
+            assert len(its) == k
+            sizes = [-(-(x[F["t_end"]] - x[F["t_begin"]]) // ps) for x in its]
+            assert max(sizes) <= max(2, -(-n // 16)) and max(sizes) - min(sizes) <= 1
+    else:
+        c = max(2, -(-8 * sum(-(-x // ps) for x in lens) // S))
+        for it in lv["items"]:
+            assert -(-(it[F["t_end"]] - it[F["t_begin"]]) // ps) <= c
 
 
 def test_append_plan_properties():
