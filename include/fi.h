@@ -145,8 +145,9 @@ typedef struct fi_plan_desc {
   int32_t causal;            /* append: 1 = bottom-right causal mask           */
   int32_t deterministic;     /* 1 = chunk boundaries depend on the request only */
   int32_t det_chunk_pages;   /* deterministic chunk size in pages (default 48)
-                                on wide levels; decode-style levels cut a
-                                unit into chunks of half that, at most 16 */
+                                on wide levels; decode-style levels of a bf16
+                                cache cut a unit into chunks of half that, at
+                                most 16 */
   int32_t min_chunk_pages;   /* balanced mode lower bound on chunk pages (default 8) */
   int32_t num_cus;           /* compute units to plan for (0 = current device) */
   int32_t workers_per_cu;    /* persistent wavefront workers per CU (default 4;
@@ -248,7 +249,7 @@ fi_status fi_workspace_size(const fi_plan_desc* desc, int64_t max_kv_pages,
  *     "Arithmetic intensity": every shared prefix is read once for all the
  *     requests under it). NULL: every group is a root.
  * The plan splits each request's KV range into chunks (deterministic mode:
- * about det_chunk_pages each, half that on decode-style levels, the same for a
+ * about det_chunk_pages each, half that on bf16 decode-style levels, the same for a
  * request in any batch; balanced: about equal total work per worker), places
  * chunks on num_cus*workers_per_cu persistent workers (longest first), and
  * uploads the result into ws_dev with one hipMemcpyAsync on `stream` from the

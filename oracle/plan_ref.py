@@ -50,8 +50,9 @@ be compared with it element for element:
 4. Deterministic mode. A unit of n pages has k chunks, chunk j covering
    pages [floor(j*n/k), floor((j+1)*n/k)): k = ceil(n / c) on a wide level
    (128-row units), k = min(ceil(n / max(1, c // 2)), DET_MAX_CHUNKS = 16)
-   on a decode-style one (16-row units), c = det_chunk_pages; boundaries
-   depend on the request alone. Chunks are
+   on a decode-style one (16-row units) of a bf16 cache (``det_half``; FP8
+   and MXFP4 decode plans take ceil(n / c) too), c = det_chunk_pages;
+   boundaries depend on the request alone. Chunks are
    placed longest-processing-time-first (Graham): sorted by (cost
    descending, enumeration index), cost = pages + 1, each given to the
    worker with the smallest load, ties to the lowest worker index; a worker
@@ -206,7 +207,8 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
              num_workers, rows_per_block, deterministic=False, det_chunk_pages=48,
              min_chunk_pages=1, qo_indptr=None, causal=False, prefix_indptr=None,
              prefix_len=None, req_group=None, prefix_parent=None, pod_blocks=None,
-             pod_wide_blocks=0, block_sparse=None, block_sparse_batch=None, fold_tiny=True):
+             pod_wide_blocks=0, block_sparse=None, block_sparse_batch=None, fold_tiny=True,
+             det_half=True):
     """Return the plan as plain lists.
 
     ``kind`` is "decode", "append" or "cascade". ``rows_per_block`` is a list
@@ -405,7 +407,8 @@ def plan_ref(kind, num_qo_heads, num_kv_heads, page_size, kv_indptr, kv_len,
                 and sum(_ceil_div(u["n_pages"], gp) for u in units) <= S)
         wg = tiny and S % 4 == 0 and 4 * len(units) <= S
         pieces, c = _unit_pieces(units, S, deterministic, det_chunk_pages, min_chunk[lev],
-                                 page_size, tiny, wg, decode_style=rows_per_block[lev] == 16)
+                                 page_size, tiny, wg,
+                                 decode_style=det_half and rows_per_block[lev] == 16)
         items = []
         chunks_of = []
         for u, lst in zip(units, pieces):

@@ -167,9 +167,9 @@ constexpr int64_t kNoSplitSteps = 12;
 // depend on its batch). A wide level (128-row units, an item costing about
 // four steps to start and end) cuts a unit of n pages into ceil(n / c)
 // chunks, c = det_chunk_pages; a decode-style level (16-row units, items
-// nearly free) into min(ceil(n / (c / 2)), kDetMaxChunks): half-size chunks
-// place evenly on the workers, and the cap keeps very long requests from
-// merging scores of parts.
+// nearly free) of a bf16 cache into min(ceil(n / (c / 2)), kDetMaxChunks):
+// half-size chunks place evenly on the workers, and the cap keeps very long
+// requests from merging scores of parts.
 constexpr int64_t kDetMaxChunks = 16;
 int64_t det_chunks(int64_t n, int64_t c, bool decode_style) {
   if (n <= 0) return 0;
@@ -205,7 +205,9 @@ void build_level(const std::vector<Unit>& units, const fi_plan_desc& d, bool all
   std::vector<std::vector<Piece>> pieces(units.size());
   int64_t c;
   if (d.deterministic) {
-    const bool decode_style = lv.rows_per_block == ROWS_DECODE;
+    // (the FP8 and MXFP4 decode kernels, with more workers per CU and a
+    // costlier item start, keep whole-size chunks)
+    const bool decode_style = lv.rows_per_block == ROWS_DECODE && d.kv_format == FI_KV_BF16;
     c = std::max(1, d.det_chunk_pages);
     if (decode_style) c = std::max<int64_t>(1, c / 2);
     for (size_t ui = 0; ui < units.size(); ++ui) {

@@ -817,3 +817,22 @@ def test_binding_tensor_checks_name_the_failure():
     assert api._device(None) is None
     assert api._device("cpu") == cpu
     assert api._ptr(None) is None and api._ptr(t) == t.data_ptr()
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "mxfp4"])
+def test_deterministic_decode_chunks_by_kv_format(fmt):
+    """Deterministic decode plans: a bf16 cache's units are cut into
+    half-size chunks (at most 16 a unit), FP8 and MXFP4 ones into whole-size
+    chunks; the C++ planner equals the reference rule either way."""
+    rng = np.random.default_rng(51)
+    lens = list(rng.integers(0, 5000, 30)) + [0, 1, 40000]
+    indptr, L_ = _decode_host(lens, 16)
+    p = host_plan("decode", indptr, L_, 32, 8, 128, 16, deterministic=True, det_chunk_pages=48,
+                  num_cus=6, kv_format=fmt)
+    info = p.info()
+    ref = plan_ref("decode", 32, 8, 16, indptr, L_, **level_params(info), deterministic=True,
+                   det_chunk_pages=48, det_half=fmt == "bf16")
+    compare(info, ref)
+    it = info["levels"][0]["items"]
+    longest_unit = [x for x in it if x[10] == 32]   # the 40000-token request's chunks
+    assert len(longest_unit) == 8 * (16 if fmt == "bf16" else -(-2500 // 48))
