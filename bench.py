@@ -462,7 +462,7 @@ def main():
     achieved = nbytes["total"] / (kern_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(nbytes["total"]),
-            "kernel": "decode_kernel<128,2>", "algorithmic_bytes_per_launch": nbytes["total"],
+            "kernel": "decode_kernel<128,2,false>", "algorithmic_bytes_per_launch": nbytes["total"],
             "avg_launch_us": round(kern_ms * 1e3, 2),
             "timing": "avg over a second pass of the same steps of each attention kernel's "
                       "execution, HIP events recorded in its dispatch (hipExtLaunchKernel) on "

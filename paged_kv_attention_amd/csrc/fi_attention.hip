@@ -43,19 +43,24 @@
 namespace fi {
 namespace {
 
-template <int D, int NP>
+// FOLD: a workgroup-folded plan's launch, whose partial states stay in the
+// dynamic LDS (FoldLds<D>::BYTES of it).
+template <int D, int NP, bool FOLD>
 __global__ __launch_bounds__(256) void decode_kernel(AttnArgs a) {
-  dec::decode_worker<D, NP>(a, blockIdx.x * WAVES_PER_BLOCK + dev::uniform(threadIdx.x >> 6));
+  extern __shared__ float fold_lds[];
+  dec::decode_worker<D, NP, false, dec::kRing, false, FOLD>(
+      a, blockIdx.x * WAVES_PER_BLOCK + dev::uniform(threadIdx.x >> 6), fold_lds);
 }
 
-template <int D>
+template <int D, bool FOLD>
 hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
+  const unsigned lds = FOLD ? dev::FoldLds<D>::BYTES : 0;
   if (a.page_size == 8) {
-    launch_timed((decode_kernel<D, 4>), grid, dim3(256), s, a);
+    launch_timed_lds((decode_kernel<D, 4, FOLD>), grid, dim3(256), lds, s, a);
   } else if (a.page_size == 16) {
-    launch_timed((decode_kernel<D, 2>), grid, dim3(256), s, a);
+    launch_timed_lds((decode_kernel<D, 2, FOLD>), grid, dim3(256), lds, s, a);
   } else {
-    launch_timed((decode_kernel<D, 1>), grid, dim3(256), s, a);
+    launch_timed_lds((decode_kernel<D, 1, FOLD>), grid, dim3(256), lds, s, a);
   }
   return hipGetLastError();
 }
@@ -65,8 +70,12 @@ hipError_t launch_d(const AttnArgs& a, dim3 grid, hipStream_t s) {
 hipError_t launch_decode(const AttnArgs& a, int head_dim, hipStream_t stream) {
   const int blocks = (a.num_workers + WAVES_PER_BLOCK - 1) / WAVES_PER_BLOCK;
   if (blocks == 0) return hipSuccess;
-  if (head_dim == 128) return launch_d<128>(a, dim3(blocks), stream);
-  if (head_dim == 64) return launch_d<64>(a, dim3(blocks), stream);
+  if (head_dim == 128)
+    return a.wg_fold ? launch_d<128, true>(a, dim3(blocks), stream)
+                     : launch_d<128, false>(a, dim3(blocks), stream);
+  if (head_dim == 64)
+    return a.wg_fold ? launch_d<64, true>(a, dim3(blocks), stream)
+                     : launch_d<64, false>(a, dim3(blocks), stream);
   return hipErrorInvalidValue;
 }
 

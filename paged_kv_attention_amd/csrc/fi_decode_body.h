@@ -134,8 +134,13 @@ __device__ __forceinline__ void compute_step(const AttnArgs& a, const Item& it, 
 // it shares them with a second wavefront (two workgroups per CU); a ring of 2
 // keeps the query out of the tiles and loads it when an item's first step is
 // computed, ahead of the next step's loads.
-template <int D, int NP, bool CAUSAL = false, int RING = kRing, bool RAGGED = false>
-__device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
+// FOLD: the launch is a workgroup-folded plan's, and lds is the workgroup's
+// LDS for the partial states (FoldLds); otherwise they go to the workspace
+// (and the stream's code has no LDS path).
+template <int D, int NP, bool CAUSAL = false, int RING = kRing, bool RAGGED = false,
+          bool FOLD = false>
+__device__ __forceinline__ void decode_worker(const AttnArgs& a, int w, float* lds = nullptr) {
+  float* const fold = FOLD ? lds : nullptr;
   static_assert(RING == 2 || RING == 4, "rings of two or four tiles");
   constexpr int KJ = Cfg<D>::KJ;
   constexpr bool QT = RING == 4;   // the query travels in the tiles
@@ -147,7 +152,7 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
   const int i_end = ld_uniform(a.worker_indptr, w + 1);
   const int i_begin = ld_uniform(a.worker_indptr, w);
   if (i_begin >= i_end) {   // (a workgroup-folded plan's barrier needs every wave)
-    fused_merge_end<D>(a, i_begin, i_end, lane);
+    fused_merge_end<D>(a, i_begin, i_end, lane, fold);
     return;
   }
 
@@ -193,7 +198,7 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
     }
     compute_step<D, CAUSAL, QT>(a, citem, cs, X, q_cur, st, col, grp);
     if (cs + 1 >= citem.nsteps) {
-      finalize_rows<D, 1, false>(a, citem, st, 0, col, grp);
+      finalize_rows<D, 1, false>(a, citem, st, 0, col, grp, fold);
       st.reset();
       if (++ci >= i_end) return false;
       cs = 0;
@@ -218,7 +223,7 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w) {
     while (advance(TA, TB) && advance(TB, TA)) {
     }
   }
-  fused_merge_end<D>(a, i_begin, i_end, lane);
+  fused_merge_end<D>(a, i_begin, i_end, lane, fold);
 }
 
 }  // namespace dec

@@ -199,12 +199,25 @@ __device__ __forceinline__ void transpose_v(const typename Cfg<D>::vrow_t (&vv)[
   }
 }
 
+// Partial states of a workgroup-folded unit (a tiny batch's plan: unit u on
+// the four waves of workgroup u, chunk j on wave j) can stay in LDS: wave j
+// writes its 16 rows to slot j, rows padded by eight floats against bank
+// conflicts (and 32-byte aligned for the fold's row reads), then the lse of
+// the four slots. The launch sizes the dynamic LDS with BYTES.
+template <int D>
+struct FoldLds {
+  static constexpr int ROW = D + 8;                 // floats per row
+  static constexpr int LSE = WAVES_PER_BLOCK * 16 * ROW;   // float offset of the lse
+  static constexpr int BYTES = (LSE + WAVES_PER_BLOCK * 16) * 4;
+};
+
 // o = acc / l and lse = (m + log2 l) ln 2 for MB row blocks, to the final
-// output or to fp32 partial rows. Rows at or past n_rows are not written.
+// output or to fp32 partial rows (in LDS slot `wave` when fold is given and
+// the plan folds in the workgroup). Rows at or past n_rows are not written.
 template <int D, int MB, bool LQ>
 __device__ __forceinline__ void finalize_rows(const AttnArgs& a, const Item& it,
                                               const State<D, MB>& st, int rl0, int col,
-                                              int grp) {
+                                              int grp, float* fold = nullptr) {
   constexpr int DPL = Cfg<D>::DPL;
   typedef typename Cfg<D>::vrow_t vrow_t;
   const int G = a.group;
@@ -218,7 +231,19 @@ __device__ __forceinline__ void finalize_rows(const AttnArgs& a, const Item& it,
     const bool live = lt > 0.f;
     const float inv = live ? 1.f / lt : 0.f;
     const float lse_v = live ? (st.m[mb] + log2f(lt)) * kLn2 : neg_inf();
-    if (it.flags & FLAG_PARTIAL) {
+    if ((it.flags & FLAG_PARTIAL) && fold && a.wg_fold) {
+      const int slot = uniform(threadIdx.x >> 6) * 16 + rl;
+      float* op = fold + slot * FoldLds<D>::ROW;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float* d0 = op + DPL * (4 * grp + r);
+#pragma unroll
+        for (int m = 0; m < DPL; m += 4)
+          *(f32x4*)(d0 + m) = f32x4{st.acc[mb][m][r] * inv, st.acc[mb][m + 1][r] * inv,
+                                    st.acc[mb][m + 2][r] * inv, st.acc[mb][m + 3][r] * inv};
+      }
+      if (grp == 0) fold[FoldLds<D>::LSE + slot] = lse_v;
+    } else if (it.flags & FLAG_PARTIAL) {
       float* op = a.part_o + (int64_t)(it.dst + rl) * D;
       // rows folded by the fused merge across workgroups: agent-scope stores
       const bool scoped = a.item_rec != nullptr && !a.wg_fold;
@@ -287,6 +312,15 @@ __device__ __forceinline__ float lse_at(const AttnArgs& a, int64_t i) {
   return SCOPED ? ld_agent(a.part_lse + i) : a.part_lse[i];
 }
 
+// FPL = D / 16 consecutive floats of row k of LDS slot j (FoldLds), from
+// column col.
+template <int D>
+__device__ __forceinline__ auto lds_row(const float* fold, int j, int k, int col) {
+  constexpr int FPL = D / 16;
+  typedef float vec __attribute__((ext_vector_type(FPL)));
+  return *(const vec*)(fold + (j * 16 + k) * FoldLds<D>::ROW + col);
+}
+
 // FPL = D / 16 consecutive floats of partial row pr, from column col.
 template <int D, bool SCOPED>
 __device__ __forceinline__ auto part_row(const AttnArgs& a, int pr, int col) {
@@ -310,10 +344,12 @@ __device__ __forceinline__ auto part_row(const AttnArgs& a, int pr, int col) {
 // Fold merge record e into the final rows (16 lanes per row, four rows per
 // pass): row k < n_rows of the record is unit row row0 + k, query q_base +
 // (row0 + k) / G, head kv_head * G + (row0 + k) % G; its parts are partial
-// rows parts[off + j] + k, j = 0..n-1. With n = 0 the rows get o = 0,
-// lse = -inf.
+// rows parts[off + j] + k, j = 0..n-1 -- or, with fold given, row k of LDS
+// slot j (a workgroup-folded unit: part j is chunk j, on wave j). With n = 0
+// the rows get o = 0, lse = -inf.
 template <int D, bool SCOPED>
-__device__ __forceinline__ void fold_record(const AttnArgs& a, int e, int lane) {
+__device__ __forceinline__ void fold_record(const AttnArgs& a, int e, int lane,
+                                            const float* fold = nullptr) {
   constexpr int FPL = D / 16;   // outputs per lane
   constexpr int kBatch = 4;     // parts loaded together
   typedef float vec __attribute__((ext_vector_type(FPL)));
@@ -339,7 +375,12 @@ __device__ __forceinline__ void fold_record(const AttnArgs& a, int e, int lane) 
 #pragma unroll
       for (int u = 0; u < 2 * kBatch; ++u) {
         l[u] = neg_inf();
-        if (u < n) {
+        if (u < n && fold) {
+          if (u < WAVES_PER_BLOCK) {   // (one slot per wave; a folded unit has at most four parts)
+            l[u] = fold[FoldLds<D>::LSE + u * 16 + rowc];
+            v[u] = lds_row<D>(fold, u, rowc, col);
+          }
+        } else if (u < n) {
           const int pr = ld_uniform(a.parts, off + u) + rowc;
           l[u] = lse_at<SCOPED>(a, pr);
           v[u] = part_row<D, SCOPED>(a, pr, col);
@@ -414,12 +455,13 @@ __device__ __forceinline__ void fused_merge_start(const AttnArgs& a, int w, int 
 //
 // A tiny batch's plan (wg_fold) puts each unit on the four waves of one
 // workgroup, one chunk per wave: every wave of the workgroup comes here once
-// (those with no item too), its partial rows become visible to the
-// workgroup, and after the barrier the wave holding chunk 0 folds the unit's
-// record -- no agent-scope fence and no count.
+// (those with no item too), its partial rows (in LDS when fold is given,
+// else in the workspace) become visible to the workgroup, and after the
+// barrier the wave holding chunk 0 folds the unit's record (at most four
+// parts) -- no agent-scope fence and no count.
 template <int D>
 __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, int i_end,
-                                                int lane) {
+                                                int lane, const float* fold = nullptr) {
   if (!a.item_rec) return;
   if (a.wg_fold) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -428,7 +470,7 @@ __device__ __forceinline__ void fused_merge_end(const AttnArgs& a, int i_begin, 
     if (i_begin < i_end) {
       const int rec = ld_uniform(a.item_rec, i_begin);
       if (rec >= 0 && ld_uniform(a.items, (int64_t)i_begin * ITEM_INTS + F_CHUNK) == 0)
-        fold_record<D, false>(a, rec, lane);
+        fold_record<D, false>(a, rec, lane, fold);
     }
     return;
   }

@@ -38,16 +38,22 @@ struct LaunchTiming {
 };
 LaunchTiming& launch_timing();   // this thread's
 
-// Launch an attention kernel (errors are left for hipGetLastError).
+// Launch an attention kernel with `lds` bytes of dynamic LDS (errors are
+// left for hipGetLastError).
 template <typename K, typename... Args>
-inline void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+inline void launch_timed_lds(K kernel, dim3 grid, dim3 block, unsigned lds, hipStream_t s,
+                             Args... args) {
   LaunchTiming& t = launch_timing();
   if (t.stop) {
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, t.start, t.stop, 0, args...);
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t.start, t.stop, 0, args...);
     t.start = nullptr;
   } else {
-    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+    hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
   }
+}
+template <typename K, typename... Args>
+inline void launch_timed(K kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  launch_timed_lds(kernel, grid, block, 0u, s, args...);
 }
 
 enum ItemField {
