@@ -147,10 +147,15 @@ __device__ __forceinline__ void decode_worker(const AttnArgs& a, int w, float* l
   typedef Tile<D, QT> TileT;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, grp = lane >> 4;
-  if (w >= a.num_workers) return;
-  fused_merge_start<D>(a, w, lane);
-  const int i_end = ld_uniform(a.worker_indptr, w + 1);
-  const int i_begin = ld_uniform(a.worker_indptr, w);
+  // the first loads of every wave in one round trip: its stream's bounds
+  // (waves past the last worker read the table's end, then leave) and the
+  // plan's count of units with no keys (the meta section is always there)
+  const int nw = a.num_workers;
+  const int i_begin = ld_uniform(a.worker_indptr, min(w, nw));
+  const int i_end = ld_uniform(a.worker_indptr, min(w + 1, nw));
+  const int n_empty = ld_uniform(a.meta, META_EMPTY);
+  if (w >= nw) return;
+  fused_merge_start<D>(a, w, lane, n_empty);
   if (i_begin >= i_end) {   // (a workgroup-folded plan's barrier needs every wave)
     fused_merge_end<D>(a, i_begin, i_end, lane, fold);
     return;

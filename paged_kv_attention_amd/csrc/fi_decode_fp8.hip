@@ -353,10 +353,13 @@ __global__ __launch_bounds__(256) void decode_fp8_kernel(AttnArgs a) {
   const int col = lane & 15, grp = lane >> 4;
   const int wave = uniform(threadIdx.x >> 6);
   const int w = blockIdx.x * WAVES_PER_BLOCK + wave;
-  if (w >= a.num_workers) return;
-  fused_merge_start<D>(a, w, lane);
-  const int i_end = ld_uniform(a.worker_indptr, w + 1);
-  const int i_begin = ld_uniform(a.worker_indptr, w);
+  // first loads in one round trip (as in the bf16 decode worker)
+  const int nw = a.num_workers;
+  const int i_begin = ld_uniform(a.worker_indptr, min(w, nw));
+  const int i_end = ld_uniform(a.worker_indptr, min(w + 1, nw));
+  const int n_empty = ld_uniform(a.meta, META_EMPTY);
+  if (w >= nw) return;
+  fused_merge_start<D>(a, w, lane, n_empty);
   if (i_begin >= i_end) {   // (a workgroup-folded plan's barrier needs every wave)
     fused_merge_end<D>(a, i_begin, i_end, lane);
     return;

@@ -439,13 +439,18 @@ __device__ __forceinline__ void fold_record(const AttnArgs& a, int e, int lane,
   }
 }
 
-// At a worker's start: write the records of units with no keys, spread over
-// the workers.
+// At a worker's start: write the records of units with no keys (n_empty of
+// them, the plan's META_EMPTY), spread over the workers.
+template <int D>
+__device__ __forceinline__ void fused_merge_start(const AttnArgs& a, int w, int lane,
+                                                  int n_empty) {
+  if (!a.item_rec) return;
+  for (int k = w; k < n_empty; k += a.num_workers) fold_record<D, false>(a, ld_uniform(a.empty_recs, k), lane);
+}
 template <int D>
 __device__ __forceinline__ void fused_merge_start(const AttnArgs& a, int w, int lane) {
   if (!a.item_rec) return;
-  const int n_empty = ld_uniform(a.meta, META_EMPTY);
-  for (int k = w; k < n_empty; k += a.num_workers) fold_record<D, false>(a, ld_uniform(a.empty_recs, k), lane);
+  fused_merge_start<D>(a, w, lane, ld_uniform(a.meta, META_EMPTY));
 }
 
 // At the end of a worker's stream (so that the wait below, for every load and
