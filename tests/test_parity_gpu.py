@@ -274,6 +274,29 @@ def test_fused_merge_bits_equal_merge_kernel(dev, cfg):
                 assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1]), (kern, det)
 
 
+@pytest.mark.parametrize("D,ps,hq,hkv", [(64, 8, 8, 2), (128, 32, 32, 8), (64, 64, 16, 2),
+                                         (128, 16, 16, 1)])
+def test_workgroup_fold_lds_shapes(dev, D, ps, hq, hkv):
+    """The bf16 kernel of a workgroup-folded plan keeps the four partial
+    states in LDS (its own instantiation per head size and pages per step):
+    every head size, page size and group size (up to 16 rows) matches the
+    oracle and repeats its bits over calls."""
+    lens = [37, 300, 5, 0, 129, 64]
+    w = make_decode(lens, hq, hkv, D, ps, seed=91, poison=True)
+    g = w.to(dev)
+    p = fi.Plan("decode", w.kv_indptr, w.kv_len, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                w.page_size, device=dev)
+    assert p.info()["wg_fold"]
+    outs = []
+    for rep in range(3):
+        outs.append(fi.paged_decode(p, g.q, g.k_cache, g.v_cache, g.kv_indices, w.sm_scale))
+        torch.cuda.synchronize()
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    o_ref, l_ref, a_ref = oracle_decode(w)
+    compare(outs[0][0], outs[0][1], o_ref, l_ref, a_ref, what=f"lds fold D={D} ps={ps} G={hq // hkv}")
+
+
 @pytest.mark.parametrize("lens", [[37, 300, 120, 5, 0, 64], [1, 2, 33, 64, 65, 400]])
 def test_workgroup_fold_tiny_decode(dev, lens):
     """A tiny decode batch (no more steps than workers, at most a quarter as
