@@ -53,16 +53,35 @@ def algorithmic_bytes(w) -> dict:
     return dict(kv=kv, total=kv + q + o + lse + idx)
 
 
-def measured_traffic(launches_bytes: float):
-    """HBM traffic per launch from the committed rocprofv3 counter summary,
-    only if it was taken on the current kernel source."""
+def _profile_summary():
+    """The committed rocprofv3 summary of the headline kernel (HBM counters
+    and kernel-trace duration), only if it was taken on the current kernel
+    source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
     if t.get("kernel_source_hash") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t
+
+
+def measured_traffic(launches_bytes: float):
+    """HBM traffic per launch from the committed rocprofv3 counter summary."""
+    t = _profile_summary()
+    return t.get("hbm_bytes_per_launch") if t else None
+
+
+def traced_launch(total_bytes: float):
+    """The kernel-trace average duration of the same kernel from the committed
+    rocprofv3 summary, and the roofline fraction it gives."""
+    t = _profile_summary()
+    k = t.get("kernel_trace") if t else None
+    if not k:
+        return None
+    return {"avg_launch_us": k["avg_us"],
+            "frac": round(total_bytes / (k["avg_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+            "source": k["source"]}
 
 
 def cpu_baseline(w, budget_s: float):
@@ -466,7 +485,8 @@ def main():
             "avg_launch_us": round(kern_ms * 1e3, 2),
             "timing": "avg over a second pass of the same steps of each attention kernel's "
                       "execution, HIP events recorded in its dispatch (hipExtLaunchKernel) on "
-                      "the launch stream"}
+                      "the launch stream",
+            "rocprof": traced_launch(nbytes["total"])}
     res = {
         "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
